@@ -1,0 +1,121 @@
+"""HSQ decode step (oracle, fp64).  TEST INFRASTRUCTURE ONLY.
+
+Source: "Tamarin (HSQ)" summary, section 2, "Decode process":
+1. Routing: a per-head router scores the L2 summary keys against the current
+   query.
+2. Fetching: under a routing budget beta the router picks the best-scoring
+   groups; their original tokens come from the L3 archive, are dequantised on
+   the GPU and rotated back to their semantic positions.
+3. Attention runs over the union of L1 tokens, L2 summaries and the recovered
+   L3 originals; the summaries of fetched groups are masked so nothing is
+   counted twice.
+
+Readings taken:
+* Query head h uses kv-head h // G (grouped-query attention, G = Hq / Hkv).
+  One selection is made per (sequence, kv-head); its score for group g
+  aggregates the scaled logits scale * q_h . k_hat_g of the G query heads of
+  that kv-head: max (default) or mean.
+* top-beta: the beta largest scores, ties to the lower group index, returned
+  in ascending group order; beta is clamped to [0, ng].
+* "Rotated back to their semantic positions" is the inverse TurboQuant
+  rotation, i.e. dequantisation; the archive holds the same (post-RoPE) keys
+  the model caches, so no positional re-rotation happens.
+* Each unfetched summary is one softmax entry with logit scale * q . k_hat_g
+  (+ summary_bias, default 0); one joint softmax over all entries;
+  scale defaults to 1 / sqrt(d).
+"""
+import numpy as np
+
+from . import codec, tiers
+
+
+def dequant_unit(unit, d, group_n, k_signs, v_signs, cb4, cb3):
+    """Dequantised tiers of one unit: dict of fp64 arrays."""
+    out = {}
+    for name, signs in (("k", k_signs), ("v", v_signs)):
+        c1 = codec.unpack(unit[f"l1{name}"], 4, d)
+        out[f"l1{name}"] = codec.decode(c1, unit[f"l1{name}_n"], signs, cb4[0])
+        c2 = codec.unpack(unit[f"l2{name}"], 3, d)
+        out[f"l2{name}"] = codec.decode(c2, unit[f"l2{name}_n"], signs, cb3[0])
+    return out
+
+
+def dequant_l3_groups(l3_records, sel, group_n, d, k_signs, v_signs, cb4):
+    """Dequantised K and V of the tokens of groups sel: ([len(sel)*N, d], same)."""
+    kp, kn, vp, vn = tiers.split_l3_record(l3_records[np.asarray(sel, dtype=np.int64)], group_n, d)
+    kc = codec.unpack(kp.reshape(-1, d // 2), 4, d)
+    vc = codec.unpack(vp.reshape(-1, d // 2), 4, d)
+    return (codec.decode(kc, kn.reshape(-1), k_signs, cb4[0]),
+            codec.decode(vc, vn.reshape(-1), v_signs, cb4[0]))
+
+
+def route_scores(q_heads, l2k_hat, scale, agg="max"):
+    """Aggregated router score per group.
+
+    q_heads: [G, d] queries of the kv-head's query heads; l2k_hat: [ng, d].
+    Returns (agg scores [ng], per-head logits [G, ng]).
+    """
+    logits = scale * (np.asarray(q_heads, dtype=np.float64) @ l2k_hat.T)
+    if logits.shape[1] == 0:
+        return np.zeros(0), logits
+    if agg == "max":
+        return logits.max(axis=0), logits
+    if agg == "mean":
+        return logits.mean(axis=0), logits
+    raise ValueError("agg must be 'max' or 'mean'")
+
+
+def top_beta(scores, beta):
+    """Indices of the beta largest scores, ties to the lower index, ascending."""
+    scores = np.asarray(scores, dtype=np.float64)
+    ng = scores.size
+    beta = max(0, min(int(beta), ng))
+    order = sorted(range(ng), key=lambda g: (-scores[g], g))
+    return np.array(sorted(order[:beta]), dtype=np.int64)
+
+
+def softmax_attention(q, keys, values, scale, bias=None):
+    """Textbook single-query softmax attention: sum_e softmax(scale q.k_e + b_e) v_e."""
+    keys = np.asarray(keys, dtype=np.float64)
+    values = np.asarray(values, dtype=np.float64)
+    if keys.shape[0] == 0:
+        return np.zeros(values.shape[1] if values.ndim == 2 else q.shape[0])
+    s = scale * (keys @ np.asarray(q, dtype=np.float64))
+    if bias is not None:
+        s = s + bias
+    s = s - s.max()
+    w = np.exp(s)
+    return (w[:, None] * values).sum(axis=0) / w.sum()
+
+
+def hsq_attention_unit(q_heads, deq, l3_records, sel, group_n, d, k_signs, v_signs,
+                       cb4, scale, summary_bias=0.0):
+    """HSQ attention for the G query heads of one unit, given the fetched set sel.
+
+    Entries: L1 tokens, summaries of unfetched groups, tokens of fetched groups.
+    Returns [G, d].
+    """
+    ng = deq["l2k"].shape[0]
+    sel = np.asarray(sel, dtype=np.int64)
+    fetched = np.zeros(ng, dtype=bool)
+    fetched[sel] = True
+    kf, vf = dequant_l3_groups(l3_records, sel, group_n, d, k_signs, v_signs, cb4)
+    keys = np.concatenate([deq["l1k"], deq["l2k"][~fetched], kf], axis=0)
+    vals = np.concatenate([deq["l1v"], deq["l2v"][~fetched], vf], axis=0)
+    bias = np.concatenate([
+        np.zeros(deq["l1k"].shape[0]),
+        np.full(int((~fetched).sum()), float(summary_bias)),
+        np.zeros(kf.shape[0]),
+    ])
+    return np.stack([softmax_attention(qh, keys, vals, scale, bias) for qh in q_heads])
+
+
+def decode_step_unit(q_heads, unit, group_n, d, k_signs, v_signs, cb4, cb3, beta,
+                     scale, agg="max", summary_bias=0.0):
+    """Route + top-beta + attention for one unit.  Returns (out [G, d], sel, scores)."""
+    deq = dequant_unit(unit, d, group_n, k_signs, v_signs, cb4, cb3)
+    scores, _ = route_scores(q_heads, deq["l2k"], scale, agg)
+    sel = top_beta(scores, beta)
+    out = hsq_attention_unit(q_heads, deq, unit["l3"], sel, group_n, d, k_signs, v_signs,
+                             cb4, scale, summary_bias)
+    return out, sel, scores

@@ -1,0 +1,289 @@
+"""Pins of the oracle's tier plan, router, top-beta and union-set attention.
+
+Page: "Tamarin (HSQ)" summary, section 2, "Three-tier architecture" and
+"Decode process" (route the L2 summary keys, fetch the top-beta groups from
+L3, attend over L1 + unfetched summaries + fetched originals, masking the
+fetched groups' summaries).
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import codebook as cb
+from oracle import codec, decode, tiers
+
+
+def make_unit(T=200, d=64, n_sink=4, n_recent=16, n_marked=10, gn=8, seed=0):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((T, d))
+    v = rng.standard_normal((T, d))
+    pool = np.arange(n_sink, T - n_recent)
+    marked = np.sort(rng.choice(pool, size=n_marked, replace=False))
+    l1, groups = tiers.tier_plan(T, n_sink, n_recent, marked, gn)
+    ks = rng.integers(0, 1 << 32, size=d // 32, dtype=np.uint64).astype(np.uint32)
+    vs = rng.integers(0, 1 << 32, size=d // 32, dtype=np.uint64).astype(np.uint32)
+    cb4, cb3 = cb.codebook_f32(d, 4), cb.codebook_f32(d, 3)
+    unit = tiers.build_unit(k, v, l1, groups, ks, vs, cb4, cb3)
+    return dict(k=k, v=v, l1=l1, groups=groups, ks=ks, vs=vs, cb4=cb4, cb3=cb3, unit=unit,
+                marked=marked, T=T, d=d, gn=gn)
+
+
+def test_tier_plan_tiny_counts():
+    # T = 512, 4 sinks, 32 recent, 16 marked: 460 remaining = 57 groups of 8 + 4
+    rng = np.random.default_rng(0)
+    marked = np.sort(rng.choice(np.arange(4, 512 - 32), size=16, replace=False))
+    l1, groups = tiers.tier_plan(512, 4, 32, marked, 8)
+    assert groups.shape == (57, 8)
+    assert l1.size == 56
+
+
+@pytest.mark.parametrize("T,ns,nr,nm,gn", [(512, 4, 32, 16, 8), (300, 4, 64, 7, 16), (50, 4, 64, 0, 8),
+                                           (1000, 0, 0, 0, 8), (129, 1, 0, 3, 16)])
+def test_tier_plan_partition(T, ns, nr, nm, gn):
+    rng = np.random.default_rng(T)
+    lo, hi = ns, max(T - nr, ns)
+    marked = np.sort(rng.choice(np.arange(lo, hi), size=min(nm, hi - lo), replace=False))
+    l1, groups = tiers.tier_plan(T, ns, nr, marked, gn)
+    allpos = np.concatenate([l1, groups.reshape(-1)])
+    np.testing.assert_array_equal(np.sort(allpos), np.arange(T))  # each position exactly once
+    assert np.all(np.diff(l1) > 0)
+    assert np.all(np.diff(groups.reshape(-1)) > 0)
+    must = set(range(min(ns, T))) | set(range(max(T - nr, 0), T)) | set(marked.tolist())
+    assert must <= set(l1.tolist())
+    assert l1.size - len(must) < gn  # only a short remainder is promoted
+    # the promoted remainder are the last non-L1 positions
+    rest = sorted(set(range(T)) - must)
+    assert set(l1.tolist()) - must == set(rest[len(rest) - (len(rest) % gn):])
+
+
+def test_l3_records_reverse_to_single_token_encodes():
+    # reversibility: every archived token decodes exactly as if encoded alone
+    u = make_unit()
+    d, gn = u["d"], u["gn"]
+    kp, kn, vp, vn = tiers.split_l3_record(u["unit"]["l3"], gn, d)
+    for g in (0, 5, u["groups"].shape[0] - 1):
+        for j in range(gn):
+            pos = u["groups"][g, j]
+            c, n, _ = codec.encode(u["k"][pos:pos + 1], u["ks"], u["cb4"][1])
+            np.testing.assert_array_equal(kp[g, j], codec.pack(c, 4)[0])
+            assert kn[g, j] == n[0]
+            c, n, _ = codec.encode(u["v"][pos:pos + 1], u["vs"], u["cb4"][1])
+            np.testing.assert_array_equal(vp[g, j], codec.pack(c, 4)[0])
+            assert vn[g, j] == n[0]
+
+
+def test_summary_is_3bit_encode_of_group_mean():
+    u = make_unit()
+    d = u["d"]
+    g = 3
+    mean = u["k"][u["groups"][g]].mean(axis=0, keepdims=True)
+    c, n, _ = codec.encode(mean, u["ks"], u["cb3"][1])
+    np.testing.assert_array_equal(u["unit"]["l2k"][g], codec.pack(c, 3)[0])
+    assert u["unit"]["l2k_n"][g] == n[0]
+    deq = codec.decode(codec.unpack(u["unit"]["l2k"][g:g + 1], 3, d), u["unit"]["l2k_n"][g:g + 1],
+                       u["ks"], u["cb3"][0])
+    # 3-bit relative error of a summary is about sqrt(d * D(d, 3)) ~ 0.18
+    assert np.linalg.norm(deq - mean) / np.linalg.norm(mean) < 0.3
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_top_beta_matches_stable_sort(seed):
+    rng = np.random.default_rng(seed)
+    s = np.round(rng.standard_normal(300), 1)  # many exact ties
+    for beta in (0, 1, 7, 50, 299, 300, 400):
+        want = np.sort(np.argsort(-s, kind="stable")[: min(beta, 300)])
+        np.testing.assert_array_equal(decode.top_beta(s, beta), want)
+
+
+def _full_dense(u, q_heads, scale):
+    """Dense attention over all T tokens, each encoded on its own at 4 bits."""
+    ck, nk, _ = codec.encode(u["k"], u["ks"], u["cb4"][1])
+    cv, nv, _ = codec.encode(u["v"], u["vs"], u["cb4"][1])
+    kh = codec.decode(ck, nk, u["ks"], u["cb4"][0])
+    vh = codec.decode(cv, nv, u["vs"], u["cb4"][0])
+    return np.stack([decode.softmax_attention(q, kh, vh, scale) for q in q_heads])
+
+
+def test_beta_all_equals_dense_attention():
+    u = make_unit(T=300, seed=4)
+    d = u["d"]
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((3, d)) * 2
+    ng = u["groups"].shape[0]
+    out, sel, _ = decode.decode_step_unit(q, u["unit"], u["gn"], d, u["ks"], u["vs"], u["cb4"],
+                                          u["cb3"], ng, 1 / math.sqrt(d))
+    assert sel.tolist() == list(range(ng))
+    np.testing.assert_allclose(out, _full_dense(u, q, 1 / math.sqrt(d)), rtol=1e-12, atol=1e-12)
+
+
+def test_beta_zero_equals_l1_plus_all_summaries():
+    u = make_unit(T=300, seed=5)
+    d, gn = u["d"], u["gn"]
+    rng = np.random.default_rng(10)
+    q = rng.standard_normal((2, d))
+    scale = 1 / math.sqrt(d)
+    out, sel, _ = decode.decode_step_unit(q, u["unit"], gn, d, u["ks"], u["vs"], u["cb4"], u["cb3"],
+                                          0, scale)
+    assert sel.size == 0
+    # independent construction: encode L1 tokens and group means directly
+    ck, nk, _ = codec.encode(u["k"][u["l1"]], u["ks"], u["cb4"][1])
+    cv, nv, _ = codec.encode(u["v"][u["l1"]], u["vs"], u["cb4"][1])
+    mk = u["k"][u["groups"]].mean(axis=1)
+    mv = u["v"][u["groups"]].mean(axis=1)
+    sk, snk, _ = codec.encode(mk, u["ks"], u["cb3"][1])
+    sv, snv, _ = codec.encode(mv, u["vs"], u["cb3"][1])
+    keys = np.concatenate([codec.decode(ck, nk, u["ks"], u["cb4"][0]),
+                           codec.decode(sk, snk, u["ks"], u["cb3"][0])])
+    vals = np.concatenate([codec.decode(cv, nv, u["vs"], u["cb4"][0]),
+                           codec.decode(sv, snv, u["vs"], u["cb3"][0])])
+    want = np.stack([decode.softmax_attention(qh, keys, vals, scale) for qh in q])
+    np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-12)
+
+
+def test_single_token_and_dominant_logit():
+    d = 64
+    c4, c3 = cb.codebook_f32(d, 4), cb.codebook_f32(d, 3)
+    rng = np.random.default_rng(2)
+    ks = rng.integers(0, 1 << 32, size=2, dtype=np.uint64).astype(np.uint32)
+    vs = rng.integers(0, 1 << 32, size=2, dtype=np.uint64).astype(np.uint32)
+    # T = 1: the output is the one dequantised value
+    k = rng.standard_normal((1, d))
+    v = rng.standard_normal((1, d))
+    l1, groups = tiers.tier_plan(1, 4, 0, [], 8)
+    unit = tiers.build_unit(k, v, l1, groups, ks, vs, c4, c3)
+    out, _, _ = decode.decode_step_unit(rng.standard_normal((1, d)), unit, 8, d, ks, vs, c4, c3, 4,
+                                        0.125)
+    cv, nv, _ = codec.encode(v, vs, c4[1])
+    np.testing.assert_allclose(out[0], codec.decode(cv, nv, vs, c4[0])[0], rtol=1e-13)
+    # one key aligned with q by a large margin: output -> that token's value
+    T = 64
+    k = rng.standard_normal((T, d)) * 0.01
+    v = rng.standard_normal((T, d))
+    k[0] = 10.0 * np.ones(d)
+    l1, groups = tiers.tier_plan(T, 1, 0, [], 8)
+    unit = tiers.build_unit(k, v, l1, groups, ks, vs, c4, c3)
+    q = np.ones((1, d))
+    out, _, _ = decode.decode_step_unit(q, unit, 8, d, ks, vs, c4, c3, 2, 1 / math.sqrt(d))
+    cv, nv, _ = codec.encode(v[:1], vs, c4[1])
+    v0 = codec.decode(cv, nv, vs, c4[0])[0]
+    np.testing.assert_allclose(out[0], v0, atol=1e-6 * np.abs(v0).max())
+
+
+def test_l1_order_invariance():
+    u = make_unit(seed=8)
+    d, gn = u["d"], u["gn"]
+    q = np.random.default_rng(1).standard_normal((2, d))
+    deq = decode.dequant_unit(u["unit"], d, gn, u["ks"], u["vs"], u["cb4"], u["cb3"])
+    sel = np.array([1, 4, 6])
+    a = decode.hsq_attention_unit(q, deq, u["unit"]["l3"], sel, gn, d, u["ks"], u["vs"], u["cb4"], 0.1)
+    perm = np.random.default_rng(2).permutation(deq["l1k"].shape[0])
+    deq2 = dict(deq, l1k=deq["l1k"][perm], l1v=deq["l1v"][perm])
+    b = decode.hsq_attention_unit(q, deq2, u["unit"]["l3"], sel, gn, d, u["ks"], u["vs"], u["cb4"], 0.1)
+    np.testing.assert_allclose(a, b, rtol=1e-12)
+
+
+def test_planted_needle_is_routed():
+    # one group's keys aligned with the query must be selected
+    u = make_unit(T=400, seed=6)
+    d, gn = u["d"], u["gn"]
+    g = 17
+    k = u["k"].copy()
+    q = np.random.default_rng(3).standard_normal((2, d))
+    k[u["groups"][g]] = 3.0 * q[0] / np.linalg.norm(q[0]) * np.sqrt(d) + 0.1 * k[u["groups"][g]]
+    unit = tiers.build_unit(k, u["v"], u["l1"], u["groups"], u["ks"], u["vs"], u["cb4"], u["cb3"])
+    _, sel, scores = decode.decode_step_unit(q, unit, gn, d, u["ks"], u["vs"], u["cb4"], u["cb3"], 1,
+                                             1 / math.sqrt(d))
+    assert sel.tolist() == [g]
+
+
+# ---------------------------------------------------------------------------
+# Independent brute force on a tiny case: pure-Python loops, Sylvester
+# Hadamard, nearest-centroid quantisation, explicit union of entries.
+
+def _bf_rotate(x, signs_pm, H):
+    d = len(x)
+    return [sum(H[i][j] * signs_pm[j] * x[j] for j in range(d)) / math.sqrt(d) for i in range(d)]
+
+
+def _bf_unrotate(y, signs_pm, H):
+    d = len(y)
+    return [signs_pm[i] * sum(H[j][i] * y[j] for j in range(d)) / math.sqrt(d) for i in range(d)]
+
+
+def _bf_quant_dequant(x, signs_pm, H, cent):
+    r = math.sqrt(sum(a * a for a in x))
+    r32 = float(np.float32(r))
+    if r == 0:
+        u = [0.0] * len(x)
+    else:
+        u = [a / r for a in x]
+    y = _bf_rotate(u, signs_pm, H)
+    idx = []
+    for yi in y:
+        best, bj = None, 0
+        for j, c in enumerate(cent):
+            dd = abs(yi - c)
+            if best is None or dd < best:
+                best, bj = dd, j
+        idx.append(bj)
+    yq = [cent[j] for j in idx]
+    return [r32 * a for a in _bf_unrotate(yq, signs_pm, H)], y
+
+
+def test_brute_force_tiny_end_to_end():
+    d, T, gn, beta = 8, 40, 4, 2
+    rng = np.random.default_rng(21)
+    k = rng.standard_normal((T, d))
+    v = rng.standard_normal((T, d))
+    q = rng.standard_normal((2, d))
+    ks = np.array([0b10110010], dtype=np.uint32)
+    vs = np.array([0b01001101], dtype=np.uint32)
+    c4, c3 = cb.codebook_f32(d, 4), cb.codebook_f32(d, 3)
+    marked = [9, 22]
+    l1, groups = tiers.tier_plan(T, 2, 5, marked, gn)
+    unit = tiers.build_unit(k, v, l1, groups, ks, vs, c4, c3)
+    scale = 1 / math.sqrt(d)
+    out, sel, scores = decode.decode_step_unit(q, unit, gn, d, ks, vs, c4, c3, beta, scale)
+
+    # --- brute force ---
+    H = [[1]]
+    while len(H) < d:
+        H = [row + row for row in H] + [row + [-a for a in row] for row in H]
+    spm_k = [(-1.0 if (int(ks[0]) >> i) & 1 else 1.0) for i in range(d)]
+    spm_v = [(-1.0 if (int(vs[0]) >> i) & 1 else 1.0) for i in range(d)]
+    cent4 = [float(c) for c in c4[0]]
+    cent3 = [float(c) for c in c3[0]]
+    l1set = set(range(2)) | set(range(T - 5, T)) | set(marked)
+    rest = [p for p in range(T) if p not in l1set]
+    ngb = len(rest) // gn
+    for p in rest[ngb * gn:]:
+        l1set.add(p)
+    grp = [rest[i * gn:(i + 1) * gn] for i in range(ngb)]
+    near_thr = False
+    kh4, vh4, sk, sv = {}, {}, [], []
+    for p in range(T):
+        kh4[p], yk = _bf_quant_dequant(list(k[p]), spm_k, H, cent4)
+        vh4[p], yv = _bf_quant_dequant(list(v[p]), spm_v, H, cent4)
+        near_thr |= min(abs(a - t) for a in yk + yv for t in c4[1]) < 1e-9
+    for gpos in grp:
+        mk = [sum(k[p][i] for p in gpos) / gn for i in range(d)]
+        mv = [sum(v[p][i] for p in gpos) / gn for i in range(d)]
+        a, _ = _bf_quant_dequant(mk, spm_k, H, cent3)
+        b, _ = _bf_quant_dequant(mv, spm_v, H, cent3)
+        sk.append(a)
+        sv.append(b)
+    assert not near_thr
+    dot = lambda a, b: sum(x * y for x, y in zip(a, b))
+    bf_scores = [max(scale * dot(qh, sk[g]) for qh in q) for g in range(ngb)]
+    np.testing.assert_allclose(scores, bf_scores, rtol=1e-12, atol=1e-12)
+    ranked = sorted(range(ngb), key=lambda g: (-bf_scores[g], g))[:beta]
+    assert sorted(ranked) == sel.tolist()
+    for h, qh in enumerate(q):
+        ents = [(scale * dot(qh, kh4[p]), vh4[p]) for p in sorted(l1set)]
+        ents += [(scale * dot(qh, sk[g]), sv[g]) for g in range(ngb) if g not in ranked]
+        ents += [(scale * dot(qh, kh4[p]), vh4[p]) for g in ranked for p in grp[g]]
+        m = max(e[0] for e in ents)
+        w = [math.exp(e[0] - m) for e in ents]
+        o = [sum(wi * e[1][i] for wi, e in zip(w, ents)) / sum(w) for i in range(d)]
+        np.testing.assert_allclose(out[h], o, rtol=1e-11, atol=1e-12)
