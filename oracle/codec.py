@@ -76,10 +76,13 @@ def encode(x, sign_words, thresholds):
     x = to_f64(x)
     n, d = x.shape
     r = np.sqrt(np.sum(x * x, axis=1))
-    u = np.zeros_like(x)
+    # y = R (x / r) = H (D x) / (sqrt(d) r).  The +-1 sums H (D x) are formed
+    # first: for fp32 / bf16 inputs they are exact in fp64, so a coordinate
+    # whose exact value sits on a threshold (0 is one) is decided exactly.
+    hx = (x * sign_vector(sign_words, d)[None, :]) @ hadamard(d).T
+    y = np.zeros_like(x)
     nz = r > 0
-    u[nz] = x[nz] / r[nz, None]
-    y = u @ rotation_matrix(sign_words, d).T
+    y[nz] = hx[nz] / (np.sqrt(d) * r[nz, None])
     t = np.asarray(thresholds, dtype=np.float32).astype(np.float64)
     codes = np.sum(y[:, :, None] > t[None, None, :], axis=2).astype(np.uint8)
     return codes, r.astype(np.float32), y

@@ -158,3 +158,17 @@ def test_encode_is_scale_invariant_and_rotation_consistent():
     direct = np.array([sum(((-1) ** bin(i & j).count("1")) * s[j] * u[j] for j in range(d))
                        for i in range(d)]) / np.sqrt(d)
     np.testing.assert_allclose(y1[0], direct, atol=1e-14)
+
+
+@pytest.mark.parametrize("d,bits", [(64, 3), (128, 4)])
+def test_exact_zero_coordinate_takes_lower_cell(d, bits):
+    # x = e_0 + e_1 with no sign flips: (H x)_i = 1 + (-1)^(i & 1), exactly 0
+    # for every odd i.  A coordinate equal to the middle threshold (0) belongs
+    # to the lower cell, so odd coordinates get code 2^(b-1) - 1.
+    c32, t32 = cb.codebook_f32(d, bits)
+    x = np.zeros((1, d))
+    x[0, 0] = x[0, 1] = 1.0
+    codes, _, y = codec.encode(x, np.zeros(d // 32, dtype=np.uint32), t32)
+    assert np.all(y[0, 1::2] == 0.0)
+    assert np.all(codes[0, 1::2] == (1 << (bits - 1)) - 1)
+    assert np.all(y[0, 0::2] > 0)
