@@ -1,0 +1,294 @@
+// C ABI of libhsq: argument validation, error reporting and launches.
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "hsq_internal.h"
+
+namespace hsq {
+
+static thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int check_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return HSQ_OK;
+  return fail(HSQ_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace hsq
+
+using namespace hsq;
+
+namespace {
+
+bool supported_d(int d) { return d == 64 || d == 128; }
+bool supported_bits(int b) { return b == 3 || b == 4; }
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int check_step_shape(const char* fn, int B, int Hq, int Hkv, int d, int n_l1, int n_groups,
+                     int group_n, int beta) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || n_l1 < 0 || n_groups < 0 || beta < 0)
+    return fail(HSQ_ERR_ARG, std::string(fn) + ": sizes must be positive (n_l1, n_groups, beta >= 0)");
+  if (Hq % Hkv) return fail(HSQ_ERR_ARG, std::string(fn) + ": Hq must be a multiple of Hkv");
+  if (Hq / Hkv > 8) return fail(HSQ_ERR_UNSUPPORTED, std::string(fn) + ": at most 8 query heads per kv-head");
+  if (!supported_d(d)) return fail(HSQ_ERR_UNSUPPORTED, std::string(fn) + ": d must be 64 or 128");
+  if (group_n != 8 && group_n != 16)
+    return fail(HSQ_ERR_UNSUPPORTED, std::string(fn) + ": group_n must be 8 or 16");
+  return HSQ_OK;
+}
+
+}  // namespace
+
+extern "C" const char* hsq_version(void) { return "hsq 0.1 gfx950"; }
+extern "C" const char* hsq_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" int hsq_encode(const void* x, int x_dtype, int64_t n_vec, int d, int bits,
+                          const int64_t* row_idx, int group_n, const uint32_t* signs,
+                          int64_t vecs_per_rot, int n_rot, const float* thresholds,
+                          uint8_t* codes, float* norms, void* stream) {
+  if (n_vec < 0 || group_n < 1 || vecs_per_rot < 1 || n_rot < 1)
+    return fail(HSQ_ERR_ARG, "hsq_encode: bad sizes");
+  if (!supported_d(d)) return fail(HSQ_ERR_UNSUPPORTED, "hsq_encode: d must be 64 or 128");
+  if (!supported_bits(bits)) return fail(HSQ_ERR_UNSUPPORTED, "hsq_encode: bits must be 3 or 4");
+  if (x_dtype != HSQ_F32 && x_dtype != HSQ_BF16)
+    return fail(HSQ_ERR_UNSUPPORTED, "hsq_encode: x_dtype must be HSQ_F32 or HSQ_BF16");
+  if (n_vec == 0) return HSQ_OK;
+  if (!x || !signs || !thresholds || !codes || !norms)
+    return fail(HSQ_ERR_ARG, "hsq_encode: null pointer");
+  EncodeJob j{};
+  j.x = x; j.dtype = x_dtype; j.n_vec = n_vec; j.d = d; j.bits = bits; j.group_n = group_n;
+  j.row_idx = row_idx;
+  j.signs = signs; j.vecs_per_rot = vecs_per_rot; j.n_rot = n_rot; j.thr = thresholds;
+  j.codes = codes; j.code_rec_bytes = d * bits / 8; j.norms = norms; j.norm_rec_floats = 1;
+  j.vecs_per_rec = 1;
+  return check_hip(launch_encode(j, as_stream(stream)), "hsq_encode launch");
+}
+
+extern "C" int hsq_decode(const uint8_t* codes, const float* norms, int64_t n_vec, int d, int bits,
+                          const uint32_t* signs, int64_t vecs_per_rot, int n_rot,
+                          const float* centroids, void* out, int out_dtype, void* stream) {
+  if (n_vec < 0 || vecs_per_rot < 1 || n_rot < 1) return fail(HSQ_ERR_ARG, "hsq_decode: bad sizes");
+  if (!supported_d(d)) return fail(HSQ_ERR_UNSUPPORTED, "hsq_decode: d must be 64 or 128");
+  if (!supported_bits(bits)) return fail(HSQ_ERR_UNSUPPORTED, "hsq_decode: bits must be 3 or 4");
+  if (out_dtype != HSQ_F32 && out_dtype != HSQ_BF16)
+    return fail(HSQ_ERR_UNSUPPORTED, "hsq_decode: out_dtype must be HSQ_F32 or HSQ_BF16");
+  if (n_vec == 0) return HSQ_OK;
+  if (!codes || !norms || !signs || !centroids || !out)
+    return fail(HSQ_ERR_ARG, "hsq_decode: null pointer");
+  DecodeJob j{codes, norms, n_vec, d, bits, signs, vecs_per_rot, n_rot, centroids, out, out_dtype};
+  return check_hip(launch_decode(j, as_stream(stream)), "hsq_decode launch");
+}
+
+extern "C" int hsq_build_tiers(const void* k, const void* v, int dtype, int B, int Hkv, int T,
+                               int d, const int32_t* l1_pos, int n1, const int32_t* group_pos,
+                               int n_groups, int group_n, const uint32_t* k_signs,
+                               const uint32_t* v_signs, const float* thr4, const float* thr3,
+                               uint8_t* l1k, float* l1k_n, uint8_t* l1v, float* l1v_n,
+                               uint8_t* l2k, float* l2k_n, uint8_t* l2v, float* l2v_n,
+                               uint8_t* l3, void* stream) {
+  if (B < 1 || Hkv < 1 || T < 1 || n1 < 0 || n_groups < 0 || group_n < 1)
+    return fail(HSQ_ERR_ARG, "hsq_build_tiers: bad sizes");
+  if ((int64_t)n1 + (int64_t)n_groups * group_n > T)
+    return fail(HSQ_ERR_ARG, "hsq_build_tiers: n1 + n_groups * group_n exceeds T");
+  if (!supported_d(d)) return fail(HSQ_ERR_UNSUPPORTED, "hsq_build_tiers: d must be 64 or 128");
+  if (dtype != HSQ_F32 && dtype != HSQ_BF16)
+    return fail(HSQ_ERR_UNSUPPORTED, "hsq_build_tiers: dtype must be HSQ_F32 or HSQ_BF16");
+  if (!k || !v || !k_signs || !v_signs || !thr4 || !thr3)
+    return fail(HSQ_ERR_ARG, "hsq_build_tiers: null input pointer");
+  if (n1 > 0 && (!l1_pos || !l1k || !l1k_n || !l1v || !l1v_n))
+    return fail(HSQ_ERR_ARG, "hsq_build_tiers: null L1 pointer");
+  if (n_groups > 0 && (!group_pos || !l2k || !l2k_n || !l2v || !l2v_n || !l3))
+    return fail(HSQ_ERR_ARG, "hsq_build_tiers: null L2/L3 pointer");
+  const hipStream_t st = as_stream(stream);
+  const int64_t units = (int64_t)B * Hkv;
+  const int64_t cb4 = d / 2, cb3 = 3 * d / 8;
+  for (int kv = 0; kv < 2; ++kv) {
+    EncodeJob j{};
+    j.x = kv ? v : k; j.dtype = dtype; j.d = d;
+    j.units_per_seq = Hkv; j.rows_per_unit = T;
+    j.signs = kv ? v_signs : k_signs; j.n_rot = Hkv;
+    if (n1 > 0) {  // L1: one 4-bit vector per L1 position
+      EncodeJob a = j;
+      a.bits = 4; a.group_n = 1; a.n_vec = units * n1; a.pos = l1_pos; a.vecs_per_unit = n1;
+      a.pos_per_seq = n1; a.vecs_per_rot = n1; a.thr = thr4;
+      a.codes = kv ? l1v : l1k; a.code_rec_bytes = cb4; a.norms = kv ? l1v_n : l1k_n;
+      a.norm_rec_floats = 1; a.vecs_per_rec = 1;
+      int rc = check_hip(launch_encode(a, st), "hsq_build_tiers L1");
+      if (rc) return rc;
+    }
+    if (n_groups > 0) {
+      // L2: 3-bit code of the mean of each group's N raw vectors
+      EncodeJob a = j;
+      a.bits = 3; a.group_n = group_n; a.n_vec = units * n_groups; a.pos = group_pos;
+      a.vecs_per_unit = n_groups; a.pos_per_seq = (int64_t)n_groups * group_n;
+      a.vecs_per_rot = n_groups; a.thr = thr3;
+      a.codes = kv ? l2v : l2k; a.code_rec_bytes = cb3; a.norms = kv ? l2v_n : l2k_n;
+      a.norm_rec_floats = 1; a.vecs_per_rec = 1;
+      int rc = check_hip(launch_encode(a, st), "hsq_build_tiers L2");
+      if (rc) return rc;
+      // L3: 4-bit code of every grouped token, written into group records
+      EncodeJob c = j;
+      const int64_t rec = (int64_t)group_n * (d + 8);
+      c.bits = 4; c.group_n = 1; c.n_vec = units * n_groups * group_n; c.pos = group_pos;
+      c.vecs_per_unit = (int64_t)n_groups * group_n; c.pos_per_seq = c.vecs_per_unit;
+      c.vecs_per_rot = c.vecs_per_unit; c.thr = thr4;
+      const int64_t base = kv ? group_n * (cb4 + 4) : 0;
+      c.codes = l3 + base; c.code_rec_bytes = rec;
+      c.norms = reinterpret_cast<float*>(l3 + base + group_n * cb4); c.norm_rec_floats = rec / 4;
+      c.vecs_per_rec = group_n;
+      rc = check_hip(launch_encode(c, st), "hsq_build_tiers L3");
+      if (rc) return rc;
+    }
+  }
+  return HSQ_OK;
+}
+
+extern "C" size_t hsq_workspace_bytes(int B, int Hq, int Hkv, int d, int n_l1, int n_groups,
+                                      int beta, int group_n) {
+  if (check_step_shape("hsq_workspace_bytes", B, Hq, Hkv, d, n_l1, n_groups, group_n, beta))
+    return 0;
+  StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, beta < n_groups ? beta : n_groups};
+  return plan_workspace(s).total;
+}
+
+namespace {
+
+int step_common(const char* fn, const StepShape& s, void* workspace, size_t ws_bytes,
+                Workspace& w) {
+  w = plan_workspace(s);
+  if (!workspace || ws_bytes < w.total)
+    return fail(HSQ_ERR_WORKSPACE, std::string(fn) + ": workspace missing or smaller than hsq_workspace_bytes()");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(HSQ_ERR_ARG, std::string(fn) + ": workspace must be 256-byte aligned");
+  return HSQ_OK;
+}
+
+}  // namespace
+
+extern "C" int hsq_route_topk(const float* q, int B, int Hq, int Hkv, int d, const uint8_t* l2k,
+                              const float* l2k_n, int n_groups, const uint32_t* k_signs,
+                              const float* cb3, float scale, int agg, int beta,
+                              int32_t* topk_idx, float* scores, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  int rc = check_step_shape("hsq_route_topk", B, Hq, Hkv, d, 0, n_groups, 8, beta);
+  if (rc) return rc;
+  if (agg != HSQ_AGG_MAX && agg != HSQ_AGG_MEAN) return fail(HSQ_ERR_ARG, "hsq_route_topk: bad agg");
+  if (!q || !k_signs || !cb3 || (n_groups > 0 && (!l2k || !l2k_n)))
+    return fail(HSQ_ERR_ARG, "hsq_route_topk: null input pointer");
+  const int b = beta < n_groups ? beta : n_groups;
+  if (b > 0 && !topk_idx) return fail(HSQ_ERR_ARG, "hsq_route_topk: null topk_idx");
+  StepShape s{B, Hq, Hkv, Hq / Hkv, d, 0, n_groups, 8, b};
+  Workspace w;
+  if ((rc = step_common("hsq_route_topk", s, workspace, ws_bytes, w))) return rc;
+  if (n_groups == 0) return HSQ_OK;
+  StepTensors t{};
+  t.q = q; t.l2k = l2k; t.l2k_n = l2k_n; t.k_signs = k_signs; t.cb3 = cb3; t.scale = scale;
+  t.agg = agg;
+  char* ws = static_cast<char*>(workspace);
+  const hipStream_t st = as_stream(stream);
+  if ((rc = check_hip(launch_qrot(s, t, w, ws, st), "hsq_route_topk qrot"))) return rc;
+  return check_hip(launch_route(s, t, w, ws, ROUTE_TOPK, nullptr, scores, topk_idx, st),
+                   "hsq_route_topk route");
+}
+
+namespace {
+
+int attn_args(const char* fn, const float* q, const uint8_t* l1k, const float* l1k_n,
+              const uint8_t* l1v, const float* l1v_n, int n_l1, const uint8_t* l2k,
+              const float* l2k_n, const uint8_t* l2v, const float* l2v_n, int n_groups,
+              const uint8_t* l3, const uint32_t* k_signs, const uint32_t* v_signs,
+              const float* cb4, const float* cb3, float* out) {
+  if (!q || !out || !k_signs || !v_signs || !cb4 || !cb3)
+    return fail(HSQ_ERR_ARG, std::string(fn) + ": null pointer");
+  if (n_l1 > 0 && (!l1k || !l1k_n || !l1v || !l1v_n))
+    return fail(HSQ_ERR_ARG, std::string(fn) + ": null L1 pointer");
+  if (n_groups > 0 && (!l2k || !l2k_n || !l2v || !l2v_n || !l3))
+    return fail(HSQ_ERR_ARG, std::string(fn) + ": null L2/L3 pointer");
+  return HSQ_OK;
+}
+
+}  // namespace
+
+extern "C" int hsq_decode_attn(const float* q, int B, int Hq, int Hkv, int d, const uint8_t* l1k,
+                               const float* l1k_n, const uint8_t* l1v, const float* l1v_n,
+                               int n_l1, const uint8_t* l2k, const float* l2k_n,
+                               const uint8_t* l2v, const float* l2v_n, int n_groups,
+                               const uint8_t* l3, int group_n, int l3_staged,
+                               const int32_t* topk_idx, int beta, const uint32_t* k_signs,
+                               const uint32_t* v_signs, const float* cb4, const float* cb3,
+                               float scale, float summary_bias, void* workspace,
+                               size_t ws_bytes, float* out, void* stream) {
+  int rc = check_step_shape("hsq_decode_attn", B, Hq, Hkv, d, n_l1, n_groups, group_n, beta);
+  if (rc) return rc;
+  if (beta > n_groups) return fail(HSQ_ERR_ARG, "hsq_decode_attn: beta exceeds n_groups");
+  if ((rc = attn_args("hsq_decode_attn", q, l1k, l1k_n, l1v, l1v_n, n_l1, l2k, l2k_n, l2v, l2v_n,
+                      n_groups, l3, k_signs, v_signs, cb4, cb3, out)))
+    return rc;
+  if (beta > 0 && !topk_idx) return fail(HSQ_ERR_ARG, "hsq_decode_attn: null topk_idx");
+  StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, beta};
+  Workspace w;
+  if ((rc = step_common("hsq_decode_attn", s, workspace, ws_bytes, w))) return rc;
+  StepTensors t{q, l1k, l1k_n, l1v, l1v_n, l2k, l2k_n, l2v, l2v_n, l3, l3_staged ? 1 : 0,
+                k_signs, v_signs, cb4, cb3, scale, summary_bias, HSQ_AGG_MAX, out};
+  char* ws = static_cast<char*>(workspace);
+  const hipStream_t st = as_stream(stream);
+  if ((rc = check_hip(launch_qrot(s, t, w, ws, st), "hsq_decode_attn qrot"))) return rc;
+  if ((rc = check_hip(launch_route(s, t, w, ws, ROUTE_PARTIALS, topk_idx, nullptr, nullptr, st),
+                      "hsq_decode_attn summaries")))
+    return rc;
+  return check_hip(launch_attn(s, t, w, ws, topk_idx, st), "hsq_decode_attn attention");
+}
+
+extern "C" int hsq_decode_step(const float* q, int B, int Hq, int Hkv, int d, const uint8_t* l1k,
+                               const float* l1k_n, const uint8_t* l1v, const float* l1v_n,
+                               int n_l1, const uint8_t* l2k, const float* l2k_n,
+                               const uint8_t* l2v, const float* l2v_n, int n_groups,
+                               const uint8_t* l3, int group_n, int beta, int agg,
+                               const uint32_t* k_signs, const uint32_t* v_signs,
+                               const float* cb4, const float* cb3, float scale,
+                               float summary_bias, int32_t* topk_idx, void* workspace,
+                               size_t ws_bytes, float* out, void* stream) {
+  int rc = check_step_shape("hsq_decode_step", B, Hq, Hkv, d, n_l1, n_groups, group_n, beta);
+  if (rc) return rc;
+  if (agg != HSQ_AGG_MAX && agg != HSQ_AGG_MEAN) return fail(HSQ_ERR_ARG, "hsq_decode_step: bad agg");
+  if ((rc = attn_args("hsq_decode_step", q, l1k, l1k_n, l1v, l1v_n, n_l1, l2k, l2k_n, l2v, l2v_n,
+                      n_groups, l3, k_signs, v_signs, cb4, cb3, out)))
+    return rc;
+  const int b = beta < n_groups ? beta : n_groups;
+  StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, b};
+  Workspace w;
+  if ((rc = step_common("hsq_decode_step", s, workspace, ws_bytes, w))) return rc;
+  StepTensors t{q, l1k, l1k_n, l1v, l1v_n, l2k, l2k_n, l2v, l2v_n, l3, 0,
+                k_signs, v_signs, cb4, cb3, scale, summary_bias, agg, out};
+  char* ws = static_cast<char*>(workspace);
+  const hipStream_t st = as_stream(stream);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + w.idx_off);
+  if ((rc = check_hip(launch_qrot(s, t, w, ws, st), "hsq_decode_step qrot"))) return rc;
+  if ((rc = check_hip(launch_route(s, t, w, ws, ROUTE_TOPK | ROUTE_PARTIALS, nullptr, nullptr,
+                                   idx, st),
+                      "hsq_decode_step route")))
+    return rc;
+  if ((rc = check_hip(launch_attn(s, t, w, ws, idx, st), "hsq_decode_step attention"))) return rc;
+  if (topk_idx && b > 0)
+    return check_hip(hipMemcpyAsync(topk_idx, idx, sizeof(int32_t) * (size_t)B * Hkv * b,
+                                    hipMemcpyDeviceToDevice, st),
+                     "hsq_decode_step topk copy");
+  return HSQ_OK;
+}
+
+extern "C" int hsq_gather_l3(const uint8_t* l3_src, size_t rec_bytes, int B, int Hkv,
+                             int n_groups, const int32_t* topk_idx, int beta, uint8_t* staging,
+                             void* stream) {
+  if (B < 1 || Hkv < 1 || n_groups < 0 || beta < 0 || beta > n_groups)
+    return fail(HSQ_ERR_ARG, "hsq_gather_l3: bad sizes");
+  if (rec_bytes == 0 || rec_bytes % 16) return fail(HSQ_ERR_ARG, "hsq_gather_l3: rec_bytes must be a positive multiple of 16");
+  if (beta == 0) return HSQ_OK;
+  if (!l3_src || !topk_idx || !staging) return fail(HSQ_ERR_ARG, "hsq_gather_l3: null pointer");
+  return check_hip(launch_gather(l3_src, rec_bytes, B * Hkv, n_groups, topk_idx, beta, staging,
+                                 as_stream(stream)),
+                   "hsq_gather_l3 launch");
+}

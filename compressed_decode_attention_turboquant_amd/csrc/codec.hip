@@ -1,0 +1,219 @@
+// TurboQuant encode / decode kernels for gfx950.
+//
+// [Tamarin (HSQ) summary, section 2, "Key technical components",
+// quantisation: scalar quantisation after a fixed random orthonormal
+// rotation; Ablation, Statistical Inference, and Validation for KV-Cache
+// Compression, technical summary, "Experimental setup": random
+// Walsh-Hadamard transform, then a Beta Lloyd-Max codebook.]
+//
+// One vector of d coordinates is spread over d/8 lanes, 8 consecutive
+// coordinates per lane (d=128: 16 lanes, 4 vectors per wave64).  The
+// Walsh-Hadamard transform runs three butterfly stages inside each lane's
+// registers and log2(d/8) stages across lanes with xor shuffles, all in fp32.
+// Quantisation counts thresholds with the codebook's odd symmetry: only the
+// 2^(b-1)-1 positive thresholds are compared, against |y| as integer bit
+// patterns (for non-negative floats the bit order is the numeric order), with
+// a +1 on the key for y <= 0 to turn "t < y" into "t <= |y|".
+#include "hsq_device.h"
+#include "hsq_internal.h"
+
+namespace hsq {
+namespace {
+
+constexpr int kWG = 256;
+
+__device__ __forceinline__ int64_t row_of(const EncodeJob& j, int64_t i, int k) {
+  if (j.row_idx) return j.row_idx[i * j.group_n + k];
+  if (j.pos) {
+    const int64_t u = i / j.vecs_per_unit;
+    const int64_t jj = i - u * j.vecs_per_unit;
+    const int64_t b = u / j.units_per_seq;
+    return u * j.rows_per_unit + j.pos[b * j.pos_per_seq + jj * j.group_n + k];
+  }
+  return i * j.group_n + k;
+}
+
+template <int DT>
+__device__ __forceinline__ void load8(const void* x, int64_t off, float (&v)[8]) {
+  if constexpr (DT == HSQ_F32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + off);
+    float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + off);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __uint_as_float(ws[k] << 16);
+      v[2 * k + 1] = __uint_as_float(ws[k] & 0xffff0000u);
+    }
+  }
+}
+
+template <int D, int BITS, int DT>
+__global__ __launch_bounds__(kWG) void encode_kernel(EncodeJob j) {
+  constexpr int LPV = D / 8;
+  constexpr int VPB = kWG / LPV;
+  constexpr int L = 1 << BITS;
+  constexpr int NPOS = L / 2 - 1;  // positive thresholds t[L/2 .. L-2]
+  const int sub = threadIdx.x % LPV;
+  const int64_t i = (int64_t)blockIdx.x * VPB + threadIdx.x / LPV;
+  const bool valid = i < j.n_vec;
+
+  uint32_t tpos[NPOS];
+#pragma unroll
+  for (int h = 0; h < NPOS; ++h) tpos[h] = __float_as_uint(j.thr[L / 2 + h]);
+
+  float v[8];
+#pragma unroll
+  for (int a = 0; a < 8; ++a) v[a] = 0.f;
+  if (valid) {
+    for (int k = 0; k < j.group_n; ++k) {
+      float t[8];
+      load8<DT>(j.x, row_of(j, i, k) * D + 8 * sub, t);
+#pragma unroll
+      for (int a = 0; a < 8; ++a) v[a] += t[a];
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int a = 0; a < 8; ++a) ss = fmaf(v[a], v[a], ss);
+#pragma unroll
+  for (int m = 1; m < LPV; m <<= 1) ss += __shfl_xor(ss, m, 64);
+  const float r = sqrtf(ss);
+  const float inv = r > 0.f ? 1.0f / (r * sqrtf((float)D)) : 0.f;
+
+  uint32_t sbyte = 0;
+  if (valid) {
+    const int64_t rot = (i / j.vecs_per_rot) % j.n_rot;
+    sbyte = (j.signs[rot * (D / 32) + sub / 4] >> (8 * (sub % 4))) & 0xffu;
+  }
+#pragma unroll
+  for (int a = 0; a < 8; ++a) v[a] = __uint_as_float(__float_as_uint(v[a]) ^ (((sbyte >> a) & 1u) << 31));
+
+  fwht8xlanes<LPV>(v, sub);
+
+  uint32_t packed = 0;
+#pragma unroll
+  for (int a = 0; a < 8; ++a) {
+    const float y = v[a] * inv;
+    const bool pos = y > 0.f;
+    const uint32_t key = (__float_as_uint(y) & 0x7fffffffu) + (pos ? 0u : 1u);
+    int cnt = 0;
+#pragma unroll
+    for (int h = 0; h < NPOS; ++h) cnt += (tpos[h] < key) ? 1 : 0;
+    const uint32_t code = pos ? (uint32_t)(L / 2 + cnt) : (uint32_t)(L / 2 - 1 - cnt);
+    packed |= code << (BITS * a);
+  }
+
+  const int64_t rec = valid ? i / j.vecs_per_rec : 0;
+  const int64_t slot = i - rec * j.vecs_per_rec;
+  constexpr int CB = D * BITS / 8;
+  uint8_t* crow = j.codes + rec * j.code_rec_bytes + slot * CB;
+  if constexpr (BITS == 4) {
+    if (valid) reinterpret_cast<uint32_t*>(crow)[sub] = packed;
+  } else {
+    // 24 bits per lane; quads of lanes write three whole dwords.
+    const uint32_t nxt = __shfl_down(packed, 1, 64);
+    const int qd = sub & 3;
+    if (valid && qd < 3)
+      reinterpret_cast<uint32_t*>(crow)[3 * (sub >> 2) + qd] = (packed >> (8 * qd)) | (nxt << (24 - 8 * qd));
+  }
+  if (valid && sub == 0) j.norms[rec * j.norm_rec_floats + slot] = r / (float)j.group_n;
+}
+
+template <int D, int BITS, int OUT>
+__global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j) {
+  constexpr int LPV = D / 8;
+  constexpr int VPB = kWG / LPV;
+  constexpr int CB = D * BITS / 8;
+  __shared__ float cent[1 << BITS];
+  if (threadIdx.x < (1 << BITS)) cent[threadIdx.x] = j.centroids[threadIdx.x];
+  __syncthreads();
+  const int sub = threadIdx.x % LPV;
+  const int64_t i = (int64_t)blockIdx.x * VPB + threadIdx.x / LPV;
+  const bool valid = i < j.n_vec;
+  uint32_t codes = 0;
+  float r = 0.f;
+  uint32_t sbyte = 0;
+  if (valid) {
+    const uint32_t* row = reinterpret_cast<const uint32_t*>(j.codes + i * CB);
+    if constexpr (BITS == 4) {
+      codes = row[sub];
+    } else {
+      const int bit = 24 * sub;
+      const uint32_t w0 = row[bit >> 5];
+      const int off = bit & 31;
+      codes = w0 >> off;
+      if (off > 8) codes |= row[(bit >> 5) + 1] << (32 - off);
+      codes &= 0xffffffu;
+    }
+    r = j.norms[i];
+    const int64_t rot = (i / j.vecs_per_rot) % j.n_rot;
+    sbyte = (j.signs[rot * (D / 32) + sub / 4] >> (8 * (sub % 4))) & 0xffu;
+  }
+  float v[8];
+#pragma unroll
+  for (int a = 0; a < 8; ++a) v[a] = cent[(codes >> (BITS * a)) & ((1u << BITS) - 1)];
+  fwht8xlanes<LPV>(v, sub);
+  const float s = r / sqrtf((float)D);
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+    v[a] = __uint_as_float(__float_as_uint(v[a] * s) ^ (((sbyte >> a) & 1u) << 31));
+  if (!valid) return;
+  if constexpr (OUT == HSQ_F32) {
+    float4* o = reinterpret_cast<float4*>(static_cast<float*>(j.out) + i * D + 8 * sub);
+    o[0] = make_float4(v[0], v[1], v[2], v[3]);
+    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t lo = __float_as_uint(v[2 * k]), hi = __float_as_uint(v[2 * k + 1]);
+      lo = (lo + 0x7fffu + ((lo >> 16) & 1u)) >> 16;
+      hi = (hi + 0x7fffu + ((hi >> 16) & 1u)) & 0xffff0000u;
+      w[k] = lo | hi;
+    }
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(j.out) + i * D + 8 * sub) =
+        make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+template <int D, int BITS>
+hipError_t encode_dt(const EncodeJob& j, hipStream_t s) {
+  constexpr int VPB = kWG / (D / 8);
+  const int64_t grid = (j.n_vec + VPB - 1) / VPB;
+  if (j.dtype == HSQ_F32)
+    hipLaunchKernelGGL((encode_kernel<D, BITS, HSQ_F32>), dim3((unsigned)grid), dim3(kWG), 0, s, j);
+  else
+    hipLaunchKernelGGL((encode_kernel<D, BITS, HSQ_BF16>), dim3((unsigned)grid), dim3(kWG), 0, s, j);
+  return hipGetLastError();
+}
+
+template <int D, int BITS>
+hipError_t decode_dt(const DecodeJob& j, hipStream_t s) {
+  constexpr int VPB = kWG / (D / 8);
+  const int64_t grid = (j.n_vec + VPB - 1) / VPB;
+  if (j.out_dtype == HSQ_F32)
+    hipLaunchKernelGGL((decode_kernel<D, BITS, HSQ_F32>), dim3((unsigned)grid), dim3(kWG), 0, s, j);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, BITS, HSQ_BF16>), dim3((unsigned)grid), dim3(kWG), 0, s, j);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_encode(const EncodeJob& j, hipStream_t s) {
+  if (j.n_vec <= 0) return hipSuccess;
+  if (j.d == 128) return j.bits == 4 ? encode_dt<128, 4>(j, s) : encode_dt<128, 3>(j, s);
+  return j.bits == 4 ? encode_dt<64, 4>(j, s) : encode_dt<64, 3>(j, s);
+}
+
+hipError_t launch_decode(const DecodeJob& j, hipStream_t s) {
+  if (j.n_vec <= 0) return hipSuccess;
+  if (j.d == 128) return j.bits == 4 ? decode_dt<128, 4>(j, s) : decode_dt<128, 3>(j, s);
+  return j.bits == 4 ? decode_dt<64, 4>(j, s) : decode_dt<64, 3>(j, s);
+}
+
+}  // namespace hsq

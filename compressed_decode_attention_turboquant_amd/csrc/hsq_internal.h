@@ -1,0 +1,112 @@
+// Internal declarations shared by the libhsq translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../include/hsq.h"
+
+namespace hsq {
+
+// ---- error reporting (api.cpp) -------------------------------------------
+int fail(int code, const std::string& msg);
+int check_hip(hipError_t e, const char* what);
+
+// ---- encode / decode (codec.hip) -----------------------------------------
+struct EncodeJob {
+  const void* x;
+  int dtype;          // HSQ_F32 / HSQ_BF16
+  int64_t n_vec;
+  int d;
+  int bits;
+  int group_n;        // rows averaged per output vector
+  // row mapping: row_idx (direct) | pos (tier build) | contiguous
+  const int64_t* row_idx;
+  const int32_t* pos;
+  int64_t vecs_per_unit;
+  int64_t rows_per_unit;
+  int64_t units_per_seq;
+  int64_t pos_per_seq;
+  // rotation: mask (i / vecs_per_rot) % n_rot
+  const uint32_t* signs;
+  int64_t vecs_per_rot;
+  int64_t n_rot;
+  const float* thr;
+  // output: vector i -> record i / vecs_per_rec, slot i % vecs_per_rec
+  uint8_t* codes;
+  int64_t code_rec_bytes;
+  float* norms;
+  int64_t norm_rec_floats;
+  int64_t vecs_per_rec;
+};
+hipError_t launch_encode(const EncodeJob& j, hipStream_t s);
+
+struct DecodeJob {
+  const uint8_t* codes;
+  const float* norms;
+  int64_t n_vec;
+  int d;
+  int bits;
+  const uint32_t* signs;
+  int64_t vecs_per_rot;
+  int64_t n_rot;
+  const float* centroids;
+  void* out;
+  int out_dtype;
+};
+hipError_t launch_decode(const DecodeJob& j, hipStream_t s);
+
+// ---- decode step (route.hip / attn.hip) ------------------------------------
+struct StepShape {
+  int B, Hq, Hkv, G, d;
+  int n_l1, n_groups, group_n, beta;  // beta already clamped to [0, n_groups]
+};
+
+struct StepTensors {
+  const float* q;
+  const uint8_t* l1k; const float* l1k_n; const uint8_t* l1v; const float* l1v_n;
+  const uint8_t* l2k; const float* l2k_n; const uint8_t* l2v; const float* l2v_n;
+  const uint8_t* l3; int l3_staged;
+  const uint32_t* k_signs; const uint32_t* v_signs;
+  const float* cb4; const float* cb3;
+  float scale, summary_bias;
+  int agg;
+  float* out;
+};
+
+// Workspace layout (all offsets 256-byte aligned).
+struct Workspace {
+  size_t qrot_off;     // fp32 [B*Hkv][G][d]  rotated, scaled queries (K rotation)
+  size_t scores_off;   // fp32 [B*Hkv][ng]    aggregated router scores
+  size_t idx_off;      // int32 [B*Hkv][beta] selection
+  size_t part_off;     // fp32 partials [B*Hkv][slots][G][d+2]
+  size_t cnt_off;      // uint32 [B*Hkv][2]  completion counters
+  size_t total;
+  int route_chunks;    // route work-groups per unit
+  int attn_slots;      // attention partial slots per unit
+  int sum_chunks;      // summary-attention work-groups per unit
+  int l1_chunks;
+  int fetch_chunks;
+};
+Workspace plan_workspace(const StepShape& s);
+
+// mode bits for the route/summary kernel
+enum { ROUTE_TOPK = 1, ROUTE_PARTIALS = 2 };
+
+hipError_t launch_qrot(const StepShape& s, const StepTensors& t, const Workspace& w,
+                       char* ws, hipStream_t st);
+hipError_t launch_route(const StepShape& s, const StepTensors& t, const Workspace& w, char* ws,
+                        int mode, const int32_t* given_idx, float* scores_out,
+                        int32_t* idx_out, hipStream_t st);
+hipError_t launch_attn(const StepShape& s, const StepTensors& t, const Workspace& w, char* ws,
+                       const int32_t* idx, hipStream_t st);
+hipError_t launch_gather(const uint8_t* src, size_t rec_bytes, int units, int n_groups,
+                         const int32_t* idx, int beta, uint8_t* dst, hipStream_t st);
+
+// ---- host-side method pieces (host.cpp) -------------------------------------
+int codebook(int d, int bits, float* centroids, float* thresholds);
+
+}  // namespace hsq

@@ -1,0 +1,311 @@
+"""Thin Python binding of libhsq (ctypes).  Argument marshalling only: every
+step of the path runs in the library's kernels; torch provides device memory
+and streams.  The names mirror the C ABI in include/hsq.h.
+"""
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhsq.so")
+
+HSQ_F32, HSQ_BF16 = 0, 1
+HSQ_AGG_MAX, HSQ_AGG_MEAN = 0, 1
+
+_c = ctypes
+_vp, _i, _i64, _f, _sz = _c.c_void_p, _c.c_int, _c.c_int64, _c.c_float, _c.c_size_t
+
+_SIGNATURES = {
+    "hsq_version": ([], _c.c_char_p),
+    "hsq_last_error": ([], _c.c_char_p),
+    "hsq_codebook": ([_i, _i, _vp, _vp], _i),
+    "hsq_tier_plan": ([_i, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp], _i),
+    "hsq_workspace_bytes": ([_i, _i, _i, _i, _i, _i, _i, _i], _sz),
+    "hsq_encode": ([_vp, _i, _i64, _i, _i, _vp, _i, _vp, _i64, _i, _vp, _vp, _vp, _vp], _i),
+    "hsq_decode": ([_vp, _vp, _i64, _i, _i, _vp, _i64, _i, _vp, _vp, _i, _vp], _i),
+    "hsq_build_tiers": ([_vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _vp, _i, _i, _vp, _vp, _vp, _vp,
+                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i),
+    "hsq_route_topk": ([_vp, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp, _f, _i, _i, _vp, _vp, _vp,
+                        _sz, _vp], _i),
+    "hsq_decode_attn": ([_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i,
+                         _vp, _i, _i, _vp, _i, _vp, _vp, _vp, _vp, _f, _f, _vp, _sz, _vp, _vp],
+                        _i),
+    "hsq_decode_step": ([_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i,
+                         _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _f, _vp, _vp, _sz, _vp, _vp],
+                        _i),
+    "hsq_gather_l3": ([_vp, _sz, _i, _i, _i, _vp, _i, _vp, _vp], _i),
+}
+
+_lib = None
+
+
+class HSQError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"libhsq error {code}: {msg}")
+        self.code = code
+
+
+def lib():
+    """Load libhsq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing; build it with "
+                "`python -m compressed_decode_attention_turboquant_amd.build`")
+        lb = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(lb, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = lb
+    return _lib
+
+
+def exported_symbols():
+    return sorted(_SIGNATURES)
+
+
+def _check(rc):
+    if rc != 0:
+        raise HSQError(rc, lib().hsq_last_error().decode())
+
+
+def _dev(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return HSQ_F32
+    if t.dtype == torch.bfloat16:
+        return HSQ_BF16
+    raise TypeError("only float32 and bfloat16 are supported")
+
+
+# ------------------------------------------------------------------ host ----
+
+def codebook(d, bits):
+    """(centroids fp32 [2^bits], thresholds fp32 [2^bits-1]) from the library."""
+    c = np.zeros(1 << bits, dtype=np.float32)
+    t = np.zeros((1 << bits) - 1, dtype=np.float32)
+    _check(lib().hsq_codebook(d, bits, c.ctypes.data, t.ctypes.data))
+    return c, t
+
+
+def tier_plan(T, n_sink, n_recent, marked, group_n):
+    """(l1 positions int32 [n1], group positions int32 [ng, group_n])."""
+    m = np.ascontiguousarray(np.asarray(marked, dtype=np.int32).reshape(-1))
+    l1 = np.zeros(T, dtype=np.int32)
+    gp = np.zeros(T, dtype=np.int32)
+    n1 = ctypes.c_int(0)
+    ng = ctypes.c_int(0)
+    _check(lib().hsq_tier_plan(T, n_sink, n_recent, m.ctypes.data if m.size else None, m.size,
+                               group_n, l1.ctypes.data, ctypes.byref(n1), gp.ctypes.data,
+                               ctypes.byref(ng)))
+    return l1[: n1.value].copy(), gp[: ng.value * group_n].reshape(ng.value, group_n).copy()
+
+
+def workspace_bytes(B, Hq, Hkv, d, n_l1, n_groups, beta, group_n):
+    return int(lib().hsq_workspace_bytes(B, Hq, Hkv, d, n_l1, n_groups, beta, group_n))
+
+
+# ---------------------------------------------------------------- device ----
+
+def encode(x, bits, signs, thresholds, vecs_per_rot=None, n_rot=1, row_idx=None, group_n=1,
+           n_vec=None):
+    """Encode rows of x ([rows, d] fp32/bf16).  Returns (codes u8 [n, bits*d/8], norms f32 [n])."""
+    d = x.shape[-1]
+    if n_vec is None:
+        n_vec = (row_idx.numel() if row_idx is not None else x.numel() // d) // group_n
+    if vecs_per_rot is None:
+        vecs_per_rot = max(n_vec, 1)
+    codes = torch.empty((n_vec, bits * d // 8), dtype=torch.uint8, device=x.device)
+    norms = torch.empty((n_vec,), dtype=torch.float32, device=x.device)
+    _check(lib().hsq_encode(_dev(x, name="x"), _dtype_code(x), n_vec, d, bits,
+                            _dev(row_idx, torch.int64, "row_idx"), group_n,
+                            _dev(signs, torch.int32, "signs"), vecs_per_rot, n_rot,
+                            _dev(thresholds, torch.float32, "thresholds"), _dev(codes),
+                            _dev(norms), _stream()))
+    return codes, norms
+
+
+def decode(codes, norms, bits, d, signs, centroids, vecs_per_rot=None, n_rot=1,
+           out_dtype=torch.float32):
+    n_vec = norms.numel()
+    if vecs_per_rot is None:
+        vecs_per_rot = max(n_vec, 1)
+    out = torch.empty((n_vec, d), dtype=out_dtype, device=codes.device)
+    _check(lib().hsq_decode(_dev(codes, torch.uint8, "codes"), _dev(norms, torch.float32, "norms"),
+                            n_vec, d, bits, _dev(signs, torch.int32, "signs"), vecs_per_rot,
+                            n_rot, _dev(centroids, torch.float32, "centroids"), _dev(out),
+                            _dtype_code(out), _stream()))
+    return out
+
+
+@dataclass
+class Tiers:
+    """Device tiers of one layer (layouts as in include/hsq.h)."""
+    B: int
+    Hkv: int
+    d: int
+    n1: int
+    ng: int
+    group_n: int
+    l1k: torch.Tensor
+    l1k_n: torch.Tensor
+    l1v: torch.Tensor
+    l1v_n: torch.Tensor
+    l2k: torch.Tensor
+    l2k_n: torch.Tensor
+    l2v: torch.Tensor
+    l2v_n: torch.Tensor
+    l3: torch.Tensor
+
+    @property
+    def rec_bytes(self):
+        return self.group_n * (self.d + 8)
+
+    def nbytes(self):
+        return sum(t.numel() * t.element_size() for t in
+                   (self.l1k, self.l1k_n, self.l1v, self.l1v_n, self.l2k, self.l2k_n,
+                    self.l2v, self.l2v_n, self.l3))
+
+
+def alloc_tiers(B, Hkv, d, n1, ng, group_n, device, l3=None):
+    e = lambda *s, dt=torch.uint8: torch.empty(s, dtype=dt, device=device)
+    f = torch.float32
+    if l3 is None:
+        l3 = e(B, Hkv, ng, group_n * (d + 8))
+    return Tiers(B, Hkv, d, n1, ng, group_n,
+                 e(B, Hkv, n1, d // 2), e(B, Hkv, n1, dt=f), e(B, Hkv, n1, d // 2),
+                 e(B, Hkv, n1, dt=f),
+                 e(B, Hkv, ng, 3 * d // 8), e(B, Hkv, ng, dt=f), e(B, Hkv, ng, 3 * d // 8),
+                 e(B, Hkv, ng, dt=f), l3)
+
+
+def build_tiers(k, v, l1_pos, group_pos, group_n, k_signs, v_signs, thr4, thr3, l3=None):
+    """Build L1/L2/L3 of one layer from raw k, v [B, Hkv, T, d].
+
+    l1_pos int32 [B, n1], group_pos int32 [B, ng*group_n] (device).  l3 may be
+    a caller-provided device-visible buffer (e.g. the alias of pinned host memory).
+    """
+    B, Hkv, T, d = k.shape
+    n1 = l1_pos.shape[1]
+    ng = group_pos.shape[1] // group_n
+    t = alloc_tiers(B, Hkv, d, n1, ng, group_n, k.device, l3)
+    _check(lib().hsq_build_tiers(
+        _dev(k, name="k"), _dev(v, name="v"), _dtype_code(k), B, Hkv, T, d,
+        _dev(l1_pos, torch.int32, "l1_pos"), n1, _dev(group_pos, torch.int32, "group_pos"), ng,
+        group_n, _dev(k_signs, torch.int32, "k_signs"), _dev(v_signs, torch.int32, "v_signs"),
+        _dev(thr4, torch.float32, "thr4"), _dev(thr3, torch.float32, "thr3"),
+        t.l1k.data_ptr(), t.l1k_n.data_ptr(), t.l1v.data_ptr(), t.l1v_n.data_ptr(),
+        t.l2k.data_ptr(), t.l2k_n.data_ptr(), t.l2v.data_ptr(), t.l2v_n.data_ptr(),
+        t.l3.data_ptr(), _stream()))
+    return t
+
+
+class Workspace:
+    """Device workspace for the decode-step calls.  Zero-filled once at
+    creation; the calls leave their completion counters at zero again."""
+
+    def __init__(self, nbytes, device):
+        self.nbytes = int(nbytes)
+        self.buf = torch.zeros(self.nbytes + 256, dtype=torch.uint8, device=device)
+        off = (-self.buf.data_ptr()) % 256
+        self.ptr = self.buf.data_ptr() + off
+
+
+def make_workspace(B, Hq, Hkv, d, n_l1, n_groups, beta, group_n, device):
+    n = workspace_bytes(B, Hq, Hkv, d, n_l1, n_groups, beta, group_n)
+    if n == 0:
+        raise HSQError(-1, "invalid sizes for hsq_workspace_bytes")
+    return Workspace(n, device)
+
+
+def route_topk(q, tiers, k_signs, cb3, beta, scale=None, agg=HSQ_AGG_MAX, ws=None,
+               want_scores=False):
+    B, Hq, d = q.shape
+    Hkv, ng = tiers.Hkv, tiers.ng
+    b = min(beta, ng)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if ws is None:
+        ws = make_workspace(B, Hq, Hkv, d, 0, ng, b, tiers.group_n, q.device)
+    idx = torch.empty((B, Hkv, b), dtype=torch.int32, device=q.device)
+    scores = torch.empty((B, Hkv, ng), dtype=torch.float32, device=q.device) if want_scores else None
+    _check(lib().hsq_route_topk(
+        _dev(q, torch.float32, "q"), B, Hq, Hkv, d, _dev(tiers.l2k), _dev(tiers.l2k_n), ng,
+        _dev(k_signs, torch.int32, "k_signs"), _dev(cb3, torch.float32, "cb3"), scale, agg,
+        beta, idx.data_ptr() if b > 0 else None, _dev(scores), ws.ptr, ws.nbytes, _stream()))
+    return idx, scores
+
+
+def decode_attn(q, tiers, idx, k_signs, v_signs, cb4, cb3, scale=None, summary_bias=0.0,
+                ws=None, l3=None, l3_staged=False):
+    B, Hq, d = q.shape
+    beta = idx.shape[-1] if idx is not None else 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if ws is None:
+        ws = make_workspace(B, Hq, tiers.Hkv, d, tiers.n1, tiers.ng, beta, tiers.group_n,
+                            q.device)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    l3p = l3 if l3 is not None else tiers.l3.data_ptr()
+    _check(lib().hsq_decode_attn(
+        _dev(q, torch.float32, "q"), B, Hq, tiers.Hkv, d, _dev(tiers.l1k), _dev(tiers.l1k_n),
+        _dev(tiers.l1v), _dev(tiers.l1v_n), tiers.n1, _dev(tiers.l2k), _dev(tiers.l2k_n),
+        _dev(tiers.l2v), _dev(tiers.l2v_n), tiers.ng, l3p, tiers.group_n, int(l3_staged),
+        _dev(idx, torch.int32, "idx") if beta > 0 else None, beta,
+        _dev(k_signs, torch.int32, "k_signs"), _dev(v_signs, torch.int32, "v_signs"),
+        _dev(cb4, torch.float32, "cb4"), _dev(cb3, torch.float32, "cb3"), scale, summary_bias,
+        ws.ptr, ws.nbytes, out.data_ptr(), _stream()))
+    return out
+
+
+def decode_step(q, tiers, beta, k_signs, v_signs, cb4, cb3, scale=None, summary_bias=0.0,
+                agg=HSQ_AGG_MAX, ws=None, out=None, idx=None, l3=None):
+    """Route + top-beta + attention for one layer.  Returns (out, idx)."""
+    B, Hq, d = q.shape
+    b = min(beta, tiers.ng)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if ws is None:
+        ws = make_workspace(B, Hq, tiers.Hkv, d, tiers.n1, tiers.ng, b, tiers.group_n, q.device)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if idx is None and b > 0:
+        idx = torch.empty((B, tiers.Hkv, b), dtype=torch.int32, device=q.device)
+    l3p = l3 if l3 is not None else tiers.l3.data_ptr()
+    _check(lib().hsq_decode_step(
+        _dev(q, torch.float32, "q"), B, Hq, tiers.Hkv, d, _dev(tiers.l1k), _dev(tiers.l1k_n),
+        _dev(tiers.l1v), _dev(tiers.l1v_n), tiers.n1, _dev(tiers.l2k), _dev(tiers.l2k_n),
+        _dev(tiers.l2v), _dev(tiers.l2v_n), tiers.ng, l3p, tiers.group_n, beta, agg,
+        _dev(k_signs, torch.int32, "k_signs"), _dev(v_signs, torch.int32, "v_signs"),
+        _dev(cb4, torch.float32, "cb4"), _dev(cb3, torch.float32, "cb3"), scale, summary_bias,
+        idx.data_ptr() if idx is not None else None, ws.ptr, ws.nbytes, out.data_ptr(),
+        _stream()))
+    return out, idx
+
+
+def gather_l3(l3_src_ptr, rec_bytes, B, Hkv, ng, idx, staging):
+    beta = idx.shape[-1]
+    _check(lib().hsq_gather_l3(l3_src_ptr, rec_bytes, B, Hkv, ng, _dev(idx, torch.int32, "idx"),
+                               beta, _dev(staging, torch.uint8, "staging"), _stream()))
+    return staging

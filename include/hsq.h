@@ -1,0 +1,246 @@
+/*
+ * hsq.h -- C ABI of libhsq: the HSQ decode step and its TurboQuant codec on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Method sources (web pages):
+ *  [HSQ]  "Tamarin (HSQ) - reversible hierarchical KV-cache compression",
+ *         technical summary, section 2 "Methodology": "Three-tier
+ *         architecture", "Decode process", "Key technical components".
+ *  [ABL]  "Ablation, Statistical Inference, and Validation for KV-Cache
+ *         Compression", technical summary, "Experimental setup" (TurboQuant =
+ *         random Walsh-Hadamard transform + data-oblivious Beta Lloyd-Max
+ *         codebook).
+ *
+ * Conventions shared by every call
+ *  - Return value: HSQ_OK (0) or a negative HSQ_ERR_* code.  Arguments are
+ *    validated on the host before anything is launched; an argument error
+ *    launches nothing.  hsq_last_error() returns a thread-local message for
+ *    the last failing call on the calling thread.
+ *  - Device calls are asynchronous on `stream` (a hipStream_t passed as
+ *    void*; NULL = the null stream).  They never allocate, never free and
+ *    never synchronise the host.  The caller owns every buffer and keeps it
+ *    alive until the stream work completes.  Pointers are device pointers
+ *    (hipMalloc'd, or the device alias of pinned mapped host memory where a
+ *    call says "device-visible").
+ *  - Shapes: d (head dim) in {64, 128}; 4-bit and 3-bit codes; group size
+ *    N in {8, 16}; Hq % Hkv == 0 with G = Hq / Hkv in 1..8.  Query head h
+ *    belongs to kv-head h / G.
+ *  - Rotation: R = H_d D / sqrt(d).  D = diag(+-1) from a sign mask of d/32
+ *    uint32 words, bit i of word i/32 set meaning coordinate i is negated;
+ *    H_d is the Sylvester Hadamard matrix, H_ij = (-1)^popcount(i & j).
+ *    One mask per (layer, kv-head, K|V) [HSQ, quantisation item: fixed random
+ *    orthonormal rotation; ABL: random Walsh-Hadamard transform].
+ *  - Vector record: r = ||x||_2 as fp32 plus codes of y = R x / r,
+ *    code_i = #{j : t_j < y_i} against the ascending fp32 thresholds.
+ *    4-bit packing: byte k = code[2k] | code[2k+1] << 4 (d/2 bytes).
+ *    3-bit packing: LSB-first bit stream, code i in bits [3i, 3i+3)
+ *    (3d/8 bytes).  Dequantisation: x_hat = r R^T c[code].
+ *  - Tier layouts (unit u = b * Hkv + kvh):
+ *      L1  codes [B][Hkv][n1][d/2] u8, norms [B][Hkv][n1] f32   (4-bit)
+ *      L2  codes [B][Hkv][ng][3d/8] u8, norms [B][Hkv][ng] f32  (3-bit)
+ *      L3  records [B][Hkv][ng], one record per group of N tokens:
+ *          [K codes N*d/2][K norms N*4][V codes N*d/2][V norms N*4] bytes,
+ *          i.e. N*(d+8) bytes.
+ *    L1 and L2 have separate K and V arrays.
+ */
+#ifndef HSQ_H
+#define HSQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  HSQ_OK = 0,
+  HSQ_ERR_ARG = -1,         /* invalid argument (null pointer, bad size) */
+  HSQ_ERR_UNSUPPORTED = -2, /* valid but unsupported shape (d, bits, N, G) */
+  HSQ_ERR_HIP = -3,         /* a HIP runtime call or launch failed */
+  HSQ_ERR_WORKSPACE = -4    /* workspace missing or smaller than required */
+};
+
+enum { HSQ_F32 = 0, HSQ_BF16 = 1 };
+enum { HSQ_AGG_MAX = 0, HSQ_AGG_MEAN = 1 };
+
+/* Library version string (static storage). */
+const char* hsq_version(void);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* hsq_last_error(void);
+
+/* ---------------------------------------------------------------- host ---- */
+
+/*
+ * hsq_codebook -- Beta Lloyd-Max codebook for (d, bits) [ABL, "Experimental
+ * setup": data-oblivious Beta Lloyd-Max codebook].  The quantised variable
+ * is one coordinate of a uniformly random unit vector in R^d, density
+ * proportional to (1 - y^2)^((d-3)/2) on [-1, 1].  Computed on the host in
+ * double precision by Lloyd iteration to its fixed point (centroid =
+ * conditional mean of its cell, threshold = midpoint of neighbouring
+ * centroids), made exactly odd-symmetric, rounded to fp32.
+ *   d           3..4096 (any integer; the codec itself needs d in {64,128})
+ *   bits        1..4
+ *   centroids   host out, [2^bits] ascending
+ *   thresholds  host out, [2^bits - 1] ascending (middle one exactly 0)
+ * Errors: HSQ_ERR_ARG for null pointers or d/bits out of range.
+ */
+int hsq_codebook(int d, int bits, float* centroids, float* thresholds);
+
+/*
+ * hsq_tier_plan -- split the T positions of one sequence into L1 and groups
+ * [HSQ, "Three-tier architecture": L1 = attention sinks + recent window +
+ * reader-marked tokens; the rest in groups of N].  L1 = positions
+ * [0, n_sink) + [T - n_recent, T) + marked + the trailing remainder of fewer
+ * than N non-L1 positions, ascending.  Groups = the other positions in
+ * ascending order, cut into consecutive runs of N.
+ *   marked      host in, [n_marked] positions in [0, T) (duplicates allowed)
+ *   l1_pos      host out [T] capacity, or NULL to query only n1
+ *   group_pos   host out [T] capacity, or NULL; group g = entries
+ *               [g*N, (g+1)*N)
+ *   n1, n_groups  host out
+ * Errors: HSQ_ERR_ARG for T < 1, negative counts, N < 1, marks out of range.
+ */
+int hsq_tier_plan(int T, int n_sink, int n_recent, const int32_t* marked, int n_marked,
+                  int group_n, int32_t* l1_pos, int* n1, int32_t* group_pos, int* n_groups);
+
+/*
+ * hsq_workspace_bytes -- device workspace needed by hsq_route_topk,
+ * hsq_decode_attn and hsq_decode_step for these sizes (one number covers
+ * all three).  Returns 0 on invalid sizes.
+ */
+size_t hsq_workspace_bytes(int B, int Hq, int Hkv, int d, int n_l1, int n_groups, int beta,
+                           int group_n);
+
+/* -------------------------------------------------------------- device ---- */
+
+/*
+ * hsq_encode -- TurboQuant encode of n_vec vectors [HSQ quantisation item;
+ * ABL "Experimental setup"]: norm, sign flip, Walsh-Hadamard transform,
+ * threshold count, bit packing.
+ *   x           [rows][d] in x_dtype (HSQ_F32 or HSQ_BF16)
+ *   row_idx     NULL: vector i reads rows [i*group_n, (i+1)*group_n);
+ *               else int64 [n_vec*group_n] row numbers
+ *   group_n     1 = encode each row; N > 1 = encode the mean of N rows
+ *   signs       uint32 [n_rot][d/32]; vector i uses mask
+ *               (i / vecs_per_rot) % n_rot
+ *   thresholds  fp32 [2^bits - 1] ascending (device)
+ *   codes       out [n_vec][bits*d/8]
+ *   norms       out [n_vec] fp32
+ * Errors: HSQ_ERR_ARG (null, n_vec < 0, vecs_per_rot < 1, n_rot < 1,
+ * group_n < 1), HSQ_ERR_UNSUPPORTED (d, bits, dtype), HSQ_ERR_HIP.
+ * n_vec == 0 is a no-op.
+ */
+int hsq_encode(const void* x, int x_dtype, int64_t n_vec, int d, int bits,
+               const int64_t* row_idx, int group_n, const uint32_t* signs,
+               int64_t vecs_per_rot, int n_rot, const float* thresholds, uint8_t* codes,
+               float* norms, void* stream);
+
+/*
+ * hsq_decode -- dequantise n_vec vectors: x_hat = r R^T c[code]
+ * [HSQ "Decode process" step 2: dequantise and rotate back].
+ *   codes/norms as written by hsq_encode; centroids fp32 [2^bits] (device);
+ *   out [n_vec][d] in out_dtype (HSQ_F32 or HSQ_BF16).
+ * Errors as hsq_encode.
+ */
+int hsq_decode(const uint8_t* codes, const float* norms, int64_t n_vec, int d, int bits,
+               const uint32_t* signs, int64_t vecs_per_rot, int n_rot, const float* centroids,
+               void* out, int out_dtype, void* stream);
+
+/*
+ * hsq_build_tiers -- build L1, L2 and L3 of one layer from raw K and V
+ * [HSQ "Three-tier architecture"; L2 summary = 3-bit code of the mean of the
+ * group's raw vectors, standing in for the trained compressor].
+ *   k, v        [B][Hkv][T][d] in dtype
+ *   l1_pos      int32 [B][n1] positions (device), as hsq_tier_plan gives
+ *   group_pos   int32 [B][n_groups*group_n] positions (device)
+ *   k_signs, v_signs  uint32 [Hkv][d/32]
+ *   thr4, thr3  fp32 thresholds for 4 and 3 bits (device)
+ *   outputs     tier arrays in the layouts above
+ * n1 == 0 or n_groups == 0 skip the matching tiers.
+ */
+int hsq_build_tiers(const void* k, const void* v, int dtype, int B, int Hkv, int T, int d,
+                    const int32_t* l1_pos, int n1, const int32_t* group_pos, int n_groups,
+                    int group_n, const uint32_t* k_signs, const uint32_t* v_signs,
+                    const float* thr4, const float* thr3, uint8_t* l1k, float* l1k_n,
+                    uint8_t* l1v, float* l1v_n, uint8_t* l2k, float* l2k_n, uint8_t* l2v,
+                    float* l2v_n, uint8_t* l3, void* stream);
+
+/*
+ * hsq_route_topk -- router + top-beta [HSQ "Decode process" steps 1-2].
+ * For every unit (b, kvh) and group g: s_g = agg over the G query heads h of
+ * kvh of scale * q_h . k_hat_g, with k_hat_g the dequantised 3-bit summary
+ * key; then the beta largest s_g, ties to the lower g, written ascending.
+ *   q           fp32 [B][Hq][d]
+ *   l2k/l2k_n   3-bit summary keys / norms
+ *   k_signs     uint32 [Hkv][d/32];  cb3 fp32 [8] centroids (device)
+ *   agg         HSQ_AGG_MAX or HSQ_AGG_MEAN
+ *   beta        >= 0, clamped to n_groups
+ *   topk_idx    out int32 [B][Hkv][min(beta, n_groups)]
+ *   scores      optional out fp32 [B][Hkv][n_groups] (NULL = not written)
+ *   workspace   device, >= hsq_workspace_bytes(...) bytes
+ */
+int hsq_route_topk(const float* q, int B, int Hq, int Hkv, int d, const uint8_t* l2k,
+                   const float* l2k_n, int n_groups, const uint32_t* k_signs, const float* cb3,
+                   float scale, int agg, int beta, int32_t* topk_idx, float* scores,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * hsq_decode_attn -- fused union-set attention given the fetched groups
+ * [HSQ "Decode process" step 3].  For query head h of unit (b, kvh):
+ *   out = sum_e softmax_e(scale * q_h . k_e + bias_e) v_e
+ * over e in L1 tokens, summaries of groups NOT in topk_idx (bias =
+ * summary_bias) and the N tokens of every group in topk_idx (dequantised
+ * 4-bit originals).  Summaries of fetched groups are excluded.
+ *   topk_idx    int32 [B][Hkv][beta] distinct group ids in [0, n_groups)
+ *   l3          device-visible L3 base.  l3_staged == 0: records
+ *               [B][Hkv][n_groups] (HBM-resident, or the device alias of a
+ *               pinned mapped host archive); l3_staged == 1: records
+ *               [B][Hkv][beta] in topk_idx order (hsq_gather_l3 output)
+ *   cb4, cb3    fp32 centroids [16], [8] (device)
+ *   out         fp32 [B][Hq][d]; a unit with no entries at all gets zeros
+ */
+int hsq_decode_attn(const float* q, int B, int Hq, int Hkv, int d, const uint8_t* l1k,
+                    const float* l1k_n, const uint8_t* l1v, const float* l1v_n, int n_l1,
+                    const uint8_t* l2k, const float* l2k_n, const uint8_t* l2v,
+                    const float* l2v_n, int n_groups, const uint8_t* l3, int group_n,
+                    int l3_staged, const int32_t* topk_idx, int beta, const uint32_t* k_signs,
+                    const uint32_t* v_signs, const float* cb4, const float* cb3, float scale,
+                    float summary_bias, void* workspace, size_t ws_bytes, float* out,
+                    void* stream);
+
+/*
+ * hsq_decode_step -- the whole decode step of one layer: route, top-beta and
+ * attention [HSQ "Decode process" steps 1-3], as hsq_route_topk followed by
+ * hsq_decode_attn with l3_staged == 0, in two launches.
+ *   topk_idx    optional out int32 [B][Hkv][min(beta, n_groups)] (NULL = not
+ *               returned; the selection then lives in the workspace)
+ *   other arguments as in hsq_route_topk / hsq_decode_attn
+ */
+int hsq_decode_step(const float* q, int B, int Hq, int Hkv, int d, const uint8_t* l1k,
+                    const float* l1k_n, const uint8_t* l1v, const float* l1v_n, int n_l1,
+                    const uint8_t* l2k, const float* l2k_n, const uint8_t* l2v,
+                    const float* l2v_n, int n_groups, const uint8_t* l3, int group_n, int beta,
+                    int agg, const uint32_t* k_signs, const uint32_t* v_signs, const float* cb4,
+                    const float* cb3, float scale, float summary_bias, int32_t* topk_idx,
+                    void* workspace, size_t ws_bytes, float* out, void* stream);
+
+/*
+ * hsq_gather_l3 -- copy the fetched L3 records into a staging buffer
+ * [HSQ "Decode process" step 2: fetch the originals of the chosen groups
+ * from the CPU archive].  Reads device-visible `l3_src` (typically the
+ * device alias of pinned mapped host memory, so the copy crosses PCIe with
+ * indices that never leave the device) and writes
+ * staging[u][i] = l3_src[u][topk_idx[u][i]] for units u < B*Hkv, i < beta.
+ *   rec_bytes   bytes per record, N*(d+8); must be a multiple of 16
+ * Errors: HSQ_ERR_ARG (null, sizes), HSQ_ERR_HIP.
+ */
+int hsq_gather_l3(const uint8_t* l3_src, size_t rec_bytes, int B, int Hkv, int n_groups,
+                  const int32_t* topk_idx, int beta, uint8_t* staging, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSQ_H */

@@ -1,0 +1,95 @@
+"""Host-side tests of libhsq: it loads, exports every declared symbol, its host
+functions agree with the oracle, and argument errors are reported before any
+launch (none of these calls touches a GPU)."""
+import ctypes
+import re
+import os
+
+import numpy as np
+import pytest
+
+from compressed_decode_attention_turboquant_amd import hsq
+from oracle import codebook as ocb
+from oracle import tiers as otiers
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_symbols():
+    src = open(os.path.join(ROOT, "include", "hsq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hsq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = hsq.lib()
+    declared = header_symbols()
+    assert declared == hsq.exported_symbols()
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.hsq_version().decode().startswith("hsq")
+
+
+@pytest.mark.parametrize("d,bits", [(64, 3), (64, 4), (128, 3), (128, 4), (16, 2), (3, 3), (256, 4)])
+def test_codebook_matches_oracle(d, bits):
+    c, t = hsq.codebook(d, bits)
+    oc, ot = ocb.codebook_f32(d, bits)
+    # two independent double-precision generators, rounded to fp32: equal up to
+    # one fp32 ulp (a value sitting on a rounding boundary may round either way)
+    np.testing.assert_array_max_ulp(c, oc, maxulp=1)
+    np.testing.assert_array_max_ulp(t, ot, maxulp=1)
+    assert t[len(t) // 2] == 0.0
+    np.testing.assert_array_equal(c, -c[::-1])
+
+
+def test_codebook_tables_for_the_codec_are_identical():
+    for d in (64, 128):
+        for bits in (3, 4):
+            c, t = hsq.codebook(d, bits)
+            oc, ot = ocb.codebook_f32(d, bits)
+            np.testing.assert_array_equal(c, oc)
+            np.testing.assert_array_equal(t, ot)
+
+
+@pytest.mark.parametrize("T,ns,nr,nm,gn", [(512, 4, 32, 16, 8), (8192, 4, 64, 164, 16),
+                                           (300, 4, 64, 7, 16), (50, 4, 64, 0, 8), (1, 4, 0, 0, 8),
+                                           (1000, 0, 0, 0, 8)])
+def test_tier_plan_matches_oracle(T, ns, nr, nm, gn):
+    rng = np.random.default_rng(T + nm)
+    lo, hi = ns, max(T - nr, ns)
+    marked = np.sort(rng.choice(np.arange(lo, hi), size=min(nm, max(hi - lo, 0)), replace=False))
+    l1, groups = hsq.tier_plan(T, ns, nr, marked, gn)
+    ol1, og = otiers.tier_plan(T, ns, nr, marked, gn)
+    np.testing.assert_array_equal(l1, ol1)
+    np.testing.assert_array_equal(groups, og)
+
+
+def test_argument_errors_are_reported_without_launch():
+    lib = hsq.lib()
+    c = np.zeros(16, np.float32)
+    assert lib.hsq_codebook(2, 4, c.ctypes.data, c.ctypes.data) == -1
+    assert lib.hsq_codebook(64, 5, c.ctypes.data, c.ctypes.data) == -1
+    assert lib.hsq_codebook(64, 4, None, c.ctypes.data) == -1
+    assert "null" in lib.hsq_last_error().decode()
+    # encode: unsupported d / bits / dtype, null pointers, bad sizes
+    p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    assert lib.hsq_encode(p, 0, 10, 96, 4, None, 1, p, 1, 1, p, p, p, None) == -2
+    assert lib.hsq_encode(p, 0, 10, 128, 2, None, 1, p, 1, 1, p, p, p, None) == -2
+    assert lib.hsq_encode(p, 7, 10, 128, 4, None, 1, p, 1, 1, p, p, p, None) == -2
+    assert lib.hsq_encode(None, 0, 10, 128, 4, None, 1, p, 1, 1, p, p, p, None) == -1
+    assert lib.hsq_encode(p, 0, -1, 128, 4, None, 1, p, 1, 1, p, p, p, None) == -1
+    assert lib.hsq_encode(p, 0, 10, 128, 4, None, 0, p, 1, 1, p, p, p, None) == -1
+    assert lib.hsq_encode(None, 0, 0, 128, 4, None, 1, None, 1, 1, None, None, None, None) == 0
+    # decode-step shapes: Hq % Hkv, G > 8, group size, beta < 0, workspace
+    assert lib.hsq_workspace_bytes(1, 10, 4, 128, 10, 10, 2, 16) == 0
+    assert lib.hsq_workspace_bytes(1, 36, 4, 128, 10, 10, 2, 16) == 0
+    assert lib.hsq_workspace_bytes(1, 32, 8, 128, 10, 10, 2, 12) == 0
+    assert lib.hsq_workspace_bytes(1, 32, 8, 128, 10, 10, -1, 16) == 0
+    assert lib.hsq_workspace_bytes(1, 32, 8, 128, 10, 10, 2, 16) > 0
+    assert lib.hsq_route_topk(p, 1, 32, 8, 128, p, p, 10, p, p, ctypes.c_float(0.1), 0, 2, p,
+                              None, None, 0, None) == -4
+    assert lib.hsq_route_topk(p, 1, 32, 8, 128, p, p, 10, p, p, ctypes.c_float(0.1), 9, 2, p,
+                              None, None, 0, None) == -1
+    assert lib.hsq_gather_l3(p, 100, 1, 1, 4, p, 2, p, None) == -1
+    assert lib.hsq_gather_l3(p, 1088, 1, 1, 4, p, 5, p, None) == -1
+    assert lib.hsq_tier_plan(10, 1, 1, None, 3, 8, None, None, None, None) == -1

@@ -1,0 +1,220 @@
+"""GPU parity of the HSQ decode step (hsq_route_topk, hsq_decode_attn,
+hsq_decode_step) against the fp64 oracle.
+
+Page: "Tamarin (HSQ)" summary, section 2, "Decode process" (routing over the
+L2 summary keys, top-beta fetch from L3, attention over L1 + unfetched
+summaries + fetched originals with the fetched summaries masked).
+
+Rules (spec tolerances): selected sets equal the oracle's except for
+groups whose oracle score is within 1e-5 of the beta-th score; attention within
+2e-3 relative L2 per unit, with the oracle fed the GPU's selection so that a
+legitimate near-tie swap cannot fail the attention check.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from compressed_decode_attention_turboquant_amd import hsq
+from compressed_decode_attention_turboquant_amd import workloads as W
+from oracle import codebook as ocb
+from oracle import decode as odec
+from oracle import tiers as otiers
+from tests.gpu_util import ATTN_REL_L2, TIE_BAND, rel_l2, signs_to_dev
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+class Scenario:
+    """One layer of a workload: raw inputs, GPU tiers and codebooks."""
+
+    def __init__(self, w, layer=0):
+        self.w = w
+        self.k, self.v = W.kv(w, layer, DEV)
+        self.q = W.query(w, layer, DEV)
+        self.ks, self.vs = W.signs(w.seed, layer, w.hkv, w.d)
+        self.plans = [hsq.tier_plan(w.T, w.n_sink, w.n_recent, W.marked(w, b), w.group_n)
+                      for b in range(w.batch)]
+        l1 = torch.from_numpy(np.stack([p[0] for p in self.plans])).to(DEV)
+        gp = torch.from_numpy(np.stack([p[1].reshape(-1) for p in self.plans])).to(DEV)
+        self.c4 = ocb.codebook_f32(w.d, 4)
+        self.c3 = ocb.codebook_f32(w.d, 3)
+        self.cb4 = torch.from_numpy(np.array(self.c4[0])).to(DEV)
+        self.cb3 = torch.from_numpy(np.array(self.c3[0])).to(DEV)
+        self.dks, self.dvs = signs_to_dev(self.ks), signs_to_dev(self.vs)
+        self.tiers = hsq.build_tiers(self.k, self.v, l1, gp, w.group_n, self.dks, self.dvs,
+                                     torch.from_numpy(np.array(self.c4[1])).to(DEV),
+                                     torch.from_numpy(np.array(self.c3[1])).to(DEV))
+        self.scale = 1.0 / math.sqrt(w.d)
+        self._units = {}
+
+    def oracle_unit(self, b, h):
+        """Oracle tiers + dequantised tiers of unit (b, h), cached."""
+        key = (b, h)
+        if key not in self._units:
+            w = self.w
+            l1, g = otiers.tier_plan(w.T, w.n_sink, w.n_recent, W.marked(w, b), w.group_n)
+            unit = otiers.build_unit(self.k[b, h].cpu(), self.v[b, h].cpu(), l1, g, self.ks[h],
+                                     self.vs[h], self.c4, self.c3)
+            deq = odec.dequant_unit(unit, w.d, w.group_n, self.ks[h], self.vs[h], self.c4, self.c3)
+            self._units[key] = (unit, deq)
+        return self._units[key]
+
+    def q_unit(self, b, h):
+        G = self.w.G
+        return self.q[b, h * G:(h + 1) * G].double().cpu().numpy()
+
+
+def check_route(sc, idx, scores, units, beta, agg="max"):
+    """GPU selection vs oracle under the near-tie rule; GPU scores vs oracle."""
+    ng = sc.tiers.ng
+    b_eff = min(beta, ng)
+    worst = 0.0
+    for (b, h) in units:
+        unit, deq = sc.oracle_unit(b, h)
+        os_, _ = odec.route_scores(sc.q_unit(b, h), deq["l2k"], sc.scale, agg)
+        osel = odec.top_beta(os_, beta)
+        gsel = idx[b, h].cpu().numpy()
+        assert gsel.shape[0] == b_eff
+        assert np.all(np.diff(gsel) > 0), "selection must be ascending and distinct"
+        if b_eff == 0:
+            continue
+        kth = np.sort(os_)[::-1][b_eff - 1]
+        diff = set(gsel.tolist()) ^ set(osel.tolist())
+        for g in diff:
+            assert abs(os_[g] - kth) < TIE_BAND, (
+                f"unit {(b, h)}: group {g} differs, score {os_[g]:.8f} vs beta-th {kth:.8f}")
+        if scores is not None:
+            worst = max(worst, float(np.max(np.abs(scores[b, h].cpu().numpy() - os_))))
+    if scores is not None:
+        assert worst < 2e-6, f"router scores differ by {worst:.3e}"
+    return worst
+
+
+def check_attn(sc, out, idx, units, summary_bias=0.0):
+    """GPU attention vs oracle attention fed the GPU's selection."""
+    w = sc.w
+    worst = 0.0
+    for (b, h) in units:
+        unit, deq = sc.oracle_unit(b, h)
+        sel = idx[b, h].cpu().numpy() if idx is not None else np.zeros(0, dtype=np.int64)
+        want = odec.hsq_attention_unit(sc.q_unit(b, h), deq, unit["l3"], sel, w.group_n, w.d,
+                                       sc.ks[h], sc.vs[h], sc.c4, sc.scale, summary_bias)
+        got = out[b, h * w.G:(h + 1) * w.G].double().cpu().numpy()
+        e = rel_l2(got, want)
+        worst = max(worst, e)
+        assert e < ATTN_REL_L2, f"unit {(b, h)}: rel L2 {e:.3e}"
+    return worst
+
+
+def all_units(w):
+    return [(b, h) for b in range(w.batch) for h in range(w.hkv)]
+
+
+SMALL = [
+    ("tiny", W.TINY),
+    ("q8-2k", W.QWEN3_8B_8K.smaller(T=2048, batch=2, n_marked=41)),
+    ("q14-2k", W.QWEN3_14B_16K.smaller(T=2048, batch=2, n_marked=20)),
+]
+
+
+@pytest.mark.parametrize("name,w", SMALL)
+def test_route_topk_parity(name, w):
+    print(f"route parity {name}", flush=True)
+    sc = Scenario(w)
+    idx, scores = hsq.route_topk(sc.q, sc.tiers, sc.dks, sc.cb3, w.beta, want_scores=True)
+    torch.cuda.synchronize()
+    worst = check_route(sc, idx, scores, all_units(w), w.beta)
+    print(f"  max |score diff| {worst:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("name,w", SMALL)
+def test_decode_attn_parity(name, w):
+    print(f"decode_attn parity {name}", flush=True)
+    sc = Scenario(w)
+    idx, _ = hsq.route_topk(sc.q, sc.tiers, sc.dks, sc.cb3, w.beta)
+    out = hsq.decode_attn(sc.q, sc.tiers, idx, sc.dks, sc.dvs, sc.cb4, sc.cb3)
+    torch.cuda.synchronize()
+    worst = check_attn(sc, out, idx, all_units(w))
+    print(f"  worst rel L2 {worst:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("name,w", SMALL)
+def test_decode_step_parity(name, w):
+    print(f"decode_step parity {name}", flush=True)
+    sc = Scenario(w)
+    out, idx = hsq.decode_step(sc.q, sc.tiers, w.beta, sc.dks, sc.dvs, sc.cb4, sc.cb3)
+    torch.cuda.synchronize()
+    check_route(sc, idx, None, all_units(w), w.beta)
+    worst = check_attn(sc, out, idx, all_units(w))
+    # the fused step (summaries removed by subtraction) agrees with the masked path
+    ref = hsq.decode_attn(sc.q, sc.tiers, idx, sc.dks, sc.dvs, sc.cb4, sc.cb3)
+    torch.cuda.synchronize()
+    assert rel_l2(out.cpu().numpy(), ref.cpu().numpy()) < 1e-4
+    print(f"  worst rel L2 {worst:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("beta", [0, 1, 7, 10_000])
+def test_step_beta_edges(beta):
+    # beta = 0: L1 + every summary; beta >= ng: every group fetched (clamped)
+    w = W.QWEN3_14B_16K.smaller(T=1024, batch=1, n_marked=10)
+    print(f"beta edge {beta}", flush=True)
+    sc = Scenario(w)
+    out, idx = hsq.decode_step(sc.q, sc.tiers, beta, sc.dks, sc.dvs, sc.cb4, sc.cb3)
+    torch.cuda.synchronize()
+    ng = sc.tiers.ng
+    b_eff = min(beta, ng)
+    if b_eff > 0:
+        check_route(sc, idx, None, all_units(w), beta)
+    if b_eff == ng:
+        assert np.all(idx.cpu().numpy() == np.arange(ng)[None, None, :])
+    check_attn(sc, out, idx if b_eff > 0 else None, all_units(w))
+
+
+@pytest.mark.parametrize("case", ["no_l1", "no_groups", "odd_beta_n8", "g8", "g1", "d64_g3",
+                                  "agg_mean", "bias"])
+def test_step_edge_shapes(case):
+    base = W.QWEN3_8B_8K.smaller(T=1024, batch=2, n_marked=12)
+    agg, bias = hsq.HSQ_AGG_MAX, 0.0
+    if case == "no_l1":          # every position grouped: T multiple of N, no sinks/window/marks
+        w = base.smaller(n_sink=0, n_recent=0, n_marked=0, T=1024)
+    elif case == "no_groups":    # everything in L1
+        w = base.smaller(T=60, n_marked=0)
+    elif case == "odd_beta_n8":
+        w = W.QWEN3_14B_16K.smaller(T=1500, batch=2, n_marked=15, beta=33)
+    elif case == "g8":
+        w = base.smaller(hq=64, hkv=8)
+    elif case == "g1":
+        w = base.smaller(hq=8, hkv=8)
+    elif case == "d64_g3":
+        w = W.TINY.smaller(hq=6, hkv=2, T=900, n_marked=9, beta=9, batch=3)
+    elif case == "agg_mean":
+        w, agg = base, hsq.HSQ_AGG_MEAN
+    else:
+        w, bias = base, -0.7
+    print(f"edge shape {case}", flush=True)
+    sc = Scenario(w)
+    out, idx = hsq.decode_step(sc.q, sc.tiers, w.beta, sc.dks, sc.dvs, sc.cb4, sc.cb3, agg=agg,
+                               summary_bias=bias)
+    torch.cuda.synchronize()
+    if sc.tiers.ng > 0 and w.beta > 0:
+        check_route(sc, idx, None, all_units(w), w.beta, "mean" if agg else "max")
+    check_attn(sc, out, idx if (sc.tiers.ng > 0 and w.beta > 0) else None, all_units(w),
+               summary_bias=bias)
+
+
+def test_repeated_calls_reuse_workspace():
+    # completion counters must return to zero: two calls in a row, same workspace
+    w = W.QWEN3_8B_8K.smaller(T=2048, batch=2, n_marked=20)
+    sc = Scenario(w)
+    t = sc.tiers
+    ws = hsq.make_workspace(w.batch, w.hq, w.hkv, w.d, t.n1, t.ng, w.beta, w.group_n, DEV)
+    o1, i1 = hsq.decode_step(sc.q, t, w.beta, sc.dks, sc.dvs, sc.cb4, sc.cb3, ws=ws)
+    o1 = o1.clone()
+    i1 = i1.clone()
+    o2, i2 = hsq.decode_step(sc.q, t, w.beta, sc.dks, sc.dvs, sc.cb4, sc.cb3, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2)
+    assert torch.equal(o1, o2)
