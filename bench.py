@@ -1,0 +1,418 @@
+#!/usr/bin/env python
+"""Benchmark of the HSQ decode step and TurboQuant codec on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one decode step of one layer: router scores over the 3-bit L2
+summary keys, top-beta selection, and fused attention over L1 + unfetched
+summaries + the fetched 4-bit L3 groups, for every (sequence, kv-head) of the
+batch.  The workload is the Qwen3-14B-shaped layer (40 query / 8 kv heads,
+head dim 128, 16K context, batch 64, groups of 8, beta = 128) with the archive
+resident in HBM.  The timed loop cycles through several independent layer
+instances (about 1.55 GB of tiers) so that the 256 MB last-level cache cannot
+hold the working set, and replays a captured HIP graph so host launch latency
+stays out of the measurement.
+
+Prints one JSON line.  Also reported (same line): the codec encode/decode
+rates on the 32K x 8-head bf16 Student-t workload, the decode step with the
+L3 archive in pinned host memory (Qwen3-8B shape, 32K context, batch 8, 36
+layers, gathered over PCIe on a side stream), and the CPU oracle on a bounded
+sample of the headline workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=800)
+    p.add_argument("--warmup", type=int, default=80)
+    p.add_argument("--layers", type=int, default=8, help="independent layer instances cycled")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-codec", action="store_true")
+    p.add_argument("--no-host", action="store_true", help="skip the pinned-host archive run")
+    p.add_argument("--only-step", action="store_true", help="headline step only (for profiling)")
+    return p.parse_args()
+
+
+def algorithmic_bytes(w, n1, ng, beta):
+    """Per-unit algorithmic bytes of the two kernels (head dim d, G heads)."""
+    d, G, N = w.d, w.G, w.group_n
+    cb3, cb4 = 3 * d // 8, d // 2
+    route = ng * (cb3 + 4) + (ng - beta) * (cb3 + 4) + G * d * 4   # keys, unfetched values, q
+    attend = n1 * 2 * (cb4 + 4) + beta * N * 2 * (cb4 + 4) + G * d * 4  # L1, fetched, out
+    return route, attend
+
+
+class Layer:
+    def __init__(self, w, layer, dev, hsq, W, cb, l3=None):
+        import torch
+        self.k_signs, self.v_signs = W.signs(w.seed, layer, w.hkv, w.d)
+        self.dks = torch.from_numpy(self.k_signs.view(np.int32)).to(dev)
+        self.dvs = torch.from_numpy(self.v_signs.view(np.int32)).to(dev)
+        plans = [hsq.tier_plan(w.T, w.n_sink, w.n_recent, W.marked(w, b), w.group_n)
+                 for b in range(w.batch)]
+        l1 = torch.from_numpy(np.stack([p[0] for p in plans])).to(dev)
+        gp = torch.from_numpy(np.stack([p[1].reshape(-1) for p in plans])).to(dev)
+        k, v = W.kv(w, layer, dev)
+        self.tiers = hsq.build_tiers(k, v, l1, gp, w.group_n, self.dks, self.dvs, cb["thr4"],
+                                     cb["thr3"], l3=l3)
+        del k, v
+        self.q = W.query(w, layer, dev)
+        t = self.tiers
+        self.beta = min(w.beta, t.ng)
+        self.ws = hsq.make_workspace(w.batch, w.hq, w.hkv, w.d, t.n1, t.ng, self.beta, w.group_n,
+                                     dev)
+        self.out = torch.empty((w.batch, w.hq, w.d), dtype=torch.float32, device=dev)
+
+
+def codebooks(hsq, d, dev):
+    import torch
+    c4, t4 = hsq.codebook(d, 4)
+    c3, t3 = hsq.codebook(d, 3)
+    f = lambda a: torch.from_numpy(a).to(dev)
+    return {"cb4": f(c4), "thr4": f(t4), "cb3": f(c3), "thr3": f(t3)}
+
+
+def time_graph(torch, graph, reps, stream):
+    """Mean-free total time of `reps` replays, bracketed by HIP events recorded
+    on the stream the replays run on."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def headline(args, torch, hsq, W):
+    dev = "cuda"
+    w = W.QWEN3_14B_16K
+    cb = codebooks(hsq, w.d, dev)
+    layers = [Layer(w, i, dev, hsq, W, cb) for i in range(args.layers)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    L = len(layers)
+
+    def route(ly):
+        hsq.step_route(ly.q, ly.tiers, w.beta, ly.dks, cb["cb3"], ly.ws)
+
+    def attend(ly):
+        hsq.step_attend(ly.q, ly.tiers, w.beta, ly.dks, ly.dvs, cb["cb4"], ly.ws, ly.out)
+
+    graphs = {}
+    with torch.cuda.stream(stream):
+        for ly in layers:  # eager run first: also leaves valid selections in every workspace
+            route(ly)
+            attend(ly)
+        stream.synchronize()
+        for name, fns in (("step", (route, attend)), ("route", (route,)), ("attend", (attend,))):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for ly in layers:
+                    for fn in fns:
+                        fn(ly)
+            graphs[name] = g
+    torch.cuda.synchronize()
+    reps = max(1, math.ceil(args.steps / L))
+    wreps = max(1, math.ceil(args.warmup / L))
+    time_graph(torch, graphs["step"], wreps, stream)
+    t0 = time.perf_counter()
+    ms = time_graph(torch, graphs["step"], reps, stream)
+    wall = time.perf_counter() - t0
+    steps = reps * L
+    ms_step = ms / steps
+    per_kernel = {}
+    for name in ("route", "attend"):
+        time_graph(torch, graphs[name], max(1, wreps // 2), stream)
+        per_kernel[name] = time_graph(torch, graphs[name], reps, stream) / steps
+    t = layers[0].tiers
+    units = w.batch * w.hkv
+    rb, ab = algorithmic_bytes(w, t.n1, t.ng, layers[0].beta)
+    kb = {"route": rb * units, "attend": ab * units}
+    dom = max(per_kernel, key=per_kernel.get)
+    achieved = kb[dom] / (per_kernel[dom] * 1e-3) / 1e9
+    step_bytes = (rb + ab) * units
+    res = {
+        "w": w, "ms_step": ms_step, "steps": steps, "wall_s": wall,
+        "value": units * w.T / (ms_step * 1e-3),
+        "step_gbs": step_bytes / (ms_step * 1e-3) / 1e9,
+        "kernels": {k: {"us": per_kernel[k] * 1e3, "bytes": kb[k],
+                        "gbs": kb[k] / (per_kernel[k] * 1e-3) / 1e9} for k in per_kernel},
+        "dominant": dom, "achieved": achieved, "n1": t.n1, "ng": t.ng,
+        "step_bytes": step_bytes,
+        "tier_bytes": t.nbytes(),
+    }
+    del graphs
+    return res, layers
+
+
+def codec_rates(torch, hsq, W):
+    dev = "cuda"
+    c = W.CODEC
+    k, v = W.codec_inputs(c, dev)
+    ks, vs = W.codec_signs(c)
+    dks = torch.from_numpy(ks.view(np.int32)).to(dev)
+    dvs = torch.from_numpy(vs.view(np.int32)).to(dev)
+    cb = codebooks(hsq, c.d, dev)
+    stream = torch.cuda.Stream()
+    n = c.heads * c.tokens
+    out = {}
+    for bits in (4, 3):
+        thr = cb["thr4" if bits == 4 else "thr3"]
+        cen = cb["cb4" if bits == 4 else "cb3"]
+        with torch.cuda.stream(stream):
+            kc, kn = hsq.encode(k.view(n, c.d), bits, dks, thr, vecs_per_rot=c.tokens, n_rot=c.heads)
+            vc, vn = hsq.encode(v.view(n, c.d), bits, dvs, thr, vecs_per_rot=c.tokens, n_rot=c.heads)
+            dk = hsq.decode(kc, kn, bits, c.d, dks, cen, vecs_per_rot=c.tokens, n_rot=c.heads,
+                            out_dtype=torch.bfloat16)
+            stream.synchronize()
+            ge = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(ge, stream=stream):
+                hsq.encode(k.view(n, c.d), bits, dks, thr, vecs_per_rot=c.tokens, n_rot=c.heads)
+                hsq.encode(v.view(n, c.d), bits, dvs, thr, vecs_per_rot=c.tokens, n_rot=c.heads)
+            gd = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gd, stream=stream):
+                hsq.decode(kc, kn, bits, c.d, dks, cen, vecs_per_rot=c.tokens, n_rot=c.heads,
+                           out_dtype=torch.bfloat16)
+                hsq.decode(vc, vn, bits, c.d, dvs, cen, vecs_per_rot=c.tokens, n_rot=c.heads,
+                           out_dtype=torch.bfloat16)
+        time_graph(torch, ge, 5, stream)
+        te = time_graph(torch, ge, 50, stream) / 50
+        time_graph(torch, gd, 5, stream)
+        td = time_graph(torch, gd, 50, stream) / 50
+        in_b = 2 * n * c.d * 2
+        code_b = 2 * n * (c.d * bits // 8 + 4)
+        # relative round-trip error of the bf16 decode (diagnostic, cf. relMSE)
+        rel = float(((dk.float() - k.view(n, c.d).float()).pow(2).sum(1) /
+                     k.view(n, c.d).float().pow(2).sum(1)).mean())
+        out[f"{bits}bit"] = {
+            "encode_us": te * 1e3, "encode_in_gbs": in_b / (te * 1e-3) / 1e9,
+            "encode_hbm_frac": (in_b + code_b) / (te * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "decode_us": td * 1e3, "decode_out_gbs": in_b / (td * 1e-3) / 1e9,
+            "decode_hbm_frac": (in_b + code_b) / (td * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "relmse_k": rel,
+        }
+    del k, v
+    return out
+
+
+def host_archive(torch, hsq, W, steps=3):
+    """Decode step of 36 layers with the L3 archive in pinned host memory."""
+    dev = "cuda"
+    w = W.QWEN3_8B_32K
+    cb = codebooks(hsq, w.d, dev)
+    l1, gp = hsq.tier_plan(w.T, w.n_sink, w.n_recent, W.marked(w, 0), w.group_n)
+    n1, ng = l1.shape[0], gp.shape[0]
+    rec = w.group_n * (w.d + 8)
+    per_layer = w.batch * w.hkv * ng * rec
+    arch = hsq.HostArchive(per_layer * w.layers)
+    # the tier builder writes each layer's archive straight into pinned host memory
+    layers = [_host_layer(w, i, dev, hsq, W, cb, arch.dev_ptr + i * per_layer)
+              for i in range(w.layers)]
+    torch.cuda.synchronize()
+    beta = min(w.beta, ng)
+    staging = torch.empty((w.batch, w.hkv, beta, rec), dtype=torch.uint8, device=dev)
+    main = torch.cuda.Stream()
+    side = torch.cuda.Stream()
+
+    def one_step():
+        for i, ly in enumerate(layers):
+            with torch.cuda.stream(main):
+                hsq.step_route(ly.q, ly.tiers, w.beta, ly.dks, cb["cb3"], ly.ws, idx=ly.ws_idx)
+                ev = torch.cuda.Event()
+                ev.record(main)
+            with torch.cuda.stream(side):
+                side.wait_event(ev)
+                idx = ly.ws_idx
+                hsq.gather_l3(arch.dev_ptr + i * per_layer, rec, w.batch, w.hkv, ng, idx, staging)
+                ev2 = torch.cuda.Event()
+                ev2.record(side)
+            with torch.cuda.stream(main):
+                main.wait_event(ev2)
+                hsq.step_attend(ly.q, ly.tiers, w.beta, ly.dks, ly.dvs, cb["cb4"], ly.ws, ly.out,
+                                l3=staging.data_ptr(), l3_staged=True)
+
+    one_step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(main)
+    for _ in range(steps):
+        one_step()
+    e1.record(main)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    link_bytes = w.layers * w.batch * w.hkv * beta * rec
+    # measured pinned host -> device copy rate, for context
+    hbuf = arch.view(0, min(per_layer, 1 << 30))
+    dbuf = torch.empty(hbuf.numel(), dtype=torch.uint8, device=dev)
+    dbuf.copy_(hbuf, non_blocking=True)
+    torch.cuda.synchronize()
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dbuf.copy_(hbuf, non_blocking=True)
+    c1.record()
+    torch.cuda.synchronize()
+    h2d = 5 * hbuf.numel() / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    res = {
+        "workload": w.name, "layers": w.layers, "batch": w.batch, "T": w.T, "beta": beta,
+        "ms_per_step": ms,
+        "value": w.batch * w.hkv * w.T * w.layers / (ms * 1e-3),
+        "unit": "heads*tokens/s",
+        "pcie_bytes_per_step": link_bytes,
+        "pcie_gbs": link_bytes / (ms * 1e-3) / 1e9,
+        "pinned_h2d_copy_gbs": h2d,
+        "archive_gib": per_layer * w.layers / 2 ** 30,
+    }
+    del layers, arch
+    return res
+
+
+class _HostLayer:
+    pass
+
+
+def _host_layer(w, layer, dev, hsq, W, cb, l3_dev_ptr):
+    import torch
+    ly = _HostLayer()
+    ly.k_signs, ly.v_signs = W.signs(w.seed, layer, w.hkv, w.d)
+    ly.dks = torch.from_numpy(ly.k_signs.view(np.int32)).to(dev)
+    ly.dvs = torch.from_numpy(ly.v_signs.view(np.int32)).to(dev)
+    plans = [hsq.tier_plan(w.T, w.n_sink, w.n_recent, W.marked(w, b), w.group_n)
+             for b in range(w.batch)]
+    l1 = torch.from_numpy(np.stack([p[0] for p in plans])).to(dev)
+    gp = torch.from_numpy(np.stack([p[1].reshape(-1) for p in plans])).to(dev)
+    k, v = W.kv(w, layer, dev)
+    n1, ng = l1.shape[1], gp.shape[1] // w.group_n
+    t = hsq.alloc_tiers(w.batch, w.hkv, w.d, n1, ng, w.group_n, dev, l3=torch.empty(0, device=dev))
+    lib = hsq.lib()
+    hsq._check(lib.hsq_build_tiers(
+        k.data_ptr(), v.data_ptr(), hsq.HSQ_BF16, w.batch, w.hkv, w.T, w.d, l1.data_ptr(), n1,
+        gp.data_ptr(), ng, w.group_n, ly.dks.data_ptr(), ly.dvs.data_ptr(), cb["thr4"].data_ptr(),
+        cb["thr3"].data_ptr(), t.l1k.data_ptr(), t.l1k_n.data_ptr(), t.l1v.data_ptr(),
+        t.l1v_n.data_ptr(), t.l2k.data_ptr(), t.l2k_n.data_ptr(), t.l2v.data_ptr(),
+        t.l2v_n.data_ptr(), l3_dev_ptr, torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    del k, v
+    ly.tiers = t
+    ly.q = W.query(w, layer, dev)
+    beta = min(w.beta, ng)
+    ly.ws = hsq.make_workspace(w.batch, w.hq, w.hkv, w.d, n1, ng, beta, w.group_n, dev)
+    ly.ws_idx = torch.empty((w.batch, w.hkv, beta), dtype=torch.int32, device=dev)
+    # step_route copies the selection into ws_idx for the side-stream gather
+    ly.out = torch.empty((w.batch, w.hq, w.d), dtype=torch.float32, device=dev)
+    return ly
+
+
+def cpu_baseline(torch, W, layers, budget_s=12.0):
+    """The oracle (fp64 numpy) on a bounded sample of the headline workload."""
+    from oracle import codebook as ocb
+    from oracle import decode as odec
+    from oracle import tiers as otiers
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    w = W.QWEN3_14B_16K
+    c4, c3 = ocb.codebook_f32(w.d, 4), ocb.codebook_f32(w.d, 3)
+    ly = layers[0]
+    sample = [(0, 0), (17, 3), (42, 7)]
+    units = []
+    k, v = W.kv(w, 0, "cuda")  # layer 0 of the timed workload, regenerated from its seed
+    raw = {(b, h): (k[b, h].cpu(), v[b, h].cpu()) for (b, h) in sample}
+    del k, v
+    torch.cuda.empty_cache()
+    for (b, h) in sample:
+        kb, vb = raw[(b, h)]
+        l1, g = otiers.tier_plan(w.T, w.n_sink, w.n_recent, W.marked(w, b), w.group_n)
+        unit = otiers.build_unit(kb, vb, l1, g, ly.k_signs[h], ly.v_signs[h], c4, c3)
+        qh = ly.q[b, h * w.G:(h + 1) * w.G].double().cpu().numpy()
+        units.append((unit, qh, h))
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        unit, qh, h = units[done % len(units)]
+        odec.decode_step_unit(qh, unit, w.group_n, w.d, ly.k_signs[h], ly.v_signs[h], c4, c3, w.beta,
+                              1.0 / math.sqrt(w.d))
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done * w.T / el, "unit": "heads*tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} (sequence, kv-head) decode steps of the {w.name} workload "
+                      f"(route + top-beta + attention over T={w.T}), cycling over units {sample}, "
+                      f"{el:.1f} s; fp64 numpy oracle"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; multi-GPU runs are not part of it",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    from compressed_decode_attention_turboquant_amd import hsq
+    from compressed_decode_attention_turboquant_amd import workloads as W
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    hsq.lib()
+    res, layers = headline(args, torch, hsq, W)
+    w = res["w"]
+    k = res["kernels"]
+    dom = res["dominant"]
+    line = {
+        "metric": "HSQ decode-step KV heads·tokens/s + % HBM roofline; codec encode GB/s",
+        "value": res["value"],
+        "unit": "heads*tokens/s",
+        "n_gpus": 1,
+        "steps": res["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 (fp16 MFMA operands, fp32 accumulate; 4-bit/3-bit codes)",
+        "data": "synthetic (seeded Student-t keys, normal values; no trained weights)",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.hq, "kv_heads": w.hkv,
+                   "head_dim": w.d, "context": w.T, "group_n": w.group_n, "beta": w.beta,
+                   "n_l1": res["n1"], "n_groups": res["ng"], "archive": "hbm",
+                   "layer_instances": args.layers, "parallelism": "single-gpu"},
+        "step_hbm_gbs": res["step_gbs"],
+        "step_hbm_frac": res["step_gbs"] / HBM_PEAK_GBS,
+        "kernels": k,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": res["achieved"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": res["achieved"] / HBM_PEAK_GBS,
+                     "traffic": None},
+    }
+    if not args.only_step and not args.no_codec:
+        line["codec"] = codec_rates(torch, hsq, W)
+    if not args.only_step and not args.no_host:
+        try:
+            line["host_archive"] = host_archive(torch, hsq, W)
+        except Exception as e:  # reported, never hides the headline
+            line["host_archive"] = {"error": repr(e)}
+    if not args.only_step and not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(torch, W, layers)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -159,6 +159,11 @@ namespace {
 
 int step_common(const char* fn, const StepShape& s, void* workspace, size_t ws_bytes,
                 Workspace& w) {
+  if (!step_limits_ok(s))
+    return fail(HSQ_ERR_UNSUPPORTED,
+                std::string(fn) + ": n_groups, G * n_groups or the L1/L3 sizes exceed the "
+                                  "kernels' limits (n_groups <= 16384, G * n_groups <= 12288, "
+                                  "per-unit L1/L3 bytes < 2 GiB)");
   w = plan_workspace(s);
   if (!workspace || ws_bytes < w.total)
     return fail(HSQ_ERR_WORKSPACE, std::string(fn) + ": workspace missing or smaller than hsq_workspace_bytes()");
@@ -190,7 +195,6 @@ extern "C" int hsq_route_topk(const float* q, int B, int Hq, int Hkv, int d, con
   t.agg = agg;
   char* ws = static_cast<char*>(workspace);
   const hipStream_t st = as_stream(stream);
-  if ((rc = check_hip(launch_qrot(s, t, w, ws, st), "hsq_route_topk qrot"))) return rc;
   return check_hip(launch_route(s, t, w, ws, ROUTE_TOPK, nullptr, scores, topk_idx, st),
                    "hsq_route_topk route");
 }
@@ -236,11 +240,69 @@ extern "C" int hsq_decode_attn(const float* q, int B, int Hq, int Hkv, int d, co
                 k_signs, v_signs, cb4, cb3, scale, summary_bias, HSQ_AGG_MAX, out};
   char* ws = static_cast<char*>(workspace);
   const hipStream_t st = as_stream(stream);
-  if ((rc = check_hip(launch_qrot(s, t, w, ws, st), "hsq_decode_attn qrot"))) return rc;
   if ((rc = check_hip(launch_route(s, t, w, ws, ROUTE_PARTIALS, topk_idx, nullptr, nullptr, st),
                       "hsq_decode_attn summaries")))
     return rc;
   return check_hip(launch_attn(s, t, w, ws, topk_idx, st), "hsq_decode_attn attention");
+}
+
+extern "C" int hsq_step_route(const float* q, int B, int Hq, int Hkv, int d, int n_l1,
+                              const uint8_t* l2k, const float* l2k_n, const uint8_t* l2v,
+                              const float* l2v_n, int n_groups, int group_n, int beta, int agg,
+                              const uint32_t* k_signs, const float* cb3, float scale,
+                              float summary_bias, int32_t* topk_idx, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  int rc = check_step_shape("hsq_step_route", B, Hq, Hkv, d, n_l1, n_groups, group_n, beta);
+  if (rc) return rc;
+  if (agg != HSQ_AGG_MAX && agg != HSQ_AGG_MEAN) return fail(HSQ_ERR_ARG, "hsq_step_route: bad agg");
+  if (!q || !k_signs || !cb3 || (n_groups > 0 && (!l2k || !l2k_n || !l2v || !l2v_n)))
+    return fail(HSQ_ERR_ARG, "hsq_step_route: null pointer");
+  const int b = beta < n_groups ? beta : n_groups;
+  StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, b};
+  Workspace w;
+  if ((rc = step_common("hsq_step_route", s, workspace, ws_bytes, w))) return rc;
+  StepTensors t{};
+  t.q = q; t.l2k = l2k; t.l2k_n = l2k_n; t.l2v = l2v; t.l2v_n = l2v_n; t.k_signs = k_signs;
+  t.cb3 = cb3; t.scale = scale; t.summary_bias = summary_bias; t.agg = agg;
+  char* ws = static_cast<char*>(workspace);
+  const hipStream_t st = as_stream(stream);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + w.idx_off);
+  if ((rc = check_hip(launch_route(s, t, w, ws, ROUTE_TOPK | ROUTE_PARTIALS, nullptr, nullptr,
+                                   idx, st),
+                      "hsq_step_route")))
+    return rc;
+  if (topk_idx && b > 0)
+    return check_hip(hipMemcpyAsync(topk_idx, idx, sizeof(int32_t) * (size_t)B * Hkv * b,
+                                    hipMemcpyDeviceToDevice, st),
+                     "hsq_step_route topk copy");
+  return HSQ_OK;
+}
+
+extern "C" int hsq_step_attend(const float* q, int B, int Hq, int Hkv, int d, const uint8_t* l1k,
+                               const float* l1k_n, const uint8_t* l1v, const float* l1v_n,
+                               int n_l1, int n_groups, const uint8_t* l3, int group_n,
+                               int l3_staged, int beta, const uint32_t* k_signs,
+                               const uint32_t* v_signs, const float* cb4, float scale,
+                               void* workspace, size_t ws_bytes, float* out, void* stream) {
+  int rc = check_step_shape("hsq_step_attend", B, Hq, Hkv, d, n_l1, n_groups, group_n, beta);
+  if (rc) return rc;
+  if (!q || !out || !k_signs || !v_signs || !cb4)
+    return fail(HSQ_ERR_ARG, "hsq_step_attend: null pointer");
+  if (n_l1 > 0 && (!l1k || !l1k_n || !l1v || !l1v_n))
+    return fail(HSQ_ERR_ARG, "hsq_step_attend: null L1 pointer");
+  const int b = beta < n_groups ? beta : n_groups;
+  if (b > 0 && !l3) return fail(HSQ_ERR_ARG, "hsq_step_attend: null L3 pointer");
+  StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, b};
+  Workspace w;
+  if ((rc = step_common("hsq_step_attend", s, workspace, ws_bytes, w))) return rc;
+  StepTensors t{};
+  t.q = q; t.l1k = l1k; t.l1k_n = l1k_n; t.l1v = l1v; t.l1v_n = l1v_n; t.l3 = l3;
+  t.l3_staged = l3_staged ? 1 : 0; t.k_signs = k_signs; t.v_signs = v_signs; t.cb4 = cb4;
+  t.scale = scale; t.out = out;
+  char* ws = static_cast<char*>(workspace);
+  return check_hip(launch_attn(s, t, w, ws, reinterpret_cast<int32_t*>(ws + w.idx_off),
+                               as_stream(stream)),
+                   "hsq_step_attend");
 }
 
 extern "C" int hsq_decode_step(const float* q, int B, int Hq, int Hkv, int d, const uint8_t* l1k,
@@ -254,30 +316,15 @@ extern "C" int hsq_decode_step(const float* q, int B, int Hq, int Hkv, int d, co
                                size_t ws_bytes, float* out, void* stream) {
   int rc = check_step_shape("hsq_decode_step", B, Hq, Hkv, d, n_l1, n_groups, group_n, beta);
   if (rc) return rc;
-  if (agg != HSQ_AGG_MAX && agg != HSQ_AGG_MEAN) return fail(HSQ_ERR_ARG, "hsq_decode_step: bad agg");
   if ((rc = attn_args("hsq_decode_step", q, l1k, l1k_n, l1v, l1v_n, n_l1, l2k, l2k_n, l2v, l2v_n,
                       n_groups, l3, k_signs, v_signs, cb4, cb3, out)))
     return rc;
-  const int b = beta < n_groups ? beta : n_groups;
-  StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, b};
-  Workspace w;
-  if ((rc = step_common("hsq_decode_step", s, workspace, ws_bytes, w))) return rc;
-  StepTensors t{q, l1k, l1k_n, l1v, l1v_n, l2k, l2k_n, l2v, l2v_n, l3, 0,
-                k_signs, v_signs, cb4, cb3, scale, summary_bias, agg, out};
-  char* ws = static_cast<char*>(workspace);
-  const hipStream_t st = as_stream(stream);
-  int32_t* idx = reinterpret_cast<int32_t*>(ws + w.idx_off);
-  if ((rc = check_hip(launch_qrot(s, t, w, ws, st), "hsq_decode_step qrot"))) return rc;
-  if ((rc = check_hip(launch_route(s, t, w, ws, ROUTE_TOPK | ROUTE_PARTIALS, nullptr, nullptr,
-                                   idx, st),
-                      "hsq_decode_step route")))
+  if ((rc = hsq_step_route(q, B, Hq, Hkv, d, n_l1, l2k, l2k_n, l2v, l2v_n, n_groups, group_n, beta,
+                           agg, k_signs, cb3, scale, summary_bias, topk_idx, workspace, ws_bytes,
+                           stream)))
     return rc;
-  if ((rc = check_hip(launch_attn(s, t, w, ws, idx, st), "hsq_decode_step attention"))) return rc;
-  if (topk_idx && b > 0)
-    return check_hip(hipMemcpyAsync(topk_idx, idx, sizeof(int32_t) * (size_t)B * Hkv * b,
-                                    hipMemcpyDeviceToDevice, st),
-                     "hsq_decode_step topk copy");
-  return HSQ_OK;
+  return hsq_step_attend(q, B, Hq, Hkv, d, l1k, l1k_n, l1v, l1v_n, n_l1, n_groups, l3, group_n, 0,
+                         beta, k_signs, v_signs, cb4, scale, workspace, ws_bytes, out, stream);
 }
 
 extern "C" int hsq_gather_l3(const uint8_t* l3_src, size_t rec_bytes, int B, int Hkv,

@@ -7,7 +7,7 @@
 #include <cstdint>
 #include <string>
 
-#include "../../include/hsq.h"
+#include "hsq.h"
 
 namespace hsq {
 
@@ -79,25 +79,17 @@ struct StepTensors {
 
 // Workspace layout (all offsets 256-byte aligned).
 struct Workspace {
-  size_t qrot_off;     // fp32 [B*Hkv][G][d]  rotated, scaled queries (K rotation)
-  size_t scores_off;   // fp32 [B*Hkv][ng]    aggregated router scores
-  size_t idx_off;      // int32 [B*Hkv][beta] selection
-  size_t part_off;     // fp32 partials [B*Hkv][slots][G][d+2]
-  size_t cnt_off;      // uint32 [B*Hkv][2]  completion counters
+  size_t idx_off;      // int32 [B*Hkv][beta]   selection
+  size_t part_off;     // fp32  [B*Hkv][G][d+2] summary-attention partial (m, l, O)
   size_t total;
-  int route_chunks;    // route work-groups per unit
-  int attn_slots;      // attention partial slots per unit
-  int sum_chunks;      // summary-attention work-groups per unit
-  int l1_chunks;
-  int fetch_chunks;
 };
 Workspace plan_workspace(const StepShape& s);
+// shapes the step kernels can hold in LDS / 32-bit buffer offsets
+int step_limits_ok(const StepShape& s);
 
-// mode bits for the route/summary kernel
+// mode bits for the summary kernel
 enum { ROUTE_TOPK = 1, ROUTE_PARTIALS = 2 };
 
-hipError_t launch_qrot(const StepShape& s, const StepTensors& t, const Workspace& w,
-                       char* ws, hipStream_t st);
 hipError_t launch_route(const StepShape& s, const StepTensors& t, const Workspace& w, char* ws,
                         int mode, const int32_t* given_idx, float* scores_out,
                         int32_t* idx_out, hipStream_t st);

@@ -37,6 +37,10 @@ _SIGNATURES = {
     "hsq_decode_step": ([_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i,
                          _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _f, _vp, _vp, _sz, _vp, _vp],
                         _i),
+    "hsq_step_route": ([_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp,
+                        _f, _f, _vp, _vp, _sz, _vp], _i),
+    "hsq_step_attend": ([_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _vp, _i, _i, _i, _vp,
+                         _vp, _vp, _f, _vp, _sz, _vp, _vp], _i),
     "hsq_gather_l3": ([_vp, _sz, _i, _i, _i, _vp, _i, _vp, _vp], _i),
 }
 
@@ -309,3 +313,62 @@ def gather_l3(l3_src_ptr, rec_bytes, B, Hkv, ng, idx, staging):
     _check(lib().hsq_gather_l3(l3_src_ptr, rec_bytes, B, Hkv, ng, _dev(idx, torch.int32, "idx"),
                                beta, _dev(staging, torch.uint8, "staging"), _stream()))
     return staging
+
+
+def step_route(q, tiers, beta, k_signs, cb3, ws, scale=None, summary_bias=0.0, agg=HSQ_AGG_MAX,
+               idx=None, stream=None):
+    """First launch of the decode step: router, top-beta, summary partials (into ws)."""
+    B, Hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(lib().hsq_step_route(
+        _dev(q, torch.float32, "q"), B, Hq, tiers.Hkv, d, tiers.n1, _dev(tiers.l2k),
+        _dev(tiers.l2k_n), _dev(tiers.l2v), _dev(tiers.l2v_n), tiers.ng, tiers.group_n, beta, agg,
+        _dev(k_signs, torch.int32, "k_signs"), _dev(cb3, torch.float32, "cb3"), scale,
+        summary_bias, idx.data_ptr() if idx is not None else None, ws.ptr, ws.nbytes,
+        stream if stream is not None else _stream()))
+
+
+def step_attend(q, tiers, beta, k_signs, v_signs, cb4, ws, out, scale=None, l3=None,
+                l3_staged=False, stream=None):
+    """Second launch: L1 + fetched-token attention, merge, inverse rotation."""
+    B, Hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    l3p = l3 if l3 is not None else tiers.l3.data_ptr()
+    _check(lib().hsq_step_attend(
+        _dev(q, torch.float32, "q"), B, Hq, tiers.Hkv, d, _dev(tiers.l1k), _dev(tiers.l1k_n),
+        _dev(tiers.l1v), _dev(tiers.l1v_n), tiers.n1, tiers.ng, l3p, tiers.group_n,
+        int(l3_staged), beta, _dev(k_signs, torch.int32, "k_signs"),
+        _dev(v_signs, torch.int32, "v_signs"), _dev(cb4, torch.float32, "cb4"), scale, ws.ptr,
+        ws.nbytes, _dev(out, torch.float32, "out"), stream if stream is not None else _stream()))
+    return out
+
+
+_hip = None
+
+
+def _hiprt():
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), _vp, _c.c_uint]
+        _hip.hipHostGetDevicePointer.restype = _i
+    return _hip
+
+
+class HostArchive:
+    """L3 records of one or more layers in pinned host memory (torch
+    pin_memory, i.e. hipHostMalloc), with the device alias kernels read over
+    PCIe."""
+
+    def __init__(self, nbytes):
+        self.host = torch.empty(int(nbytes), dtype=torch.uint8, pin_memory=True)
+        dptr = ctypes.c_void_p()
+        rc = _hiprt().hipHostGetDevicePointer(ctypes.byref(dptr), self.host.data_ptr(), 0)
+        if rc != 0:
+            raise HSQError(-3, f"hipHostGetDevicePointer failed ({rc})")
+        self.dev_ptr = dptr.value
+
+    def view(self, offset, nbytes):
+        return self.host[offset:offset + nbytes]

@@ -179,7 +179,11 @@ int hsq_build_tiers(const void* k, const void* v, int dtype, int B, int Hkv, int
  *   beta        >= 0, clamped to n_groups
  *   topk_idx    out int32 [B][Hkv][min(beta, n_groups)]
  *   scores      optional out fp32 [B][Hkv][n_groups] (NULL = not written)
- *   workspace   device, >= hsq_workspace_bytes(...) bytes
+ *   workspace   device, >= hsq_workspace_bytes(...) bytes, 256-byte aligned,
+ *               zero-filled before its first use (the calls keep their
+ *               completion counters at zero between calls; after an
+ *               HSQ_ERR_HIP failure, zero it again).  Calls that share a
+ *               workspace must be ordered on one stream.
  */
 int hsq_route_topk(const float* q, int B, int Hq, int Hkv, int d, const uint8_t* l2k,
                    const float* l2k_n, int n_groups, const uint32_t* k_signs, const float* cb3,
@@ -225,6 +229,33 @@ int hsq_decode_step(const float* q, int B, int Hq, int Hkv, int d, const uint8_t
                     int agg, const uint32_t* k_signs, const uint32_t* v_signs, const float* cb4,
                     const float* cb3, float scale, float summary_bias, int32_t* topk_idx,
                     void* workspace, size_t ws_bytes, float* out, void* stream);
+
+/*
+ * hsq_step_route / hsq_step_attend -- the two launches of hsq_decode_step,
+ * exposed so a caller can put work between them: the host-archive path runs
+ * hsq_step_route, then hsq_gather_l3 (PCIe, side stream), then
+ * hsq_step_attend with l3_staged = 1 [HSQ "Decode process": routing, then
+ * fetching from the CPU archive, then attention].
+ *   hsq_step_route   router scores, top-beta and the summary-attention
+ *                    partials (all summaries, then the fetched ones removed)
+ *                    into the workspace; topk_idx (optional) receives a copy
+ *                    of the selection.
+ *   hsq_step_attend  L1 and fetched-token attention, merge with the summary
+ *                    partials, inverse V rotation, out.  Reads the selection
+ *                    from the workspace written by the preceding
+ *                    hsq_step_route with the same sizes and workspace.
+ * Both take n_l1 and n_groups so they size the workspace identically.
+ */
+int hsq_step_route(const float* q, int B, int Hq, int Hkv, int d, int n_l1, const uint8_t* l2k,
+                   const float* l2k_n, const uint8_t* l2v, const float* l2v_n, int n_groups,
+                   int group_n, int beta, int agg, const uint32_t* k_signs, const float* cb3,
+                   float scale, float summary_bias, int32_t* topk_idx, void* workspace,
+                   size_t ws_bytes, void* stream);
+int hsq_step_attend(const float* q, int B, int Hq, int Hkv, int d, const uint8_t* l1k,
+                    const float* l1k_n, const uint8_t* l1v, const float* l1v_n, int n_l1,
+                    int n_groups, const uint8_t* l3, int group_n, int l3_staged, int beta,
+                    const uint32_t* k_signs, const uint32_t* v_signs, const float* cb4,
+                    float scale, void* workspace, size_t ws_bytes, float* out, void* stream);
 
 /*
  * hsq_gather_l3 -- copy the fetched L3 records into a staging buffer
