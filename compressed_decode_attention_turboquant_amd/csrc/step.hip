@@ -107,6 +107,43 @@ __device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Runs use(i, buf) for i in [0, iters) with each buffer's loads issued two
+// iterations before its use, so every wave keeps two tiles in flight.  load(i)
+// is also called for i >= iters; it must then read out of bounds (buffer loads
+// past num_records return zero without memory traffic).  iters is wave-uniform.
+template <typename Buf, typename LoadF, typename UseF>
+__device__ __forceinline__ void pipeline3(int iters, LoadF load, UseF use) {
+  Buf b0, b1, b2;
+  load(0, b0);
+  load(1, b1);
+  // whole triples only: a loop body with no exit in the middle keeps the same
+  // number of loads in flight on every back edge, so the waits stay partial
+  int i = 0;
+  // the scheduling barriers keep the compiler from sinking the loads below
+  // the previous tile's arithmetic
+  for (; i + 3 <= iters; i += 3) {
+    load(i + 2, b2);
+    __builtin_amdgcn_sched_barrier(0);
+    use(i, b0);
+    load(i + 3, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    use(i + 1, b1);
+    load(i + 4, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    use(i + 2, b2);
+  }
+  if (i < iters) use(i, b0);
+  if (i + 1 < iters) use(i + 1, b1);
+}
+
+// Wave index as a scalar (wave-uniform for the compiler).
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+__device__ __forceinline__ int wave_iters(int n_tiles, int wave) {
+  return wave < n_tiles ? (n_tiles - wave + kWaves - 1) / kWaves : 0;
+}
+
 // ---------------------------------------------------------------- tables ---
 
 // 4-bit: byte b (codes b & 15, b >> 4) -> fp16 pair; copy l at dword b*64 + l,
@@ -217,8 +254,9 @@ struct Online {
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     const float mn = fmaxf(m, mt);
     const float ms = (mn == kNegInf) ? 0.f : mn;
-    if (mn > m) {  // rescale only when the running max moves
-      const float alpha = __expf(m - ms);
+    // rescale only when some column's running max moved (wave-uniform branch)
+    if (__builtin_amdgcn_ballot_w64(mn > m)) {
+      const float alpha = (mn > m) ? __expf(m - ms) : 1.f;
       l *= alpha;
 #pragma unroll
       for (int t = 0; t < D / 32; ++t) O[t] *= alpha;
@@ -490,40 +528,59 @@ __device__ __forceinline__ void load_keys(rsrc_t rk, rsrc_t rn, int t, int lane,
   if constexpr (D == 128) {  // 96 bits at byte 12*gq
     const u32x3 w = ld96(rk, row + 12 * gq);
     T.kw[0] = w.x; T.kw[1] = w.y; T.kw[2] = w.z; T.kw[3] = 0u;
-  } else {                   // 48 bits at bit 48*gq
+  } else {                   // 48 bits at bit 48*gq: raw dwords, aligned by key_bits
     const u32x2 w = ld64(rk, row + 4 * ((3 * gq) >> 1));
-    const uint32_t s = (gq & 1) ? 16u : 0u;
-    T.kw[0] = __builtin_amdgcn_alignbit(w.y, w.x, s);
-    T.kw[1] = w.y >> s;
-    T.kw[2] = 0u; T.kw[3] = 0u;
+    T.kw[0] = w.x; T.kw[1] = w.y; T.kw[2] = 0u; T.kw[3] = 0u;
   }
   T.kn = ldf1x4(rn, (uint32_t)(16 * t + 4 * gq) * 4);
 }
 
-// Values of tile t: this lane's value bits (dims [2T*rho, 2T*rho + 2T), T = D/32)
-// of rows 4gq+j and their norms; rows flagged in `skip` read as zero.
+// This lane's key bits from the words load_keys left (the loads stay free of
+// arithmetic so that no wait is forced before the tile is used).
+template <int D>
+__device__ __forceinline__ void key_bits(const uint32_t (&w)[4], int lane, uint32_t (&kw)[4]) {
+  if constexpr (D == 128) {
+    kw[0] = w[0]; kw[1] = w[1]; kw[2] = w[2]; kw[3] = 0u;
+  } else {
+    const uint32_t s = ((lane >> 4) & 1) ? 16u : 0u;
+    kw[0] = __builtin_amdgcn_alignbit(w[1], w[0], s);
+    kw[1] = w[1] >> s;
+    kw[2] = 0u; kw[3] = 0u;
+  }
+}
+
+// Values of tile t: the dword of row 4gq+j that holds this lane's value bits
+// (dims [2T*rho, 2T*rho + 2T), T = D/32; shifted into place by the consumer)
+// and the rows' norms; rows flagged in `skip` read as zero.
 struct ValTile {
   uint32_t va[4];
   f32x4 vn;
+  uint32_t skip;
 };
+// The dword holding this lane's value bits starts at byte min(bit/8, RB-4)
+// (so it never crosses the end of the row; buffer loads need only byte
+// alignment); val_shift is where the bits start in it.
+template <int D>
+__device__ __forceinline__ uint32_t val_byte(int lane) {
+  constexpr int RB = 3 * D / 8;        // bytes per row
+  constexpr int BITS = 6 * (D / 32);   // bits per lane per row
+  return (uint32_t)min((BITS * (lane & 15)) >> 3, RB - 4);
+}
+template <int D>
+__device__ __forceinline__ uint32_t val_shift(int lane) {
+  constexpr int BITS = 6 * (D / 32);
+  return (uint32_t)(BITS * (lane & 15)) - 8u * val_byte<D>(lane);
+}
 template <int D>
 __device__ __forceinline__ void load_vals(rsrc_t rv, rsrc_t rvn, int t, int lane, uint32_t skip,
                                           ValTile& T) {
-  constexpr int CB3 = 3 * D / 8;
-  constexpr int NW = CB3 / 4;          // dwords per row
-  constexpr int BITS = 6 * (D / 32);   // bits per lane per row
-  const int rho = lane & 15, gq = lane >> 4;
-  const int bit = BITS * rho;
-  // the 8-byte window starts at most at the row's second-to-last dword so it
-  // never crosses the end of the row
-  const int w0 = min(bit >> 5, NW - 2);
-  const uint32_t wofs = 4u * (uint32_t)w0;
-  const uint32_t s = (uint32_t)(bit - 32 * w0);  // 0..63
+  constexpr int RB = 3 * D / 8;
+  const int gq = lane >> 4;
+  const uint32_t wofs = val_byte<D>(lane);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t row = (uint32_t)(16 * t + 4 * gq + j) * CB3;
-    const u32x2 w = ld64(rv, ((skip >> j) & 1u) ? kFar : row + wofs);
-    T.va[j] = (s < 32) ? __builtin_amdgcn_alignbit(w.y, w.x, s) : (w.y >> (s - 32));
+    const uint32_t row = (uint32_t)(16 * t + 4 * gq + j) * RB;
+    T.va[j] = ld32(rv, ((skip >> j) & 1u) ? kFar : row + wofs);
   }
   T.vn = ldf1x4(rvn, (uint32_t)(16 * t + 4 * gq) * 4);
 }
@@ -535,8 +592,8 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   __shared__ float s_cb[8];
   __shared__ int s_tmp[kWaves];
   // layout: [lut3 16 KB][qf 8*D f32][logits G*ngp f32][keys ngp u32][hist 256]
-  //         [sel beta][fetched bitmap]; the wave-combine scratch reuses the
-  //         front once the tiles are done.
+  //         [sel beta][fetched bitmap][dummy 64x4 f32]; the wave-combine
+  //         scratch reuses the front once the tiles are done.
   const int ngp = (a.ng + 15) & ~15;
   uint32_t* lut3 = reinterpret_cast<uint32_t*>(smem);
   float* qf = reinterpret_cast<float*>(smem + 64 * kNC3 * 8);
@@ -545,9 +602,10 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   int* hist = reinterpret_cast<int*>(keys + ngp);
   int32_t* sel = hist + 256;
   uint32_t* fmask = reinterpret_cast<uint32_t*>(sel + ((a.beta + 3) & ~3));
+  float* dummy = reinterpret_cast<float*>(fmask + (((ngp + 31) / 32 + 3) & ~3));  // [64][4]
   float* scratch = reinterpret_cast<float*>(smem);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int unit = blockIdx.x;
   const int kvh = unit % a.Hkv;
   const uint32_t lane4 = (uint32_t)(lane & 31) << 2;
@@ -569,26 +627,19 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
 
   // (1) keys -> per-head logits in LDS (column 2h holds head h)
   const int n_tiles = ngp >> 4;
+  // lanes that hold no head's logits store into a dummy slot (no branch)
   const bool writer = !(c & 1) && (c >> 1) < a.G;
-  float* lw = logits + (c >> 1) * ngp + 4 * gq;
+  float* lw = writer ? logits + (c >> 1) * ngp + 4 * gq : dummy + 4 * lane;
   {
-    KeyTile A, B;
-    int t = wave;
-    if (t < n_tiles) load_keys<D>(rk, rkn, t, lane, A);
-    for (; t < n_tiles; t += 2 * kWaves) {
-      const int t1 = t + kWaves, t2 = t + 2 * kWaves;
-      if (t1 < n_tiles) load_keys<D>(rk, rkn, t1, lane, B);
-      {
-        const f32x4 acc = qk3<D>(A.kw, qh, ql, lut3, lane4);
-        if (writer) *reinterpret_cast<f32x4*>(lw + 16 * t) = acc * A.kn;
-      }
-      if (t1 >= n_tiles) break;
-      if (t2 < n_tiles) load_keys<D>(rk, rkn, t2, lane, A);
-      {
-        const f32x4 acc = qk3<D>(B.kw, qh, ql, lut3, lane4);
-        if (writer) *reinterpret_cast<f32x4*>(lw + 16 * t1) = acc * B.kn;
-      }
-    }
+    pipeline3<KeyTile>(
+        wave_iters(n_tiles, wave),
+        [&](int i, KeyTile& T) { load_keys<D>(rk, rkn, wave + i * kWaves, lane, T); },
+        [&](int i, const KeyTile& T) {
+          uint32_t kw[4];
+          key_bits<D>(T.kw, lane, kw);
+          const f32x4 acc = qk3<D>(kw, qh, ql, lut3, lane4);
+          *reinterpret_cast<f32x4*>(lw + (writer ? 16 * (wave + i * kWaves) : 0)) = acc * T.kn;
+        });
   }
   __syncthreads();
 
@@ -633,12 +684,14 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   st.init();
   const float* lrow = logits + min(c >> 1, a.G - 1) * ngp + 4 * gq;
   auto skip_of = [&](int t) -> uint32_t {  // rows 4gq+j of tile t fetched or past the end
-    const int g0 = 16 * t + 4 * gq;
+    const int g0 = 16 * max(min(t, n_tiles - 1), 0) + 4 * gq;
     const uint32_t fm = (fmask[g0 >> 5] >> (g0 & 31)) & 15u;  // g0 % 4 == 0: one word
+    if (t >= n_tiles) return 15u;
     const int valid = a.ng - g0;
     const uint32_t vm = valid >= 4 ? 15u : (valid <= 0 ? 0u : ((1u << valid) - 1u));
     return fm | (~vm & 15u);
   };
+  const uint32_t vsh = val_shift<D>(lane);
   auto consume = [&](int t, const ValTile& V, uint32_t skip) {
     const f32x4 lg4 = *reinterpret_cast<const f32x4*>(lrow + 16 * t);
     float lg[4], p[4];
@@ -652,30 +705,20 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
       p[i] *= V.vn[i];
     }
     st.l += psum;
-    pv3<D>(V.va, p, lane, lane4, lut3, st.O);
+    uint32_t va[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) va[j] = V.va[j] >> vsh;
+    pv3<D>(va, p, lane, lane4, lut3, st.O);
   };
   {
-    ValTile A, B;
-    uint32_t sa = 0, sb = 0;
-    int t = wave;
-    if (t < n_tiles) {
-      sa = skip_of(t);
-      load_vals<D>(rv, rvn, t, lane, sa, A);
-    }
-    for (; t < n_tiles; t += 2 * kWaves) {
-      const int t1 = t + kWaves, t2 = t + 2 * kWaves;
-      if (t1 < n_tiles) {
-        sb = skip_of(t1);
-        load_vals<D>(rv, rvn, t1, lane, sb, B);
-      }
-      consume(t, A, sa);
-      if (t1 >= n_tiles) break;
-      if (t2 < n_tiles) {
-        sa = skip_of(t2);
-        load_vals<D>(rv, rvn, t2, lane, sa, A);
-      }
-      consume(t1, B, sb);
-    }
+    pipeline3<ValTile>(
+        wave_iters(n_tiles, wave),
+        [&](int i, ValTile& V) {
+          const int t = wave + i * kWaves;
+          V.skip = skip_of(t);
+          load_vals<D>(rv, rvn, t, lane, V.skip, V);
+        },
+        [&](int i, const ValTile& V) { consume(wave + i * kWaves, V, V.skip); });
   }
   __syncthreads();  // the tables and logits are no longer needed: reuse as scratch
   combine_waves<D>(st, a.G, scratch, a.part + (size_t)unit * a.G * (D + 2), tid);
@@ -703,66 +746,62 @@ struct TokTile {
   uint32_t ok;     // bit i: row 4gq+i is a real token
 };
 
+struct TokRsrc {
+  rsrc_t l1k, l1kn, l1v, l1vn, l3;
+};
+
+// Tile t: L1 rows 16t .. 16t+15 for t < n1t, else the fetched archive groups
+// of tile t - n1t (N = 16: one group; N = 8: two).  Both kinds issue the same
+// loads in the same order; only the buffers (picked by the wave-uniform test)
+// and the per-lane offsets differ, so the loads sit in straight-line code.
 template <int D>
-__device__ __forceinline__ void load_tok(const TokArgs& a, rsrc_t r1k, rsrc_t r1kn, rsrc_t r1v,
-                                         rsrc_t r1vn, rsrc_t r3, const int32_t* sel, int t,
-                                         int n1t, int lane, TokTile& T) {
+__device__ __forceinline__ void load_tok(const TokArgs& a, const TokRsrc& R, const int32_t* sel,
+                                         int t, int n1t, int lane, TokTile& T) {
   constexpr int CB = D / 2;
+  constexpr uint32_t KB = D / 8;  // key code bytes per lane
   const int n = lane & 15, gq = lane >> 4;
-  if (t < n1t) {  // wave-uniform: L1 tile
-    const uint32_t r0 = (uint32_t)(16 * t);
-    if constexpr (D == 128) {
-      T.kw = ld128(r1k, (r0 + n) * CB + 16 * gq);
-    } else {
-      const u32x2 w = ld64(r1k, (r0 + n) * CB + 8 * gq);
-      T.kw = u32x4{w.x, w.y, 0u, 0u};
-    }
-    T.kn = ldf1x4(r1kn, (r0 + 4 * gq) * 4);
-    T.vn = ldf1x4(r1vn, (r0 + 4 * gq) * 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t row = (r0 + 4 * gq + j) * CB;
-      T.va[j] = (D == 128) ? ld32(r1v, row + 4 * n)
-                           : (ld32(r1v, row + 4 * (n >> 1)) >> (16 * (n & 1)));
-    }
-    const int valid = a.n1 - (int)(r0 + 4 * gq);
-    T.ok = valid >= 4 ? 15u : (valid <= 0 ? 0u : ((1u << valid) - 1u));
-    return;
-  }
-  // fetched groups: record = [K codes N*CB][K norms N*4][V codes N*CB][V norms N*4]
+  const bool l1 = t < n1t;
+  // archive record = [K codes N*CB][K norms N*4][V codes N*CB][V norms N*4]
   const int N = a.group_n;
   const uint32_t rec = (uint32_t)N * (D + 8);
   const int f = t - n1t;
   auto rec_off = [&](int slot) -> uint32_t {
-    if (slot >= a.beta) return kFar;
-    if (a.l3_staged) return (uint32_t)slot * rec;
-    const int g = sel[slot];
-    return (g >= 0 && g < a.ng) ? (uint32_t)g * rec : kFar;
+    const int g = a.l3_staged ? slot : sel[min(max(slot, 0), max(a.beta - 1, 0))];
+    const int lim = a.l3_staged ? a.beta : a.ng;
+    return (slot >= 0 && slot < a.beta && g >= 0 && g < lim) ? (uint32_t)g * rec : kFar;
   };
-  // key row n: slot and token within the group
+  // key row n: slot and token within the group; rows 4gq .. 4gq+3 lie in one
+  // group (N is a multiple of 4)
   const int sk = (N == 16) ? f : 2 * f + (n >> 3);
   const int tk = (N == 16) ? n : (n & 7);
-  const uint32_t bk = rec_off(sk);
-  if constexpr (D == 128) {
-    T.kw = ld128(r3, bk == kFar ? kFar : bk + tk * CB + 16 * gq);
-  } else {
-    const u32x2 w = ld64(r3, bk == kFar ? kFar : bk + tk * CB + 8 * gq);
-    T.kw = u32x4{w.x, w.y, 0u, 0u};
-  }
-  // rows 4gq .. 4gq+3 lie in one group (N is a multiple of 4)
   const int sr = (N == 16) ? f : 2 * f + (gq >> 1);
   const int tr = (N == 16) ? 4 * gq : 4 * (gq & 1);
-  const uint32_t br = rec_off(sr);
+  const uint32_t bk = rec_off(sk), br = rec_off(sr);
   const bool okr = br != kFar;
-  T.kn = ldf4(r3, okr ? br + N * CB + 4 * tr : kFar);
-  T.vn = ldf4(r3, okr ? br + N * (2 * CB + 4) + 4 * tr : kFar);
+  const uint32_t r0 = (uint32_t)(16 * t);
+  // an offset built on kFar stays past the end of every buffer (reads zero)
+  const uint32_t ko = l1 ? (r0 + n) * CB + KB * gq : bk + tk * CB + KB * gq;
+  const uint32_t kno = l1 ? (r0 + 4 * gq) * 4 : br + N * CB + 4 * tr;
+  const uint32_t vno = l1 ? (r0 + 4 * gq) * 4 : br + N * (2 * CB + 4) + 4 * tr;
+  const uint32_t vo = (l1 ? (r0 + 4 * gq) * CB : br + N * (CB + 4) + tr * CB) +
+                      ((D == 128) ? 4 * n : 4 * (n >> 1));
+  const rsrc_t rk = l1 ? R.l1k : R.l3, rkn = l1 ? R.l1kn : R.l3;
+  const rsrc_t rv = l1 ? R.l1v : R.l3, rvn = l1 ? R.l1vn : R.l3;
+  if constexpr (D == 128) {
+    T.kw = ld128(rk, ko);
+  } else {
+    const u32x2 w = ld64(rk, ko);
+    T.kw = u32x4{w.x, w.y, 0u, 0u};
+  }
+  T.kn = ldf1x4(rkn, kno);
+  T.vn = ldf1x4(rvn, vno);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t row = br + N * (CB + 4) + (tr + j) * CB;
-    T.va[j] = (D == 128) ? ld32(r3, okr ? row + 4 * n : kFar)
-                         : (ld32(r3, okr ? row + 4 * (n >> 1) : kFar) >> (16 * (n & 1)));
+    T.va[j] = ld32(rv, vo + j * CB);  // D = 64: consume_tok takes the lane's half
   }
-  T.ok = okr ? 15u : 0u;
+  const int valid = a.n1 - (int)(r0 + 4 * gq);
+  const uint32_t ok1 = valid >= 4 ? 15u : (valid <= 0 ? 0u : ((1u << valid) - 1u));
+  T.ok = l1 ? ok1 : (okr ? 15u : 0u);
 }
 
 template <int D>
@@ -790,11 +829,16 @@ __device__ __forceinline__ void consume_tok(const TokTile& T, const half8 (&qh)[
     p[i] *= T.vn[i];
   }
   st.l += psum;
-  pv4<D>(T.va, p, lane, lane4, lut4, st.O);
+  uint32_t va[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) va[j] = (D == 128) ? T.va[j] : (T.va[j] >> (16 * (lane & 1)));
+  pv4<D>(va, p, lane, lane4, lut4, st.O);
 }
 
+// at most 128 VGPRs so that two work-groups (the LDS limit) fit on a CU
 template <int D>
-__global__ __launch_bounds__(kThreads) void token_kernel(TokArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void token_kernel(TokArgs a) {
   constexpr int CB = D / 2;
   extern __shared__ __align__(16) char smem[];
   __shared__ float s_cb[16];
@@ -805,7 +849,7 @@ __global__ __launch_bounds__(kThreads) void token_kernel(TokArgs a) {
   int32_t* sel = reinterpret_cast<int32_t*>(qf + kMaxG * D);
   float* scratch = reinterpret_cast<float*>(smem);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int unit = blockIdx.x;
   const int kvh = unit % a.Hkv;
   const uint32_t lane4 = (uint32_t)lane << 2;
@@ -822,13 +866,13 @@ __global__ __launch_bounds__(kThreads) void token_kernel(TokArgs a) {
   __syncthreads();
 
   const size_t o1 = (size_t)unit * a.n1;
-  const rsrc_t r1k = make_rsrc(a.l1k + o1 * CB, (uint32_t)a.n1 * CB);
-  const rsrc_t r1kn = make_rsrc(a.l1k_n + o1, (uint32_t)a.n1 * 4);
-  const rsrc_t r1v = make_rsrc(a.l1v + o1 * CB, (uint32_t)a.n1 * CB);
-  const rsrc_t r1vn = make_rsrc(a.l1v_n + o1, (uint32_t)a.n1 * 4);
   const size_t rec = (size_t)a.group_n * (D + 8);
   const int recs = a.l3_staged ? a.beta : a.ng;
-  const rsrc_t r3 = make_rsrc(a.l3 + (size_t)unit * recs * rec, (uint32_t)(recs * rec));
+  const TokRsrc R{make_rsrc(a.l1k + o1 * CB, (uint32_t)a.n1 * CB),
+                  make_rsrc(a.l1k_n + o1, (uint32_t)a.n1 * 4),
+                  make_rsrc(a.l1v + o1 * CB, (uint32_t)a.n1 * CB),
+                  make_rsrc(a.l1v_n + o1, (uint32_t)a.n1 * 4),
+                  make_rsrc(a.l3 + (size_t)unit * recs * rec, (uint32_t)(recs * rec))};
 
   const int n1t = (a.n1 + 15) / 16;
   const int nft = (a.group_n == 16) ? a.beta : (a.beta + 1) / 2;
@@ -836,17 +880,12 @@ __global__ __launch_bounds__(kThreads) void token_kernel(TokArgs a) {
   Online<D> st;
   st.init();
   {
-    TokTile A, B;
-    int t = wave;
-    if (t < total) load_tok<D>(a, r1k, r1kn, r1v, r1vn, r3, sel, t, n1t, lane, A);
-    for (; t < total; t += 2 * kWaves) {
-      const int t1 = t + kWaves, t2 = t + 2 * kWaves;
-      if (t1 < total) load_tok<D>(a, r1k, r1kn, r1v, r1vn, r3, sel, t1, n1t, lane, B);
-      consume_tok<D>(A, qh, lut4, lane, lane4, st);
-      if (t1 >= total) break;
-      if (t2 < total) load_tok<D>(a, r1k, r1kn, r1v, r1vn, r3, sel, t2, n1t, lane, A);
-      consume_tok<D>(B, qh, lut4, lane, lane4, st);
-    }
+    pipeline3<TokTile>(
+        wave_iters(total, wave),
+        [&](int i, TokTile& T) {
+          load_tok<D>(a, R, sel, wave + i * kWaves, n1t, lane, T);
+        },
+        [&](int i, const TokTile& T) { consume_tok<D>(T, qh, lut4, lane, lane4, st); });
   }
   __syncthreads();  // the table is no longer needed: reuse as scratch
   float* mine = scratch + kWaves * kMaxG * (D + 2);  // [G][D+2] this unit's token partial
@@ -895,13 +934,14 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 size_t summary_smem(int D, const StepShape& s) {
   const size_t ngp = (size_t)((s.n_groups + 15) & ~15);
   const size_t body = 64 * kNC3 * 8 + (size_t)kMaxG * D * 4 + (size_t)s.G * ngp * 4 + ngp * 4 +
-                      256 * 4 + (size_t)((s.beta + 3) & ~3) * 4 + (ngp + 31) / 32 * 4;
+                      256 * 4 + (size_t)((s.beta + 3) & ~3) * 4 +
+                      (((ngp + 31) / 32 + 3) & ~size_t(3)) * 4 + 64 * 16;
   const size_t comb = (size_t)kWaves * kMaxG * (D + 2) * 4;
   return std::max(body, comb);
 }
 
 size_t token_smem(int D, const StepShape& s) {
-  const size_t body = 256 * kNC4 * 4 + (size_t)kMaxG * D * 4 + (size_t)s.beta * 4;
+  const size_t body = 256 * kNC4 * 4 + (size_t)kMaxG * D * 4 + (size_t)((s.beta + 4) & ~3) * 4;
   const size_t comb = (size_t)kWaves * kMaxG * (D + 2) * 4 + (size_t)kMaxG * (D + 2) * 4 +
                       (size_t)kMaxG * D * 4;
   return std::max(body, comb);
