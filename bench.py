@@ -29,6 +29,38 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "compressed_decode_attention_turboquant_amd", "csrc")
+# HBM byte counts of the step kernels, taken with rocprofv3 --pmc (text summary)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_step_kernels_qwen3-14b-16k.txt")
+STEP_SOURCES = ("step.hip", "hsq_device.h", "hsq_internal.h")
+
+
+def step_source_digest():
+    """sha256 over the sources the step kernels are built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in STEP_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """Calibrated HBM bytes per launch of `kernel` ("route" / "attend") from the
+    committed counter summary, or None when it is missing or was taken on other
+    kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            kv = dict(l.split(":", 1) for l in fh.read().splitlines()
+                      if ":" in l and not l.startswith("#"))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("step_source_sha256") != step_source_digest():
+        return None
+    v = kv.get(f"{kernel}_traffic_bytes")
+    return float(v) if v else None
 
 
 def parse():
@@ -41,6 +73,8 @@ def parse():
     p.add_argument("--no-codec", action="store_true")
     p.add_argument("--no-host", action="store_true", help="skip the pinned-host archive run")
     p.add_argument("--only-step", action="store_true", help="headline step only (for profiling)")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run a plain 1 GiB device copy (calibrates HBM byte counters)")
     return p.parse_args()
 
 
@@ -400,8 +434,16 @@ def main():
         "kernels": k,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": res["achieved"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": res["achieved"] / HBM_PEAK_GBS,
-                     "traffic": None},
+                     "traffic": measured_traffic(dom)},
     }
+    if args.calib_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["calib_copy_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
+        del src, dst
     if not args.only_step and not args.no_codec:
         line["codec"] = codec_rates(torch, hsq, W)
     if not args.only_step and not args.no_host:

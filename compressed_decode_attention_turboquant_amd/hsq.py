@@ -226,12 +226,13 @@ def build_tiers(k, v, l1_pos, group_pos, group_n, k_signs, v_signs, thr4, thr3, 
 
 
 class Workspace:
-    """Device workspace for the decode-step calls.  Zero-filled once at
-    creation; the calls leave their completion counters at zero again."""
+    """Device workspace for the decode-step calls (256-byte aligned).  It
+    carries the selection and the summary partials from the route launch to
+    the attend launch; it needs no initial contents."""
 
     def __init__(self, nbytes, device):
         self.nbytes = int(nbytes)
-        self.buf = torch.zeros(self.nbytes + 256, dtype=torch.uint8, device=device)
+        self.buf = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=device)
         off = (-self.buf.data_ptr()) % 256
         self.ptr = self.buf.data_ptr() + off
 

@@ -179,11 +179,11 @@ int hsq_build_tiers(const void* k, const void* v, int dtype, int B, int Hkv, int
  *   beta        >= 0, clamped to n_groups
  *   topk_idx    out int32 [B][Hkv][min(beta, n_groups)]
  *   scores      optional out fp32 [B][Hkv][n_groups] (NULL = not written)
- *   workspace   device, >= hsq_workspace_bytes(...) bytes, 256-byte aligned,
- *               zero-filled before its first use (the calls keep their
- *               completion counters at zero between calls; after an
- *               HSQ_ERR_HIP failure, zero it again).  Calls that share a
- *               workspace must be ordered on one stream.
+ *   workspace   device, >= hsq_workspace_bytes(...) bytes, 256-byte aligned;
+ *               holds the selection and the summary-attention partials
+ *               between the launches of one call.  No initial contents are
+ *               needed.  Calls that share a workspace must be ordered on one
+ *               stream.
  */
 int hsq_route_topk(const float* q, int B, int Hq, int Hkv, int d, const uint8_t* l2k,
                    const float* l2k_n, int n_groups, const uint32_t* k_signs, const float* cb3,
