@@ -68,6 +68,7 @@ constexpr int kMaxGroups = 16384;
 constexpr int kMaxLogits = 12288;        // G * n_groups kept in LDS
 constexpr uint32_t kFar = 0x80000000u;   // buffer offset that reads as zero
 constexpr float kNegInf = -INFINITY;
+constexpr float kPosInf = INFINITY;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
@@ -456,6 +457,105 @@ __device__ void top_beta(const uint32_t* keys, int ng, int beta, int* hist, int*
   __syncthreads();
 }
 
+// Inverse of fkey.
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Bucket of a score in 256 equal steps of [lo, hi]: a non-decreasing map of
+// the score, so a larger key never lands in a lower bucket.
+__device__ __forceinline__ int score_bucket(uint32_t key, float lo, float scale) {
+  const float b = (key_float(key) - lo) * scale;
+  return (int)fminf(fmaxf(b, 0.f), 255.f);
+}
+
+constexpr int kCandCap = 1024;  // candidates the bucket pass can rank
+
+// Top-beta by a score histogram, 0 < beta < ng.  Every bucket above the one
+// that holds the beta-th largest score is taken whole; the scores in that
+// bucket are ranked exactly by (key descending, index ascending), which is
+// the order of the full sort.  Sets the selected groups' bits in fmask (zero
+// on entry) and returns true, or returns false with fmask untouched when the
+// threshold bucket holds more than kCandCap scores.
+__device__ bool select_top_hist(const uint32_t* keys, int ng, int beta, float lo, float hi,
+                                int* hist, uint2* cand, uint32_t* fmask, int* st, int tid) {
+  const float scale = (hi > lo) ? 256.f / (hi - lo) : 0.f;
+  for (int g = tid; g < ng; g += kThreads) atomicAdd(&hist[score_bucket(keys[g], lo, scale)], 1);
+  __syncthreads();
+  if (tid < 64) {  // lane l owns buckets 255-4l .. 252-4l (descending)
+    int cnt[4], sum = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      cnt[k] = hist[255 - 4 * tid - k];
+      sum += cnt[k];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (tid >= o) incl += y;
+    }
+    const int excl = incl - sum;
+    if (excl < beta && incl >= beta) {
+      int acc = excl;
+      for (int k = 0; k < 4; ++k) {
+        if (acc + cnt[k] >= beta) {
+          st[0] = 255 - 4 * tid - k;  // threshold bucket
+          st[1] = beta - acc;         // how many of its scores to take
+          break;
+        }
+        acc += cnt[k];
+      }
+    }
+  }
+  __syncthreads();
+  const int bt = st[0], need = st[1];
+  if (hist[bt] > kCandCap) return false;  // uniform: every thread reads the same count
+  for (int g = tid; g < ng; g += kThreads) {
+    const uint32_t k = keys[g];
+    const int b = score_bucket(k, lo, scale);
+    if (b > bt) atomicOr(&fmask[g >> 5], 1u << (g & 31));
+    else if (b == bt) cand[atomicAdd(&st[2], 1)] = make_uint2((uint32_t)g, k);
+  }
+  __syncthreads();
+  const int nc = st[2];
+  for (int i = tid; i < nc; i += kThreads) {
+    const uint2 me = cand[i];
+    int rank = 0;
+    for (int j = 0; j < nc; ++j) {
+      const uint2 o = cand[j];
+      rank += (o.y > me.y) || (o.y == me.y && o.x < me.x);
+    }
+    if (rank < need) atomicOr(&fmask[me.x >> 5], 1u << (me.x & 31));
+  }
+  __syncthreads();
+  return true;
+}
+
+// Writes the set bits of fmask (the selection) as ascending group ids to
+// idx[0 .. count); run by one wave.
+__device__ void emit_selection(const uint32_t* fmask, int words, int32_t* idx, int lane) {
+  const int per = (words + 63) / 64;
+  const int w0 = min(lane * per, words), w1 = min(w0 + per, words);
+  int n = 0;
+  for (int w = w0; w < w1; ++w) n += __popc(fmask[w]);
+  int incl = n;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  int pos = incl - n;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t m = fmask[w];
+    while (m) {
+      const int b = __ffs(m) - 1;
+      idx[pos++] = 32 * w + b;
+      m &= m - 1u;
+    }
+  }
+}
+
 // -------------------------------------------------------- summary kernel ---
 
 struct SumArgs {
@@ -591,8 +691,11 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   extern __shared__ __align__(16) char smem[];
   __shared__ float s_cb[8];
   __shared__ int s_tmp[kWaves];
+  __shared__ int s_sel[4];
+  __shared__ float s_lo[kWaves], s_hi[kWaves];
   // layout: [lut3 16 KB][qf 8*D f32][logits G*ngp f32][keys ngp u32][hist 256]
-  //         [sel beta][fetched bitmap][dummy 64x4 f32]; the wave-combine
+  //         [fetched bitmap][dummy 64x4 f32][selection scratch: candidates
+  //         (uint2) or, in the fallback, the selected ids]; the wave-combine
   //         scratch reuses the front once the tiles are done.
   const int ngp = (a.ng + 15) & ~15;
   uint32_t* lut3 = reinterpret_cast<uint32_t*>(smem);
@@ -600,9 +703,10 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   float* logits = qf + kMaxG * D;
   uint32_t* keys = reinterpret_cast<uint32_t*>(logits + a.G * ngp);
   int* hist = reinterpret_cast<int*>(keys + ngp);
-  int32_t* sel = hist + 256;
-  uint32_t* fmask = reinterpret_cast<uint32_t*>(sel + ((a.beta + 3) & ~3));
+  uint32_t* fmask = reinterpret_cast<uint32_t*>(hist + 256);
   float* dummy = reinterpret_cast<float*>(fmask + (((ngp + 31) / 32 + 3) & ~3));  // [64][4]
+  uint2* cand = reinterpret_cast<uint2*>(dummy + 256);
+  int32_t* sel = reinterpret_cast<int32_t*>(cand);
   float* scratch = reinterpret_cast<float*>(smem);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -619,6 +723,8 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
                     a.scale * rsqrtf((float)D), qf, tid);
   const int words = (ngp + 31) >> 5;
   for (int w = tid; w < words; w += kThreads) fmask[w] = 0u;
+  for (int b = tid; b < 256; b += kThreads) hist[b] = 0;
+  if (tid < 4) s_sel[tid] = 0;
   __syncthreads();
   build_lut3(lut3, s_cb, tid);
   half8 qh[D / 32], ql[D / 32];
@@ -646,6 +752,7 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   // (2) router scores, top-beta, fetched bitmap
   if (a.want_topk) {
     const float inv_g = 1.f / (float)a.G;
+    float lo = kPosInf, hi = kNegInf;
     for (int g = tid; g < a.ng; g += kThreads) {
       float v = logits[g];
       if (a.agg == HSQ_AGG_MAX) {
@@ -655,19 +762,37 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
         v *= inv_g;
       }
       keys[g] = fkey(v);
+      lo = fminf(lo, v);
+      hi = fmaxf(hi, v);
       if (a.scores_out) a.scores_out[(size_t)unit * a.ng + g] = v;
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      lo = fminf(lo, __shfl_xor(lo, o, 64));
+      hi = fmaxf(hi, __shfl_xor(hi, o, 64));
+    }
+    if (lane == 0) {
+      s_lo[wave] = lo;
+      s_hi[wave] = hi;
+    }
     __syncthreads();
+    for (int w = 0; w < kWaves; ++w) {
+      lo = fminf(lo, s_lo[w]);
+      hi = fmaxf(hi, s_hi[w]);
+    }
     if (a.beta >= a.ng) {
-      for (int g = tid; g < a.ng; g += kThreads) sel[g] = g;
-      __syncthreads();
+      for (int w = tid; w < words; w += kThreads) {
+        const int left = a.ng - 32 * w;
+        fmask[w] = left >= 32 ? 0xffffffffu : (left <= 0 ? 0u : ((1u << left) - 1u));
+      }
     } else if (a.beta > 0) {
-      top_beta(keys, a.ng, a.beta, hist, s_tmp, sel, tid);
+      if (!select_top_hist(keys, a.ng, a.beta, lo, hi, hist, cand, fmask, s_sel, tid)) {
+        top_beta(keys, a.ng, a.beta, hist, s_tmp, sel, tid);
+        for (int i = tid; i < a.beta; i += kThreads) atomicOr(&fmask[sel[i] >> 5], 1u << (sel[i] & 31));
+      }
     }
-    for (int i = tid; i < a.beta; i += kThreads) {
-      a.idx[(size_t)unit * a.beta + i] = sel[i];
-      atomicOr(&fmask[sel[i] >> 5], 1u << (sel[i] & 31));
-    }
+    __syncthreads();
+    if (wave == 0) emit_selection(fmask, words, a.idx + (size_t)unit * a.beta, lane);
   } else if (a.given) {
     for (int i = tid; i < a.beta; i += kThreads) {
       const int g = a.given[(size_t)unit * a.beta + i];
@@ -934,8 +1059,8 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 size_t summary_smem(int D, const StepShape& s) {
   const size_t ngp = (size_t)((s.n_groups + 15) & ~15);
   const size_t body = 64 * kNC3 * 8 + (size_t)kMaxG * D * 4 + (size_t)s.G * ngp * 4 + ngp * 4 +
-                      256 * 4 + (size_t)((s.beta + 3) & ~3) * 4 +
-                      (((ngp + 31) / 32 + 3) & ~size_t(3)) * 4 + 64 * 16;
+                      256 * 4 + (((ngp + 31) / 32 + 3) & ~size_t(3)) * 4 + 64 * 16 +
+                      std::max((size_t)s.beta * 4, (size_t)std::min<size_t>(ngp, kCandCap) * 8);
   const size_t comb = (size_t)kWaves * kMaxG * (D + 2) * 4;
   return std::max(body, comb);
 }

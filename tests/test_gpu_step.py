@@ -30,9 +30,9 @@ DEV = "cuda"
 class Scenario:
     """One layer of a workload: raw inputs, GPU tiers and codebooks."""
 
-    def __init__(self, w, layer=0):
+    def __init__(self, w, layer=0, kv=None):
         self.w = w
-        self.k, self.v = W.kv(w, layer, DEV)
+        self.k, self.v = W.kv(w, layer, DEV) if kv is None else kv
         self.q = W.query(w, layer, DEV)
         self.ks, self.vs = W.signs(w.seed, layer, w.hkv, w.d)
         self.plans = [hsq.tier_plan(w.T, w.n_sink, w.n_recent, W.marked(w, b), w.group_n)
@@ -218,3 +218,36 @@ def test_repeated_calls_reuse_workspace():
     torch.cuda.synchronize()
     assert torch.equal(i1, i2)
     assert torch.equal(o1, o2)
+
+
+def _patterned_keys(w, n_pat):
+    """Raw keys whose group summaries take n_pat distinct values: position t
+    carries pattern (t // N) % n_pat of its (b, kv-head), so with N sinks, no
+    marks and no remainder every group is N copies of one pattern (its mean
+    is exact) and equal patterns give exactly equal router scores."""
+    k, v = W.kv(w, 0, DEV)
+    pat = torch.arange(w.T, device=DEV) // w.group_n % n_pat
+    base = k[:, :, :n_pat, :].clone()
+    return base[:, :, pat, :].contiguous(), v
+
+
+@pytest.mark.parametrize("case", ["five_patterns_2k", "five_patterns_20k", "all_equal_20k"])
+def test_route_exact_ties(case):
+    # exact ties go to the lower group index: the selection must equal the
+    # oracle's stable sort by (-score, index) exactly, with no near-tie slack
+    T = 2048 if case.endswith("2k") else 20480
+    w = W.QWEN3_8B_8K.smaller(T=T, batch=1, n_sink=16, n_recent=64, n_marked=0, beta=40)
+    n_pat = 1 if case.startswith("all_equal") else 5
+    print(f"exact ties {case}", flush=True)
+    sc = Scenario(w, kv=_patterned_keys(w, n_pat))
+    assert (w.T - w.n_sink - w.n_recent) % w.group_n == 0
+    idx, scores = hsq.route_topk(sc.q, sc.tiers, sc.dks, sc.cb3, w.beta, want_scores=True)
+    torch.cuda.synchronize()
+    for (b, h) in all_units(w):
+        unit, deq = sc.oracle_unit(b, h)
+        os_, _ = odec.route_scores(sc.q_unit(b, h), deq["l2k"], sc.scale, "max")
+        assert len(np.unique(os_)) == n_pat
+        osel = odec.top_beta(os_, w.beta)
+        gs = scores[b, h].cpu().numpy()
+        assert len(np.unique(gs)) == n_pat, "equal summaries must score exactly equal"
+        np.testing.assert_array_equal(idx[b, h].cpu().numpy(), osel, err_msg=f"unit {(b, h)}")
