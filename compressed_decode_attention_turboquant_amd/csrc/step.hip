@@ -109,32 +109,31 @@ __device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c) {
 }
 
 // Runs use(i, buf) for i in [0, iters) with each buffer's loads issued two
-// iterations before its use, so every wave keeps two tiles in flight.  load(i)
-// is also called for i >= iters; it must then read out of bounds (buffer loads
-// past num_records return zero without memory traffic).  iters is wave-uniform.
+// iterations before its use, so every wave keeps two tiles in flight.  The
+// caller has issued load(0, b0) and load(1, b1) (as early as it likes).
+// load(i) is also called for i >= iters; it must then read out of bounds
+// (buffer loads past num_records return zero without memory traffic).  iters
+// is wave-uniform.
 template <typename Buf, typename LoadF, typename UseF>
-__device__ __forceinline__ void pipeline3(int iters, LoadF load, UseF use) {
-  Buf b0, b1, b2;
-  load(0, b0);
-  load(1, b1);
-  // whole triples only: a loop body with no exit in the middle keeps the same
-  // number of loads in flight on every back edge, so the waits stay partial
-  int i = 0;
-  // the scheduling barriers keep the compiler from sinking the loads below
-  // the previous tile's arithmetic
-  for (; i + 3 <= iters; i += 3) {
+__device__ __forceinline__ void pipeline3(int iters, Buf& b0, Buf& b1, LoadF load, UseF use) {
+  Buf b2;
+  // Every pass issues all three loads (the ones past the end read nothing),
+  // so the number of loads in flight is the same on every path through the
+  // body and the waits stay partial; the trailing uses are skipped by
+  // wave-uniform tests instead of a second copy of the body.  The scheduling
+  // barriers keep the compiler from sinking the loads below the previous
+  // tile's arithmetic.
+  for (int i = 0; i < iters; i += 3) {
     load(i + 2, b2);
     __builtin_amdgcn_sched_barrier(0);
     use(i, b0);
     load(i + 3, b0);
     __builtin_amdgcn_sched_barrier(0);
-    use(i + 1, b1);
+    if (i + 1 < iters) use(i + 1, b1);
     load(i + 4, b1);
     __builtin_amdgcn_sched_barrier(0);
-    use(i + 2, b2);
+    if (i + 2 < iters) use(i + 2, b2);
   }
-  if (i < iters) use(i, b0);
-  if (i + 1 < iters) use(i + 1, b1);
 }
 
 // Wave index as a scalar (wave-uniform for the compiler).
@@ -145,15 +144,48 @@ __device__ __forceinline__ int wave_iters(int n_tiles, int wave) {
   return wave < n_tiles ? (n_tiles - wave + kWaves - 1) / kWaves : 0;
 }
 
+// Work-group barrier for LDS traffic only.  Every hand-over between the waves
+// of a work-group goes through LDS, so global loads still in flight (tiles
+// prefetched for the next phase) stay in flight across it; __syncthreads()
+// would wait for them.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Wave-wide maximum / minimum by DPP row operations (GFX9 row broadcasts);
+// the result is read from the last lane, so it is wave-uniform.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_f(float x) {
+  const int v = __float_as_int(x);
+  return __int_as_float(__builtin_amdgcn_update_dpp(v, v, CTRL, ROWS, 0xf, false));
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f<0xb1>(x));        // quad_perm 1,0,3,2
+  x = fmaxf(x, dpp_f<0x4e>(x));        // quad_perm 2,3,0,1
+  x = fmaxf(x, dpp_f<0x141>(x));       // row_half_mirror
+  x = fmaxf(x, dpp_f<0x140>(x));       // row_mirror
+  x = fmaxf(x, dpp_f<0x142, 0xa>(x));  // row_bcast:15
+  x = fmaxf(x, dpp_f<0x143, 0xc>(x));  // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+__device__ __forceinline__ float wave_min(float x) { return -wave_max(-x); }
+
 // ---------------------------------------------------------------- tables ---
+//
+// The dequantisation tables live in static LDS, so their base folds into the
+// ds_read offset field and a lookup costs one address instruction.
 
 // 4-bit: byte b (codes b & 15, b >> 4) -> fp16 pair; copy l at dword b*64 + l,
 // so lane l's address is (b << 8) | (l << 2): one v_perm from the code dword.
 __device__ void build_lut4(uint32_t* lut, const float* cb, int tid) {
-  for (int i = tid; i < 256 * kNC4; i += kThreads) {
-    const int e = i / kNC4;
-    lut[i] = h2u((_Float16)cb[e & 15], (_Float16)cb[e >> 4]);
-  }
+  // thread t fills copies 32(t&1) .. 32(t&1)+31 of entry t/2
+  const int e = tid >> 1;
+  const uint32_t v = h2u((_Float16)cb[e & 15], (_Float16)cb[e >> 4]);
+  u32x4* dst = reinterpret_cast<u32x4*>(lut + e * kNC4 + 32 * (tid & 1));
+#pragma unroll
+  for (int k = 0; k < 8; ++k) dst[k] = u32x4{v, v, v, v};
 }
 // byte K of w as a table address for this lane
 template <int K>
@@ -161,59 +193,74 @@ __device__ __forceinline__ uint32_t lut4_addr(uint32_t w, uint32_t lane4) {
   // bytes of {lane4 (sel 4..7), w (sel 0..3)}: result = [lane4.b0, w.bK, 0, 0]
   return __builtin_amdgcn_perm(lane4, w, 0x0c0c0004u | (uint32_t(K) << 8));
 }
-__device__ __forceinline__ uint32_t lut4_rd(const uint32_t* lut, uint32_t addr) {
-  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(lut) + addr);
+__device__ __forceinline__ uint32_t lds_at(const uint32_t* base, uint32_t byte_addr) {
+  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(base) + byte_addr);
 }
 
-// 3-bit: 6-bit field e (codes e & 7, e >> 3) -> hi fp16 pair at lut[e*32 + l%32]
-// and lo fp16 pair 64*32 dwords further (same address + 8 KB), c = hi + lo to
-// ~2^-22 relative.
+// 3-bit: 6-bit field e (codes e & 7, e >> 3) -> hi fp16 pair at dword
+// e*32 + l%32 and lo fp16 pair at kLut3Lo + e*32 + l%32, c = hi + lo to ~2^-22
+// relative.  The lo table sits 16 bytes past a multiple of 256 bytes from the
+// hi table so that the compiler cannot fuse a hi and a lo read into one
+// two-dword read (whose results would land in adjacent registers and need
+// moves to form the MFMA operands).
+constexpr int kLut3Lo = 64 * kNC3 + 4;
 __device__ void build_lut3(uint32_t* lut, const float* cb, int tid) {
-  for (int i = tid; i < 64 * kNC3; i += kThreads) {
-    const int e = i / kNC3;
-    const float c0 = cb[e & 7], c1 = cb[e >> 3];
-    const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
-    const _Float16 l0 = (_Float16)(c0 - (float)h0), l1 = (_Float16)(c1 - (float)h1);
-    lut[i] = h2u(h0, h1);
-    lut[64 * kNC3 + i] = h2u(l0, l1);
-  }
+  // thread t fills copies 4(t&7) .. 4(t&7)+3 of entry t/8 in both tables
+  const int e = tid >> 3;
+  const float c0 = cb[e & 7], c1 = cb[e >> 3];
+  const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
+  const _Float16 l0 = (_Float16)(c0 - (float)h0), l1 = (_Float16)(c1 - (float)h1);
+  const uint32_t hv = h2u(h0, h1), lv = h2u(l0, l1);
+  *reinterpret_cast<u32x4*>(lut + e * kNC3 + 4 * (tid & 7)) = u32x4{hv, hv, hv, hv};
+  *reinterpret_cast<u32x4*>(lut + kLut3Lo + e * kNC3 + 4 * (tid & 7)) = u32x4{lv, lv, lv, lv};
 }
+// table address of 6-bit field e for this lane (lane4 = (lane & 31) << 2)
 __device__ __forceinline__ uint32_t lut3_addr(uint32_t e, uint32_t lane4) {
-  return (e << 7) | lane4;  // lane4 = (lane & 31) << 2
-}
-__device__ __forceinline__ uint32_t lut3_hi(const uint32_t* lut, uint32_t addr) {
-  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(lut) + addr);
-}
-__device__ __forceinline__ uint32_t lut3_lo(const uint32_t* lut, uint32_t addr) {
-  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(lut) + addr +
-                                            64 * kNC3 * 4);
+  return (e << 7) | lane4;
 }
 
 // -------------------------------------------------------- query rotation ---
 
-// qf[h][i] = mult * (H D q_h)[i] for h < G, 0 for G <= h < 8, on the first
-// 8*D/8 threads (whole waves).
+// Query rotation in two steps so that its global loads can be issued with
+// the first tile loads: load_query, then rotate_query writes
+// qf[h*QS + i] = mult * (H D q_h)[i] for h < G and 0 for G <= h < 8.  Both run
+// on the first 8*D/8 threads (whole waves).  Rows are padded to QS = D + 4
+// floats so that the 16-byte operand reads of different heads fall in
+// different LDS banks.
 template <int D>
-__device__ void rotate_queries(const float* q, const uint32_t* mask, int G, float mult, float* qf,
-                               int tid) {
+constexpr int kQS = D + 4;
+struct QueryIn {
+  float v[8];
+  uint32_t sb;
+};
+template <int D>
+__device__ __forceinline__ void load_query(const float* q, const uint32_t* mask, int G, int tid,
+                                           QueryIn& Q) {
+  constexpr int LPV = D / 8;
+  const int h = tid / LPV, sub = tid % LPV;
+  if (tid < kMaxG * LPV && h < G) {
+    const float4* p = reinterpret_cast<const float4*>(q + h * D + 8 * sub);
+    const float4 a = p[0], b = p[1];
+    Q.v[0] = a.x; Q.v[1] = a.y; Q.v[2] = a.z; Q.v[3] = a.w;
+    Q.v[4] = b.x; Q.v[5] = b.y; Q.v[6] = b.z; Q.v[7] = b.w;
+    Q.sb = sign_byte(mask, sub);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) Q.v[k] = 0.f;
+    Q.sb = 0u;
+  }
+}
+template <int D>
+__device__ __forceinline__ void rotate_query(QueryIn& Q, float mult, float* qf, int tid) {
   constexpr int LPV = D / 8;
   if (tid < kMaxG * LPV) {
     const int h = tid / LPV, sub = tid % LPV;
-    float v[8];
-    if (h < G) {
-      const float4* p = reinterpret_cast<const float4*>(q + h * D + 8 * sub);
-      const float4 a = p[0], b = p[1];
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-      const uint32_t sb = sign_byte(mask, sub);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = flip(v[k], (sb >> k) & 1u);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = 0.f;
-    }
-    fwht8xlanes<LPV>(v, sub);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) qf[h * D + 8 * sub + k] = v[k] * mult;
+    for (int k = 0; k < 8; ++k) Q.v[k] = flip(Q.v[k], (Q.sb >> k) & 1u);
+    fwht8xlanes<LPV>(Q.v, sub);
+    f32x4* dst = reinterpret_cast<f32x4*>(qf + h * kQS<D> + 8 * sub);
+    dst[0] = f32x4{Q.v[0], Q.v[1], Q.v[2], Q.v[3]} * mult;
+    dst[1] = f32x4{Q.v[4], Q.v[5], Q.v[6], Q.v[7]} * mult;
   }
 }
 
@@ -223,11 +270,13 @@ template <int D>
 __device__ void query_operands(const float* qf, int lane, half8 (&hi)[D / 32],
                                half8 (&lo)[D / 32]) {
   const int c = lane & 15, gq = lane >> 4, h = c >> 1;
+  const f32x4* src = reinterpret_cast<const f32x4*>(qf + h * kQS<D> + gq * (D / 4));
 #pragma unroll
   for (int m = 0; m < D / 32; ++m) {
+    const f32x4 x0 = src[2 * m], x1 = src[2 * m + 1];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float x = qf[h * D + gq * (D / 4) + 8 * m + j];
+      const float x = (j < 4) ? x0[j] : x1[j - 4];
       const _Float16 xh = (_Float16)x;
       hi[m][j] = xh;
       lo[m][j] = (_Float16)(x - (float)xh);
@@ -237,47 +286,68 @@ __device__ void query_operands(const float* qf, int lane, half8 (&hi)[D / 32],
 
 // ---------------------------------------------------------- online softmax ---
 
+constexpr float kLog2e = 1.4426950408889634f;
+// A logit may exceed the running reference maximum by this much (natural
+// log units) before the state is rescaled: weights stay <= e^4, well inside
+// fp16 even after multiplication by a value norm.
+constexpr float kLazy = 4.f;
+
+// Softmax state of one lane: reference maximum m of its column (equal on the
+// 4 row groups), its share l of the denominator (its 4 rows), and the MFMA
+// accumulators O of the value product.
 template <int D>
-struct Online {
-  float m;   // running max of this lane's column (equal on the 4 row groups)
-  float l;   // this lane's share of the denominator (its 4 rows)
+struct Softmax {
+  float m, mL;  // mL = m * log2(e)
+  float l;
   f32x4 O[D / 32];
-  __device__ void init() {
-    m = kNegInf;
+  __device__ void init(float m0) {
+    m = m0;
+    mL = m0 * kLog2e;
     l = 0.f;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // Fold in 4 logits of this lane (rows 4gq+i); p = exp(lg - m_new).
+  // p_i = exp(lg_i - m)
+  __device__ __forceinline__ void weights(const float (&lg)[4], float (&p)[4]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(lg[i], kLog2e, -mL));
+  }
+  // Fold in 4 logits of this lane (rows 4gq+i) with a lazily moved maximum:
+  // the state is rescaled only when some column's tile maximum exceeds its
+  // reference by more than kLazy (rare once the first tiles are in).
   __device__ __forceinline__ void update(const float (&lg)[4], float (&p)[4]) {
     float mt = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float mn = fmaxf(m, mt);
-    const float ms = (mn == kNegInf) ? 0.f : mn;
-    // rescale only when some column's running max moved (wave-uniform branch)
-    if (__builtin_amdgcn_ballot_w64(mn > m)) {
-      const float alpha = (mn > m) ? __expf(m - ms) : 1.f;
+    const bool up = mt > m + kLazy;
+    if (__builtin_amdgcn_ballot_w64(up)) {  // wave-uniform branch
+      const float mn = up ? mt : m;
+      const float alpha = (m == kNegInf) ? 0.f : __expf(m - mn);
       l *= alpha;
 #pragma unroll
       for (int t = 0; t < D / 32; ++t) O[t] *= alpha;
+      m = mn;
+      mL = mn * kLog2e;
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __expf(lg[i] - ms);
-    m = mn;
+    weights(lg, p);
   }
 };
 
-// PV with 4-bit values: va[j] = this lane's value bits of token 4gq+j, p[j] =
-// weight (times the value norm) of token 4gq+j for this lane's column (h, e').
-template <int D>
-__device__ __forceinline__ void pv4(const uint32_t (&va)[4], const float (&p)[4], int lane,
-                                    uint32_t lane4, const uint32_t* lut4, f32x4 (&O)[D / 32]) {
+// B operand of the value products from 4 weights of this lane's column
+// (h, e'): token 4gq+j, element e' of each dimension pair.
+__device__ __forceinline__ half8 weight_operand(const float (&w)[4], int lane) {
   const uint32_t sh = (lane & 1) ? 16u : 0u;
   uint32_t pb[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) pb[j] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)p[j]) << sh;
-  const half8 b = as_h8(pb[0], pb[1], pb[2], pb[3]);
+  for (int j = 0; j < 4; ++j) pb[j] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)w[j]) << sh;
+  return as_h8(pb[0], pb[1], pb[2], pb[3]);
+}
+
+// PV with 4-bit values: va[j] = this lane's value bits of token 4gq+j (low
+// bytes first); b = weight operand.
+template <int D>
+__device__ __forceinline__ void pv4(const uint32_t (&va)[4], half8 b, uint32_t lane4,
+                                    const uint32_t* lut4, f32x4 (&O)[D / 32]) {
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) {
     uint32_t a[4];
@@ -288,26 +358,23 @@ __device__ __forceinline__ void pv4(const uint32_t (&va)[4], const float (&p)[4]
       else if (t == 1) addr = lut4_addr<1>(va[j], lane4);
       else if (t == 2) addr = lut4_addr<2>(va[j], lane4);
       else addr = lut4_addr<3>(va[j], lane4);
-      a[j] = lut4_rd(lut4, addr);
+      a[j] = lds_at(lut4, addr);
     }
     O[t] = mfma16(as_h8(a[0], a[1], a[2], a[3]), b, O[t]);
   }
 }
 
-// PV with 3-bit values (hi part of the table; V needs no split).
+// PV with 3-bit values (hi table only: V needs no split).  va[j]: this lane's
+// value bits of token 4gq+j start at bit `sh`.
 template <int D>
-__device__ __forceinline__ void pv3(const uint32_t (&va)[4], const float (&p)[4], int lane,
-                                    uint32_t lane4, const uint32_t* lut3, f32x4 (&O)[D / 32]) {
-  const uint32_t sh = (lane & 1) ? 16u : 0u;
-  uint32_t pb[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) pb[j] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)p[j]) << sh;
-  const half8 b = as_h8(pb[0], pb[1], pb[2], pb[3]);
+__device__ __forceinline__ void pv3(const uint32_t (&va)[4], uint32_t sh, half8 b, uint32_t lane4,
+                                    const uint32_t* lut3, f32x4 (&O)[D / 32]) {
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) {
     uint32_t a[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) a[j] = lut3_hi(lut3, lut3_addr((va[j] >> (6 * t)) & 63u, lane4));
+    for (int j = 0; j < 4; ++j)
+      a[j] = lds_at(lut3, lut3_addr(__builtin_amdgcn_ubfe(va[j], sh + 6 * t, 6), lane4));
     O[t] = mfma16(as_h8(a[0], a[1], a[2], a[3]), b, O[t]);
   }
 }
@@ -315,7 +382,7 @@ __device__ __forceinline__ void pv3(const uint32_t (&va)[4], const float (&p)[4]
 // Combine the waves' states; result per head written to dst[h][D+2] as
 // [m, l, O[0..D)] (dst may be LDS or global).  scratch: kWaves*kMaxG*(D+2) floats.
 template <int D>
-__device__ void combine_waves(const Online<D>& st, int G, float* scratch, float* dst, int tid) {
+__device__ void combine_waves(const Softmax<D>& st, int G, float* scratch, float* dst, int tid) {
   const int lane = tid & 63, wave = tid >> 6, c = lane & 15, gq = lane >> 4;
   float l = st.l;
   l += __shfl_xor(l, 16, 64);
@@ -333,7 +400,7 @@ __device__ void combine_waves(const Online<D>& st, int G, float* scratch, float*
 #pragma unroll
       for (int i = 0; i < 4; ++i) w[2 + 2 * (T * (4 * gq + i) + t) + (c & 1)] = st.O[t][i];
   }
-  __syncthreads();
+  lds_barrier();
   for (int k = tid; k < G * (D + 2); k += kThreads) {
     const int hh = k / (D + 2), e = k % (D + 2);
     float M = kNegInf;
@@ -350,7 +417,7 @@ __device__ void combine_waves(const Online<D>& st, int G, float* scratch, float*
     }
     dst[k] = (e == 0) ? M : acc;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // ------------------------------------------------------------ top-beta ------
@@ -371,10 +438,10 @@ __device__ int block_exclusive_scan(int v, int* tmp, int tid) {
     if (lane >= o) x += y;
   }
   if (lane == 63) tmp[wave] = x;
-  __syncthreads();
+  lds_barrier();
   int base = 0;
   for (int w = 0; w < wave; ++w) base += tmp[w];
-  __syncthreads();
+  lds_barrier();
   return base + x - v;
 }
 
@@ -391,16 +458,16 @@ __device__ void top_beta(const uint32_t* keys, int ng, int beta, int* hist, int*
     s_mask = 0u;
     s_need = beta;
   }
-  __syncthreads();
+  lds_barrier();
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int b = tid; b < 256; b += kThreads) hist[b] = 0;
-    __syncthreads();
+    lds_barrier();
     const uint32_t pre = s_prefix, msk = s_mask;
     for (int g = tid; g < ng; g += kThreads) {
       const uint32_t k = keys[g];
       if ((k & msk) == pre) atomicAdd(&hist[(k >> shift) & 255u], 1);
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < 64) {
       // lane l owns bins 255-4l .. 252-4l (descending order)
       int cnt[4], sum = 0;
@@ -431,7 +498,7 @@ __device__ void top_beta(const uint32_t* keys, int ng, int beta, int* hist, int*
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
   const uint32_t kth = s_prefix;
   const int ties_needed = s_need;  // keys equal to kth to take
@@ -454,7 +521,7 @@ __device__ void top_beta(const uint32_t* keys, int ng, int beta, int* hist, int*
     if (k == kth) take = (e++ < ties_needed);
     if (take) sel[pos++] = g;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // Inverse of fkey.
@@ -471,69 +538,56 @@ __device__ __forceinline__ int score_bucket(uint32_t key, float lo, float scale)
 
 constexpr int kCandCap = 1024;  // candidates the bucket pass can rank
 
-// Top-beta by a score histogram, 0 < beta < ng.  Every bucket above the one
-// that holds the beta-th largest score is taken whole; the scores in that
-// bucket are ranked exactly by (key descending, index ascending), which is
-// the order of the full sort.  Sets the selected groups' bits in fmask (zero
-// on entry) and returns true, or returns false with fmask untouched when the
-// threshold bucket holds more than kCandCap scores.
-__device__ bool select_top_hist(const uint32_t* keys, int ng, int beta, float lo, float hi,
-                                int* hist, uint2* cand, uint32_t* fmask, int* st, int tid) {
-  const float scale = (hi > lo) ? 256.f / (hi - lo) : 0.f;
-  for (int g = tid; g < ng; g += kThreads) atomicAdd(&hist[score_bucket(keys[g], lo, scale)], 1);
-  __syncthreads();
-  if (tid < 64) {  // lane l owns buckets 255-4l .. 252-4l (descending)
-    int cnt[4], sum = 0;
+// Top-beta by a score histogram (0 < beta < ng).  The scores are bucketed
+// over [lo, hi] (any bounds of the scores) in 256 equal steps; every bucket
+// above the one holding the beta-th largest score is taken whole, and the
+// scores of that bucket are ranked exactly by (key descending, index
+// ascending), which is the order of the full sort.
+
+// The threshold bucket and how many of its scores to take, from the full
+// histogram; every wave computes it (no barrier needed).
+__device__ __forceinline__ void hist_threshold(const int* hist, int beta, int lane, int& bt,
+                                               int& need) {
+  int cnt[4], sum = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      cnt[k] = hist[255 - 4 * tid - k];
-      sum += cnt[k];
-    }
-    int incl = sum;
+  for (int k = 0; k < 4; ++k) {  // lane l owns buckets 255-4l .. 252-4l
+    cnt[k] = hist[255 - 4 * lane - k];
+    sum += cnt[k];
+  }
+  int incl = sum;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, 64);
-      if (tid >= o) incl += y;
-    }
-    const int excl = incl - sum;
-    if (excl < beta && incl >= beta) {
-      int acc = excl;
-      for (int k = 0; k < 4; ++k) {
-        if (acc + cnt[k] >= beta) {
-          st[0] = 255 - 4 * tid - k;  // threshold bucket
-          st[1] = beta - acc;         // how many of its scores to take
-          break;
-        }
-        acc += cnt[k];
-      }
-    }
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
   }
-  __syncthreads();
-  const int bt = st[0], need = st[1];
-  if (hist[bt] > kCandCap) return false;  // uniform: every thread reads the same count
-  for (int g = tid; g < ng; g += kThreads) {
-    const uint32_t k = keys[g];
-    const int b = score_bucket(k, lo, scale);
-    if (b > bt) atomicOr(&fmask[g >> 5], 1u << (g & 31));
-    else if (b == bt) cand[atomicAdd(&st[2], 1)] = make_uint2((uint32_t)g, k);
-  }
-  __syncthreads();
-  const int nc = st[2];
-  for (int i = tid; i < nc; i += kThreads) {
-    const uint2 me = cand[i];
-    int rank = 0;
-    for (int j = 0; j < nc; ++j) {
-      const uint2 o = cand[j];
-      rank += (o.y > me.y) || (o.y == me.y && o.x < me.x);
+  int my_bt = 0, my_need = 0, acc = incl - sum;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (acc < beta && acc + cnt[k] >= beta) {
+      my_bt = 255 - 4 * lane - k;
+      my_need = beta - acc;
     }
-    if (rank < need) atomicOr(&fmask[me.x >> 5], 1u << (me.x & 31));
+    acc += cnt[k];
   }
-  __syncthreads();
-  return true;
+  const int src = __ffsll((unsigned long long)__builtin_amdgcn_ballot_w64(my_need > 0)) - 1;
+  bt = __builtin_amdgcn_readlane(my_bt, src);
+  need = __builtin_amdgcn_readlane(my_need, src);
 }
 
-// Writes the set bits of fmask (the selection) as ascending group ids to
-// idx[0 .. count); run by one wave.
+// Candidate i (i < nc) of the threshold bucket is selected iff fewer than
+// `need` candidates precede it in (key desc, index asc) order.
+__device__ __forceinline__ bool cand_selected(const uint2* cand, int nc, int need, uint2 me) {
+  int rank = 0;
+#pragma unroll 8
+  for (int j = 0; j < nc; ++j) {
+    const uint2 o = cand[j];
+    rank += (o.y > me.y) || (o.y == me.y && o.x < me.x);
+  }
+  return rank < need;
+}
+
+// Writes the set bits of fmask as ascending group ids to idx[0 .. count);
+// run by one wave.
 __device__ void emit_selection(const uint32_t* fmask, int words, int32_t* idx, int lane) {
   const int per = (words + 63) / 64;
   const int w0 = min(lane * per, words), w1 = min(w0 + per, words);
@@ -549,8 +603,7 @@ __device__ void emit_selection(const uint32_t* fmask, int words, int32_t* idx, i
   for (int w = w0; w < w1; ++w) {
     uint32_t m = fmask[w];
     while (m) {
-      const int b = __ffs(m) - 1;
-      idx[pos++] = 32 * w + b;
+      idx[pos++] = 32 * w + __ffs(m) - 1;
       m &= m - 1u;
     }
   }
@@ -577,36 +630,36 @@ template <int BIT>
 __device__ __forceinline__ uint32_t field6(const uint32_t* w) {
   constexpr int k = BIT >> 5, s = BIT & 31;
   if constexpr (s <= 26) {
-    return (w[k] >> s) & 63u;
+    return __builtin_amdgcn_ubfe(w[k], s, 6);
   } else {
     return __builtin_amdgcn_alignbit(w[k + 1], w[k], s) & 63u;
   }
 }
 
-template <int D, int P>
-__device__ __forceinline__ void key3_pairs(const uint32_t* kw, const uint32_t* lut, uint32_t lane4,
-                                           uint32_t (&hi)[D / 8], uint32_t (&lo)[D / 8]) {
-  if constexpr (P < D / 8) {
-    const uint32_t a = lut3_addr(field6<6 * P>(kw), lane4);
-    hi[P] = lut3_hi(lut, a);
-    lo[P] = lut3_lo(lut, a);
-    key3_pairs<D, P + 1>(kw, lut, lane4, hi, lo);
-  }
-}
-
-// QK of 16 summaries: three-term split product.  kw: this lane's 3D/4 key bits
-// (summary lane&15, dims gq*D/4 ..) from bit 0.
+// QK of 16 summaries: three-term split product q_hi c_hi + q_lo c_hi +
+// q_hi c_lo (fp32-accurate scores).  kw: this lane's 3D/4 key bits (summary
+// lane&15, dims gq*D/4 ..) from bit 0.  Every table read goes straight into
+// its operand register.
 template <int D>
-__device__ __forceinline__ f32x4 qk3(const uint32_t (&kw)[4], const half8 (&qh)[D / 32],
+__device__ __forceinline__ f32x4 qk3(const uint32_t (&kw)[3], const half8 (&qh)[D / 32],
                                      const half8 (&ql)[D / 32], const uint32_t* lut,
                                      uint32_t lane4) {
-  uint32_t hi[D / 8], lo[D / 8];
-  key3_pairs<D, 0>(kw, lut, lane4, hi, lo);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  uint32_t a[D / 8];
+#define HSQ_FIELD_ADDR(P) a[P] = lut3_addr(field6<6 * (P)>(kw), lane4)
+  HSQ_FIELD_ADDR(0); HSQ_FIELD_ADDR(1); HSQ_FIELD_ADDR(2); HSQ_FIELD_ADDR(3);
+  HSQ_FIELD_ADDR(4); HSQ_FIELD_ADDR(5); HSQ_FIELD_ADDR(6); HSQ_FIELD_ADDR(7);
+  if constexpr (D == 128) {
+    HSQ_FIELD_ADDR(8); HSQ_FIELD_ADDR(9); HSQ_FIELD_ADDR(10); HSQ_FIELD_ADDR(11);
+    HSQ_FIELD_ADDR(12); HSQ_FIELD_ADDR(13); HSQ_FIELD_ADDR(14); HSQ_FIELD_ADDR(15);
+  }
+#undef HSQ_FIELD_ADDR
 #pragma unroll
   for (int m = 0; m < D / 32; ++m) {
-    const half8 ah = as_h8(hi[4 * m], hi[4 * m + 1], hi[4 * m + 2], hi[4 * m + 3]);
-    const half8 al = as_h8(lo[4 * m], lo[4 * m + 1], lo[4 * m + 2], lo[4 * m + 3]);
+    const half8 ah = as_h8(lds_at(lut, a[4 * m]), lds_at(lut, a[4 * m + 1]),
+                           lds_at(lut, a[4 * m + 2]), lds_at(lut, a[4 * m + 3]));
+    const half8 al = as_h8(lds_at(lut + kLut3Lo, a[4 * m]), lds_at(lut + kLut3Lo, a[4 * m + 1]),
+                           lds_at(lut + kLut3Lo, a[4 * m + 2]), lds_at(lut + kLut3Lo, a[4 * m + 3]));
     acc = mfma16(ah, qh[m], acc);
     acc = mfma16(ah, ql[m], acc);
     acc = mfma16(al, qh[m], acc);
@@ -614,10 +667,11 @@ __device__ __forceinline__ f32x4 qk3(const uint32_t (&kw)[4], const half8 (&qh)[
   return acc;
 }
 
-// Keys of tile t (16 summaries): this lane's key bits and the key norms of rows
-// 4gq .. 4gq+3.
+// Keys of tile t (16 summaries): this lane's raw key words (D = 128: 96 bits
+// at byte 12gq of row lane&15; D = 64: 64 bits from the dword holding bit
+// 48gq, aligned by key_bits) and the key norms of rows 4gq .. 4gq+3.
 struct KeyTile {
-  uint32_t kw[4];
+  uint32_t kw[3];
   f32x4 kn;
 };
 template <int D>
@@ -625,37 +679,35 @@ __device__ __forceinline__ void load_keys(rsrc_t rk, rsrc_t rn, int t, int lane,
   constexpr int CB3 = 3 * D / 8;
   const int n = lane & 15, gq = lane >> 4;
   const uint32_t row = (uint32_t)(16 * t + n) * CB3;
-  if constexpr (D == 128) {  // 96 bits at byte 12*gq
+  if constexpr (D == 128) {
     const u32x3 w = ld96(rk, row + 12 * gq);
-    T.kw[0] = w.x; T.kw[1] = w.y; T.kw[2] = w.z; T.kw[3] = 0u;
-  } else {                   // 48 bits at bit 48*gq: raw dwords, aligned by key_bits
+    T.kw[0] = w.x; T.kw[1] = w.y; T.kw[2] = w.z;
+  } else {
     const u32x2 w = ld64(rk, row + 4 * ((3 * gq) >> 1));
-    T.kw[0] = w.x; T.kw[1] = w.y; T.kw[2] = 0u; T.kw[3] = 0u;
+    T.kw[0] = w.x; T.kw[1] = w.y; T.kw[2] = 0u;
   }
   T.kn = ldf1x4(rn, (uint32_t)(16 * t + 4 * gq) * 4);
 }
-
 // This lane's key bits from the words load_keys left (the loads stay free of
 // arithmetic so that no wait is forced before the tile is used).
 template <int D>
-__device__ __forceinline__ void key_bits(const uint32_t (&w)[4], int lane, uint32_t (&kw)[4]) {
+__device__ __forceinline__ void key_bits(const uint32_t (&w)[3], int lane, uint32_t (&kw)[3]) {
   if constexpr (D == 128) {
-    kw[0] = w[0]; kw[1] = w[1]; kw[2] = w[2]; kw[3] = 0u;
+    kw[0] = w[0]; kw[1] = w[1]; kw[2] = w[2];
   } else {
     const uint32_t s = ((lane >> 4) & 1) ? 16u : 0u;
     kw[0] = __builtin_amdgcn_alignbit(w[1], w[0], s);
     kw[1] = w[1] >> s;
-    kw[2] = 0u; kw[3] = 0u;
+    kw[2] = 0u;
   }
 }
 
 // Values of tile t: the dword of row 4gq+j that holds this lane's value bits
-// (dims [2T*rho, 2T*rho + 2T), T = D/32; shifted into place by the consumer)
-// and the rows' norms; rows flagged in `skip` read as zero.
+// (dims [2T*rho, 2T*rho + 2T), T = D/32; the bits start at val_shift) and the
+// rows' norms.
 struct ValTile {
   uint32_t va[4];
   f32x4 vn;
-  uint32_t skip;
 };
 // The dword holding this lane's value bits starts at byte min(bit/8, RB-4)
 // (so it never crosses the end of the row; buffer loads need only byte
@@ -672,16 +724,12 @@ __device__ __forceinline__ uint32_t val_shift(int lane) {
   return (uint32_t)(BITS * (lane & 15)) - 8u * val_byte<D>(lane);
 }
 template <int D>
-__device__ __forceinline__ void load_vals(rsrc_t rv, rsrc_t rvn, int t, int lane, uint32_t skip,
-                                          ValTile& T) {
+__device__ __forceinline__ void load_vals(rsrc_t rv, rsrc_t rvn, int t, int lane, ValTile& T) {
   constexpr int RB = 3 * D / 8;
   const int gq = lane >> 4;
-  const uint32_t wofs = val_byte<D>(lane);
+  const uint32_t base = (uint32_t)(16 * t + 4 * gq) * RB + val_byte<D>(lane);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t row = (uint32_t)(16 * t + 4 * gq + j) * RB;
-    T.va[j] = ld32(rv, ((skip >> j) & 1u) ? kFar : row + wofs);
-  }
+  for (int j = 0; j < 4; ++j) T.va[j] = ld32(rv, base + j * RB);
   T.vn = ldf1x4(rvn, (uint32_t)(16 * t + 4 * gq) * 4);
 }
 
@@ -689,25 +737,27 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   constexpr int CB3 = 3 * D / 8;
   extern __shared__ __align__(16) char smem[];
+  __shared__ __align__(16) uint32_t s_lut3[kLut3Lo + 64 * kNC3];
   __shared__ float s_cb[8];
   __shared__ int s_tmp[kWaves];
   __shared__ int s_sel[4];
   __shared__ float s_lo[kWaves], s_hi[kWaves];
-  // layout: [lut3 16 KB][qf 8*D f32][logits G*ngp f32][keys ngp u32][hist 256]
-  //         [fetched bitmap][dummy 64x4 f32][selection scratch: candidates
-  //         (uint2) or, in the fallback, the selected ids]; the wave-combine
-  //         scratch reuses the front once the tiles are done.
+  __shared__ float s_mh[kWaves][kMaxG];
+  // dynamic layout: [qf 8*(D+4) f32][logits G*ngp f32][keys ngp u32][hist 256]
+  //   [fetched bitmap][selection scratch: candidates (uint2) or, in the
+  //   fallback, the selected ids].  qf doubles as the landing slot of the
+  //   phase-1 stores of lanes that hold no head; the wave-combine scratch
+  //   reuses the front once the tiles are done.
   const int ngp = (a.ng + 15) & ~15;
-  uint32_t* lut3 = reinterpret_cast<uint32_t*>(smem);
-  float* qf = reinterpret_cast<float*>(smem + 64 * kNC3 * 8);
-  float* logits = qf + kMaxG * D;
+  float* qf = reinterpret_cast<float*>(smem);
+  float* logits = qf + kMaxG * kQS<D>;
   uint32_t* keys = reinterpret_cast<uint32_t*>(logits + a.G * ngp);
-  int* hist = reinterpret_cast<int*>(keys + ngp);
+  int* hist = reinterpret_cast<int*>(keys + ((ngp + 31) & ~31));
   uint32_t* fmask = reinterpret_cast<uint32_t*>(hist + 256);
-  float* dummy = reinterpret_cast<float*>(fmask + (((ngp + 31) / 32 + 3) & ~3));  // [64][4]
-  uint2* cand = reinterpret_cast<uint2*>(dummy + 256);
+  uint2* cand = reinterpret_cast<uint2*>(fmask + (((ngp + 31) / 32 + 3) & ~3));
   int32_t* sel = reinterpret_cast<int32_t*>(cand);
   float* scratch = reinterpret_cast<float*>(smem);
+  const uint32_t* lut3 = s_lut3;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int unit = blockIdx.x;
@@ -717,135 +767,210 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
 
   const rsrc_t rk = make_rsrc(a.l2k + (size_t)unit * a.ng * CB3, (uint32_t)a.ng * CB3);
   const rsrc_t rkn = make_rsrc(a.l2k_n + (size_t)unit * a.ng, (uint32_t)a.ng * 4);
+  const rsrc_t rv = make_rsrc(a.l2v + (size_t)unit * a.ng * CB3, (uint32_t)a.ng * CB3);
+  const rsrc_t rvn = make_rsrc(a.l2v_n + (size_t)unit * a.ng, (uint32_t)a.ng * 4);
 
-  if (tid < 8) s_cb[tid] = a.cb3[tid];
-  rotate_queries<D>(a.q + (size_t)unit * a.G * D, a.k_signs + kvh * (D / 32), a.G,
-                    a.scale * rsqrtf((float)D), qf, tid);
+  // global loads first: the set-up inputs, then the first two key tiles of
+  // this wave, whose latency the set-up arithmetic below then overlaps
+  const float cbv = (tid < 8) ? a.cb3[tid] : 0.f;
+  QueryIn qin;
+  load_query<D>(a.q + (size_t)unit * a.G * D, a.k_signs + kvh * (D / 32), a.G, tid, qin);
+  KeyTile kt0, kt1;
+  load_keys<D>(rk, rkn, wave, lane, kt0);
+  load_keys<D>(rk, rkn, wave + kWaves, lane, kt1);
+
+  if (tid < 8) s_cb[tid] = cbv;
+  rotate_query<D>(qin, a.scale * rsqrtf((float)D), qf, tid);
   const int words = (ngp + 31) >> 5;
   for (int w = tid; w < words; w += kThreads) fmask[w] = 0u;
   for (int b = tid; b < 256; b += kThreads) hist[b] = 0;
   if (tid < 4) s_sel[tid] = 0;
-  __syncthreads();
-  build_lut3(lut3, s_cb, tid);
+  lds_barrier();
+  build_lut3(s_lut3, s_cb, tid);
   half8 qh[D / 32], ql[D / 32];
   query_operands<D>(qf, lane, qh, ql);
-  __syncthreads();
+  lds_barrier();
 
   // (1) keys -> per-head logits in LDS (column 2h holds head h)
   const int n_tiles = ngp >> 4;
   // lanes that hold no head's logits store into a dummy slot (no branch)
   const bool writer = !(c & 1) && (c >> 1) < a.G;
-  float* lw = writer ? logits + (c >> 1) * ngp + 4 * gq : dummy + 4 * lane;
+  float* lw = writer ? logits + (c >> 1) * ngp + 4 * gq : qf + 4 * lane;
+  float blo = kPosInf, bhi = kNegInf;
   {
     pipeline3<KeyTile>(
-        wave_iters(n_tiles, wave),
+        wave_iters(n_tiles, wave), kt0, kt1,
         [&](int i, KeyTile& T) { load_keys<D>(rk, rkn, wave + i * kWaves, lane, T); },
         [&](int i, const KeyTile& T) {
-          uint32_t kw[4];
+          uint32_t kw[3];
           key_bits<D>(T.kw, lane, kw);
-          const f32x4 acc = qk3<D>(kw, qh, ql, lut3, lane4);
-          *reinterpret_cast<f32x4*>(lw + (writer ? 16 * (wave + i * kWaves) : 0)) = acc * T.kn;
+          const f32x4 lg = qk3<D>(kw, qh, ql, lut3, lane4) * T.kn;
+          *reinterpret_cast<f32x4*>(lw + (writer ? 16 * (wave + i * kWaves) : 0)) = lg;
+          // bounds of every score (max or mean over heads of these logits)
+          blo = fminf(blo, fminf(fminf(lg[0], lg[1]), fminf(lg[2], lg[3])));
+          bhi = fmaxf(bhi, fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])));
         });
   }
-  __syncthreads();
+  blo = wave_min(blo);
+  bhi = wave_max(bhi);
+  if (lane == 0) {
+    s_lo[wave] = blo;
+    s_hi[wave] = bhi;
+  }
+  // the first two value tiles of this wave load while the selection runs
+  ValTile vt0, vt1;
+  if (a.want_partial) {
+    load_vals<D>(rv, rvn, wave, lane, vt0);
+    load_vals<D>(rv, rvn, wave + kWaves, lane, vt1);
+  }
+  lds_barrier();
 
-  // (2) router scores, top-beta, fetched bitmap
-  if (a.want_topk) {
-    const float inv_g = 1.f / (float)a.G;
-    float lo = kPosInf, hi = kNegInf;
-    for (int g = tid; g < a.ng; g += kThreads) {
-      float v = logits[g];
-      if (a.agg == HSQ_AGG_MAX) {
-        for (int h = 1; h < a.G; ++h) v = fmaxf(v, logits[h * ngp + g]);
-      } else {
-        for (int h = 1; h < a.G; ++h) v += logits[h * ngp + g];
-        v *= inv_g;
-      }
-      keys[g] = fkey(v);
-      lo = fminf(lo, v);
-      hi = fmaxf(hi, v);
-      if (a.scores_out) a.scores_out[(size_t)unit * a.ng + g] = v;
-    }
+  // (2) router scores, per-head maxima, score histogram: thread t takes
+  // groups 4t .. 4t+3 (+2048 per pass), one 16-byte read per head
+  const bool hsel = a.want_topk && a.beta > 0 && a.beta < a.ng;
+  float lo = kPosInf, hi = kNegInf;
+  for (int w = 0; w < kWaves; ++w) {
+    lo = fminf(lo, s_lo[w]);
+    hi = fmaxf(hi, s_hi[w]);
+  }
+  const float bscale = (hi > lo) ? 256.f / (hi - lo) : 0.f;
+  float mh[kMaxG];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      lo = fminf(lo, __shfl_xor(lo, o, 64));
-      hi = fmaxf(hi, __shfl_xor(hi, o, 64));
-    }
-    if (lane == 0) {
-      s_lo[wave] = lo;
-      s_hi[wave] = hi;
-    }
-    __syncthreads();
-    for (int w = 0; w < kWaves; ++w) {
-      lo = fminf(lo, s_lo[w]);
-      hi = fmaxf(hi, s_hi[w]);
-    }
-    if (a.beta >= a.ng) {
-      for (int w = tid; w < words; w += kThreads) {
-        const int left = a.ng - 32 * w;
-        fmask[w] = left >= 32 ? 0xffffffffu : (left <= 0 ? 0u : ((1u << left) - 1u));
-      }
-    } else if (a.beta > 0) {
-      if (!select_top_hist(keys, a.ng, a.beta, lo, hi, hist, cand, fmask, s_sel, tid)) {
-        top_beta(keys, a.ng, a.beta, hist, s_tmp, sel, tid);
-        for (int i = tid; i < a.beta; i += kThreads) atomicOr(&fmask[sel[i] >> 5], 1u << (sel[i] & 31));
+  for (int h = 0; h < kMaxG; ++h) mh[h] = kNegInf;
+  const float inv_g = 1.f / (float)a.G;
+  for (int g0 = 4 * tid; g0 < 32 * words; g0 += 4 * kThreads) {
+    f32x4 vmax = {kNegInf, kNegInf, kNegInf, kNegInf}, vsum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < kMaxG; ++h) {
+      if (h < a.G) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(logits + h * ngp + g0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float xe = (g0 + e < a.ng) ? x[e] : kNegInf;
+          mh[h] = fmaxf(mh[h], xe);
+          vmax[e] = fmaxf(vmax[e], xe);
+          vsum[e] += x[e];
+        }
       }
     }
-    __syncthreads();
-    if (wave == 0) emit_selection(fmask, words, a.idx + (size_t)unit * a.beta, lane);
-  } else if (a.given) {
+    if (a.want_topk) {
+      u32x4 k4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = g0 + e < a.ng;
+        const float v = (a.agg == HSQ_AGG_MAX) ? vmax[e] : vsum[e] * inv_g;
+        k4[e] = ok ? fkey(v) : 0u;
+        if (ok) {
+          if (hsel) atomicAdd(&hist[score_bucket(k4[e], lo, bscale)], 1);
+          if (a.scores_out) a.scores_out[(size_t)unit * a.ng + g0 + e] = v;
+        }
+      }
+      *reinterpret_cast<u32x4*>(keys + g0) = k4;
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < kMaxG; ++h)
+    if (h < a.G) mh[h] = wave_max(mh[h]);
+  if (lane == 0)
+#pragma unroll
+    for (int h = 0; h < kMaxG; ++h) s_mh[wave][h] = mh[h];
+  if (a.want_topk && a.beta >= a.ng) {  // every group fetched
+    for (int w = tid; w < words; w += kThreads) {
+      const int left = a.ng - 32 * w;
+      fmask[w] = left >= 32 ? 0xffffffffu : (left <= 0 ? 0u : ((1u << left) - 1u));
+    }
+  } else if (!a.want_topk && a.given) {  // the given selection
     for (int i = tid; i < a.beta; i += kThreads) {
       const int g = a.given[(size_t)unit * a.beta + i];
       if (g >= 0 && g < a.ng) atomicOr(&fmask[g >> 5], 1u << (g & 31));
     }
   }
-  __syncthreads();
+  lds_barrier();
+
+  // buckets above the threshold -> fetched bitmap; threshold bucket ->
+  // candidate list (both from every thread's own groups)
+  int bt = 0, need = 0;
+  bool fallback = false;
+  if (hsel) {
+    hist_threshold(hist, a.beta, lane, bt, need);
+    fallback = hist[bt] > kCandCap;  // the same on every thread
+    if (!fallback) {
+      for (int g = tid; g < a.ng; g += kThreads) {
+        const uint32_t k = keys[g];
+        const int b = score_bucket(k, lo, bscale);
+        if (b > bt) atomicOr(&fmask[g >> 5], 1u << (g & 31));
+        else if (b == bt) cand[atomicAdd(&s_sel[2], 1)] = make_uint2((uint32_t)g, k);
+      }
+    } else {  // more ties in one bucket than the ranking takes: radix select
+      top_beta(keys, a.ng, a.beta, hist, s_tmp, sel, tid);
+      for (int i = tid; i < a.beta; i += kThreads) atomicOr(&fmask[sel[i] >> 5], 1u << (sel[i] & 31));
+    }
+  }
+  lds_barrier();
+
+  // every wave: the selected candidates (ranked redundantly per wave), then
+  // the fetched groups and padding rows of its own tiles leave the summary
+  // softmax (the tiles' logits are read by this wave only, so no barrier)
+  const int nc = (hsel && !fallback) ? s_sel[2] : 0;
+  if (a.want_partial) {
+    const int my_tiles = wave_iters(n_tiles, wave);
+    for (int i = lane; i < my_tiles; i += 64) {
+      const int t = wave + i * kWaves;
+      uint32_t bits = (fmask[t >> 1] >> (16 * (t & 1))) & 0xffffu;
+      const int valid = a.ng - 16 * t;
+      if (valid < 16) bits |= (0xffffu << max(valid, 0)) & 0xffffu;
+      while (bits) {
+        const int g = 16 * t + __ffs(bits) - 1;
+        for (int h = 0; h < a.G; ++h) logits[h * ngp + g] = kNegInf;
+        bits &= bits - 1u;
+      }
+    }
+    for (int i = lane; i < nc; i += 64) {
+      const uint2 me = cand[i];
+      const int t = (int)(me.x >> 4);
+      if (t % kWaves == wave && cand_selected(cand, nc, need, me))
+        for (int h = 0; h < a.G; ++h) logits[h * ngp + me.x] = kNegInf;
+    }
+  }
+  if (wave == 0 && a.want_topk) {
+    for (int i = lane; i < nc; i += 64) {
+      const uint2 me = cand[i];
+      if (cand_selected(cand, nc, need, me)) atomicOr(&fmask[me.x >> 5], 1u << (me.x & 31));
+    }
+    emit_selection(fmask, words, a.idx + (size_t)unit * a.beta, lane);
+  }
   if (!a.want_partial) return;
 
-  // (3) values of the unfetched summaries -> partial
-  const rsrc_t rv = make_rsrc(a.l2v + (size_t)unit * a.ng * CB3, (uint32_t)a.ng * CB3);
-  const rsrc_t rvn = make_rsrc(a.l2v_n + (size_t)unit * a.ng, (uint32_t)a.ng * 4);
-  Online<D> st;
-  st.init();
-  const float* lrow = logits + min(c >> 1, a.G - 1) * ngp + 4 * gq;
-  auto skip_of = [&](int t) -> uint32_t {  // rows 4gq+j of tile t fetched or past the end
-    const int g0 = 16 * max(min(t, n_tiles - 1), 0) + 4 * gq;
-    const uint32_t fm = (fmask[g0 >> 5] >> (g0 & 31)) & 15u;  // g0 % 4 == 0: one word
-    if (t >= n_tiles) return 15u;
-    const int valid = a.ng - g0;
-    const uint32_t vm = valid >= 4 ? 15u : (valid <= 0 ? 0u : ((1u << valid) - 1u));
-    return fm | (~vm & 15u);
-  };
+  // (3) values of the unfetched summaries -> partial.  The maximum of every
+  // head's logits is known, so the weights need no running rescale.
+  const int hcol = min(c >> 1, a.G - 1);
+  float m0 = kNegInf;
+  for (int w = 0; w < kWaves; ++w) m0 = fmaxf(m0, s_mh[w][hcol]);
+  Softmax<D> st;
+  st.init(m0 + a.bias);  // every weight exp(logit + bias - m) <= 1
+  const float* lrow = logits + hcol * ngp + 4 * gq;
   const uint32_t vsh = val_shift<D>(lane);
-  auto consume = [&](int t, const ValTile& V, uint32_t skip) {
-    const f32x4 lg4 = *reinterpret_cast<const f32x4*>(lrow + 16 * t);
-    float lg[4], p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lg[i] = ((skip >> i) & 1u) ? kNegInf : lg4[i] + a.bias;
-    st.update(lg, p);
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      psum += p[i];
-      p[i] *= V.vn[i];
-    }
-    st.l += psum;
-    uint32_t va[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) va[j] = V.va[j] >> vsh;
-    pv3<D>(va, p, lane, lane4, lut3, st.O);
-  };
   {
     pipeline3<ValTile>(
-        wave_iters(n_tiles, wave),
-        [&](int i, ValTile& V) {
+        wave_iters(n_tiles, wave), vt0, vt1,
+        [&](int i, ValTile& V) { load_vals<D>(rv, rvn, wave + i * kWaves, lane, V); },
+        [&](int i, const ValTile& V) {
           const int t = wave + i * kWaves;
-          V.skip = skip_of(t);
-          load_vals<D>(rv, rvn, t, lane, V.skip, V);
-        },
-        [&](int i, const ValTile& V) { consume(wave + i * kWaves, V, V.skip); });
+          const f32x4 lg4 = *reinterpret_cast<const f32x4*>(lrow + 16 * t);
+          float lg[4], p[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) lg[r] = lg4[r] + a.bias;
+          st.weights(lg, p);
+          float w[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            st.l += p[r];
+            w[r] = p[r] * V.vn[r];
+          }
+          pv3<D>(V.va, vsh, weight_operand(w, lane), lane4, lut3, st.O);
+        });
   }
-  __syncthreads();  // the tables and logits are no longer needed: reuse as scratch
+  lds_barrier();  // the logits are no longer needed: reuse as scratch
   combine_waves<D>(st, a.G, scratch, a.part + (size_t)unit * a.G * (D + 2), tid);
 }
 
@@ -871,47 +996,56 @@ struct TokTile {
   uint32_t ok;     // bit i: row 4gq+i is a real token
 };
 
-struct TokRsrc {
+// Per-unit buffers of the token tiles.  Tile t < n1t holds L1 rows 16t ..
+// 16t+15; tile n1t + f holds the fetched archive groups of slot f (N = 16) or
+// of slots 2f, 2f+1 (N = 8, rows n < 8 and n >= 8).  Archive record =
+// [K codes N*CB][K norms N*4][V codes N*CB][V norms N*4].
+struct TokBufs {
   rsrc_t l1k, l1kn, l1v, l1vn, l3;
 };
 
-// Tile t: L1 rows 16t .. 16t+15 for t < n1t, else the fetched archive groups
-// of tile t - n1t (N = 16: one group; N = 8: two).  Both kinds issue the same
-// loads in the same order; only the buffers (picked by the wave-uniform test)
-// and the per-lane offsets differ, so the loads sit in straight-line code.
-template <int D>
-__device__ __forceinline__ void load_tok(const TokArgs& a, const TokRsrc& R, const int32_t* sel,
-                                         int t, int n1t, int lane, TokTile& T) {
+template <int D, int N>
+__device__ __forceinline__ TokBufs tok_bufs(const TokArgs& a, int unit) {
+  constexpr int CB = D / 2;
+  const size_t o1 = (size_t)unit * a.n1;
+  const size_t rec = (size_t)N * (D + 8);
+  const int recs = a.l3_staged ? a.beta : a.ng;
+  TokBufs B;
+  B.l1k = make_rsrc(a.l1k + o1 * CB, (uint32_t)a.n1 * CB);
+  B.l1kn = make_rsrc(a.l1k_n + o1, (uint32_t)a.n1 * 4);
+  B.l1v = make_rsrc(a.l1v + o1 * CB, (uint32_t)a.n1 * CB);
+  B.l1vn = make_rsrc(a.l1v_n + o1, (uint32_t)a.n1 * 4);
+  B.l3 = make_rsrc(a.l3 + (size_t)unit * recs * rec, (uint32_t)(recs * rec));
+  return B;
+}
+
+// recoff[s]: byte offset of slot s's record in the unit's archive buffer, or
+// kFar (reads zero) for a slot without a valid group; recoff[beta] = kFar.
+// Loads of tile t: straight-line code for both kinds (the wave-uniform kind
+// picks the buffers, per-lane selects pick the offsets).
+template <int D, int N>
+__device__ __forceinline__ void load_tok(const TokBufs& B, const int32_t* recoff, int t, int n1t,
+                                         int n1, int beta, int lane, TokTile& T) {
   constexpr int CB = D / 2;
   constexpr uint32_t KB = D / 8;  // key code bytes per lane
   const int n = lane & 15, gq = lane >> 4;
+  const int tk = (N == 16) ? n : (n & 7);            // key row within the group
+  const int tr = (N == 16) ? 4 * gq : 4 * (gq & 1);  // first value row within the group
+  const uint32_t vl = (D == 128) ? 4u * n : 4u * (n >> 1);  // this lane's value dword
   const bool l1 = t < n1t;
-  // archive record = [K codes N*CB][K norms N*4][V codes N*CB][V norms N*4]
-  const int N = a.group_n;
-  const uint32_t rec = (uint32_t)N * (D + 8);
   const int f = t - n1t;
-  auto rec_off = [&](int slot) -> uint32_t {
-    const int g = a.l3_staged ? slot : sel[min(max(slot, 0), max(a.beta - 1, 0))];
-    const int lim = a.l3_staged ? a.beta : a.ng;
-    return (slot >= 0 && slot < a.beta && g >= 0 && g < lim) ? (uint32_t)g * rec : kFar;
-  };
-  // key row n: slot and token within the group; rows 4gq .. 4gq+3 lie in one
-  // group (N is a multiple of 4)
-  const int sk = (N == 16) ? f : 2 * f + (n >> 3);
-  const int tk = (N == 16) ? n : (n & 7);
-  const int sr = (N == 16) ? f : 2 * f + (gq >> 1);
-  const int tr = (N == 16) ? 4 * gq : 4 * (gq & 1);
-  const uint32_t bk = rec_off(sk), br = rec_off(sr);
-  const bool okr = br != kFar;
-  const uint32_t r0 = (uint32_t)(16 * t);
+  const int s0 = (N == 16) ? f : 2 * f;
+  const int xk = (N == 16) ? 0 : (n >> 3), xr = (N == 16) ? 0 : (gq >> 1);
+  const uint32_t bk = (uint32_t)recoff[min(max(s0 + xk, 0), beta)];
+  const uint32_t br = (uint32_t)recoff[min(max(s0 + xr, 0), beta)];
+  const uint32_t r0 = 16u * (uint32_t)t;
   // an offset built on kFar stays past the end of every buffer (reads zero)
   const uint32_t ko = l1 ? (r0 + n) * CB + KB * gq : bk + tk * CB + KB * gq;
   const uint32_t kno = l1 ? (r0 + 4 * gq) * 4 : br + N * CB + 4 * tr;
   const uint32_t vno = l1 ? (r0 + 4 * gq) * 4 : br + N * (2 * CB + 4) + 4 * tr;
-  const uint32_t vo = (l1 ? (r0 + 4 * gq) * CB : br + N * (CB + 4) + tr * CB) +
-                      ((D == 128) ? 4 * n : 4 * (n >> 1));
-  const rsrc_t rk = l1 ? R.l1k : R.l3, rkn = l1 ? R.l1kn : R.l3;
-  const rsrc_t rv = l1 ? R.l1v : R.l3, rvn = l1 ? R.l1vn : R.l3;
+  const uint32_t vo = (l1 ? (r0 + 4 * gq) * CB : br + N * (CB + 4) + tr * CB) + vl;
+  const rsrc_t rk = l1 ? B.l1k : B.l3, rkn = l1 ? B.l1kn : B.l3;
+  const rsrc_t rv = l1 ? B.l1v : B.l3, rvn = l1 ? B.l1vn : B.l3;
   if constexpr (D == 128) {
     T.kw = ld128(rk, ko);
   } else {
@@ -921,123 +1055,135 @@ __device__ __forceinline__ void load_tok(const TokArgs& a, const TokRsrc& R, con
   T.kn = ldf1x4(rkn, kno);
   T.vn = ldf1x4(rvn, vno);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    T.va[j] = ld32(rv, vo + j * CB);  // D = 64: consume_tok takes the lane's half
-  }
-  const int valid = a.n1 - (int)(r0 + 4 * gq);
+  for (int j = 0; j < 4; ++j) T.va[j] = ld32(rv, vo + j * CB);
+  const int valid = n1 - (int)(r0 + 4 * gq);
   const uint32_t ok1 = valid >= 4 ? 15u : (valid <= 0 ? 0u : ((1u << valid) - 1u));
-  T.ok = l1 ? ok1 : (okr ? 15u : 0u);
+  T.ok = l1 ? ok1 : (br != kFar ? 15u : 0u);
 }
 
 template <int D>
 __device__ __forceinline__ void consume_tok(const TokTile& T, const half8 (&qh)[D / 32],
                                             const uint32_t* lut4, int lane, uint32_t lane4,
-                                            Online<D>& st) {
+                                            Softmax<D>& st) {
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int m = 0; m < D / 32; ++m) {
     const uint32_t w = T.kw[m];
-    const half8 av = as_h8(lut4_rd(lut4, lut4_addr<0>(w, lane4)),
-                           lut4_rd(lut4, lut4_addr<1>(w, lane4)),
-                           lut4_rd(lut4, lut4_addr<2>(w, lane4)),
-                           lut4_rd(lut4, lut4_addr<3>(w, lane4)));
+    const half8 av = as_h8(lds_at(lut4, lut4_addr<0>(w, lane4)), lds_at(lut4, lut4_addr<1>(w, lane4)),
+                           lds_at(lut4, lut4_addr<2>(w, lane4)), lds_at(lut4, lut4_addr<3>(w, lane4)));
     acc = mfma16(av, qh[m], acc);
   }
   float lg[4], p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) lg[i] = ((T.ok >> i) & 1u) ? acc[i] * T.kn[i] : kNegInf;
   st.update(lg, p);
-  float psum = 0.f;
+  float w[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    psum += p[i];
-    p[i] *= T.vn[i];
+    st.l += p[i];
+    w[i] = p[i] * T.vn[i];
   }
-  st.l += psum;
   uint32_t va[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) va[j] = (D == 128) ? T.va[j] : (T.va[j] >> (16 * (lane & 1)));
-  pv4<D>(va, p, lane, lane4, lut4, st.O);
+  pv4<D>(va, weight_operand(w, lane), lane4, lut4, st.O);
 }
 
 // at most 128 VGPRs so that two work-groups (the LDS limit) fit on a CU
-template <int D>
+template <int D, int N>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void token_kernel(TokArgs a) {
-  constexpr int CB = D / 2;
   extern __shared__ __align__(16) char smem[];
+  __shared__ __align__(16) uint32_t s_lut4[256 * kNC4];
   __shared__ float s_cb[16];
-  // layout: [lut4 64 KB][qf 8*D f32][sel beta]; the combine scratch reuses the
-  // front once the tiles are done.
-  uint32_t* lut4 = reinterpret_cast<uint32_t*>(smem);
-  float* qf = reinterpret_cast<float*>(smem + 256 * kNC4 * 4);
-  int32_t* sel = reinterpret_cast<int32_t*>(qf + kMaxG * D);
-  float* scratch = reinterpret_cast<float*>(smem);
+  __shared__ uint32_t s_vsb[kMaxG * (D / 8)];
+  // dynamic layout: [qf 8*(D+4) f32][summary partial 8*(D+2) f32][recoff beta+1];
+  // the combine scratch reuses the table once the tiles are done.
+  const uint32_t* lut4 = s_lut4;
+  float* qf = reinterpret_cast<float*>(smem);
+  float* part = qf + kMaxG * kQS<D>;
+  int32_t* recoff = reinterpret_cast<int32_t*>(part + kMaxG * (D + 2));
+  float* scratch = reinterpret_cast<float*>(s_lut4);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int unit = blockIdx.x;
   const int kvh = unit % a.Hkv;
   const uint32_t lane4 = (uint32_t)lane << 2;
+  const TokBufs B = tok_bufs<D, N>(a, unit);
+  const int n1t = (a.n1 + 15) / 16;
+  const int nft = (N == 16) ? a.beta : (a.beta + 1) / 2;
+  const int total = n1t + nft;
+  const size_t rec = (size_t)N * (D + 8);
+  constexpr int LPV = D / 8;
 
-  if (tid < 16) s_cb[tid] = a.cb4[tid];
-  if (!a.l3_staged)
-    for (int i = tid; i < a.beta; i += kThreads) sel[i] = a.idx[(size_t)unit * a.beta + i];
-  rotate_queries<D>(a.q + (size_t)unit * a.G * D, a.k_signs + kvh * (D / 32), a.G,
-                    a.scale * rsqrtf((float)D), qf, tid);
-  __syncthreads();
-  build_lut4(lut4, s_cb, tid);
+  // global loads first: the set-up inputs and the summary partial merged at
+  // the end; the record offsets are needed before the first archive tile
+  const float cbv = (tid < 16) ? a.cb4[tid] : 0.f;
+  QueryIn qin;
+  load_query<D>(a.q + (size_t)unit * a.G * D, a.k_signs + kvh * (D / 32), a.G, tid, qin);
+  const uint32_t vsb = (tid < kMaxG * LPV) ? sign_byte(a.v_signs + kvh * (D / 32), tid % LPV) : 0u;
+  const float* ps = a.part ? a.part + (size_t)unit * a.G * (D + 2) : nullptr;
+  const int np = a.G * (D + 2);
+  float pv[3];
+#pragma unroll
+  for (int r = 0; r < 3; ++r) {
+    const int k = tid + r * kThreads;
+    pv[r] = (k < np) ? (ps ? ps[k] : ((k % (D + 2)) == 0 ? kNegInf : 0.f)) : 0.f;
+  }
+  for (int s = tid; s <= a.beta; s += kThreads) {
+    int g = -1;
+    if (s < a.beta) g = a.l3_staged ? s : a.idx[(size_t)unit * a.beta + s];
+    const int lim = a.l3_staged ? a.beta : a.ng;
+    recoff[s] = (g >= 0 && g < lim) ? (int32_t)((uint32_t)g * (uint32_t)rec) : (int32_t)kFar;
+  }
+  if (tid < 16) s_cb[tid] = cbv;
+  if (tid < kMaxG * LPV) s_vsb[tid] = vsb;
+#pragma unroll
+  for (int r = 0; r < 3; ++r)
+    if (tid + r * kThreads < np) part[tid + r * kThreads] = pv[r];
+  rotate_query<D>(qin, a.scale * rsqrtf((float)D), qf, tid);
+  lds_barrier();
+  // first two tiles of this wave, loading while the table is built
+  TokTile tt0, tt1;
+  load_tok<D, N>(B, recoff, wave, n1t, a.n1, a.beta, lane, tt0);
+  load_tok<D, N>(B, recoff, wave + kWaves, n1t, a.n1, a.beta, lane, tt1);
+  build_lut4(s_lut4, s_cb, tid);
   half8 qh[D / 32], ql[D / 32];
   query_operands<D>(qf, lane, qh, ql);
-  __syncthreads();
+  lds_barrier();
 
-  const size_t o1 = (size_t)unit * a.n1;
-  const size_t rec = (size_t)a.group_n * (D + 8);
-  const int recs = a.l3_staged ? a.beta : a.ng;
-  const TokRsrc R{make_rsrc(a.l1k + o1 * CB, (uint32_t)a.n1 * CB),
-                  make_rsrc(a.l1k_n + o1, (uint32_t)a.n1 * 4),
-                  make_rsrc(a.l1v + o1 * CB, (uint32_t)a.n1 * CB),
-                  make_rsrc(a.l1v_n + o1, (uint32_t)a.n1 * 4),
-                  make_rsrc(a.l3 + (size_t)unit * recs * rec, (uint32_t)(recs * rec))};
-
-  const int n1t = (a.n1 + 15) / 16;
-  const int nft = (a.group_n == 16) ? a.beta : (a.beta + 1) / 2;
-  const int total = n1t + nft;
-  Online<D> st;
-  st.init();
+  Softmax<D> st;
+  st.init(kNegInf);
   {
     pipeline3<TokTile>(
-        wave_iters(total, wave),
+        wave_iters(total, wave), tt0, tt1,
         [&](int i, TokTile& T) {
-          load_tok<D>(a, R, sel, wave + i * kWaves, n1t, lane, T);
+          load_tok<D, N>(B, recoff, wave + i * kWaves, n1t, a.n1, a.beta, lane, T);
         },
         [&](int i, const TokTile& T) { consume_tok<D>(T, qh, lut4, lane, lane4, st); });
   }
-  __syncthreads();  // the table is no longer needed: reuse as scratch
+  lds_barrier();  // the table is no longer needed: reuse as scratch
   float* mine = scratch + kWaves * kMaxG * (D + 2);  // [G][D+2] this unit's token partial
   combine_waves<D>(st, a.G, scratch, mine, tid);
 
   // merge with the summary partial, normalise
   float* o = mine + kMaxG * (D + 2);  // [G][D]
-  const float* ps = a.part ? a.part + (size_t)unit * a.G * (D + 2) : nullptr;
-  for (int k = tid; k < a.G * D; k += kThreads) {
-    const int h = k / D, e = k % D;
-    const float* pm = mine + h * (D + 2);
-    const float m1 = pm[0], l1 = pm[1], v1 = pm[2 + e];
-    float m2 = kNegInf, l2 = 0.f, v2 = 0.f;
-    if (ps) {
-      m2 = ps[h * (D + 2)];
-      l2 = ps[h * (D + 2) + 1];
-      v2 = ps[h * (D + 2) + 2 + e];
-    }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int k = tid + r * kThreads, h = k / D, e = k % D;
+    if (k >= a.G * D) break;
+    const float* mp = mine + h * (D + 2);
+    const float m1 = mp[0], l1 = mp[1], v1 = mp[2 + e];
+    const float* pp = part + h * (D + 2);
+    const float m2 = pp[0], l2 = pp[1], v2 = pp[2 + e];
     const float M = fmaxf(m1, m2);
     const float w1 = (m1 == kNegInf) ? 0.f : __expf(m1 - M);
     const float w2 = (m2 == kNegInf) ? 0.f : __expf(m2 - M);
     const float L = w1 * l1 + w2 * l2;
     o[k] = (L > 0.f) ? (w1 * v1 + w2 * v2) / L : 0.f;
   }
-  __syncthreads();
+  lds_barrier();
   // inverse V rotation: out = D H o / sqrt(D)
-  constexpr int LPV = D / 8;
   if (tid < kMaxG * LPV) {
     const int h = tid / LPV, sub = tid % LPV;
     float v[8];
@@ -1045,7 +1191,7 @@ void token_kernel(TokArgs a) {
     for (int k = 0; k < 8; ++k) v[k] = (h < a.G) ? o[h * D + 8 * sub + k] : 0.f;
     fwht8xlanes<LPV>(v, sub);
     if (h < a.G) {
-      const uint32_t sb = sign_byte(a.v_signs + kvh * (D / 32), sub);
+      const uint32_t sb = s_vsb[tid];
       const float sc = rsqrtf((float)D);
       float* dst = a.out + ((size_t)unit * a.G + h) * D + 8 * sub;
 #pragma unroll
@@ -1058,18 +1204,16 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t summary_smem(int D, const StepShape& s) {
   const size_t ngp = (size_t)((s.n_groups + 15) & ~15);
-  const size_t body = 64 * kNC3 * 8 + (size_t)kMaxG * D * 4 + (size_t)s.G * ngp * 4 + ngp * 4 +
-                      256 * 4 + (((ngp + 31) / 32 + 3) & ~size_t(3)) * 4 + 64 * 16 +
+  const size_t body = (size_t)kMaxG * (D + 4) * 4 + (size_t)s.G * ngp * 4 +
+                      ((ngp + 31) & ~size_t(31)) * 4 + 256 * 4 +
+                      (((ngp + 31) / 32 + 3) & ~size_t(3)) * 4 +
                       std::max((size_t)s.beta * 4, (size_t)std::min<size_t>(ngp, kCandCap) * 8);
   const size_t comb = (size_t)kWaves * kMaxG * (D + 2) * 4;
   return std::max(body, comb);
 }
 
 size_t token_smem(int D, const StepShape& s) {
-  const size_t body = 256 * kNC4 * 4 + (size_t)kMaxG * D * 4 + (size_t)((s.beta + 4) & ~3) * 4;
-  const size_t comb = (size_t)kWaves * kMaxG * (D + 2) * 4 + (size_t)kMaxG * (D + 2) * 4 +
-                      (size_t)kMaxG * D * 4;
-  return std::max(body, comb);
+  return (size_t)kMaxG * (D + 4) * 4 + (size_t)kMaxG * (D + 2) * 4 + (size_t)(s.beta + 1) * 4;
 }
 
 }  // namespace
@@ -1129,8 +1273,12 @@ hipError_t token_d(const StepShape& s, const StepTensors& t, const Workspace& w,
   a.beta = s.beta;
   a.part = s.n_groups > 0 ? reinterpret_cast<const float*>(ws + w.part_off) : nullptr;
   a.out = t.out;
-  hipLaunchKernelGGL(token_kernel<D>, dim3((unsigned)(s.B * s.Hkv)), dim3(kThreads),
-                     token_smem(D, s), st, a);
+  if (s.group_n == 16)
+    hipLaunchKernelGGL((token_kernel<D, 16>), dim3((unsigned)(s.B * s.Hkv)), dim3(kThreads),
+                       token_smem(D, s), st, a);
+  else
+    hipLaunchKernelGGL((token_kernel<D, 8>), dim3((unsigned)(s.B * s.Hkv)), dim3(kThreads),
+                       token_smem(D, s), st, a);
   return hipGetLastError();
 }
 
