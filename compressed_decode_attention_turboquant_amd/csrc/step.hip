@@ -95,6 +95,12 @@ __device__ __forceinline__ f32x4 ldf1x4(rsrc_t r, uint32_t off) {
   for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(ld32(r, off + 4 * i));
   return v;
 }
+// Four consecutive floats in one 16-byte load, or, where the 16 bytes may
+// cross the end of the buffer (`edge`, wave-uniform), in four range-checked
+// loads so that every float in range is read.
+__device__ __forceinline__ f32x4 ldf4_edge(rsrc_t r, uint32_t off, bool edge) {
+  return edge ? ldf1x4(r, off) : ldf4(r, off);
+}
 
 __device__ __forceinline__ uint32_t h2u(_Float16 lo, _Float16 hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, lo) |
@@ -127,6 +133,27 @@ __device__ __forceinline__ void pipeline3(int iters, Buf& b0, Buf& b1, LoadF loa
     load(i + 2, b2);
     __builtin_amdgcn_sched_barrier(0);
     use(i, b0);
+    load(i + 3, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 1 < iters) use(i + 1, b1);
+    load(i + 4, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 2 < iters) use(i + 2, b2);
+  }
+}
+
+// The same pipeline run in segments: uses [3*q0, 3*q1) of a run of `iters`
+// (q0, q1 counted in triples), so that other work can go between segments
+// while the loads issued at the end of one segment are in flight.  On entry
+// b0, b1 hold (or are loading) tiles 3*q0, 3*q0+1; on exit 3*q1, 3*q1+1.
+template <typename Buf, typename LoadF, typename UseF>
+__device__ __forceinline__ void pipeline3_seg(int q0, int q1, int iters, Buf& b0, Buf& b1,
+                                              LoadF load, UseF use) {
+  Buf b2;
+  for (int i = 3 * q0; i < 3 * q1; i += 3) {
+    load(i + 2, b2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i < iters) use(i, b0);
     load(i + 3, b0);
     __builtin_amdgcn_sched_barrier(0);
     if (i + 1 < iters) use(i + 1, b1);
@@ -586,27 +613,16 @@ __device__ __forceinline__ bool cand_selected(const uint2* cand, int nc, int nee
   return rank < need;
 }
 
-// Writes the set bits of fmask as ascending group ids to idx[0 .. count);
-// run by one wave.
-__device__ void emit_selection(const uint32_t* fmask, int words, int32_t* idx, int lane) {
-  const int per = (words + 63) / 64;
-  const int w0 = min(lane * per, words), w1 = min(w0 + per, words);
-  int n = 0;
-  for (int w = w0; w < w1; ++w) n += __popc(fmask[w]);
-  int incl = n;
+// Exclusive prefix sum of v over the lanes of a wave, plus the wave total.
+__device__ __forceinline__ int wave_excl_scan(int v, int lane, int& total) {
+  int incl = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int y = __shfl_up(incl, o, 64);
     if (lane >= o) incl += y;
   }
-  int pos = incl - n;
-  for (int w = w0; w < w1; ++w) {
-    uint32_t m = fmask[w];
-    while (m) {
-      idx[pos++] = 32 * w + __ffs(m) - 1;
-      m &= m - 1u;
-    }
-  }
+  total = __builtin_amdgcn_readlane(incl, 63);
+  return incl - v;
 }
 
 // -------------------------------------------------------- summary kernel ---
@@ -674,8 +690,10 @@ struct KeyTile {
   uint32_t kw[3];
   f32x4 kn;
 };
+// edge_tile: the one tile whose rows run past the last group (or -1)
 template <int D>
-__device__ __forceinline__ void load_keys(rsrc_t rk, rsrc_t rn, int t, int lane, KeyTile& T) {
+__device__ __forceinline__ void load_keys(rsrc_t rk, rsrc_t rn, int t, int edge_tile, int lane,
+                                          KeyTile& T) {
   constexpr int CB3 = 3 * D / 8;
   const int n = lane & 15, gq = lane >> 4;
   const uint32_t row = (uint32_t)(16 * t + n) * CB3;
@@ -686,7 +704,7 @@ __device__ __forceinline__ void load_keys(rsrc_t rk, rsrc_t rn, int t, int lane,
     const u32x2 w = ld64(rk, row + 4 * ((3 * gq) >> 1));
     T.kw[0] = w.x; T.kw[1] = w.y; T.kw[2] = 0u;
   }
-  T.kn = ldf1x4(rn, (uint32_t)(16 * t + 4 * gq) * 4);
+  T.kn = ldf4_edge(rn, (uint32_t)(16 * t + 4 * gq) * 4, t == edge_tile);
 }
 // This lane's key bits from the words load_keys left (the loads stay free of
 // arithmetic so that no wait is forced before the tile is used).
@@ -724,13 +742,14 @@ __device__ __forceinline__ uint32_t val_shift(int lane) {
   return (uint32_t)(BITS * (lane & 15)) - 8u * val_byte<D>(lane);
 }
 template <int D>
-__device__ __forceinline__ void load_vals(rsrc_t rv, rsrc_t rvn, int t, int lane, ValTile& T) {
+__device__ __forceinline__ void load_vals(rsrc_t rv, rsrc_t rvn, int t, int edge_tile, int lane,
+                                          ValTile& T) {
   constexpr int RB = 3 * D / 8;
   const int gq = lane >> 4;
   const uint32_t base = (uint32_t)(16 * t + 4 * gq) * RB + val_byte<D>(lane);
 #pragma unroll
   for (int j = 0; j < 4; ++j) T.va[j] = ld32(rv, base + j * RB);
-  T.vn = ldf1x4(rvn, (uint32_t)(16 * t + 4 * gq) * 4);
+  T.vn = ldf4_edge(rvn, (uint32_t)(16 * t + 4 * gq) * 4, t == edge_tile);
 }
 
 template <int D>
@@ -743,9 +762,9 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   __shared__ int s_sel[4];
   __shared__ float s_lo[kWaves], s_hi[kWaves];
   __shared__ float s_mh[kWaves][kMaxG];
-  // dynamic layout: [qf 8*(D+4) f32][logits G*ngp f32][keys ngp u32][hist 256]
-  //   [fetched bitmap][selection scratch: candidates (uint2) or, in the
-  //   fallback, the selected ids].  qf doubles as the landing slot of the
+  // dynamic layout: [qf 8*(D+4) f32][logits G*ngp f32][keys u32][hist 256]
+  //   [fetched bitmap: buckets above the threshold][selected candidates]
+  //   [selection scratch: candidates (uint2), then the selected ids].  qf doubles as the landing slot of the
   //   phase-1 stores of lanes that hold no head; the wave-combine scratch
   //   reuses the front once the tiles are done.
   const int ngp = (a.ng + 15) & ~15;
@@ -754,7 +773,8 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   uint32_t* keys = reinterpret_cast<uint32_t*>(logits + a.G * ngp);
   int* hist = reinterpret_cast<int*>(keys + ((ngp + 31) & ~31));
   uint32_t* fmask = reinterpret_cast<uint32_t*>(hist + 256);
-  uint2* cand = reinterpret_cast<uint2*>(fmask + (((ngp + 31) / 32 + 3) & ~3));
+  uint32_t* cmask = fmask + (((ngp + 31) / 32 + 3) & ~3);
+  uint2* cand = reinterpret_cast<uint2*>(cmask + (((ngp + 31) / 32 + 3) & ~3));
   int32_t* sel = reinterpret_cast<int32_t*>(cand);
   float* scratch = reinterpret_cast<float*>(smem);
   const uint32_t* lut3 = s_lut3;
@@ -776,13 +796,17 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   QueryIn qin;
   load_query<D>(a.q + (size_t)unit * a.G * D, a.k_signs + kvh * (D / 32), a.G, tid, qin);
   KeyTile kt0, kt1;
-  load_keys<D>(rk, rkn, wave, lane, kt0);
-  load_keys<D>(rk, rkn, wave + kWaves, lane, kt1);
+  const int edge_tile = (a.ng & 15) ? (a.ng >> 4) : -1;
+  load_keys<D>(rk, rkn, wave, edge_tile, lane, kt0);
+  load_keys<D>(rk, rkn, wave + kWaves, edge_tile, lane, kt1);
 
   if (tid < 8) s_cb[tid] = cbv;
   rotate_query<D>(qin, a.scale * rsqrtf((float)D), qf, tid);
   const int words = (ngp + 31) >> 5;
-  for (int w = tid; w < words; w += kThreads) fmask[w] = 0u;
+  for (int w = tid; w < words; w += kThreads) {
+    fmask[w] = 0u;
+    cmask[w] = 0u;
+  }
   for (int b = tid; b < 256; b += kThreads) hist[b] = 0;
   if (tid < 4) s_sel[tid] = 0;
   lds_barrier();
@@ -796,37 +820,98 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   // lanes that hold no head's logits store into a dummy slot (no branch)
   const bool writer = !(c & 1) && (c >> 1) < a.G;
   float* lw = writer ? logits + (c >> 1) * ngp + 4 * gq : qf + 4 * lane;
-  float blo = kPosInf, bhi = kNegInf;
+  float blo = kPosInf, bhi = kNegInf, cmax = kNegInf;
+  // rows of tile t past the last group (only the last tile has any)
+  auto tail_rows = [&](int t) -> uint32_t {
+    const int valid = a.ng - (16 * t + 4 * gq);
+    return valid >= 4 ? 0u : (valid <= 0 ? 15u : (15u & ~((1u << valid) - 1u)));
+  };
   {
     pipeline3<KeyTile>(
         wave_iters(n_tiles, wave), kt0, kt1,
-        [&](int i, KeyTile& T) { load_keys<D>(rk, rkn, wave + i * kWaves, lane, T); },
+        [&](int i, KeyTile& T) { load_keys<D>(rk, rkn, wave + i * kWaves, edge_tile, lane, T); },
         [&](int i, const KeyTile& T) {
+          const int t = wave + i * kWaves;
           uint32_t kw[3];
           key_bits<D>(T.kw, lane, kw);
-          const f32x4 lg = qk3<D>(kw, qh, ql, lut3, lane4) * T.kn;
-          *reinterpret_cast<f32x4*>(lw + (writer ? 16 * (wave + i * kWaves) : 0)) = lg;
+          f32x4 lg = qk3<D>(kw, qh, ql, lut3, lane4) * T.kn;
+          *reinterpret_cast<f32x4*>(lw + (writer ? 16 * t : 0)) = lg;
           // bounds of every score (max or mean over heads of these logits)
           blo = fminf(blo, fminf(fminf(lg[0], lg[1]), fminf(lg[2], lg[3])));
           bhi = fmaxf(bhi, fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])));
+          if (t == n_tiles - 1) {  // wave-uniform
+            const uint32_t tr = tail_rows(t);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) lg[r] = ((tr >> r) & 1u) ? kNegInf : lg[r];
+          }
+          cmax = fmaxf(cmax, fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])));
         });
   }
   blo = wave_min(blo);
   bhi = wave_max(bhi);
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
   if (lane == 0) {
     s_lo[wave] = blo;
     s_hi[wave] = bhi;
   }
-  // the first two value tiles of this wave load while the selection runs
+  if (gq == 0 && writer) s_mh[wave][c >> 1] = cmax;
+  // From here on every wave streams the values of ALL summaries into the
+  // softmax partial; the top-beta selection runs in steps between segments
+  // of that stream (its LDS work overlaps the loads in flight), and at the
+  // end every wave subtracts the contribution of its share of the fetched
+  // summaries, computed with the same arithmetic.
+  const bool stream = a.want_partial && a.beta < a.ng;  // else the partial is empty
+  const int iters = stream ? wave_iters(n_tiles, wave) : 0;
   ValTile vt0, vt1;
-  if (a.want_partial) {
-    load_vals<D>(rv, rvn, wave, lane, vt0);
-    load_vals<D>(rv, rvn, wave + kWaves, lane, vt1);
+  if (stream) {
+    load_vals<D>(rv, rvn, wave, edge_tile, lane, vt0);
+    load_vals<D>(rv, rvn, wave + kWaves, edge_tile, lane, vt1);
   }
   lds_barrier();
 
-  // (2) router scores, per-head maxima, score histogram: thread t takes
-  // groups 4t .. 4t+3 (+2048 per pass), one 16-byte read per head
+  // every weight exp(logit + bias - m) <= 1 with m the head's maximum logit
+  const int hcol = min(c >> 1, a.G - 1);
+  float m0 = kNegInf;
+  for (int w = 0; w < kWaves; ++w) m0 = fmaxf(m0, s_mh[w][hcol]);
+  Softmax<D> st;
+  st.init(m0 + a.bias);
+  const uint32_t vsh = val_shift<D>(lane);
+  // sign = +1: add the rows' contributions; -1: subtract them
+  auto consume = [&](const float (&lgr)[4], const ValTile& V, float sign) {
+    float lg[4], p[4], w[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lg[r] = lgr[r] + a.bias;
+    st.weights(lg, p);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      st.l += sign * p[r];
+      w[r] = sign * p[r] * V.vn[r];
+    }
+    pv3<D>(V.va, vsh, weight_operand(w, lane), lane4, lut3, st.O);
+  };
+  const float* lrow = logits + hcol * ngp + 4 * gq;
+  auto vload = [&](int i, ValTile& V) {
+    load_vals<D>(rv, rvn, wave + i * kWaves, edge_tile, lane, V);
+  };
+  auto vuse = [&](int i, const ValTile& V) {
+    const int t = wave + i * kWaves;
+    const f32x4 lg4 = *reinterpret_cast<const f32x4*>(lrow + 16 * t);
+    float lg[4] = {lg4[0], lg4[1], lg4[2], lg4[3]};
+    if (t == n_tiles - 1) {  // wave-uniform
+      const uint32_t tr = tail_rows(t);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) lg[r] = ((tr >> r) & 1u) ? kNegInf : lg[r];
+    }
+    consume(lg, V, 1.f);
+  };
+  const int triples = (iters + 2) / 3;
+
+  // values, first segment
+  pipeline3_seg(0, min(1, triples), iters, vt0, vt1, vload, vuse);
+
+  // (2a) router scores of this thread's groups 4t .. 4t+3 (+2048 per pass),
+  // score histogram
   const bool hsel = a.want_topk && a.beta > 0 && a.beta < a.ng;
   float lo = kPosInf, hi = kNegInf;
   for (int w = 0; w < kWaves; ++w) {
@@ -834,26 +919,16 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
     hi = fmaxf(hi, s_hi[w]);
   }
   const float bscale = (hi > lo) ? 256.f / (hi - lo) : 0.f;
-  float mh[kMaxG];
-#pragma unroll
-  for (int h = 0; h < kMaxG; ++h) mh[h] = kNegInf;
-  const float inv_g = 1.f / (float)a.G;
-  for (int g0 = 4 * tid; g0 < 32 * words; g0 += 4 * kThreads) {
-    f32x4 vmax = {kNegInf, kNegInf, kNegInf, kNegInf}, vsum = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int h = 0; h < kMaxG; ++h) {
-      if (h < a.G) {
+  if (a.want_topk) {
+    const float inv_g = 1.f / (float)a.G;
+    for (int g0 = 4 * tid; g0 < 32 * words; g0 += 4 * kThreads) {
+      f32x4 vmax = {kNegInf, kNegInf, kNegInf, kNegInf}, vsum = {0.f, 0.f, 0.f, 0.f};
+      for (int h = 0; h < a.G; ++h) {
         const f32x4 x = *reinterpret_cast<const f32x4*>(logits + h * ngp + g0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float xe = (g0 + e < a.ng) ? x[e] : kNegInf;
-          mh[h] = fmaxf(mh[h], xe);
-          vmax[e] = fmaxf(vmax[e], xe);
-          vsum[e] += x[e];
-        }
+        vmax = f32x4{fmaxf(vmax[0], x[0]), fmaxf(vmax[1], x[1]), fmaxf(vmax[2], x[2]),
+                     fmaxf(vmax[3], x[3])};
+        vsum += x;
       }
-    }
-    if (a.want_topk) {
       u32x4 k4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -867,19 +942,12 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
       }
       *reinterpret_cast<u32x4*>(keys + g0) = k4;
     }
-  }
-#pragma unroll
-  for (int h = 0; h < kMaxG; ++h)
-    if (h < a.G) mh[h] = wave_max(mh[h]);
-  if (lane == 0)
-#pragma unroll
-    for (int h = 0; h < kMaxG; ++h) s_mh[wave][h] = mh[h];
-  if (a.want_topk && a.beta >= a.ng) {  // every group fetched
-    for (int w = tid; w < words; w += kThreads) {
-      const int left = a.ng - 32 * w;
-      fmask[w] = left >= 32 ? 0xffffffffu : (left <= 0 ? 0u : ((1u << left) - 1u));
-    }
-  } else if (!a.want_topk && a.given) {  // the given selection
+    if (a.beta >= a.ng)  // every group fetched
+      for (int w = tid; w < words; w += kThreads) {
+        const int left = a.ng - 32 * w;
+        fmask[w] = left >= 32 ? 0xffffffffu : (left <= 0 ? 0u : ((1u << left) - 1u));
+      }
+  } else if (a.given) {  // the given selection
     for (int i = tid; i < a.beta; i += kThreads) {
       const int g = a.given[(size_t)unit * a.beta + i];
       if (g >= 0 && g < a.ng) atomicOr(&fmask[g >> 5], 1u << (g & 31));
@@ -887,19 +955,38 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   }
   lds_barrier();
 
-  // buckets above the threshold -> fetched bitmap; threshold bucket ->
-  // candidate list (both from every thread's own groups)
+  // values, second segment
+  pipeline3_seg(min(1, triples), min(2, triples), iters, vt0, vt1, vload, vuse);
+
+  // (2b) buckets above the threshold -> fetched bitmap; the threshold bucket
+  // -> candidate list (compacted per wave)
   int bt = 0, need = 0;
   bool fallback = false;
   if (hsel) {
     hist_threshold(hist, a.beta, lane, bt, need);
     fallback = hist[bt] > kCandCap;  // the same on every thread
     if (!fallback) {
-      for (int g = tid; g < a.ng; g += kThreads) {
-        const uint32_t k = keys[g];
-        const int b = score_bucket(k, lo, bscale);
-        if (b > bt) atomicOr(&fmask[g >> 5], 1u << (g & 31));
-        else if (b == bt) cand[atomicAdd(&s_sel[2], 1)] = make_uint2((uint32_t)g, k);
+      // lane 0 holds a wave's lowest groups, so it is active whenever any lane is
+      for (int g0 = 4 * tid; g0 < 32 * words; g0 += 4 * kThreads) {
+        const u32x4 k4 = *reinterpret_cast<const u32x4*>(keys + g0);
+        uint32_t above = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int b = score_bucket(k4[e], lo, bscale);
+          const bool in = g0 + e < a.ng;
+          if (in && b > bt) above |= 1u << e;
+          const bool isc = in && b == bt;
+          const uint64_t m = __builtin_amdgcn_ballot_w64(isc);
+          int base = 0;
+          if (lane == 0 && m) base = atomicAdd(&s_sel[2], __popcll(m));
+          base = __builtin_amdgcn_readfirstlane(__shfl(base, 0, 64));
+          if (isc) {
+            const int pos = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                       (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            cand[pos] = make_uint2((uint32_t)(g0 + e), k4[e]);
+          }
+        }
+        if (above) atomicOr(&fmask[g0 >> 5], above << (g0 & 31));
       }
     } else {  // more ties in one bucket than the ranking takes: radix select
       top_beta(keys, a.ng, a.beta, hist, s_tmp, sel, tid);
@@ -908,67 +995,69 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   }
   lds_barrier();
 
-  // every wave: the selected candidates (ranked redundantly per wave), then
-  // the fetched groups and padding rows of its own tiles leave the summary
-  // softmax (the tiles' logits are read by this wave only, so no barrier)
+  // values, third segment
+  pipeline3_seg(min(2, triples), min(3, triples), iters, vt0, vt1, vload, vuse);
+
+  // (2c) every wave ranks the candidates (the same result everywhere) and adds
+  // the selected ones to its view of the bitmap; then every wave emits its
+  // share of the selection in ascending order (the offsets come from the
+  // per-word counts, which every wave computes)
   const int nc = (hsel && !fallback) ? s_sel[2] : 0;
-  if (a.want_partial) {
-    const int my_tiles = wave_iters(n_tiles, wave);
-    for (int i = lane; i < my_tiles; i += 64) {
-      const int t = wave + i * kWaves;
-      uint32_t bits = (fmask[t >> 1] >> (16 * (t & 1))) & 0xffffu;
-      const int valid = a.ng - 16 * t;
-      if (valid < 16) bits |= (0xffffu << max(valid, 0)) & 0xffffu;
-      while (bits) {
-        const int g = 16 * t + __ffs(bits) - 1;
-        for (int h = 0; h < a.G; ++h) logits[h * ngp + g] = kNegInf;
-        bits &= bits - 1u;
-      }
-    }
-    for (int i = lane; i < nc; i += 64) {
-      const uint2 me = cand[i];
-      const int t = (int)(me.x >> 4);
-      if (t % kWaves == wave && cand_selected(cand, nc, need, me))
-        for (int h = 0; h < a.G; ++h) logits[h * ngp + me.x] = kNegInf;
-    }
+  for (int i = lane; i < nc; i += 64) {
+    const uint2 me = cand[i];
+    if (cand_selected(cand, nc, need, me)) atomicOr(&cmask[me.x >> 5], 1u << (me.x & 31));
   }
-  if (wave == 0 && a.want_topk) {
-    for (int i = lane; i < nc; i += 64) {
-      const uint2 me = cand[i];
-      if (cand_selected(cand, nc, need, me)) atomicOr(&fmask[me.x >> 5], 1u << (me.x & 31));
+  int nsel = 0;
+  {
+    int before = 0;
+    for (int w0 = 0; w0 < words; w0 += 64) {
+      const int w = w0 + lane;
+      const uint32_t bits = (w < words) ? (fmask[w] | cmask[w]) : 0u;
+      int total;
+      const int pos0 = before + wave_excl_scan(__popc(bits), lane, total);
+      if (w < words && (w & (kWaves - 1)) == wave) {  // this wave's words
+        uint32_t m = bits;
+        int pos = pos0;
+        while (m) {
+          const int g = 32 * w + __ffs(m) - 1;
+          sel[pos] = g;
+          if (a.want_topk) a.idx[(size_t)unit * a.beta + pos] = g;
+          ++pos;
+          m &= m - 1u;
+        }
+      }
+      before += total;
     }
-    emit_selection(fmask, words, a.idx + (size_t)unit * a.beta, lane);
+    nsel = before;
   }
   if (!a.want_partial) return;
+  lds_barrier();
 
-  // (3) values of the unfetched summaries -> partial.  The maximum of every
-  // head's logits is known, so the weights need no running rescale.
-  const int hcol = min(c >> 1, a.G - 1);
-  float m0 = kNegInf;
-  for (int w = 0; w < kWaves; ++w) m0 = fmaxf(m0, s_mh[w][hcol]);
-  Softmax<D> st;
-  st.init(m0 + a.bias);  // every weight exp(logit + bias - m) <= 1
-  const float* lrow = logits + hcol * ngp + 4 * gq;
-  const uint32_t vsh = val_shift<D>(lane);
-  {
-    pipeline3<ValTile>(
-        wave_iters(n_tiles, wave), vt0, vt1,
-        [&](int i, ValTile& V) { load_vals<D>(rv, rvn, wave + i * kWaves, lane, V); },
-        [&](int i, const ValTile& V) {
-          const int t = wave + i * kWaves;
-          const f32x4 lg4 = *reinterpret_cast<const f32x4*>(lrow + 16 * t);
-          float lg[4], p[4];
+  // the fetched summaries are subtracted: list tiles j = wave, wave + 8, ...;
+  // the first one loads during the last values segment
+  constexpr int RB = 3 * D / 8;
+  const uint32_t vb = val_byte<D>(lane);
+  const int ntl = stream ? (nsel + 15) / 16 : 0;
+  auto corr_load = [&](int j, ValTile& V, float (&lg)[4]) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) lg[r] = lg4[r] + a.bias;
-          st.weights(lg, p);
-          float w[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            st.l += p[r];
-            w[r] = p[r] * V.vn[r];
-          }
-          pv3<D>(V.va, vsh, weight_operand(w, lane), lane4, lut3, st.O);
-        });
+    for (int r = 0; r < 4; ++r) {
+      const int k = 16 * j + 4 * gq + r;
+      const int g = (k < nsel) ? sel[k] : -1;
+      V.va[r] = ld32(rv, g >= 0 ? (uint32_t)g * RB + vb : kFar);
+      V.vn[r] = __uint_as_float(ld32(rvn, g >= 0 ? (uint32_t)g * 4 : kFar));
+      lg[r] = (g >= 0) ? logits[hcol * ngp + g] : kNegInf;
+    }
+  };
+  ValTile ct;
+  float clg[4];
+  if (wave < ntl) corr_load(wave, ct, clg);
+
+  // values, the rest
+  pipeline3_seg(min(3, triples), triples, iters, vt0, vt1, vload, vuse);
+
+  for (int j = wave; j < ntl; j += kWaves) {
+    if (j != wave) corr_load(j, ct, clg);
+    consume(clg, ct, -1.f);
   }
   lds_barrier();  // the logits are no longer needed: reuse as scratch
   combine_waves<D>(st, a.G, scratch, a.part + (size_t)unit * a.G * (D + 2), tid);
@@ -1052,8 +1141,9 @@ __device__ __forceinline__ void load_tok(const TokBufs& B, const int32_t* recoff
     const u32x2 w = ld64(rk, ko);
     T.kw = u32x4{w.x, w.y, 0u, 0u};
   }
-  T.kn = ldf1x4(rkn, kno);
-  T.vn = ldf1x4(rvn, vno);
+  const bool edge = l1 && t == n1t - 1 && (n1 & 15);  // the ragged last L1 tile
+  T.kn = ldf4_edge(rkn, kno, edge);
+  T.vn = ldf4_edge(rvn, vno, edge);
 #pragma unroll
   for (int j = 0; j < 4; ++j) T.va[j] = ld32(rv, vo + j * CB);
   const int valid = n1 - (int)(r0 + 4 * gq);
@@ -1206,7 +1296,7 @@ size_t summary_smem(int D, const StepShape& s) {
   const size_t ngp = (size_t)((s.n_groups + 15) & ~15);
   const size_t body = (size_t)kMaxG * (D + 4) * 4 + (size_t)s.G * ngp * 4 +
                       ((ngp + 31) & ~size_t(31)) * 4 + 256 * 4 +
-                      (((ngp + 31) / 32 + 3) & ~size_t(3)) * 4 +
+                      (((ngp + 31) / 32 + 3) & ~size_t(3)) * 8 +
                       std::max((size_t)s.beta * 4, (size_t)std::min<size_t>(ngp, kCandCap) * 8);
   const size_t comb = (size_t)kWaves * kMaxG * (D + 2) * 4;
   return std::max(body, comb);
