@@ -191,6 +191,12 @@ class Tiers:
                    (self.l1k, self.l1k_n, self.l1v, self.l1v_n, self.l2k, self.l2k_n,
                     self.l2v, self.l2v_n, self.l3))
 
+    def batch_slice(self, b0, b1):
+        """Tiers of sequences b0 .. b1-1 (views; the arrays are batch-major)."""
+        v = {k: getattr(self, k)[b0:b1] for k in
+             ("l1k", "l1k_n", "l1v", "l1v_n", "l2k", "l2k_n", "l2v", "l2v_n", "l3")}
+        return Tiers(b1 - b0, self.Hkv, self.d, self.n1, self.ng, self.group_n, **v)
+
 
 def alloc_tiers(B, Hkv, d, n1, ng, group_n, device, l3=None):
     e = lambda *s, dt=torch.uint8: torch.empty(s, dtype=dt, device=device)

@@ -251,3 +251,27 @@ def test_route_exact_ties(case):
         gs = scores[b, h].cpu().numpy()
         assert len(np.unique(gs)) == n_pat, "equal summaries must score exactly equal"
         np.testing.assert_array_equal(idx[b, h].cpu().numpy(), osel, err_msg=f"unit {(b, h)}")
+
+
+def test_batch_halves_match_full_batch():
+    # the decode step is per (sequence, kv-head): running the two halves of a
+    # batch on two streams gives the full batch's results exactly
+    w = W.QWEN3_14B_16K.smaller(T=1500, batch=4, n_marked=15)
+    print("batch halves", flush=True)
+    sc = Scenario(w)
+    t = sc.tiers
+    out, idx = hsq.decode_step(sc.q, t, w.beta, sc.dks, sc.dvs, sc.cb4, sc.cb3)
+    torch.cuda.synchronize()
+    h = w.batch // 2
+    s0, s1 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for (b0, b1), s in (((0, h), s0), ((h, w.batch), s1)):
+        ts = t.batch_slice(b0, b1)
+        ws = hsq.make_workspace(b1 - b0, w.hq, w.hkv, w.d, t.n1, t.ng, w.beta, w.group_n, DEV)
+        o = torch.empty((b1 - b0, w.hq, w.d), dtype=torch.float32, device=DEV)
+        with torch.cuda.stream(s):
+            hsq.step_route(sc.q[b0:b1], ts, w.beta, sc.dks, sc.cb3, ws)
+            hsq.step_attend(sc.q[b0:b1], ts, w.beta, sc.dks, sc.dvs, sc.cb4, ws, o)
+        outs.append((o, ws))
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([o for o, _ in outs]), out)
