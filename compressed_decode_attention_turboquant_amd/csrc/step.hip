@@ -18,14 +18,18 @@
 // cross-work-group communication inside a kernel (the kernel boundary orders
 // the hand-over), so no device-scope fences or atomics:
 //   summary_kernel  (1) streams the 3-bit summary keys: 16 summaries per MFMA
-//                   tile, codes turned into fp16 pairs through a lane-replicated
-//                   LDS table, split hi + lo so q_hi k_hi + q_hi k_lo + q_lo k_hi
-//                   (three v_mfma_f32_16x16x32_f16) gives fp32-accurate scores;
-//                   the per-head logits stay in LDS.  (2) router score per group
-//                   (max or mean over the G heads), top-beta by radix select in
-//                   LDS, selection written out.  (3) streams the values of the
-//                   UNFETCHED summaries only (fetched rows cost no traffic),
-//                   online softmax, PV on MFMA; one partial per unit.
+//                   tile, codes turned into exact fp16 centroid pairs through
+//                   a lane-replicated LDS table; the query split q_hi + q_lo
+//                   (two v_mfma_f32_16x16x32_f16) gives fp32-accurate scores;
+//                   the per-head logits stay in LDS.  (2)+(3) every wave
+//                   streams the values of ALL summaries into the softmax
+//                   partial (each head's maximum logit is known from (1)),
+//                   while the router scores (max or mean over the G heads) and
+//                   the exact top-beta (score histogram, then an exact ranking
+//                   of the threshold bucket) run in steps between segments of
+//                   that stream; finally the fetched summaries are subtracted
+//                   with the same weights and dequantised values.  One partial
+//                   per unit.
 //   token_kernel    16 tokens per tile from L1 and from the fetched L3 records;
 //                   4-bit codes through a byte -> fp16-pair table (one LDS copy
 //                   per lane, address built by one v_perm); QK and PV on MFMA;
@@ -33,8 +37,9 @@
 //                   rotation; output.
 // Loads go through buffer descriptors scoped to the unit, so rows past the end
 // and masked rows read as zero without touching memory, and the tile loops
-// need no per-lane branches.  Each wave keeps the next tile's loads in flight
-// while it computes the current one.
+// need no per-lane branches.  Each wave keeps two tiles' loads in flight while
+// it computes the current one; work-group barriers wait for LDS traffic only,
+// so those loads stay in flight across them.
 //
 // Value product layout.  O^T[dims][heads] = V^T P^T would need each lane to
 // hold one dimension of several tokens, but codes are stored token-major.
@@ -224,22 +229,13 @@ __device__ __forceinline__ uint32_t lds_at(const uint32_t* base, uint32_t byte_a
   return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(base) + byte_addr);
 }
 
-// 3-bit: 6-bit field e (codes e & 7, e >> 3) -> hi fp16 pair at dword
-// e*32 + l%32 and lo fp16 pair at kLut3Lo + e*32 + l%32, c = hi + lo to ~2^-22
-// relative.  The lo table sits 16 bytes past a multiple of 256 bytes from the
-// hi table so that the compiler cannot fuse a hi and a lo read into one
-// two-dword read (whose results would land in adjacent registers and need
-// moves to form the MFMA operands).
-constexpr int kLut3Lo = 64 * kNC3 + 4;
+// 3-bit: 6-bit field e (codes e & 7, e >> 3) -> fp16 pair at dword e*32 + l%32.
+// The stored centroids are fp16 values, so the pair is exact.
 __device__ void build_lut3(uint32_t* lut, const float* cb, int tid) {
-  // thread t fills copies 4(t&7) .. 4(t&7)+3 of entry t/8 in both tables
+  // thread t fills copies 4(t&7) .. 4(t&7)+3 of entry t/8
   const int e = tid >> 3;
-  const float c0 = cb[e & 7], c1 = cb[e >> 3];
-  const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
-  const _Float16 l0 = (_Float16)(c0 - (float)h0), l1 = (_Float16)(c1 - (float)h1);
-  const uint32_t hv = h2u(h0, h1), lv = h2u(l0, l1);
-  *reinterpret_cast<u32x4*>(lut + e * kNC3 + 4 * (tid & 7)) = u32x4{hv, hv, hv, hv};
-  *reinterpret_cast<u32x4*>(lut + kLut3Lo + e * kNC3 + 4 * (tid & 7)) = u32x4{lv, lv, lv, lv};
+  const uint32_t v = h2u((_Float16)cb[e & 7], (_Float16)cb[e >> 3]);
+  *reinterpret_cast<u32x4*>(lut + e * kNC3 + 4 * (tid & 7)) = u32x4{v, v, v, v};
 }
 // table address of 6-bit field e for this lane (lane4 = (lane & 31) << 2)
 __device__ __forceinline__ uint32_t lut3_addr(uint32_t e, uint32_t lane4) {
@@ -652,15 +648,16 @@ __device__ __forceinline__ uint32_t field6(const uint32_t* w) {
   }
 }
 
-// QK of 16 summaries: three-term split product q_hi c_hi + q_lo c_hi +
-// q_hi c_lo (fp32-accurate scores).  kw: this lane's 3D/4 key bits (summary
-// lane&15, dims gq*D/4 ..) from bit 0.  Every table read goes straight into
-// its operand register.
+// QK of 16 summaries: the dequantised keys are exact fp16 values, so the
+// two-term split q_hi c + q_lo c gives fp32-accurate scores.  kw: this lane's
+// 3D/4 key bits (summary lane&15, dims gq*D/4 ..) from bit 0.  The table
+// reads go straight into the operand registers; the two products accumulate
+// separately so that consecutive MFMAs do not wait on each other.
 template <int D>
 __device__ __forceinline__ f32x4 qk3(const uint32_t (&kw)[3], const half8 (&qh)[D / 32],
                                      const half8 (&ql)[D / 32], const uint32_t* lut,
                                      uint32_t lane4) {
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc_h = {0.f, 0.f, 0.f, 0.f}, acc_l = {0.f, 0.f, 0.f, 0.f};
   uint32_t a[D / 8];
 #define HSQ_FIELD_ADDR(P) a[P] = lut3_addr(field6<6 * (P)>(kw), lane4)
   HSQ_FIELD_ADDR(0); HSQ_FIELD_ADDR(1); HSQ_FIELD_ADDR(2); HSQ_FIELD_ADDR(3);
@@ -672,15 +669,12 @@ __device__ __forceinline__ f32x4 qk3(const uint32_t (&kw)[3], const half8 (&qh)[
 #undef HSQ_FIELD_ADDR
 #pragma unroll
   for (int m = 0; m < D / 32; ++m) {
-    const half8 ah = as_h8(lds_at(lut, a[4 * m]), lds_at(lut, a[4 * m + 1]),
+    const half8 ak = as_h8(lds_at(lut, a[4 * m]), lds_at(lut, a[4 * m + 1]),
                            lds_at(lut, a[4 * m + 2]), lds_at(lut, a[4 * m + 3]));
-    const half8 al = as_h8(lds_at(lut + kLut3Lo, a[4 * m]), lds_at(lut + kLut3Lo, a[4 * m + 1]),
-                           lds_at(lut + kLut3Lo, a[4 * m + 2]), lds_at(lut + kLut3Lo, a[4 * m + 3]));
-    acc = mfma16(ah, qh[m], acc);
-    acc = mfma16(ah, ql[m], acc);
-    acc = mfma16(al, qh[m], acc);
+    acc_h = mfma16(ak, qh[m], acc_h);
+    acc_l = mfma16(ak, ql[m], acc_l);
   }
-  return acc;
+  return acc_h + acc_l;
 }
 
 // Keys of tile t (16 summaries): this lane's raw key words (D = 128: 96 bits
@@ -756,7 +750,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   constexpr int CB3 = 3 * D / 8;
   extern __shared__ __align__(16) char smem[];
-  __shared__ __align__(16) uint32_t s_lut3[kLut3Lo + 64 * kNC3];
+  __shared__ __align__(16) uint32_t s_lut3[64 * kNC3];
   __shared__ float s_cb[8];
   __shared__ int s_tmp[kWaves];
   __shared__ int s_sel[4];
@@ -1155,14 +1149,16 @@ template <int D>
 __device__ __forceinline__ void consume_tok(const TokTile& T, const half8 (&qh)[D / 32],
                                             const uint32_t* lut4, int lane, uint32_t lane4,
                                             Softmax<D>& st) {
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // two accumulators so that consecutive MFMAs do not wait on each other
+  f32x4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
   for (int m = 0; m < D / 32; ++m) {
     const uint32_t w = T.kw[m];
     const half8 av = as_h8(lds_at(lut4, lut4_addr<0>(w, lane4)), lds_at(lut4, lut4_addr<1>(w, lane4)),
                            lds_at(lut4, lut4_addr<2>(w, lane4)), lds_at(lut4, lut4_addr<3>(w, lane4)));
-    acc = mfma16(av, qh[m], acc);
+    acc2[m & 1] = mfma16(av, qh[m], acc2[m & 1]);
   }
+  const f32x4 acc = acc2[0] + acc2[1];
   float lg[4], p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) lg[i] = ((T.ok >> i) & 1u) ? acc[i] * T.kn[i] : kNegInf;

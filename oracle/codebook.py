@@ -116,9 +116,17 @@ def distortion(c, thr, d):
 
 @functools.lru_cache(maxsize=None)
 def codebook_f32(d, bits):
-    """The codebook as the fp32 tables the codec consumes: (centroids, thresholds)."""
-    c, thr = lloyd_max(d, bits)
-    c32, t32 = c.astype(np.float32), thr.astype(np.float32)
+    """The stored codebook the codec consumes, as fp32 arrays.
+
+    Centroids: the Lloyd-Max fixed point rounded to fp32 and then to fp16
+    (round to nearest even each time), the precision in which dequantised
+    values enter the matrix products.  Thresholds: the midpoints of adjacent
+    stored centroids, which are exact in fp32, so that counting the
+    thresholds below y is nearest-stored-centroid quantisation.
+    """
+    c, _ = lloyd_max(d, bits)
+    c32 = c.astype(np.float32).astype(np.float16).astype(np.float32)
+    t32 = (0.5 * (c32[:-1].astype(np.float64) + c32[1:].astype(np.float64))).astype(np.float32)
     c32.setflags(write=False)
     t32.setflags(write=False)
     return c32, t32

@@ -128,8 +128,22 @@ def test_monte_carlo_marginal_and_mse(d, bits, n):
     assert abs(emp - pred) / pred < 0.02
 
 
-def test_f32_tables_are_fp32_rounding_of_fixed_point():
-    c, t = cb.lloyd_max(128, 4)
-    c32, t32 = cb.codebook_f32(128, 4)
-    np.testing.assert_array_equal(c32, c.astype(np.float32))
-    np.testing.assert_array_equal(t32, t.astype(np.float32))
+def test_stored_tables_are_fp16_centroids_and_exact_midpoints():
+    for d, bits in ((128, 4), (128, 3), (64, 4), (64, 3)):
+        c, _ = cb.lloyd_max(d, bits)
+        c32, t32 = cb.codebook_f32(d, bits)
+        want = c.astype(np.float32).astype(np.float16).astype(np.float32)
+        np.testing.assert_array_equal(c32, want)
+        # every stored centroid is an fp16 value, within half an fp16 ulp of
+        # the fixed point
+        np.testing.assert_array_equal(c32.astype(np.float16).astype(np.float32), c32)
+        assert np.all(np.abs(c32 - c) <= np.spacing(np.abs(c).astype(np.float16)).astype(np.float64))
+        # thresholds: exact midpoints (fp32 holds them exactly), symmetric
+        mid = 0.5 * (c32[:-1].astype(np.float64) + c32[1:].astype(np.float64))
+        np.testing.assert_array_equal(t32.astype(np.float64), mid)
+        np.testing.assert_array_equal(c32, -c32[::-1])
+        assert t32[len(t32) // 2] == 0.0 and np.all(np.diff(t32) > 0)
+        # the stored codebook's distortion is the fixed point's to 1e-4
+        assert abs(cb.distortion(c32.astype(np.float64), mid, d) / cb.distortion(c, 0.5 * (c[:-1] + c[1:]), d) - 1) < 1e-4
+
+

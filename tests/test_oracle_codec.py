@@ -58,18 +58,17 @@ def test_sign_mask_bit_order():
 
 @pytest.mark.parametrize("bits", [3, 4])
 def test_threshold_count_equals_nearest_centroid(bits):
-    # brute force: argmin_j |y - c_j|, first index on ties, with the same
-    # fp32 centroid table; exempt values within 1e-7 of a threshold (there the
-    # fp32-rounded midpoint and the midpoint of fp32 centroids may differ).
+    # brute force: argmin_j |y - c_j|, first index on ties, with the stored
+    # centroids; the thresholds are their exact midpoints, so the two agree
+    # everywhere (a value on a midpoint is a tie and goes to the lower cell)
     d = 128
     c32, t32 = cb.codebook_f32(d, bits)
     rng = np.random.default_rng(7)
     y = rng.standard_normal(10 ** 6) / np.sqrt(d)
+    y[:1000] = t32[rng.integers(0, len(t32), 1000)]  # values exactly on thresholds
     brute = np.argmin(np.abs(y[:, None] - c32.astype(np.float64)[None, :]), axis=1)
     count = np.sum(y[:, None] > t32.astype(np.float64)[None, :], axis=1)
-    near = np.min(np.abs(y[:, None] - t32.astype(np.float64)[None, :]), axis=1) < 1e-7
-    assert np.all((brute == count) | near)
-    assert near.mean() < 1e-4
+    np.testing.assert_array_equal(brute, count)
 
 
 def test_pack_fixed_patterns():
