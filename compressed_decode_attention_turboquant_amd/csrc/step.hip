@@ -74,6 +74,19 @@ constexpr int kMaxLogits = 12288;        // G * n_groups kept in LDS
 constexpr uint32_t kFar = 0x80000000u;   // buffer offset that reads as zero
 constexpr float kNegInf = -INFINITY;
 constexpr float kPosInf = INFINITY;
+// tiles per wave in the load pipelines (K-1 in flight while one computes)
+#ifndef HSQ_KEY_DEPTH
+#define HSQ_KEY_DEPTH 3
+#endif
+#ifndef HSQ_VAL_DEPTH
+#define HSQ_VAL_DEPTH 3
+#endif
+#ifndef HSQ_TOK_DEPTH
+#define HSQ_TOK_DEPTH 3
+#endif
+constexpr int kKeyDepth = HSQ_KEY_DEPTH;
+constexpr int kValDepth = HSQ_VAL_DEPTH;
+constexpr int kTokDepth = HSQ_TOK_DEPTH;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
@@ -119,53 +132,37 @@ __device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// Runs use(i, buf) for i in [0, iters) with each buffer's loads issued two
-// iterations before its use, so every wave keeps two tiles in flight.  The
-// caller has issued load(0, b0) and load(1, b1) (as early as it likes).
-// load(i) is also called for i >= iters; it must then read out of bounds
-// (buffer loads past num_records return zero without memory traffic).  iters
-// is wave-uniform.
-template <typename Buf, typename LoadF, typename UseF>
-__device__ __forceinline__ void pipeline3(int iters, Buf& b0, Buf& b1, LoadF load, UseF use) {
-  Buf b2;
-  // Every pass issues all three loads (the ones past the end read nothing),
-  // so the number of loads in flight is the same on every path through the
-  // body and the waits stay partial; the trailing uses are skipped by
-  // wave-uniform tests instead of a second copy of the body.  The scheduling
-  // barriers keep the compiler from sinking the loads below the previous
-  // tile's arithmetic.
-  for (int i = 0; i < iters; i += 3) {
-    load(i + 2, b2);
-    __builtin_amdgcn_sched_barrier(0);
-    use(i, b0);
-    load(i + 3, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (i + 1 < iters) use(i + 1, b1);
-    load(i + 4, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (i + 2 < iters) use(i + 2, b2);
+// Runs use(i, B[i % K]) for i in [0, iters) with each buffer's loads
+// issued K-1 iterations before its use, so every wave keeps K-1 tiles in
+// flight while it computes one.  The uses run in segments: [K*q0, K*q1) of a
+// run of `iters` (q0, q1 counted in K-tuples), so that other work can go
+// between segments while the loads issued at the end of one are in flight.
+// On entry B[0..K-2] hold (or are loading) tiles K*q0 .. K*q0+K-2; on exit
+// the tiles K*q1 .. K*q1+K-2.  load(i) is also called for i >= iters; it must
+// then read out of bounds (buffer loads past num_records return zero without
+// memory traffic).  iters is wave-uniform.
+//
+// Every pass issues all K loads, so the number of loads in flight is the same
+// on every path through the body and the waits stay partial; the trailing
+// uses are skipped by wave-uniform tests instead of a second copy of the
+// body.  The scheduling barriers keep the compiler from sinking the loads
+// below the previous tile's arithmetic.
+template <int K, typename Buf, typename LoadF, typename UseF>
+__device__ __forceinline__ void pipeline_seg(int q0, int q1, int iters, Buf (&B)[K], LoadF load,
+                                             UseF use) {
+  for (int i = K * q0; i < K * q1; i += K) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      load(i + j + K - 1, B[(j + K - 1) % K]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + j < iters) use(i + j, B[j]);
+    }
   }
 }
-
-// The same pipeline run in segments: uses [3*q0, 3*q1) of a run of `iters`
-// (q0, q1 counted in triples), so that other work can go between segments
-// while the loads issued at the end of one segment are in flight.  On entry
-// b0, b1 hold (or are loading) tiles 3*q0, 3*q0+1; on exit 3*q1, 3*q1+1.
-template <typename Buf, typename LoadF, typename UseF>
-__device__ __forceinline__ void pipeline3_seg(int q0, int q1, int iters, Buf& b0, Buf& b1,
-                                              LoadF load, UseF use) {
-  Buf b2;
-  for (int i = 3 * q0; i < 3 * q1; i += 3) {
-    load(i + 2, b2);
-    __builtin_amdgcn_sched_barrier(0);
-    if (i < iters) use(i, b0);
-    load(i + 3, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (i + 1 < iters) use(i + 1, b1);
-    load(i + 4, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (i + 2 < iters) use(i + 2, b2);
-  }
+// The whole run in one segment.
+template <int K, typename Buf, typename LoadF, typename UseF>
+__device__ __forceinline__ void pipeline(int iters, Buf (&B)[K], LoadF load, UseF use) {
+  pipeline_seg<K>(0, (iters + K - 1) / K, iters, B, load, use);
 }
 
 // Wave index as a scalar (wave-uniform for the compiler).
@@ -758,9 +755,11 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   __shared__ float s_mh[kWaves][kMaxG];
   // dynamic layout: [qf 8*(D+4) f32][logits G*ngp f32][keys u32][hist 256]
   //   [fetched bitmap: buckets above the threshold][selected candidates]
-  //   [selection scratch: candidates (uint2), then the selected ids].  qf doubles as the landing slot of the
-  //   phase-1 stores of lanes that hold no head; the wave-combine scratch
-  //   reuses the front once the tiles are done.
+  //   [candidates (uint2), or the fallback's selection].  qf doubles as the
+  //   landing slot of the phase-1 stores of lanes that hold no head; the
+  //   emitted selection reuses the keys once the threshold step is done (the
+  //   candidates may still be read by slower waves while it is written); the
+  //   wave-combine scratch reuses the front once the tiles are done.
   const int ngp = (a.ng + 15) & ~15;
   float* qf = reinterpret_cast<float*>(smem);
   float* logits = qf + kMaxG * kQS<D>;
@@ -769,7 +768,7 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   uint32_t* fmask = reinterpret_cast<uint32_t*>(hist + 256);
   uint32_t* cmask = fmask + (((ngp + 31) / 32 + 3) & ~3);
   uint2* cand = reinterpret_cast<uint2*>(cmask + (((ngp + 31) / 32 + 3) & ~3));
-  int32_t* sel = reinterpret_cast<int32_t*>(cand);
+  int32_t* sel = reinterpret_cast<int32_t*>(keys);
   float* scratch = reinterpret_cast<float*>(smem);
   const uint32_t* lut3 = s_lut3;
 
@@ -789,10 +788,11 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   const float cbv = (tid < 8) ? a.cb3[tid] : 0.f;
   QueryIn qin;
   load_query<D>(a.q + (size_t)unit * a.G * D, a.k_signs + kvh * (D / 32), a.G, tid, qin);
-  KeyTile kt0, kt1;
+  KeyTile kt[kKeyDepth];
   const int edge_tile = (a.ng & 15) ? (a.ng >> 4) : -1;
-  load_keys<D>(rk, rkn, wave, edge_tile, lane, kt0);
-  load_keys<D>(rk, rkn, wave + kWaves, edge_tile, lane, kt1);
+#pragma unroll
+  for (int j = 0; j < kKeyDepth - 1; ++j)
+    load_keys<D>(rk, rkn, wave + j * kWaves, edge_tile, lane, kt[j]);
 
   if (tid < 8) s_cb[tid] = cbv;
   rotate_query<D>(qin, a.scale * rsqrtf((float)D), qf, tid);
@@ -821,8 +821,8 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
     return valid >= 4 ? 0u : (valid <= 0 ? 15u : (15u & ~((1u << valid) - 1u)));
   };
   {
-    pipeline3<KeyTile>(
-        wave_iters(n_tiles, wave), kt0, kt1,
+    pipeline<kKeyDepth>(
+        wave_iters(n_tiles, wave), kt,
         [&](int i, KeyTile& T) { load_keys<D>(rk, rkn, wave + i * kWaves, edge_tile, lane, T); },
         [&](int i, const KeyTile& T) {
           const int t = wave + i * kWaves;
@@ -857,10 +857,11 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   // summaries, computed with the same arithmetic.
   const bool stream = a.want_partial && a.beta < a.ng;  // else the partial is empty
   const int iters = stream ? wave_iters(n_tiles, wave) : 0;
-  ValTile vt0, vt1;
+  ValTile vt[kValDepth];
   if (stream) {
-    load_vals<D>(rv, rvn, wave, edge_tile, lane, vt0);
-    load_vals<D>(rv, rvn, wave + kWaves, edge_tile, lane, vt1);
+#pragma unroll
+    for (int j = 0; j < kValDepth - 1; ++j)
+      load_vals<D>(rv, rvn, wave + j * kWaves, edge_tile, lane, vt[j]);
   }
   lds_barrier();
 
@@ -899,10 +900,10 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
     }
     consume(lg, V, 1.f);
   };
-  const int triples = (iters + 2) / 3;
+  const int segs = (iters + kValDepth - 1) / kValDepth;
 
   // values, first segment
-  pipeline3_seg(0, min(1, triples), iters, vt0, vt1, vload, vuse);
+  pipeline_seg<kValDepth>(0, min(1, segs), iters, vt, vload, vuse);
 
   // (2a) router scores of this thread's groups 4t .. 4t+3 (+2048 per pass),
   // score histogram
@@ -950,7 +951,7 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   lds_barrier();
 
   // values, second segment
-  pipeline3_seg(min(1, triples), min(2, triples), iters, vt0, vt1, vload, vuse);
+  pipeline_seg<kValDepth>(min(1, segs), min(2, segs), iters, vt, vload, vuse);
 
   // (2b) buckets above the threshold -> fetched bitmap; the threshold bucket
   // -> candidate list (compacted per wave)
@@ -983,14 +984,15 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
         if (above) atomicOr(&fmask[g0 >> 5], above << (g0 & 31));
       }
     } else {  // more ties in one bucket than the ranking takes: radix select
-      top_beta(keys, a.ng, a.beta, hist, s_tmp, sel, tid);
-      for (int i = tid; i < a.beta; i += kThreads) atomicOr(&fmask[sel[i] >> 5], 1u << (sel[i] & 31));
+      int32_t* tsel = reinterpret_cast<int32_t*>(cand);
+      top_beta(keys, a.ng, a.beta, hist, s_tmp, tsel, tid);
+      for (int i = tid; i < a.beta; i += kThreads) atomicOr(&fmask[tsel[i] >> 5], 1u << (tsel[i] & 31));
     }
   }
   lds_barrier();
 
   // values, third segment
-  pipeline3_seg(min(2, triples), min(3, triples), iters, vt0, vt1, vload, vuse);
+  pipeline_seg<kValDepth>(min(2, segs), min(3, segs), iters, vt, vload, vuse);
 
   // (2c) every wave ranks the candidates (the same result everywhere) and adds
   // the selected ones to its view of the bitmap; then every wave emits its
@@ -1047,7 +1049,7 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   if (wave < ntl) corr_load(wave, ct, clg);
 
   // values, the rest
-  pipeline3_seg(min(3, triples), triples, iters, vt0, vt1, vload, vuse);
+  pipeline_seg<kValDepth>(min(3, segs), segs, iters, vt, vload, vuse);
 
   for (int j = wave; j < ntl; j += kWaves) {
     if (j != wave) corr_load(j, ct, clg);
@@ -1230,9 +1232,10 @@ void token_kernel(TokArgs a) {
   rotate_query<D>(qin, a.scale * rsqrtf((float)D), qf, tid);
   lds_barrier();
   // first two tiles of this wave, loading while the table is built
-  TokTile tt0, tt1;
-  load_tok<D, N>(B, recoff, wave, n1t, a.n1, a.beta, lane, tt0);
-  load_tok<D, N>(B, recoff, wave + kWaves, n1t, a.n1, a.beta, lane, tt1);
+  TokTile tt[kTokDepth];
+#pragma unroll
+  for (int j = 0; j < kTokDepth - 1; ++j)
+    load_tok<D, N>(B, recoff, wave + j * kWaves, n1t, a.n1, a.beta, lane, tt[j]);
   build_lut4(s_lut4, s_cb, tid);
   half8 qh[D / 32], ql[D / 32];
   query_operands<D>(qf, lane, qh, ql);
@@ -1241,8 +1244,8 @@ void token_kernel(TokArgs a) {
   Softmax<D> st;
   st.init(kNegInf);
   {
-    pipeline3<TokTile>(
-        wave_iters(total, wave), tt0, tt1,
+    pipeline<kTokDepth>(
+        wave_iters(total, wave), tt,
         [&](int i, TokTile& T) {
           load_tok<D, N>(B, recoff, wave + i * kWaves, n1t, a.n1, a.beta, lane, T);
         },

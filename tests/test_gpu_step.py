@@ -19,9 +19,11 @@ import torch
 from compressed_decode_attention_turboquant_amd import hsq
 from compressed_decode_attention_turboquant_amd import workloads as W
 from oracle import codebook as ocb
+from oracle import codec as ocodec
 from oracle import decode as odec
 from oracle import tiers as otiers
-from tests.gpu_util import ATTN_REL_L2, TIE_BAND, rel_l2, signs_to_dev
+from tests.gpu_util import (ATTN_REL_L2, CODE_BAND, TIE_BAND, compare_codes, rel_l2,
+                            signs_to_dev)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -67,8 +69,28 @@ class Scenario:
         return self.q[b, h * G:(h + 1) * G].double().cpu().numpy()
 
 
+def flip_slack(sc, unit, b, h):
+    """Per group, the largest change of its router score that the code
+    tolerance allows: each L2 key coordinate whose oracle value lies within
+    CODE_BAND of a threshold may take the adjacent cell, which moves the
+    head-h logit by scale * r * |c[j+1] - c[j]| * |(R q_h)_i|.  Computed from
+    the oracle's values alone."""
+    c, t = (np.asarray(a, dtype=np.float32).astype(np.float64) for a in sc.c3)
+    y = unit["l2k_y"]                                   # [ng, d]
+    if y.shape[0] == 0:
+        return np.zeros(0)
+    dist = np.abs(y[:, :, None] - t[None, None, :])     # [ng, d, 7]
+    j = np.argmin(dist, axis=2)
+    near = np.take_along_axis(dist, j[:, :, None], axis=2)[:, :, 0] < CODE_BAND
+    step = np.where(near, c[j + 1] - c[j], 0.0)         # [ng, d]
+    rq = np.abs(sc.q_unit(b, h) @ ocodec.rotation_matrix(sc.ks[h], sc.w.d).T)  # [G, d]
+    r = unit["l2k_n"].astype(np.float64)
+    return sc.scale * r * np.max(step @ rq.T, axis=1)
+
+
 def check_route(sc, idx, scores, units, beta, agg="max"):
-    """GPU selection vs oracle under the near-tie rule; GPU scores vs oracle."""
+    """GPU selection vs oracle under the near-tie rule; GPU scores vs oracle.
+    Both rules widen by what near-threshold code differences can cause."""
     ng = sc.tiers.ng
     b_eff = min(beta, ng)
     worst = 0.0
@@ -79,18 +101,34 @@ def check_route(sc, idx, scores, units, beta, agg="max"):
         gsel = idx[b, h].cpu().numpy()
         assert gsel.shape[0] == b_eff
         assert np.all(np.diff(gsel) > 0), "selection must be ascending and distinct"
+        slack = flip_slack(sc, unit, b, h)
+        if scores is not None:
+            err = np.abs(scores[b, h].cpu().numpy() - os_)
+            bad = err > 2e-6 + slack
+            assert not bad.any(), (
+                f"unit {(b, h)}: router scores differ by {err[bad].max():.3e} "
+                f"(allowed {2e-6 + slack[bad][np.argmax(err[bad])]:.3e})")
+            worst = max(worst, float(np.max(err - slack, initial=0.0)))
         if b_eff == 0:
             continue
         kth = np.sort(os_)[::-1][b_eff - 1]
-        diff = set(gsel.tolist()) ^ set(osel.tolist())
+        diff = sorted(set(gsel.tolist()) ^ set(osel.tolist()))
+        wide = max((slack[g] for g in diff), default=0.0)
         for g in diff:
-            assert abs(os_[g] - kth) < TIE_BAND, (
+            assert abs(os_[g] - kth) < TIE_BAND + slack[g] + wide, (
                 f"unit {(b, h)}: group {g} differs, score {os_[g]:.8f} vs beta-th {kth:.8f}")
-        if scores is not None:
-            worst = max(worst, float(np.max(np.abs(scores[b, h].cpu().numpy() - os_))))
-    if scores is not None:
-        assert worst < 2e-6, f"router scores differ by {worst:.3e}"
     return worst
+
+
+def check_l2_codes(sc, units):
+    """The GPU's L2 key codes of these units under the code tolerance."""
+    for (b, h) in units:
+        unit, _ = sc.oracle_unit(b, h)
+        n_bad, total = compare_codes(sc.tiers.l2k[b, h].cpu().numpy(), unit["l2k_codes"],
+                                     unit["l2k_y"], sc.c3[1], 3, sc.w.d, f"l2k {(b, h)}")
+        if n_bad:
+            print(f"  unit {(b, h)}: {n_bad} near-threshold L2 key code differences of {total}",
+                  flush=True)
 
 
 def check_attn(sc, out, idx, units, summary_bias=0.0):
@@ -275,3 +313,66 @@ def test_batch_halves_match_full_batch():
         outs.append((o, ws))
     torch.cuda.synchronize()
     assert torch.equal(torch.cat([o for o, _ in outs]), out)
+
+
+def test_headline_full_size():
+    # the 40/8-head, d=128, T=16384, batch-64, N=8, beta=128 layer at full size,
+    # launched as the timed loop launches it (route + attend with a workspace,
+    # replayed from a captured graph).  Every unit: the selection is ascending,
+    # distinct, in range and exactly the top-beta of the kernel's own router
+    # scores; replays reproduce the eager call bit for bit.  Sampled units:
+    # scores, selection and attention against the oracle.
+    w = W.QWEN3_14B_16K
+    print("headline full size: build", flush=True)
+    sc = Scenario(w)
+    t = sc.tiers
+    beta = min(w.beta, t.ng)
+    ws = hsq.make_workspace(w.batch, w.hq, w.hkv, w.d, t.n1, t.ng, beta, w.group_n, DEV)
+    out = torch.empty((w.batch, w.hq, w.d), dtype=torch.float32, device=DEV)
+    idx = torch.empty((w.batch, w.hkv, beta), dtype=torch.int32, device=DEV)
+
+    def step():
+        hsq.step_route(sc.q, t, w.beta, sc.dks, sc.cb3, ws, idx=idx)
+        hsq.step_attend(sc.q, t, w.beta, sc.dks, sc.dvs, sc.cb4, ws, out)
+
+    print("headline full size: eager step", flush=True)
+    step()
+    torch.cuda.synchronize()
+    out0, idx0 = out.clone(), idx.clone()
+    assert torch.isfinite(out0).all()
+    ia = idx0.long()
+    assert (ia >= 0).all() and (ia < t.ng).all()
+    assert (ia[..., 1:] > ia[..., :-1]).all(), "selection must be ascending and distinct"
+
+    print("headline full size: graph replays", flush=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        step()  # warm-up on the capture stream
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            step()
+    for r in range(3):
+        out.zero_()
+        idx.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, idx0), f"replay {r}: selection differs"
+        assert torch.equal(out, out0), f"replay {r}: output differs"
+
+    print("headline full size: selection vs the kernel's own scores", flush=True)
+    idx2, scores = hsq.route_topk(sc.q, t, sc.dks, sc.cb3, w.beta, want_scores=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx2, idx0)
+    order = torch.sort(scores, dim=-1, descending=True, stable=True).indices[..., :beta]
+    top = torch.sort(order, dim=-1).values.to(torch.int32)
+    assert torch.equal(top, idx0), "selection is not the top-beta of the router scores"
+
+    units = [(0, 0), (17, 3), (42, 7), (63, 5)]
+    print(f"headline full size: oracle on units {units}", flush=True)
+    check_l2_codes(sc, units)
+    check_route(sc, idx0, scores, units, w.beta)
+    worst = check_attn(sc, out0, idx0, units)
+    print(f"  worst rel L2 {worst:.3e}", flush=True)
