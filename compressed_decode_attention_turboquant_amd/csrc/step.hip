@@ -201,6 +201,21 @@ __device__ __forceinline__ float wave_max(float x) {
 }
 __device__ __forceinline__ float wave_min(float x) { return -wave_max(-x); }
 
+// Three-way minimum / maximum as one VALU instruction.  fminf/fmaxf would
+// first quiet every operand the compiler cannot prove canonical (one more
+// instruction each); the bounds below only need an order, and a NaN operand
+// is dropped by the instruction itself.
+__device__ __forceinline__ float min3f(float a, float b, float c) {
+  float r;
+  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // ---------------------------------------------------------------- tables ---
 //
 // The dequantisation tables live in static LDS, so their base folds into the
@@ -318,11 +333,13 @@ constexpr float kLazy = 4.f;
 template <int D>
 struct Softmax {
   float m, mL;  // mL = m * log2(e)
+  float mth;    // m + kLazy
   float l;
   f32x4 O[D / 32];
   __device__ void init(float m0) {
     m = m0;
     mL = m0 * kLog2e;
+    mth = m0 + kLazy;
     l = 0.f;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -333,21 +350,23 @@ struct Softmax {
     for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(lg[i], kLog2e, -mL));
   }
   // Fold in 4 logits of this lane (rows 4gq+i) with a lazily moved maximum:
-  // the state is rescaled only when some column's tile maximum exceeds its
-  // reference by more than kLazy (rare once the first tiles are in).
+  // the state is rescaled only when a logit exceeds the reference by more
+  // than kLazy (rare once the first tiles are in).  Each lane tests its own
+  // rows; only a rescale takes the maximum over the column's four lanes, so
+  // the lanes of a column keep one reference.
   __device__ __forceinline__ void update(const float (&lg)[4], float (&p)[4]) {
-    float mt = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const bool up = mt > m + kLazy;
-    if (__builtin_amdgcn_ballot_w64(up)) {  // wave-uniform branch
-      const float mn = up ? mt : m;
+    float mt = max3f(max3f(lg[0], lg[1], lg[2]), lg[3], lg[3]);
+    if (__builtin_amdgcn_ballot_w64(mt > mth)) {  // wave-uniform branch
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float mn = (mt > mth) ? mt : m;
       const float alpha = (m == kNegInf) ? 0.f : __expf(m - mn);
       l *= alpha;
 #pragma unroll
       for (int t = 0; t < D / 32; ++t) O[t] *= alpha;
       m = mn;
       mL = mn * kLog2e;
+      mth = mn + kLazy;
     }
     weights(lg, p);
   }
@@ -737,7 +756,10 @@ __device__ __forceinline__ void load_vals(rsrc_t rv, rsrc_t rvn, int t, int edge
                                           ValTile& T) {
   constexpr int RB = 3 * D / 8;
   const int gq = lane >> 4;
-  const uint32_t base = (uint32_t)(16 * t + 4 * gq) * RB + val_byte<D>(lane);
+  uint32_t base = (uint32_t)(16 * t + 4 * gq) * RB + val_byte<D>(lane);
+  // kept opaque so that the row steps j * RB become immediate offsets of
+  // the loads (range-checked like the register part) instead of adds
+  asm("" : "+v"(base));
 #pragma unroll
   for (int j = 0; j < 4; ++j) T.va[j] = ld32(rv, base + j * RB);
   T.vn = ldf4_edge(rvn, (uint32_t)(16 * t + 4 * gq) * 4, t == edge_tile);
@@ -814,7 +836,7 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   // lanes that hold no head's logits store into a dummy slot (no branch)
   const bool writer = !(c & 1) && (c >> 1) < a.G;
   float* lw = writer ? logits + (c >> 1) * ngp + 4 * gq : qf + 4 * lane;
-  float blo = kPosInf, bhi = kNegInf, cmax = kNegInf;
+  float blo = kPosInf, cmax = kNegInf;
   // rows of tile t past the last group (only the last tile has any)
   auto tail_rows = [&](int t) -> uint32_t {
     const int valid = a.ng - (16 * t + 4 * gq);
@@ -830,24 +852,24 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
           key_bits<D>(T.kw, lane, kw);
           f32x4 lg = qk3<D>(kw, qh, ql, lut3, lane4) * T.kn;
           *reinterpret_cast<f32x4*>(lw + (writer ? 16 * t : 0)) = lg;
-          // bounds of every score (max or mean over heads of these logits)
-          blo = fminf(blo, fminf(fminf(lg[0], lg[1]), fminf(lg[2], lg[3])));
-          bhi = fmaxf(bhi, fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])));
-          if (t == n_tiles - 1) {  // wave-uniform
+          // a lower bound of every score (max or mean over heads of these
+          // logits); the heads' maxima below bound them from above
+          blo = min3f(min3f(blo, lg[0], lg[1]), lg[2], lg[3]);
+          if (t == n_tiles - 1) {  // wave-uniform: rows past the last group
             const uint32_t tr = tail_rows(t);
 #pragma unroll
             for (int r = 0; r < 4; ++r) lg[r] = ((tr >> r) & 1u) ? kNegInf : lg[r];
           }
-          cmax = fmaxf(cmax, fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])));
+          cmax = max3f(max3f(cmax, lg[0], lg[1]), lg[2], lg[3]);
         });
   }
   blo = wave_min(blo);
-  bhi = wave_max(bhi);
   cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
   cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+  const float whi = wave_max(writer ? cmax : kNegInf);  // this wave's largest logit
   if (lane == 0) {
     s_lo[wave] = blo;
-    s_hi[wave] = bhi;
+    s_hi[wave] = whi;
   }
   if (gq == 0 && writer) s_mh[wave][c >> 1] = cmax;
   // From here on every wave streams the values of ALL summaries into the
@@ -870,13 +892,13 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   float m0 = kNegInf;
   for (int w = 0; w < kWaves; ++w) m0 = fmaxf(m0, s_mh[w][hcol]);
   Softmax<D> st;
-  st.init(m0 + a.bias);
+  // the summary bias shifts every summary logit and the reference alike, so
+  // the weights are taken without it and it is added to m at the end
+  st.init(m0);
   const uint32_t vsh = val_shift<D>(lane);
   // sign = +1: add the rows' contributions; -1: subtract them
-  auto consume = [&](const float (&lgr)[4], const ValTile& V, float sign) {
-    float lg[4], p[4], w[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) lg[r] = lgr[r] + a.bias;
+  auto consume = [&](const float (&lg)[4], const ValTile& V, float sign) {
+    float p[4], w[4];
     st.weights(lg, p);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -1056,6 +1078,7 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
     consume(clg, ct, -1.f);
   }
   lds_barrier();  // the logits are no longer needed: reuse as scratch
+  st.m += a.bias;
   combine_waves<D>(st, a.G, scratch, a.part + (size_t)unit * a.G * (D + 2), tid);
 }
 
@@ -1078,7 +1101,6 @@ struct TokTile {
   f32x4 kn;        // key norms of rows 4gq+i
   f32x4 vn;        // value norms of rows 4gq+i
   uint32_t va[4];  // value bits of rows 4gq+j for lane rho = lane&15
-  uint32_t ok;     // bit i: row 4gq+i is a real token
 };
 
 // Per-unit buffers of the token tiles.  Tile t < n1t holds L1 rows 16t ..
@@ -1108,9 +1130,11 @@ __device__ __forceinline__ TokBufs tok_bufs(const TokArgs& a, int unit) {
 // kFar (reads zero) for a slot without a valid group; recoff[beta] = kFar.
 // Loads of tile t: straight-line code for both kinds (the wave-uniform kind
 // picks the buffers, per-lane selects pick the offsets).
+// Loads of tile t given the record offsets bk (key rows) and br (value
+// rows, norms) of its archive slot(s); an L1 tile ignores them.
 template <int D, int N>
-__device__ __forceinline__ void load_tok(const TokBufs& B, const int32_t* recoff, int t, int n1t,
-                                         int n1, int beta, int lane, TokTile& T) {
+__device__ __forceinline__ void load_tok_at(const TokBufs& B, int t, int n1t, int n1, uint32_t bk,
+                                            uint32_t br, int lane, TokTile& T) {
   constexpr int CB = D / 2;
   constexpr uint32_t KB = D / 8;  // key code bytes per lane
   const int n = lane & 15, gq = lane >> 4;
@@ -1118,17 +1142,13 @@ __device__ __forceinline__ void load_tok(const TokBufs& B, const int32_t* recoff
   const int tr = (N == 16) ? 4 * gq : 4 * (gq & 1);  // first value row within the group
   const uint32_t vl = (D == 128) ? 4u * n : 4u * (n >> 1);  // this lane's value dword
   const bool l1 = t < n1t;
-  const int f = t - n1t;
-  const int s0 = (N == 16) ? f : 2 * f;
-  const int xk = (N == 16) ? 0 : (n >> 3), xr = (N == 16) ? 0 : (gq >> 1);
-  const uint32_t bk = (uint32_t)recoff[min(max(s0 + xk, 0), beta)];
-  const uint32_t br = (uint32_t)recoff[min(max(s0 + xr, 0), beta)];
   const uint32_t r0 = 16u * (uint32_t)t;
   // an offset built on kFar stays past the end of every buffer (reads zero)
   const uint32_t ko = l1 ? (r0 + n) * CB + KB * gq : bk + tk * CB + KB * gq;
   const uint32_t kno = l1 ? (r0 + 4 * gq) * 4 : br + N * CB + 4 * tr;
   const uint32_t vno = l1 ? (r0 + 4 * gq) * 4 : br + N * (2 * CB + 4) + 4 * tr;
-  const uint32_t vo = (l1 ? (r0 + 4 * gq) * CB : br + N * (CB + 4) + tr * CB) + vl;
+  uint32_t vo = (l1 ? (r0 + 4 * gq) * CB : br + N * (CB + 4) + tr * CB) + vl;
+  asm("" : "+v"(vo));  // the row steps j * CB become immediate offsets
   const rsrc_t rk = l1 ? B.l1k : B.l3, rkn = l1 ? B.l1kn : B.l3;
   const rsrc_t rv = l1 ? B.l1v : B.l3, rvn = l1 ? B.l1vn : B.l3;
   if constexpr (D == 128) {
@@ -1142,15 +1162,56 @@ __device__ __forceinline__ void load_tok(const TokBufs& B, const int32_t* recoff
   T.vn = ldf4_edge(rvn, vno, edge);
 #pragma unroll
   for (int j = 0; j < 4; ++j) T.va[j] = ld32(rv, vo + j * CB);
-  const int valid = n1 - (int)(r0 + 4 * gq);
-  const uint32_t ok1 = valid >= 4 ? 15u : (valid <= 0 ? 0u : ((1u << valid) - 1u));
-  T.ok = l1 ? ok1 : (br != kFar ? 15u : 0u);
+}
+// First archive slot of tile t (wave-uniform; 0 for L1 tiles, whose loads
+// ignore the record offsets).
+template <int N>
+__device__ __forceinline__ int tile_slot(int t, int n1t) {
+  return max(t - n1t, 0) * (N == 16 ? 1 : 2);
+}
+// Loads of tile t, the record offsets read from recoff (which covers every
+// slot a tile of the pipeline can name, see tok_slots).
+template <int D, int N>
+__device__ __forceinline__ void load_tok(const TokBufs& B, const int32_t* recoff, int t, int n1t,
+                                         int n1, int lane, TokTile& T) {
+  const int n = lane & 15, gq = lane >> 4;
+  const int xk = (N == 16) ? 0 : (n >> 3), xr = (N == 16) ? 0 : (gq >> 1);
+  const int32_t* rs = recoff + tile_slot<N>(t, n1t);
+  const uint32_t bk = (uint32_t)rs[xk];
+  const uint32_t br = (uint32_t)rs[xr];
+  load_tok_at<D, N>(B, t, n1t, n1, bk, br, lane, T);
+}
+// Entries of the record-offset table: every slot of the fetched tiles and of
+// the tiles the pipeline loads past the last one (they read kFar).  A wave's
+// loads run at most 2K-2 of its tiles (8 tile indices apart) past its last.
+template <int N>
+__host__ __device__ constexpr int tok_slots(int beta) {
+  return (N == 16 ? 1 : 2) * ((N == 16 ? beta : (beta + 1) / 2) + 2 * kWaves * kTokDepth);
 }
 
-template <int D>
-__device__ __forceinline__ void consume_tok(const TokTile& T, const half8 (&qh)[D / 32],
-                                            const uint32_t* lut4, int lane, uint32_t lane4,
-                                            Softmax<D>& st) {
+// Rows of tile t that hold no token: lg = -inf.  Only the ragged last L1
+// tile and archive tiles with an empty slot have any (wave-uniform test by
+// the caller).
+template <int N>
+__device__ __forceinline__ void mask_rows(float (&lg)[4], int t, int n1t, int n1, int beta,
+                                          const int32_t* recoff, int lane) {
+  const int gq = lane >> 4;
+  uint32_t ok;
+  if (t < n1t) {
+    const int valid = n1 - (16 * t + 4 * gq);
+    ok = valid >= 4 ? 15u : (valid <= 0 ? 0u : ((1u << valid) - 1u));
+  } else {
+    const int s = tile_slot<N>(t, n1t) + ((N == 16) ? 0 : (gq >> 1));
+    ok = (s < beta && recoff[s] != (int32_t)kFar) ? 15u : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lg[i] = ((ok >> i) & 1u) ? lg[i] : kNegInf;
+}
+
+template <int D, typename MaskF>
+__device__ __forceinline__ void consume_tok(const TokTile& T, bool masked, MaskF mask,
+                                            const half8 (&qh)[D / 32], const uint32_t* lut4,
+                                            int lane, uint32_t lane4, Softmax<D>& st) {
   // two accumulators so that consecutive MFMAs do not wait on each other
   f32x4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -1163,7 +1224,8 @@ __device__ __forceinline__ void consume_tok(const TokTile& T, const half8 (&qh)[
   const f32x4 acc = acc2[0] + acc2[1];
   float lg[4], p[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lg[i] = ((T.ok >> i) & 1u) ? acc[i] * T.kn[i] : kNegInf;
+  for (int i = 0; i < 4; ++i) lg[i] = acc[i] * T.kn[i];
+  if (masked) mask(lg);  // wave-uniform
   st.update(lg, p);
   float w[4];
 #pragma unroll
@@ -1185,8 +1247,10 @@ void token_kernel(TokArgs a) {
   __shared__ __align__(16) uint32_t s_lut4[256 * kNC4];
   __shared__ float s_cb[16];
   __shared__ uint32_t s_vsb[kMaxG * (D / 8)];
-  // dynamic layout: [qf 8*(D+4) f32][summary partial 8*(D+2) f32][recoff beta+1];
-  // the combine scratch reuses the table once the tiles are done.
+  __shared__ int s_bad;  // some slot names no record
+  // dynamic layout: [qf 8*(D+4) f32][summary partial 8*(D+2) f32]
+  //   [recoff tok_slots(beta)]; the combine scratch reuses the table once the
+  //   tiles are done.
   const uint32_t* lut4 = s_lut4;
   float* qf = reinterpret_cast<float*>(smem);
   float* part = qf + kMaxG * kQS<D>;
@@ -1204,8 +1268,13 @@ void token_kernel(TokArgs a) {
   const size_t rec = (size_t)N * (D + 8);
   constexpr int LPV = D / 8;
 
-  // global loads first: the set-up inputs and the summary partial merged at
-  // the end; the record offsets are needed before the first archive tile
+  // global loads first: this wave's first L1 tiles (they need no record
+  // offsets), the set-up inputs and the summary partial merged at the end
+  TokTile tt[kTokDepth];
+#pragma unroll
+  for (int j = 0; j < kTokDepth - 1; ++j)
+    if (wave + j * kWaves < n1t)  // wave-uniform
+      load_tok_at<D, N>(B, wave + j * kWaves, n1t, a.n1, kFar, kFar, lane, tt[j]);
   const float cbv = (tid < 16) ? a.cb4[tid] : 0.f;
   QueryIn qin;
   load_query<D>(a.q + (size_t)unit * a.G * D, a.k_signs + kvh * (D / 32), a.G, tid, qin);
@@ -1218,12 +1287,16 @@ void token_kernel(TokArgs a) {
     const int k = tid + r * kThreads;
     pv[r] = (k < np) ? (ps ? ps[k] : ((k % (D + 2)) == 0 ? kNegInf : 0.f)) : 0.f;
   }
-  for (int s = tid; s <= a.beta; s += kThreads) {
+  bool bad = false;
+  for (int s = tid; s < tok_slots<N>(a.beta); s += kThreads) {
     int g = -1;
     if (s < a.beta) g = a.l3_staged ? s : a.idx[(size_t)unit * a.beta + s];
     const int lim = a.l3_staged ? a.beta : a.ng;
-    recoff[s] = (g >= 0 && g < lim) ? (int32_t)((uint32_t)g * (uint32_t)rec) : (int32_t)kFar;
+    const bool ok = g >= 0 && g < lim;
+    bad |= s < a.beta && !ok;
+    recoff[s] = ok ? (int32_t)((uint32_t)g * (uint32_t)rec) : (int32_t)kFar;
   }
+  if (tid == 0) s_bad = 0;
   if (tid < 16) s_cb[tid] = cbv;
   if (tid < kMaxG * LPV) s_vsb[tid] = vsb;
 #pragma unroll
@@ -1231,11 +1304,12 @@ void token_kernel(TokArgs a) {
     if (tid + r * kThreads < np) part[tid + r * kThreads] = pv[r];
   rotate_query<D>(qin, a.scale * rsqrtf((float)D), qf, tid);
   lds_barrier();
-  // first two tiles of this wave, loading while the table is built
-  TokTile tt[kTokDepth];
+  if (bad) s_bad = 1;
+  // this wave's first archive tiles, loading while the table is built
 #pragma unroll
   for (int j = 0; j < kTokDepth - 1; ++j)
-    load_tok<D, N>(B, recoff, wave + j * kWaves, n1t, a.n1, a.beta, lane, tt[j]);
+    if (wave + j * kWaves >= n1t)  // wave-uniform
+      load_tok<D, N>(B, recoff, wave + j * kWaves, n1t, a.n1, lane, tt[j]);
   build_lut4(s_lut4, s_cb, tid);
   half8 qh[D / 32], ql[D / 32];
   query_operands<D>(qf, lane, qh, ql);
@@ -1244,12 +1318,25 @@ void token_kernel(TokArgs a) {
   Softmax<D> st;
   st.init(kNegInf);
   {
+    // tiles with rows that hold no token: the ragged last L1 tile, the last
+    // archive tile when its second slot is empty, every archive tile when
+    // some slot names no record
+    const bool any_bad = __builtin_amdgcn_readfirstlane(s_bad) != 0;
+    const int ragged = (a.n1 & 15) ? n1t - 1 : -1;
+    const int half = (N == 8 && (a.beta & 1)) ? total - 1 : -1;
     pipeline<kTokDepth>(
         wave_iters(total, wave), tt,
         [&](int i, TokTile& T) {
-          load_tok<D, N>(B, recoff, wave + i * kWaves, n1t, a.n1, a.beta, lane, T);
+          load_tok<D, N>(B, recoff, wave + i * kWaves, n1t, a.n1, lane, T);
         },
-        [&](int i, const TokTile& T) { consume_tok<D>(T, qh, lut4, lane, lane4, st); });
+        [&](int i, const TokTile& T) {
+          const int t = wave + i * kWaves;
+          const bool masked = t == ragged || t == half || (any_bad && t >= n1t);
+          consume_tok<D>(
+              T, masked,
+              [&](float (&lg)[4]) { mask_rows<N>(lg, t, n1t, a.n1, a.beta, recoff, lane); }, qh,
+              lut4, lane, lane4, st);
+        });
   }
   lds_barrier();  // the table is no longer needed: reuse as scratch
   float* mine = scratch + kWaves * kMaxG * (D + 2);  // [G][D+2] this unit's token partial
@@ -1302,7 +1389,8 @@ size_t summary_smem(int D, const StepShape& s) {
 }
 
 size_t token_smem(int D, const StepShape& s) {
-  return (size_t)kMaxG * (D + 4) * 4 + (size_t)kMaxG * (D + 2) * 4 + (size_t)(s.beta + 1) * 4;
+  const int slots = s.group_n == 16 ? tok_slots<16>(s.beta) : tok_slots<8>(s.beta);
+  return (size_t)kMaxG * (D + 4) * 4 + (size_t)kMaxG * (D + 2) * 4 + (size_t)slots * 4;
 }
 
 }  // namespace
