@@ -319,6 +319,20 @@ extern "C" int hsq_decode_step(const float* q, int B, int Hq, int Hkv, int d, co
   if ((rc = attn_args("hsq_decode_step", q, l1k, l1k_n, l1v, l1v_n, n_l1, l2k, l2k_n, l2v, l2v_n,
                       n_groups, l3, k_signs, v_signs, cb4, cb3, out)))
     return rc;
+  if (agg != HSQ_AGG_MAX && agg != HSQ_AGG_MEAN) return fail(HSQ_ERR_ARG, "hsq_decode_step: bad agg");
+  const int b = beta < n_groups ? beta : n_groups;
+  StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, b};
+  Workspace w;
+  if ((rc = step_common("hsq_decode_step", s, workspace, ws_bytes, w))) return rc;
+  if (step_fused_ok(s)) {  // one launch: route and attend on the same work-group
+    StepTensors t{};
+    t.q = q; t.l1k = l1k; t.l1k_n = l1k_n; t.l1v = l1v; t.l1v_n = l1v_n;
+    t.l2k = l2k; t.l2k_n = l2k_n; t.l2v = l2v; t.l2v_n = l2v_n; t.l3 = l3; t.l3_staged = 0;
+    t.k_signs = k_signs; t.v_signs = v_signs; t.cb4 = cb4; t.cb3 = cb3; t.scale = scale;
+    t.summary_bias = summary_bias; t.agg = agg; t.out = out;
+    return check_hip(launch_step(s, t, b > 0 ? topk_idx : nullptr, as_stream(stream)),
+                     "hsq_decode_step");
+  }
   if ((rc = hsq_step_route(q, B, Hq, Hkv, d, n_l1, l2k, l2k_n, l2v, l2v_n, n_groups, group_n, beta,
                            agg, k_signs, cb3, scale, summary_bias, topk_idx, workspace, ws_bytes,
                            stream)))

@@ -95,6 +95,11 @@ hipError_t launch_route(const StepShape& s, const StepTensors& t, const Workspac
                         int32_t* idx_out, hipStream_t st);
 hipError_t launch_attn(const StepShape& s, const StepTensors& t, const Workspace& w, char* ws,
                        const int32_t* idx, hipStream_t st);
+// The whole step in one launch (route + attend per work-group); only for
+// shapes where step_fused_ok holds.  idx_out (optional): [units][beta].
+int step_fused_ok(const StepShape& s);
+hipError_t launch_step(const StepShape& s, const StepTensors& t, int32_t* idx_out,
+                       hipStream_t st);
 hipError_t launch_gather(const uint8_t* src, size_t rec_bytes, int units, int n_groups,
                          const int32_t* idx, int beta, uint8_t* dst, hipStream_t st);
 

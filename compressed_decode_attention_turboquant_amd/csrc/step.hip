@@ -71,6 +71,7 @@ constexpr int kNC3 = 32;                 // 3-bit table copies (lanes l, l+32 sh
 constexpr int kNC4 = 64;                 // 4-bit table copies (one per lane)
 constexpr int kMaxGroups = 16384;
 constexpr int kMaxLogits = 12288;        // G * n_groups kept in LDS
+constexpr size_t kMaxFusedLds = 150 * 1024;  // dynamic LDS of the one-launch step
 constexpr uint32_t kFar = 0x80000000u;   // buffer offset that reads as zero
 constexpr float kNegInf = -INFINITY;
 constexpr float kPosInf = INFINITY;
@@ -765,37 +766,87 @@ __device__ __forceinline__ void load_vals(rsrc_t rv, rsrc_t rvn, int t, int edge
   T.vn = ldf4_edge(rvn, (uint32_t)(16 * t + 4 * gq) * 4, t == edge_tile);
 }
 
+// Byte offsets of the route body's LDS arrays after `base` (16-byte aligned):
+// [logits G*ngp f32][keys u32, then the emitted selection][hist 256]
+// [fetched bitmap][selected candidates][candidates (uint2) or the fallback's
+// selection].
+struct RouteLayout {
+  int logits, keys, hist, fmask, cmask, cand, end;
+};
+__host__ __device__ inline RouteLayout route_layout(int G, int ng, int beta, int base) {
+  const int ngp = (ng + 15) & ~15;
+  const int words4 = ((ngp + 31) / 32 + 3) & ~3;
+  const int cand_bytes = (beta * 4 > (ngp < kCandCap ? ngp : kCandCap) * 8)
+                             ? beta * 4 : (ngp < kCandCap ? ngp : kCandCap) * 8;
+  RouteLayout r;
+  r.logits = base;
+  r.keys = r.logits + G * ngp * 4;
+  r.hist = r.keys + ((ngp + 31) & ~31) * 4;
+  r.fmask = r.hist + 256 * 4;
+  r.cmask = r.fmask + words4 * 4;
+  r.cand = r.cmask + words4 * 4;
+  r.end = r.cand + ((cand_bytes + 15) & ~15);
+  return r;
+}
+
+// LDS used by the route body.  lut3 and the tables' users are inlined, so a
+// table at a fixed address folds into the reads' offsets.
+struct RouteLds {
+  uint32_t* lut3;   // 64 * kNC3 words
+  float* qf;        // rotated query rows, kMaxG * kQS<D>
+  float* logits;
+  uint32_t* keys;
+  int* hist;
+  uint32_t* fmask;
+  uint32_t* cmask;
+  uint2* cand;
+  float* dummy;     // 64 x 4 floats: landing slot of the lanes without a head
+  float* scratch;   // wave-combine scratch, kWaves * kMaxG * (D+2) floats, free
+                    // once the logits are no longer needed
+};
 template <int D>
-__global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
+__device__ __forceinline__ RouteLds route_lds(char* base, const RouteLayout& r, uint32_t* lut3,
+                                              float* qf, float* dummy, float* scratch) {
+  RouteLds L;
+  L.lut3 = lut3;
+  L.qf = qf;
+  L.logits = reinterpret_cast<float*>(base + r.logits);
+  L.keys = reinterpret_cast<uint32_t*>(base + r.keys);
+  L.hist = reinterpret_cast<int*>(base + r.hist);
+  L.fmask = reinterpret_cast<uint32_t*>(base + r.fmask);
+  L.cmask = reinterpret_cast<uint32_t*>(base + r.cmask);
+  L.cand = reinterpret_cast<uint2*>(base + r.cand);
+  L.dummy = dummy;
+  L.scratch = scratch;
+  return L;
+}
+
+// Router, top-beta and summary partial of one unit (the whole work-group).
+// part_out: [G][D+2] (m, l, O) of the summary partial (global or LDS);
+// recoff: if not null, LDS table that receives g * rec for selection slot s.
+template <int D>
+__device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, float* part_out,
+                                           int32_t* recoff, uint32_t rec, int unit) {
   constexpr int CB3 = 3 * D / 8;
-  extern __shared__ __align__(16) char smem[];
-  __shared__ __align__(16) uint32_t s_lut3[64 * kNC3];
   __shared__ float s_cb[8];
   __shared__ int s_tmp[kWaves];
   __shared__ int s_sel[4];
   __shared__ float s_lo[kWaves], s_hi[kWaves];
   __shared__ float s_mh[kWaves][kMaxG];
-  // dynamic layout: [qf 8*(D+4) f32][logits G*ngp f32][keys u32][hist 256]
-  //   [fetched bitmap: buckets above the threshold][selected candidates]
-  //   [candidates (uint2), or the fallback's selection].  qf doubles as the
-  //   landing slot of the phase-1 stores of lanes that hold no head; the
-  //   emitted selection reuses the keys once the threshold step is done (the
-  //   candidates may still be read by slower waves while it is written); the
-  //   wave-combine scratch reuses the front once the tiles are done.
   const int ngp = (a.ng + 15) & ~15;
-  float* qf = reinterpret_cast<float*>(smem);
-  float* logits = qf + kMaxG * kQS<D>;
-  uint32_t* keys = reinterpret_cast<uint32_t*>(logits + a.G * ngp);
-  int* hist = reinterpret_cast<int*>(keys + ((ngp + 31) & ~31));
-  uint32_t* fmask = reinterpret_cast<uint32_t*>(hist + 256);
-  uint32_t* cmask = fmask + (((ngp + 31) / 32 + 3) & ~3);
-  uint2* cand = reinterpret_cast<uint2*>(cmask + (((ngp + 31) / 32 + 3) & ~3));
+  float* qf = L.qf;
+  float* logits = L.logits;
+  uint32_t* keys = L.keys;
+  int* hist = L.hist;
+  uint32_t* fmask = L.fmask;
+  uint32_t* cmask = L.cmask;
+  uint2* cand = L.cand;
+  // the emitted selection reuses the keys once the threshold step is done
+  // (the candidates may still be read by slower waves while it is written)
   int32_t* sel = reinterpret_cast<int32_t*>(keys);
-  float* scratch = reinterpret_cast<float*>(smem);
-  const uint32_t* lut3 = s_lut3;
+  const uint32_t* lut3 = L.lut3;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int unit = blockIdx.x;
   const int kvh = unit % a.Hkv;
   const uint32_t lane4 = (uint32_t)(lane & 31) << 2;
   const int c = lane & 15, gq = lane >> 4;
@@ -826,7 +877,7 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   for (int b = tid; b < 256; b += kThreads) hist[b] = 0;
   if (tid < 4) s_sel[tid] = 0;
   lds_barrier();
-  build_lut3(s_lut3, s_cb, tid);
+  build_lut3(L.lut3, s_cb, tid);
   half8 qh[D / 32], ql[D / 32];
   query_operands<D>(qf, lane, qh, ql);
   lds_barrier();
@@ -835,7 +886,7 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   const int n_tiles = ngp >> 4;
   // lanes that hold no head's logits store into a dummy slot (no branch)
   const bool writer = !(c & 1) && (c >> 1) < a.G;
-  float* lw = writer ? logits + (c >> 1) * ngp + 4 * gq : qf + 4 * lane;
+  float* lw = writer ? logits + (c >> 1) * ngp + 4 * gq : L.dummy + 4 * lane;
   float blo = kPosInf, cmax = kNegInf;
   // rows of tile t past the last group (only the last tile has any)
   auto tail_rows = [&](int t) -> uint32_t {
@@ -1039,7 +1090,8 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
         while (m) {
           const int g = 32 * w + __ffs(m) - 1;
           sel[pos] = g;
-          if (a.want_topk) a.idx[(size_t)unit * a.beta + pos] = g;
+          if (a.want_topk && a.idx) a.idx[(size_t)unit * a.beta + pos] = g;
+          if (recoff) recoff[pos] = (int32_t)((uint32_t)g * rec);
           ++pos;
           m &= m - 1u;
         }
@@ -1079,7 +1131,21 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   }
   lds_barrier();  // the logits are no longer needed: reuse as scratch
   st.m += a.bias;
-  combine_waves<D>(st, a.G, scratch, a.part + (size_t)unit * a.G * (D + 2), tid);
+  combine_waves<D>(st, a.G, L.scratch, part_out, tid);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
+  // dynamic layout: [qf 8*(D+4) f32][route_layout]; qf doubles as the landing
+  // slot of the phase-1 stores of lanes that hold no head; the wave-combine
+  // scratch reuses the front once the tiles are done.
+  extern __shared__ __align__(16) char smem[];
+  __shared__ __align__(16) uint32_t s_lut3[64 * kNC3];
+  float* qf = reinterpret_cast<float*>(smem);
+  const RouteLayout r = route_layout(a.G, a.ng, a.beta, kMaxG * kQS<D> * 4);
+  const RouteLds L = route_lds<D>(smem, r, s_lut3, qf, qf, qf);
+  const int unit = blockIdx.x;
+  route_unit<D>(a, L, a.part + (size_t)unit * a.G * (D + 2), nullptr, 0u, unit);
 }
 
 // ----------------------------------------------------------- token kernel ---
@@ -1239,6 +1305,107 @@ __device__ __forceinline__ void consume_tok(const TokTile& T, bool masked, MaskF
   pv4<D>(va, weight_operand(w, lane), lane4, lut4, st.O);
 }
 
+// LDS used by the attend body.  lut4 is inlined as a fixed address.
+struct AttendLds {
+  uint32_t* lut4;   // 256 * kNC4 words; the combine scratch once the tiles are done
+  float* qf;        // rotated query rows, kMaxG * kQS<D>
+  float* part;      // summary partial [G][D+2]
+  int32_t* recoff;  // record offset per slot, tok_slots(beta) entries
+  float* cb;        // 16 centroids of the 4-bit codebook
+  uint32_t* vsb;    // V sign byte per (head, lane of the inverse rotation)
+};
+
+// L1 + fetched-token attention of one unit, merged with the summary partial,
+// inverse V rotation, output.  On entry every array of L except the table
+// is filled and visible to all waves, and the table is free; tt[j] holds the
+// loads of this wave's tile wave + 8j already when l1_issued and that tile is
+// an L1 tile.  bad_flag (read after the first barrier here), if not null:
+// nonzero when some slot of recoff names no record.
+template <int D, int N>
+__device__ __forceinline__ void attend_unit(const TokArgs& a, const AttendLds& L,
+                                            TokTile (&tt)[kTokDepth], bool l1_issued,
+                                            const int* bad_flag, int unit) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const uint32_t lane4 = (uint32_t)lane << 2;
+  const uint32_t* lut4 = L.lut4;
+  const TokBufs B = tok_bufs<D, N>(a, unit);
+  const int n1t = (a.n1 + 15) / 16;
+  const int nft = (N == 16) ? a.beta : (a.beta + 1) / 2;
+  const int total = n1t + nft;
+  constexpr int LPV = D / 8;
+
+  // this wave's first tiles not issued yet, loading while the table is built
+#pragma unroll
+  for (int j = 0; j < kTokDepth - 1; ++j)
+    if (!(l1_issued && wave + j * kWaves < n1t))  // wave-uniform
+      load_tok<D, N>(B, L.recoff, wave + j * kWaves, n1t, a.n1, lane, tt[j]);
+  build_lut4(L.lut4, L.cb, tid);
+  half8 qh[D / 32], ql[D / 32];
+  query_operands<D>(L.qf, lane, qh, ql);
+  lds_barrier();
+
+  Softmax<D> st;
+  st.init(kNegInf);
+  {
+    // tiles with rows that hold no token: the ragged last L1 tile, the last
+    // archive tile when its second slot is empty, every archive tile when
+    // some slot names no record
+    const bool any_bad = bad_flag && __builtin_amdgcn_readfirstlane(*bad_flag) != 0;
+    const int ragged = (a.n1 & 15) ? n1t - 1 : -1;
+    const int half = (N == 8 && (a.beta & 1)) ? total - 1 : -1;
+    pipeline<kTokDepth>(
+        wave_iters(total, wave), tt,
+        [&](int i, TokTile& T) {
+          load_tok<D, N>(B, L.recoff, wave + i * kWaves, n1t, a.n1, lane, T);
+        },
+        [&](int i, const TokTile& T) {
+          const int t = wave + i * kWaves;
+          const bool masked = t == ragged || t == half || (any_bad && t >= n1t);
+          consume_tok<D>(
+              T, masked,
+              [&](float (&lg)[4]) { mask_rows<N>(lg, t, n1t, a.n1, a.beta, L.recoff, lane); },
+              qh, lut4, lane, lane4, st);
+        });
+  }
+  lds_barrier();  // the table is no longer needed: reuse as scratch
+  float* scratch = reinterpret_cast<float*>(L.lut4);
+  float* mine = scratch + kWaves * kMaxG * (D + 2);  // [G][D+2] this unit's token partial
+  combine_waves<D>(st, a.G, scratch, mine, tid);
+
+  // merge with the summary partial, normalise
+  float* o = mine + kMaxG * (D + 2);  // [G][D]
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int k = tid + r * kThreads, h = k / D, e = k % D;
+    if (k >= a.G * D) break;
+    const float* mp = mine + h * (D + 2);
+    const float m1 = mp[0], l1 = mp[1], v1 = mp[2 + e];
+    const float* pp = L.part + h * (D + 2);
+    const float m2 = pp[0], l2 = pp[1], v2 = pp[2 + e];
+    const float M = fmaxf(m1, m2);
+    const float w1 = (m1 == kNegInf) ? 0.f : __expf(m1 - M);
+    const float w2 = (m2 == kNegInf) ? 0.f : __expf(m2 - M);
+    const float Lsum = w1 * l1 + w2 * l2;
+    o[k] = (Lsum > 0.f) ? (w1 * v1 + w2 * v2) / Lsum : 0.f;
+  }
+  lds_barrier();
+  // inverse V rotation: out = D H o / sqrt(D)
+  if (tid < kMaxG * LPV) {
+    const int h = tid / LPV, sub = tid % LPV;
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = (h < a.G) ? o[h * D + 8 * sub + k] : 0.f;
+    fwht8xlanes<LPV>(v, sub);
+    if (h < a.G) {
+      const uint32_t sb = L.vsb[tid];
+      const float sc = rsqrtf((float)D);
+      float* dst = a.out + ((size_t)unit * a.G + h) * D + 8 * sub;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) dst[k] = flip(v[k] * sc, (sb >> k) & 1u);
+    }
+  }
+}
+
 // at most 128 VGPRs so that two work-groups (the LDS limit) fit on a CU
 template <int D, int N>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
@@ -1249,32 +1416,30 @@ void token_kernel(TokArgs a) {
   __shared__ uint32_t s_vsb[kMaxG * (D / 8)];
   __shared__ int s_bad;  // some slot names no record
   // dynamic layout: [qf 8*(D+4) f32][summary partial 8*(D+2) f32]
-  //   [recoff tok_slots(beta)]; the combine scratch reuses the table once the
-  //   tiles are done.
-  const uint32_t* lut4 = s_lut4;
-  float* qf = reinterpret_cast<float*>(smem);
-  float* part = qf + kMaxG * kQS<D>;
-  int32_t* recoff = reinterpret_cast<int32_t*>(part + kMaxG * (D + 2));
-  float* scratch = reinterpret_cast<float*>(s_lut4);
+  //   [recoff tok_slots(beta)]
+  AttendLds L;
+  L.lut4 = s_lut4;
+  L.qf = reinterpret_cast<float*>(smem);
+  L.part = L.qf + kMaxG * kQS<D>;
+  L.recoff = reinterpret_cast<int32_t*>(L.part + kMaxG * (D + 2));
+  L.cb = s_cb;
+  L.vsb = s_vsb;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int tid = threadIdx.x, wave = wave_id();
   const int unit = blockIdx.x;
   const int kvh = unit % a.Hkv;
-  const uint32_t lane4 = (uint32_t)lane << 2;
-  const TokBufs B = tok_bufs<D, N>(a, unit);
   const int n1t = (a.n1 + 15) / 16;
-  const int nft = (N == 16) ? a.beta : (a.beta + 1) / 2;
-  const int total = n1t + nft;
   const size_t rec = (size_t)N * (D + 8);
   constexpr int LPV = D / 8;
 
   // global loads first: this wave's first L1 tiles (they need no record
   // offsets), the set-up inputs and the summary partial merged at the end
+  const TokBufs B = tok_bufs<D, N>(a, unit);
   TokTile tt[kTokDepth];
 #pragma unroll
   for (int j = 0; j < kTokDepth - 1; ++j)
     if (wave + j * kWaves < n1t)  // wave-uniform
-      load_tok_at<D, N>(B, wave + j * kWaves, n1t, a.n1, kFar, kFar, lane, tt[j]);
+      load_tok_at<D, N>(B, wave + j * kWaves, n1t, a.n1, kFar, kFar, tid & 63, tt[j]);
   const float cbv = (tid < 16) ? a.cb4[tid] : 0.f;
   QueryIn qin;
   load_query<D>(a.q + (size_t)unit * a.G * D, a.k_signs + kvh * (D / 32), a.G, tid, qin);
@@ -1294,96 +1459,97 @@ void token_kernel(TokArgs a) {
     const int lim = a.l3_staged ? a.beta : a.ng;
     const bool ok = g >= 0 && g < lim;
     bad |= s < a.beta && !ok;
-    recoff[s] = ok ? (int32_t)((uint32_t)g * (uint32_t)rec) : (int32_t)kFar;
+    L.recoff[s] = ok ? (int32_t)((uint32_t)g * (uint32_t)rec) : (int32_t)kFar;
   }
   if (tid == 0) s_bad = 0;
   if (tid < 16) s_cb[tid] = cbv;
   if (tid < kMaxG * LPV) s_vsb[tid] = vsb;
 #pragma unroll
   for (int r = 0; r < 3; ++r)
-    if (tid + r * kThreads < np) part[tid + r * kThreads] = pv[r];
-  rotate_query<D>(qin, a.scale * rsqrtf((float)D), qf, tid);
+    if (tid + r * kThreads < np) L.part[tid + r * kThreads] = pv[r];
+  rotate_query<D>(qin, a.scale * rsqrtf((float)D), L.qf, tid);
   lds_barrier();
-  if (bad) s_bad = 1;
-  // this wave's first archive tiles, loading while the table is built
-#pragma unroll
-  for (int j = 0; j < kTokDepth - 1; ++j)
-    if (wave + j * kWaves >= n1t)  // wave-uniform
-      load_tok<D, N>(B, recoff, wave + j * kWaves, n1t, a.n1, lane, tt[j]);
-  build_lut4(s_lut4, s_cb, tid);
-  half8 qh[D / 32], ql[D / 32];
-  query_operands<D>(qf, lane, qh, ql);
-  lds_barrier();
+  if (bad) s_bad = 1;  // read after the next barrier
+  attend_unit<D, N>(a, L, tt, true, &s_bad, unit);
+}
 
-  Softmax<D> st;
-  st.init(kNegInf);
-  {
-    // tiles with rows that hold no token: the ragged last L1 tile, the last
-    // archive tile when its second slot is empty, every archive tile when
-    // some slot names no record
-    const bool any_bad = __builtin_amdgcn_readfirstlane(s_bad) != 0;
-    const int ragged = (a.n1 & 15) ? n1t - 1 : -1;
-    const int half = (N == 8 && (a.beta & 1)) ? total - 1 : -1;
-    pipeline<kTokDepth>(
-        wave_iters(total, wave), tt,
-        [&](int i, TokTile& T) {
-          load_tok<D, N>(B, recoff, wave + i * kWaves, n1t, a.n1, lane, T);
-        },
-        [&](int i, const TokTile& T) {
-          const int t = wave + i * kWaves;
-          const bool masked = t == ragged || t == half || (any_bad && t >= n1t);
-          consume_tok<D>(
-              T, masked,
-              [&](float (&lg)[4]) { mask_rows<N>(lg, t, n1t, a.n1, a.beta, recoff, lane); }, qh,
-              lut4, lane, lane4, st);
-        });
-  }
-  lds_barrier();  // the table is no longer needed: reuse as scratch
-  float* mine = scratch + kWaves * kMaxG * (D + 2);  // [G][D+2] this unit's token partial
-  combine_waves<D>(st, a.G, scratch, mine, tid);
+// Byte layout of the one-launch step's dynamic LDS: [0, union) holds the
+// 4-bit table in the attend phase and, in the route phase, the 3-bit table
+// (first kLut3Bytes), the route arrays, the landing slot of lanes without a
+// head and, once the logits are done, the route's combine scratch; then the
+// arrays both phases use: [qf][summary partial][record offsets].
+constexpr int kLut4Bytes = 256 * kNC4 * 4;
+constexpr int kLut3Bytes = 64 * kNC3 * 4;
+struct StepLayout {
+  RouteLayout r;
+  int dummy, uni, qf, part, recoff, end;
+};
+template <int D, int N>
+__host__ __device__ inline StepLayout step_layout(int G, int ng, int beta) {
+  StepLayout L;
+  L.r = route_layout(G, ng, beta, kLut3Bytes);
+  L.dummy = L.r.end;
+  const int comb = kLut3Bytes + kWaves * kMaxG * (D + 2) * 4;
+  int u = L.dummy + 64 * 16;
+  u = u > kLut4Bytes ? u : kLut4Bytes;
+  u = u > comb ? u : comb;
+  L.uni = u;
+  L.qf = u;
+  L.part = L.qf + kMaxG * kQS<D> * 4;
+  L.recoff = L.part + kMaxG * (D + 2) * 4;
+  L.end = L.recoff + ((tok_slots<N>(beta) * 4 + 15) & ~15);
+  return L;
+}
 
-  // merge with the summary partial, normalise
-  float* o = mine + kMaxG * (D + 2);  // [G][D]
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int k = tid + r * kThreads, h = k / D, e = k % D;
-    if (k >= a.G * D) break;
-    const float* mp = mine + h * (D + 2);
-    const float m1 = mp[0], l1 = mp[1], v1 = mp[2 + e];
-    const float* pp = part + h * (D + 2);
-    const float m2 = pp[0], l2 = pp[1], v2 = pp[2 + e];
-    const float M = fmaxf(m1, m2);
-    const float w1 = (m1 == kNegInf) ? 0.f : __expf(m1 - M);
-    const float w2 = (m2 == kNegInf) ? 0.f : __expf(m2 - M);
-    const float L = w1 * l1 + w2 * l2;
-    o[k] = (L > 0.f) ? (w1 * v1 + w2 * v2) / L : 0.f;
-  }
-  lds_barrier();
-  // inverse V rotation: out = D H o / sqrt(D)
-  if (tid < kMaxG * LPV) {
-    const int h = tid / LPV, sub = tid % LPV;
-    float v[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = (h < a.G) ? o[h * D + 8 * sub + k] : 0.f;
-    fwht8xlanes<LPV>(v, sub);
-    if (h < a.G) {
-      const uint32_t sb = s_vsb[tid];
-      const float sc = rsqrtf((float)D);
-      float* dst = a.out + ((size_t)unit * a.G + h) * D + 8 * sub;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) dst[k] = flip(v[k] * sc, (sb >> k) & 1u);
-    }
-  }
+// The whole decode step in one launch (archive in device-visible memory,
+// n_groups > 0): route_unit, then attend_unit on the same work-group, with
+// the selection, the record offsets and the summary partial handed over in
+// LDS.
+template <int D, int N>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void step_kernel(SumArgs ra, TokArgs ta) {
+  extern __shared__ __align__(16) char smem[];
+  __shared__ float s_cb4[16];
+  __shared__ uint32_t s_vsb[kMaxG * (D / 8)];
+  const StepLayout S = step_layout<D, N>(ra.G, ra.ng, ra.beta);
+  uint32_t* tab = reinterpret_cast<uint32_t*>(smem);
+  float* qf = reinterpret_cast<float*>(smem + S.qf);
+  float* part = reinterpret_cast<float*>(smem + S.part);
+  int32_t* recoff = reinterpret_cast<int32_t*>(smem + S.recoff);
+  const int tid = threadIdx.x;
+  const int unit = blockIdx.x;
+  const int kvh = unit % ta.Hkv;
+  constexpr int LPV = D / 8;
+
+  // the attend phase's small inputs; the empty slots past beta
+  const float cbv = (tid < 16) ? ta.cb4[tid] : 0.f;
+  const uint32_t vsb =
+      (tid < kMaxG * LPV) ? sign_byte(ta.v_signs + kvh * (D / 32), tid % LPV) : 0u;
+  for (int s = ra.beta + tid; s < tok_slots<N>(ra.beta); s += kThreads) recoff[s] = (int32_t)kFar;
+  if (tid < 16) s_cb4[tid] = cbv;
+  if (tid < kMaxG * LPV) s_vsb[tid] = vsb;
+
+  const RouteLds R = route_lds<D>(smem, S.r, tab, qf, reinterpret_cast<float*>(smem + S.dummy),
+                                  reinterpret_cast<float*>(smem + kLut3Bytes));
+  // ends with a barrier: partial, selection and record offsets are visible
+  // and the union is free
+  route_unit<D>(ra, R, part, recoff, (uint32_t)(N * (D + 8)), unit);
+
+  AttendLds L;
+  L.lut4 = tab;
+  L.qf = qf;
+  L.part = part;
+  L.recoff = recoff;
+  L.cb = s_cb4;
+  L.vsb = s_vsb;
+  TokTile tt[kTokDepth];
+  attend_unit<D, N>(ta, L, tt, false, nullptr, unit);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t summary_smem(int D, const StepShape& s) {
-  const size_t ngp = (size_t)((s.n_groups + 15) & ~15);
-  const size_t body = (size_t)kMaxG * (D + 4) * 4 + (size_t)s.G * ngp * 4 +
-                      ((ngp + 31) & ~size_t(31)) * 4 + 256 * 4 +
-                      (((ngp + 31) / 32 + 3) & ~size_t(3)) * 8 +
-                      std::max((size_t)s.beta * 4, (size_t)std::min<size_t>(ngp, kCandCap) * 8);
+  const size_t body = (size_t)route_layout(s.G, s.n_groups, s.beta, kMaxG * (D + 4) * 4).end;
   const size_t comb = (size_t)kWaves * kMaxG * (D + 2) * 4;
   return std::max(body, comb);
 }
@@ -1391,6 +1557,14 @@ size_t summary_smem(int D, const StepShape& s) {
 size_t token_smem(int D, const StepShape& s) {
   const int slots = s.group_n == 16 ? tok_slots<16>(s.beta) : tok_slots<8>(s.beta);
   return (size_t)kMaxG * (D + 4) * 4 + (size_t)kMaxG * (D + 2) * 4 + (size_t)slots * 4;
+}
+
+size_t step_smem(const StepShape& s) {
+  if (s.d == 128)
+    return (size_t)(s.group_n == 16 ? step_layout<128, 16>(s.G, s.n_groups, s.beta).end
+                                    : step_layout<128, 8>(s.G, s.n_groups, s.beta).end);
+  return (size_t)(s.group_n == 16 ? step_layout<64, 16>(s.G, s.n_groups, s.beta).end
+                                  : step_layout<64, 8>(s.G, s.n_groups, s.beta).end);
 }
 
 }  // namespace
@@ -1411,14 +1585,30 @@ int step_limits_ok(const StepShape& s) {
          (size_t)s.n_groups * rec < 0x7fffffffu && (size_t)s.n_l1 * s.d < 0x7fffffffu;
 }
 
-template <int D>
-hipError_t summary_d(const StepShape& s, const StepTensors& t, const Workspace& w, char* ws,
-                     int mode, const int32_t* given, float* scores_out, int32_t* idx_out,
-                     hipStream_t st) {
+SumArgs sum_args(const StepShape& s, const StepTensors& t) {
   SumArgs a{};
   a.q = t.q; a.l2k = t.l2k; a.l2k_n = t.l2k_n; a.l2v = t.l2v; a.l2v_n = t.l2v_n;
   a.k_signs = t.k_signs; a.cb3 = t.cb3; a.scale = t.scale; a.bias = t.summary_bias;
   a.agg = t.agg; a.Hkv = s.Hkv; a.G = s.G; a.ng = s.n_groups; a.beta = s.beta;
+  return a;
+}
+
+TokArgs tok_args(const StepShape& s, const StepTensors& t) {
+  TokArgs a{};
+  a.q = t.q; a.l1k = t.l1k; a.l1k_n = t.l1k_n; a.l1v = t.l1v; a.l1v_n = t.l1v_n;
+  a.l3 = t.l3; a.l3_staged = t.l3_staged;
+  a.k_signs = t.k_signs; a.v_signs = t.v_signs; a.cb4 = t.cb4; a.scale = t.scale;
+  a.Hkv = s.Hkv; a.G = s.G; a.n1 = s.n_l1; a.ng = s.n_groups; a.group_n = s.group_n;
+  a.beta = s.beta;
+  a.out = t.out;
+  return a;
+}
+
+template <int D>
+hipError_t summary_d(const StepShape& s, const StepTensors& t, const Workspace& w, char* ws,
+                     int mode, const int32_t* given, float* scores_out, int32_t* idx_out,
+                     hipStream_t st) {
+  SumArgs a = sum_args(s, t);
   a.want_topk = (mode & ROUTE_TOPK) ? 1 : 0;
   a.want_partial = (mode & ROUTE_PARTIALS) ? 1 : 0;
   a.given = a.want_topk ? nullptr : given;
@@ -1442,14 +1632,9 @@ hipError_t launch_route(const StepShape& s, const StepTensors& t, const Workspac
 template <int D>
 hipError_t token_d(const StepShape& s, const StepTensors& t, const Workspace& w, char* ws,
                    const int32_t* idx, hipStream_t st) {
-  TokArgs a{};
-  a.q = t.q; a.l1k = t.l1k; a.l1k_n = t.l1k_n; a.l1v = t.l1v; a.l1v_n = t.l1v_n;
-  a.l3 = t.l3; a.l3_staged = t.l3_staged; a.idx = idx;
-  a.k_signs = t.k_signs; a.v_signs = t.v_signs; a.cb4 = t.cb4; a.scale = t.scale;
-  a.Hkv = s.Hkv; a.G = s.G; a.n1 = s.n_l1; a.ng = s.n_groups; a.group_n = s.group_n;
-  a.beta = s.beta;
+  TokArgs a = tok_args(s, t);
+  a.idx = idx;
   a.part = s.n_groups > 0 ? reinterpret_cast<const float*>(ws + w.part_off) : nullptr;
-  a.out = t.out;
   if (s.group_n == 16)
     hipLaunchKernelGGL((token_kernel<D, 16>), dim3((unsigned)(s.B * s.Hkv)), dim3(kThreads),
                        token_smem(D, s), st, a);
@@ -1463,6 +1648,30 @@ hipError_t launch_attn(const StepShape& s, const StepTensors& t, const Workspace
                        const int32_t* idx, hipStream_t st) {
   if (!step_limits_ok(s)) return hipErrorInvalidValue;
   return s.d == 128 ? token_d<128>(s, t, w, ws, idx, st) : token_d<64>(s, t, w, ws, idx, st);
+}
+
+template <int D, int N>
+hipError_t step_dn(const StepShape& s, const StepTensors& t, int32_t* idx_out, hipStream_t st) {
+  SumArgs ra = sum_args(s, t);
+  ra.want_topk = 1;
+  ra.want_partial = 1;
+  ra.idx = idx_out;
+  TokArgs ta = tok_args(s, t);
+  hipLaunchKernelGGL((step_kernel<D, N>), dim3((unsigned)(s.B * s.Hkv)), dim3(kThreads),
+                     step_smem(s), st, ra, ta);
+  return hipGetLastError();
+}
+
+int step_fused_ok(const StepShape& s) {
+  return s.n_groups > 0 && step_limits_ok(s) && step_smem(s) <= kMaxFusedLds;
+}
+
+hipError_t launch_step(const StepShape& s, const StepTensors& t, int32_t* idx_out,
+                       hipStream_t st) {
+  if (!step_fused_ok(s)) return hipErrorInvalidValue;
+  if (s.d == 128)
+    return s.group_n == 16 ? step_dn<128, 16>(s, t, idx_out, st) : step_dn<128, 8>(s, t, idx_out, st);
+  return s.group_n == 16 ? step_dn<64, 16>(s, t, idx_out, st) : step_dn<64, 8>(s, t, idx_out, st);
 }
 
 }  // namespace hsq

@@ -317,11 +317,12 @@ def test_batch_halves_match_full_batch():
 
 def test_headline_full_size():
     # the 40/8-head, d=128, T=16384, batch-64, N=8, beta=128 layer at full size,
-    # launched as the timed loop launches it (route + attend with a workspace,
-    # replayed from a captured graph).  Every unit: the selection is ascending,
-    # distinct, in range and exactly the top-beta of the kernel's own router
-    # scores; replays reproduce the eager call bit for bit.  Sampled units:
-    # scores, selection and attention against the oracle.
+    # launched as the timed loop launches it (the one-launch step, replayed
+    # from a captured graph); the two-launch form gives the same bits.  Every
+    # unit: the selection is ascending, distinct, in range and exactly the
+    # top-beta of the kernel's own router scores; replays reproduce the eager
+    # call bit for bit.  Sampled units: scores, selection and attention
+    # against the oracle.
     w = W.QWEN3_14B_16K
     print("headline full size: build", flush=True)
     sc = Scenario(w)
@@ -331,9 +332,8 @@ def test_headline_full_size():
     out = torch.empty((w.batch, w.hq, w.d), dtype=torch.float32, device=DEV)
     idx = torch.empty((w.batch, w.hkv, beta), dtype=torch.int32, device=DEV)
 
-    def step():
-        hsq.step_route(sc.q, t, w.beta, sc.dks, sc.cb3, ws, idx=idx)
-        hsq.step_attend(sc.q, t, w.beta, sc.dks, sc.dvs, sc.cb4, ws, out)
+    def step():  # one launch per layer, as timed
+        hsq.decode_step(sc.q, t, w.beta, sc.dks, sc.dvs, sc.cb4, sc.cb3, ws=ws, out=out, idx=idx)
 
     print("headline full size: eager step", flush=True)
     step()
@@ -361,6 +361,14 @@ def test_headline_full_size():
         torch.cuda.synchronize()
         assert torch.equal(idx, idx0), f"replay {r}: selection differs"
         assert torch.equal(out, out0), f"replay {r}: output differs"
+
+    print("headline full size: two-launch form", flush=True)
+    out2 = torch.empty_like(out)
+    idx2 = torch.empty_like(idx)
+    hsq.step_route(sc.q, t, w.beta, sc.dks, sc.cb3, ws, idx=idx2)
+    hsq.step_attend(sc.q, t, w.beta, sc.dks, sc.dvs, sc.cb4, ws, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(idx2, idx0) and torch.equal(out2, out0)
 
     print("headline full size: selection vs the kernel's own scores", flush=True)
     idx2, scores = hsq.route_topk(sc.q, t, sc.dks, sc.cb3, w.beta, want_scores=True)
