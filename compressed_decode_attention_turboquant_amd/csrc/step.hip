@@ -320,6 +320,27 @@ __device__ void query_operands(const float* qf, int lane, half8 (&hi)[D / 32],
   }
 }
 
+// B operand of the router products: lane (c, gq) holds, for column c < 8,
+// the fp16 high part of head c's rotated query and, for column 8 + h, its
+// low part x - fp16(x) (dims as in query_operands; rows of absent heads are
+// zero).
+template <int D>
+__device__ void router_operands(const float* qf, int lane, half8 (&b)[D / 32]) {
+  const int c = lane & 15, gq = lane >> 4, h = c & 7;
+  const bool low = c >= 8;
+  const f32x4* src = reinterpret_cast<const f32x4*>(qf + h * kQS<D> + gq * (D / 4));
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m) {
+    const f32x4 x0 = src[2 * m], x1 = src[2 * m + 1];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float x = (j < 4) ? x0[j] : x1[j - 4];
+      const _Float16 xh = (_Float16)x;
+      b[m][j] = low ? (_Float16)(x - (float)xh) : xh;
+    }
+  }
+}
+
 // ---------------------------------------------------------- online softmax ---
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -666,15 +687,16 @@ __device__ __forceinline__ uint32_t field6(const uint32_t* w) {
 }
 
 // QK of 16 summaries: the dequantised keys are exact fp16 values, so the
-// two-term split q_hi c + q_lo c gives fp32-accurate scores.  kw: this lane's
-// 3D/4 key bits (summary lane&15, dims gq*D/4 ..) from bit 0.  The table
-// reads go straight into the operand registers; the two products accumulate
-// separately so that consecutive MFMAs do not wait on each other.
+// two-term split q_hi c + q_lo c gives fp32-accurate scores.  b: router
+// operand (column h < 8: q_hi of head h, column 8 + h: q_lo), so one MFMA
+// chain forms both products and a row rotation by 8 adds them; lanes with
+// column c < 8 return head c's logits.  kw: this lane's 3D/4 key bits
+// (summary lane&15, dims gq*D/4 ..) from bit 0.  The table reads go straight
+// into the operand registers.
 template <int D>
-__device__ __forceinline__ f32x4 qk3(const uint32_t (&kw)[3], const half8 (&qh)[D / 32],
-                                     const half8 (&ql)[D / 32], const uint32_t* lut,
-                                     uint32_t lane4) {
-  f32x4 acc_h = {0.f, 0.f, 0.f, 0.f}, acc_l = {0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ f32x4 qk3(const uint32_t (&kw)[3], const half8 (&b)[D / 32],
+                                     const uint32_t* lut, uint32_t lane4) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   uint32_t a[D / 8];
 #define HSQ_FIELD_ADDR(P) a[P] = lut3_addr(field6<6 * (P)>(kw), lane4)
   HSQ_FIELD_ADDR(0); HSQ_FIELD_ADDR(1); HSQ_FIELD_ADDR(2); HSQ_FIELD_ADDR(3);
@@ -688,10 +710,12 @@ __device__ __forceinline__ f32x4 qk3(const uint32_t (&kw)[3], const half8 (&qh)[
   for (int m = 0; m < D / 32; ++m) {
     const half8 ak = as_h8(lds_at(lut, a[4 * m]), lds_at(lut, a[4 * m + 1]),
                            lds_at(lut, a[4 * m + 2]), lds_at(lut, a[4 * m + 3]));
-    acc_h = mfma16(ak, qh[m], acc_h);
-    acc_l = mfma16(ak, ql[m], acc_l);
+    acc = mfma16(ak, b[m], acc);
   }
-  return acc_h + acc_l;
+  f32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = acc[i] + dpp_f<0x128>(acc[i]);  // row_ror:8
+  return r;
 }
 
 // Keys of tile t (16 summaries): this lane's raw key words (D = 128: 96 bits
@@ -878,15 +902,15 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   if (tid < 4) s_sel[tid] = 0;
   lds_barrier();
   build_lut3(L.lut3, s_cb, tid);
-  half8 qh[D / 32], ql[D / 32];
-  query_operands<D>(qf, lane, qh, ql);
+  half8 qb[D / 32];
+  router_operands<D>(qf, lane, qb);
   lds_barrier();
 
   // (1) keys -> per-head logits in LDS (column 2h holds head h)
   const int n_tiles = ngp >> 4;
   // lanes that hold no head's logits store into a dummy slot (no branch)
-  const bool writer = !(c & 1) && (c >> 1) < a.G;
-  float* lw = writer ? logits + (c >> 1) * ngp + 4 * gq : L.dummy + 4 * lane;
+  const bool writer = c < a.G;
+  float* lw = writer ? logits + c * ngp + 4 * gq : L.dummy + 4 * lane;
   float blo = kPosInf, cmax = kNegInf;
   // rows of tile t past the last group (only the last tile has any)
   auto tail_rows = [&](int t) -> uint32_t {
@@ -901,7 +925,7 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
           const int t = wave + i * kWaves;
           uint32_t kw[3];
           key_bits<D>(T.kw, lane, kw);
-          f32x4 lg = qk3<D>(kw, qh, ql, lut3, lane4) * T.kn;
+          f32x4 lg = qk3<D>(kw, qb, lut3, lane4) * T.kn;
           *reinterpret_cast<f32x4*>(lw + (writer ? 16 * t : 0)) = lg;
           // a lower bound of every score (max or mean over heads of these
           // logits); the heads' maxima below bound them from above
@@ -922,7 +946,7 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
     s_lo[wave] = blo;
     s_hi[wave] = whi;
   }
-  if (gq == 0 && writer) s_mh[wave][c >> 1] = cmax;
+  if (gq == 0 && writer) s_mh[wave][c] = cmax;
   // From here on every wave streams the values of ALL summaries into the
   // softmax partial; the top-beta selection runs in steps between segments
   // of that stream (its LDS work overlaps the loads in flight), and at the
