@@ -869,6 +869,11 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   // (the candidates may still be read by slower waves while it is written)
   int32_t* sel = reinterpret_cast<int32_t*>(keys);
   const uint32_t* lut3 = L.lut3;
+  // Wave priorities fall as a work-group moves through the step (router 3,
+  // values and selection 2, attend tiles 1, epilogue 0): where two
+  // work-groups share a CU, the one that is behind gets the issue slots
+  // first, instead of the older one by age, so both finish closer together.
+  __builtin_amdgcn_s_setprio(3);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int kvh = unit % a.Hkv;
@@ -962,6 +967,7 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   }
   lds_barrier();
 
+  __builtin_amdgcn_s_setprio(2);
   // every weight exp(logit + bias - m) <= 1 with m the head's maximum logit
   const int hcol = min(c >> 1, a.G - 1);
   float m0 = kNegInf;
@@ -1357,6 +1363,7 @@ __device__ __forceinline__ void attend_unit(const TokArgs& a, const AttendLds& L
   const int nft = (N == 16) ? a.beta : (a.beta + 1) / 2;
   const int total = n1t + nft;
   constexpr int LPV = D / 8;
+  __builtin_amdgcn_s_setprio(1);  // see route_unit
 
   // this wave's first tiles not issued yet, loading while the table is built
 #pragma unroll
@@ -1392,6 +1399,7 @@ __device__ __forceinline__ void attend_unit(const TokArgs& a, const AttendLds& L
         });
   }
   lds_barrier();  // the table is no longer needed: reuse as scratch
+  __builtin_amdgcn_s_setprio(0);
   float* scratch = reinterpret_cast<float*>(L.lut4);
   float* mine = scratch + kWaves * kMaxG * (D + 2);  // [G][D+2] this unit's token partial
   combine_waves<D>(st, a.G, scratch, mine, tid);
