@@ -71,7 +71,7 @@ constexpr int kNC3 = 32;                 // 3-bit table copies (lanes l, l+32 sh
 constexpr int kNC4 = 64;                 // 4-bit table copies (one per lane)
 constexpr int kMaxGroups = 16384;
 constexpr int kMaxLogits = 12288;        // G * n_groups kept in LDS
-constexpr size_t kMaxFusedLds = 150 * 1024;  // dynamic LDS of the one-launch step
+constexpr size_t kMaxFusedLds = 92 * 1024;  // dynamic LDS of the one-launch step (64 KB static)
 constexpr uint32_t kFar = 0x80000000u;   // buffer offset that reads as zero
 constexpr float kNegInf = -INFINITY;
 constexpr float kPosInf = INFINITY;
@@ -597,7 +597,7 @@ __device__ __forceinline__ int score_bucket(uint32_t key, float lo, float scale)
   return (int)fminf(fmaxf(b, 0.f), 255.f);
 }
 
-constexpr int kCandCap = 1024;  // candidates the bucket pass can rank
+constexpr int kCandCap = 512;  // candidates the bucket pass can rank
 
 // Top-beta by a score histogram (0 < beta < ng).  The scores are bucketed
 // over [lo, hi] (any bounds of the scores) in 256 equal steps; every bucket
@@ -1505,33 +1505,36 @@ void token_kernel(TokArgs a) {
   attend_unit<D, N>(a, L, tt, true, &s_bad, unit);
 }
 
-// Byte layout of the one-launch step's dynamic LDS: [0, union) holds the
-// 4-bit table in the attend phase and, in the route phase, the 3-bit table
-// (first kLut3Bytes), the route arrays, the landing slot of lanes without a
-// head and, once the logits are done, the route's combine scratch; then the
-// arrays both phases use: [qf][summary partial][record offsets].
+// LDS of the one-launch step.  A static 64 KB table region holds the 4-bit
+// table in the attend phase and, in the route phase, the 3-bit table (first
+// kLut3Bytes), then the route arrays and the landing slot of lanes without a
+// head when they fit (else those go to the front of the dynamic LDS), and,
+// once the logits are done, the route's combine scratch.  The tables sit at
+// fixed addresses, so the table reads fold them into their offsets.  The
+// dynamic LDS then holds the arrays both phases use: [qf][summary
+// partial][record offsets].
 constexpr int kLut4Bytes = 256 * kNC4 * 4;
 constexpr int kLut3Bytes = 64 * kNC3 * 4;
 struct StepLayout {
-  RouteLayout r;
-  int dummy, uni, qf, part, recoff, end;
+  RouteLayout r;   // offsets from the table (in_tab) or from the dynamic LDS
+  bool in_tab;
+  int dummy, qf, part, recoff, end;  // end: dynamic LDS bytes
 };
 template <int D, int N>
 __host__ __device__ inline StepLayout step_layout(int G, int ng, int beta) {
   StepLayout L;
   L.r = route_layout(G, ng, beta, kLut3Bytes);
+  L.in_tab = L.r.end + 64 * 16 <= kLut4Bytes;
+  if (!L.in_tab) L.r = route_layout(G, ng, beta, 0);
   L.dummy = L.r.end;
-  const int comb = kLut3Bytes + kWaves * kMaxG * (D + 2) * 4;
-  int u = L.dummy + 64 * 16;
-  u = u > kLut4Bytes ? u : kLut4Bytes;
-  u = u > comb ? u : comb;
-  L.uni = u;
-  L.qf = u;
+  L.qf = L.in_tab ? 0 : L.dummy + 64 * 16;
   L.part = L.qf + kMaxG * kQS<D> * 4;
   L.recoff = L.part + kMaxG * (D + 2) * 4;
   L.end = L.recoff + ((tok_slots<N>(beta) * 4 + 15) & ~15);
   return L;
 }
+static_assert(kLut3Bytes + kWaves * kMaxG * (128 + 2) * 4 <= kLut4Bytes,
+              "the route's combine scratch must fit in the table region");
 
 // The whole decode step in one launch (archive in device-visible memory,
 // n_groups > 0): route_unit, then attend_unit on the same work-group, with
@@ -1541,10 +1544,12 @@ template <int D, int N>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void step_kernel(SumArgs ra, TokArgs ta) {
   extern __shared__ __align__(16) char smem[];
+  __shared__ __align__(16) uint32_t s_tab[kLut4Bytes / 4];
   __shared__ float s_cb4[16];
   __shared__ uint32_t s_vsb[kMaxG * (D / 8)];
   const StepLayout S = step_layout<D, N>(ra.G, ra.ng, ra.beta);
-  uint32_t* tab = reinterpret_cast<uint32_t*>(smem);
+  uint32_t* tab = s_tab;
+  char* rbase = S.in_tab ? reinterpret_cast<char*>(s_tab) : smem;
   float* qf = reinterpret_cast<float*>(smem + S.qf);
   float* part = reinterpret_cast<float*>(smem + S.part);
   int32_t* recoff = reinterpret_cast<int32_t*>(smem + S.recoff);
@@ -1561,8 +1566,9 @@ void step_kernel(SumArgs ra, TokArgs ta) {
   if (tid < 16) s_cb4[tid] = cbv;
   if (tid < kMaxG * LPV) s_vsb[tid] = vsb;
 
-  const RouteLds R = route_lds<D>(smem, S.r, tab, qf, reinterpret_cast<float*>(smem + S.dummy),
-                                  reinterpret_cast<float*>(smem + kLut3Bytes));
+  const RouteLds R =
+      route_lds<D>(rbase, S.r, tab, qf, reinterpret_cast<float*>(rbase + S.dummy),
+                   reinterpret_cast<float*>(reinterpret_cast<char*>(s_tab) + kLut3Bytes));
   // ends with a barrier: partial, selection and record offsets are visible
   // and the union is free
   route_unit<D>(ra, R, part, recoff, (uint32_t)(N * (D + 8)), unit);
