@@ -79,7 +79,11 @@ const char* hsq_last_error(void);
  * proportional to (1 - y^2)^((d-3)/2) on [-1, 1].  Computed on the host in
  * double precision by Lloyd iteration to its fixed point (centroid =
  * conditional mean of its cell, threshold = midpoint of neighbouring
- * centroids), made exactly odd-symmetric, rounded to fp32.
+ * centroids), made exactly odd-symmetric.  Stored tables: each centroid
+ * rounded to the nearest fp16 value (via fp32, ties to even), returned as
+ * fp32; each threshold the exact midpoint of its two stored neighbours (an
+ * fp32 value), so quantising with the thresholds is nearest-centroid
+ * against the stored centroids.
  *   d           3..4096 (any integer; the codec itself needs d in {64,128})
  *   bits        1..4
  *   centroids   host out, [2^bits] ascending
@@ -216,10 +220,14 @@ int hsq_decode_attn(const float* q, int B, int Hq, int Hkv, int d, const uint8_t
 
 /*
  * hsq_decode_step -- the whole decode step of one layer: route, top-beta and
- * attention [HSQ "Decode process" steps 1-3], as hsq_route_topk followed by
- * hsq_decode_attn with l3_staged == 0, in two launches.
+ * attention [HSQ "Decode process" steps 1-3], the result of hsq_route_topk
+ * followed by hsq_decode_attn with l3_staged == 0 (bit for bit).  Runs as
+ * one launch, one work-group per (b, kvh) with the selection and the
+ * summary partial kept on chip; when n_groups == 0 or the shape needs more
+ * on-chip memory than that launch has, as two launches through the
+ * workspace.
  *   topk_idx    optional out int32 [B][Hkv][min(beta, n_groups)] (NULL = not
- *               returned; the selection then lives in the workspace)
+ *               returned)
  *   other arguments as in hsq_route_topk / hsq_decode_attn
  */
 int hsq_decode_step(const float* q, int B, int Hq, int Hkv, int d, const uint8_t* l1k,
