@@ -220,8 +220,9 @@ int hsq_decode_attn(const float* q, int B, int Hq, int Hkv, int d, const uint8_t
 
 /*
  * hsq_decode_step -- the whole decode step of one layer: route, top-beta and
- * attention [HSQ "Decode process" steps 1-3], the result of hsq_route_topk
- * followed by hsq_decode_attn with l3_staged == 0 (bit for bit).  Runs as
+ * attention [HSQ "Decode process" steps 1-3]: hsq_route_topk followed by
+ * hsq_decode_attn with l3_staged == 0, with the same bits as hsq_step_route
+ * followed by hsq_step_attend.  Runs as
  * one launch, one work-group per (b, kvh) with the selection and the
  * summary partial kept on chip; when n_groups == 0 or the shape needs more
  * on-chip memory than that launch has, as two launches through the
