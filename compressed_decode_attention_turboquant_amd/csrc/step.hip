@@ -1138,25 +1138,35 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   constexpr int RB = 3 * D / 8;
   const uint32_t vb = val_byte<D>(lane);
   const int ntl = stream ? (nsel + 15) / 16 : 0;
+  // rows past the list read nothing: their offsets are moved past the end
+  // by an OR (kept opaque, so that each row stays one load at one address)
   auto corr_load = [&](int j, ValTile& V, float (&lg)[4]) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int k = 16 * j + 4 * gq + r;
-      const int g = (k < nsel) ? sel[k] : -1;
-      V.va[r] = ld32(rv, g >= 0 ? (uint32_t)g * RB + vb : kFar);
-      V.vn[r] = __uint_as_float(ld32(rvn, g >= 0 ? (uint32_t)g * 4 : kFar));
-      lg[r] = (g >= 0) ? logits[hcol * ngp + g] : kNegInf;
+      const bool in = k < nsel;
+      const uint32_t g = (uint32_t)sel[max(min(k, nsel - 1), 0)];
+      const uint32_t far = in ? 0u : kFar;
+      uint32_t vo = (g * RB + vb) | far, no = (g * 4u) | far;
+      asm("" : "+v"(vo), "+v"(no));
+      V.va[r] = ld32(rv, vo);
+      V.vn[r] = __uint_as_float(ld32(rvn, no));
+      const float x = logits[hcol * ngp + (int)g];
+      lg[r] = in ? x : kNegInf;
     }
   };
   ValTile ct;
   float clg[4];
-  if (wave < ntl) corr_load(wave, ct, clg);
+  corr_load(wave, ct, clg);
 
   // values, the rest
   pipeline_seg<kValDepth>(min(3, segs), segs, iters, vt, vload, vuse);
 
-  for (int j = wave; j < ntl; j += kWaves) {
-    if (j != wave) corr_load(j, ct, clg);
+  // the first list tile outside the loop: its loads were issued before the
+  // last segment
+  if (wave < ntl) consume(clg, ct, -1.f);
+  for (int j = wave + kWaves; j < ntl; j += kWaves) {
+    corr_load(j, ct, clg);
     consume(clg, ct, -1.f);
   }
   lds_barrier();  // the logits are no longer needed: reuse as scratch
