@@ -75,19 +75,13 @@ constexpr size_t kMaxFusedLds = 92 * 1024;  // dynamic LDS of the one-launch ste
 constexpr uint32_t kFar = 0x80000000u;   // buffer offset that reads as zero
 constexpr float kNegInf = -INFINITY;
 constexpr float kPosInf = INFINITY;
-// tiles per wave in the load pipelines (K-1 in flight while one computes)
-#ifndef HSQ_KEY_DEPTH
-#define HSQ_KEY_DEPTH 3
-#endif
-#ifndef HSQ_VAL_DEPTH
-#define HSQ_VAL_DEPTH 3
-#endif
-#ifndef HSQ_TOK_DEPTH
-#define HSQ_TOK_DEPTH 3
-#endif
-constexpr int kKeyDepth = HSQ_KEY_DEPTH;
-constexpr int kValDepth = HSQ_VAL_DEPTH;
-constexpr int kTokDepth = HSQ_TOK_DEPTH;
+// tiles per wave in the load pipelines (K-1 in flight while one computes);
+// measured best on the 16K-context headline layer (deeper value pipelines
+// lengthen the segments between the selection steps; the token tiles are
+// held to 3 by the register budget)
+constexpr int kKeyDepth = 4;
+constexpr int kValDepth = 4;
+constexpr int kTokDepth = 3;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
@@ -104,21 +98,13 @@ __device__ __forceinline__ u32x3 ld96(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ u32x4 ld128(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
+// Four consecutive floats in one 16-byte load.  The buffer range check is
+// made per dword, so a load that crosses the end of the buffer returns the
+// floats in range and zeros past the end (the ragged-tail parity tests cover
+// this); the tile loads need no edge case, and every path through a
+// pipelined loop issues the same loads, which keeps the waits exact.
 __device__ __forceinline__ f32x4 ldf4(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(f32x4, ld128(r, off));
-}
-// four consecutive floats, each range-checked separately
-__device__ __forceinline__ f32x4 ldf1x4(rsrc_t r, uint32_t off) {
-  f32x4 v;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(ld32(r, off + 4 * i));
-  return v;
-}
-// Four consecutive floats in one 16-byte load, or, where the 16 bytes may
-// cross the end of the buffer (`edge`, wave-uniform), in four range-checked
-// loads so that every float in range is read.
-__device__ __forceinline__ f32x4 ldf4_edge(rsrc_t r, uint32_t off, bool edge) {
-  return edge ? ldf1x4(r, off) : ldf4(r, off);
 }
 
 __device__ __forceinline__ uint32_t h2u(_Float16 lo, _Float16 hi) {
@@ -725,9 +711,8 @@ struct KeyTile {
   uint32_t kw[3];
   f32x4 kn;
 };
-// edge_tile: the one tile whose rows run past the last group (or -1)
 template <int D>
-__device__ __forceinline__ void load_keys(rsrc_t rk, rsrc_t rn, int t, int edge_tile, int lane,
+__device__ __forceinline__ void load_keys(rsrc_t rk, rsrc_t rn, int t, int lane,
                                           KeyTile& T) {
   constexpr int CB3 = 3 * D / 8;
   const int n = lane & 15, gq = lane >> 4;
@@ -739,7 +724,7 @@ __device__ __forceinline__ void load_keys(rsrc_t rk, rsrc_t rn, int t, int edge_
     const u32x2 w = ld64(rk, row + 4 * ((3 * gq) >> 1));
     T.kw[0] = w.x; T.kw[1] = w.y; T.kw[2] = 0u;
   }
-  T.kn = ldf4_edge(rn, (uint32_t)(16 * t + 4 * gq) * 4, t == edge_tile);
+  T.kn = ldf4(rn, (uint32_t)(16 * t + 4 * gq) * 4);
 }
 // This lane's key bits from the words load_keys left (the loads stay free of
 // arithmetic so that no wait is forced before the tile is used).
@@ -777,7 +762,7 @@ __device__ __forceinline__ uint32_t val_shift(int lane) {
   return (uint32_t)(BITS * (lane & 15)) - 8u * val_byte<D>(lane);
 }
 template <int D>
-__device__ __forceinline__ void load_vals(rsrc_t rv, rsrc_t rvn, int t, int edge_tile, int lane,
+__device__ __forceinline__ void load_vals(rsrc_t rv, rsrc_t rvn, int t, int lane,
                                           ValTile& T) {
   constexpr int RB = 3 * D / 8;
   const int gq = lane >> 4;
@@ -787,7 +772,7 @@ __device__ __forceinline__ void load_vals(rsrc_t rv, rsrc_t rvn, int t, int edge
   asm("" : "+v"(base));
 #pragma unroll
   for (int j = 0; j < 4; ++j) T.va[j] = ld32(rv, base + j * RB);
-  T.vn = ldf4_edge(rvn, (uint32_t)(16 * t + 4 * gq) * 4, t == edge_tile);
+  T.vn = ldf4(rvn, (uint32_t)(16 * t + 4 * gq) * 4);
 }
 
 // Byte offsets of the route body's LDS arrays after `base` (16-byte aligned):
@@ -891,10 +876,9 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   QueryIn qin;
   load_query<D>(a.q + (size_t)unit * a.G * D, a.k_signs + kvh * (D / 32), a.G, tid, qin);
   KeyTile kt[kKeyDepth];
-  const int edge_tile = (a.ng & 15) ? (a.ng >> 4) : -1;
 #pragma unroll
   for (int j = 0; j < kKeyDepth - 1; ++j)
-    load_keys<D>(rk, rkn, wave + j * kWaves, edge_tile, lane, kt[j]);
+    load_keys<D>(rk, rkn, wave + j * kWaves, lane, kt[j]);
 
   if (tid < 8) s_cb[tid] = cbv;
   rotate_query<D>(qin, a.scale * rsqrtf((float)D), qf, tid);
@@ -925,7 +909,7 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   {
     pipeline<kKeyDepth>(
         wave_iters(n_tiles, wave), kt,
-        [&](int i, KeyTile& T) { load_keys<D>(rk, rkn, wave + i * kWaves, edge_tile, lane, T); },
+        [&](int i, KeyTile& T) { load_keys<D>(rk, rkn, wave + i * kWaves, lane, T); },
         [&](int i, const KeyTile& T) {
           const int t = wave + i * kWaves;
           uint32_t kw[3];
@@ -963,7 +947,7 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   if (stream) {
 #pragma unroll
     for (int j = 0; j < kValDepth - 1; ++j)
-      load_vals<D>(rv, rvn, wave + j * kWaves, edge_tile, lane, vt[j]);
+      load_vals<D>(rv, rvn, wave + j * kWaves, lane, vt[j]);
   }
   lds_barrier();
 
@@ -990,7 +974,7 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   };
   const float* lrow = logits + hcol * ngp + 4 * gq;
   auto vload = [&](int i, ValTile& V) {
-    load_vals<D>(rv, rvn, wave + i * kWaves, edge_tile, lane, V);
+    load_vals<D>(rv, rvn, wave + i * kWaves, lane, V);
   };
   auto vuse = [&](int i, const ValTile& V) {
     const int t = wave + i * kWaves;
@@ -1263,9 +1247,8 @@ __device__ __forceinline__ void load_tok_at(const TokBufs& B, int t, int n1t, in
     const u32x2 w = ld64(rk, ko);
     T.kw = u32x4{w.x, w.y, 0u, 0u};
   }
-  const bool edge = l1 && t == n1t - 1 && (n1 & 15);  // the ragged last L1 tile
-  T.kn = ldf4_edge(rkn, kno, edge);
-  T.vn = ldf4_edge(rvn, vno, edge);
+  T.kn = ldf4(rkn, kno);
+  T.vn = ldf4(rvn, vno);
 #pragma unroll
   for (int j = 0; j < 4; ++j) T.va[j] = ld32(rv, vo + j * CB);
 }
