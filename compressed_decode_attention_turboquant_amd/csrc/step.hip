@@ -831,11 +831,15 @@ __device__ __forceinline__ RouteLds route_lds(char* base, const RouteLayout& r, 
 }
 
 // Router, top-beta and summary partial of one unit (the whole work-group).
-// part_out: [G][D+2] (m, l, O) of the summary partial (global or LDS);
+// The summary partial goes either, combined over the waves, to part_out
+// ([G][D+2] (m, l, O), global memory), or, when st_out is not null, stays
+// per wave in *st_out (reference maximum including the summary bias) for
+// the attend phase of the same work-group to continue.
 // recoff: if not null, LDS table that receives g * rec for selection slot s.
 template <int D>
 __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, float* part_out,
-                                           int32_t* recoff, uint32_t rec, int unit) {
+                                           Softmax<D>* st_out, int32_t* recoff, uint32_t rec,
+                                           int unit) {
   constexpr int CB3 = 3 * D / 8;
   __shared__ float s_cb[8];
   __shared__ int s_tmp[kWaves];
@@ -1155,6 +1159,12 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   }
   lds_barrier();  // the logits are no longer needed: reuse as scratch
   st.m += a.bias;
+  if (st_out) {
+    st.mL = st.m * kLog2e;
+    st.mth = st.m + kLazy;
+    *st_out = st;
+    return;
+  }
   combine_waves<D>(st, a.G, L.scratch, part_out, tid);
 }
 
@@ -1169,7 +1179,7 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   const RouteLayout r = route_layout(a.G, a.ng, a.beta, kMaxG * kQS<D> * 4);
   const RouteLds L = route_lds<D>(smem, r, s_lut3, qf, qf, qf);
   const int unit = blockIdx.x;
-  route_unit<D>(a, L, a.part + (size_t)unit * a.G * (D + 2), nullptr, 0u, unit);
+  route_unit<D>(a, L, a.part + (size_t)unit * a.G * (D + 2), nullptr, nullptr, 0u, unit);
 }
 
 // ----------------------------------------------------------- token kernel ---
@@ -1343,11 +1353,15 @@ struct AttendLds {
 // is filled and visible to all waves, and the table is free; tt[j] holds the
 // loads of this wave's tile wave + 8j already when l1_issued and that tile is
 // an L1 tile.  bad_flag (read after the first barrier here), if not null:
-// nonzero when some slot of recoff names no record.
+// nonzero when some slot of recoff names no record.  st_in, if not null:
+// this wave's softmax state of the summary partial, which the token tiles
+// continue (L.part is then not used); else the waves' states start empty
+// and the combined result is merged with L.part.
 template <int D, int N>
 __device__ __forceinline__ void attend_unit(const TokArgs& a, const AttendLds& L,
                                             TokTile (&tt)[kTokDepth], bool l1_issued,
-                                            const int* bad_flag, int unit) {
+                                            const int* bad_flag, const Softmax<D>* st_in,
+                                            int unit) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const uint32_t lane4 = (uint32_t)lane << 2;
   const uint32_t* lut4 = L.lut4;
@@ -1369,7 +1383,10 @@ __device__ __forceinline__ void attend_unit(const TokArgs& a, const AttendLds& L
   lds_barrier();
 
   Softmax<D> st;
-  st.init(kNegInf);
+  if (st_in)
+    st = *st_in;
+  else
+    st.init(kNegInf);
   {
     // tiles with rows that hold no token: the ragged last L1 tile, the last
     // archive tile when its second slot is empty, every archive tile when
@@ -1405,8 +1422,13 @@ __device__ __forceinline__ void attend_unit(const TokArgs& a, const AttendLds& L
     if (k >= a.G * D) break;
     const float* mp = mine + h * (D + 2);
     const float m1 = mp[0], l1 = mp[1], v1 = mp[2 + e];
-    const float* pp = L.part + h * (D + 2);
-    const float m2 = pp[0], l2 = pp[1], v2 = pp[2 + e];
+    float m2 = kNegInf, l2 = 0.f, v2 = 0.f;
+    if (L.part) {
+      const float* pp = L.part + h * (D + 2);
+      m2 = pp[0];
+      l2 = pp[1];
+      v2 = pp[2 + e];
+    }
     const float M = fmaxf(m1, m2);
     const float w1 = (m1 == kNegInf) ? 0.f : __expf(m1 - M);
     const float w2 = (m2 == kNegInf) ? 0.f : __expf(m2 - M);
@@ -1495,23 +1517,22 @@ void token_kernel(TokArgs a) {
   rotate_query<D>(qin, a.scale * rsqrtf((float)D), L.qf, tid);
   lds_barrier();
   if (bad) s_bad = 1;  // read after the next barrier
-  attend_unit<D, N>(a, L, tt, true, &s_bad, unit);
+  attend_unit<D, N>(a, L, tt, true, &s_bad, nullptr, unit);
 }
 
 // LDS of the one-launch step.  A static 64 KB table region holds the 4-bit
-// table in the attend phase and, in the route phase, the 3-bit table (first
-// kLut3Bytes), then the route arrays and the landing slot of lanes without a
-// head when they fit (else those go to the front of the dynamic LDS), and,
-// once the logits are done, the route's combine scratch.  The tables sit at
-// fixed addresses, so the table reads fold them into their offsets.  The
-// dynamic LDS then holds the arrays both phases use: [qf][summary
-// partial][record offsets].
+// table in the attend phase (and its combine scratch after the tiles) and,
+// in the route phase, the 3-bit table (first kLut3Bytes), then the route
+// arrays and the landing slot of lanes without a head when they fit (else
+// those go to the front of the dynamic LDS).  The tables sit at fixed
+// addresses, so the table reads fold them into their offsets.  The dynamic
+// LDS then holds the arrays both phases use: [qf][record offsets].
 constexpr int kLut4Bytes = 256 * kNC4 * 4;
 constexpr int kLut3Bytes = 64 * kNC3 * 4;
 struct StepLayout {
   RouteLayout r;   // offsets from the table (in_tab) or from the dynamic LDS
   bool in_tab;
-  int dummy, qf, part, recoff, end;  // end: dynamic LDS bytes
+  int dummy, qf, recoff, end;  // end: dynamic LDS bytes
 };
 template <int D, int N>
 __host__ __device__ inline StepLayout step_layout(int G, int ng, int beta) {
@@ -1521,18 +1542,18 @@ __host__ __device__ inline StepLayout step_layout(int G, int ng, int beta) {
   if (!L.in_tab) L.r = route_layout(G, ng, beta, 0);
   L.dummy = L.r.end;
   L.qf = L.in_tab ? 0 : L.dummy + 64 * 16;
-  L.part = L.qf + kMaxG * kQS<D> * 4;
-  L.recoff = L.part + kMaxG * (D + 2) * 4;
+  L.recoff = L.qf + kMaxG * kQS<D> * 4;
   L.end = L.recoff + ((tok_slots<N>(beta) * 4 + 15) & ~15);
   return L;
 }
-static_assert(kLut3Bytes + kWaves * kMaxG * (128 + 2) * 4 <= kLut4Bytes,
-              "the route's combine scratch must fit in the table region");
+static_assert((kWaves + 2) * kMaxG * (128 + 2) * 4 <= kLut4Bytes,
+              "the attend phase's combine scratch must fit in the table region");
 
 // The whole decode step in one launch (archive in device-visible memory,
-// n_groups > 0): route_unit, then attend_unit on the same work-group, with
-// the selection, the record offsets and the summary partial handed over in
-// LDS.
+// n_groups > 0): route_unit, then attend_unit on the same work-group.  The
+// selection reaches the attend phase as record offsets in LDS, and each
+// wave's softmax state of the summary partial carries on into the token
+// tiles, so the partial is combined over the waves only once, at the end.
 template <int D, int N>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void step_kernel(SumArgs ra, TokArgs ta) {
@@ -1544,7 +1565,6 @@ void step_kernel(SumArgs ra, TokArgs ta) {
   uint32_t* tab = s_tab;
   char* rbase = S.in_tab ? reinterpret_cast<char*>(s_tab) : smem;
   float* qf = reinterpret_cast<float*>(smem + S.qf);
-  float* part = reinterpret_cast<float*>(smem + S.part);
   int32_t* recoff = reinterpret_cast<int32_t*>(smem + S.recoff);
   const int tid = threadIdx.x;
   const int unit = blockIdx.x;
@@ -1559,22 +1579,22 @@ void step_kernel(SumArgs ra, TokArgs ta) {
   if (tid < 16) s_cb4[tid] = cbv;
   if (tid < kMaxG * LPV) s_vsb[tid] = vsb;
 
-  const RouteLds R =
-      route_lds<D>(rbase, S.r, tab, qf, reinterpret_cast<float*>(rbase + S.dummy),
-                   reinterpret_cast<float*>(reinterpret_cast<char*>(s_tab) + kLut3Bytes));
-  // ends with a barrier: partial, selection and record offsets are visible
-  // and the union is free
-  route_unit<D>(ra, R, part, recoff, (uint32_t)(N * (D + 8)), unit);
+  const RouteLds R = route_lds<D>(rbase, S.r, tab, qf,
+                                  reinterpret_cast<float*>(rbase + S.dummy), nullptr);
+  // ends with a barrier: the selection and record offsets are visible and
+  // the union is free; each wave's summary partial stays in st
+  Softmax<D> st;
+  route_unit<D>(ra, R, nullptr, &st, recoff, (uint32_t)(N * (D + 8)), unit);
 
   AttendLds L;
   L.lut4 = tab;
   L.qf = qf;
-  L.part = part;
+  L.part = nullptr;
   L.recoff = recoff;
   L.cb = s_cb4;
   L.vsb = s_vsb;
   TokTile tt[kTokDepth];
-  attend_unit<D, N>(ta, L, tt, false, nullptr, unit);
+  attend_unit<D, N>(ta, L, tt, false, nullptr, &st, unit);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }

@@ -221,8 +221,8 @@ int hsq_decode_attn(const float* q, int B, int Hq, int Hkv, int d, const uint8_t
 /*
  * hsq_decode_step -- the whole decode step of one layer: route, top-beta and
  * attention [HSQ "Decode process" steps 1-3]: hsq_route_topk followed by
- * hsq_decode_attn with l3_staged == 0, with the same bits as hsq_step_route
- * followed by hsq_step_attend.  Runs as
+ * hsq_decode_attn with l3_staged == 0 (the same selection; the output to
+ * fp32 rounding of the order in which the partials merge).  Runs as
  * one launch, one work-group per (b, kvh) with the selection and the
  * summary partial kept on chip; when n_groups == 0 or the shape needs more
  * on-chip memory than that launch has, as two launches through the

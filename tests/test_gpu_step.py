@@ -27,6 +27,10 @@ from tests.gpu_util import (ATTN_REL_L2, CODE_BAND, TIE_BAND, compare_codes, rel
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
+# two GPU paths whose fp16 value weights are taken against different
+# reference maxima: a dominant weight rounds differently by up to 2^-11 in
+# each, so their outputs may differ by about 2 x 2^-11 relative
+PATHS_REL_L2 = 1e-3
 
 
 class Scenario:
@@ -187,10 +191,12 @@ def test_decode_step_parity(name, w):
     torch.cuda.synchronize()
     check_route(sc, idx, None, all_units(w), w.beta)
     worst = check_attn(sc, out, idx, all_units(w))
-    # the fused step (summaries removed by subtraction) agrees with the masked path
+    # the one-launch step agrees with the two-launch path given its selection;
+    # their value weights go to fp16 against different reference maxima, so
+    # they differ by up to fp16 rounding of a dominant weight (2 x 2^-11)
     ref = hsq.decode_attn(sc.q, sc.tiers, idx, sc.dks, sc.dvs, sc.cb4, sc.cb3)
     torch.cuda.synchronize()
-    assert rel_l2(out.cpu().numpy(), ref.cpu().numpy()) < 1e-4
+    assert rel_l2(out.cpu().numpy(), ref.cpu().numpy()) < PATHS_REL_L2
     print(f"  worst rel L2 {worst:.3e}", flush=True)
 
 
@@ -308,17 +314,27 @@ def test_batch_halves_match_full_batch():
         ws = hsq.make_workspace(b1 - b0, w.hq, w.hkv, w.d, t.n1, t.ng, w.beta, w.group_n, DEV)
         o = torch.empty((b1 - b0, w.hq, w.d), dtype=torch.float32, device=DEV)
         with torch.cuda.stream(s):
-            hsq.step_route(sc.q[b0:b1], ts, w.beta, sc.dks, sc.cb3, ws)
-            hsq.step_attend(sc.q[b0:b1], ts, w.beta, sc.dks, sc.dvs, sc.cb4, ws, o)
+            hsq.decode_step(sc.q[b0:b1], ts, w.beta, sc.dks, sc.dvs, sc.cb4, sc.cb3, ws=ws, out=o)
         outs.append((o, ws))
     torch.cuda.synchronize()
     assert torch.equal(torch.cat([o for o, _ in outs]), out)
+    # the two-launch form (summary partial combined through the workspace)
+    # selects the same groups and agrees to fp16 rounding of the weights
+    ws = hsq.make_workspace(w.batch, w.hq, w.hkv, w.d, t.n1, t.ng, w.beta, w.group_n, DEV)
+    o2 = torch.empty_like(out)
+    i2 = torch.empty_like(idx)
+    hsq.step_route(sc.q, t, w.beta, sc.dks, sc.cb3, ws, idx=i2)
+    hsq.step_attend(sc.q, t, w.beta, sc.dks, sc.dvs, sc.cb4, ws, o2)
+    torch.cuda.synchronize()
+    assert torch.equal(i2, idx)
+    assert rel_l2(o2.double().cpu().numpy(), out.double().cpu().numpy()) < PATHS_REL_L2
 
 
 def test_headline_full_size():
     # the 40/8-head, d=128, T=16384, batch-64, N=8, beta=128 layer at full size,
     # launched as the timed loop launches it (the one-launch step, replayed
-    # from a captured graph); the two-launch form gives the same bits.  Every
+    # from a captured graph); the two-launch form selects the same groups and
+    # agrees to fp16 rounding of the weights.  Every
     # unit: the selection is ascending, distinct, in range and exactly the
     # top-beta of the kernel's own router scores; replays reproduce the eager
     # call bit for bit.  Sampled units: scores, selection and attention
@@ -368,7 +384,9 @@ def test_headline_full_size():
     hsq.step_route(sc.q, t, w.beta, sc.dks, sc.cb3, ws, idx=idx2)
     hsq.step_attend(sc.q, t, w.beta, sc.dks, sc.dvs, sc.cb4, ws, out2)
     torch.cuda.synchronize()
-    assert torch.equal(idx2, idx0) and torch.equal(out2, out0)
+    assert torch.equal(idx2, idx0)
+    for b in range(w.batch):  # per sequence, to fp16 rounding of the weights
+        assert rel_l2(out2[b].double().cpu().numpy(), out0[b].double().cpu().numpy()) < PATHS_REL_L2
 
     print("headline full size: selection vs the kernel's own scores", flush=True)
     idx2, scores = hsq.route_topk(sc.q, t, sc.dks, sc.cb3, w.beta, want_scores=True)
