@@ -940,19 +940,28 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
     s_hi[wave] = whi;
   }
   if (gq == 0 && writer) s_mh[wave][c] = cmax;
-  // From here on every wave streams the values of ALL summaries into the
-  // softmax partial; the top-beta selection runs in steps between segments
-  // of that stream (its LDS work overlaps the loads in flight), and at the
-  // end every wave subtracts the contribution of its share of the fetched
-  // summaries, computed with the same arithmetic.
+  // Phase 2.  Every wave streams the values of ALL summaries into its
+  // softmax partial; the fetched ones are subtracted at the end with the
+  // same weights.  The top-beta runs alongside: once every wave has its
+  // first K value tiles, the work-group forms the router scores and their
+  // histogram (2a); then the last wave alone finds the threshold, ranks the
+  // groups of the threshold bucket, emits the selection and subtracts the
+  // fetched summaries (2b), while the other waves stream the remaining value
+  // tiles.  No barrier separates the selection steps.
+  constexpr int K = kValDepth;
+  constexpr int kSel = kWaves - 1;  // the selecting wave
   const bool stream = a.want_partial && a.beta < a.ng;  // else the partial is empty
-  const int iters = stream ? wave_iters(n_tiles, wave) : 0;
-  ValTile vt[kValDepth];
-  if (stream) {
+  // part 1: tiles wave + 8i (i < K) on every wave; part 2: the tiles from 8K
+  // on, round-robin over the other waves.  Indices past a part read nothing.
+  const int n1v = stream ? min(K, wave_iters(n_tiles, wave)) : 0;
+  const int n2v = (stream && wave != kSel && kWaves * K + wave < n_tiles)
+                      ? (n_tiles - kWaves * K - wave + kSel - 1) / kSel
+                      : 0;
+  auto tile1 = [&](int i) { return i < n1v ? wave + i * kWaves : n_tiles; };
+  auto tile2 = [&](int i) { return i < n2v ? kWaves * K + wave + i * kSel : n_tiles; };
+  ValTile vt[K];
 #pragma unroll
-    for (int j = 0; j < kValDepth - 1; ++j)
-      load_vals<D>(rv, rvn, wave + j * kWaves, lane, vt[j]);
-  }
+  for (int j = 0; j < K - 1; ++j) load_vals<D>(rv, rvn, tile1(j), lane, vt[j]);
   lds_barrier();
 
   __builtin_amdgcn_s_setprio(2);
@@ -977,11 +986,7 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
     pv3<D>(V.va, vsh, weight_operand(w, lane), lane4, lut3, st.O);
   };
   const float* lrow = logits + hcol * ngp + 4 * gq;
-  auto vload = [&](int i, ValTile& V) {
-    load_vals<D>(rv, rvn, wave + i * kWaves, lane, V);
-  };
-  auto vuse = [&](int i, const ValTile& V) {
-    const int t = wave + i * kWaves;
+  auto use_tile = [&](int t, const ValTile& V) {
     const f32x4 lg4 = *reinterpret_cast<const f32x4*>(lrow + 16 * t);
     float lg[4] = {lg4[0], lg4[1], lg4[2], lg4[3]};
     if (t == n_tiles - 1) {  // wave-uniform
@@ -991,10 +996,14 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
     }
     consume(lg, V, 1.f);
   };
-  const int segs = (iters + kValDepth - 1) / kValDepth;
 
-  // values, first segment
-  pipeline_seg<kValDepth>(0, min(1, segs), iters, vt, vload, vuse);
+  // values, part 1
+  pipeline<K>(
+      n1v, vt, [&](int i, ValTile& V) { load_vals<D>(rv, rvn, tile1(i), lane, V); },
+      [&](int i, const ValTile& V) { use_tile(tile1(i), V); });
+  // part 2's first tiles load during the score step
+#pragma unroll
+  for (int j = 0; j < K - 1; ++j) load_vals<D>(rv, rvn, tile2(j), lane, vt[j]);
 
   // (2a) router scores of this thread's groups 4t .. 4t+3 (+2048 per pass),
   // score histogram
@@ -1041,122 +1050,142 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   }
   lds_barrier();
 
-  // values, second segment
-  pipeline_seg<kValDepth>(min(1, segs), min(2, segs), iters, vt, vload, vuse);
-
-  // (2b) buckets above the threshold -> fetched bitmap; the threshold bucket
-  // -> candidate list (compacted per wave)
+  // (2b) the threshold bucket and how many of its groups to take (every
+  // wave reads them off the histogram).  More than 64 groups in that bucket
+  // (heavy ties): radix select over all keys, block-wide, into the bitmap.
   int bt = 0, need = 0;
   bool fallback = false;
   if (hsel) {
     hist_threshold(hist, a.beta, lane, bt, need);
-    fallback = hist[bt] > kCandCap;  // the same on every thread
-    if (!fallback) {
-      // lane 0 holds a wave's lowest groups, so it is active whenever any lane is
-      for (int g0 = 4 * tid; g0 < 32 * words; g0 += 4 * kThreads) {
-        const u32x4 k4 = *reinterpret_cast<const u32x4*>(keys + g0);
-        uint32_t above = 0u;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int b = score_bucket(k4[e], lo, bscale);
-          const bool in = g0 + e < a.ng;
-          if (in && b > bt) above |= 1u << e;
-          const bool isc = in && b == bt;
-          const uint64_t m = __builtin_amdgcn_ballot_w64(isc);
-          int base = 0;
-          if (lane == 0 && m) base = atomicAdd(&s_sel[2], __popcll(m));
-          base = __builtin_amdgcn_readfirstlane(__shfl(base, 0, 64));
-          if (isc) {
-            const int pos = base + (int)__builtin_amdgcn_mbcnt_hi(
-                                       (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-            cand[pos] = make_uint2((uint32_t)(g0 + e), k4[e]);
-          }
-        }
-        if (above) atomicOr(&fmask[g0 >> 5], above << (g0 & 31));
-      }
-    } else {  // more ties in one bucket than the ranking takes: radix select
+    fallback = __builtin_amdgcn_readfirstlane(hist[bt]) > 64;
+    if (fallback) {
       int32_t* tsel = reinterpret_cast<int32_t*>(cand);
       top_beta(keys, a.ng, a.beta, hist, s_tmp, tsel, tid);
       for (int i = tid; i < a.beta; i += kThreads) atomicOr(&fmask[tsel[i] >> 5], 1u << (tsel[i] & 31));
+      lds_barrier();
     }
   }
-  lds_barrier();
 
-  // values, third segment
-  pipeline_seg<kValDepth>(min(2, segs), min(3, segs), iters, vt, vload, vuse);
-
-  // (2c) every wave ranks the candidates (the same result everywhere) and adds
-  // the selected ones to its view of the bitmap; then every wave emits its
-  // share of the selection in ascending order (the offsets come from the
-  // per-word counts, which every wave computes)
-  const int nc = (hsel && !fallback) ? s_sel[2] : 0;
-  for (int i = lane; i < nc; i += 64) {
-    const uint2 me = cand[i];
-    if (cand_selected(cand, nc, need, me)) atomicOr(&cmask[me.x >> 5], 1u << (me.x & 31));
-  }
-  int nsel = 0;
-  {
-    int before = 0;
-    for (int w0 = 0; w0 < words; w0 += 64) {
-      const int w = w0 + lane;
-      const uint32_t bits = (w < words) ? (fmask[w] | cmask[w]) : 0u;
-      int total;
-      const int pos0 = before + wave_excl_scan(__popc(bits), lane, total);
-      if (w < words && (w & (kWaves - 1)) == wave) {  // this wave's words
-        uint32_t m = bits;
-        int pos = pos0;
-        while (m) {
-          const int g = 32 * w + __ffs(m) - 1;
-          sel[pos] = g;
-          if (a.want_topk && a.idx) a.idx[(size_t)unit * a.beta + pos] = g;
-          if (recoff) recoff[pos] = (int32_t)((uint32_t)g * rec);
-          ++pos;
-          m &= m - 1u;
+  if (wave != kSel) {
+    // values, part 2
+    pipeline<K>(
+        n2v, vt, [&](int i, ValTile& V) { load_vals<D>(rv, rvn, tile2(i), lane, V); },
+        [&](int i, const ValTile& V) { use_tile(tile2(i), V); });
+  } else {
+    // bitmap word w (lane w % 64): groups in buckets above bt, and the
+    // groups of bucket bt
+    const bool rank_here = hsel && !fallback;
+    auto word_bits = [&](int w, uint32_t& above, uint32_t& inb) {
+      above = 0u;
+      inb = 0u;
+      if (w >= words) return;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const u32x4 k4 = *reinterpret_cast<const u32x4*>(keys + 32 * w + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int b = score_bucket(k4[e], lo, bscale);
+          const bool in = 32 * w + 4 * q + e < a.ng;
+          above |= (in && b > bt) ? 1u << (4 * q + e) : 0u;
+          inb |= (in && b == bt) ? 1u << (4 * q + e) : 0u;
         }
       }
-      before += total;
+    };
+    // the threshold bucket's groups, lane i holding the i-th (at most 64);
+    // the first 64 words' above-threshold bits are kept for the emission
+    uint2 me = make_uint2(0u, 0u);
+    uint32_t above0 = 0u;
+    int nc = 0;
+    if (rank_here) {
+      for (int w0 = 0; w0 < words; w0 += 64) {
+        uint32_t above, inb;
+        word_bits(w0 + lane, above, inb);
+        if (w0 == 0) above0 = above;
+        int total;
+        int pos = nc + wave_excl_scan(__popc(inb), lane, total);
+        while (inb) {
+          const int g = 32 * (w0 + lane) + __ffs(inb) - 1;
+          cand[pos++] = make_uint2((uint32_t)g, keys[g]);
+          inb &= inb - 1u;
+        }
+        nc += total;
+      }
+      if (lane < nc) me = cand[lane];
     }
-    nsel = before;
+    // rank by (key descending, index ascending): the first `need` are taken
+    bool chosen = false;
+    if (rank_here) {
+      int rank = 0;
+      for (int j = 0; j < nc; ++j) {
+        const uint32_t og = __builtin_amdgcn_readlane(me.x, j);
+        const uint32_t ok = __builtin_amdgcn_readlane(me.y, j);
+        rank += (ok > me.y) || (ok == me.y && og < me.x);
+      }
+      chosen = lane < nc && rank < need;
+    }
+    const uint64_t chosen_mask = __builtin_amdgcn_ballot_w64(chosen);
+    // emit the selection in ascending order
+    int nsel = 0;
+    for (int w0 = 0; w0 < words; w0 += 64) {
+      const int w = w0 + lane;
+      uint32_t bits;
+      if (rank_here) {
+        uint32_t inb;
+        if (w0 == 0)
+          bits = above0;
+        else
+          word_bits(w, bits, inb);
+        for (uint64_t m = chosen_mask; m; m &= m - 1u) {
+          const int j = __ffsll((unsigned long long)m) - 1;
+          const uint32_t g = __builtin_amdgcn_readlane(me.x, j);
+          bits |= ((int)(g >> 5) == w) ? 1u << (g & 31) : 0u;
+        }
+      } else {
+        bits = (w < words) ? fmask[w] : 0u;
+      }
+      int total;
+      int pos = nsel + wave_excl_scan(__popc(bits), lane, total);
+      while (bits) {
+        const int g = 32 * w + __ffs(bits) - 1;
+        sel[pos] = g;
+        if (a.want_topk && a.idx) a.idx[(size_t)unit * a.beta + pos] = g;
+        if (recoff) recoff[pos] = (int32_t)((uint32_t)g * rec);
+        ++pos;
+        bits &= bits - 1u;
+      }
+      nsel += total;
+    }
+
+    // subtract the fetched summaries (list tiles of 16) with the same
+    // arithmetic as they were added; rows past the list read nothing
+    constexpr int RB = 3 * D / 8;
+    const uint32_t vb = val_byte<D>(lane);
+    const int ntl = stream ? (nsel + 15) / 16 : 0;
+    struct CorrTile {
+      ValTile V;
+      float lg[4];
+    };
+    auto corr_load = [&](int j, CorrTile& C) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int k = 16 * j + 4 * gq + r;
+        const bool in = k < nsel;
+        const uint32_t g = (uint32_t)sel[max(min(k, nsel - 1), 0)];
+        const uint32_t far = in ? 0u : kFar;
+        uint32_t vo = (g * RB + vb) | far, no = (g * 4u) | far;
+        asm("" : "+v"(vo), "+v"(no));  // one load at one address per row
+        C.V.va[r] = ld32(rv, vo);
+        C.V.vn[r] = __uint_as_float(ld32(rvn, no));
+        const float x = logits[hcol * ngp + (int)g];
+        C.lg[r] = in ? x : kNegInf;
+      }
+    };
+    CorrTile ct[K];
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j) corr_load(j, ct[j]);
+    pipeline<K>(ntl, ct, corr_load, [&](int, const CorrTile& C) { consume(C.lg, C.V, -1.f); });
   }
   if (!a.want_partial) return;
-  lds_barrier();
-
-  // the fetched summaries are subtracted: list tiles j = wave, wave + 8, ...;
-  // the first one loads during the last values segment
-  constexpr int RB = 3 * D / 8;
-  const uint32_t vb = val_byte<D>(lane);
-  const int ntl = stream ? (nsel + 15) / 16 : 0;
-  // rows past the list read nothing: their offsets are moved past the end
-  // by an OR (kept opaque, so that each row stays one load at one address)
-  auto corr_load = [&](int j, ValTile& V, float (&lg)[4]) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int k = 16 * j + 4 * gq + r;
-      const bool in = k < nsel;
-      const uint32_t g = (uint32_t)sel[max(min(k, nsel - 1), 0)];
-      const uint32_t far = in ? 0u : kFar;
-      uint32_t vo = (g * RB + vb) | far, no = (g * 4u) | far;
-      asm("" : "+v"(vo), "+v"(no));
-      V.va[r] = ld32(rv, vo);
-      V.vn[r] = __uint_as_float(ld32(rvn, no));
-      const float x = logits[hcol * ngp + (int)g];
-      lg[r] = in ? x : kNegInf;
-    }
-  };
-  ValTile ct;
-  float clg[4];
-  corr_load(wave, ct, clg);
-
-  // values, the rest
-  pipeline_seg<kValDepth>(min(3, segs), segs, iters, vt, vload, vuse);
-
-  // the first list tile outside the loop: its loads were issued before the
-  // last segment
-  if (wave < ntl) consume(clg, ct, -1.f);
-  for (int j = wave + kWaves; j < ntl; j += kWaves) {
-    corr_load(j, ct, clg);
-    consume(clg, ct, -1.f);
-  }
   lds_barrier();  // the logits are no longer needed: reuse as scratch
   st.m += a.bias;
   if (st_out) {
