@@ -476,100 +476,7 @@ __device__ __forceinline__ uint32_t fkey(float f) {
 }
 
 // Exclusive prefix sum over the work-group.
-__device__ int block_exclusive_scan(int v, int* tmp, int tid) {
-  const int lane = tid & 63, wave = tid >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) tmp[wave] = x;
-  lds_barrier();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += tmp[w];
-  lds_barrier();
-  return base + x - v;
-}
 
-// Top-beta of keys[0..ng): sel[0..beta) ascending group ids.  Radix select (4
-// passes of 8 bits, most significant first) finds the key of the beta-th
-// largest score and how many of its ties to take; an in-order scan then emits
-// the selected ids, ties resolved to the lower index.  0 < beta < ng.
-__device__ void top_beta(const uint32_t* keys, int ng, int beta, int* hist, int* tmp,
-                         int32_t* sel, int tid) {
-  __shared__ uint32_t s_prefix, s_mask;
-  __shared__ int s_need;
-  if (tid == 0) {
-    s_prefix = 0u;
-    s_mask = 0u;
-    s_need = beta;
-  }
-  lds_barrier();
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int b = tid; b < 256; b += kThreads) hist[b] = 0;
-    lds_barrier();
-    const uint32_t pre = s_prefix, msk = s_mask;
-    for (int g = tid; g < ng; g += kThreads) {
-      const uint32_t k = keys[g];
-      if ((k & msk) == pre) atomicAdd(&hist[(k >> shift) & 255u], 1);
-    }
-    lds_barrier();
-    if (tid < 64) {
-      // lane l owns bins 255-4l .. 252-4l (descending order)
-      int cnt[4], sum = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        cnt[k] = hist[255 - 4 * tid - k];
-        sum += cnt[k];
-      }
-      int incl = sum;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, 64);
-        if (tid >= o) incl += y;
-      }
-      const int need = s_need;
-      const int excl = incl - sum;
-      if (excl < need && incl >= need) {
-        int acc = excl;
-        for (int k = 0; k < 4; ++k) {
-          if (acc + cnt[k] >= need) {
-            const uint32_t bin = 255u - 4u * tid - k;
-            s_prefix = pre | (bin << shift);
-            s_mask = msk | (255u << shift);
-            s_need = need - acc;
-            break;
-          }
-          acc += cnt[k];
-        }
-      }
-    }
-    lds_barrier();
-  }
-  const uint32_t kth = s_prefix;
-  const int ties_needed = s_need;  // keys equal to kth to take
-  const int per = (ng + kThreads - 1) / kThreads;
-  const int lo = min(tid * per, ng), hi = min(lo + per, ng);
-  int n_eq = 0;
-  for (int g = lo; g < hi; ++g) n_eq += keys[g] == kth;
-  const int eq_base = block_exclusive_scan(n_eq, tmp, tid);
-  int n_sel = 0, e = eq_base;
-  for (int g = lo; g < hi; ++g) {
-    const uint32_t k = keys[g];
-    if (k > kth) ++n_sel;
-    else if (k == kth) n_sel += (e++ < ties_needed);
-  }
-  int pos = block_exclusive_scan(n_sel, tmp, tid);
-  e = eq_base;
-  for (int g = lo; g < hi; ++g) {
-    const uint32_t k = keys[g];
-    bool take = k > kth;
-    if (k == kth) take = (e++ < ties_needed);
-    if (take) sel[pos++] = g;
-  }
-  lds_barrier();
-}
 
 // Inverse of fkey.
 __device__ __forceinline__ float key_float(uint32_t k) {
@@ -583,7 +490,6 @@ __device__ __forceinline__ int score_bucket(uint32_t key, float lo, float scale)
   return (int)fminf(fmaxf(b, 0.f), 255.f);
 }
 
-constexpr int kCandCap = 512;  // candidates the bucket pass can rank
 
 // Top-beta by a score histogram (0 < beta < ng).  The scores are bucketed
 // over [lo, hi] (any bounds of the scores) in 256 equal steps; every bucket
@@ -621,17 +527,6 @@ __device__ __forceinline__ void hist_threshold(const int* hist, int beta, int la
   need = __builtin_amdgcn_readlane(my_need, src);
 }
 
-// Candidate i (i < nc) of the threshold bucket is selected iff fewer than
-// `need` candidates precede it in (key desc, index asc) order.
-__device__ __forceinline__ bool cand_selected(const uint2* cand, int nc, int need, uint2 me) {
-  int rank = 0;
-#pragma unroll 8
-  for (int j = 0; j < nc; ++j) {
-    const uint2 o = cand[j];
-    rank += (o.y > me.y) || (o.y == me.y && o.x < me.x);
-  }
-  return rank < need;
-}
 
 // Exclusive prefix sum of v over the lanes of a wave, plus the wave total.
 __device__ __forceinline__ int wave_excl_scan(int v, int lane, int& total) {
@@ -643,6 +538,74 @@ __device__ __forceinline__ int wave_excl_scan(int v, int lane, int& total) {
   }
   total = __builtin_amdgcn_readlane(incl, 63);
   return incl - v;
+}
+
+// Orders the LDS accesses of one wave around this point (the wave's LDS
+// operations complete in order; this keeps the compiler from moving them).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// Top-beta of keys[0..ng) by one wave: sel[0..beta) ascending group ids.
+// Radix select (4 passes of 8 bits, most significant first, histogram in
+// LDS) finds the key of the beta-th largest score and how many of its ties
+// to take; an in-order pass then emits the selected ids, ties resolved to the
+// lower index.  0 < beta < ng.
+__device__ void top_beta_wave(const uint32_t* keys, int ng, int beta, int* hist, int32_t* sel,
+                              int lane) {
+  uint32_t pre = 0u, msk = 0u;
+  int need = beta;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int b = lane; b < 256; b += 64) hist[b] = 0;
+    wave_lds_sync();
+    for (int g = lane; g < ng; g += 64) {
+      const uint32_t k = keys[g];
+      if ((k & msk) == pre) atomicAdd(&hist[(k >> shift) & 255u], 1);
+    }
+    wave_lds_sync();
+    int cnt[4], sum = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {  // lane l owns bins 255-4l .. 252-4l
+      cnt[k] = hist[255 - 4 * lane - k];
+      sum += cnt[k];
+    }
+    int total;
+    const int excl = wave_excl_scan(sum, lane, total);
+    int my_bin = -1, my_acc = 0;
+    if (excl < need && excl + sum >= need) {
+      int acc = excl;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (my_bin < 0 && acc + cnt[k] >= need) {
+          my_bin = 255 - 4 * lane - k;
+          my_acc = acc;
+        }
+        acc += cnt[k];
+      }
+    }
+    const int src = __ffsll((unsigned long long)__builtin_amdgcn_ballot_w64(my_bin >= 0)) - 1;
+    pre |= (uint32_t)__builtin_amdgcn_readlane(my_bin, src) << shift;
+    msk |= 255u << shift;
+    need -= __builtin_amdgcn_readlane(my_acc, src);
+    wave_lds_sync();
+  }
+  int pos = 0, eq_before = 0;
+  for (int g0 = 0; g0 < ng; g0 += 64) {
+    const int g = g0 + lane;
+    const uint32_t k = g < ng ? keys[g] : 0u;
+    const bool eq = g < ng && k == pre;
+    int n_eq;
+    const int eq_excl = wave_excl_scan(eq ? 1 : 0, lane, n_eq);
+    const bool take = (g < ng && k > pre) || (eq && eq_before + eq_excl < need);
+    int n_take;
+    const int p = wave_excl_scan(take ? 1 : 0, lane, n_take);
+    if (take) sel[pos + p] = g;
+    pos += n_take;
+    eq_before += n_eq;
+  }
+  wave_lds_sync();
 }
 
 // -------------------------------------------------------- summary kernel ---
@@ -777,24 +740,21 @@ __device__ __forceinline__ void load_vals(rsrc_t rv, rsrc_t rvn, int t, int lane
 
 // Byte offsets of the route body's LDS arrays after `base` (16-byte aligned):
 // [logits G*ngp f32][keys u32, then the emitted selection][hist 256]
-// [fetched bitmap][selected candidates][candidates (uint2) or the fallback's
-// selection].
+// [fetched bitmap][the threshold bucket's groups (uint2 x 64)].
 struct RouteLayout {
-  int logits, keys, hist, fmask, cmask, cand, end;
+  int logits, keys, hist, fmask, cand, end;
 };
 __host__ __device__ inline RouteLayout route_layout(int G, int ng, int beta, int base) {
+  (void)beta;
   const int ngp = (ng + 15) & ~15;
   const int words4 = ((ngp + 31) / 32 + 3) & ~3;
-  const int cand_bytes = (beta * 4 > (ngp < kCandCap ? ngp : kCandCap) * 8)
-                             ? beta * 4 : (ngp < kCandCap ? ngp : kCandCap) * 8;
   RouteLayout r;
   r.logits = base;
   r.keys = r.logits + G * ngp * 4;
   r.hist = r.keys + ((ngp + 31) & ~31) * 4;
   r.fmask = r.hist + 256 * 4;
-  r.cmask = r.fmask + words4 * 4;
-  r.cand = r.cmask + words4 * 4;
-  r.end = r.cand + ((cand_bytes + 15) & ~15);
+  r.cand = r.fmask + words4 * 4;
+  r.end = r.cand + 64 * 8;
   return r;
 }
 
@@ -807,7 +767,6 @@ struct RouteLds {
   uint32_t* keys;
   int* hist;
   uint32_t* fmask;
-  uint32_t* cmask;
   uint2* cand;
   float* dummy;     // 64 x 4 floats: landing slot of the lanes without a head
   float* scratch;   // wave-combine scratch, kWaves * kMaxG * (D+2) floats, free
@@ -823,7 +782,6 @@ __device__ __forceinline__ RouteLds route_lds(char* base, const RouteLayout& r, 
   L.keys = reinterpret_cast<uint32_t*>(base + r.keys);
   L.hist = reinterpret_cast<int*>(base + r.hist);
   L.fmask = reinterpret_cast<uint32_t*>(base + r.fmask);
-  L.cmask = reinterpret_cast<uint32_t*>(base + r.cmask);
   L.cand = reinterpret_cast<uint2*>(base + r.cand);
   L.dummy = dummy;
   L.scratch = scratch;
@@ -842,8 +800,6 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
                                            int unit) {
   constexpr int CB3 = 3 * D / 8;
   __shared__ float s_cb[8];
-  __shared__ int s_tmp[kWaves];
-  __shared__ int s_sel[4];
   __shared__ float s_lo[kWaves], s_hi[kWaves];
   __shared__ float s_mh[kWaves][kMaxG];
   const int ngp = (a.ng + 15) & ~15;
@@ -852,7 +808,6 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   uint32_t* keys = L.keys;
   int* hist = L.hist;
   uint32_t* fmask = L.fmask;
-  uint32_t* cmask = L.cmask;
   uint2* cand = L.cand;
   // the emitted selection reuses the keys once the threshold step is done
   // (the candidates may still be read by slower waves while it is written)
@@ -887,12 +842,8 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   if (tid < 8) s_cb[tid] = cbv;
   rotate_query<D>(qin, a.scale * rsqrtf((float)D), qf, tid);
   const int words = (ngp + 31) >> 5;
-  for (int w = tid; w < words; w += kThreads) {
-    fmask[w] = 0u;
-    cmask[w] = 0u;
-  }
+  for (int w = tid; w < words; w += kThreads) fmask[w] = 0u;
   for (int b = tid; b < 256; b += kThreads) hist[b] = 0;
-  if (tid < 4) s_sel[tid] = 0;
   lds_barrier();
   build_lut3(L.lut3, s_cb, tid);
   half8 qb[D / 32];
@@ -940,28 +891,22 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
     s_hi[wave] = whi;
   }
   if (gq == 0 && writer) s_mh[wave][c] = cmax;
-  // Phase 2.  Every wave streams the values of ALL summaries into its
-  // softmax partial; the fetched ones are subtracted at the end with the
-  // same weights.  The top-beta runs alongside: once every wave has its
-  // first K value tiles, the work-group forms the router scores and their
-  // histogram (2a); then the last wave alone finds the threshold, ranks the
-  // groups of the threshold bucket, emits the selection and subtracts the
-  // fetched summaries (2b), while the other waves stream the remaining value
-  // tiles.  No barrier separates the selection steps.
+  // Phase 2.  Seven waves stream the values of ALL summaries into their
+  // softmax partials (tiles w, w + 7, ...); the fetched ones are subtracted
+  // at the end with the same weights.  The eighth wave meanwhile forms the
+  // router scores and their histogram, finds the threshold, ranks the
+  // threshold bucket, emits the selection and subtracts the fetched
+  // summaries.  No barrier until the end.
   constexpr int K = kValDepth;
   constexpr int kSel = kWaves - 1;  // the selecting wave
   const bool stream = a.want_partial && a.beta < a.ng;  // else the partial is empty
-  // part 1: tiles wave + 8i (i < K) on every wave; part 2: the tiles from 8K
-  // on, round-robin over the other waves.  Indices past a part read nothing.
-  const int n1v = stream ? min(K, wave_iters(n_tiles, wave)) : 0;
-  const int n2v = (stream && wave != kSel && kWaves * K + wave < n_tiles)
-                      ? (n_tiles - kWaves * K - wave + kSel - 1) / kSel
-                      : 0;
-  auto tile1 = [&](int i) { return i < n1v ? wave + i * kWaves : n_tiles; };
-  auto tile2 = [&](int i) { return i < n2v ? kWaves * K + wave + i * kSel : n_tiles; };
+  const int nv = (stream && wave != kSel && wave < n_tiles) ? (n_tiles - wave + kSel - 1) / kSel : 0;
+  auto tile = [&](int i) { return i < nv ? wave + i * kSel : n_tiles; };  // past the end: no reads
   ValTile vt[K];
+  if (wave != kSel) {
 #pragma unroll
-  for (int j = 0; j < K - 1; ++j) load_vals<D>(rv, rvn, tile1(j), lane, vt[j]);
+    for (int j = 0; j < K - 1; ++j) load_vals<D>(rv, rvn, tile(j), lane, vt[j]);
+  }
   lds_barrier();
 
   __builtin_amdgcn_s_setprio(2);
@@ -986,95 +931,79 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
     pv3<D>(V.va, vsh, weight_operand(w, lane), lane4, lut3, st.O);
   };
   const float* lrow = logits + hcol * ngp + 4 * gq;
-  auto use_tile = [&](int t, const ValTile& V) {
-    const f32x4 lg4 = *reinterpret_cast<const f32x4*>(lrow + 16 * t);
-    float lg[4] = {lg4[0], lg4[1], lg4[2], lg4[3]};
-    if (t == n_tiles - 1) {  // wave-uniform
-      const uint32_t tr = tail_rows(t);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) lg[r] = ((tr >> r) & 1u) ? kNegInf : lg[r];
-    }
-    consume(lg, V, 1.f);
-  };
-
-  // values, part 1
-  pipeline<K>(
-      n1v, vt, [&](int i, ValTile& V) { load_vals<D>(rv, rvn, tile1(i), lane, V); },
-      [&](int i, const ValTile& V) { use_tile(tile1(i), V); });
-  // part 2's first tiles load during the score step
-#pragma unroll
-  for (int j = 0; j < K - 1; ++j) load_vals<D>(rv, rvn, tile2(j), lane, vt[j]);
-
-  // (2a) router scores of this thread's groups 4t .. 4t+3 (+2048 per pass),
-  // score histogram
-  const bool hsel = a.want_topk && a.beta > 0 && a.beta < a.ng;
-  float lo = kPosInf, hi = kNegInf;
-  for (int w = 0; w < kWaves; ++w) {
-    lo = fminf(lo, s_lo[w]);
-    hi = fmaxf(hi, s_hi[w]);
-  }
-  const float bscale = (hi > lo) ? 256.f / (hi - lo) : 0.f;
-  if (a.want_topk) {
-    const float inv_g = 1.f / (float)a.G;
-    for (int g0 = 4 * tid; g0 < 32 * words; g0 += 4 * kThreads) {
-      f32x4 vmax = {kNegInf, kNegInf, kNegInf, kNegInf}, vsum = {0.f, 0.f, 0.f, 0.f};
-      for (int h = 0; h < a.G; ++h) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(logits + h * ngp + g0);
-        vmax = f32x4{fmaxf(vmax[0], x[0]), fmaxf(vmax[1], x[1]), fmaxf(vmax[2], x[2]),
-                     fmaxf(vmax[3], x[3])};
-        vsum += x;
-      }
-      u32x4 k4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool ok = g0 + e < a.ng;
-        const float v = (a.agg == HSQ_AGG_MAX) ? vmax[e] : vsum[e] * inv_g;
-        k4[e] = ok ? fkey(v) : 0u;
-        if (ok) {
-          if (hsel) atomicAdd(&hist[score_bucket(k4[e], lo, bscale)], 1);
-          if (a.scores_out) a.scores_out[(size_t)unit * a.ng + g0 + e] = v;
-        }
-      }
-      *reinterpret_cast<u32x4*>(keys + g0) = k4;
-    }
-    if (a.beta >= a.ng)  // every group fetched
-      for (int w = tid; w < words; w += kThreads) {
-        const int left = a.ng - 32 * w;
-        fmask[w] = left >= 32 ? 0xffffffffu : (left <= 0 ? 0u : ((1u << left) - 1u));
-      }
-  } else if (a.given) {  // the given selection
-    for (int i = tid; i < a.beta; i += kThreads) {
-      const int g = a.given[(size_t)unit * a.beta + i];
-      if (g >= 0 && g < a.ng) atomicOr(&fmask[g >> 5], 1u << (g & 31));
-    }
-  }
-  lds_barrier();
-
-  // (2b) the threshold bucket and how many of its groups to take (every
-  // wave reads them off the histogram).  More than 64 groups in that bucket
-  // (heavy ties): radix select over all keys, block-wide, into the bitmap.
-  int bt = 0, need = 0;
-  bool fallback = false;
-  if (hsel) {
-    hist_threshold(hist, a.beta, lane, bt, need);
-    fallback = __builtin_amdgcn_readfirstlane(hist[bt]) > 64;
-    if (fallback) {
-      int32_t* tsel = reinterpret_cast<int32_t*>(cand);
-      top_beta(keys, a.ng, a.beta, hist, s_tmp, tsel, tid);
-      for (int i = tid; i < a.beta; i += kThreads) atomicOr(&fmask[tsel[i] >> 5], 1u << (tsel[i] & 31));
-      lds_barrier();
-    }
-  }
 
   if (wave != kSel) {
-    // values, part 2
     pipeline<K>(
-        n2v, vt, [&](int i, ValTile& V) { load_vals<D>(rv, rvn, tile2(i), lane, V); },
-        [&](int i, const ValTile& V) { use_tile(tile2(i), V); });
+        nv, vt, [&](int i, ValTile& V) { load_vals<D>(rv, rvn, tile(i), lane, V); },
+        [&](int i, const ValTile& V) {
+          const int t = tile(i);
+          const f32x4 lg4 = *reinterpret_cast<const f32x4*>(lrow + 16 * t);
+          float lg[4] = {lg4[0], lg4[1], lg4[2], lg4[3]};
+          if (t == n_tiles - 1) {  // wave-uniform
+            const uint32_t tr = tail_rows(t);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) lg[r] = ((tr >> r) & 1u) ? kNegInf : lg[r];
+          }
+          consume(lg, V, 1.f);
+        });
   } else {
-    // bitmap word w (lane w % 64): groups in buckets above bt, and the
-    // groups of bucket bt
+    // (2a) router scores (max or mean over the G heads) as order-preserving
+    // keys, 4 groups per lane and pass; their histogram over [lo, hi]
+    const bool hsel = a.want_topk && a.beta > 0 && a.beta < a.ng;
+    float lo = kPosInf, hi = kNegInf;
+    for (int w = 0; w < kWaves; ++w) {
+      lo = fminf(lo, s_lo[w]);
+      hi = fmaxf(hi, s_hi[w]);
+    }
+    const float bscale = (hi > lo) ? 256.f / (hi - lo) : 0.f;
+    if (a.want_topk) {
+      const float inv_g = 1.f / (float)a.G;
+      for (int g0 = 4 * lane; g0 < 32 * words; g0 += 256) {
+        f32x4 vmax = {kNegInf, kNegInf, kNegInf, kNegInf}, vsum = {0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < a.G; ++h) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(logits + h * ngp + g0);
+          vmax = f32x4{fmaxf(vmax[0], x[0]), fmaxf(vmax[1], x[1]), fmaxf(vmax[2], x[2]),
+                       fmaxf(vmax[3], x[3])};
+          vsum += x;
+        }
+        u32x4 k4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = g0 + e < a.ng;
+          const float v = (a.agg == HSQ_AGG_MAX) ? vmax[e] : vsum[e] * inv_g;
+          k4[e] = ok ? fkey(v) : 0u;
+          if (ok) {
+            if (hsel) atomicAdd(&hist[score_bucket(k4[e], lo, bscale)], 1);
+            if (a.scores_out) a.scores_out[(size_t)unit * a.ng + g0 + e] = v;
+          }
+        }
+        *reinterpret_cast<u32x4*>(keys + g0) = k4;
+      }
+      if (a.beta >= a.ng)  // every group fetched
+        for (int w = lane; w < words; w += 64) {
+          const int left = a.ng - 32 * w;
+          fmask[w] = left >= 32 ? 0xffffffffu : (left <= 0 ? 0u : ((1u << left) - 1u));
+        }
+    } else if (a.given) {  // the given selection
+      for (int i = lane; i < a.beta; i += 64) {
+        const int g = a.given[(size_t)unit * a.beta + i];
+        if (g >= 0 && g < a.ng) atomicOr(&fmask[g >> 5], 1u << (g & 31));
+      }
+    }
+    wave_lds_sync();
+
+    // (2b) the threshold bucket and how many of its groups to take.  At most
+    // 64 groups in it: rank them here.  More (heavy ties): radix select.
+    int bt = 0, need = 0;
+    bool fallback = false;
+    if (hsel) {
+      hist_threshold(hist, a.beta, lane, bt, need);
+      fallback = __builtin_amdgcn_readfirstlane(hist[bt]) > 64;
+      if (fallback) top_beta_wave(keys, a.ng, a.beta, hist, sel, lane);
+    }
     const bool rank_here = hsel && !fallback;
+    // bitmap word w (lane w % 64): groups in buckets above bt, and the groups
+    // of bucket bt
     auto word_bits = [&](int w, uint32_t& above, uint32_t& inb) {
       above = 0u;
       inb = 0u;
@@ -1110,6 +1039,7 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
         }
         nc += total;
       }
+      wave_lds_sync();
       if (lane < nc) me = cand[lane];
     }
     // rank by (key descending, index ascending): the first `need` are taken
@@ -1124,37 +1054,47 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
       chosen = lane < nc && rank < need;
     }
     const uint64_t chosen_mask = __builtin_amdgcn_ballot_w64(chosen);
-    // emit the selection in ascending order
+    // emit the selection in ascending order (the radix select already did)
     int nsel = 0;
-    for (int w0 = 0; w0 < words; w0 += 64) {
-      const int w = w0 + lane;
-      uint32_t bits;
-      if (rank_here) {
-        uint32_t inb;
-        if (w0 == 0)
-          bits = above0;
-        else
-          word_bits(w, bits, inb);
-        for (uint64_t m = chosen_mask; m; m &= m - 1u) {
-          const int j = __ffsll((unsigned long long)m) - 1;
-          const uint32_t g = __builtin_amdgcn_readlane(me.x, j);
-          bits |= ((int)(g >> 5) == w) ? 1u << (g & 31) : 0u;
-        }
-      } else {
-        bits = (w < words) ? fmask[w] : 0u;
-      }
-      int total;
-      int pos = nsel + wave_excl_scan(__popc(bits), lane, total);
-      while (bits) {
-        const int g = 32 * w + __ffs(bits) - 1;
-        sel[pos] = g;
+    if (fallback) {
+      nsel = a.beta;
+      for (int pos = lane; pos < nsel; pos += 64) {
+        const int g = sel[pos];
         if (a.want_topk && a.idx) a.idx[(size_t)unit * a.beta + pos] = g;
         if (recoff) recoff[pos] = (int32_t)((uint32_t)g * rec);
-        ++pos;
-        bits &= bits - 1u;
       }
-      nsel += total;
+    } else {
+      for (int w0 = 0; w0 < words; w0 += 64) {
+        const int w = w0 + lane;
+        uint32_t bits;
+        if (rank_here) {
+          uint32_t inb;
+          if (w0 == 0)
+            bits = above0;
+          else
+            word_bits(w, bits, inb);
+          for (uint64_t m = chosen_mask; m; m &= m - 1u) {
+            const int j = __ffsll((unsigned long long)m) - 1;
+            const uint32_t g = __builtin_amdgcn_readlane(me.x, j);
+            bits |= ((int)(g >> 5) == w) ? 1u << (g & 31) : 0u;
+          }
+        } else {
+          bits = (w < words) ? fmask[w] : 0u;
+        }
+        int total;
+        int pos = nsel + wave_excl_scan(__popc(bits), lane, total);
+        while (bits) {
+          const int g = 32 * w + __ffs(bits) - 1;
+          sel[pos] = g;
+          if (a.want_topk && a.idx) a.idx[(size_t)unit * a.beta + pos] = g;
+          if (recoff) recoff[pos] = (int32_t)((uint32_t)g * rec);
+          ++pos;
+          bits &= bits - 1u;
+        }
+        nsel += total;
+      }
     }
+    wave_lds_sync();
 
     // subtract the fetched summaries (list tiles of 16) with the same
     // arithmetic as they were added; rows past the list read nothing
