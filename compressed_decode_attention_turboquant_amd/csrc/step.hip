@@ -947,6 +947,8 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
           consume(lg, V, 1.f);
         });
   } else {
+    // this wave gates the work-group's finish: its selection goes first
+    __builtin_amdgcn_s_setprio(3);
     // (2a) router scores (max or mean over the G heads) as order-preserving
     // keys, 4 groups per lane and pass; their histogram over [lo, hi]
     const bool hsel = a.want_topk && a.beta > 0 && a.beta < a.ng;
@@ -1096,6 +1098,7 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
     }
     wave_lds_sync();
 
+    __builtin_amdgcn_s_setprio(2);
     // subtract the fetched summaries (list tiles of 16) with the same
     // arithmetic as they were added; rows past the list read nothing
     constexpr int RB = 3 * D / 8;
