@@ -663,7 +663,10 @@ __device__ __forceinline__ f32x4 qk3(const uint32_t (&kw)[3], const half8 (&b)[D
   }
   f32x4 r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = acc[i] + dpp_f<0x128>(acc[i]);  // row_ror:8
+  for (int i = 0; i < 4; ++i) {  // row_ror:8 (a plain move, so that it fuses into the add)
+    const int v = __float_as_int(acc[i]);
+    r[i] = acc[i] + __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x128, 0xf, 0xf, true));
+  }
   return r;
 }
 
@@ -729,13 +732,16 @@ __device__ __forceinline__ void load_vals(rsrc_t rv, rsrc_t rvn, int t, int lane
                                           ValTile& T) {
   constexpr int RB = 3 * D / 8;
   const int gq = lane >> 4;
-  uint32_t base = (uint32_t)(16 * t + 4 * gq) * RB + val_byte<D>(lane);
+  // the tile's part of the offsets is wave-uniform (scalar arithmetic)
+  const uint32_t tv = (uint32_t)__builtin_amdgcn_readfirstlane(t * (16 * RB));
+  const uint32_t tn = (uint32_t)__builtin_amdgcn_readfirstlane(t * 64);
+  uint32_t base = tv + (uint32_t)(4 * gq * RB) + val_byte<D>(lane);
   // kept opaque so that the row steps j * RB become immediate offsets of
   // the loads (range-checked like the register part) instead of adds
   asm("" : "+v"(base));
 #pragma unroll
   for (int j = 0; j < 4; ++j) T.va[j] = ld32(rv, base + j * RB);
-  T.vn = ldf4(rvn, (uint32_t)(16 * t + 4 * gq) * 4);
+  T.vn = ldf4(rvn, tn + (uint32_t)(16 * gq));
 }
 
 // Byte offsets of the route body's LDS arrays after `base` (16-byte aligned):
@@ -901,7 +907,8 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   constexpr int kSel = kWaves - 1;  // the selecting wave
   const bool stream = a.want_partial && a.beta < a.ng;  // else the partial is empty
   const int nv = (stream && wave != kSel && wave < n_tiles) ? (n_tiles - wave + kSel - 1) / kSel : 0;
-  auto tile = [&](int i) { return i < nv ? wave + i * kSel : n_tiles; };  // past the end: no reads
+  // past its last tile a wave names tiles past the end (no reads)
+  auto tile = [&](int i) { return wave + i * kSel + (i < nv ? 0 : n_tiles); };
   ValTile vt[K];
   if (wave != kSel) {
 #pragma unroll
