@@ -1220,26 +1220,38 @@ __device__ __forceinline__ void load_tok_at(const TokBufs& B, int t, int n1t, in
   const int tk = (N == 16) ? n : (n & 7);            // key row within the group
   const int tr = (N == 16) ? 4 * gq : 4 * (gq & 1);  // first value row within the group
   const uint32_t vl = (D == 128) ? 4u * n : 4u * (n >> 1);  // this lane's value dword
-  const bool l1 = t < n1t;
-  const uint32_t r0 = 16u * (uint32_t)t;
-  // an offset built on kFar stays past the end of every buffer (reads zero)
-  const uint32_t ko = l1 ? (r0 + n) * CB + KB * gq : bk + tk * CB + KB * gq;
-  const uint32_t kno = l1 ? (r0 + 4 * gq) * 4 : br + N * CB + 4 * tr;
-  const uint32_t vno = l1 ? (r0 + 4 * gq) * 4 : br + N * (2 * CB + 4) + 4 * tr;
-  uint32_t vo = (l1 ? (r0 + 4 * gq) * CB : br + N * (CB + 4) + tr * CB) + vl;
-  asm("" : "+v"(vo));  // the row steps j * CB become immediate offsets
-  const rsrc_t rk = l1 ? B.l1k : B.l3, rkn = l1 ? B.l1kn : B.l3;
-  const rsrc_t rv = l1 ? B.l1v : B.l3, rvn = l1 ? B.l1vn : B.l3;
-  if constexpr (D == 128) {
-    T.kw = ld128(rk, ko);
-  } else {
-    const u32x2 w = ld64(rk, ko);
-    T.kw = u32x4{w.x, w.y, 0u, 0u};
-  }
-  T.kn = ldf4(rkn, kno);
-  T.vn = ldf4(rvn, vno);
+  // Two straight-line forms with the same loads (so the waits stay exact);
+  // the tile's part of the L1 offsets is wave-uniform (scalar arithmetic).
+  // An archive offset built on kFar stays past the end of every buffer.
+  if (t < n1t) {  // wave-uniform
+    const uint32_t tc = (uint32_t)__builtin_amdgcn_readfirstlane(t * (16 * CB));
+    const uint32_t tn = (uint32_t)__builtin_amdgcn_readfirstlane(t * 64);
+    uint32_t vo = tc + (uint32_t)(4 * gq * CB) + vl;
+    asm("" : "+v"(vo));  // the row steps j * CB become immediate offsets
+    if constexpr (D == 128) {
+      T.kw = ld128(B.l1k, tc + (uint32_t)(n * CB) + KB * gq);
+    } else {
+      const u32x2 w = ld64(B.l1k, tc + (uint32_t)(n * CB) + KB * gq);
+      T.kw = u32x4{w.x, w.y, 0u, 0u};
+    }
+    T.kn = ldf4(B.l1kn, tn + (uint32_t)(16 * gq));
+    T.vn = ldf4(B.l1vn, tn + (uint32_t)(16 * gq));
 #pragma unroll
-  for (int j = 0; j < 4; ++j) T.va[j] = ld32(rv, vo + j * CB);
+    for (int j = 0; j < 4; ++j) T.va[j] = ld32(B.l1v, vo + j * CB);
+  } else {
+    uint32_t vo = br + (uint32_t)(N * (CB + 4) + tr * CB) + vl;
+    asm("" : "+v"(vo));
+    if constexpr (D == 128) {
+      T.kw = ld128(B.l3, bk + (uint32_t)(tk * CB) + KB * gq);
+    } else {
+      const u32x2 w = ld64(B.l3, bk + (uint32_t)(tk * CB) + KB * gq);
+      T.kw = u32x4{w.x, w.y, 0u, 0u};
+    }
+    T.kn = ldf4(B.l3, br + (uint32_t)(N * CB + 4 * tr));
+    T.vn = ldf4(B.l3, br + (uint32_t)(N * (2 * CB + 4) + 4 * tr));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) T.va[j] = ld32(B.l3, vo + j * CB);
+  }
 }
 // First archive slot of tile t (wave-uniform; 0 for L1 tiles, whose loads
 // ignore the record offsets).
