@@ -967,13 +967,21 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
     const float bscale = (hi > lo) ? 256.f / (hi - lo) : 0.f;
     if (a.want_topk) {
       const float inv_g = 1.f / (float)a.G;
+      const int hl = a.G - 1;
       for (int g0 = 4 * lane; g0 < 32 * words; g0 += 256) {
-        f32x4 vmax = {kNegInf, kNegInf, kNegInf, kNegInf}, vsum = {0.f, 0.f, 0.f, 0.f};
-        for (int h = 0; h < a.G; ++h) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(logits + h * ngp + g0);
-          vmax = f32x4{fmaxf(vmax[0], x[0]), fmaxf(vmax[1], x[1]), fmaxf(vmax[2], x[2]),
-                       fmaxf(vmax[3], x[3])};
-          vsum += x;
+        // every head's row is read before the first use (one LDS round trip
+        // per pass); rows past the last head repeat it, and the sum skips them
+        f32x4 x[kMaxG];
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h)
+          x[h] = *reinterpret_cast<const f32x4*>(logits + min(h, hl) * ngp + g0);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 vmax = x[0], vsum = x[0];
+#pragma unroll
+        for (int h = 1; h < kMaxG; ++h) {
+          vmax = f32x4{fmaxf(vmax[0], x[h][0]), fmaxf(vmax[1], x[h][1]),
+                       fmaxf(vmax[2], x[h][2]), fmaxf(vmax[3], x[h][3])};
+          if (h <= hl) vsum += x[h];  // wave-uniform
         }
         u32x4 k4;
 #pragma unroll
@@ -1016,13 +1024,18 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
     auto word_bits = [&](int w, uint32_t& above, uint32_t& inb) {
       above = 0u;
       inb = 0u;
-      if (w >= words) return;
+      // the word's eight reads go out together (lanes past the last word
+      // read the last one and keep no bits)
+      const int wr = min(w, words - 1);
+      u32x4 k4[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) k4[q] = *reinterpret_cast<const u32x4*>(keys + 32 * wr + 4 * q);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const u32x4 k4 = *reinterpret_cast<const u32x4*>(keys + 32 * w + 4 * q);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int b = score_bucket(k4[e], lo, bscale);
+          const int b = score_bucket(k4[q][e], lo, bscale);
           const bool in = 32 * w + 4 * q + e < a.ng;
           above |= (in && b > bt) ? 1u << (4 * q + e) : 0u;
           inb |= (in && b == bt) ? 1u << (4 * q + e) : 0u;
@@ -1115,25 +1128,38 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
       ValTile V;
       float lg[4];
     };
+    // The list rows of tile j + 1 are read while tile j's loads are issued
+    // (the list's last tile is reread past its end; sel holds 16 * ntl
+    // entries); the logits are masked at their use, so no load waits on LDS.
+    const float* lcol = logits + hcol * ngp;
+    auto sel_rows = [&](int j) {
+      return *reinterpret_cast<const u32x4*>(sel + 16 * min(j, max(ntl - 1, 0)) + 4 * gq);
+    };
+    u32x4 gnext = sel_rows(0);
     auto corr_load = [&](int j, CorrTile& C) {
+      const u32x4 g4 = gnext;
+      gnext = sel_rows(j + 1);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int k = 16 * j + 4 * gq + r;
-        const bool in = k < nsel;
-        const uint32_t g = (uint32_t)sel[max(min(k, nsel - 1), 0)];
+        const bool in = 16 * j + 4 * gq + r < nsel;
+        const uint32_t g = in ? g4[r] : 0u;
         const uint32_t far = in ? 0u : kFar;
         uint32_t vo = (g * RB + vb) | far, no = (g * 4u) | far;
         asm("" : "+v"(vo), "+v"(no));  // one load at one address per row
         C.V.va[r] = ld32(rv, vo);
         C.V.vn[r] = __uint_as_float(ld32(rvn, no));
-        const float x = logits[hcol * ngp + (int)g];
-        C.lg[r] = in ? x : kNegInf;
+        C.lg[r] = lcol[g];
       }
     };
     CorrTile ct[K];
 #pragma unroll
     for (int j = 0; j < K - 1; ++j) corr_load(j, ct[j]);
-    pipeline<K>(ntl, ct, corr_load, [&](int, const CorrTile& C) { consume(C.lg, C.V, -1.f); });
+    pipeline<K>(ntl, ct, corr_load, [&](int j, const CorrTile& C) {
+      float lg[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) lg[r] = (16 * j + 4 * gq + r < nsel) ? C.lg[r] : kNegInf;
+      consume(lg, C.V, -1.f);
+    });
   }
   if (!a.want_partial) return;
   lds_barrier();  // the logits are no longer needed: reuse as scratch
