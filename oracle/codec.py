@@ -23,6 +23,16 @@ Readings taken where the pages are silent:
   equals nearest-centroid with ties to the lower index.
 * Packing: 4-bit, byte k = code[2k] | code[2k+1] << 4.  3-bit, an LSB-first
   bit stream, code i in bits [3i, 3i+3), bit j in byte j // 8 at position j % 8.
+  2-bit, the same stream: byte k = code[4k] | code[4k+1] << 2 | code[4k+2] << 4
+  | code[4k+3] << 6.
+
+Variants from the same page's ablation (its list of non-dominated methods and
+its results at a 2-bit budget):
+* Plain-KV, scalar quantisation with the rotation off.  Reading: R = I, every
+  other step unchanged (norm, the same Beta Lloyd-Max codebook for (d, b),
+  threshold count, packing); sign_words=None selects it.  On isotropic data
+  x / r is already a uniform unit vector, so the codebook fits it exactly.
+* b = 2: a four-cell codebook of the same family.
 """
 import numpy as np
 
@@ -76,25 +86,30 @@ def encode(x, sign_words, thresholds):
     x = to_f64(x)
     n, d = x.shape
     r = np.sqrt(np.sum(x * x, axis=1))
-    # y = R (x / r) = H (D x) / (sqrt(d) r).  The +-1 sums H (D x) are formed
-    # first: for fp32 / bf16 inputs they are exact in fp64, so a coordinate
-    # whose exact value sits on a threshold (0 is one) is decided exactly.
-    hx = (x * sign_vector(sign_words, d)[None, :]) @ hadamard(d).T
     y = np.zeros_like(x)
     nz = r > 0
-    y[nz] = hx[nz] / (np.sqrt(d) * r[nz, None])
+    if sign_words is None:  # Plain-KV: no rotation, y = x / r
+        y[nz] = x[nz] / r[nz, None]
+    else:
+        # y = R (x / r) = H (D x) / (sqrt(d) r).  The +-1 sums H (D x) are
+        # formed first: for fp32 / bf16 inputs they are exact in fp64, so a
+        # coordinate whose exact value sits on a threshold (0 is one) is
+        # decided exactly.
+        hx = (x * sign_vector(sign_words, d)[None, :]) @ hadamard(d).T
+        y[nz] = hx[nz] / (np.sqrt(d) * r[nz, None])
     t = np.asarray(thresholds, dtype=np.float32).astype(np.float64)
     codes = np.sum(y[:, :, None] > t[None, None, :], axis=2).astype(np.uint8)
     return codes, r.astype(np.float32), y
 
 
 def decode(codes, norms, sign_words, centroids):
-    """x_hat = r * R^T c[code] for every row; fp64 [n, d]."""
+    """x_hat = r * R^T c[code] for every row (R = I when sign_words is None);
+    fp64 [n, d]."""
     codes = np.asarray(codes)
     n, d = codes.shape
     c = np.asarray(centroids, dtype=np.float32).astype(np.float64)
     unit_rot = c[codes.astype(np.int64)]
-    x_unit = unit_rot @ rotation_matrix(sign_words, d)
+    x_unit = unit_rot if sign_words is None else unit_rot @ rotation_matrix(sign_words, d)
     return x_unit * np.asarray(norms, dtype=np.float32).astype(np.float64)[:, None]
 
 
@@ -104,13 +119,16 @@ def pack(codes, bits):
     n, d = codes.shape
     if bits == 4:
         return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    if bits == 2:
+        return (codes[:, 0::4] | (codes[:, 1::4] << 2) | (codes[:, 2::4] << 4)
+                | (codes[:, 3::4] << 6)).astype(np.uint8)
     if bits == 3:
         # bit stream: bit j of row = bit (j % 3) of code j // 3
         stream = np.zeros((n, 3 * d), dtype=np.uint8)
         for b in range(3):
             stream[:, b::3] = (codes >> b) & 1
         return np.packbits(stream, axis=1, bitorder="little")
-    raise ValueError("bits must be 3 or 4")
+    raise ValueError("bits must be 2, 3 or 4")
 
 
 def unpack(packed, bits, d):
@@ -122,13 +140,18 @@ def unpack(packed, bits, d):
         out[:, 0::2] = packed & 0x0F
         out[:, 1::2] = packed >> 4
         return out
+    if bits == 2:
+        out = np.empty((n, d), dtype=np.uint8)
+        for k in range(4):
+            out[:, k::4] = (packed >> (2 * k)) & 0x03
+        return out
     if bits == 3:
         stream = np.unpackbits(packed, axis=1, bitorder="little")[:, : 3 * d]
         out = np.zeros((n, d), dtype=np.uint8)
         for b in range(3):
             out |= (stream[:, b::3] << b).astype(np.uint8)
         return out
-    raise ValueError("bits must be 3 or 4")
+    raise ValueError("bits must be 2, 3 or 4")
 
 
 def code_bytes(d, bits):
