@@ -200,6 +200,12 @@ def headline(args, torch, hsq, W):
     return res, layers
 
 
+# (label, bits, rotation on): TurboQuant at the tier widths, and the ablation's
+# 2-bit budget and Plain-KV (rotation off) variants
+CODEC_VARIANTS = (("4bit", 4, True), ("3bit", 3, True), ("2bit", 2, True),
+                  ("plain_4bit", 4, False), ("plain_2bit", 2, False))
+
+
 def codec_rates(torch, hsq, W):
     dev = "cuda"
     c = W.CODEC
@@ -207,29 +213,26 @@ def codec_rates(torch, hsq, W):
     ks, vs = W.codec_signs(c)
     dks = torch.from_numpy(ks.view(np.int32)).to(dev)
     dvs = torch.from_numpy(vs.view(np.int32)).to(dev)
-    cb = codebooks(hsq, c.d, dev)
     stream = torch.cuda.Stream()
     n = c.heads * c.tokens
     out = {}
-    for bits in (4, 3):
-        thr = cb["thr4" if bits == 4 else "thr3"]
-        cen = cb["cb4" if bits == 4 else "cb3"]
+    for label, bits, rot in CODEC_VARIANTS:
+        cen, thr = (torch.from_numpy(a).to(dev) for a in hsq.codebook(c.d, bits))
+        sk, sv = (dks, dvs) if rot else (None, None)
+        rk = dict(vecs_per_rot=c.tokens, n_rot=c.heads)
         with torch.cuda.stream(stream):
-            kc, kn = hsq.encode(k.view(n, c.d), bits, dks, thr, vecs_per_rot=c.tokens, n_rot=c.heads)
-            vc, vn = hsq.encode(v.view(n, c.d), bits, dvs, thr, vecs_per_rot=c.tokens, n_rot=c.heads)
-            dk = hsq.decode(kc, kn, bits, c.d, dks, cen, vecs_per_rot=c.tokens, n_rot=c.heads,
-                            out_dtype=torch.bfloat16)
+            kc, kn = hsq.encode(k.view(n, c.d), bits, sk, thr, **rk)
+            vc, vn = hsq.encode(v.view(n, c.d), bits, sv, thr, **rk)
+            dk = hsq.decode(kc, kn, bits, c.d, sk, cen, out_dtype=torch.bfloat16, **rk)
             stream.synchronize()
             ge = torch.cuda.CUDAGraph()
             with torch.cuda.graph(ge, stream=stream):
-                hsq.encode(k.view(n, c.d), bits, dks, thr, vecs_per_rot=c.tokens, n_rot=c.heads)
-                hsq.encode(v.view(n, c.d), bits, dvs, thr, vecs_per_rot=c.tokens, n_rot=c.heads)
+                hsq.encode(k.view(n, c.d), bits, sk, thr, **rk)
+                hsq.encode(v.view(n, c.d), bits, sv, thr, **rk)
             gd = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gd, stream=stream):
-                hsq.decode(kc, kn, bits, c.d, dks, cen, vecs_per_rot=c.tokens, n_rot=c.heads,
-                           out_dtype=torch.bfloat16)
-                hsq.decode(vc, vn, bits, c.d, dvs, cen, vecs_per_rot=c.tokens, n_rot=c.heads,
-                           out_dtype=torch.bfloat16)
+                hsq.decode(kc, kn, bits, c.d, sk, cen, out_dtype=torch.bfloat16, **rk)
+                hsq.decode(vc, vn, bits, c.d, sv, cen, out_dtype=torch.bfloat16, **rk)
         time_graph(torch, ge, 5, stream)
         te = time_graph(torch, ge, 50, stream) / 50
         time_graph(torch, gd, 5, stream)
@@ -239,13 +242,14 @@ def codec_rates(torch, hsq, W):
         # relative round-trip error of the bf16 decode (diagnostic, cf. relMSE)
         rel = float(((dk.float() - k.view(n, c.d).float()).pow(2).sum(1) /
                      k.view(n, c.d).float().pow(2).sum(1)).mean())
-        out[f"{bits}bit"] = {
+        out[label] = {
             "encode_us": te * 1e3, "encode_in_gbs": in_b / (te * 1e-3) / 1e9,
             "encode_hbm_frac": (in_b + code_b) / (te * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "decode_us": td * 1e3, "decode_out_gbs": in_b / (td * 1e-3) / 1e9,
             "decode_hbm_frac": (in_b + code_b) / (td * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "relmse_k": rel,
         }
+        del kc, kn, vc, vn, dk, ge, gd
     del k, v
     return out
 

@@ -27,6 +27,7 @@ namespace {
 
 bool supported_d(int d) { return d == 64 || d == 128; }
 bool supported_bits(int b) { return b == 3 || b == 4; }
+bool codec_bits(int b) { return b >= 2 && b <= 4; }
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 int check_step_shape(const char* fn, int B, int Hq, int Hkv, int d, int n_l1, int n_groups,
@@ -53,11 +54,11 @@ extern "C" int hsq_encode(const void* x, int x_dtype, int64_t n_vec, int d, int 
   if (n_vec < 0 || group_n < 1 || vecs_per_rot < 1 || n_rot < 1)
     return fail(HSQ_ERR_ARG, "hsq_encode: bad sizes");
   if (!supported_d(d)) return fail(HSQ_ERR_UNSUPPORTED, "hsq_encode: d must be 64 or 128");
-  if (!supported_bits(bits)) return fail(HSQ_ERR_UNSUPPORTED, "hsq_encode: bits must be 3 or 4");
+  if (!codec_bits(bits)) return fail(HSQ_ERR_UNSUPPORTED, "hsq_encode: bits must be 2, 3 or 4");
   if (x_dtype != HSQ_F32 && x_dtype != HSQ_BF16)
     return fail(HSQ_ERR_UNSUPPORTED, "hsq_encode: x_dtype must be HSQ_F32 or HSQ_BF16");
   if (n_vec == 0) return HSQ_OK;
-  if (!x || !signs || !thresholds || !codes || !norms)
+  if (!x || !thresholds || !codes || !norms)  // signs may be null: rotation off
     return fail(HSQ_ERR_ARG, "hsq_encode: null pointer");
   EncodeJob j{};
   j.x = x; j.dtype = x_dtype; j.n_vec = n_vec; j.d = d; j.bits = bits; j.group_n = group_n;
@@ -73,11 +74,11 @@ extern "C" int hsq_decode(const uint8_t* codes, const float* norms, int64_t n_ve
                           const float* centroids, void* out, int out_dtype, void* stream) {
   if (n_vec < 0 || vecs_per_rot < 1 || n_rot < 1) return fail(HSQ_ERR_ARG, "hsq_decode: bad sizes");
   if (!supported_d(d)) return fail(HSQ_ERR_UNSUPPORTED, "hsq_decode: d must be 64 or 128");
-  if (!supported_bits(bits)) return fail(HSQ_ERR_UNSUPPORTED, "hsq_decode: bits must be 3 or 4");
+  if (!codec_bits(bits)) return fail(HSQ_ERR_UNSUPPORTED, "hsq_decode: bits must be 2, 3 or 4");
   if (out_dtype != HSQ_F32 && out_dtype != HSQ_BF16)
     return fail(HSQ_ERR_UNSUPPORTED, "hsq_decode: out_dtype must be HSQ_F32 or HSQ_BF16");
   if (n_vec == 0) return HSQ_OK;
-  if (!codes || !norms || !signs || !centroids || !out)
+  if (!codes || !norms || !centroids || !out)  // signs may be null: rotation off
     return fail(HSQ_ERR_ARG, "hsq_decode: null pointer");
   DecodeJob j{codes, norms, n_vec, d, bits, signs, vecs_per_rot, n_rot, centroids, out, out_dtype};
   return check_hip(launch_decode(j, as_stream(stream)), "hsq_decode launch");

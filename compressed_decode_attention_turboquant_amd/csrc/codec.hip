@@ -14,6 +14,11 @@
 // 2^(b-1)-1 positive thresholds are compared, against |y| as integer bit
 // patterns (for non-negative floats the bit order is the numeric order), with
 // a +1 on the key for y <= 0 to turn "t < y" into "t <= |y|".
+//
+// Variants [Ablation ..., "Key contributions" item 1 and "Results and
+// recommendations"]: ROT = false is Plain-KV, the same steps with the
+// rotation off (y = x / r); BITS = 2 packs four codes per byte in the same
+// LSB-first order as the 3-bit stream.
 #include "hsq_device.h"
 #include "hsq_internal.h"
 
@@ -51,7 +56,7 @@ __device__ __forceinline__ void load8(const void* x, int64_t off, float (&v)[8])
   }
 }
 
-template <int D, int BITS, int DT>
+template <int D, int BITS, int DT, bool ROT>
 __global__ __launch_bounds__(kWG) void encode_kernel(EncodeJob j) {
   constexpr int LPV = D / 8;
   constexpr int VPB = kWG / LPV;
@@ -82,17 +87,20 @@ __global__ __launch_bounds__(kWG) void encode_kernel(EncodeJob j) {
 #pragma unroll
   for (int m = 1; m < LPV; m <<= 1) ss += __shfl_xor(ss, m, 64);
   const float r = sqrtf(ss);
-  const float inv = r > 0.f ? 1.0f / (r * sqrtf((float)D)) : 0.f;
+  // the unnormalised transform scales by sqrt(d)
+  const float inv = r > 0.f ? 1.0f / (ROT ? r * sqrtf((float)D) : r) : 0.f;
 
-  uint32_t sbyte = 0;
-  if (valid) {
-    const int64_t rot = (i / j.vecs_per_rot) % j.n_rot;
-    sbyte = (j.signs[rot * (D / 32) + sub / 4] >> (8 * (sub % 4))) & 0xffu;
-  }
+  if constexpr (ROT) {
+    uint32_t sbyte = 0;
+    if (valid) {
+      const int64_t rot = (i / j.vecs_per_rot) % j.n_rot;
+      sbyte = (j.signs[rot * (D / 32) + sub / 4] >> (8 * (sub % 4))) & 0xffu;
+    }
 #pragma unroll
-  for (int a = 0; a < 8; ++a) v[a] = __uint_as_float(__float_as_uint(v[a]) ^ (((sbyte >> a) & 1u) << 31));
-
-  fwht8xlanes<LPV>(v, sub);
+    for (int a = 0; a < 8; ++a)
+      v[a] = __uint_as_float(__float_as_uint(v[a]) ^ (((sbyte >> a) & 1u) << 31));
+    fwht8xlanes<LPV>(v, sub);
+  }
 
   uint32_t packed = 0;
 #pragma unroll
@@ -113,6 +121,10 @@ __global__ __launch_bounds__(kWG) void encode_kernel(EncodeJob j) {
   uint8_t* crow = j.codes + rec * j.code_rec_bytes + slot * CB;
   if constexpr (BITS == 4) {
     if (valid) reinterpret_cast<uint32_t*>(crow)[sub] = packed;
+  } else if constexpr (BITS == 2) {
+    // 16 bits per lane; pairs of lanes write one dword
+    const uint32_t nxt = __shfl_down(packed, 1, 64);
+    if (valid && !(sub & 1)) reinterpret_cast<uint32_t*>(crow)[sub >> 1] = packed | (nxt << 16);
   } else {
     // 24 bits per lane; quads of lanes write three whole dwords.
     const uint32_t nxt = __shfl_down(packed, 1, 64);
@@ -123,7 +135,7 @@ __global__ __launch_bounds__(kWG) void encode_kernel(EncodeJob j) {
   if (valid && sub == 0) j.norms[rec * j.norm_rec_floats + slot] = r / (float)j.group_n;
 }
 
-template <int D, int BITS, int OUT>
+template <int D, int BITS, int OUT, bool ROT>
 __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j) {
   constexpr int LPV = D / 8;
   constexpr int VPB = kWG / LPV;
@@ -141,6 +153,8 @@ __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j) {
     const uint32_t* row = reinterpret_cast<const uint32_t*>(j.codes + i * CB);
     if constexpr (BITS == 4) {
       codes = row[sub];
+    } else if constexpr (BITS == 2) {
+      codes = (row[sub >> 1] >> (16 * (sub & 1))) & 0xffffu;
     } else {
       const int bit = 24 * sub;
       const uint32_t w0 = row[bit >> 5];
@@ -150,14 +164,16 @@ __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j) {
       codes &= 0xffffffu;
     }
     r = j.norms[i];
-    const int64_t rot = (i / j.vecs_per_rot) % j.n_rot;
-    sbyte = (j.signs[rot * (D / 32) + sub / 4] >> (8 * (sub % 4))) & 0xffu;
+    if constexpr (ROT) {
+      const int64_t rot = (i / j.vecs_per_rot) % j.n_rot;
+      sbyte = (j.signs[rot * (D / 32) + sub / 4] >> (8 * (sub % 4))) & 0xffu;
+    }
   }
   float v[8];
 #pragma unroll
   for (int a = 0; a < 8; ++a) v[a] = cent[(codes >> (BITS * a)) & ((1u << BITS) - 1)];
-  fwht8xlanes<LPV>(v, sub);
-  const float s = r / sqrtf((float)D);
+  if constexpr (ROT) fwht8xlanes<LPV>(v, sub);
+  const float s = ROT ? r / sqrtf((float)D) : r;
 #pragma unroll
   for (int a = 0; a < 8; ++a)
     v[a] = __uint_as_float(__float_as_uint(v[a] * s) ^ (((sbyte >> a) & 1u) << 31));
@@ -180,40 +196,57 @@ __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j) {
   }
 }
 
-template <int D, int BITS>
+template <int D, int BITS, bool ROT>
 hipError_t encode_dt(const EncodeJob& j, hipStream_t s) {
   constexpr int VPB = kWG / (D / 8);
   const int64_t grid = (j.n_vec + VPB - 1) / VPB;
   if (j.dtype == HSQ_F32)
-    hipLaunchKernelGGL((encode_kernel<D, BITS, HSQ_F32>), dim3((unsigned)grid), dim3(kWG), 0, s, j);
+    hipLaunchKernelGGL((encode_kernel<D, BITS, HSQ_F32, ROT>), dim3((unsigned)grid), dim3(kWG), 0, s, j);
   else
-    hipLaunchKernelGGL((encode_kernel<D, BITS, HSQ_BF16>), dim3((unsigned)grid), dim3(kWG), 0, s, j);
+    hipLaunchKernelGGL((encode_kernel<D, BITS, HSQ_BF16, ROT>), dim3((unsigned)grid), dim3(kWG), 0, s, j);
   return hipGetLastError();
 }
 
-template <int D, int BITS>
+template <int D, int BITS, bool ROT>
 hipError_t decode_dt(const DecodeJob& j, hipStream_t s) {
   constexpr int VPB = kWG / (D / 8);
   const int64_t grid = (j.n_vec + VPB - 1) / VPB;
   if (j.out_dtype == HSQ_F32)
-    hipLaunchKernelGGL((decode_kernel<D, BITS, HSQ_F32>), dim3((unsigned)grid), dim3(kWG), 0, s, j);
+    hipLaunchKernelGGL((decode_kernel<D, BITS, HSQ_F32, ROT>), dim3((unsigned)grid), dim3(kWG), 0, s, j);
   else
-    hipLaunchKernelGGL((decode_kernel<D, BITS, HSQ_BF16>), dim3((unsigned)grid), dim3(kWG), 0, s, j);
+    hipLaunchKernelGGL((decode_kernel<D, BITS, HSQ_BF16, ROT>), dim3((unsigned)grid), dim3(kWG), 0, s, j);
   return hipGetLastError();
+}
+
+template <int D, bool ROT>
+hipError_t encode_bits(const EncodeJob& j, hipStream_t s) {
+  if (j.bits == 4) return encode_dt<D, 4, ROT>(j, s);
+  if (j.bits == 3) return encode_dt<D, 3, ROT>(j, s);
+  return encode_dt<D, 2, ROT>(j, s);
+}
+
+template <int D, bool ROT>
+hipError_t decode_bits(const DecodeJob& j, hipStream_t s) {
+  if (j.bits == 4) return decode_dt<D, 4, ROT>(j, s);
+  if (j.bits == 3) return decode_dt<D, 3, ROT>(j, s);
+  return decode_dt<D, 2, ROT>(j, s);
 }
 
 }  // namespace
 
+// signs == nullptr selects the rotation-off variant
 hipError_t launch_encode(const EncodeJob& j, hipStream_t s) {
   if (j.n_vec <= 0) return hipSuccess;
-  if (j.d == 128) return j.bits == 4 ? encode_dt<128, 4>(j, s) : encode_dt<128, 3>(j, s);
-  return j.bits == 4 ? encode_dt<64, 4>(j, s) : encode_dt<64, 3>(j, s);
+  const bool rot = j.signs != nullptr;
+  if (j.d == 128) return rot ? encode_bits<128, true>(j, s) : encode_bits<128, false>(j, s);
+  return rot ? encode_bits<64, true>(j, s) : encode_bits<64, false>(j, s);
 }
 
 hipError_t launch_decode(const DecodeJob& j, hipStream_t s) {
   if (j.n_vec <= 0) return hipSuccess;
-  if (j.d == 128) return j.bits == 4 ? decode_dt<128, 4>(j, s) : decode_dt<128, 3>(j, s);
-  return j.bits == 4 ? decode_dt<64, 4>(j, s) : decode_dt<64, 3>(j, s);
+  const bool rot = j.signs != nullptr;
+  if (j.d == 128) return rot ? decode_bits<128, true>(j, s) : decode_bits<128, false>(j, s);
+  return rot ? decode_bits<64, true>(j, s) : decode_bits<64, false>(j, s);
 }
 
 }  // namespace hsq

@@ -122,18 +122,25 @@ size_t hsq_workspace_bytes(int B, int Hq, int Hkv, int d, int n_l1, int n_groups
 /*
  * hsq_encode -- TurboQuant encode of n_vec vectors [HSQ quantisation item;
  * ABL "Experimental setup"]: norm, sign flip, Walsh-Hadamard transform,
- * threshold count, bit packing.
+ * threshold count, bit packing.  Variants [ABL "Key contributions" item 1,
+ * "Results and recommendations"]: signs == NULL is Plain-KV (rotation off:
+ * the unit vector x / r is quantised as it is); bits == 2 is the 2-bit budget.
  *   x           [rows][d] in x_dtype (HSQ_F32 or HSQ_BF16)
  *   row_idx     NULL: vector i reads rows [i*group_n, (i+1)*group_n);
  *               else int64 [n_vec*group_n] row numbers
  *   group_n     1 = encode each row; N > 1 = encode the mean of N rows
  *   signs       uint32 [n_rot][d/32]; vector i uses mask
- *               (i / vecs_per_rot) % n_rot
+ *               (i / vecs_per_rot) % n_rot; NULL = no rotation
+ *               (vecs_per_rot and n_rot are then not used, but must be >= 1)
+ *   bits        2, 3 or 4
  *   thresholds  fp32 [2^bits - 1] ascending (device)
- *   codes       out [n_vec][bits*d/8]
+ *   codes       out [n_vec][bits*d/8]: 4-bit, byte k = code[2k] |
+ *               code[2k+1] << 4; 2- and 3-bit, an LSB-first bit stream
+ *               with code i in bits [bits*i, bits*i + bits)
  *   norms       out [n_vec] fp32
- * Errors: HSQ_ERR_ARG (null, n_vec < 0, vecs_per_rot < 1, n_rot < 1,
- * group_n < 1), HSQ_ERR_UNSUPPORTED (d, bits, dtype), HSQ_ERR_HIP.
+ * Errors: HSQ_ERR_ARG (null x, thresholds, codes or norms, n_vec < 0,
+ * vecs_per_rot < 1, n_rot < 1, group_n < 1), HSQ_ERR_UNSUPPORTED (d, bits,
+ * dtype), HSQ_ERR_HIP.
  * n_vec == 0 is a no-op.
  */
 int hsq_encode(const void* x, int x_dtype, int64_t n_vec, int d, int bits,
@@ -145,6 +152,7 @@ int hsq_encode(const void* x, int x_dtype, int64_t n_vec, int d, int bits,
  * hsq_decode -- dequantise n_vec vectors: x_hat = r R^T c[code]
  * [HSQ "Decode process" step 2: dequantise and rotate back].
  *   codes/norms as written by hsq_encode; centroids fp32 [2^bits] (device);
+ *   signs as for hsq_encode (NULL: R = I, x_hat = r c[code]);
  *   out [n_vec][d] in out_dtype (HSQ_F32 or HSQ_BF16).
  * Errors as hsq_encode.
  */

@@ -74,7 +74,13 @@ def test_argument_errors_are_reported_without_launch():
     # encode: unsupported d / bits / dtype, null pointers, bad sizes
     p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
     assert lib.hsq_encode(p, 0, 10, 96, 4, None, 1, p, 1, 1, p, p, p, None) == -2
-    assert lib.hsq_encode(p, 0, 10, 128, 2, None, 1, p, 1, 1, p, p, p, None) == -2
+    assert lib.hsq_encode(p, 0, 10, 128, 1, None, 1, p, 1, 1, p, p, p, None) == -2
+    assert lib.hsq_encode(p, 0, 10, 128, 5, None, 1, p, 1, 1, p, p, p, None) == -2
+    assert lib.hsq_decode(p, p, 10, 128, 1, None, 1, 1, p, p, 0, None) == -2
+    assert lib.hsq_decode(p, p, 10, 128, 5, None, 1, 1, p, p, 0, None) == -2
+    # signs may be null (rotation off); the other pointers may not
+    assert lib.hsq_encode(p, 0, 10, 128, 2, None, 1, None, 1, 1, None, p, p, None) == -1
+    assert lib.hsq_decode(p, p, 10, 128, 2, None, 1, 1, None, p, 0, None) == -1
     assert lib.hsq_encode(p, 7, 10, 128, 4, None, 1, p, 1, 1, p, p, p, None) == -2
     assert lib.hsq_encode(None, 0, 10, 128, 4, None, 1, p, 1, 1, p, p, p, None) == -1
     assert lib.hsq_encode(p, 0, -1, 128, 4, None, 1, p, 1, 1, p, p, p, None) == -1
