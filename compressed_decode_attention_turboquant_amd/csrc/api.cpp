@@ -57,6 +57,8 @@ extern "C" int hsq_encode(const void* x, int x_dtype, int64_t n_vec, int d, int 
   if (!codec_bits(bits)) return fail(HSQ_ERR_UNSUPPORTED, "hsq_encode: bits must be 2, 3 or 4");
   if (x_dtype != HSQ_F32 && x_dtype != HSQ_BF16)
     return fail(HSQ_ERR_UNSUPPORTED, "hsq_encode: x_dtype must be HSQ_F32 or HSQ_BF16");
+  if (n_vec > (int64_t)UINT32_MAX)
+    return fail(HSQ_ERR_UNSUPPORTED, "hsq_encode: at most 2^32 - 1 vectors per call");
   if (n_vec == 0) return HSQ_OK;
   if (!x || !thresholds || !codes || !norms)  // signs may be null: rotation off
     return fail(HSQ_ERR_ARG, "hsq_encode: null pointer");
@@ -77,6 +79,8 @@ extern "C" int hsq_decode(const uint8_t* codes, const float* norms, int64_t n_ve
   if (!codec_bits(bits)) return fail(HSQ_ERR_UNSUPPORTED, "hsq_decode: bits must be 2, 3 or 4");
   if (out_dtype != HSQ_F32 && out_dtype != HSQ_BF16)
     return fail(HSQ_ERR_UNSUPPORTED, "hsq_decode: out_dtype must be HSQ_F32 or HSQ_BF16");
+  if (n_vec > (int64_t)UINT32_MAX)
+    return fail(HSQ_ERR_UNSUPPORTED, "hsq_decode: at most 2^32 - 1 vectors per call");
   if (n_vec == 0) return HSQ_OK;
   if (!codes || !norms || !centroids || !out)  // signs may be null: rotation off
     return fail(HSQ_ERR_ARG, "hsq_decode: null pointer");
@@ -93,6 +97,8 @@ extern "C" int hsq_build_tiers(const void* k, const void* v, int dtype, int B, i
                                uint8_t* l3, void* stream) {
   if (B < 1 || Hkv < 1 || T < 1 || n1 < 0 || n_groups < 0 || group_n < 1)
     return fail(HSQ_ERR_ARG, "hsq_build_tiers: bad sizes");
+  if ((int64_t)B * Hkv * T > (int64_t)UINT32_MAX)
+    return fail(HSQ_ERR_UNSUPPORTED, "hsq_build_tiers: at most 2^32 - 1 rows (B * Hkv * T)");
   if ((int64_t)n1 + (int64_t)n_groups * group_n > T)
     return fail(HSQ_ERR_ARG, "hsq_build_tiers: n1 + n_groups * group_n exceeds T");
   if (!supported_d(d)) return fail(HSQ_ERR_UNSUPPORTED, "hsq_build_tiers: d must be 64 or 128");

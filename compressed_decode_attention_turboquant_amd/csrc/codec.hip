@@ -27,15 +27,52 @@ namespace {
 
 constexpr int kWG = 256;
 
-__device__ __forceinline__ int64_t row_of(const EncodeJob& j, int64_t i, int k) {
-  if (j.row_idx) return j.row_idx[i * j.group_n + k];
+// Division of a 32-bit index by a divisor fixed for the launch, with one
+// multiply-high, a subtract, an add and two shifts (Granlund and Montgomery,
+// "Division by invariant integers using multiplication", PLDI 1994, section 4:
+// with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1, the quotient
+// of every n < 2^32 is (t + ((n - t) >> min(l, 1))) >> max(l - 1, 0), t the
+// high word of m n).  Vector indices stay below 2^32 (the entry points
+// reject larger counts), so the kernels never divide 64-bit integers.
+struct Div32 {
+  uint32_t d, m, s1, s2;
+};
+
+Div32 make_div32(int64_t div) {
+  // a divisor the job does not use may be 0; one of 2^32 or more divides
+  // every index to 0, as UINT32_MAX does
+  const uint32_t d = div < 1 ? 1u : (uint32_t)(div > (int64_t)UINT32_MAX ? UINT32_MAX : div);
+  uint32_t l = 0;
+  while (l < 32 && (1ull << l) < d) ++l;
+  const uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+  return Div32{d, (uint32_t)m, l < 1 ? l : 1u, l > 1 ? l - 1 : 0u};
+}
+
+__device__ __forceinline__ uint32_t udiv(uint32_t n, const Div32& q) {
+  const uint32_t t = __umulhi(q.m, n);
+  return (t + ((n - t) >> q.s1)) >> q.s2;
+}
+
+// vector i -> rotation mask (i / vecs_per_rot) % n_rot
+__device__ __forceinline__ uint32_t rot_of(uint32_t i, const Div32& per_rot, const Div32& n_rot) {
+  const uint32_t q = udiv(i, per_rot);
+  return q - udiv(q, n_rot) * n_rot.d;
+}
+
+struct EncodeDivs {
+  Div32 unit, seq, rot, nrot, rec;
+};
+
+__device__ __forceinline__ int64_t row_of(const EncodeJob& j, const EncodeDivs& q, uint32_t i,
+                                          int k) {
+  if (j.row_idx) return j.row_idx[(int64_t)i * j.group_n + k];
   if (j.pos) {
-    const int64_t u = i / j.vecs_per_unit;
-    const int64_t jj = i - u * j.vecs_per_unit;
-    const int64_t b = u / j.units_per_seq;
-    return u * j.rows_per_unit + j.pos[b * j.pos_per_seq + jj * j.group_n + k];
+    const uint32_t u = udiv(i, q.unit);
+    const uint32_t jj = i - u * q.unit.d;
+    const uint32_t b = udiv(u, q.seq);
+    return (int64_t)u * j.rows_per_unit + j.pos[(int64_t)b * j.pos_per_seq + (int64_t)jj * j.group_n + k];
   }
-  return i * j.group_n + k;
+  return (int64_t)i * j.group_n + k;
 }
 
 template <int DT>
@@ -57,28 +94,37 @@ __device__ __forceinline__ void load8(const void* x, int64_t off, float (&v)[8])
 }
 
 template <int D, int BITS, int DT, bool ROT>
-__global__ __launch_bounds__(kWG) void encode_kernel(EncodeJob j) {
+__global__ __launch_bounds__(kWG) void encode_kernel(EncodeJob j, EncodeDivs q) {
   constexpr int LPV = D / 8;
   constexpr int VPB = kWG / LPV;
   constexpr int L = 1 << BITS;
   constexpr int NPOS = L / 2 - 1;  // positive thresholds t[L/2 .. L-2]
   const int sub = threadIdx.x % LPV;
-  const int64_t i = (int64_t)blockIdx.x * VPB + threadIdx.x / LPV;
+  const uint32_t i = blockIdx.x * VPB + threadIdx.x / LPV;
   const bool valid = i < j.n_vec;
 
   uint32_t tpos[NPOS];
 #pragma unroll
   for (int h = 0; h < NPOS; ++h) tpos[h] = __float_as_uint(j.thr[L / 2 + h]);
 
+  // the sign word goes out with the data loads (no second round trip)
+  uint32_t sword = 0;
+  if constexpr (ROT)
+    if (valid) sword = j.signs[rot_of(i, q.rot, q.nrot) * (D / 32) + sub / 4];
+
   float v[8];
 #pragma unroll
   for (int a = 0; a < 8; ++a) v[a] = 0.f;
   if (valid) {
-    for (int k = 0; k < j.group_n; ++k) {
-      float t[8];
-      load8<DT>(j.x, row_of(j, i, k) * D + 8 * sub, t);
+    if (j.group_n == 1 && !j.row_idx && !j.pos) {  // one row, contiguous: a single load
+      load8<DT>(j.x, (int64_t)i * D + 8 * sub, v);
+    } else {
+      for (int k = 0; k < j.group_n; ++k) {
+        float t[8];
+        load8<DT>(j.x, row_of(j, q, i, k) * D + 8 * sub, t);
 #pragma unroll
-      for (int a = 0; a < 8; ++a) v[a] += t[a];
+        for (int a = 0; a < 8; ++a) v[a] += t[a];
+      }
     }
   }
   float ss = 0.f;
@@ -91,11 +137,7 @@ __global__ __launch_bounds__(kWG) void encode_kernel(EncodeJob j) {
   const float inv = r > 0.f ? 1.0f / (ROT ? r * sqrtf((float)D) : r) : 0.f;
 
   if constexpr (ROT) {
-    uint32_t sbyte = 0;
-    if (valid) {
-      const int64_t rot = (i / j.vecs_per_rot) % j.n_rot;
-      sbyte = (j.signs[rot * (D / 32) + sub / 4] >> (8 * (sub % 4))) & 0xffu;
-    }
+    const uint32_t sbyte = (sword >> (8 * (sub % 4))) & 0xffu;
 #pragma unroll
     for (int a = 0; a < 8; ++a)
       v[a] = __uint_as_float(__float_as_uint(v[a]) ^ (((sbyte >> a) & 1u) << 31));
@@ -115,10 +157,10 @@ __global__ __launch_bounds__(kWG) void encode_kernel(EncodeJob j) {
     packed |= code << (BITS * a);
   }
 
-  const int64_t rec = valid ? i / j.vecs_per_rec : 0;
-  const int64_t slot = i - rec * j.vecs_per_rec;
+  const uint32_t rec = valid ? udiv(i, q.rec) : 0u;
+  const uint32_t slot = i - rec * q.rec.d;
   constexpr int CB = D * BITS / 8;
-  uint8_t* crow = j.codes + rec * j.code_rec_bytes + slot * CB;
+  uint8_t* crow = j.codes + (int64_t)rec * j.code_rec_bytes + (int64_t)slot * CB;
   if constexpr (BITS == 4) {
     if (valid) reinterpret_cast<uint32_t*>(crow)[sub] = packed;
   } else if constexpr (BITS == 2) {
@@ -132,11 +174,11 @@ __global__ __launch_bounds__(kWG) void encode_kernel(EncodeJob j) {
     if (valid && qd < 3)
       reinterpret_cast<uint32_t*>(crow)[3 * (sub >> 2) + qd] = (packed >> (8 * qd)) | (nxt << (24 - 8 * qd));
   }
-  if (valid && sub == 0) j.norms[rec * j.norm_rec_floats + slot] = r / (float)j.group_n;
+  if (valid && sub == 0) j.norms[(int64_t)rec * j.norm_rec_floats + slot] = r / (float)j.group_n;
 }
 
 template <int D, int BITS, int OUT, bool ROT>
-__global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j) {
+__global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j, Div32 per_rot, Div32 n_rot) {
   constexpr int LPV = D / 8;
   constexpr int VPB = kWG / LPV;
   constexpr int CB = D * BITS / 8;
@@ -144,13 +186,13 @@ __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j) {
   if (threadIdx.x < (1 << BITS)) cent[threadIdx.x] = j.centroids[threadIdx.x];
   __syncthreads();
   const int sub = threadIdx.x % LPV;
-  const int64_t i = (int64_t)blockIdx.x * VPB + threadIdx.x / LPV;
+  const uint32_t i = blockIdx.x * VPB + threadIdx.x / LPV;
   const bool valid = i < j.n_vec;
   uint32_t codes = 0;
   float r = 0.f;
   uint32_t sbyte = 0;
   if (valid) {
-    const uint32_t* row = reinterpret_cast<const uint32_t*>(j.codes + i * CB);
+    const uint32_t* row = reinterpret_cast<const uint32_t*>(j.codes + (int64_t)i * CB);
     if constexpr (BITS == 4) {
       codes = row[sub];
     } else if constexpr (BITS == 2) {
@@ -164,10 +206,8 @@ __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j) {
       codes &= 0xffffffu;
     }
     r = j.norms[i];
-    if constexpr (ROT) {
-      const int64_t rot = (i / j.vecs_per_rot) % j.n_rot;
-      sbyte = (j.signs[rot * (D / 32) + sub / 4] >> (8 * (sub % 4))) & 0xffu;
-    }
+    if constexpr (ROT)
+      sbyte = (j.signs[rot_of(i, per_rot, n_rot) * (D / 32) + sub / 4] >> (8 * (sub % 4))) & 0xffu;
   }
   float v[8];
 #pragma unroll
@@ -179,7 +219,7 @@ __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j) {
     v[a] = __uint_as_float(__float_as_uint(v[a] * s) ^ (((sbyte >> a) & 1u) << 31));
   if (!valid) return;
   if constexpr (OUT == HSQ_F32) {
-    float4* o = reinterpret_cast<float4*>(static_cast<float*>(j.out) + i * D + 8 * sub);
+    float4* o = reinterpret_cast<float4*>(static_cast<float*>(j.out) + (int64_t)i * D + 8 * sub);
     o[0] = make_float4(v[0], v[1], v[2], v[3]);
     o[1] = make_float4(v[4], v[5], v[6], v[7]);
   } else {
@@ -191,7 +231,7 @@ __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j) {
       hi = (hi + 0x7fffu + ((hi >> 16) & 1u)) & 0xffff0000u;
       w[k] = lo | hi;
     }
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(j.out) + i * D + 8 * sub) =
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(j.out) + (int64_t)i * D + 8 * sub) =
         make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
@@ -200,10 +240,12 @@ template <int D, int BITS, bool ROT>
 hipError_t encode_dt(const EncodeJob& j, hipStream_t s) {
   constexpr int VPB = kWG / (D / 8);
   const int64_t grid = (j.n_vec + VPB - 1) / VPB;
+  const EncodeDivs q{make_div32(j.vecs_per_unit), make_div32(j.units_per_seq),
+                     make_div32(j.vecs_per_rot), make_div32(j.n_rot), make_div32(j.vecs_per_rec)};
   if (j.dtype == HSQ_F32)
-    hipLaunchKernelGGL((encode_kernel<D, BITS, HSQ_F32, ROT>), dim3((unsigned)grid), dim3(kWG), 0, s, j);
+    hipLaunchKernelGGL((encode_kernel<D, BITS, HSQ_F32, ROT>), dim3((unsigned)grid), dim3(kWG), 0, s, j, q);
   else
-    hipLaunchKernelGGL((encode_kernel<D, BITS, HSQ_BF16, ROT>), dim3((unsigned)grid), dim3(kWG), 0, s, j);
+    hipLaunchKernelGGL((encode_kernel<D, BITS, HSQ_BF16, ROT>), dim3((unsigned)grid), dim3(kWG), 0, s, j, q);
   return hipGetLastError();
 }
 
@@ -211,10 +253,13 @@ template <int D, int BITS, bool ROT>
 hipError_t decode_dt(const DecodeJob& j, hipStream_t s) {
   constexpr int VPB = kWG / (D / 8);
   const int64_t grid = (j.n_vec + VPB - 1) / VPB;
+  const Div32 per_rot = make_div32(j.vecs_per_rot), n_rot = make_div32(j.n_rot);
   if (j.out_dtype == HSQ_F32)
-    hipLaunchKernelGGL((decode_kernel<D, BITS, HSQ_F32, ROT>), dim3((unsigned)grid), dim3(kWG), 0, s, j);
+    hipLaunchKernelGGL((decode_kernel<D, BITS, HSQ_F32, ROT>), dim3((unsigned)grid), dim3(kWG), 0, s, j,
+                       per_rot, n_rot);
   else
-    hipLaunchKernelGGL((decode_kernel<D, BITS, HSQ_BF16, ROT>), dim3((unsigned)grid), dim3(kWG), 0, s, j);
+    hipLaunchKernelGGL((decode_kernel<D, BITS, HSQ_BF16, ROT>), dim3((unsigned)grid), dim3(kWG), 0, s, j,
+                       per_rot, n_rot);
   return hipGetLastError();
 }
 
@@ -237,6 +282,7 @@ hipError_t decode_bits(const DecodeJob& j, hipStream_t s) {
 // signs == nullptr selects the rotation-off variant
 hipError_t launch_encode(const EncodeJob& j, hipStream_t s) {
   if (j.n_vec <= 0) return hipSuccess;
+  if (j.n_vec > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
   const bool rot = j.signs != nullptr;
   if (j.d == 128) return rot ? encode_bits<128, true>(j, s) : encode_bits<128, false>(j, s);
   return rot ? encode_bits<64, true>(j, s) : encode_bits<64, false>(j, s);
@@ -244,6 +290,7 @@ hipError_t launch_encode(const EncodeJob& j, hipStream_t s) {
 
 hipError_t launch_decode(const DecodeJob& j, hipStream_t s) {
   if (j.n_vec <= 0) return hipSuccess;
+  if (j.n_vec > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
   const bool rot = j.signs != nullptr;
   if (j.d == 128) return rot ? decode_bits<128, true>(j, s) : decode_bits<128, false>(j, s);
   return rot ? decode_bits<64, true>(j, s) : decode_bits<64, false>(j, s);

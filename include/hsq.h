@@ -140,7 +140,7 @@ size_t hsq_workspace_bytes(int B, int Hq, int Hkv, int d, int n_l1, int n_groups
  *   norms       out [n_vec] fp32
  * Errors: HSQ_ERR_ARG (null x, thresholds, codes or norms, n_vec < 0,
  * vecs_per_rot < 1, n_rot < 1, group_n < 1), HSQ_ERR_UNSUPPORTED (d, bits,
- * dtype), HSQ_ERR_HIP.
+ * dtype, n_vec >= 2^32), HSQ_ERR_HIP.
  * n_vec == 0 is a no-op.
  */
 int hsq_encode(const void* x, int x_dtype, int64_t n_vec, int d, int bits,
@@ -171,6 +171,8 @@ int hsq_decode(const uint8_t* codes, const float* norms, int64_t n_vec, int d, i
  *   thr4, thr3  fp32 thresholds for 4 and 3 bits (device)
  *   outputs     tier arrays in the layouts above
  * n1 == 0 or n_groups == 0 skip the matching tiers.
+ * Errors: HSQ_ERR_ARG (null pointers, bad sizes, n1 + n_groups*group_n > T),
+ * HSQ_ERR_UNSUPPORTED (d, dtype, B*Hkv*T >= 2^32), HSQ_ERR_HIP.
  */
 int hsq_build_tiers(const void* k, const void* v, int dtype, int B, int Hkv, int T, int d,
                     const int32_t* l1_pos, int n1, const int32_t* group_pos, int n_groups,

@@ -78,6 +78,11 @@ def test_argument_errors_are_reported_without_launch():
     assert lib.hsq_encode(p, 0, 10, 128, 5, None, 1, p, 1, 1, p, p, p, None) == -2
     assert lib.hsq_decode(p, p, 10, 128, 1, None, 1, 1, p, p, 0, None) == -2
     assert lib.hsq_decode(p, p, 10, 128, 5, None, 1, 1, p, p, 0, None) == -2
+    # vector counts of 2^32 and more are refused before any launch
+    assert lib.hsq_encode(p, 0, 1 << 32, 128, 4, None, 1, p, 1, 1, p, p, p, None) == -2
+    assert lib.hsq_decode(p, p, 1 << 32, 128, 4, p, 1, 1, p, p, 0, None) == -2
+    assert lib.hsq_build_tiers(p, p, 0, 1 << 16, 1 << 8, 1 << 8, 128, p, 16, p, 4, 8, p, p, p, p,
+                               p, p, p, p, p, p, p, p, p, None) == -2
     # signs may be null (rotation off); the other pointers may not
     assert lib.hsq_encode(p, 0, 10, 128, 2, None, 1, None, 1, 1, None, p, p, None) == -1
     assert lib.hsq_decode(p, p, 10, 128, 2, None, 1, 1, None, p, 0, None) == -1

@@ -98,3 +98,33 @@ def test_plain_round_trip_on_codec_workload_shape(bits):
     g_rel = np.sum((xh.cpu().double().numpy() - xf) ** 2) / np.sum(xf * xf)
     o_rel = np.sum((ox - xf) ** 2) / np.sum(xf * xf)
     assert abs(g_rel - o_rel) <= 1e-4 * o_rel
+
+
+@pytest.mark.parametrize("vpr,n_rot", [(1, 7), (2, 3), (64, 5), (999, 2), (4999, 3), (5000, 1),
+                                       (1 << 20, 4)])
+def test_rotation_index_for_many_divisors(vpr, n_rot):
+    # vector i uses mask (i / vecs_per_rot) % n_rot, for divisors of every
+    # kind (1, powers of two, odd, near the count, beyond it), in encode and
+    # in decode
+    d, bits, n = 64, 4, 5000
+    print(f"rotation index vpr={vpr} n_rot={n_rot}", flush=True)
+    rng = np.random.default_rng(vpr * 31 + n_rot)
+    signs = rng.integers(0, 1 << 32, size=(n_rot, d // 32), dtype=np.uint64).astype(np.uint32)
+    x = _inputs(n, d, "f32", seed=vpr + n_rot)
+    c32, t32 = ocb.codebook_f32(d, bits)
+    codes, norms = hsq.encode(x.to(DEV), bits, signs_to_dev(signs), torch.from_numpy(t32).to(DEV),
+                              vecs_per_rot=vpr, n_rot=n_rot)
+    xh = hsq.decode(codes, norms, bits, d, signs_to_dev(signs), torch.from_numpy(c32).to(DEV),
+                    vecs_per_rot=vpr, n_rot=n_rot)
+    torch.cuda.synchronize()
+    rot = (np.arange(n) // vpr) % n_rot
+    gc, gn, gx = codes.cpu().numpy(), norms.cpu().numpy(), xh.cpu().double().numpy()
+    for r in range(n_rot):
+        sel = np.nonzero(rot == r)[0]
+        if sel.size == 0:
+            continue
+        oc, on, oy = codec.encode(x[sel], signs[r], t32)
+        compare_codes(gc[sel], oc, oy, t32, bits, d, f"rot {r}")
+        compare_norms(gn[sel], on, f"rot {r}")
+        od = codec.decode(codec.unpack(gc[sel], bits, d), gn[sel], signs[r], c32)
+        np.testing.assert_allclose(gx[sel], od, rtol=2e-6, atol=1e-6 * np.abs(od).max())
