@@ -26,6 +26,7 @@ namespace hsq {
 namespace {
 
 constexpr int kWG = 256;
+constexpr int kVPT = 2;  // vectors per thread in the encoder
 
 // Division of a 32-bit index by a divisor fixed for the launch, with one
 // multiply-high, a subtract, an add and two shifts (Granlund and Montgomery,
@@ -93,40 +94,17 @@ __device__ __forceinline__ void load8(const void* x, int64_t off, float (&v)[8])
   }
 }
 
-template <int D, int BITS, int DT, bool ROT>
-__global__ __launch_bounds__(kWG) void encode_kernel(EncodeJob j, EncodeDivs q) {
+// Norm, rotation, quantisation and packing of vector i, whose 8 coordinates
+// of this lane are in v (LPV lanes per vector).
+template <int D, int BITS, bool ROT, int kBins>
+__device__ __forceinline__ void encode_one(const EncodeJob& j, const EncodeDivs& q, uint32_t i,
+                                           int sub, float (&v)[8], uint32_t sword,
+                                           const uint32_t (&tpos)[(1 << BITS) / 2 - 1], bool binned,
+                                           const uint2* s_bin) {
   constexpr int LPV = D / 8;
-  constexpr int VPB = kWG / LPV;
   constexpr int L = 1 << BITS;
-  constexpr int NPOS = L / 2 - 1;  // positive thresholds t[L/2 .. L-2]
-  const int sub = threadIdx.x % LPV;
-  const uint32_t i = blockIdx.x * VPB + threadIdx.x / LPV;
+  constexpr int NPOS = L / 2 - 1;
   const bool valid = i < j.n_vec;
-
-  uint32_t tpos[NPOS];
-#pragma unroll
-  for (int h = 0; h < NPOS; ++h) tpos[h] = __float_as_uint(j.thr[L / 2 + h]);
-
-  // the sign word goes out with the data loads (no second round trip)
-  uint32_t sword = 0;
-  if constexpr (ROT)
-    if (valid) sword = j.signs[rot_of(i, q.rot, q.nrot) * (D / 32) + sub / 4];
-
-  float v[8];
-#pragma unroll
-  for (int a = 0; a < 8; ++a) v[a] = 0.f;
-  if (valid) {
-    if (j.group_n == 1 && !j.row_idx && !j.pos) {  // one row, contiguous: a single load
-      load8<DT>(j.x, (int64_t)i * D + 8 * sub, v);
-    } else {
-      for (int k = 0; k < j.group_n; ++k) {
-        float t[8];
-        load8<DT>(j.x, row_of(j, q, i, k) * D + 8 * sub, t);
-#pragma unroll
-        for (int a = 0; a < 8; ++a) v[a] += t[a];
-      }
-    }
-  }
   float ss = 0.f;
 #pragma unroll
   for (int a = 0; a < 8; ++a) ss = fmaf(v[a], v[a], ss);
@@ -145,16 +123,31 @@ __global__ __launch_bounds__(kWG) void encode_kernel(EncodeJob j, EncodeDivs q) 
   }
 
   uint32_t packed = 0;
+  if (binned) {  // work-group uniform
 #pragma unroll
-  for (int a = 0; a < 8; ++a) {
-    const float y = v[a] * inv;
-    const bool pos = y > 0.f;
-    const uint32_t key = (__float_as_uint(y) & 0x7fffffffu) + (pos ? 0u : 1u);
-    int cnt = 0;
+    for (int a = 0; a < 8; ++a) {
+      const float y = v[a] * inv;
+      const bool pos = y > 0.f;
+      const float ay = fabsf(y);
+      const uint32_t key = __float_as_uint(ay) + (pos ? 0u : 1u);
+      const uint32_t b = min((uint32_t)(ay * (float)kBins), (uint32_t)(kBins - 1));
+      const uint2 e = s_bin[b];
+      const uint32_t cnt = e.x + (e.y < key ? 1u : 0u);
+      const uint32_t code = pos ? (uint32_t)(L / 2) + cnt : (uint32_t)(L / 2 - 1) - cnt;
+      packed |= code << (BITS * a);
+    }
+  } else {
 #pragma unroll
-    for (int h = 0; h < NPOS; ++h) cnt += (tpos[h] < key) ? 1 : 0;
-    const uint32_t code = pos ? (uint32_t)(L / 2 + cnt) : (uint32_t)(L / 2 - 1 - cnt);
-    packed |= code << (BITS * a);
+    for (int a = 0; a < 8; ++a) {
+      const float y = v[a] * inv;
+      const bool pos = y > 0.f;
+      const uint32_t key = (__float_as_uint(y) & 0x7fffffffu) + (pos ? 0u : 1u);
+      int cnt = 0;
+#pragma unroll
+      for (int h = 0; h < NPOS; ++h) cnt += (tpos[h] < key) ? 1 : 0;
+      const uint32_t code = pos ? (uint32_t)(L / 2 + cnt) : (uint32_t)(L / 2 - 1 - cnt);
+      packed |= code << (BITS * a);
+    }
   }
 
   const uint32_t rec = valid ? udiv(i, q.rec) : 0u;
@@ -176,6 +169,89 @@ __global__ __launch_bounds__(kWG) void encode_kernel(EncodeJob j, EncodeDivs q) 
   }
   if (valid && sub == 0) j.norms[(int64_t)rec * j.norm_rec_floats + slot] = r / (float)j.group_n;
 }
+
+// CONTIG: one row per vector, row i (group_n == 1, no row_idx, no pos); the
+// loads are then straight-line, at indices clamped into the array, so that
+// no wait sits between them.
+template <int D, int BITS, int DT, bool ROT, bool CONTIG>
+__global__ __launch_bounds__(kWG) void encode_kernel(EncodeJob j, EncodeDivs q) {
+  constexpr int LPV = D / 8;
+  constexpr int VPB = kWG / LPV;  // vectors per pass of the work-group
+  constexpr int L = 1 << BITS;
+  constexpr int NPOS = L / 2 - 1;  // positive thresholds t[L/2 .. L-2]
+  const int sub = threadIdx.x % LPV;
+  const uint32_t i0 = blockIdx.x * (kVPT * VPB) + threadIdx.x / LPV;
+
+  // Global loads first: the thresholds, then every vector of this thread
+  // (i0 + u VPB) with its sign word, all in flight together.
+  uint32_t tpos[NPOS];
+#pragma unroll
+  for (int h = 0; h < NPOS; ++h) tpos[h] = __float_as_uint(j.thr[L / 2 + h]);
+  uint32_t sword[kVPT];
+  float v[kVPT][8];
+#pragma unroll
+  for (int u = 0; u < kVPT; ++u) {
+    const uint32_t i = i0 + u * VPB;
+    const bool valid = i < j.n_vec;
+    const uint32_t ic = valid ? i : (uint32_t)(j.n_vec - 1);  // past the end: reread the last
+    sword[u] = 0u;
+    if constexpr (ROT) sword[u] = j.signs[rot_of(ic, q.rot, q.nrot) * (D / 32) + sub / 4];
+    if constexpr (CONTIG) {
+      load8<DT>(j.x, (int64_t)ic * D + 8 * sub, v[u]);
+    } else {
+#pragma unroll
+      for (int a = 0; a < 8; ++a) v[u][a] = 0.f;
+      if (valid) {
+        for (int k = 0; k < j.group_n; ++k) {
+          float t[8];
+          load8<DT>(j.x, row_of(j, q, i, k) * D + 8 * sub, t);
+#pragma unroll
+          for (int a = 0; a < 8; ++a) v[u][a] += t[a];
+        }
+      }
+    }
+  }
+
+  // 4 bits: a table of kBins equal bins of |y| over [0, 1) (the last one open
+  // above) replaces the seven compares.  Bin b holds the number of positive
+  // thresholds below its start and the threshold inside it, if any; the count
+  // for a key in the bin is then that number plus one compare.  It is exact
+  // when no bin holds two thresholds (true for the Beta codebooks at d = 64
+  // and 128, whose closest thresholds are >= 0.022 apart); otherwise the
+  // work-group counts all seven.  Built while the loads above are in flight.
+  constexpr int kBins = 64;
+  __shared__ uint2 s_bin[kBins];
+  __shared__ int s_two_in_a_bin;
+  bool binned = false;
+  if constexpr (BITS == 4) {
+    if (threadIdx.x == 0) s_two_in_a_bin = 0;
+    lds_barrier();
+    if (threadIdx.x < kBins) {
+      const uint32_t lo = __float_as_uint((float)threadIdx.x * (1.f / kBins));
+      const uint32_t hi = threadIdx.x == kBins - 1 ? 0xffffffffu
+                                                   : __float_as_uint((float)(threadIdx.x + 1) * (1.f / kBins));
+      uint32_t below = 0, inside = 0xffffffffu;
+      int n_in = 0;
+#pragma unroll
+      for (int h = 0; h < NPOS; ++h) {
+        below += tpos[h] < lo ? 1u : 0u;
+        if (tpos[h] >= lo && tpos[h] < hi) {
+          inside = tpos[h];
+          ++n_in;
+        }
+      }
+      s_bin[threadIdx.x] = make_uint2(below, inside);
+      if (n_in > 1) s_two_in_a_bin = 1;
+    }
+    lds_barrier();
+    binned = s_two_in_a_bin == 0;
+  }
+
+#pragma unroll
+  for (int u = 0; u < kVPT; ++u)
+    encode_one<D, BITS, ROT, kBins>(j, q, i0 + u * VPB, sub, v[u], sword[u], tpos, binned, s_bin);
+}
+
 
 template <int D, int BITS, int OUT, bool ROT>
 __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j, Div32 per_rot, Div32 n_rot) {
@@ -238,14 +314,23 @@ __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j, Div32 per_rot,
 
 template <int D, int BITS, bool ROT>
 hipError_t encode_dt(const EncodeJob& j, hipStream_t s) {
-  constexpr int VPB = kWG / (D / 8);
+  constexpr int VPB = kVPT * kWG / (D / 8);
   const int64_t grid = (j.n_vec + VPB - 1) / VPB;
   const EncodeDivs q{make_div32(j.vecs_per_unit), make_div32(j.units_per_seq),
                      make_div32(j.vecs_per_rot), make_div32(j.n_rot), make_div32(j.vecs_per_rec)};
-  if (j.dtype == HSQ_F32)
-    hipLaunchKernelGGL((encode_kernel<D, BITS, HSQ_F32, ROT>), dim3((unsigned)grid), dim3(kWG), 0, s, j, q);
-  else
-    hipLaunchKernelGGL((encode_kernel<D, BITS, HSQ_BF16, ROT>), dim3((unsigned)grid), dim3(kWG), 0, s, j, q);
+  const bool contig = j.group_n == 1 && !j.row_idx && !j.pos;
+  const dim3 g((unsigned)grid), b(kWG);
+  if (j.dtype == HSQ_F32) {
+    if (contig)
+      hipLaunchKernelGGL((encode_kernel<D, BITS, HSQ_F32, ROT, true>), g, b, 0, s, j, q);
+    else
+      hipLaunchKernelGGL((encode_kernel<D, BITS, HSQ_F32, ROT, false>), g, b, 0, s, j, q);
+  } else {
+    if (contig)
+      hipLaunchKernelGGL((encode_kernel<D, BITS, HSQ_BF16, ROT, true>), g, b, 0, s, j, q);
+    else
+      hipLaunchKernelGGL((encode_kernel<D, BITS, HSQ_BF16, ROT, false>), g, b, 0, s, j, q);
+  }
   return hipGetLastError();
 }
 

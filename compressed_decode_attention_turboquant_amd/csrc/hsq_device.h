@@ -7,6 +7,16 @@
 
 namespace hsq {
 
+// Work-group barrier for LDS traffic only.  Every hand-over between the waves
+// of a work-group goes through LDS, so global loads still in flight (tiles
+// prefetched for the next phase) stay in flight across it; __syncthreads()
+// would wait for them.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Value of v in lane l ^ M (M = 1, 2, 4 or 8; pairs never leave a row of 16
 // lanes), over DPP with permutations that are their own inverses, so no
 // shift direction is involved: quad permutations for M = 1, 2; for M = 4 the

@@ -160,16 +160,6 @@ __device__ __forceinline__ int wave_iters(int n_tiles, int wave) {
   return wave < n_tiles ? (n_tiles - wave + kWaves - 1) / kWaves : 0;
 }
 
-// Work-group barrier for LDS traffic only.  Every hand-over between the waves
-// of a work-group goes through LDS, so global loads still in flight (tiles
-// prefetched for the next phase) stay in flight across it; __syncthreads()
-// would wait for them.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // Wave-wide maximum / minimum by DPP row operations (GFX9 row broadcasts);
 // the result is read from the last lane, so it is wave-uniform.
 template <int CTRL, int ROWS = 0xf>

@@ -133,7 +133,9 @@ size_t hsq_workspace_bytes(int B, int Hq, int Hkv, int d, int n_l1, int n_groups
  *               (i / vecs_per_rot) % n_rot; NULL = no rotation
  *               (vecs_per_rot and n_rot are then not used, but must be >= 1)
  *   bits        2, 3 or 4
- *   thresholds  fp32 [2^bits - 1] ascending (device)
+ *   thresholds  fp32 [2^bits - 1] ascending and symmetric about 0 (the
+ *               middle one 0, t[2^bits - 2 - k] = -t[k]), as hsq_codebook
+ *               gives (device)
  *   codes       out [n_vec][bits*d/8]: 4-bit, byte k = code[2k] |
  *               code[2k+1] << 4; 2- and 3-bit, an LSB-first bit stream
  *               with code i in bits [bits*i, bits*i + bits)

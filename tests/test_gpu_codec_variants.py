@@ -128,3 +128,23 @@ def test_rotation_index_for_many_divisors(vpr, n_rot):
         compare_norms(gn[sel], on, f"rot {r}")
         od = codec.decode(codec.unpack(gc[sel], bits, d), gn[sel], signs[r], c32)
         np.testing.assert_allclose(gx[sel], od, rtol=2e-6, atol=1e-6 * np.abs(od).max())
+
+
+@pytest.mark.parametrize("close", [False, True])
+def test_encode_4bit_any_symmetric_thresholds(close):
+    # the 4-bit encoder counts thresholds through a table of 64 bins of |y|
+    # when no bin holds two of them, else by seven compares; both give the
+    # oracle's codes (thresholds symmetric about 0, as the entry point asks)
+    d, n = 128, 3000
+    print(f"encode 4-bit custom thresholds close={close}", flush=True)
+    pos = [0.005, 0.01, 0.0105, 0.05, 0.1, 0.2, 0.5] if close else \
+          [0.02, 0.045, 0.07, 0.1, 0.13, 0.17, 0.99]
+    t = np.array([-p for p in pos[::-1]] + [0.0] + pos, dtype=np.float32)
+    rng = np.random.default_rng(8 + close)
+    signs = rng.integers(0, 1 << 32, size=(1, d // 32), dtype=np.uint64).astype(np.uint32)
+    x = _inputs(n, d, "f32", seed=77 + close)
+    codes, norms = hsq.encode(x.to(DEV), 4, signs_to_dev(signs), torch.from_numpy(t).to(DEV))
+    torch.cuda.synchronize()
+    oc, on, oy = codec.encode(x, signs[0], t)
+    compare_codes(codes.cpu().numpy(), oc, oy, t, 4, d, f"close {close}")
+    compare_norms(norms.cpu().numpy(), on, f"close {close}")
