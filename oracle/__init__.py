@@ -22,6 +22,8 @@ Modules:
   codec      random-sign Walsh-Hadamard rotation, norm scaling, scalar
              quantisation, 4-bit / 3-bit packing, dequantisation.
   tiers      L1 / L2 / L3 tier plan and build.
+  cache      decode-time tier maintenance: append a token, evict from the
+             recent window, seal N pending tokens into a group.
   decode     router scores, top-beta, union-set softmax attention, dense
              attention.
 """
