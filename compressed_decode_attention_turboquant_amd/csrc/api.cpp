@@ -360,3 +360,112 @@ extern "C" int hsq_gather_l3(const uint8_t* l3_src, size_t rec_bytes, int B, int
                                  as_stream(stream)),
                    "hsq_gather_l3 launch");
 }
+
+extern "C" int hsq_cache_append(const void* k_new, const void* v_new, int dtype, int B, int Hkv,
+                                int d, int group_n, int n_fix, int n_recent, int64_t t,
+                                int n_pending, int n_groups, int l1_cap, int ng_cap,
+                                const uint32_t* k_signs, const uint32_t* v_signs,
+                                const float* thr4, const float* thr3, uint8_t* l1k, float* l1k_n,
+                                uint8_t* l1v, float* l1v_n, void* raw_k, void* raw_v,
+                                uint8_t* l2k, float* l2k_n, uint8_t* l2v, float* l2v_n,
+                                uint8_t* l3, void* stream) {
+  if (B < 1 || Hkv < 1 || n_fix < 0 || n_recent < 1 || n_pending < 0 || n_groups < 0 ||
+      l1_cap < 1 || ng_cap < 1)
+    return fail(HSQ_ERR_ARG, "hsq_cache_append: bad sizes");
+  if (!supported_d(d)) return fail(HSQ_ERR_UNSUPPORTED, "hsq_cache_append: d must be 64 or 128");
+  if (group_n != 8 && group_n != 16)
+    return fail(HSQ_ERR_UNSUPPORTED, "hsq_cache_append: group_n must be 8 or 16");
+  if (dtype != HSQ_F32 && dtype != HSQ_BF16)
+    return fail(HSQ_ERR_UNSUPPORTED, "hsq_cache_append: dtype must be HSQ_F32 or HSQ_BF16");
+  if (t < n_recent) return fail(HSQ_ERR_ARG, "hsq_cache_append: t must be >= n_recent (full window)");
+  if (n_pending >= group_n) return fail(HSQ_ERR_ARG, "hsq_cache_append: n_pending must be < group_n");
+  if ((int64_t)n_fix + n_recent + group_n > l1_cap)
+    return fail(HSQ_ERR_ARG, "hsq_cache_append: l1_cap < n_fix + n_recent + group_n");
+  const bool seal = n_pending + 1 == group_n;
+  if (n_groups > ng_cap || (seal && n_groups >= ng_cap))
+    return fail(HSQ_ERR_ARG, "hsq_cache_append: the group capacity ng_cap is full");
+  const int64_t units = (int64_t)B * Hkv;
+  if (units * l1_cap >= (int64_t)UINT32_MAX || units * ng_cap >= (int64_t)UINT32_MAX)
+    return fail(HSQ_ERR_UNSUPPORTED, "hsq_cache_append: B * Hkv * capacity must be < 2^32");
+  if (!k_new || !v_new || !k_signs || !v_signs || !thr4 || !thr3 || !l1k || !l1k_n || !l1v ||
+      !l1v_n || !raw_k || !raw_v || !l2k || !l2k_n || !l2v || !l2v_n || !l3)
+    return fail(HSQ_ERR_ARG, "hsq_cache_append: null pointer");
+  const hipStream_t st = as_stream(stream);
+  const int slot = (int)(t % n_recent);
+  const int esize = dtype == HSQ_F32 ? 4 : 2;
+  EvictJob e{k_new, v_new, esize, (int)units, d, group_n, n_fix, n_recent, slot, n_pending,
+             l1_cap, ng_cap, n_groups, seal ? 1 : 0, l1k, l1k_n, l1v, l1v_n, raw_k, raw_v, l3};
+  int rc = check_hip(launch_cache_evict(e, st), "hsq_cache_append evict");
+  if (rc) return rc;
+  const int64_t cb4 = d / 2, cb3 = 3 * d / 8;
+  for (int kv = 0; kv < 2; ++kv) {
+    // the new token -> the window slot's L1 row, 4-bit
+    EncodeJob a{};
+    a.x = kv ? v_new : k_new; a.dtype = dtype; a.n_vec = units; a.d = d; a.bits = 4;
+    a.group_n = 1; a.signs = kv ? v_signs : k_signs; a.vecs_per_rot = 1; a.n_rot = Hkv;
+    a.thr = thr4;
+    a.codes = (kv ? l1v : l1k) + (size_t)(n_fix + slot) * cb4;
+    a.code_rec_bytes = (int64_t)l1_cap * cb4;
+    a.norms = (kv ? l1v_n : l1k_n) + n_fix + slot;
+    a.norm_rec_floats = l1_cap; a.vecs_per_rec = 1;
+    if ((rc = check_hip(launch_encode(a, st), "hsq_cache_append encode"))) return rc;
+    if (!seal) continue;
+    // the sealed group's summary: 3-bit code of the mean of its N raw rows
+    EncodeJob m{};
+    m.x = static_cast<const char*>(kv ? raw_v : raw_k) + (size_t)n_recent * d * esize;
+    m.dtype = dtype; m.n_vec = units; m.d = d; m.bits = 3; m.group_n = group_n;
+    m.row_step = n_recent + group_n;
+    m.signs = kv ? v_signs : k_signs; m.vecs_per_rot = 1; m.n_rot = Hkv; m.thr = thr3;
+    m.codes = (kv ? l2v : l2k) + (size_t)n_groups * cb3;
+    m.code_rec_bytes = (int64_t)ng_cap * cb3;
+    m.norms = (kv ? l2v_n : l2k_n) + n_groups;
+    m.norm_rec_floats = ng_cap; m.vecs_per_rec = 1;
+    if ((rc = check_hip(launch_encode(m, st), "hsq_cache_append summary"))) return rc;
+  }
+  return HSQ_OK;
+}
+
+extern "C" int hsq_cache_decode_step(const float* q, int B, int Hq, int Hkv, int d,
+                                     const uint8_t* l1k, const float* l1k_n, const uint8_t* l1v,
+                                     const float* l1v_n, int n_l1, int l1_cap,
+                                     const uint8_t* l2k, const float* l2k_n, const uint8_t* l2v,
+                                     const float* l2v_n, int n_groups, int ng_cap,
+                                     const uint8_t* l3, int group_n, int beta, int agg,
+                                     const uint32_t* k_signs, const uint32_t* v_signs,
+                                     const float* cb4, const float* cb3, float scale,
+                                     float summary_bias, int32_t* topk_idx, void* workspace,
+                                     size_t ws_bytes, float* out, void* stream) {
+  const char* fn = "hsq_cache_decode_step";
+  int rc = check_step_shape(fn, B, Hq, Hkv, d, n_l1, n_groups, group_n, beta);
+  if (rc) return rc;
+  if (l1_cap < n_l1 || ng_cap < n_groups || l1_cap < 1 || ng_cap < 1)
+    return fail(HSQ_ERR_ARG, "hsq_cache_decode_step: capacities below the counts");
+  if ((int64_t)B * Hkv * l1_cap >= (int64_t)UINT32_MAX ||
+      (int64_t)B * Hkv * ng_cap >= (int64_t)UINT32_MAX)
+    return fail(HSQ_ERR_UNSUPPORTED, "hsq_cache_decode_step: B * Hkv * capacity must be < 2^32");
+  if ((rc = attn_args(fn, q, l1k, l1k_n, l1v, l1v_n, n_l1, l2k, l2k_n, l2v, l2v_n, n_groups, l3,
+                      k_signs, v_signs, cb4, cb3, out)))
+    return rc;
+  if (agg != HSQ_AGG_MAX && agg != HSQ_AGG_MEAN) return fail(HSQ_ERR_ARG, "hsq_cache_decode_step: bad agg");
+  const int b = beta < n_groups ? beta : n_groups;
+  StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, b, l1_cap, ng_cap};
+  Workspace w;
+  if ((rc = step_common(fn, s, workspace, ws_bytes, w))) return rc;
+  StepTensors t{q, l1k, l1k_n, l1v, l1v_n, l2k, l2k_n, l2v, l2v_n, l3, 0,
+                k_signs, v_signs, cb4, cb3, scale, summary_bias, agg, out};
+  const hipStream_t st = as_stream(stream);
+  if (step_fused_ok(s))
+    return check_hip(launch_step(s, t, b > 0 ? topk_idx : nullptr, st), fn);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + w.idx_off);
+  if ((rc = check_hip(launch_route(s, t, w, ws, ROUTE_TOPK | ROUTE_PARTIALS, nullptr, nullptr,
+                                   idx, st),
+                      "hsq_cache_decode_step route")))
+    return rc;
+  if (topk_idx && b > 0 &&
+      (rc = check_hip(hipMemcpyAsync(topk_idx, idx, sizeof(int32_t) * (size_t)B * Hkv * b,
+                                     hipMemcpyDeviceToDevice, st),
+                      "hsq_cache_decode_step topk copy")))
+    return rc;
+  return check_hip(launch_attn(s, t, w, ws, idx, st), "hsq_cache_decode_step attend");
+}

@@ -73,7 +73,7 @@ __device__ __forceinline__ int64_t row_of(const EncodeJob& j, const EncodeDivs& 
     const uint32_t b = udiv(u, q.seq);
     return (int64_t)u * j.rows_per_unit + j.pos[(int64_t)b * j.pos_per_seq + (int64_t)jj * j.group_n + k];
   }
-  return (int64_t)i * j.group_n + k;
+  return (int64_t)i * (j.row_step > 0 ? j.row_step : j.group_n) + k;
 }
 
 template <int DT>
@@ -318,7 +318,7 @@ hipError_t encode_dt(const EncodeJob& j, hipStream_t s) {
   const int64_t grid = (j.n_vec + VPB - 1) / VPB;
   const EncodeDivs q{make_div32(j.vecs_per_unit), make_div32(j.units_per_seq),
                      make_div32(j.vecs_per_rot), make_div32(j.n_rot), make_div32(j.vecs_per_rec)};
-  const bool contig = j.group_n == 1 && !j.row_idx && !j.pos;
+  const bool contig = j.group_n == 1 && !j.row_idx && !j.pos && j.row_step <= 1;
   const dim3 g((unsigned)grid), b(kWG);
   if (j.dtype == HSQ_F32) {
     if (contig)

@@ -23,13 +23,15 @@ struct EncodeJob {
   int d;
   int bits;
   int group_n;        // rows averaged per output vector
-  // row mapping: row_idx (direct) | pos (tier build) | contiguous
+  // row mapping: row_idx (direct) | pos (tier build) | contiguous: rows
+  // [i * row_step, i * row_step + group_n) with row_step 0 meaning group_n
   const int64_t* row_idx;
   const int32_t* pos;
   int64_t vecs_per_unit;
   int64_t rows_per_unit;
   int64_t units_per_seq;
   int64_t pos_per_seq;
+  int64_t row_step;
   // rotation: mask (i / vecs_per_rot) % n_rot
   const uint32_t* signs;
   int64_t vecs_per_rot;
@@ -63,6 +65,10 @@ hipError_t launch_decode(const DecodeJob& j, hipStream_t s);
 struct StepShape {
   int B, Hq, Hkv, G, d;
   int n_l1, n_groups, group_n, beta;  // beta already clamped to [0, n_groups]
+  // rows between consecutive units of the L1 arrays and groups between those
+  // of the L2 / L3 arrays (capacities of a decode-time cache); 0 = n_l1 /
+  // n_groups (dense tiers)
+  int l1_stride, ng_stride;
 };
 
 struct StepTensors {
@@ -102,6 +108,20 @@ hipError_t launch_step(const StepShape& s, const StepTensors& t, int32_t* idx_ou
                        hipStream_t st);
 hipError_t launch_gather(const uint8_t* src, size_t rec_bytes, int units, int n_groups,
                          const int32_t* idx, int beta, uint8_t* dst, hipStream_t st);
+
+// ---- decode-time tier maintenance (cache.hip) -------------------------------
+// Per unit: L1 ring row n_fix + slot -> pending row n_fix + W + p (codes and
+// norms), raw ring row slot -> raw pending row W + p, new raw row -> raw ring
+// row slot; with seal, the N pending tokens (row p taken from the ring row)
+// -> L3 record ng.
+struct EvictJob {
+  const void* k_new; const void* v_new; int esize;  // raw element bytes (2 or 4)
+  int units, d, group_n, n_fix, n_recent, slot, pending, l1_cap, ng_cap, ng, seal;
+  uint8_t* l1k; float* l1k_n; uint8_t* l1v; float* l1v_n;
+  void* raw_k; void* raw_v;                          // [units][W + N][d]
+  uint8_t* l3;
+};
+hipError_t launch_cache_evict(const EvictJob& j, hipStream_t s);
 
 // ---- host-side method pieces (host.cpp) -------------------------------------
 int codebook(int d, int bits, float* centroids, float* thresholds);

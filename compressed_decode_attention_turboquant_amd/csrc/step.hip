@@ -606,6 +606,7 @@ struct SumArgs {
   const uint32_t* k_signs; const float* cb3;
   float scale, bias;
   int agg, Hkv, G, ng, beta;
+  int ngs;                 // groups between consecutive units of the L2 arrays
   int want_topk;           // route: compute scores + top-beta
   int want_partial;        // attention: summary partial
   const int32_t* given;    // fetched set to mask when not selecting here, or null
@@ -820,10 +821,10 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   const uint32_t lane4 = (uint32_t)(lane & 31) << 2;
   const int c = lane & 15, gq = lane >> 4;
 
-  const rsrc_t rk = make_rsrc(a.l2k + (size_t)unit * a.ng * CB3, (uint32_t)a.ng * CB3);
-  const rsrc_t rkn = make_rsrc(a.l2k_n + (size_t)unit * a.ng, (uint32_t)a.ng * 4);
-  const rsrc_t rv = make_rsrc(a.l2v + (size_t)unit * a.ng * CB3, (uint32_t)a.ng * CB3);
-  const rsrc_t rvn = make_rsrc(a.l2v_n + (size_t)unit * a.ng, (uint32_t)a.ng * 4);
+  const rsrc_t rk = make_rsrc(a.l2k + (size_t)unit * a.ngs * CB3, (uint32_t)a.ng * CB3);
+  const rsrc_t rkn = make_rsrc(a.l2k_n + (size_t)unit * a.ngs, (uint32_t)a.ng * 4);
+  const rsrc_t rv = make_rsrc(a.l2v + (size_t)unit * a.ngs * CB3, (uint32_t)a.ng * CB3);
+  const rsrc_t rvn = make_rsrc(a.l2v_n + (size_t)unit * a.ngs, (uint32_t)a.ng * 4);
 
   // global loads first: the set-up inputs, then the first two key tiles of
   // this wave, whose latency the set-up arithmetic below then overlaps
@@ -1187,6 +1188,7 @@ struct TokArgs {
   const uint32_t* k_signs; const uint32_t* v_signs; const float* cb4;
   float scale;
   int Hkv, G, n1, ng, group_n, beta;
+  int n1s, ngs;            // rows / groups between consecutive units of L1 / L3
   const float* part;       // summary partial per unit, or null when there are none
   float* out;
 };
@@ -1209,7 +1211,7 @@ struct TokBufs {
 template <int D, int N>
 __device__ __forceinline__ TokBufs tok_bufs(const TokArgs& a, int unit) {
   constexpr int CB = D / 2;
-  const size_t o1 = (size_t)unit * a.n1;
+  const size_t o1 = (size_t)unit * a.n1s;
   const size_t rec = (size_t)N * (D + 8);
   const int recs = a.l3_staged ? a.beta : a.ng;
   TokBufs B;
@@ -1217,7 +1219,8 @@ __device__ __forceinline__ TokBufs tok_bufs(const TokArgs& a, int unit) {
   B.l1kn = make_rsrc(a.l1k_n + o1, (uint32_t)a.n1 * 4);
   B.l1v = make_rsrc(a.l1v + o1 * CB, (uint32_t)a.n1 * CB);
   B.l1vn = make_rsrc(a.l1v_n + o1, (uint32_t)a.n1 * 4);
-  B.l3 = make_rsrc(a.l3 + (size_t)unit * recs * rec, (uint32_t)(recs * rec));
+  B.l3 = make_rsrc(a.l3 + (size_t)unit * (a.l3_staged ? a.beta : a.ngs) * rec,
+                   (uint32_t)(recs * rec));
   return B;
 }
 
@@ -1648,6 +1651,7 @@ SumArgs sum_args(const StepShape& s, const StepTensors& t) {
   a.q = t.q; a.l2k = t.l2k; a.l2k_n = t.l2k_n; a.l2v = t.l2v; a.l2v_n = t.l2v_n;
   a.k_signs = t.k_signs; a.cb3 = t.cb3; a.scale = t.scale; a.bias = t.summary_bias;
   a.agg = t.agg; a.Hkv = s.Hkv; a.G = s.G; a.ng = s.n_groups; a.beta = s.beta;
+  a.ngs = s.ng_stride > 0 ? s.ng_stride : s.n_groups;
   return a;
 }
 
@@ -1658,6 +1662,8 @@ TokArgs tok_args(const StepShape& s, const StepTensors& t) {
   a.k_signs = t.k_signs; a.v_signs = t.v_signs; a.cb4 = t.cb4; a.scale = t.scale;
   a.Hkv = s.Hkv; a.G = s.G; a.n1 = s.n_l1; a.ng = s.n_groups; a.group_n = s.group_n;
   a.beta = s.beta;
+  a.n1s = s.l1_stride > 0 ? s.l1_stride : s.n_l1;
+  a.ngs = s.ng_stride > 0 ? s.ng_stride : s.n_groups;
   a.out = t.out;
   return a;
 }

@@ -42,6 +42,11 @@ _SIGNATURES = {
     "hsq_step_attend": ([_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _vp, _i, _i, _i, _vp,
                          _vp, _vp, _f, _vp, _sz, _vp, _vp], _i),
     "hsq_gather_l3": ([_vp, _sz, _i, _i, _i, _vp, _i, _vp, _vp], _i),
+    "hsq_cache_append": ([_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i64, _i, _i, _i, _i]
+                         + [_vp] * 16, _i),
+    "hsq_cache_decode_step": ([_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp,
+                               _vp, _i, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _f, _vp,
+                               _vp, _sz, _vp, _vp], _i),
 }
 
 _lib = None
@@ -379,3 +384,154 @@ class HostArchive:
 
     def view(self, offset, nbytes):
         return self.host[offset:offset + nbytes]
+
+
+# ------------------------------------------------- decode-time tier cache ----
+
+class Cache:
+    """Tiers of one layer that grow during decoding, in the capacity layout of
+    include/hsq.h ("Cache layout").  The arrays have fixed capacities; the
+    counts (context length t, pending tokens, groups) are kept here on the
+    host and passed to every call.  pos_l1[b] lists the position held by each
+    used L1 row of sequence b (the same for every kv-head)."""
+
+    def __init__(self, B, Hkv, d, group_n, n_fix, n_recent, ng_cap, raw_dtype, device):
+        self.B, self.Hkv, self.d, self.group_n = B, Hkv, d, group_n
+        self.n_fix, self.n_recent, self.ng_cap = n_fix, n_recent, ng_cap
+        self.l1_cap = n_fix + n_recent + group_n
+        e = lambda *sh, dt=torch.uint8: torch.zeros(sh, dtype=dt, device=device)
+        f = torch.float32
+        c4, c3 = d // 2, 3 * d // 8
+        self.l1k, self.l1v = e(B, Hkv, self.l1_cap, c4), e(B, Hkv, self.l1_cap, c4)
+        self.l1k_n, self.l1v_n = e(B, Hkv, self.l1_cap, dt=f), e(B, Hkv, self.l1_cap, dt=f)
+        self.raw_k = e(B, Hkv, n_recent + group_n, d, dt=raw_dtype)
+        self.raw_v = e(B, Hkv, n_recent + group_n, d, dt=raw_dtype)
+        self.l2k, self.l2v = e(B, Hkv, ng_cap, c3), e(B, Hkv, ng_cap, c3)
+        self.l2k_n, self.l2v_n = e(B, Hkv, ng_cap, dt=f), e(B, Hkv, ng_cap, dt=f)
+        self.l3 = e(B, Hkv, ng_cap, group_n * (d + 8))
+        self.t = 0
+        self.n_pending = 0
+        self.n_groups = 0
+        self.fixed = [[] for _ in range(B)]
+        self.pending = [[] for _ in range(B)]
+
+    @property
+    def n1(self):
+        return self.n_fix + self.n_recent + self.n_pending
+
+    def pos_l1(self, b):
+        """Positions of the used L1 rows of sequence b, row by row."""
+        W, t = self.n_recent, self.t
+        ring = [0] * W
+        for p in range(t - W, t):
+            ring[p % W] = p
+        return list(self.fixed[b]) + ring + list(self.pending[b])
+
+    @classmethod
+    def from_prefix(cls, k, v, n_sink, n_recent, marked, group_n, k_signs, v_signs, thr4, thr3,
+                    ng_cap):
+        """Compress-time build of the prefix k, v [B, Hkv, T, d] (hsq_build_tiers)
+        placed into a cache.  marked[b]: reader marks of sequence b, all of
+        the same count, between the sinks and the window."""
+        B, Hkv, T, d = k.shape
+        W = n_recent
+        if T < n_sink + W:
+            raise ValueError("the prefix must hold the sinks and a full recent window")
+        rows, fixed, pend = [], [], []
+        for b in range(B):
+            mk = sorted(set(int(x) for x in np.asarray(marked[b]).reshape(-1)))
+            if mk and (mk[0] < n_sink or mk[-1] >= T - W):
+                raise ValueError("marks must lie between the sinks and the recent window")
+            l1, _ = tier_plan(T, n_sink, n_recent, mk, group_n)
+            fx = list(range(n_sink)) + mk
+            ring = [0] * W
+            for p in range(T - W, T):
+                ring[p % W] = p
+            rest = sorted(set(l1.tolist()) - set(fx) - set(range(T - W, T)))
+            fixed.append(fx)
+            pend.append(rest)
+            rows.append(fx + ring + rest)
+        if len({len(r) for r in rows}) != 1:
+            raise ValueError("every sequence needs the same number of marks")
+        gp = np.stack([tier_plan(T, n_sink, n_recent, sorted(set(int(x) for x in
+                                 np.asarray(marked[b]).reshape(-1))), group_n)[1].reshape(-1)
+                       for b in range(B)])
+        dev = k.device
+        l1_pos = torch.from_numpy(np.array(rows, dtype=np.int32)).to(dev)
+        t = build_tiers(k, v, l1_pos, torch.from_numpy(gp.astype(np.int32)).to(dev), group_n,
+                        k_signs, v_signs, thr4, thr3)
+        n_fix = len(fixed[0])
+        c = cls(B, Hkv, d, group_n, n_fix, W, ng_cap, k.dtype, dev)
+        if t.ng > ng_cap:
+            raise ValueError("ng_cap is below the prefix's group count")
+        n1 = t.n1
+        for name in ("l1k", "l1k_n", "l1v", "l1v_n"):
+            getattr(c, name)[:, :, :n1].copy_(getattr(t, name))
+        for name in ("l2k", "l2k_n", "l2v", "l2v_n", "l3"):
+            getattr(c, name)[:, :, :t.ng].copy_(getattr(t, name))
+        # raw vectors of the window (row p % W) and of the pending tokens
+        idx = torch.from_numpy(np.array([r[n_fix:] for r in rows], dtype=np.int64)).to(dev)
+        for raw, src in ((c.raw_k, k), (c.raw_v, v)):
+            g = torch.gather(src, 2, idx[:, None, :, None].expand(B, Hkv, idx.shape[1], d))
+            raw[:, :, :idx.shape[1]].copy_(g)
+        c.t, c.n_pending, c.n_groups = T, len(pend[0]), t.ng
+        c.fixed, c.pending = fixed, pend
+        return c
+
+    def append(self, k_new, v_new, k_signs, v_signs, thr4, thr3):
+        """Append one token per (sequence, kv-head): k_new, v_new [B, Hkv, d]."""
+        if k_new.dtype != self.raw_k.dtype or v_new.dtype != self.raw_k.dtype:
+            raise TypeError("k_new / v_new must have the cache's raw dtype")
+        _check(lib().hsq_cache_append(
+            _dev(k_new, name="k_new"), _dev(v_new, name="v_new"), _dtype_code(k_new), self.B,
+            self.Hkv, self.d, self.group_n, self.n_fix, self.n_recent, self.t, self.n_pending,
+            self.n_groups, self.l1_cap, self.ng_cap, _dev(k_signs, torch.int32, "k_signs"),
+            _dev(v_signs, torch.int32, "v_signs"), _dev(thr4, torch.float32, "thr4"),
+            _dev(thr3, torch.float32, "thr3"), self.l1k.data_ptr(), self.l1k_n.data_ptr(),
+            self.l1v.data_ptr(), self.l1v_n.data_ptr(), self.raw_k.data_ptr(),
+            self.raw_v.data_ptr(), self.l2k.data_ptr(), self.l2k_n.data_ptr(),
+            self.l2v.data_ptr(), self.l2v_n.data_ptr(), self.l3.data_ptr(), _stream()))
+        ev = self.t - self.n_recent
+        for b in range(self.B):
+            self.pending[b].append(ev)
+        if self.n_pending + 1 == self.group_n:
+            self.n_groups += 1
+            self.n_pending = 0
+            self.pending = [[] for _ in range(self.B)]
+        else:
+            self.n_pending += 1
+        self.t += 1
+
+    def tiers(self):
+        """Dense copies of the used rows as a Tiers (for comparisons)."""
+        n1, ng = self.n1, self.n_groups
+        return Tiers(self.B, self.Hkv, self.d, n1, ng, self.group_n,
+                     *(getattr(self, x)[:, :, :n1].contiguous() for x in
+                       ("l1k", "l1k_n", "l1v", "l1v_n")),
+                     *(getattr(self, x)[:, :, :ng].contiguous() for x in
+                       ("l2k", "l2k_n", "l2v", "l2v_n", "l3")))
+
+    def decode_step(self, q, beta, k_signs, v_signs, cb4, cb3, scale=None, summary_bias=0.0,
+                    agg=HSQ_AGG_MAX, ws=None, out=None, idx=None):
+        """Route + top-beta + attention over the cache.  Returns (out, idx)."""
+        B, Hq, d = q.shape
+        ng = self.n_groups
+        b = min(beta, ng)
+        if scale is None:
+            scale = 1.0 / math.sqrt(d)
+        if ws is None:
+            ws = make_workspace(B, Hq, self.Hkv, d, self.n1, ng, b, self.group_n, q.device)
+        if out is None:
+            out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+        if idx is None and b > 0:
+            idx = torch.empty((B, self.Hkv, b), dtype=torch.int32, device=q.device)
+        _check(lib().hsq_cache_decode_step(
+            _dev(q, torch.float32, "q"), B, Hq, self.Hkv, d, self.l1k.data_ptr(),
+            self.l1k_n.data_ptr(), self.l1v.data_ptr(), self.l1v_n.data_ptr(), self.n1,
+            self.l1_cap, self.l2k.data_ptr(), self.l2k_n.data_ptr(), self.l2v.data_ptr(),
+            self.l2v_n.data_ptr(), ng, self.ng_cap, self.l3.data_ptr(), self.group_n, beta, agg,
+            _dev(k_signs, torch.int32, "k_signs"), _dev(v_signs, torch.int32, "v_signs"),
+            _dev(cb4, torch.float32, "cb4"), _dev(cb3, torch.float32, "cb3"), scale,
+            summary_bias, idx.data_ptr() if idx is not None else None, ws.ptr, ws.nbytes,
+            out.data_ptr(), _stream()))
+        return out, idx

@@ -291,6 +291,75 @@ int hsq_step_attend(const float* q, int B, int Hq, int Hkv, int d, const uint8_t
 int hsq_gather_l3(const uint8_t* l3_src, size_t rec_bytes, int B, int Hkv, int n_groups,
                   const int32_t* topk_idx, int beta, uint8_t* staging, void* stream);
 
+/* ------------------------------------------ decode-time tier maintenance -- */
+
+/*
+ * Cache layout.  The tiers of a layer that grows during decoding, with room
+ * reserved per unit u = b * Hkv + kvh (capacities l1_cap rows, ng_cap groups):
+ *   L1   codes [B][Hkv][l1_cap][d/2] u8, norms [B][Hkv][l1_cap] f32 (K and V).
+ *        Rows [0, n_fix): sinks and reader-marked tokens; rows
+ *        [n_fix, n_fix + W): the recent window, position p in row
+ *        n_fix + p % W; rows [n_fix + W, n_fix + W + n_pending): the pending
+ *        tokens (left the window, not yet grouped) in position order.
+ *        n_l1 = n_fix + W + n_pending.
+ *   raw  K and V [B][Hkv][W + N][d] in the append dtype: row p % W holds the
+ *        raw vector of window position p, row W + j that of pending token j
+ *        (a group summary is the mean of raw vectors).
+ *   L2   codes [B][Hkv][ng_cap][3d/8] u8, norms [B][Hkv][ng_cap] f32.
+ *   L3   records [B][Hkv][ng_cap], N*(d+8) bytes each (layout above).
+ * A compress-time build (hsq_build_tiers with l1_pos listing the L1 rows in
+ * this order) placed into these arrays gives the starting cache.
+ */
+
+/*
+ * hsq_cache_append -- append one token per unit at position t (the context
+ * held t tokens) [HSQ "Three-tier architecture": the tiers after the call
+ * are those the compress-time build gives for the t + 1 tokens with the same
+ * reader marks; new tokens are not marked].  Steps, in stream order:
+ *   1. position t - W leaves the window: its L1 row and raw row move to
+ *      pending slot n_pending;
+ *   2. the new token is encoded at 4 bits into the window row of slot t % W
+ *      and its raw vector stored in raw row t % W;
+ *   3. if n_pending + 1 == group_n, the N pending tokens are sealed as group
+ *      n_groups: their codes and norms form its L3 record, and the 3-bit
+ *      code of the mean of their raw vectors its K and V summaries in L2.
+ * After the call the caller's counts are n_pending + 1 (or 0 after a seal,
+ * with n_groups + 1).  Requires every position of the window to be bound for
+ * a group (the window past the sinks and holding no marked position), which
+ * a cache built from a prefix of at least n_sink + W tokens satisfies.
+ *   k_new, v_new  [B][Hkv][d] in dtype (HSQ_F32 or HSQ_BF16), the raw dtype
+ *   t             >= n_recent;  0 <= n_pending < group_n
+ *   l1_cap        >= n_fix + n_recent + group_n;  ng_cap > n_groups on a seal
+ *   k_signs, v_signs, thr4, thr3  as for hsq_build_tiers
+ * Errors: HSQ_ERR_ARG (null pointers, sizes, a full group capacity),
+ * HSQ_ERR_UNSUPPORTED (d, group_n, dtype, B*Hkv*capacity >= 2^32),
+ * HSQ_ERR_HIP.  Calls on one cache must be ordered on one stream.
+ */
+int hsq_cache_append(const void* k_new, const void* v_new, int dtype, int B, int Hkv, int d,
+                     int group_n, int n_fix, int n_recent, int64_t t, int n_pending,
+                     int n_groups, int l1_cap, int ng_cap, const uint32_t* k_signs,
+                     const uint32_t* v_signs, const float* thr4, const float* thr3,
+                     uint8_t* l1k, float* l1k_n, uint8_t* l1v, float* l1v_n, void* raw_k,
+                     void* raw_v, uint8_t* l2k, float* l2k_n, uint8_t* l2v, float* l2v_n,
+                     uint8_t* l3, void* stream);
+
+/*
+ * hsq_cache_decode_step -- hsq_decode_step over a cache laid out with
+ * capacities: unit u's L1 rows start at row u * l1_cap and its groups at
+ * group u * ng_cap; n_l1 rows and n_groups groups of each unit are used.
+ * Archive in device memory (one launch, or two through the workspace as
+ * hsq_decode_step).  Workspace sized by hsq_workspace_bytes with the counts.
+ * Errors as hsq_decode_step, and HSQ_ERR_ARG for capacities below the counts.
+ */
+int hsq_cache_decode_step(const float* q, int B, int Hq, int Hkv, int d, const uint8_t* l1k,
+                          const float* l1k_n, const uint8_t* l1v, const float* l1v_n, int n_l1,
+                          int l1_cap, const uint8_t* l2k, const float* l2k_n,
+                          const uint8_t* l2v, const float* l2v_n, int n_groups, int ng_cap,
+                          const uint8_t* l3, int group_n, int beta, int agg,
+                          const uint32_t* k_signs, const uint32_t* v_signs, const float* cb4,
+                          const float* cb3, float scale, float summary_bias, int32_t* topk_idx,
+                          void* workspace, size_t ws_bytes, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

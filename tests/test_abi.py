@@ -104,3 +104,36 @@ def test_argument_errors_are_reported_without_launch():
     assert lib.hsq_gather_l3(p, 100, 1, 1, 4, p, 2, p, None) == -1
     assert lib.hsq_gather_l3(p, 1088, 1, 1, 4, p, 5, p, None) == -1
     assert lib.hsq_tier_plan(10, 1, 1, None, 3, 8, None, None, None, None) == -1
+
+
+def test_cache_argument_errors_are_reported_without_launch():
+    lib = hsq.lib()
+    p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    P = [p] * 16
+
+    def app(dtype=0, B=1, Hkv=1, d=128, N=8, n_fix=4, W=16, t=100, pend=0, ng=3, l1_cap=28,
+            ng_cap=10, ptrs=None):
+        return lib.hsq_cache_append(p, p, dtype, B, Hkv, d, N, n_fix, W, t, pend, ng, l1_cap,
+                                    ng_cap, *(ptrs or P)[:4], *(ptrs or P)[4:15], None)
+
+    assert app(d=96) == -2
+    assert app(N=12) == -2
+    assert app(dtype=5) == -2
+    assert app(t=15) == -1                 # window not full
+    assert app(pend=8) == -1               # pending must be < N
+    assert app(l1_cap=27) == -1            # no room for the pending tokens
+    assert app(pend=7, ng=10) == -1        # a seal with the group capacity full
+    assert app(ng=11) == -1
+    assert app(ptrs=[p] * 10 + [None] + [p] * 5) == -1
+    assert "null" in lib.hsq_last_error().decode()
+    f = ctypes.c_float(0.1)
+
+    def step(n_l1=20, l1_cap=28, ng=3, ng_cap=10, G=4):
+        return lib.hsq_cache_decode_step(p, 1, 8 * G, 8, 128, p, p, p, p, n_l1, l1_cap, p, p, p,
+                                         p, ng, ng_cap, p, 8, 2, 0, p, p, p, p, f, f, None, None,
+                                         0, p, None)
+
+    assert step(l1_cap=19) == -1           # capacity below the count
+    assert step(ng_cap=2) == -1
+    assert step(G=9) == -2
+    assert step() == -4                    # no workspace
