@@ -14,7 +14,8 @@ hold the working set, and replays a captured HIP graph so host launch latency
 stays out of the measurement.
 
 Prints one JSON line.  Also reported (same line): the codec encode/decode
-rates on the 32K x 8-head bf16 Student-t workload, the decode step with the
+rates on the 32K x 8-head bf16 Student-t workload, the decode-time append
+(tier maintenance) at the headline layer's shape, the decode step with the
 L3 archive in pinned host memory (Qwen3-8B shape, 32K context, batch 8, 36
 layers, gathered over PCIe on a side stream), and the CPU oracle on a bounded
 sample of the headline workload.
@@ -71,6 +72,7 @@ def parse():
     p.add_argument("--layers", type=int, default=8, help="independent layer instances cycled")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-codec", action="store_true")
+    p.add_argument("--no-cache", action="store_true", help="skip the cache-append timing")
     p.add_argument("--no-host", action="store_true", help="skip the pinned-host archive run")
     p.add_argument("--only-step", action="store_true", help="headline step only (for profiling)")
     p.add_argument("--calib-copy", action="store_true",
@@ -328,6 +330,49 @@ def host_archive(torch, hsq, W, steps=3):
     return res
 
 
+def cache_append_rate(torch, hsq, W, cycles=20):
+    """Decode-time tier maintenance at the headline layer's shape: one token
+    appended per (sequence, kv-head), a group sealed every N appends.  One
+    seal cycle (N appends) is captured in a graph and replayed; each replay
+    repeats the same slots' work (the same bytes), so the figure is the GPU
+    time of N appends, launch overhead excluded."""
+    dev = "cuda"
+    w = W.QWEN3_14B_16K
+    T0 = w.T - w.group_n
+    k, v = W.kv(w, 0, dev)  # the layer's raw K / V; the last N tokens are appended
+    cb = codebooks(hsq, w.d, dev)
+    ks, vs = W.signs(w.seed, 0, w.hkv, w.d)
+    dks = torch.from_numpy(ks.view(np.int32)).to(dev)
+    dvs = torch.from_numpy(vs.view(np.int32)).to(dev)
+    marks = [W.marked(w.smaller(T=T0), b) for b in range(w.batch)]
+    c = hsq.Cache.from_prefix(k[:, :, :T0].contiguous(), v[:, :, :T0].contiguous(), w.n_sink,
+                              w.n_recent, marks, w.group_n, dks, dvs, cb["thr4"], cb["thr3"],
+                              w.T // w.group_n + 1)
+    new = [(k[:, :, t].contiguous(), v[:, :, t].contiguous()) for t in range(T0, w.T)]
+    del k, v
+    stream = torch.cuda.Stream()
+    state = (c.t, c.n_pending, c.n_groups, [list(p) for p in c.pending])
+
+    def cycle():
+        c.t, c.n_pending, c.n_groups = state[0], state[1], state[2]
+        c.pending = [list(p) for p in state[3]]
+        for kn, vn in new:
+            c.append(kn, vn, dks, dvs, cb["thr4"], cb["thr3"])
+
+    with torch.cuda.stream(stream):
+        cycle()
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            cycle()
+    torch.cuda.synchronize()
+    time_graph(torch, g, 3, stream)
+    ms = time_graph(torch, g, cycles, stream) / cycles
+    return {"workload": w.name, "batch": w.batch, "kv_heads": w.hkv, "group_n": w.group_n,
+            "us_per_append": ms * 1e3 / w.group_n, "us_per_seal_cycle": ms * 1e3,
+            "launches_per_cycle": w.group_n}
+
+
 class _HostLayer:
     pass
 
@@ -457,6 +502,8 @@ def main():
         del src, dst
     if not args.only_step and not args.no_codec:
         line["codec"] = codec_rates(torch, hsq, W)
+    if not args.only_step and not args.no_cache:
+        line["cache_append"] = cache_append_rate(torch, hsq, W)
     if not args.only_step and not args.no_host:
         try:
             line["host_archive"] = host_archive(torch, hsq, W)

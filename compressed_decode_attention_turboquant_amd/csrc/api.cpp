@@ -390,39 +390,11 @@ extern "C" int hsq_cache_append(const void* k_new, const void* v_new, int dtype,
   if (!k_new || !v_new || !k_signs || !v_signs || !thr4 || !thr3 || !l1k || !l1k_n || !l1v ||
       !l1v_n || !raw_k || !raw_v || !l2k || !l2k_n || !l2v || !l2v_n || !l3)
     return fail(HSQ_ERR_ARG, "hsq_cache_append: null pointer");
-  const hipStream_t st = as_stream(stream);
-  const int slot = (int)(t % n_recent);
-  const int esize = dtype == HSQ_F32 ? 4 : 2;
-  EvictJob e{k_new, v_new, esize, (int)units, d, group_n, n_fix, n_recent, slot, n_pending,
-             l1_cap, ng_cap, n_groups, seal ? 1 : 0, l1k, l1k_n, l1v, l1v_n, raw_k, raw_v, l3};
-  int rc = check_hip(launch_cache_evict(e, st), "hsq_cache_append evict");
-  if (rc) return rc;
-  const int64_t cb4 = d / 2, cb3 = 3 * d / 8;
-  for (int kv = 0; kv < 2; ++kv) {
-    // the new token -> the window slot's L1 row, 4-bit
-    EncodeJob a{};
-    a.x = kv ? v_new : k_new; a.dtype = dtype; a.n_vec = units; a.d = d; a.bits = 4;
-    a.group_n = 1; a.signs = kv ? v_signs : k_signs; a.vecs_per_rot = 1; a.n_rot = Hkv;
-    a.thr = thr4;
-    a.codes = (kv ? l1v : l1k) + (size_t)(n_fix + slot) * cb4;
-    a.code_rec_bytes = (int64_t)l1_cap * cb4;
-    a.norms = (kv ? l1v_n : l1k_n) + n_fix + slot;
-    a.norm_rec_floats = l1_cap; a.vecs_per_rec = 1;
-    if ((rc = check_hip(launch_encode(a, st), "hsq_cache_append encode"))) return rc;
-    if (!seal) continue;
-    // the sealed group's summary: 3-bit code of the mean of its N raw rows
-    EncodeJob m{};
-    m.x = static_cast<const char*>(kv ? raw_v : raw_k) + (size_t)n_recent * d * esize;
-    m.dtype = dtype; m.n_vec = units; m.d = d; m.bits = 3; m.group_n = group_n;
-    m.row_step = n_recent + group_n;
-    m.signs = kv ? v_signs : k_signs; m.vecs_per_rot = 1; m.n_rot = Hkv; m.thr = thr3;
-    m.codes = (kv ? l2v : l2k) + (size_t)n_groups * cb3;
-    m.code_rec_bytes = (int64_t)ng_cap * cb3;
-    m.norms = (kv ? l2v_n : l2k_n) + n_groups;
-    m.norm_rec_floats = ng_cap; m.vecs_per_rec = 1;
-    if ((rc = check_hip(launch_encode(m, st), "hsq_cache_append summary"))) return rc;
-  }
-  return HSQ_OK;
+  AppendJob j{k_new, v_new, dtype, (int)units, Hkv, d, group_n, n_fix, n_recent,
+              (int)(t % n_recent), n_pending, l1_cap, ng_cap, n_groups, seal ? 1 : 0,
+              k_signs, v_signs, thr4, thr3, l1k, l1k_n, l1v, l1v_n, raw_k, raw_v,
+              l2k, l2k_n, l2v, l2v_n, l3};
+  return check_hip(launch_cache_append(j, as_stream(stream)), "hsq_cache_append");
 }
 
 extern "C" int hsq_cache_decode_step(const float* q, int B, int Hq, int Hkv, int d,

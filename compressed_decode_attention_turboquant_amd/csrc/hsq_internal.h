@@ -23,15 +23,13 @@ struct EncodeJob {
   int d;
   int bits;
   int group_n;        // rows averaged per output vector
-  // row mapping: row_idx (direct) | pos (tier build) | contiguous: rows
-  // [i * row_step, i * row_step + group_n) with row_step 0 meaning group_n
+  // row mapping: row_idx (direct) | pos (tier build) | contiguous
   const int64_t* row_idx;
   const int32_t* pos;
   int64_t vecs_per_unit;
   int64_t rows_per_unit;
   int64_t units_per_seq;
   int64_t pos_per_seq;
-  int64_t row_step;
   // rotation: mask (i / vecs_per_rot) % n_rot
   const uint32_t* signs;
   int64_t vecs_per_rot;
@@ -110,18 +108,18 @@ hipError_t launch_gather(const uint8_t* src, size_t rec_bytes, int units, int n_
                          const int32_t* idx, int beta, uint8_t* dst, hipStream_t st);
 
 // ---- decode-time tier maintenance (cache.hip) -------------------------------
-// Per unit: L1 ring row n_fix + slot -> pending row n_fix + W + p (codes and
-// norms), raw ring row slot -> raw pending row W + p, new raw row -> raw ring
-// row slot; with seal, the N pending tokens (row p taken from the ring row)
-// -> L3 record ng.
-struct EvictJob {
-  const void* k_new; const void* v_new; int esize;  // raw element bytes (2 or 4)
-  int units, d, group_n, n_fix, n_recent, slot, pending, l1_cap, ng_cap, ng, seal;
+// One token appended per unit; layouts as in include/hsq.h ("Cache layout").
+struct AppendJob {
+  const void* k_new; const void* v_new; int dtype;  // [units][d] raw
+  int units, Hkv, d, group_n, n_fix, n_recent, slot, pending, l1_cap, ng_cap, ng, seal;
+  const uint32_t* k_signs; const uint32_t* v_signs;
+  const float* thr4; const float* thr3;
   uint8_t* l1k; float* l1k_n; uint8_t* l1v; float* l1v_n;
   void* raw_k; void* raw_v;                          // [units][W + N][d]
+  uint8_t* l2k; float* l2k_n; uint8_t* l2v; float* l2v_n;
   uint8_t* l3;
 };
-hipError_t launch_cache_evict(const EvictJob& j, hipStream_t s);
+hipError_t launch_cache_append(const AppendJob& j, hipStream_t s);
 
 // ---- host-side method pieces (host.cpp) -------------------------------------
 int codebook(int d, int bits, float* centroids, float* thresholds);
