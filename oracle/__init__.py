@@ -26,4 +26,6 @@ Modules:
              recent window, seal N pending tokens into a group.
   decode     router scores, top-beta, union-set softmax attention, dense
              attention.
+  qjl        TQ-QKV: 1-bit QJL sketch of the key residual and the corrected
+             logits.
 """
