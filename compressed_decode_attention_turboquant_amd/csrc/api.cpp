@@ -441,3 +441,38 @@ extern "C" int hsq_cache_decode_step(const float* q, int B, int Hq, int Hkv, int
     return rc;
   return check_hip(launch_attn(s, t, w, ws, idx, st), "hsq_cache_decode_step attend");
 }
+
+extern "C" int hsq_encode_qjl(const void* x, int x_dtype, int64_t n_vec, int d, int bits,
+                              const uint32_t* signs, const float* thresholds,
+                              const float* centroids, const float* S, uint8_t* codes,
+                              float* norms, uint8_t* sketch, float* gamma, void* stream) {
+  if (n_vec < 0) return fail(HSQ_ERR_ARG, "hsq_encode_qjl: n_vec must be >= 0");
+  if (!supported_d(d)) return fail(HSQ_ERR_UNSUPPORTED, "hsq_encode_qjl: d must be 64 or 128");
+  if (!supported_bits(bits)) return fail(HSQ_ERR_UNSUPPORTED, "hsq_encode_qjl: bits must be 3 or 4");
+  if (x_dtype != HSQ_F32 && x_dtype != HSQ_BF16)
+    return fail(HSQ_ERR_UNSUPPORTED, "hsq_encode_qjl: dtype must be HSQ_F32 or HSQ_BF16");
+  if (n_vec == 0) return HSQ_OK;
+  if (!x || !signs || !thresholds || !centroids || !S || !codes || !norms || !sketch || !gamma)
+    return fail(HSQ_ERR_ARG, "hsq_encode_qjl: null pointer");
+  QjlJob j{x, x_dtype, n_vec, d, bits, signs, thresholds, centroids, S, codes, norms, sketch,
+           gamma};
+  return check_hip(launch_qjl_encode(j, as_stream(stream)), "hsq_encode_qjl");
+}
+
+extern "C" int hsq_qjl_logits(const float* q, int n_q, int d, int bits, const uint8_t* codes,
+                              const float* norms, const uint8_t* sketch, const float* gamma,
+                              int64_t n_keys, const uint32_t* signs, const float* centroids,
+                              const float* S, float scale, float* out, void* stream) {
+  if (n_q < 1 || n_q > 8 || n_keys < 0)
+    return fail(HSQ_ERR_ARG, "hsq_qjl_logits: n_q must be in 1..8, n_keys >= 0");
+  if (!supported_d(d)) return fail(HSQ_ERR_UNSUPPORTED, "hsq_qjl_logits: d must be 64 or 128");
+  if (!supported_bits(bits)) return fail(HSQ_ERR_UNSUPPORTED, "hsq_qjl_logits: bits must be 3 or 4");
+  if (n_keys >= (int64_t)UINT32_MAX * 256)
+    return fail(HSQ_ERR_UNSUPPORTED, "hsq_qjl_logits: too many keys");
+  if (n_keys == 0) return HSQ_OK;
+  if (!q || !codes || !norms || !sketch || !gamma || !signs || !centroids || !S || !out)
+    return fail(HSQ_ERR_ARG, "hsq_qjl_logits: null pointer");
+  QjlLogitsJob j{q, n_q, d, bits, codes, norms, sketch, gamma, n_keys, signs, centroids, S, scale,
+                 out};
+  return check_hip(launch_qjl_logits(j, as_stream(stream)), "hsq_qjl_logits");
+}

@@ -121,6 +121,23 @@ struct AppendJob {
 };
 hipError_t launch_cache_append(const AppendJob& j, hipStream_t s);
 
+// ---- TQ-QKV key path (qjl.hip) -----------------------------------------------
+// Keys of one rotation (one sign mask, one sketch matrix S [d][d] fp32).
+struct QjlJob {
+  const void* x; int dtype; int64_t n_vec; int d, bits;
+  const uint32_t* signs; const float* thr; const float* centroids; const float* S;
+  uint8_t* codes; float* norms; uint8_t* sketch; float* gamma;
+};
+hipError_t launch_qjl_encode(const QjlJob& j, hipStream_t s);
+struct QjlLogitsJob {
+  const float* q; int n_q, d, bits;
+  const uint8_t* codes; const float* norms; const uint8_t* sketch; const float* gamma;
+  int64_t n_keys;
+  const uint32_t* signs; const float* centroids; const float* S; float scale;
+  float* out;
+};
+hipError_t launch_qjl_logits(const QjlLogitsJob& j, hipStream_t s);
+
 // ---- host-side method pieces (host.cpp) -------------------------------------
 int codebook(int d, int bits, float* centroids, float* thresholds);
 

@@ -1,0 +1,238 @@
+// TQ-QKV key path for gfx950: TurboQuant key codes plus a 1-bit QJL sketch of
+// the key's residual, and the corrected logits.
+//
+// [Ablation, Statistical Inference, and Validation for KV-Cache Compression,
+// technical summary, "Experimental setup": TurboQuant may add a 1-bit
+// Johnson-Lindenstrauss (QJL) residual sketch on the key or value path;
+// "Key contributions" 1: TQ-QKV adds it on the key path.]  The estimator is
+// the published QJL one (Zandieh, Daliri and Han, 2024): with S of i.i.d.
+// N(0, 1) entries (m = d rows), sign(S u) and ||u|| give
+// sqrt(pi/2) / m * ||u|| * <S z, sign(S u)> as an unbiased estimate of
+// <z, u>.  Here u = y - c[code] is the TurboQuant error of the key in the
+// rotated unit domain (y = R x / r), so for a query q the residual's share of
+// the logit is r <R q, u>, estimated with z = R q; gamma = r ||u|| is stored.
+//
+// qjl_encode_kernel: one vector per d/8 lanes (as the codec's encoder) for
+// the norm, rotation, threshold count and packing; then the pass's residuals
+// go to LDS and every lane forms 8 of the m projections of its vector from S,
+// which sits in LDS for the work-group's whole loop over the vectors.  One
+// rotation (one S) per launch.
+// qjl_logits_kernel: R q and S R q for up to 8 query rows in LDS, then one key
+// per thread: r <R q, c[code]> + sqrt(pi/2)/m gamma <S R q, 1 - 2 bits>.
+#include "encode_device.h"
+
+namespace hsq {
+namespace {
+
+constexpr int kQWG = 256;
+
+// LDS rows of S and of the residuals padded to d + 1 floats: the 16 (or 8)
+// rows one vector's lanes read at a time, and the residual rows of different
+// vectors, then fall in different banks.
+template <int D>
+constexpr int kSP = D + 1;
+
+template <int D, int BITS, int DT>
+__global__ __launch_bounds__(kQWG) void qjl_encode_kernel(QjlJob j) {
+  constexpr int LPV = D / 8;
+  constexpr int VPP = kQWG / LPV;  // vectors per pass
+  constexpr int L = 1 << BITS;
+  constexpr int NPOS = L / 2 - 1;
+  constexpr int CB = D * BITS / 8;
+  __shared__ float s_S[D * kSP<D>];
+  __shared__ float s_u[VPP * kSP<D>];
+  __shared__ float s_c[16];
+  const int tid = threadIdx.x, sub = tid % LPV, vl = tid / LPV;
+  for (int e = tid; e < D * D; e += kQWG) s_S[(e / D) * kSP<D> + e % D] = j.S[e];
+  if (tid < L) s_c[tid] = j.centroids[tid];
+  uint32_t tpos[NPOS];
+#pragma unroll
+  for (int h = 0; h < NPOS; ++h) tpos[h] = __float_as_uint(j.thr[L / 2 + h]);
+  const uint32_t sbyte = (j.signs[sub / 4] >> (8 * (sub % 4))) & 0xffu;
+  __syncthreads();
+
+  const int64_t passes = (j.n_vec + VPP - 1) / VPP;
+  for (int64_t p = blockIdx.x; p < passes; p += gridDim.x) {
+    const int64_t i = p * VPP + vl;
+    const bool valid = i < j.n_vec;
+    float v[8];
+    if (valid) {
+      load8<DT>(j.x, i * D + 8 * sub, v);
+    } else {
+#pragma unroll
+      for (int a = 0; a < 8; ++a) v[a] = 0.f;
+    }
+    // norm, rotation, threshold count and packing: the codec's arithmetic
+    float ss = 0.f;
+#pragma unroll
+    for (int a = 0; a < 8; ++a) ss = fmaf(v[a], v[a], ss);
+#pragma unroll
+    for (int m = 1; m < LPV; m <<= 1) ss += __shfl_xor(ss, m, 64);
+    const float r = sqrtf(ss);
+    const float inv = r > 0.f ? 1.0f / (r * sqrtf((float)D)) : 0.f;
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+      v[a] = __uint_as_float(__float_as_uint(v[a]) ^ (((sbyte >> a) & 1u) << 31));
+    fwht8xlanes<LPV>(v, sub);
+    uint32_t packed = 0;
+    float uu = 0.f;
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      const float y = v[a] * inv;
+      const bool pos = y > 0.f;
+      const uint32_t key = (__float_as_uint(y) & 0x7fffffffu) + (pos ? 0u : 1u);
+      int cnt = 0;
+#pragma unroll
+      for (int h = 0; h < NPOS; ++h) cnt += (tpos[h] < key) ? 1 : 0;
+      const uint32_t code = pos ? (uint32_t)(L / 2 + cnt) : (uint32_t)(L / 2 - 1 - cnt);
+      packed |= code << (BITS * a);
+      const float u = (r > 0.f) ? y - s_c[code] : 0.f;
+      uu = fmaf(u, u, uu);
+      s_u[vl * kSP<D> + 8 * sub + a] = u;
+    }
+#pragma unroll
+    for (int m = 1; m < LPV; m <<= 1) uu += __shfl_xor(uu, m, 64);
+    uint8_t* crow = j.codes + i * CB;
+    if constexpr (BITS == 4) {
+      if (valid) reinterpret_cast<uint32_t*>(crow)[sub] = packed;
+    } else {
+      const uint32_t nxt = __shfl_down(packed, 1, 64);
+      const int qd = sub & 3;
+      if (valid && qd < 3)
+        reinterpret_cast<uint32_t*>(crow)[3 * (sub >> 2) + qd] =
+            (packed >> (8 * qd)) | (nxt << (24 - 8 * qd));
+    }
+    if (valid && sub == 0) {
+      j.norms[i] = r;
+      j.gamma[i] = r * sqrtf(uu);
+    }
+    __syncthreads();
+    // projections j = sub + LPV k (k < 8) of this vector, each summed over the
+    // coordinates in ascending order; a ballot per k then holds, for every
+    // vector of the wave, its LPV consecutive sketch bits LPV k .. LPV k + LPV - 1
+    float pj[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) pj[k] = 0.f;
+    const float* urow = s_u + vl * kSP<D>;
+    const float* srow = s_S + sub * kSP<D>;
+    for (int e = 0; e < D; ++e) {
+      const float ue = urow[e];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) pj[k] = fmaf(srow[k * LPV * kSP<D> + e], ue, pj[k]);
+    }
+    const int lane = tid & 63, g0 = lane - sub;  // first lane of this vector in the wave
+    uint32_t sk[D / 32];
+#pragma unroll
+    for (int w = 0; w < D / 32; ++w) sk[w] = 0u;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint64_t b = __builtin_amdgcn_ballot_w64(pj[k] < 0.f);
+      const uint32_t mine = (uint32_t)(b >> g0) & ((1u << LPV) - 1u);
+      const int pos = LPV * k;  // first sketch bit of this group
+      sk[pos >> 5] |= mine << (pos & 31);
+    }
+    if (valid && sub == 0) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(j.sketch + i * (D / 8));
+#pragma unroll
+      for (int w = 0; w < D / 32; ++w) dst[w] = sk[w];
+    }
+    __syncthreads();
+  }
+}
+
+template <int D, int BITS>
+__global__ __launch_bounds__(kQWG) void qjl_logits_kernel(QjlLogitsJob j) {
+  constexpr int LPV = D / 8;
+  constexpr int CB = D * BITS / 8;
+  __shared__ float s_qr[8 * D];  // R q per row
+  __shared__ float s_sq[8 * D];  // S R q per row
+  __shared__ float s_c[16];
+  const int tid = threadIdx.x;
+  if (tid < (1 << BITS)) s_c[tid] = j.centroids[tid];
+  // R q = H D q / sqrt(d) for each query row (8 rows of LPV lanes)
+  if (tid < 8 * LPV) {
+    const int h = tid / LPV, sub = tid % LPV;
+    float v[8];
+    const uint32_t sb = (j.signs[sub / 4] >> (8 * (sub % 4))) & 0xffu;
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      const float x = (h < j.n_q) ? j.q[h * D + 8 * sub + a] : 0.f;
+      v[a] = __uint_as_float(__float_as_uint(x) ^ (((sb >> a) & 1u) << 31));
+    }
+    fwht8xlanes<LPV>(v, sub);
+#pragma unroll
+    for (int a = 0; a < 8; ++a) s_qr[h * D + 8 * sub + a] = v[a] * rsqrtf((float)D);
+  }
+  __syncthreads();
+  for (int e = tid; e < j.n_q * D; e += kQWG) {
+    const int h = e / D, row = e % D;
+    float acc = 0.f;
+    for (int i = 0; i < D; ++i) acc = fmaf(j.S[row * D + i], s_qr[h * D + i], acc);
+    s_sq[e] = acc;
+  }
+  __syncthreads();
+  const int64_t k = (int64_t)blockIdx.x * kQWG + tid;
+  if (k >= j.n_keys) return;
+  uint32_t cw[CB / 4];
+#pragma unroll
+  for (int w = 0; w < CB / 4; ++w) cw[w] = reinterpret_cast<const uint32_t*>(j.codes + k * CB)[w];
+  uint32_t sw[D / 32];
+#pragma unroll
+  for (int w = 0; w < D / 32; ++w) sw[w] = reinterpret_cast<const uint32_t*>(j.sketch + k * (D / 8))[w];
+  const float r = j.norms[k], g = j.gamma[k];
+  const float cq = 1.2533141373155003f / (float)D;  // sqrt(pi / 2) / m
+  for (int h = 0; h < j.n_q; ++h) {
+    float dot = 0.f, corr = 0.f;
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const int bit = BITS * i;
+      uint32_t code;
+      if constexpr (BITS == 4) {
+        code = (cw[bit >> 5] >> (bit & 31)) & 15u;
+      } else {
+        const uint32_t lo = cw[bit >> 5] >> (bit & 31);
+        const uint32_t hi = ((bit & 31) > 29) ? (cw[(bit >> 5) + 1] << (32 - (bit & 31))) : 0u;
+        code = (lo | hi) & 7u;
+      }
+      dot = fmaf(s_qr[h * D + i], s_c[code], dot);
+      const float sgn = ((sw[i >> 5] >> (i & 31)) & 1u) ? -1.f : 1.f;
+      corr = fmaf(s_sq[h * D + i], sgn, corr);
+    }
+    j.out[h * j.n_keys + k] = j.scale * (r * dot + cq * g * corr);
+  }
+}
+
+template <int D, int BITS>
+hipError_t qjl_encode_db(const QjlJob& j, hipStream_t s) {
+  constexpr int VPP = kQWG / (D / 8);
+  const int64_t passes = (j.n_vec + VPP - 1) / VPP;
+  const unsigned grid = (unsigned)(passes < 1024 ? passes : 1024);
+  if (j.dtype == HSQ_F32)
+    hipLaunchKernelGGL((qjl_encode_kernel<D, BITS, HSQ_F32>), dim3(grid), dim3(kQWG), 0, s, j);
+  else
+    hipLaunchKernelGGL((qjl_encode_kernel<D, BITS, HSQ_BF16>), dim3(grid), dim3(kQWG), 0, s, j);
+  return hipGetLastError();
+}
+
+template <int D, int BITS>
+hipError_t qjl_logits_db(const QjlLogitsJob& j, hipStream_t s) {
+  const int64_t grid = (j.n_keys + kQWG - 1) / kQWG;
+  hipLaunchKernelGGL((qjl_logits_kernel<D, BITS>), dim3((unsigned)grid), dim3(kQWG), 0, s, j);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_qjl_encode(const QjlJob& j, hipStream_t s) {
+  if (j.n_vec <= 0) return hipSuccess;
+  if (j.d == 128) return j.bits == 4 ? qjl_encode_db<128, 4>(j, s) : qjl_encode_db<128, 3>(j, s);
+  return j.bits == 4 ? qjl_encode_db<64, 4>(j, s) : qjl_encode_db<64, 3>(j, s);
+}
+
+hipError_t launch_qjl_logits(const QjlLogitsJob& j, hipStream_t s) {
+  if (j.n_keys <= 0 || j.n_q <= 0) return hipSuccess;
+  if (j.d == 128) return j.bits == 4 ? qjl_logits_db<128, 4>(j, s) : qjl_logits_db<128, 3>(j, s);
+  return j.bits == 4 ? qjl_logits_db<64, 4>(j, s) : qjl_logits_db<64, 3>(j, s);
+}
+
+}  // namespace hsq

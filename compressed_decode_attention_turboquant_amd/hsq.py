@@ -44,6 +44,9 @@ _SIGNATURES = {
     "hsq_gather_l3": ([_vp, _sz, _i, _i, _i, _vp, _i, _vp, _vp], _i),
     "hsq_cache_append": ([_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i64, _i, _i, _i, _i]
                          + [_vp] * 16, _i),
+    "hsq_encode_qjl": ([_vp, _i, _i64, _i, _i] + [_vp] * 9, _i),
+    "hsq_qjl_logits": ([_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _f, _vp, _vp],
+                       _i),
     "hsq_cache_decode_step": ([_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp,
                                _vp, _i, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _f, _vp,
                                _vp, _sz, _vp, _vp], _i),
@@ -535,3 +538,39 @@ class Cache:
             summary_bias, idx.data_ptr() if idx is not None else None, ws.ptr, ws.nbytes,
             out.data_ptr(), _stream()))
         return out, idx
+
+
+# -------------------------------------------------------- TQ-QKV key path ----
+
+def encode_qjl(x, bits, signs, thresholds, centroids, S):
+    """TurboQuant codes of the rows of x ([n, d], one rotation) plus the 1-bit
+    QJL sketch of each residual.  Returns (codes, norms, sketch, gamma)."""
+    n, d = x.shape
+    dev = x.device
+    codes = torch.empty((n, bits * d // 8), dtype=torch.uint8, device=dev)
+    norms = torch.empty((n,), dtype=torch.float32, device=dev)
+    sketch = torch.empty((n, d // 8), dtype=torch.uint8, device=dev)
+    gamma = torch.empty((n,), dtype=torch.float32, device=dev)
+    _check(lib().hsq_encode_qjl(_dev(x, name="x"), _dtype_code(x), n, d, bits,
+                                _dev(signs, torch.int32, "signs"),
+                                _dev(thresholds, torch.float32, "thresholds"),
+                                _dev(centroids, torch.float32, "centroids"),
+                                _dev(S, torch.float32, "S"), codes.data_ptr(), norms.data_ptr(),
+                                sketch.data_ptr(), gamma.data_ptr(), _stream()))
+    return codes, norms, sketch, gamma
+
+
+def qjl_logits(q, bits, codes, norms, sketch, gamma, signs, centroids, S, scale):
+    """TQ-QKV logits [n_q, n_keys] of query rows q [n_q, d] (n_q <= 8)."""
+    n_q, d = q.shape
+    n = norms.numel()
+    out = torch.empty((n_q, n), dtype=torch.float32, device=q.device)
+    _check(lib().hsq_qjl_logits(_dev(q, torch.float32, "q"), n_q, d, bits,
+                                _dev(codes, torch.uint8, "codes"),
+                                _dev(norms, torch.float32, "norms"),
+                                _dev(sketch, torch.uint8, "sketch"),
+                                _dev(gamma, torch.float32, "gamma"), n,
+                                _dev(signs, torch.int32, "signs"),
+                                _dev(centroids, torch.float32, "centroids"),
+                                _dev(S, torch.float32, "S"), scale, out.data_ptr(), _stream()))
+    return out

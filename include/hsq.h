@@ -360,6 +360,48 @@ int hsq_cache_decode_step(const float* q, int B, int Hq, int Hkv, int d, const u
                           const float* cb3, float scale, float summary_bias, int32_t* topk_idx,
                           void* workspace, size_t ws_bytes, float* out, void* stream);
 
+/* ---------------------------------------------------- TQ-QKV key path --- */
+
+/*
+ * hsq_encode_qjl -- TurboQuant key codes plus a 1-bit QJL sketch of the key's
+ * residual [ABL "Experimental setup": an optional 1-bit Johnson-Lindenstrauss
+ * residual sketch on the K or V path; "Key contributions" 1: TQ-QKV adds it on
+ * the key path].  Estimator: the published QJL one (Zandieh, Daliri and Han,
+ * 2024).  For each row: codes and norm exactly as hsq_encode (rotation on,
+ * one mask for all rows); u = y - c[code], the TurboQuant error in the rotated
+ * unit domain (y = R x / r); sketch bit j set when (S u)_j < 0 (LSB-first, bit
+ * j in byte j / 8, d bits per row); gamma = r * ||u||_2.
+ *   x           [n_vec][d] in x_dtype (HSQ_F32 or HSQ_BF16)
+ *   bits        3 or 4;  signs uint32 [d/32];  thresholds fp32 [2^bits - 1]
+ *   centroids   fp32 [2^bits] (the thresholds' codebook)
+ *   S           fp32 [d][d], row j the j-th sketch direction (i.i.d. N(0,1)
+ *               data, one per (layer, kv-head))
+ *   codes       out [n_vec][bits*d/8];  norms out fp32 [n_vec]
+ *   sketch      out [n_vec][d/8];  gamma out fp32 [n_vec]
+ * Errors: HSQ_ERR_ARG (null pointers, n_vec < 0), HSQ_ERR_UNSUPPORTED (d,
+ * bits, dtype), HSQ_ERR_HIP.  n_vec == 0 is a no-op.
+ */
+int hsq_encode_qjl(const void* x, int x_dtype, int64_t n_vec, int d, int bits,
+                   const uint32_t* signs, const float* thresholds, const float* centroids,
+                   const float* S, uint8_t* codes, float* norms, uint8_t* sketch, float* gamma,
+                   void* stream);
+
+/*
+ * hsq_qjl_logits -- TQ-QKV logits of n_q query rows against n_keys keys
+ * encoded by hsq_encode_qjl (same signs, centroids and S):
+ *   out[h][k] = scale * (r_k <R q_h, c[code_k]> +
+ *               sqrt(pi/2) / d * gamma_k * sum_j (S R q_h)_j (1 - 2 bit_kj))
+ * i.e. the TurboQuant logit plus the unbiased QJL estimate of the residual's
+ * share [ABL "Key contributions" 2: this correction is zero-mean but its
+ * variance inflates softmax weights by about exp(sigma^2 / 2)].
+ *   q    fp32 [n_q][d], 1 <= n_q <= 8;  out fp32 [n_q][n_keys]
+ * Errors: HSQ_ERR_ARG, HSQ_ERR_UNSUPPORTED (d, bits), HSQ_ERR_HIP.
+ */
+int hsq_qjl_logits(const float* q, int n_q, int d, int bits, const uint8_t* codes,
+                   const float* norms, const uint8_t* sketch, const float* gamma, int64_t n_keys,
+                   const uint32_t* signs, const float* centroids, const float* S, float scale,
+                   float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
