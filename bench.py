@@ -14,7 +14,8 @@ hold the working set, and replays a captured HIP graph so host launch latency
 stays out of the measurement.
 
 Prints one JSON line.  Also reported (same line): the codec encode/decode
-rates on the 32K x 8-head bf16 Student-t workload, the decode-time append
+rates on the 32K x 8-head bf16 Student-t workload (and its TQ-QKV key path),
+the decode-time append
 (tier maintenance) at the headline layer's shape, the decode step with the
 L3 archive in pinned host memory (Qwen3-8B shape, 32K context, batch 8, 36
 layers, gathered over PCIe on a side stream), and the CPU oracle on a bounded
@@ -330,6 +331,61 @@ def host_archive(torch, hsq, W, steps=3):
     return res
 
 
+def qjl_rates(torch, hsq, W, reps=20):
+    """TQ-QKV key path on the codec workload's keys (32768 tokens x 8 heads,
+    d = 128, bf16 Student-t with outlier channels): 4-bit codes plus the 1-bit
+    QJL residual sketch, one launch per head (one S per head); then the
+    corrected logits of 5 query rows against one head's keys, and the logit
+    error of TQ-KV and TQ-QKV against the exact logits on that head (the
+    page's Jensen concern: the correction is unbiased but adds variance)."""
+    dev = "cuda"
+    c = W.CODEC
+    k, _ = W.codec_inputs(c, dev)
+    ks, _ = W.codec_signs(c)
+    kh = k.view(c.heads, c.tokens, c.d)
+    rng = np.random.default_rng([c.seed, 7])
+    S = [torch.from_numpy(rng.standard_normal((c.d, c.d)).astype(np.float32)).to(dev)
+         for _ in range(c.heads)]
+    sg = [torch.from_numpy(ks[h].view(np.int32)).to(dev) for h in range(c.heads)]
+    cen, thr = (torch.from_numpy(a).to(dev) for a in hsq.codebook(c.d, 4))
+    stream = torch.cuda.Stream()
+    outs = [None] * c.heads
+    with torch.cuda.stream(stream):
+        for h in range(c.heads):
+            outs[h] = hsq.encode_qjl(kh[h], 4, sg[h], thr, cen, S[h])
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for h in range(c.heads):
+                hsq.encode_qjl(kh[h], 4, sg[h], thr, cen, S[h])
+    time_graph(torch, g, 3, stream)
+    te = time_graph(torch, g, reps, stream) / reps
+    q = torch.from_numpy(rng.standard_normal((5, c.d)).astype(np.float32)).to(dev)
+    codes, norms, sketch, gamma = outs[0]
+    scale = 1.0 / math.sqrt(c.d)
+    with torch.cuda.stream(stream):
+        lg = hsq.qjl_logits(q, 4, codes, norms, sketch, gamma, sg[0], cen, S[0], scale)
+        gl = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gl, stream=stream):
+            hsq.qjl_logits(q, 4, codes, norms, sketch, gamma, sg[0], cen, S[0], scale)
+    time_graph(torch, gl, 3, stream)
+    tl = time_graph(torch, gl, reps, stream) / reps
+    # logit errors against the exact bf16 keys: TQ-KV (decode + dot) vs TQ-QKV
+    exact = scale * (q.double() @ kh[0].double().T)
+    tq = scale * (q.double() @ hsq.decode(codes, norms, 4, c.d, sg[0], cen).double().T)
+    e_tq, e_qjl = (tq - exact), (lg.double() - exact)
+    n = c.heads * c.tokens
+    in_b = n * c.d * 2
+    out_b = n * (c.d // 2 + 4 + c.d // 8 + 4)
+    res = {"encode_us": te * 1e3, "encode_in_gbs": in_b / (te * 1e-3) / 1e9,
+           "encode_hbm_frac": (in_b + out_b) / (te * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "logits_us": tl * 1e3, "logit_rows": 5, "keys": c.tokens,
+           "logit_err_mean_tq": float(e_tq.mean()), "logit_err_var_tq": float(e_tq.var()),
+           "logit_err_mean_qjl": float(e_qjl.mean()), "logit_err_var_qjl": float(e_qjl.var())}
+    del k, kh, outs, g, gl
+    return res
+
+
 def cache_append_rate(torch, hsq, W, cycles=20):
     """Decode-time tier maintenance at the headline layer's shape: one token
     appended per (sequence, kv-head), a group sealed every N appends.  One
@@ -502,6 +558,8 @@ def main():
         del src, dst
     if not args.only_step and not args.no_codec:
         line["codec"] = codec_rates(torch, hsq, W)
+    if not args.only_step and not args.no_codec:
+        line["qjl"] = qjl_rates(torch, hsq, W)
     if not args.only_step and not args.no_cache:
         line["cache_append"] = cache_append_rate(torch, hsq, W)
     if not args.only_step and not args.no_host:
