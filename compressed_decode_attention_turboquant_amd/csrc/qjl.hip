@@ -14,15 +14,17 @@
 //
 // qjl_encode_kernel: one vector per d/8 lanes (as the codec's encoder) for
 // the norm, rotation, threshold count and packing; then the pass's residuals
-// go to LDS and every lane forms 8 of the m projections of its vector from S,
-// which sits in LDS for the work-group's whole loop over the vectors.  One
-// rotation (one S) per launch.
+// go to LDS, and the projections S u of the whole pass are one small matrix
+// product on fp32 MFMA against S, which sits in LDS for the work-group's loop
+// over the vectors.  One rotation (one S) per launch.
 // qjl_logits_kernel: R q and S R q for up to 8 query rows in LDS, then one key
 // per thread: r <R q, c[code]> + sqrt(pi/2)/m gamma <S R q, 1 - 2 bits>.
 #include "encode_device.h"
 
 namespace hsq {
 namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kQWG = 256;
 
@@ -107,34 +109,31 @@ __global__ __launch_bounds__(kQWG) void qjl_encode_kernel(QjlJob j) {
       j.gamma[i] = r * sqrtf(uu);
     }
     __syncthreads();
-    // projections j = sub + LPV k (k < 8) of this vector, each summed over the
-    // coordinates in ascending order; a ballot per k then holds, for every
-    // vector of the wave, its LPV consecutive sketch bits LPV k .. LPV k + LPV - 1
-    float pj[8];
+    // projections of the pass's residuals, P = U S^T (VPP x d), on fp32 MFMA
+    // (16 x 16 x 4 blocks): the 8 output tiles of 16 x 16 go two to a wave.
+    // In a tile, lane l holds P[4 (l / 16) + e][l % 16] (e < 4), so one
+    // ballot per e gives, for the four vectors of each 16-lane row, 16
+    // consecutive sketch bits.
+    const int lane = tid & 63, wv = tid >> 6;
+    const int lr = lane & 15, lk = lane >> 4;
+    constexpr int CT = D / 16;  // column tiles
 #pragma unroll
-    for (int k = 0; k < 8; ++k) pj[k] = 0.f;
-    const float* urow = s_u + vl * kSP<D>;
-    const float* srow = s_S + sub * kSP<D>;
-    for (int e = 0; e < D; ++e) {
-      const float ue = urow[e];
+    for (int tt = 0; tt < 2; ++tt) {
+      const int tile = 2 * wv + tt, rt = tile / CT, ct = tile % CT;
+      const float* ua = s_u + (16 * rt + lr) * kSP<D> + lk;
+      const float* sb = s_S + (16 * ct + lr) * kSP<D> + lk;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int k0 = 0; k0 < D; k0 += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ua[k0], sb[k0], acc, 0, 0, 0);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) pj[k] = fmaf(srow[k * LPV * kSP<D> + e], ue, pj[k]);
-    }
-    const int lane = tid & 63, g0 = lane - sub;  // first lane of this vector in the wave
-    uint32_t sk[D / 32];
-#pragma unroll
-    for (int w = 0; w < D / 32; ++w) sk[w] = 0u;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint64_t b = __builtin_amdgcn_ballot_w64(pj[k] < 0.f);
-      const uint32_t mine = (uint32_t)(b >> g0) & ((1u << LPV) - 1u);
-      const int pos = LPV * k;  // first sketch bit of this group
-      sk[pos >> 5] |= mine << (pos & 31);
-    }
-    if (valid && sub == 0) {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(j.sketch + i * (D / 8));
-#pragma unroll
-      for (int w = 0; w < D / 32; ++w) dst[w] = sk[w];
+      for (int e = 0; e < 4; ++e) {
+        const uint64_t b = __builtin_amdgcn_ballot_w64(acc[e] < 0.f);
+        const int64_t vi = p * VPP + 16 * rt + 4 * lk + e;
+        if (lr == 0 && vi < j.n_vec)
+          *reinterpret_cast<uint16_t*>(j.sketch + vi * (D / 8) + 2 * ct) =
+              (uint16_t)(b >> (16 * lk));
+      }
     }
     __syncthreads();
   }
