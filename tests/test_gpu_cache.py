@@ -191,3 +191,38 @@ def test_headline_shape_append_and_decode():
     out2, idx2 = hsq.decode_step(c.q, c.cache.tiers(), w.beta, c.dks, c.dvs, c.cb4, c.cb3)
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2) and torch.equal(out, out2)
+
+
+@pytest.mark.parametrize("beta", [0, 1, 10000])
+def test_cache_decode_beta_edges(beta):
+    # nothing fetched, one group, every group: the strided step equals the
+    # dense one bit for bit, and the oracle within the attention tolerance
+    w = W.TINY.smaller(batch=2, hq=4, hkv=2, n_recent=16, n_marked=10, beta=beta)
+    T0, K = 200, 11
+    print(f"[cache decode beta={beta}]", flush=True)
+    c = CacheCase(w, T0, K)
+    for t in range(T0, T0 + K):
+        c.append(t)
+    g = c.cache
+    out, idx = g.decode_step(c.q, beta, c.dks, c.dvs, c.cb4, c.cb3)
+    out2, idx2 = hsq.decode_step(c.q, g.tiers(), beta, c.dks, c.dvs, c.cb4, c.cb3)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    b_eff = min(beta, g.n_groups)
+    if b_eff > 0:
+        assert torch.equal(idx, idx2) and idx.shape[-1] == b_eff
+    kc, vc = c.k.cpu(), c.v.cpu()
+    scale = 1 / math.sqrt(w.d)
+    for b in range(w.batch):
+        for h in range(w.hkv):
+            o = ocache.UnitCache(kc[b, h, :T0], vc[b, h, :T0], w.n_sink, w.n_recent, c.marks[b],
+                                 w.group_n, c.ks[h], c.vs[h], c.c4, c.c3)
+            for t in range(T0, T0 + K):
+                o.append(kc[b, h, t], vc[b, h, t])
+            u = o.as_unit()
+            deq = odec.dequant_unit(u, w.d, w.group_n, c.ks[h], c.vs[h], c.c4, c.c3)
+            sel = idx[b, h].cpu().numpy() if b_eff > 0 else np.zeros(0, np.int64)
+            qh = c.q[b, h * w.G:(h + 1) * w.G].double().cpu().numpy()
+            want = odec.hsq_attention_unit(qh, deq, u["l3"], sel, w.group_n, w.d, c.ks[h],
+                                           c.vs[h], c.c4, scale)
+            assert rel_l2(out[b, h * w.G:(h + 1) * w.G].cpu().numpy(), want) < ATTN_REL_L2
