@@ -137,3 +137,26 @@ def test_cache_argument_errors_are_reported_without_launch():
     assert step(ng_cap=2) == -1
     assert step(G=9) == -2
     assert step() == -4                    # no workspace
+
+
+def test_qjl_argument_errors_are_reported_without_launch():
+    lib = hsq.lib()
+    p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    P = [p] * 9
+    enc = lambda d=128, bits=4, dtype=0, n=10, ptrs=P: lib.hsq_encode_qjl(p, dtype, n, d, bits,
+                                                                          *ptrs[:8], None)
+    assert enc(d=96) == -2
+    assert enc(bits=2) == -2
+    assert enc(dtype=3) == -2
+    assert enc(n=-1) == -1
+    assert enc(ptrs=[p] * 4 + [None] + [p] * 4) == -1
+    assert "null" in lib.hsq_last_error().decode()
+    assert enc(n=0, ptrs=[None] * 9) == 0  # nothing to do
+    f = ctypes.c_float(0.1)
+    lg = lambda n_q=4, d=128, bits=4, n=10: lib.hsq_qjl_logits(p, n_q, d, bits, p, p, p, p, n, p,
+                                                                p, p, f, p, None)
+    assert lg(n_q=0) == -1
+    assert lg(n_q=9) == -1
+    assert lg(d=32) == -2
+    assert lg(bits=5) == -2
+    assert lg(n=-1) == -1
