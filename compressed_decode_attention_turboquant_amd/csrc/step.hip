@@ -201,12 +201,18 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 // 4-bit: byte b (codes b & 15, b >> 4) -> fp16 pair; copy l at dword b*64 + l,
 // so lane l's address is (b << 8) | (l << 2): one v_perm from the code dword.
 __device__ void build_lut4(uint32_t* lut, const float* cb, int tid) {
-  // thread t fills copies 32(t&1) .. 32(t&1)+31 of entry t/2
-  const int e = tid >> 1;
-  const uint32_t v = h2u((_Float16)cb[e & 15], (_Float16)cb[e >> 4]);
-  u32x4* dst = reinterpret_cast<u32x4*>(lut + e * kNC4 + 32 * (tid & 1));
+  // 16-byte chunk c holds copies 4(c%16) .. 4(c%16)+3 of entry c/16; thread t
+  // writes chunks t, t + 512, ..., so the lanes of a wave write consecutive
+  // chunks (a write per entry and lane pair would put every even lane of a
+  // wave on the same four banks)
+  u32x4* dst = reinterpret_cast<u32x4*>(lut);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) dst[k] = u32x4{v, v, v, v};
+  for (int k = 0; k < 8; ++k) {
+    const int c = k * kThreads + tid;
+    const int e = c >> 4;
+    const uint32_t v = h2u((_Float16)cb[e & 15], (_Float16)cb[e >> 4]);
+    dst[c] = u32x4{v, v, v, v};
+  }
 }
 // byte K of w as a table address for this lane
 template <int K>
