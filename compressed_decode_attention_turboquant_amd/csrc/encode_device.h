@@ -77,6 +77,32 @@ __device__ __forceinline__ void load8(const void* x, int64_t off, float (&v)[8])
   }
 }
 
+// Sum of x over the LPV lanes of a vector (xor butterflies over DPP, no LDS
+// round trip).
+template <int LPV>
+__device__ __forceinline__ float lanes_sum(float x) {
+  x += xor_lane<1>(x);
+  x += xor_lane<2>(x);
+  x += xor_lane<4>(x);
+  if constexpr (LPV == 16) x += xor_lane<8>(x);
+  return x;
+}
+
+// Norm r = ||x|| of the vector whose lanes' sums of squares are ss, and the
+// scale inv applied to its unnormalised transform (1 / (r sqrt(d)); 1 / r with
+// the rotation off; 0 for the zero vector).  The hardware square root and
+// reciprocal (within 1 ulp): every encoder shares this function, so they all
+// take the same codes; against the fp64 oracle the differences stay far inside
+// the code and norm tolerances.
+template <int D, bool ROT>
+__device__ __forceinline__ void norm_scale(float ss_lane, float& r, float& inv) {
+  constexpr int LPV = D / 8;
+  const float ss = lanes_sum<LPV>(ss_lane);
+  r = __builtin_amdgcn_sqrtf(ss);
+  const float den = ROT ? r * __builtin_sqrtf((float)D) : r;
+  inv = r > 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;
+}
+
 // Norm, rotation, quantisation and packing of vector i, whose 8 coordinates
 // of this lane are in v (LPV lanes per vector).
 template <int D, int BITS, bool ROT, int kBins>
@@ -91,11 +117,8 @@ __device__ __forceinline__ void encode_one(const EncodeJob& j, const EncodeDivs&
   float ss = 0.f;
 #pragma unroll
   for (int a = 0; a < 8; ++a) ss = fmaf(v[a], v[a], ss);
-#pragma unroll
-  for (int m = 1; m < LPV; m <<= 1) ss += __shfl_xor(ss, m, 64);
-  const float r = sqrtf(ss);
-  // the unnormalised transform scales by sqrt(d)
-  const float inv = r > 0.f ? 1.0f / (ROT ? r * sqrtf((float)D) : r) : 0.f;
+  float r, inv;  // the unnormalised transform scales by sqrt(d)
+  norm_scale<D, ROT>(ss, r, inv);
 
   if constexpr (ROT) {
     const uint32_t sbyte = (sword >> (8 * (sub % 4))) & 0xffu;

@@ -68,10 +68,8 @@ __global__ __launch_bounds__(kQWG) void qjl_encode_kernel(QjlJob j) {
     float ss = 0.f;
 #pragma unroll
     for (int a = 0; a < 8; ++a) ss = fmaf(v[a], v[a], ss);
-#pragma unroll
-    for (int m = 1; m < LPV; m <<= 1) ss += __shfl_xor(ss, m, 64);
-    const float r = sqrtf(ss);
-    const float inv = r > 0.f ? 1.0f / (r * sqrtf((float)D)) : 0.f;
+    float r, inv;
+    norm_scale<D, true>(ss, r, inv);
 #pragma unroll
     for (int a = 0; a < 8; ++a)
       v[a] = __uint_as_float(__float_as_uint(v[a]) ^ (((sbyte >> a) & 1u) << 31));
@@ -92,8 +90,7 @@ __global__ __launch_bounds__(kQWG) void qjl_encode_kernel(QjlJob j) {
       uu = fmaf(u, u, uu);
       s_u[vl * kSP<D> + 8 * sub + a] = u;
     }
-#pragma unroll
-    for (int m = 1; m < LPV; m <<= 1) uu += __shfl_xor(uu, m, 64);
+    uu = lanes_sum<LPV>(uu);
     uint8_t* crow = j.codes + i * CB;
     if constexpr (BITS == 4) {
       if (valid) reinterpret_cast<uint32_t*>(crow)[sub] = packed;
