@@ -26,6 +26,8 @@ namespace {
 
 constexpr int kWG = 256;
 constexpr int kVPT = 2;  // vectors per thread in the encoder
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // CONTIG: one row per vector, row i (group_n == 1, no row_idx, no pos); the
 // loads are then straight-line, at indices clamped into the array, so that
@@ -146,7 +148,8 @@ __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j, Div32 per_rot,
 #pragma unroll
   for (int a = 0; a < 8; ++a) v[a] = cent[(codes >> (BITS * a)) & ((1u << BITS) - 1)];
   if constexpr (ROT) fwht8xlanes<LPV>(v, sub);
-  const float s = ROT ? r / sqrtf((float)D) : r;
+  // 1 / sqrt(d) is a compile-time constant: one multiply, not a division
+  const float s = ROT ? r * (1.f / __builtin_sqrtf((float)D)) : r;
 #pragma unroll
   for (int a = 0; a < 8; ++a)
     v[a] = __uint_as_float(__float_as_uint(v[a] * s) ^ (((sbyte >> a) & 1u) << 31));
@@ -156,14 +159,11 @@ __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j, Div32 per_rot,
     o[0] = make_float4(v[0], v[1], v[2], v[3]);
     o[1] = make_float4(v[4], v[5], v[6], v[7]);
   } else {
+    // round to nearest even, two values per conversion instruction
     uint32_t w[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t lo = __float_as_uint(v[2 * k]), hi = __float_as_uint(v[2 * k + 1]);
-      lo = (lo + 0x7fffu + ((lo >> 16) & 1u)) >> 16;
-      hi = (hi + 0x7fffu + ((hi >> 16) & 1u)) & 0xffff0000u;
-      w[k] = lo | hi;
-    }
+    for (int k = 0; k < 4; ++k)
+      w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v[2 * k], v[2 * k + 1]}, bf16x2));
     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(j.out) + (int64_t)i * D + 8 * sub) =
         make_uint4(w[0], w[1], w[2], w[3]);
   }
