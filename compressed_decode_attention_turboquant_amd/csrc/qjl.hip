@@ -18,7 +18,7 @@
 // product on fp32 MFMA against S, which sits in LDS for the work-group's loop
 // over the vectors.  One rotation (one S) per launch.
 // qjl_logits_kernel: R q and S R q for up to 8 query rows in LDS, then one key
-// per thread: r <R q, c[code]> + sqrt(pi/2)/m gamma <S R q, 1 - 2 bits>.
+// per d/8 lanes: r <R q, c[code]> + sqrt(pi/2)/m gamma <S R q, 1 - 2 bits>.
 #include "encode_device.h"
 
 namespace hsq {
@@ -167,34 +167,46 @@ __global__ __launch_bounds__(kQWG) void qjl_logits_kernel(QjlLogitsJob j) {
     s_sq[e] = acc;
   }
   __syncthreads();
-  const int64_t k = (int64_t)blockIdx.x * kQWG + tid;
-  if (k >= j.n_keys) return;
-  uint32_t cw[CB / 4];
-#pragma unroll
-  for (int w = 0; w < CB / 4; ++w) cw[w] = reinterpret_cast<const uint32_t*>(j.codes + k * CB)[w];
-  uint32_t sw[D / 32];
-#pragma unroll
-  for (int w = 0; w < D / 32; ++w) sw[w] = reinterpret_cast<const uint32_t*>(j.sketch + k * (D / 8))[w];
-  const float r = j.norms[k], g = j.gamma[k];
+  // one key per LPV lanes, 8 coordinates per lane (as the codec): each lane
+  // forms its share of every row's two sums, then the LPV lanes add them
+  const int sub = tid % LPV, kl = tid / LPV;
+  constexpr int KPP = kQWG / LPV;  // keys per pass
   const float cq = 1.2533141373155003f / (float)D;  // sqrt(pi / 2) / m
-  for (int h = 0; h < j.n_q; ++h) {
-    float dot = 0.f, corr = 0.f;
-#pragma unroll
-    for (int i = 0; i < D; ++i) {
-      const int bit = BITS * i;
-      uint32_t code;
-      if constexpr (BITS == 4) {
-        code = (cw[bit >> 5] >> (bit & 31)) & 15u;
-      } else {
-        const uint32_t lo = cw[bit >> 5] >> (bit & 31);
-        const uint32_t hi = ((bit & 31) > 29) ? (cw[(bit >> 5) + 1] << (32 - (bit & 31))) : 0u;
-        code = (lo | hi) & 7u;
-      }
-      dot = fmaf(s_qr[h * D + i], s_c[code], dot);
-      const float sgn = ((sw[i >> 5] >> (i & 31)) & 1u) ? -1.f : 1.f;
-      corr = fmaf(s_sq[h * D + i], sgn, corr);
+  for (int64_t k0 = (int64_t)blockIdx.x * KPP; k0 < j.n_keys; k0 += (int64_t)gridDim.x * KPP) {
+    const int64_t k = k0 + kl;
+    const bool valid = k < j.n_keys;
+    const int64_t kc = valid ? k : j.n_keys - 1;  // past the end: reread the last key
+    const uint32_t* row = reinterpret_cast<const uint32_t*>(j.codes + kc * CB);
+    uint32_t codes;
+    if constexpr (BITS == 4) {
+      codes = row[sub];
+    } else {
+      const int bit = 24 * sub, off = bit & 31;
+      codes = row[bit >> 5] >> off;
+      if (off > 8) codes |= row[(bit >> 5) + 1] << (32 - off);
+      codes &= 0xffffffu;
     }
-    j.out[h * j.n_keys + k] = j.scale * (r * dot + cq * g * corr);
+    const uint32_t sb = j.sketch[kc * (D / 8) + sub];
+    const float r = j.norms[kc], g = j.gamma[kc];
+    float c[8];
+#pragma unroll
+    for (int a = 0; a < 8; ++a) c[a] = s_c[(codes >> (BITS * a)) & ((1u << BITS) - 1u)];
+    for (int h = 0; h < j.n_q; ++h) {
+      const f32x4* qv = reinterpret_cast<const f32x4*>(s_qr + h * D + 8 * sub);
+      const f32x4* sv = reinterpret_cast<const f32x4*>(s_sq + h * D + 8 * sub);
+      const f32x4 q0 = qv[0], q1 = qv[1], s0 = sv[0], s1 = sv[1];
+      float dot = 0.f, corr = 0.f;
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        const float qa = a < 4 ? q0[a] : q1[a - 4];
+        const float sa = a < 4 ? s0[a] : s1[a - 4];
+        dot = fmaf(qa, c[a], dot);
+        corr += ((sb >> a) & 1u) ? -sa : sa;
+      }
+      dot = lanes_sum<LPV>(dot);
+      corr = lanes_sum<LPV>(corr);
+      if (valid && sub == 0) j.out[h * j.n_keys + k] = j.scale * (r * dot + cq * g * corr);
+    }
   }
 }
 
@@ -212,7 +224,10 @@ hipError_t qjl_encode_db(const QjlJob& j, hipStream_t s) {
 
 template <int D, int BITS>
 hipError_t qjl_logits_db(const QjlLogitsJob& j, hipStream_t s) {
-  const int64_t grid = (j.n_keys + kQWG - 1) / kQWG;
+  // every work-group forms R q and S R q once, then loops over its keys
+  constexpr int KPP = kQWG / (D / 8);
+  const int64_t passes = (j.n_keys + KPP - 1) / KPP;
+  const int64_t grid = passes < 512 ? passes : 512;
   hipLaunchKernelGGL((qjl_logits_kernel<D, BITS>), dim3((unsigned)grid), dim3(kQWG), 0, s, j);
   return hipGetLastError();
 }

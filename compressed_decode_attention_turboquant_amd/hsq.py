@@ -440,12 +440,13 @@ class Cache:
         W = n_recent
         if T < n_sink + W:
             raise ValueError("the prefix must hold the sinks and a full recent window")
-        rows, fixed, pend = [], [], []
+        rows, fixed, pend, gps = [], [], [], []
         for b in range(B):
             mk = sorted(set(int(x) for x in np.asarray(marked[b]).reshape(-1)))
             if mk and (mk[0] < n_sink or mk[-1] >= T - W):
                 raise ValueError("marks must lie between the sinks and the recent window")
-            l1, _ = tier_plan(T, n_sink, n_recent, mk, group_n)
+            l1, gp_b = tier_plan(T, n_sink, n_recent, mk, group_n)
+            gps.append(gp_b.reshape(-1))
             fx = list(range(n_sink)) + mk
             ring = [0] * W
             for p in range(T - W, T):
@@ -456,9 +457,7 @@ class Cache:
             rows.append(fx + ring + rest)
         if len({len(r) for r in rows}) != 1:
             raise ValueError("every sequence needs the same number of marks")
-        gp = np.stack([tier_plan(T, n_sink, n_recent, sorted(set(int(x) for x in
-                                 np.asarray(marked[b]).reshape(-1))), group_n)[1].reshape(-1)
-                       for b in range(B)])
+        gp = np.stack(gps)
         dev = k.device
         l1_pos = torch.from_numpy(np.array(rows, dtype=np.int32)).to(dev)
         t = build_tiers(k, v, l1_pos, torch.from_numpy(gp.astype(np.int32)).to(dev), group_n,
