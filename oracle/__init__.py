@@ -28,4 +28,6 @@ Modules:
              attention.
   qjl        TQ-QKV: 1-bit QJL sketch of the key residual and the corrected
              logits.
+  rope       pre-RoPE archive: dequantise, then rotate to the token's
+             position.
 """
