@@ -14,8 +14,9 @@ hold the working set, and replays a captured HIP graph so host launch latency
 stays out of the measurement.
 
 Prints one JSON line.  Also reported (same line): the codec encode/decode
-rates on the 32K x 8-head bf16 Student-t workload (and its TQ-QKV key path),
-the decode-time append
+rates on the 32K x 8-head bf16 Student-t workload (with the pre-RoPE fetch,
+dequantise then RoPE at each token's position, and the TQ-QKV key path), the
+decode-time append
 (tier maintenance) at the headline layer's shape, the decode step with the
 L3 archive in pinned host memory (Qwen3-8B shape, 32K context, batch 8, 36
 layers, gathered over PCIe on a side stream), and the CPU oracle on a bounded
@@ -30,6 +31,7 @@ import time
 
 import numpy as np
 
+ROPE_BASE = 1e6  # the Qwen3 models' rotary base
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "compressed_decode_attention_turboquant_amd", "csrc")
@@ -252,6 +254,23 @@ def codec_rates(torch, hsq, W):
             "decode_hbm_frac": (in_b + code_b) / (td * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "relmse_k": rel,
         }
+        if label == "4bit":
+            # pre-RoPE archive fetch: the keys dequantised and rotated to
+            # their positions (every head's tokens at 0 .. tokens - 1)
+            pos = torch.arange(c.tokens, dtype=torch.int32, device=dev).repeat(c.heads)
+            with torch.cuda.stream(stream):
+                hsq.decode_rope(kc, kn, bits, c.d, sk, cen, pos, ROPE_BASE,
+                                out_dtype=torch.bfloat16, **rk)
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr, stream=stream):
+                    hsq.decode_rope(kc, kn, bits, c.d, sk, cen, pos, ROPE_BASE,
+                                    out_dtype=torch.bfloat16, **rk)
+            time_graph(torch, gr, 5, stream)
+            tr = time_graph(torch, gr, 50, stream) / 50
+            out[label].update({
+                "rope_decode_k_us": tr * 1e3, "rope_decode_out_gbs": in_b / 2 / (tr * 1e-3) / 1e9,
+                "rope_decode_hbm_frac": (in_b + code_b) / 2 / (tr * 1e-3) / 1e9 / HBM_PEAK_GBS})
+            del gr, pos
         del kc, kn, vc, vn, dk, ge, gd
     del k, v
     return out

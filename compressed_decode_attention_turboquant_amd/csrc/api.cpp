@@ -1,4 +1,5 @@
 // C ABI of libhsq: argument validation, error reporting and launches.
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -86,6 +87,28 @@ extern "C" int hsq_decode(const uint8_t* codes, const float* norms, int64_t n_ve
     return fail(HSQ_ERR_ARG, "hsq_decode: null pointer");
   DecodeJob j{codes, norms, n_vec, d, bits, signs, vecs_per_rot, n_rot, centroids, out, out_dtype};
   return check_hip(launch_decode(j, as_stream(stream)), "hsq_decode launch");
+}
+
+extern "C" int hsq_decode_rope(const uint8_t* codes, const float* norms, int64_t n_vec, int d,
+                               int bits, const uint32_t* signs, int64_t vecs_per_rot, int n_rot,
+                               const float* centroids, const int32_t* positions,
+                               double rope_base, void* out, int out_dtype, void* stream) {
+  if (n_vec < 0 || vecs_per_rot < 1 || n_rot < 1)
+    return fail(HSQ_ERR_ARG, "hsq_decode_rope: bad sizes");
+  if (!supported_d(d)) return fail(HSQ_ERR_UNSUPPORTED, "hsq_decode_rope: d must be 64 or 128");
+  if (!codec_bits(bits)) return fail(HSQ_ERR_UNSUPPORTED, "hsq_decode_rope: bits must be 2, 3 or 4");
+  if (out_dtype != HSQ_F32 && out_dtype != HSQ_BF16)
+    return fail(HSQ_ERR_UNSUPPORTED, "hsq_decode_rope: out_dtype must be HSQ_F32 or HSQ_BF16");
+  if (!(rope_base > 0.0) || !std::isfinite(rope_base))
+    return fail(HSQ_ERR_ARG, "hsq_decode_rope: rope_base must be finite and positive");
+  if (n_vec > (int64_t)UINT32_MAX)
+    return fail(HSQ_ERR_UNSUPPORTED, "hsq_decode_rope: at most 2^32 - 1 vectors per call");
+  if (n_vec == 0) return HSQ_OK;
+  if (!codes || !norms || !centroids || !positions || !out)  // signs may be null: rotation off
+    return fail(HSQ_ERR_ARG, "hsq_decode_rope: null pointer");
+  DecodeJob j{codes, norms, n_vec, d, bits, signs, vecs_per_rot, n_rot, centroids, out, out_dtype,
+              positions, rope_base};
+  return check_hip(launch_decode(j, as_stream(stream)), "hsq_decode_rope launch");
 }
 
 extern "C" int hsq_build_tiers(const void* k, const void* v, int dtype, int B, int Hkv, int T,

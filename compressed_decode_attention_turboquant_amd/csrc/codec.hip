@@ -112,60 +112,119 @@ __global__ __launch_bounds__(kWG) void encode_kernel(EncodeJob j, EncodeDivs q) 
 }
 
 
-template <int D, int BITS, int OUT, bool ROT>
+template <int D, int BITS, int OUT, bool ROT, bool ROPE>
 __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j, Div32 per_rot, Div32 n_rot) {
   constexpr int LPV = D / 8;
   constexpr int VPB = kWG / LPV;
   constexpr int CB = D * BITS / 8;
   __shared__ float cent[1 << BITS];
+  // RoPE: turns per position of each coordinate pair, base^(-2f/d) / (2 pi),
+  // as a 64-bit binary fraction (low and high words), so that the fraction of
+  // a turn at any int32 position is one wrapping integer product
+  __shared__ uint32_t turns_lo[ROPE ? D / 2 : 1], turns_hi[ROPE ? D / 2 : 1];
   if (threadIdx.x < (1 << BITS)) cent[threadIdx.x] = j.centroids[threadIdx.x];
+  if constexpr (ROPE) {
+    if (threadIdx.x < D / 2) {
+      const double t = pow(j.rope_base, -2.0 * threadIdx.x / D) * (0.5 / 3.141592653589793);
+      const uint64_t fx = (uint64_t)((t - __builtin_floor(t)) * 0x1p64);
+      turns_lo[threadIdx.x] = (uint32_t)fx;
+      turns_hi[threadIdx.x] = (uint32_t)(fx >> 32);
+    }
+  }
   __syncthreads();
   const int sub = threadIdx.x % LPV;
-  const uint32_t i = blockIdx.x * VPB + threadIdx.x / LPV;
-  const bool valid = i < j.n_vec;
-  uint32_t codes = 0;
-  float r = 0.f;
-  uint32_t sbyte = 0;
-  if (valid) {
-    const uint32_t* row = reinterpret_cast<const uint32_t*>(j.codes + (int64_t)i * CB);
-    if constexpr (BITS == 4) {
-      codes = row[sub];
-    } else if constexpr (BITS == 2) {
-      codes = (row[sub >> 1] >> (16 * (sub & 1))) & 0xffffu;
-    } else {
-      const int bit = 24 * sub;
-      const uint32_t w0 = row[bit >> 5];
-      const int off = bit & 31;
-      codes = w0 >> off;
-      if (off > 8) codes |= row[(bit >> 5) + 1] << (32 - off);
-      codes &= 0xffffffu;
+  // RoPE: lane sub holds coordinates 8 sub .. 8 sub + 7; coordinate f < d/2
+  // pairs with f + d/2, in the same slot of lane sub ^ LPV/2.  Both lanes of
+  // a pair need the same angles: the lower one takes slots 0..3, the upper
+  // one slots 4..7, and they swap the results.
+  constexpr int HALF = LPV / 2;
+  const bool upper = sub >= HALF;
+  uint32_t tlo[4] = {}, thi[4] = {};
+  if constexpr (ROPE) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int f = 8 * (sub % HALF) + (upper ? 4 : 0) + k;
+      tlo[k] = turns_lo[f];
+      thi[k] = turns_hi[f];
     }
-    r = j.norms[i];
-    if constexpr (ROT)
-      sbyte = (j.signs[rot_of(i, per_rot, n_rot) * (D / 32) + sub / 4] >> (8 * (sub % 4))) & 0xffu;
   }
-  float v[8];
+  // one block of VPB vectors per work-group; the RoPE variant, whose table
+  // costs a set-up per work-group, strides over blocks with a smaller grid
+  const uint32_t nblk = ROPE ? (uint32_t)((j.n_vec + VPB - 1) / VPB) : blockIdx.x + 1;
+  for (uint32_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    const uint64_t i64 = (uint64_t)blk * VPB + threadIdx.x / LPV;
+    const bool valid = i64 < (uint64_t)j.n_vec;
+    const uint32_t i = (uint32_t)i64;
+    uint32_t codes = 0;
+    float r = 0.f;
+    uint32_t sbyte = 0;
+    if (valid) {
+      const uint32_t* row = reinterpret_cast<const uint32_t*>(j.codes + (int64_t)i * CB);
+      if constexpr (BITS == 4) {
+        codes = row[sub];
+      } else if constexpr (BITS == 2) {
+        codes = (row[sub >> 1] >> (16 * (sub & 1))) & 0xffffu;
+      } else {
+        const int bit = 24 * sub;
+        const uint32_t w0 = row[bit >> 5];
+        const int off = bit & 31;
+        codes = w0 >> off;
+        if (off > 8) codes |= row[(bit >> 5) + 1] << (32 - off);
+        codes &= 0xffffffu;
+      }
+      r = j.norms[i];
+      if constexpr (ROT)
+        sbyte = (j.signs[rot_of(i, per_rot, n_rot) * (D / 32) + sub / 4] >> (8 * (sub % 4))) & 0xffu;
+    }
+    float v[8];
 #pragma unroll
-  for (int a = 0; a < 8; ++a) v[a] = cent[(codes >> (BITS * a)) & ((1u << BITS) - 1)];
-  if constexpr (ROT) fwht8xlanes<LPV>(v, sub);
-  // 1 / sqrt(d) is a compile-time constant: one multiply, not a division
-  const float s = ROT ? r * (1.f / __builtin_sqrtf((float)D)) : r;
+    for (int a = 0; a < 8; ++a) v[a] = cent[(codes >> (BITS * a)) & ((1u << BITS) - 1)];
+    if constexpr (ROT) fwht8xlanes<LPV>(v, sub);
+    // 1 / sqrt(d) is a compile-time constant: one multiply, not a division
+    const float s = ROT ? r * (1.f / __builtin_sqrtf((float)D)) : r;
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
-    v[a] = __uint_as_float(__float_as_uint(v[a] * s) ^ (((sbyte >> a) & 1u) << 31));
-  if (!valid) return;
-  if constexpr (OUT == HSQ_F32) {
-    float4* o = reinterpret_cast<float4*>(static_cast<float*>(j.out) + (int64_t)i * D + 8 * sub);
-    o[0] = make_float4(v[0], v[1], v[2], v[3]);
-    o[1] = make_float4(v[4], v[5], v[6], v[7]);
-  } else {
-    // round to nearest even, two values per conversion instruction
-    uint32_t w[4];
+    for (int a = 0; a < 8; ++a)
+      v[a] = __uint_as_float(__float_as_uint(v[a] * s) ^ (((sbyte >> a) & 1u) << 31));
+    if constexpr (ROPE) {
+      const int32_t p = valid ? j.pos[i] : 0;
+      const uint32_t pu = (uint32_t)p;
+      float sn[8], cs[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v[2 * k], v[2 * k + 1]}, bf16x2));
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(j.out) + (int64_t)i * D + 8 * sub) =
-        make_uint4(w[0], w[1], w[2], w[3]);
+      for (int k = 0; k < 4; ++k) {
+        // top word of p * turns mod 2^64: the fraction of a turn in units
+        // of 2^-32 (a negative p is pu - 2^32, which takes tlo off that word)
+        const uint32_t top = __umulhi(pu, tlo[k]) + pu * thi[k] - (p < 0 ? tlo[k] : 0u);
+        const float rev = (float)top * 0x1p-32f;
+        // the hardware sine and cosine take their argument in turns
+        const float s1 = __builtin_amdgcn_sinf(rev), c1 = __builtin_amdgcn_cosf(rev);
+        const float s2 = xor_lane<HALF>(s1), c2 = xor_lane<HALF>(c1);
+        sn[k] = upper ? s2 : s1;
+        cs[k] = upper ? c2 : c1;
+        sn[k + 4] = upper ? s1 : s2;
+        cs[k + 4] = upper ? c1 : c2;
+      }
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        const float partner = xor_lane<HALF>(v[a]);
+        v[a] = v[a] * cs[a] + (upper ? partner : -partner) * sn[a];
+      }
+    }
+    if (valid) {
+      if constexpr (OUT == HSQ_F32) {
+        float4* o = reinterpret_cast<float4*>(static_cast<float*>(j.out) + (int64_t)i * D + 8 * sub);
+        o[0] = make_float4(v[0], v[1], v[2], v[3]);
+        o[1] = make_float4(v[4], v[5], v[6], v[7]);
+      } else {
+        // round to nearest even, two values per conversion instruction
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          w[k] = __builtin_bit_cast(uint32_t,
+                                    __builtin_convertvector(f32x2{v[2 * k], v[2 * k + 1]}, bf16x2));
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(j.out) + (int64_t)i * D + 8 * sub) =
+            make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
   }
 }
 
@@ -191,18 +250,26 @@ hipError_t encode_dt(const EncodeJob& j, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, int BITS, bool ROT>
-hipError_t decode_dt(const DecodeJob& j, hipStream_t s) {
+template <int D, int BITS, bool ROT, bool ROPE>
+hipError_t decode_out(const DecodeJob& j, hipStream_t s) {
   constexpr int VPB = kWG / (D / 8);
-  const int64_t grid = (j.n_vec + VPB - 1) / VPB;
+  // the RoPE variant: at most a full chip of resident work-groups (256 CUs,
+  // 8 work-groups of 4 waves each), each striding over the blocks
+  const int64_t blocks = (j.n_vec + VPB - 1) / VPB;
+  const int64_t grid = ROPE ? std::min<int64_t>(blocks, 256 * 8) : blocks;
   const Div32 per_rot = make_div32(j.vecs_per_rot), n_rot = make_div32(j.n_rot);
   if (j.out_dtype == HSQ_F32)
-    hipLaunchKernelGGL((decode_kernel<D, BITS, HSQ_F32, ROT>), dim3((unsigned)grid), dim3(kWG), 0, s, j,
-                       per_rot, n_rot);
+    hipLaunchKernelGGL((decode_kernel<D, BITS, HSQ_F32, ROT, ROPE>), dim3((unsigned)grid), dim3(kWG),
+                       0, s, j, per_rot, n_rot);
   else
-    hipLaunchKernelGGL((decode_kernel<D, BITS, HSQ_BF16, ROT>), dim3((unsigned)grid), dim3(kWG), 0, s, j,
-                       per_rot, n_rot);
+    hipLaunchKernelGGL((decode_kernel<D, BITS, HSQ_BF16, ROT, ROPE>), dim3((unsigned)grid), dim3(kWG),
+                       0, s, j, per_rot, n_rot);
   return hipGetLastError();
+}
+
+template <int D, int BITS, bool ROT>
+hipError_t decode_dt(const DecodeJob& j, hipStream_t s) {
+  return j.pos ? decode_out<D, BITS, ROT, true>(j, s) : decode_out<D, BITS, ROT, false>(j, s);
 }
 
 template <int D, bool ROT>

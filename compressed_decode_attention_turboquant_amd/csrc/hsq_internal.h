@@ -56,6 +56,10 @@ struct DecodeJob {
   const float* centroids;
   void* out;
   int out_dtype;
+  // RoPE at fetch: when pos is set, row i is rotated to position pos[i]
+  // with the rotary base rope_base after dequantisation
+  const int32_t* pos;
+  double rope_base;
 };
 hipError_t launch_decode(const DecodeJob& j, hipStream_t s);
 

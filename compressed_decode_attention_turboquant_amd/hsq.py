@@ -27,6 +27,8 @@ _SIGNATURES = {
     "hsq_workspace_bytes": ([_i, _i, _i, _i, _i, _i, _i, _i], _sz),
     "hsq_encode": ([_vp, _i, _i64, _i, _i, _vp, _i, _vp, _i64, _i, _vp, _vp, _vp, _vp], _i),
     "hsq_decode": ([_vp, _vp, _i64, _i, _i, _vp, _i64, _i, _vp, _vp, _i, _vp], _i),
+    "hsq_decode_rope": ([_vp, _vp, _i64, _i, _i, _vp, _i64, _i, _vp, _vp, _c.c_double, _vp, _i,
+                         _vp], _i),
     "hsq_build_tiers": ([_vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _vp, _i, _i, _vp, _vp, _vp, _vp,
                          _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i),
     "hsq_route_topk": ([_vp, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp, _f, _i, _i, _vp, _vp, _vp,
@@ -168,6 +170,24 @@ def decode(codes, norms, bits, d, signs, centroids, vecs_per_rot=None, n_rot=1,
                             n_vec, d, bits, _dev(signs, torch.int32, "signs"), vecs_per_rot,
                             n_rot, _dev(centroids, torch.float32, "centroids"), _dev(out),
                             _dtype_code(out), _stream()))
+    return out
+
+
+def decode_rope(codes, norms, bits, d, signs, centroids, positions, rope_base,
+                vecs_per_rot=None, n_rot=1, out_dtype=torch.float32):
+    """hsq_decode_rope: dequantise, then rotate row i to position positions[i]."""
+    n_vec = norms.numel()
+    if positions.numel() != n_vec:
+        raise ValueError("positions must hold one entry per vector")
+    if vecs_per_rot is None:
+        vecs_per_rot = max(n_vec, 1)
+    out = torch.empty((n_vec, d), dtype=out_dtype, device=codes.device)
+    _check(lib().hsq_decode_rope(_dev(codes, torch.uint8, "codes"),
+                                 _dev(norms, torch.float32, "norms"), n_vec, d, bits,
+                                 _dev(signs, torch.int32, "signs"), vecs_per_rot, n_rot,
+                                 _dev(centroids, torch.float32, "centroids"),
+                                 _dev(positions, torch.int32, "positions"), float(rope_base),
+                                 _dev(out), _dtype_code(out), _stream()))
     return out
 
 

@@ -163,6 +163,29 @@ int hsq_decode(const uint8_t* codes, const float* norms, int64_t n_vec, int d, i
                void* out, int out_dtype, void* stream);
 
 /*
+ * hsq_decode_rope -- the fetch of a pre-RoPE archive: dequantise n_vec
+ * vectors as hsq_decode does, then rotate vector i to position positions[i]
+ * with the rotary position embedding
+ * [HSQ "Decode process" step 2: dequantise, then rotate to the semantic
+ * positions; RoPE as in Su et al., RoFormer (2021)].
+ *   Coordinate f < d/2 pairs with f + d/2 and turns by the angle
+ *   positions[i] * rope_base^(-2f/d):
+ *     (a, b) -> (a cos - b sin, b cos + a sin).
+ *   The angle's fraction of a turn comes from a 64-bit fixed-point product
+ *   (within 2e-7 rad at any int32 position); sine, cosine and the rotation
+ *   are fp32.
+ *   positions   int32 [n_vec] (device), any value (negative turns backwards)
+ *   rope_base   the rotary base (1e6 for the Qwen3 models), finite, > 0
+ *   everything else as for hsq_decode.
+ * Errors as hsq_decode, plus HSQ_ERR_ARG for a null positions or a bad
+ * rope_base.
+ */
+int hsq_decode_rope(const uint8_t* codes, const float* norms, int64_t n_vec, int d, int bits,
+                    const uint32_t* signs, int64_t vecs_per_rot, int n_rot,
+                    const float* centroids, const int32_t* positions, double rope_base,
+                    void* out, int out_dtype, void* stream);
+
+/*
  * hsq_build_tiers -- build L1, L2 and L3 of one layer from raw K and V
  * [HSQ "Three-tier architecture"; L2 summary = 3-bit code of the mean of the
  * group's raw vectors, standing in for the trained compressor].

@@ -160,3 +160,21 @@ def test_qjl_argument_errors_are_reported_without_launch():
     assert lg(d=32) == -2
     assert lg(bits=5) == -2
     assert lg(n=-1) == -1
+
+
+def test_decode_rope_argument_errors_are_reported_without_launch():
+    lib = hsq.lib()
+    p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+
+    def call(n=10, d=128, bits=4, base=1e6, pos=p, out_dtype=0, signs=p):
+        return lib.hsq_decode_rope(p, p, n, d, bits, signs, 1, 1, p, pos, ctypes.c_double(base),
+                                   p, out_dtype, None)
+
+    assert call(d=96) == -2 and call(bits=5) == -2 and call(out_dtype=3) == -2
+    assert call(n=1 << 32) == -2
+    assert call(n=-1) == -1
+    assert call(pos=None) == -1 and "null" in lib.hsq_last_error().decode()
+    for base in (0.0, -2.0, float("inf"), float("nan")):
+        assert call(base=base) == -1
+        assert "rope_base" in lib.hsq_last_error().decode()
+    assert call(n=0, pos=None) == 0  # empty: no-op before the pointer checks
