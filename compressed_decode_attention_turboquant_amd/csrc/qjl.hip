@@ -17,8 +17,9 @@
 // go to LDS, and the projections S u of the whole pass are one small matrix
 // product on fp32 MFMA against S, which sits in LDS for the work-group's loop
 // over the vectors.  One rotation (one S) per launch.
-// qjl_logits_kernel: R q and S R q for up to 8 query rows in LDS, then one key
-// per d/8 lanes: r <R q, c[code]> + sqrt(pi/2)/m gamma <S R q, 1 - 2 bits>.
+// qjl_logits_kernel: S staged in LDS, R q and S R q for up to 8 query rows
+// there too, then one key per d/8 lanes:
+// r <R q, c[code]> + sqrt(pi/2)/m gamma <S R q, 1 - 2 bits>.
 #include "encode_device.h"
 
 namespace hsq {
@@ -34,6 +35,26 @@ constexpr int kQWG = 256;
 template <int D>
 constexpr int kSP = D + 1;
 
+// S (d x d fp32, row-major) into LDS rows padded to d + 1 floats: coalesced
+// loads, 16 in flight per thread before their LDS writes.
+template <int D>
+__device__ __forceinline__ void stage_S(float* s_S, const float* S, int tid) {
+  constexpr int PER = D * D / kQWG;  // elements per thread
+  constexpr int BATCH = 16;
+  static_assert(PER % BATCH == 0, "whole batches");
+#pragma unroll
+  for (int b0 = 0; b0 < PER; b0 += BATCH) {
+    float t[BATCH];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) t[k] = S[(b0 + k) * kQWG + tid];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int e = (b0 + k) * kQWG + tid;
+      s_S[(e / D) * kSP<D> + e % D] = t[k];
+    }
+  }
+}
+
 template <int D, int BITS, int DT>
 __global__ __launch_bounds__(kQWG) void qjl_encode_kernel(QjlJob j) {
   constexpr int LPV = D / 8;
@@ -45,7 +66,7 @@ __global__ __launch_bounds__(kQWG) void qjl_encode_kernel(QjlJob j) {
   __shared__ float s_u[VPP * kSP<D>];
   __shared__ float s_c[16];
   const int tid = threadIdx.x, sub = tid % LPV, vl = tid / LPV;
-  for (int e = tid; e < D * D; e += kQWG) s_S[(e / D) * kSP<D> + e % D] = j.S[e];
+  stage_S<D>(s_S, j.S, tid);
   if (tid < L) s_c[tid] = j.centroids[tid];
   uint32_t tpos[NPOS];
 #pragma unroll
@@ -142,9 +163,11 @@ __global__ __launch_bounds__(kQWG) void qjl_logits_kernel(QjlLogitsJob j) {
   constexpr int CB = D * BITS / 8;
   __shared__ float s_qr[8 * D];  // R q per row
   __shared__ float s_sq[8 * D];  // S R q per row
+  __shared__ float s_S[D * kSP<D>];
   __shared__ float s_c[16];
   const int tid = threadIdx.x;
   if (tid < (1 << BITS)) s_c[tid] = j.centroids[tid];
+  stage_S<D>(s_S, j.S, tid);
   // R q = H D q / sqrt(d) for each query row (8 rows of LPV lanes)
   if (tid < 8 * LPV) {
     const int h = tid / LPV, sub = tid % LPV;
@@ -160,10 +183,13 @@ __global__ __launch_bounds__(kQWG) void qjl_logits_kernel(QjlLogitsJob j) {
     for (int a = 0; a < 8; ++a) s_qr[h * D + 8 * sub + a] = v[a] * rsqrtf((float)D);
   }
   __syncthreads();
+  // consecutive threads take consecutive rows of S: padded LDS rows keep
+  // their column reads on different banks
   for (int e = tid; e < j.n_q * D; e += kQWG) {
     const int h = e / D, row = e % D;
     float acc = 0.f;
-    for (int i = 0; i < D; ++i) acc = fmaf(j.S[row * D + i], s_qr[h * D + i], acc);
+#pragma unroll 16
+    for (int i = 0; i < D; ++i) acc = fmaf(s_S[row * kSP<D> + i], s_qr[h * D + i], acc);
     s_sq[e] = acc;
   }
   __syncthreads();
@@ -214,7 +240,9 @@ template <int D, int BITS>
 hipError_t qjl_encode_db(const QjlJob& j, hipStream_t s) {
   constexpr int VPP = kQWG / (D / 8);
   const int64_t passes = (j.n_vec + VPP - 1) / VPP;
-  const unsigned grid = (unsigned)(passes < 1024 ? passes : 1024);
+  // two work-groups fit a CU's LDS (S and the residuals, 74 KB each): one
+  // resident round of 512 stages S once each and strides over the passes
+  const unsigned grid = (unsigned)(passes < 512 ? passes : 512);
   if (j.dtype == HSQ_F32)
     hipLaunchKernelGGL((qjl_encode_kernel<D, BITS, HSQ_F32>), dim3(grid), dim3(kQWG), 0, s, j);
   else
