@@ -7,8 +7,8 @@ Tolerances: codes and norms as for the codec; a sketch bit may differ only
 where the oracle's projection (S u)_j lies within 1e-5 of zero, in rows whose
 codes all match (a code that takes the adjacent cell near a threshold changes
 that row's residual), fewer than 1e-4 of those bits; gamma to 1e-5 relative;
-logits, computed from the GPU's stored keys on both sides, to 1e-5 of the
-largest term of the sum.
+logits, computed on both sides from the same key records (written by the
+oracle's encoder), to 1e-5 of the largest term of the sum.
 """
 import numpy as np
 import pytest
@@ -92,17 +92,20 @@ def test_qjl_logits_parity(d, bits, n_q):
     print(f"[qjl logits] d={d} bits={bits} n_q={n_q}", flush=True)
     n = 777
     xt, signs, S = inputs(n, d, "bf16", seed=d * bits + n_q, student=True)
-    g, o, (c, t) = encode_both(xt, signs, S, bits)
-    codes, norms, sketch, gamma = g
+    c, t = ocb.codebook_f32(d, bits)
+    # the stored keys come from the oracle's encoder (the GPU encoder has its
+    # own parity test), so both sides read the same records
+    from oracle import codec
+    o = qjl.encode(xt, signs, t, c, S)
+    codes, norms, gamma = codec.pack(o["codes"], bits), o["norms"], o["gamma"]
+    sketch = qjl.pack_bits(o["bits"])
     rng = np.random.default_rng(n_q)
     q = rng.standard_normal((n_q, d)).astype(np.float32)
     scale = 1 / np.sqrt(d)
     f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
     got = hsq.qjl_logits(f(q), bits, f(codes), f(norms), f(sketch), f(gamma), signs_to_dev(signs),
                          f(c), f(S), float(scale)).cpu().numpy()
-    from oracle import codec
-    want = qjl.logits_qjl(q, codec.unpack(codes, bits, d), norms, qjl.unpack_bits(sketch, d),
-                          gamma, signs, c, S, scale)
+    want = qjl.logits_qjl(q, o["codes"], norms, o["bits"], gamma, signs, c, S, scale)
     # largest term: the norm times |R q| . |c| plus the correction's magnitude
     bound = scale * (np.abs(norms)[None, :] * np.abs(q).sum(1, keepdims=True) * np.abs(c).max()
                      + np.sqrt(np.pi / 2) / d * gamma[None, :] * np.abs(q @ S.T).sum(1, keepdims=True))
@@ -110,7 +113,7 @@ def test_qjl_logits_parity(d, bits, n_q):
     assert np.all(err <= 1e-5 * bound + 1e-6), float(np.max(err / (bound + 1e-30)))
     # and the correction moves the TQ-KV logit towards the exact one on average
     exact = scale * (q.astype(np.float64) @ xt.double().numpy().T)
-    tq = qjl.logits_tq(q, codec.unpack(codes, bits, d), norms, signs, c, scale)
+    tq = qjl.logits_tq(q, o["codes"], norms, signs, c, scale)
     assert abs(float(np.mean(got - exact))) <= abs(float(np.mean(tq - exact))) + 3 * float(
         np.std(got - exact)) / np.sqrt(got.size)
 
