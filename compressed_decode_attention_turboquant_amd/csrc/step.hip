@@ -971,25 +971,35 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
         f32x4 x[kMaxG];
 #pragma unroll
         for (int h = 0; h < kMaxG; ++h)
-          x[h] = *reinterpret_cast<const f32x4*>(logits + min(h, hl) * ngp + g0);
+          if (h <= hl) x[h] = *reinterpret_cast<const f32x4*>(logits + h * ngp + g0);
         __builtin_amdgcn_sched_barrier(0);
         f32x4 vmax = x[0], vsum = x[0];
 #pragma unroll
         for (int h = 1; h < kMaxG; ++h) {
-          vmax = f32x4{fmaxf(vmax[0], x[h][0]), fmaxf(vmax[1], x[h][1]),
-                       fmaxf(vmax[2], x[h][2]), fmaxf(vmax[3], x[h][3])};
-          if (h <= hl) vsum += x[h];  // wave-uniform
+          if (h <= hl) {  // wave-uniform
+            vmax = f32x4{__builtin_amdgcn_fmed3f(vmax[0], x[h][0], kPosInf),
+                         __builtin_amdgcn_fmed3f(vmax[1], x[h][1], kPosInf),
+                         __builtin_amdgcn_fmed3f(vmax[2], x[h][2], kPosInf),
+                         __builtin_amdgcn_fmed3f(vmax[3], x[h][3], kPosInf)};
+            vsum += x[h];
+          }
         }
         u32x4 k4;
+        const bool want_mean = a.agg != HSQ_AGG_MAX;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bool ok = g0 + e < a.ng;
-          const float v = (a.agg == HSQ_AGG_MAX) ? vmax[e] : vsum[e] * inv_g;
+          const float v = want_mean ? vsum[e] * inv_g : vmax[e];
           k4[e] = ok ? fkey(v) : 0u;
-          if (ok) {
-            if (hsel) atomicAdd(&hist[score_bucket(k4[e], lo, bscale)], 1);
-            if (a.scores_out) a.scores_out[(size_t)unit * a.ng + g0 + e] = v;
-          }
+          // branch-free: a slot past the end adds 0 to bucket 0
+          if (hsel) atomicAdd(&hist[ok ? score_bucket(k4[e], lo, bscale) : 0], ok ? 1 : 0);
+        }
+        if (a.scores_out) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (g0 + e < a.ng)
+              a.scores_out[(size_t)unit * a.ng + g0 + e] =
+                  want_mean ? vsum[e] * inv_g : vmax[e];
         }
         *reinterpret_cast<u32x4*>(keys + g0) = k4;
       }
