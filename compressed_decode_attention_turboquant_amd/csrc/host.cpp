@@ -118,13 +118,11 @@ int codebook(int d, int bits, float* centroids, float* thresholds) {
     c[L - 1 - j] = m;
     c[j] = -m;
   }
-  // stored codebook: centroids rounded to fp32 and then to fp16 (the
-  // precision in which dequantised values enter the matrix products);
-  // thresholds are the midpoints of adjacent stored centroids (exact in fp32),
-  // so counting thresholds is nearest-stored-centroid quantisation
-  for (int j = 0; j < L; ++j) centroids[j] = (float)(_Float16)(float)c[j];
-  for (int j = 0; j < L - 1; ++j)
-    thresholds[j] = (float)(0.5 * ((double)centroids[j] + (double)centroids[j + 1]));
+  // stored codebook: the fixed point's centroids and its thresholds (the
+  // fp64 midpoints), each rounded to the nearest fp32, so the stored tables
+  // satisfy both Lloyd conditions to fp32 rounding
+  for (int j = 0; j < L; ++j) centroids[j] = (float)c[j];
+  for (int j = 0; j < L - 1; ++j) thresholds[j] = (float)(0.5 * (c[j] + c[j + 1]));
   return HSQ_OK;
 }
 

@@ -224,12 +224,23 @@ __device__ __forceinline__ uint32_t lds_at(const uint32_t* base, uint32_t byte_a
   return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(base) + byte_addr);
 }
 
-// 3-bit: 6-bit field e (codes e & 7, e >> 3) -> fp16 pair at dword e*32 + l%32.
-// The stored centroids are fp16 values, so the pair is exact.
+// 3-bit: 6-bit field e (codes e & 7, e >> 3) -> fp16 pair at dword e*32 + l%32
+// (the stored fp32 centroids rounded to the nearest fp16).
 __device__ void build_lut3(uint32_t* lut, const float* cb, int tid) {
   // thread t fills copies 4(t&7) .. 4(t&7)+3 of entry t/8
   const int e = tid >> 3;
   const uint32_t v = h2u((_Float16)cb[e & 7], (_Float16)cb[e >> 3]);
+  *reinterpret_cast<u32x4*>(lut + e * kNC3 + 4 * (tid & 7)) = u32x4{v, v, v, v};
+}
+// 3-bit low parts for the exact router: entry e holds the fp16 pair of
+// kLoScale * (c - fp16(c)) for codes e & 7, e >> 3 (scaled so that the parts
+// stay normal fp16 numbers); hi + lo / kLoScale = c to about 2^-23 relative.
+constexpr float kLoScale = 4096.f;
+__device__ void build_lut3_lo(uint32_t* lut, const float* cb, int tid) {
+  const int e = tid >> 3;
+  const float c0 = cb[e & 7], c1 = cb[e >> 3];
+  const uint32_t v = h2u((_Float16)((c0 - (float)(_Float16)c0) * kLoScale),
+                         (_Float16)((c1 - (float)(_Float16)c1) * kLoScale));
   *reinterpret_cast<u32x4*>(lut + e * kNC3 + 4 * (tid & 7)) = u32x4{v, v, v, v};
 }
 // table address of 6-bit field e for this lane (lane4 = (lane & 31) << 2)
@@ -544,13 +555,12 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
-// Top-beta of keys[0..ng) by one wave: sel[0..beta) ascending group ids.
-// Radix select (4 passes of 8 bits, most significant first, histogram in
-// LDS) finds the key of the beta-th largest score and how many of its ties
-// to take; an in-order pass then emits the selected ids, ties resolved to the
-// lower index.  0 < beta < ng.
-__device__ void top_beta_wave(const uint32_t* keys, int ng, int beta, int* hist, int32_t* sel,
-                              int lane) {
+// Radix select of the beta-th largest of keys[0..ng) by one wave: 4 passes
+// of 8 bits, most significant first, histogram in LDS.  Returns that key;
+// need = how many of the keys equal to it rank among the beta largest.
+// 0 < beta < ng.
+__device__ uint32_t radix_kth(const uint32_t* keys, int ng, int beta, int* hist, int lane,
+                              int& need_out) {
   uint32_t pre = 0u, msk = 0u;
   int need = beta;
   for (int shift = 24; shift >= 0; shift -= 8) {
@@ -587,6 +597,19 @@ __device__ void top_beta_wave(const uint32_t* keys, int ng, int beta, int* hist,
     need -= __builtin_amdgcn_readlane(my_acc, src);
     wave_lds_sync();
   }
+  need_out = need;
+  return pre;
+}
+
+// Top-beta of keys[0..ng) by one wave: sel[0..beta) ascending group ids.
+// The radix select finds the key of the beta-th largest score and how many
+// of its ties to take; an in-order pass then emits the selected ids, ties
+// resolved to the lower index.  0 < beta < ng.  sel may alias keys (an id
+// is written at or below the position of the keys still to be read).
+__device__ void top_beta_wave(const uint32_t* keys, int ng, int beta, int* hist, int32_t* sel,
+                              int lane) {
+  int need;
+  const uint32_t pre = radix_kth(keys, ng, beta, hist, lane, need);
   int pos = 0, eq_before = 0;
   for (int g0 = 0; g0 < ng; g0 += 64) {
     const int g = g0 + lane;
@@ -632,17 +655,20 @@ __device__ __forceinline__ uint32_t field6(const uint32_t* w) {
   }
 }
 
-// QK of 16 summaries: the dequantised keys are exact fp16 values, so the
-// two-term split q_hi c + q_lo c gives fp32-accurate scores.  b: router
-// operand (column h < 8: q_hi of head h, column 8 + h: q_lo), so one MFMA
-// chain forms both products and a row rotation by 8 adds them; lanes with
-// column c < 8 return head c's logits.  kw: this lane's 3D/4 key bits
-// (summary lane&15, dims gq*D/4 ..) from bit 0.  The table reads go straight
-// into the operand registers.
-template <int D>
+// QK of 16 summaries.  b: router operand (column h < 8: q_hi of head h,
+// column 8 + h: q_lo), so one MFMA chain forms both query parts and a row
+// rotation by 8 adds them; lanes with column c < 8 return head c's logits.
+// The keys enter as fp16 roundings of the stored centroids; with EXACT a
+// second chain adds the centroids' low parts (lo table), which makes the
+// logits fp32-accurate.  Without it they differ from the exact ones by at
+// most r * ||q'||_1 * max |c - fp16(c)| (plus fp32 rounding), the bound the
+// selection works with.  kw: this lane's 3D/4 key bits (summary lane&15,
+// dims gq*D/4 ..) from bit 0.  The table reads go straight into the operand
+// registers.
+template <int D, bool EXACT>
 __device__ __forceinline__ f32x4 qk3(const uint32_t (&kw)[3], const half8 (&b)[D / 32],
-                                     const uint32_t* lut, uint32_t lane4) {
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                                     const uint32_t* lut, const uint32_t* lutlo, uint32_t lane4) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, accl = {0.f, 0.f, 0.f, 0.f};
   uint32_t a[D / 8];
 #define HSQ_FIELD_ADDR(P) a[P] = lut3_addr(field6<6 * (P)>(kw), lane4)
   HSQ_FIELD_ADDR(0); HSQ_FIELD_ADDR(1); HSQ_FIELD_ADDR(2); HSQ_FIELD_ADDR(3);
@@ -657,7 +683,13 @@ __device__ __forceinline__ f32x4 qk3(const uint32_t (&kw)[3], const half8 (&b)[D
     const half8 ak = as_h8(lds_at(lut, a[4 * m]), lds_at(lut, a[4 * m + 1]),
                            lds_at(lut, a[4 * m + 2]), lds_at(lut, a[4 * m + 3]));
     acc = mfma16(ak, b[m], acc);
+    if constexpr (EXACT) {
+      const half8 al = as_h8(lds_at(lutlo, a[4 * m]), lds_at(lutlo, a[4 * m + 1]),
+                             lds_at(lutlo, a[4 * m + 2]), lds_at(lutlo, a[4 * m + 3]));
+      accl = mfma16(al, b[m], accl);
+    }
   }
+  if constexpr (EXACT) acc += accl * (1.f / kLoScale);
   f32x4 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {  // row_ror:8 (a plain move, so that it fuses into the add)
@@ -665,6 +697,37 @@ __device__ __forceinline__ f32x4 qk3(const uint32_t (&kw)[3], const half8 (&b)[D
     r[i] = acc[i] + __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x128, 0xf, 0xf, true));
   }
   return r;
+}
+
+// Router score of group g with the stored fp32 centroids and fp32 sums (the
+// selection's tie-break for groups near the beta-th score).  The 16 lanes of
+// a row (sub = lane & 15) share the work, D/16 coordinates each; every lane
+// of the row returns the score.  qf: rotated, scaled query rows; cb: the
+// eight fp32 centroids.
+template <int D>
+__device__ __forceinline__ float exact_score(rsrc_t rk, rsrc_t rkn, int g, int sub, const float* qf,
+                                             const float* cb, int G, bool mean) {
+  constexpr int CB3 = 3 * D / 8, PER = D / 16;
+  const uint32_t bit = 3u * PER * (uint32_t)sub;
+  const uint32_t byte = min(bit >> 3, (uint32_t)(CB3 - 4));  // the dword stays inside the row
+  const uint32_t w = ld32(rk, (uint32_t)g * CB3 + byte) >> (bit - 8u * byte);
+  const float r = __uint_as_float(ld32(rkn, (uint32_t)g * 4u));
+  float cv[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) cv[k] = cb[(w >> (3 * k)) & 7u];
+  float best = kNegInf, sum = 0.f;
+  for (int h = 0; h < G; ++h) {
+    const float* qr = qf + h * kQS<D> + PER * sub;
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc = __builtin_fmaf(qr[k], cv[k], acc);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o, 64);
+    const float lg = acc * r;
+    best = fmaxf(best, lg);
+    sum += lg;
+  }
+  return mean ? sum * (1.f / (float)G) : best;
 }
 
 // Keys of tile t (16 summaries): this lane's raw key words (D = 128: 96 bits
@@ -765,6 +828,7 @@ __host__ __device__ inline RouteLayout route_layout(int G, int ng, int beta, int
 // table at a fixed address folds into the reads' offsets.
 struct RouteLds {
   uint32_t* lut3;   // 64 * kNC3 words
+  uint32_t* lut3lo; // low parts, 64 * kNC3 words (exact router only)
   float* qf;        // rotated query rows, kMaxG * kQS<D>
   float* logits;
   uint32_t* keys;
@@ -780,6 +844,7 @@ __device__ __forceinline__ RouteLds route_lds(char* base, const RouteLayout& r, 
                                               float* qf, float* dummy, float* scratch) {
   RouteLds L;
   L.lut3 = lut3;
+  L.lut3lo = nullptr;
   L.qf = qf;
   L.logits = reinterpret_cast<float*>(base + r.logits);
   L.keys = reinterpret_cast<uint32_t*>(base + r.keys);
@@ -797,7 +862,7 @@ __device__ __forceinline__ RouteLds route_lds(char* base, const RouteLayout& r, 
 // per wave in *st_out (reference maximum including the summary bias) for
 // the attend phase of the same work-group to continue.
 // recoff: if not null, LDS table that receives g * rec for selection slot s.
-template <int D>
+template <int D, bool EXACT>
 __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, float* part_out,
                                            Softmax<D>* st_out, int32_t* recoff, uint32_t rec,
                                            int unit) {
@@ -805,6 +870,7 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   __shared__ float s_cb[8];
   __shared__ float s_lo[kWaves], s_hi[kWaves];
   __shared__ float s_mh[kWaves][kMaxG];
+  __shared__ float s_rn[kWaves];  // largest key norm seen by each wave
   const int ngp = (a.ng + 15) & ~15;
   float* qf = L.qf;
   float* logits = L.logits;
@@ -849,6 +915,7 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   for (int b = tid; b < 256; b += kThreads) hist[b] = 0;
   lds_barrier();
   build_lut3(L.lut3, s_cb, tid);
+  if constexpr (EXACT) build_lut3_lo(L.lut3lo, s_cb, tid);
   half8 qb[D / 32];
   router_operands<D>(qf, lane, qb);
   lds_barrier();
@@ -858,7 +925,7 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   // lanes that hold no head's logits store into a dummy slot (no branch)
   const bool writer = c < a.G;
   float* lw = writer ? logits + c * ngp + 4 * gq : L.dummy + 4 * lane;
-  float blo = kPosInf, cmax = kNegInf;
+  float blo = kPosInf, cmax = kNegInf, rn = 0.f;
   // rows of tile t past the last group (only the last tile has any)
   auto tail_rows = [&](int t) -> uint32_t {
     const int valid = a.ng - (16 * t + 4 * gq);
@@ -872,7 +939,8 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
           const int t = wave + i * kWaves;
           uint32_t kw[3];
           key_bits<D>(T.kw, lane, kw);
-          f32x4 lg = qk3<D>(kw, qb, lut3, lane4) * T.kn;
+          f32x4 lg = qk3<D, EXACT>(kw, qb, lut3, L.lut3lo, lane4) * T.kn;
+          if constexpr (!EXACT) rn = max3f(max3f(rn, T.kn[0], T.kn[1]), T.kn[2], T.kn[3]);
           *reinterpret_cast<f32x4*>(lw + (writer ? 16 * t : 0)) = lg;
           // a lower bound of every score (max or mean over heads of these
           // logits); the heads' maxima below bound them from above
@@ -889,9 +957,11 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
   cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
   const float whi = wave_max(writer ? cmax : kNegInf);  // this wave's largest logit
+  if constexpr (!EXACT) rn = wave_max(rn);
   if (lane == 0) {
     s_lo[wave] = blo;
     s_hi[wave] = whi;
+    s_rn[wave] = rn;
   }
   if (gq == 0 && writer) s_mh[wave][c] = cmax;
   // Phase 2.  Seven waves stream the values of ALL summaries into their
@@ -994,7 +1064,7 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
           // branch-free: a slot past the end adds 0 to bucket 0
           if (hsel) atomicAdd(&hist[ok ? score_bucket(k4[e], lo, bscale) : 0], ok ? 1 : 0);
         }
-        if (a.scores_out) {
+        if (EXACT && a.scores_out) {  // only the exact router's scores are written
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if (g0 + e < a.ng)
@@ -1016,23 +1086,97 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
     }
     wave_lds_sync();
 
-    // (2b) the threshold bucket and how many of its groups to take.  At most
-    // 64 groups in it: rank them here.  More (heavy ties): radix select.
-    int bt = 0, need = 0;
-    bool fallback = false;
+    // (2b) theta: the key of the beta-th largest computed score.  The
+    // histogram gives its bucket; the bucket's groups (at most 64) are
+    // ranked exactly by (key descending, index ascending); more (heavy
+    // ties): radix select.
+    uint32_t theta = 0u;
     if (hsel) {
+      int bt, need;
       hist_threshold(hist, a.beta, lane, bt, need);
-      fallback = __builtin_amdgcn_readfirstlane(hist[bt]) > 64;
-      if (fallback) top_beta_wave(keys, a.ng, a.beta, hist, sel, lane);
+      if (__builtin_amdgcn_readfirstlane(hist[bt]) > 64) {
+        int nd;
+        theta = radix_kth(keys, a.ng, a.beta, hist, lane, nd);
+      } else {
+        int nc = 0;
+        for (int w0 = 0; w0 < words; w0 += 64) {
+          // the word's eight reads go out together (lanes past the last
+          // word read the last one and keep no bits)
+          const int w = w0 + lane, wr = min(w, words - 1);
+          u32x4 k4[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) k4[q] = *reinterpret_cast<const u32x4*>(keys + 32 * wr + 4 * q);
+          __builtin_amdgcn_sched_barrier(0);
+          uint32_t inb = 0u;
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const bool in = 32 * w + 4 * q + e < a.ng;
+              inb |= (in && score_bucket(k4[q][e], lo, bscale) == bt) ? 1u << (4 * q + e) : 0u;
+            }
+          int total;
+          int pos = nc + wave_excl_scan(__popc(inb), lane, total);
+          while (inb) {
+            const int g = 32 * w + __ffs(inb) - 1;
+            cand[pos++] = make_uint2((uint32_t)g, keys[g]);
+            inb &= inb - 1u;
+          }
+          nc += total;
+        }
+        wave_lds_sync();
+        const uint2 me = lane < nc ? cand[lane] : make_uint2(0u, 0u);
+        int rank = 0;
+        for (int j = 0; j < nc; ++j) {
+          const uint32_t og = __builtin_amdgcn_readlane(me.x, j);
+          const uint32_t ok = __builtin_amdgcn_readlane(me.y, j);
+          rank += (ok > me.y) || (ok == me.y && og < me.x);
+        }
+        const uint64_t at = __builtin_amdgcn_ballot_w64(lane < nc && rank == need - 1);
+        theta = __builtin_amdgcn_readlane(me.y, __ffsll((unsigned long long)at) - 1);
+        wave_lds_sync();
+      }
     }
-    const bool rank_here = hsel && !fallback;
-    // bitmap word w (lane w % 64): groups in buckets above bt, and the groups
-    // of bucket bt
+    // (2c) The band.  Without the exact router a computed score s differs
+    // from the exact one by at most bnd, so the beta-th exact score lies
+    // within bnd of theta: groups above theta + 2 bnd are taken, groups below
+    // theta - 2 bnd are not, and the groups between (the band; with the
+    // exact router, bnd = 0 and the band is theta's ties) are ranked by
+    // their exact scores (key descending, index ascending).
+    const bool mean = a.agg != HSQ_AGG_MAX;
+    float bnd = 0.f;
+    if constexpr (!EXACT) {
+      if (hsel) {
+        // bnd = r_max * max_h ||q'_h||_1 * (max |c - fp16(c)| + c_max 2^-14):
+        // the fp16 centroids, plus the fp32 rounding of the MFMA sums and of
+        // the query split (both far below 2^-14 of the terms' magnitudes)
+        float rmax = 0.f;
+        for (int w = 0; w < kWaves; ++w) rmax = fmaxf(rmax, s_rn[w]);
+        float qn = 0.f;
+        for (int h = 0; h < a.G; ++h) {
+          float sabs = 0.f;
+          for (int i = lane; i < D; i += 64) sabs += fabsf(qf[h * kQS<D> + i]);
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) sabs += __shfl_xor(sabs, o, 64);
+          qn = fmaxf(qn, sabs);
+        }
+        const float cl = lane < 8 ? s_cb[lane] : 0.f;
+        const float dl = wave_max(fabsf(cl - (float)(_Float16)cl));
+        const float cm = wave_max(fabsf(cl));
+        bnd = rmax * qn * (dl + cm * 0x1p-14f) * 1.0625f;
+      }
+    }
+    const float tf = key_float(theta);
+    const float tup = tf + 2.f * bnd, tdn = tf - 2.f * bnd;
+    // a bound that is not finite (overflowing inputs) puts every group in
+    // the band
+    const bool fin = __builtin_isfinite(tup) && __builtin_isfinite(tdn);
+    const uint32_t khi = EXACT ? theta : (fin ? fkey(tup) : 0xffffffffu);
+    const uint32_t klo = EXACT ? theta : (fin ? fkey(tdn) : 0u);
+    // bitmap word w (lane w % 64): groups above the band, and the band's
     auto word_bits = [&](int w, uint32_t& above, uint32_t& inb) {
       above = 0u;
       inb = 0u;
-      // the word's eight reads go out together (lanes past the last word
-      // read the last one and keep no bits)
       const int wr = min(w, words - 1);
       u32x4 k4[8];
 #pragma unroll
@@ -1042,47 +1186,79 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
       for (int q = 0; q < 8; ++q) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int b = score_bucket(k4[q][e], lo, bscale);
+          const uint32_t k = k4[q][e];
           const bool in = 32 * w + 4 * q + e < a.ng;
-          above |= (in && b > bt) ? 1u << (4 * q + e) : 0u;
-          inb |= (in && b == bt) ? 1u << (4 * q + e) : 0u;
+          above |= (in && k > khi) ? 1u << (4 * q + e) : 0u;
+          inb |= (in && k >= klo && k <= khi) ? 1u << (4 * q + e) : 0u;
         }
       }
     };
-    // the threshold bucket's groups, lane i holding the i-th (at most 64);
-    // the first 64 words' above-threshold bits are kept for the emission
+    // the band's groups, lane i holding the i-th (when at most 64); the
+    // first 64 words' above-band bits are kept for the emission
     uint2 me = make_uint2(0u, 0u);
     uint32_t above0 = 0u;
-    int nc = 0;
-    if (rank_here) {
+    int nb = 0, n_above = 0;
+    if (hsel) {
       for (int w0 = 0; w0 < words; w0 += 64) {
         uint32_t above, inb;
         word_bits(w0 + lane, above, inb);
         if (w0 == 0) above0 = above;
+        int tot_a;
+        wave_excl_scan(__popc(above), lane, tot_a);
+        n_above += tot_a;
         int total;
-        int pos = nc + wave_excl_scan(__popc(inb), lane, total);
+        int pos = nb + wave_excl_scan(__popc(inb), lane, total);
         while (inb) {
-          const int g = 32 * (w0 + lane) + __ffs(inb) - 1;
-          cand[pos++] = make_uint2((uint32_t)g, keys[g]);
+          if (pos < 64) cand[pos] = make_uint2((uint32_t)(32 * (w0 + lane) + __ffs(inb) - 1), 0u);
+          ++pos;
           inb &= inb - 1u;
         }
-        nc += total;
+        nb += total;
       }
       wave_lds_sync();
-      if (lane < nc) me = cand[lane];
     }
-    // rank by (key descending, index ascending): the first `need` are taken
+    const bool fallback = hsel && nb > 64;
+    const int sub = lane & 15, row = lane >> 4;
+    if (hsel && !fallback) {
+      // exact keys of the band's groups, four groups per pass (16 lanes each)
+      for (int j0 = 0; j0 < nb; j0 += 4) {
+        const int j = min(j0 + row, nb - 1);
+        const int g = (int)cand[j].x;
+        uint32_t k;
+        if constexpr (EXACT)
+          k = keys[g];
+        else
+          k = fkey(exact_score<D>(rk, rkn, g, sub, qf, s_cb, a.G, mean));
+        if (sub == 0 && j0 + row < nb) cand[j].y = k;
+      }
+      wave_lds_sync();
+      if (lane < nb) me = cand[lane];
+    } else if (fallback) {
+      // heavy ties: every group's exact key, then the radix select emits
+      if constexpr (!EXACT) {
+        for (int g0 = 0; g0 < a.ng; g0 += 4) {
+          const int g = min(g0 + row, a.ng - 1);
+          const uint32_t k = fkey(exact_score<D>(rk, rkn, g, sub, qf, s_cb, a.G, mean));
+          if (sub == 0 && g0 + row < a.ng) keys[g] = k;
+        }
+        wave_lds_sync();
+      }
+      top_beta_wave(keys, a.ng, a.beta, hist, sel, lane);
+    }
+    // rank the band by (exact key descending, index ascending): the first
+    // beta - n_above are taken
     bool chosen = false;
-    if (rank_here) {
+    if (hsel && !fallback) {
       int rank = 0;
-      for (int j = 0; j < nc; ++j) {
+      for (int j = 0; j < nb; ++j) {
         const uint32_t og = __builtin_amdgcn_readlane(me.x, j);
         const uint32_t ok = __builtin_amdgcn_readlane(me.y, j);
         rank += (ok > me.y) || (ok == me.y && og < me.x);
       }
-      chosen = lane < nc && rank < need;
+      chosen = lane < nb && rank < a.beta - n_above;
     }
     const uint64_t chosen_mask = __builtin_amdgcn_ballot_w64(chosen);
+    const bool rank_here = hsel && !fallback;
     // emit the selection in ascending order (the radix select already did)
     int nsel = 0;
     if (fallback) {
@@ -1180,18 +1356,25 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   combine_waves<D>(st, a.G, L.scratch, part_out, tid);
 }
 
-template <int D>
+// EXACT: the router adds the centroids' low parts (fp32-accurate scores,
+// used when the scores are returned); else the selection's band rescoring
+// keeps the selected set exact.
+template <int D, bool EXACT>
 __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
-  // dynamic layout: [qf 8*(D+4) f32][route_layout]; qf doubles as the landing
-  // slot of the phase-1 stores of lanes that hold no head; the wave-combine
-  // scratch reuses the front once the tiles are done.
+  // dynamic layout: [qf 8*(D+4) f32][landing slot of the phase-1 stores of
+  // lanes that hold no head, 64 x 16 B][route_layout]; the rotated query is
+  // read again by the selection's rescoring, so nothing else lands on it.
+  // The wave-combine scratch reuses the front once the tiles are done.
   extern __shared__ __align__(16) char smem[];
   __shared__ __align__(16) uint32_t s_lut3[64 * kNC3];
+  __shared__ __align__(16) uint32_t s_lut3lo[EXACT ? 64 * kNC3 : 4];
   float* qf = reinterpret_cast<float*>(smem);
-  const RouteLayout r = route_layout(a.G, a.ng, a.beta, kMaxG * kQS<D> * 4);
-  const RouteLds L = route_lds<D>(smem, r, s_lut3, qf, qf, qf);
+  float* dummy = reinterpret_cast<float*>(smem + kMaxG * kQS<D> * 4);
+  const RouteLayout r = route_layout(a.G, a.ng, a.beta, kMaxG * kQS<D> * 4 + 64 * 16);
+  RouteLds L = route_lds<D>(smem, r, s_lut3, qf, dummy, qf);
+  L.lut3lo = s_lut3lo;
   const int unit = blockIdx.x;
-  route_unit<D>(a, L, a.part + (size_t)unit * a.G * (D + 2), nullptr, nullptr, 0u, unit);
+  route_unit<D, EXACT>(a, L, a.part + (size_t)unit * a.G * (D + 2), nullptr, nullptr, 0u, unit);
 }
 
 // ----------------------------------------------------------- token kernel ---
@@ -1610,7 +1793,7 @@ void step_kernel(SumArgs ra, TokArgs ta) {
   // ends with a barrier: the selection and record offsets are visible and
   // the union is free; each wave's summary partial stays in st
   Softmax<D> st;
-  route_unit<D>(ra, R, nullptr, &st, recoff, (uint32_t)(N * (D + 8)), unit);
+  route_unit<D, false>(ra, R, nullptr, &st, recoff, (uint32_t)(N * (D + 8)), unit);
 
   AttendLds L;
   L.lut4 = tab;
@@ -1626,7 +1809,8 @@ void step_kernel(SumArgs ra, TokArgs ta) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t summary_smem(int D, const StepShape& s) {
-  const size_t body = (size_t)route_layout(s.G, s.n_groups, s.beta, kMaxG * (D + 4) * 4).end;
+  const size_t body =
+      (size_t)route_layout(s.G, s.n_groups, s.beta, kMaxG * (D + 4) * 4 + 64 * 16).end;
   const size_t comb = (size_t)kWaves * kMaxG * (D + 2) * 4;
   return std::max(body, comb);
 }
@@ -1695,8 +1879,12 @@ hipError_t summary_d(const StepShape& s, const StepTensors& t, const Workspace& 
   a.scores_out = scores_out;
   a.idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + w.idx_off);
   a.part = reinterpret_cast<float*>(ws + w.part_off);
-  hipLaunchKernelGGL(summary_kernel<D>, dim3((unsigned)(s.B * s.Hkv)), dim3(kThreads),
-                     summary_smem(D, s), st, a);
+  if (scores_out)
+    hipLaunchKernelGGL((summary_kernel<D, true>), dim3((unsigned)(s.B * s.Hkv)), dim3(kThreads),
+                       summary_smem(D, s), st, a);
+  else
+    hipLaunchKernelGGL((summary_kernel<D, false>), dim3((unsigned)(s.B * s.Hkv)), dim3(kThreads),
+                       summary_smem(D, s), st, a);
   return hipGetLastError();
 }
 

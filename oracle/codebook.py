@@ -118,15 +118,16 @@ def distortion(c, thr, d):
 def codebook_f32(d, bits):
     """The stored codebook the codec consumes, as fp32 arrays.
 
-    Centroids: the Lloyd-Max fixed point rounded to fp32 and then to fp16
-    (round to nearest even each time), the precision in which dequantised
-    values enter the matrix products.  Thresholds: the midpoints of adjacent
-    stored centroids, which are exact in fp32, so that counting the
-    thresholds below y is nearest-stored-centroid quantisation.
+    The pages fix the codebook (the Beta Lloyd-Max fixed point) but not its
+    storage precision; both tables are the fixed point's own values rounded
+    to the nearest fp32: centroids c_j, and thresholds (c_j + c_{j+1}) / 2
+    formed in fp64 before the rounding.  The stored tables therefore satisfy
+    both Lloyd conditions to fp32 rounding.  Exact odd symmetry survives the
+    rounding, so the middle threshold is exactly 0.
     """
-    c, _ = lloyd_max(d, bits)
-    c32 = c.astype(np.float32).astype(np.float16).astype(np.float32)
-    t32 = (0.5 * (c32[:-1].astype(np.float64) + c32[1:].astype(np.float64))).astype(np.float32)
+    c, t = lloyd_max(d, bits)
+    c32 = c.astype(np.float32)
+    t32 = t.astype(np.float32)
     c32.setflags(write=False)
     t32.setflags(write=False)
     return c32, t32

@@ -98,7 +98,10 @@ def encode(x, sign_words, thresholds):
         hx = (x * sign_vector(sign_words, d)[None, :]) @ hadamard(d).T
         y[nz] = hx[nz] / (np.sqrt(d) * r[nz, None])
     t = np.asarray(thresholds, dtype=np.float32).astype(np.float64)
-    codes = np.sum(y[:, :, None] > t[None, None, :], axis=2).astype(np.uint8)
+    if np.any(np.diff(t) <= 0):
+        raise ValueError("thresholds must be strictly ascending")
+    # code = #{j : t_j < y}: for ascending t, the left insertion point of y
+    codes = np.searchsorted(t, y, side="left").astype(np.uint8)
     return codes, r.astype(np.float32), y
 
 

@@ -119,3 +119,55 @@ def decode_step_unit(q_heads, unit, group_n, d, k_signs, v_signs, cb4, cb3, beta
     out = hsq_attention_unit(q_heads, deq, unit["l3"], sel, group_n, d, k_signs, v_signs,
                              cb4, scale, summary_bias)
     return out, sel, scores
+
+
+def decode_step_from_raw(q_heads, k_raw, v_raw, l1_pos, groups, k_signs, v_signs, cb4, cb3,
+                         beta, scale, agg="max", summary_bias=0.0, sel=None):
+    """Route + top-beta + attention for one unit straight from its raw K and V.
+
+    The same result as tiers.build_unit followed by decode_step_unit: every
+    vector is encoded on its own, so encoding only the vectors the step reads
+    (the L1 tokens, the group summaries and the tokens of the fetched groups)
+    changes nothing.  sel, if given, is the fetched set the attention uses
+    (the oracle's own top-beta is still computed and returned).
+
+    Returns (out [G, d], oracle selection, scores, l2k) with l2k a dict of
+    the summary keys' codes, rotated unit vectors y and norms.
+    """
+    k = codec.to_f64(k_raw)
+    v = codec.to_f64(v_raw)
+    groups = np.asarray(groups, dtype=np.int64)
+    l1_pos = np.asarray(l1_pos, dtype=np.int64)
+    ng, gn = groups.shape
+    d = k.shape[1]
+
+    def deq(x, signs, cbk, bits):
+        c, n, y = codec.encode(x, signs, cbk[1])
+        c = codec.unpack(codec.pack(c, bits), bits, d)
+        return codec.decode(c, n, signs, cbk[0]), c, y, n
+
+    l1k = deq(k[l1_pos], k_signs, cb4, 4)[0]
+    l1v = deq(v[l1_pos], v_signs, cb4, 4)[0]
+    if ng:
+        mk = k[groups.reshape(-1)].reshape(ng, gn, d).mean(axis=1)
+        mv = v[groups.reshape(-1)].reshape(ng, gn, d).mean(axis=1)
+    else:
+        mk = mv = np.zeros((0, d))
+    l2k, l2k_codes, l2k_y, l2k_n = deq(mk, k_signs, cb3, 3)
+    l2v = deq(mv, v_signs, cb3, 3)[0]
+    scores, _ = route_scores(q_heads, l2k, scale, agg)
+    osel = top_beta(scores, beta)
+    use = osel if sel is None else np.asarray(sel, dtype=np.int64)
+    fetched = np.zeros(ng, dtype=bool)
+    fetched[use] = True
+    pos = groups[use].reshape(-1)
+    kf = deq(k[pos], k_signs, cb4, 4)[0]
+    vf = deq(v[pos], v_signs, cb4, 4)[0]
+    keys = np.concatenate([l1k, l2k[~fetched], kf], axis=0)
+    vals = np.concatenate([l1v, l2v[~fetched], vf], axis=0)
+    bias = np.concatenate([np.zeros(l1k.shape[0]),
+                           np.full(int((~fetched).sum()), float(summary_bias)),
+                           np.zeros(kf.shape[0])])
+    out = np.stack([softmax_attention(qh, keys, vals, scale, bias) for qh in q_heads])
+    return out, osel, scores, {"codes": l2k_codes, "y": l2k_y, "n": l2k_n}
+

@@ -23,9 +23,10 @@ def signs_to_dev(words, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(words).view(np.int32)).to(device)
 
 
-def compare_codes(gpu_packed, ora_codes, ora_y, thresholds, bits, d, label=""):
+def compare_codes(gpu_packed, ora_codes, ora_y, thresholds, bits, d, label="", fraction=True):
     """Assert the GPU's packed codes equal the oracle's except near thresholds.
-    Returns (mismatches, total)."""
+    fraction=False leaves the "fewer than 1e-5 of the total" part to the
+    caller, which applies it to a whole workload.  Returns (mismatches, total)."""
     g = codec.unpack(np.asarray(gpu_packed).reshape(-1, bits * d // 8), bits, d)
     o = np.asarray(ora_codes).reshape(-1, d)
     y = np.asarray(ora_y).reshape(-1, d)
@@ -36,7 +37,7 @@ def compare_codes(gpu_packed, ora_codes, ora_y, thresholds, bits, d, label=""):
         dist = np.min(np.abs(y[bad][:, None] - t[None, :]), axis=1)
         assert np.all(dist < CODE_BAND), (
             f"{label}: {n_bad} code mismatches, max threshold distance {dist.max():.3e}")
-        assert n_bad < CODE_FRACTION * o.size or n_bad <= 1, (
+        assert not fraction or n_bad < CODE_FRACTION * o.size, (
             f"{label}: {n_bad} near-threshold mismatches of {o.size}")
     return n_bad, o.size
 

@@ -138,3 +138,45 @@ def test_build_tiers_parity(wl, T, B):
             compare_codes(vp, u["l3v_codes"], u["l3v_y"], c4[1], 4, w.d, lab + " L3v")
             compare_norms(kn, u["l3k_n"], lab)
             compare_norms(vn, u["l3v_n"], lab)
+
+
+@pytest.mark.parametrize("bits", [4, 3])
+def test_codec_workload_all_heads(bits):
+    # The codec workload at full size: 32768 tokens x 8 heads x d = 128, bf16
+    # Student-t(3) K and V with 4 outlier channels x20 per head, one rotation
+    # per head, encoded and decoded in one call each (as timed).  Every
+    # head, 4096 sampled rows per head and K|V, against the oracle: codes
+    # under the code rule, norms to 1e-6, the bf16 decode of the GPU's codes
+    # against the oracle's dequantisation of the same codes.
+    c = W.CODEC
+    print(f"codec workload bits={bits}", flush=True)
+    k, v = W.codec_inputs(c, DEV)
+    ks, vs = W.codec_signs(c)
+    c32, t32 = ocb.codebook_f32(c.d, bits)
+    n = c.heads * c.tokens
+    rng = np.random.default_rng(31 + bits)
+    rows = np.sort(rng.choice(c.tokens, size=4096, replace=False))
+    total_bad = total = 0
+    for name, x, sg in (("K", k, ks), ("V", v, vs)):
+        codes, norms = hsq.encode(x.view(n, c.d), bits, signs_to_dev(sg),
+                                  torch.from_numpy(t32).to(DEV), vecs_per_rot=c.tokens,
+                                  n_rot=c.heads)
+        dec = hsq.decode(codes, norms, bits, c.d, signs_to_dev(sg), torch.from_numpy(c32).to(DEV),
+                         vecs_per_rot=c.tokens, n_rot=c.heads, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        gc = codes.view(c.heads, c.tokens, -1).cpu().numpy()
+        gn = norms.view(c.heads, c.tokens).cpu().numpy()
+        gd = dec.view(c.heads, c.tokens, c.d).float().cpu().numpy().astype(np.float64)
+        xh = x.cpu()
+        for h in range(c.heads):
+            oc, on, oy = codec.encode(xh[h, rows], sg[h], t32)
+            nb, tot = compare_codes(gc[h, rows], oc, oy, t32, bits, c.d, f"{name} head {h}")
+            total_bad += nb
+            total += tot
+            compare_norms(gn[h, rows], on, f"{name} head {h}")
+            want = codec.decode(codec.unpack(gc[h, rows], bits, c.d), gn[h, rows], sg[h], c32)
+            wb = torch.from_numpy(want).to(torch.bfloat16).double().numpy()
+            np.testing.assert_allclose(gd[h, rows], wb, rtol=2 ** -7,
+                                       atol=1e-6 * np.abs(want).max(), err_msg=f"{name} head {h}")
+    assert total_bad < 1e-5 * total
+    print(f"  {total_bad} near-threshold code differences of {total}", flush=True)

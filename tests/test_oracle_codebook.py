@@ -128,22 +128,33 @@ def test_monte_carlo_marginal_and_mse(d, bits, n):
     assert abs(emp - pred) / pred < 0.02
 
 
-def test_stored_tables_are_fp16_centroids_and_exact_midpoints():
-    for d, bits in ((128, 4), (128, 3), (64, 4), (64, 3)):
-        c, _ = cb.lloyd_max(d, bits)
-        c32, t32 = cb.codebook_f32(d, bits)
-        want = c.astype(np.float32).astype(np.float16).astype(np.float32)
-        np.testing.assert_array_equal(c32, want)
-        # every stored centroid is an fp16 value, within half an fp16 ulp of
-        # the fixed point
-        np.testing.assert_array_equal(c32.astype(np.float16).astype(np.float32), c32)
-        assert np.all(np.abs(c32 - c) <= np.spacing(np.abs(c).astype(np.float16)).astype(np.float64))
-        # thresholds: exact midpoints (fp32 holds them exactly), symmetric
-        mid = 0.5 * (c32[:-1].astype(np.float64) + c32[1:].astype(np.float64))
-        np.testing.assert_array_equal(t32.astype(np.float64), mid)
-        np.testing.assert_array_equal(c32, -c32[::-1])
-        assert t32[len(t32) // 2] == 0.0 and np.all(np.diff(t32) > 0)
-        # the stored codebook's distortion is the fixed point's to 1e-4
-        assert abs(cb.distortion(c32.astype(np.float64), mid, d) / cb.distortion(c, 0.5 * (c[:-1] + c[1:]), d) - 1) < 1e-4
-
-
+@pytest.mark.parametrize("d,bits", [(128, 4), (128, 3), (64, 4), (64, 3), (128, 2), (64, 2)])
+def test_stored_tables_are_the_fixed_point_in_fp32(d, bits):
+    # The stored fp32 tables satisfy both Lloyd conditions to fp32 rounding:
+    # each stored centroid is the fp32 value nearest to the conditional mean
+    # of its cell under the fp64 thresholds, and each stored threshold is the
+    # fp32 value nearest to the midpoint of the fp64 centroids.  The
+    # conditional means are recomputed here by adaptive quadrature of the
+    # density (scipy.integrate.quad), not by the oracle's closed forms.
+    from scipy import integrate
+    c, t = cb.lloyd_max(d, bits)
+    c32, t32 = cb.codebook_f32(d, bits)
+    k = (d - 3) / 2.0
+    f = lambda y: (1.0 - y * y) ** k
+    edges = np.concatenate([[-1.0], t, [1.0]])
+    for j in range(len(c)):
+        m0 = integrate.quad(f, edges[j], edges[j + 1], epsabs=0, epsrel=1e-13, limit=200)[0]
+        m1 = integrate.quad(lambda y: y * f(y), edges[j], edges[j + 1], epsabs=0,
+                            epsrel=1e-13, limit=200)[0]
+        cond_mean = m1 / m0
+        # within half an fp32 ulp (plus the quadrature's own error)
+        assert abs(float(c32[j]) - cond_mean) <= 0.5 * np.spacing(np.float32(abs(cond_mean))) * 1.001 + 1e-15
+    mid = 0.5 * (c[:-1] + c[1:])
+    for j in range(len(t)):
+        assert abs(float(t32[j]) - mid[j]) <= 0.5 * float(np.spacing(np.float32(abs(mid[j])))) + 1e-300
+    # exact odd symmetry survives the rounding; middle threshold 0; order kept
+    np.testing.assert_array_equal(c32, -c32[::-1])
+    np.testing.assert_array_equal(t32, -t32[::-1])
+    assert t32[len(t32) // 2] == 0.0 and np.all(np.diff(t32) > 0) and np.all(np.diff(c32) > 0)
+    # every threshold separates its two centroids
+    assert np.all((c32[:-1] < t32) & (t32 < c32[1:]))

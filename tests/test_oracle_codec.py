@@ -58,17 +58,36 @@ def test_sign_mask_bit_order():
 
 @pytest.mark.parametrize("bits", [3, 4])
 def test_threshold_count_equals_nearest_centroid(bits):
-    # brute force: argmin_j |y - c_j|, first index on ties, with the stored
-    # centroids; the thresholds are their exact midpoints, so the two agree
-    # everywhere (a value on a midpoint is a tie and goes to the lower cell)
+    # brute force: argmin_j |y - c_j| against the fp64 fixed-point centroids,
+    # first index on ties.  The stored thresholds are the fp32 roundings of
+    # those centroids' midpoints, so the threshold count agrees with the brute
+    # force everywhere except between a midpoint and its fp32 rounding (half
+    # an fp32 ulp wide); a value exactly on a stored threshold goes to the
+    # lower cell.
     d = 128
+    c64, m64 = cb.lloyd_max(d, bits)
     c32, t32 = cb.codebook_f32(d, bits)
     rng = np.random.default_rng(7)
     y = rng.standard_normal(10 ** 6) / np.sqrt(d)
-    y[:1000] = t32[rng.integers(0, len(t32), 1000)]  # values exactly on thresholds
-    brute = np.argmin(np.abs(y[:, None] - c32.astype(np.float64)[None, :]), axis=1)
+    j = rng.integers(0, len(t32), 1000)
+    y[:1000] = t32[j]                                   # values exactly on thresholds
+    y[1000:2000] = np.nextafter(t32[j].astype(np.float64), np.inf)  # just above
+    brute = np.argmin(np.abs(y[:, None] - c64[None, :]), axis=1)
     count = np.sum(y[:, None] > t32.astype(np.float64)[None, :], axis=1)
-    np.testing.assert_array_equal(brute, count)
+    np.testing.assert_array_equal(count[:1000], j)
+    np.testing.assert_array_equal(count[1000:2000], j + 1)
+    t = t32.astype(np.float64)
+    lo = np.minimum(t, m64)
+    hi = np.maximum(t, m64)
+    between = np.any((y[:, None] >= lo[None, :]) & (y[:, None] <= hi[None, :]), axis=1)
+    assert np.all(np.abs(t - m64) <= 0.5 * np.spacing(np.abs(t32)).astype(np.float64))
+    # the generic draws (all but the planted ones, which sit closer to a
+    # threshold than fp64 can resolve against the centroids) agree except
+    # inside the half-ulp bands, where they essentially never fall
+    gen = ~between
+    gen[:2000] = False
+    np.testing.assert_array_equal(brute[gen], count[gen])
+    assert between[2000:].sum() <= 2
 
 
 def test_pack_fixed_patterns():

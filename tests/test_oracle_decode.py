@@ -183,6 +183,31 @@ def test_l1_order_invariance():
     np.testing.assert_allclose(a, b, rtol=1e-12)
 
 
+@pytest.mark.parametrize("agg,bias,given", [("max", 0.0, None), ("mean", -0.4, None),
+                                             ("max", 0.9, [0, 3, 11])])
+def test_decode_from_raw_equals_full_build(agg, bias, given):
+    # encoding only what the step reads gives the full build's result
+    u = make_unit(T=260, seed=12)
+    d, gn = u["d"], u["gn"]
+    q = np.random.default_rng(4).standard_normal((3, d))
+    scale = 1 / math.sqrt(d)
+    want, wsel, wsc = decode.decode_step_unit(q, u["unit"], gn, d, u["ks"], u["vs"], u["cb4"],
+                                             u["cb3"], 5, scale, agg, bias)
+    if given is not None:
+        deq = decode.dequant_unit(u["unit"], d, gn, u["ks"], u["vs"], u["cb4"], u["cb3"])
+        want = decode.hsq_attention_unit(q, deq, u["unit"]["l3"], given, gn, d, u["ks"], u["vs"],
+                                         u["cb4"], scale, bias)
+    got, osel, sc, l2 = decode.decode_step_from_raw(
+        q, u["k"], u["v"], u["l1"], u["groups"], u["ks"], u["vs"], u["cb4"], u["cb3"], 5, scale,
+        agg, bias, sel=given)
+    np.testing.assert_array_equal(osel, wsel)
+    np.testing.assert_array_equal(sc, wsc)
+    np.testing.assert_array_equal(l2["codes"], u["unit"]["l2k_codes"])
+    np.testing.assert_array_equal(l2["y"], u["unit"]["l2k_y"])
+    np.testing.assert_array_equal(l2["n"], u["unit"]["l2k_n"])
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-14)
+
+
 def test_planted_needle_is_routed():
     # one group's keys aligned with the query must be selected
     u = make_unit(T=400, seed=6)
@@ -231,7 +256,51 @@ def _bf_quant_dequant(x, signs_pm, H, cent):
     return [r32 * a for a in _bf_unrotate(yq, signs_pm, H)], y
 
 
-def test_brute_force_tiny_end_to_end():
+def test_route_scores_hand_worked_max_and_mean():
+    # two query heads against three summary keys, scale 1/2:
+    #   head 0: q = (1, 0): logits 0.5, 1.0, 0.0
+    #   head 1: q = (0, 2): logits 1.0, -1.0, 0.0
+    q = np.array([[1.0, 0.0], [0.0, 2.0]])
+    khat = np.array([[1.0, 1.0], [2.0, -1.0], [0.0, 0.0]])
+    s_max, lg = decode.route_scores(q, khat, 0.5, "max")
+    s_mean, _ = decode.route_scores(q, khat, 0.5, "mean")
+    np.testing.assert_array_equal(lg, [[0.5, 1.0, 0.0], [1.0, -1.0, 0.0]])
+    np.testing.assert_array_equal(s_max, [1.0, 1.0, 0.0])
+    np.testing.assert_array_equal(s_mean, [0.75, 0.0, 0.0])
+    # max: groups 0 and 1 tie, the lower index wins; mean: group 0 alone
+    assert decode.top_beta(s_max, 1).tolist() == [0]
+    assert decode.top_beta(s_mean, 1).tolist() == [0]
+    # mean, beta 2: groups 1 and 2 tie at 0, the lower index wins
+    assert decode.top_beta(s_mean, 2).tolist() == [0, 1]
+    with pytest.raises(ValueError):
+        decode.route_scores(q, khat, 0.5, "median")
+
+
+@pytest.mark.parametrize("bias", [0.0, -0.7, 1.3])
+def test_summary_bias_hand_worked(bias):
+    # one L1 token and one unfetched summary, both with key 0 (logit 0):
+    # the softmax weights are 1 and e^bias, so
+    #   out = (v_L1 + e^bias v_summary) / (1 + e^bias)
+    d, gn = 4, 8
+    deq = {"l1k": np.zeros((1, d)), "l1v": np.array([[1.0, 0.0, 0.0, 0.0]]),
+           "l2k": np.zeros((1, d)), "l2v": np.array([[0.0, 2.0, 0.0, 0.0]])}
+    l3 = np.zeros((1, gn * (d + 8)), dtype=np.uint8)
+    signs = np.zeros(1, dtype=np.uint32)
+    c4 = cb.codebook_f32(d, 4)
+    q = np.array([[0.3, -0.2, 0.5, 0.1]])
+    out = decode.hsq_attention_unit(q, deq, l3, [], gn, d, signs, signs, c4, 0.5, bias)
+    e = math.exp(bias)
+    np.testing.assert_allclose(out[0], [1.0 / (1 + e), 2.0 * e / (1 + e), 0.0, 0.0], rtol=1e-15)
+    # a fetched summary takes no bias: with the group fetched the summary is
+    # gone and the group's tokens enter unbiased
+    out_f = decode.hsq_attention_unit(q, deq, l3, [0], gn, d, signs, signs, c4, 0.5, bias)
+    # the fetched record is all-zero codes with zero norms: gn tokens with
+    # key 0 and value 0 next to the L1 token
+    np.testing.assert_allclose(out_f[0], [1.0 / (1 + gn), 0.0, 0.0, 0.0], rtol=1e-15)
+
+
+@pytest.mark.parametrize("agg,bias", [("max", 0.0), ("mean", 0.0), ("max", -0.7), ("mean", 1.3)])
+def test_brute_force_tiny_end_to_end(agg, bias):
     d, T, gn, beta = 8, 40, 4, 2
     rng = np.random.default_rng(21)
     k = rng.standard_normal((T, d))
@@ -244,7 +313,8 @@ def test_brute_force_tiny_end_to_end():
     l1, groups = tiers.tier_plan(T, 2, 5, marked, gn)
     unit = tiers.build_unit(k, v, l1, groups, ks, vs, c4, c3)
     scale = 1 / math.sqrt(d)
-    out, sel, scores = decode.decode_step_unit(q, unit, gn, d, ks, vs, c4, c3, beta, scale)
+    out, sel, scores = decode.decode_step_unit(q, unit, gn, d, ks, vs, c4, c3, beta, scale,
+                                               agg=agg, summary_bias=bias)
 
     # --- brute force ---
     H = [[1]]
@@ -275,13 +345,16 @@ def test_brute_force_tiny_end_to_end():
         sv.append(b)
     assert not near_thr
     dot = lambda a, b: sum(x * y for x, y in zip(a, b))
-    bf_scores = [max(scale * dot(qh, sk[g]) for qh in q) for g in range(ngb)]
+    if agg == "max":
+        bf_scores = [max(scale * dot(qh, sk[g]) for qh in q) for g in range(ngb)]
+    else:
+        bf_scores = [sum(scale * dot(qh, sk[g]) for qh in q) / len(q) for g in range(ngb)]
     np.testing.assert_allclose(scores, bf_scores, rtol=1e-12, atol=1e-12)
     ranked = sorted(range(ngb), key=lambda g: (-bf_scores[g], g))[:beta]
     assert sorted(ranked) == sel.tolist()
     for h, qh in enumerate(q):
         ents = [(scale * dot(qh, kh4[p]), vh4[p]) for p in sorted(l1set)]
-        ents += [(scale * dot(qh, sk[g]), sv[g]) for g in range(ngb) if g not in ranked]
+        ents += [(scale * dot(qh, sk[g]) + bias, sv[g]) for g in range(ngb) if g not in ranked]
         ents += [(scale * dot(qh, kh4[p]), vh4[p]) for g in ranked for p in grp[g]]
         m = max(e[0] for e in ents)
         w = [math.exp(e[0] - m) for e in ents]
