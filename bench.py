@@ -6,21 +6,23 @@
 A step is one decode step of one layer: router scores over the 3-bit L2
 summary keys, top-beta selection, and fused attention over L1 + unfetched
 summaries + the fetched 4-bit L3 groups, for every (sequence, kv-head) of the
-batch.  The workload is the Qwen3-14B-shaped layer (40 query / 8 kv heads,
-head dim 128, 16K context, batch 64, groups of 8, beta = 128) with the archive
-resident in HBM.  The timed loop cycles through several independent layer
-instances (about 1.55 GB of tiers) so that the 256 MB last-level cache cannot
-hold the working set, and replays a captured HIP graph so host launch latency
-stays out of the measurement.
+batch.  The headline workload is the Qwen3-14B-shaped layer (40 query / 8 kv
+heads, head dim 128, 16K context, batch 64, groups of 8, beta = 128) with the
+archive resident in HBM.  The launches cycle through eight independent layer
+instances (about 1.55 GB of tiers), so the 256 MB last-level cache cannot
+hold the working set, and run from a captured HIP graph, so host launch
+latency stays out of the measurement.  W untimed warm-up steps run first;
+then a graph of exactly K steps is timed with HIP events on its stream, R
+times (R >= 20), and the line reports the median.
 
-Prints one JSON line.  Also reported (same line): the codec encode/decode
-rates on the 32K x 8-head bf16 Student-t workload (with the pre-RoPE fetch,
-dequantise then RoPE at each token's position, and the TQ-QKV key path), the
-decode-time append
-(tier maintenance) at the headline layer's shape, the decode step with the
-L3 archive in pinned host memory (Qwen3-8B shape, 32K context, batch 8, 36
-layers, gathered over PCIe on a side stream), and the CPU oracle on a bounded
-sample of the headline workload.
+Prints one JSON line.  Also reported (same line): the Qwen3-8B 8K layer
+(batch 1, a chain of 512 layer instances), the Qwen3-8B 32K workload's 36
+layers per step with the archive in HBM and, as a PCIe-inclusive figure,
+in pinned host memory (gathered over PCIe); the codec encode/decode rates on
+the 32K x 8-head bf16 Student-t workload on buffers cycled over more than the
+last-level cache (with the pre-RoPE fetch and the TQ-QKV key path); the
+decode-time append at the headline layer's shape; and the CPU oracle on a
+sample of the headline workload, run on every host core.
 """
 import argparse
 import json
@@ -70,13 +72,16 @@ def measured_traffic(kernel):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=800)
-    p.add_argument("--warmup", type=int, default=80)
+    p.add_argument("--steps", type=int, default=20, help="layer-steps per timed graph")
+    p.add_argument("--warmup", type=int, default=5, help="untimed layer-steps before timing")
+    p.add_argument("--reps", type=int, default=20, help="timed graph replays (median reported)")
     p.add_argument("--layers", type=int, default=8, help="independent layer instances cycled")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-codec", action="store_true")
     p.add_argument("--no-cache", action="store_true", help="skip the cache-append timing")
     p.add_argument("--no-host", action="store_true", help="skip the pinned-host archive run")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the Qwen3-8B 8K and 32K (HBM archive) lines")
     p.add_argument("--only-step", action="store_true", help="headline step only (for profiling)")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (calibrates HBM byte counters)")
@@ -123,8 +128,8 @@ def codebooks(hsq, d, dev):
 
 
 def time_graph(torch, graph, reps, stream):
-    """Mean-free total time of `reps` replays, bracketed by HIP events recorded
-    on the stream the replays run on."""
+    """Total time of `reps` back-to-back replays, bracketed by HIP events
+    recorded on the stream the replays run on (ms)."""
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -135,6 +140,36 @@ def time_graph(torch, graph, reps, stream):
         e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1)
+
+
+def time_reps(torch, graph, reps, stream):
+    """Each of `reps` replays timed on its own (synchronised on both sides,
+    HIP events on the replay stream); returns the list of times in ms.  A
+    short spin kernel (torch.cuda._sleep) goes first on the stream, outside
+    the timed interval, so that the replay is queued behind the start event
+    before the GPU reaches it: the interval holds the replay's kernels, not
+    the host's submission latency."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    out = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(1_000_000)
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1))
+    return out
+
+
+def capture(torch, stream, fn):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+    return g
 
 
 def headline(args, torch, hsq, W):
@@ -156,42 +191,37 @@ def headline(args, torch, hsq, W):
     def attend(ly):
         hsq.step_attend(ly.q, ly.tiers, w.beta, ly.dks, ly.dvs, cb["cb4"], ly.ws, ly.out)
 
-    graphs = {}
     with torch.cuda.stream(stream):
         for ly in layers:  # eager runs first: also leave valid selections in every workspace
             route(ly)
             attend(ly)
             step(ly)
         stream.synchronize()
-        for name, fns in (("step", (step,)), ("route", (route,)), ("attend", (attend,))):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                for ly in layers:
-                    for fn in fns:
-                        fn(ly)
-            graphs[name] = g
-    torch.cuda.synchronize()
-    reps = max(1, math.ceil(args.steps / L))
-    wreps = max(1, math.ceil(args.warmup / L))
-    time_graph(torch, graphs["step"], wreps, stream)
+    K, Wm = max(1, args.steps), max(0, args.warmup)
+    # exactly K (timed) and W (warm-up) layer-steps, cycling the instances
+    g_steps = capture(torch, stream, lambda: [step(layers[i % L]) for i in range(K)])
+    if Wm:
+        g_warm = capture(torch, stream, lambda: [step(layers[i % L]) for i in range(Wm)])
+        time_graph(torch, g_warm, 1, stream)
     t0 = time.perf_counter()
-    ms = time_graph(torch, graphs["step"], reps, stream)
+    reps = time_reps(torch, g_steps, max(20, args.reps), stream)
     wall = time.perf_counter() - t0
-    steps = reps * L
-    ms_step = ms / steps
+    ms_step = float(np.median(reps)) / K
     two = {}
-    for name in ("route", "attend"):
-        time_graph(torch, graphs[name], max(1, wreps // 2), stream)
-        two[name] = time_graph(torch, graphs[name], reps, stream) / steps
+    for name, fn in (("route", route), ("attend", attend)):
+        g = capture(torch, stream, lambda fn=fn: [fn(ly) for ly in layers])
+        time_graph(torch, g, 2, stream)
+        two[name] = float(np.median(time_reps(torch, g, 10, stream))) / L
+        del g
     t = layers[0].tiers
     units = w.batch * w.hkv
     rb, ab = algorithmic_bytes(w, t.n1, t.ng, layers[0].beta)
     step_bytes = (rb + ab) * units
-    # the step is one kernel (step_kernel) per layer: the timed launches are it
     achieved = step_bytes / (ms_step * 1e-3) / 1e9
     kb = {"route": rb * units, "attend": ab * units}
     res = {
-        "w": w, "ms_step": ms_step, "steps": steps, "wall_s": wall,
+        "w": w, "ms_step": ms_step, "steps": K, "reps": len(reps), "wall_s": wall,
+        "rep_ms_per_step": {"min": min(reps) / K, "median": ms_step, "max": max(reps) / K},
         "value": units * w.T / (ms_step * 1e-3),
         "step_gbs": achieved,
         "kernels": {"step_kernel": {"us": ms_step * 1e3, "bytes": step_bytes, "gbs": achieved}},
@@ -201,8 +231,50 @@ def headline(args, torch, hsq, W):
         "step_bytes": step_bytes,
         "tier_bytes": t.nbytes(),
     }
-    del graphs
+    del g_steps
     return res, layers
+
+
+def layer_chain(args, torch, hsq, W, w, n_inst, label):
+    """One decode step of each of n_inst layer instances of workload w (archive
+    in HBM), launched back to back from one captured graph; the median of R
+    replays.  n_inst = w.layers for a model's layers, or a chain of
+    independent instances that overflows the last-level cache."""
+    dev = "cuda"
+    cb = codebooks(hsq, w.d, dev)
+    layers = [Layer(w, i, dev, hsq, W, cb) for i in range(n_inst)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+
+    def step(ly):
+        hsq.decode_step(ly.q, ly.tiers, w.beta, ly.dks, ly.dvs, cb["cb4"], cb["cb3"], ws=ly.ws,
+                        out=ly.out)
+
+    with torch.cuda.stream(stream):
+        for ly in layers:
+            step(ly)
+        stream.synchronize()
+    g = capture(torch, stream, lambda: [step(ly) for ly in layers])
+    time_graph(torch, g, 2, stream)
+    reps = time_reps(torch, g, max(20, args.reps), stream)
+    ms = float(np.median(reps))
+    t = layers[0].tiers
+    units = w.batch * w.hkv
+    rb, ab = algorithmic_bytes(w, t.n1, t.ng, layers[0].beta)
+    step_bytes = (rb + ab) * units * n_inst
+    out = {
+        "workload": w.name, "what": label, "batch": w.batch, "q_heads": w.hq, "kv_heads": w.hkv,
+        "context": w.T, "group_n": w.group_n, "beta": w.beta, "n_l1": t.n1, "n_groups": t.ng,
+        "archive": "hbm", "layer_launches": n_inst, "reps": len(reps),
+        "ms_per_chain": ms, "us_per_layer_step": ms * 1e3 / n_inst,
+        "value": units * w.T * n_inst / (ms * 1e-3), "unit": "heads*tokens/s",
+        "hbm_bytes_per_chain": step_bytes, "hbm_gbs": step_bytes / (ms * 1e-3) / 1e9,
+        "hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "tier_bytes_per_layer": t.nbytes(),
+    }
+    del g, layers
+    torch.cuda.empty_cache()
+    return out
 
 
 # (label, bits, rotation on): TurboQuant at the tier widths, and the ablation's
@@ -211,42 +283,61 @@ CODEC_VARIANTS = (("4bit", 4, True), ("3bit", 3, True), ("2bit", 2, True),
                   ("plain_4bit", 4, False), ("plain_2bit", 2, False))
 
 
-def codec_rates(torch, hsq, W):
+def codec_rates(torch, hsq, W, n_sets=3, reps=20):
+    """Encode (K and V, one launch each) and decode of the codec workload.
+    The timed graphs cycle n_sets copies of the inputs and outputs (the bf16
+    inputs alone are 3 x 134 MB), so the last-level cache cannot serve a
+    launch from the previous one; per-launch-pair times are medians."""
     dev = "cuda"
     c = W.CODEC
-    k, v = W.codec_inputs(c, dev)
+    k0, v0 = W.codec_inputs(c, dev)
     ks, vs = W.codec_signs(c)
     dks = torch.from_numpy(ks.view(np.int32)).to(dev)
     dvs = torch.from_numpy(vs.view(np.int32)).to(dev)
     stream = torch.cuda.Stream()
     n = c.heads * c.tokens
-    out = {}
+    ins = [(k0.view(n, c.d), v0.view(n, c.d))] + [
+        (k0.view(n, c.d).clone(), v0.view(n, c.d).clone()) for _ in range(n_sets - 1)]
+    out = {"sets_cycled": n_sets, "bytes_cycled_in": n_sets * 2 * n * c.d * 2}
     for label, bits, rot in CODEC_VARIANTS:
         cen, thr = (torch.from_numpy(a).to(dev) for a in hsq.codebook(c.d, bits))
         sk, sv = (dks, dvs) if rot else (None, None)
         rk = dict(vecs_per_rot=c.tokens, n_rot=c.heads)
         with torch.cuda.stream(stream):
-            kc, kn = hsq.encode(k.view(n, c.d), bits, sk, thr, **rk)
-            vc, vn = hsq.encode(v.view(n, c.d), bits, sv, thr, **rk)
-            dk = hsq.decode(kc, kn, bits, c.d, sk, cen, out_dtype=torch.bfloat16, **rk)
+            codes = [(hsq.encode(ki, bits, sk, thr, **rk), hsq.encode(vi, bits, sv, thr, **rk))
+                     for ki, vi in ins]
+            decs = [(torch.empty((n, c.d), dtype=torch.bfloat16, device=dev),
+                     torch.empty((n, c.d), dtype=torch.bfloat16, device=dev)) for _ in ins]
             stream.synchronize()
-            ge = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(ge, stream=stream):
-                hsq.encode(k.view(n, c.d), bits, sk, thr, **rk)
-                hsq.encode(v.view(n, c.d), bits, sv, thr, **rk)
-            gd = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gd, stream=stream):
-                hsq.decode(kc, kn, bits, c.d, sk, cen, out_dtype=torch.bfloat16, **rk)
-                hsq.decode(vc, vn, bits, c.d, sv, cen, out_dtype=torch.bfloat16, **rk)
-        time_graph(torch, ge, 5, stream)
-        te = time_graph(torch, ge, 50, stream) / 50
-        time_graph(torch, gd, 5, stream)
-        td = time_graph(torch, gd, 50, stream) / 50
+        lib = hsq.lib()
+
+        def enc_all():
+            for (ki, vi), ((kc, kn), (vc, vn)) in zip(ins, codes):
+                for x, (cc, nn), sg in ((ki, (kc, kn), sk), (vi, (vc, vn), sv)):
+                    hsq._check(lib.hsq_encode(x.data_ptr(), hsq.HSQ_BF16, n, c.d, bits, None, 1,
+                                              sg.data_ptr() if sg is not None else None,
+                                              c.tokens, c.heads, thr.data_ptr(), cc.data_ptr(),
+                                              nn.data_ptr(), stream.cuda_stream))
+
+        def dec_all():
+            for ((kc, kn), (vc, vn)), (dk, dv) in zip(codes, decs):
+                for (cc, nn), o, sg in (((kc, kn), dk, sk), ((vc, vn), dv, sv)):
+                    hsq._check(lib.hsq_decode(cc.data_ptr(), nn.data_ptr(), n, c.d, bits,
+                                              sg.data_ptr() if sg is not None else None,
+                                              c.tokens, c.heads, cen.data_ptr(), o.data_ptr(),
+                                              hsq.HSQ_BF16, stream.cuda_stream))
+
+        ge = capture(torch, stream, enc_all)
+        gd = capture(torch, stream, dec_all)
+        time_graph(torch, ge, 2, stream)
+        te = float(np.median(time_reps(torch, ge, reps, stream))) / n_sets
+        time_graph(torch, gd, 2, stream)
+        td = float(np.median(time_reps(torch, gd, reps, stream))) / n_sets
         in_b = 2 * n * c.d * 2
         code_b = 2 * n * (c.d * bits // 8 + 4)
         # relative round-trip error of the bf16 decode (diagnostic, cf. relMSE)
-        rel = float(((dk.float() - k.view(n, c.d).float()).pow(2).sum(1) /
-                     k.view(n, c.d).float().pow(2).sum(1)).mean())
+        kf = ins[0][0].float()
+        rel = float(((decs[0][0].float() - kf).pow(2).sum(1) / kf.pow(2).sum(1)).mean())
         out[label] = {
             "encode_us": te * 1e3, "encode_in_gbs": in_b / (te * 1e-3) / 1e9,
             "encode_hbm_frac": (in_b + code_b) / (te * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -258,26 +349,33 @@ def codec_rates(torch, hsq, W):
             # pre-RoPE archive fetch: the keys dequantised and rotated to
             # their positions (every head's tokens at 0 .. tokens - 1)
             pos = torch.arange(c.tokens, dtype=torch.int32, device=dev).repeat(c.heads)
-            with torch.cuda.stream(stream):
-                hsq.decode_rope(kc, kn, bits, c.d, sk, cen, pos, ROPE_BASE,
-                                out_dtype=torch.bfloat16, **rk)
-                gr = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(gr, stream=stream):
-                    hsq.decode_rope(kc, kn, bits, c.d, sk, cen, pos, ROPE_BASE,
-                                    out_dtype=torch.bfloat16, **rk)
-            time_graph(torch, gr, 5, stream)
-            tr = time_graph(torch, gr, 50, stream) / 50
+
+            def rope_all():
+                for ((kc, kn), _), (dk, _) in zip(codes, decs):
+                    hsq._check(lib.hsq_decode_rope(kc.data_ptr(), kn.data_ptr(), n, c.d, bits,
+                                                   sk.data_ptr(), c.tokens, c.heads,
+                                                   cen.data_ptr(), pos.data_ptr(), ROPE_BASE,
+                                                   dk.data_ptr(), hsq.HSQ_BF16,
+                                                   stream.cuda_stream))
+
+            gr = capture(torch, stream, rope_all)
+            time_graph(torch, gr, 2, stream)
+            tr = float(np.median(time_reps(torch, gr, reps, stream))) / n_sets
             out[label].update({
                 "rope_decode_k_us": tr * 1e3, "rope_decode_out_gbs": in_b / 2 / (tr * 1e-3) / 1e9,
                 "rope_decode_hbm_frac": (in_b + code_b) / 2 / (tr * 1e-3) / 1e9 / HBM_PEAK_GBS})
             del gr, pos
-        del kc, kn, vc, vn, dk, ge, gd
-    del k, v
+        del codes, decs, ge, gd
+    del k0, v0, ins
+    torch.cuda.empty_cache()
     return out
 
 
-def host_archive(torch, hsq, W, steps=3):
-    """Decode step of 36 layers with the L3 archive in pinned host memory."""
+def host_archive(torch, hsq, W, reps=5):
+    """Decode step of 36 layers with the L3 archive in pinned host memory:
+    per layer the route launch, the gather of the selected records over PCIe
+    (through the device alias of the pinned archive) into HBM staging, and
+    the attend launch, as one captured graph per decode step."""
     dev = "cuda"
     w = W.QWEN3_8B_32K
     cb = codebooks(hsq, w.d, dev)
@@ -293,35 +391,21 @@ def host_archive(torch, hsq, W, steps=3):
     beta = min(w.beta, ng)
     staging = torch.empty((w.batch, w.hkv, beta, rec), dtype=torch.uint8, device=dev)
     main = torch.cuda.Stream()
-    side = torch.cuda.Stream()
 
     def one_step():
         for i, ly in enumerate(layers):
-            with torch.cuda.stream(main):
-                hsq.step_route(ly.q, ly.tiers, w.beta, ly.dks, cb["cb3"], ly.ws, idx=ly.ws_idx)
-                ev = torch.cuda.Event()
-                ev.record(main)
-            with torch.cuda.stream(side):
-                side.wait_event(ev)
-                idx = ly.ws_idx
-                hsq.gather_l3(arch.dev_ptr + i * per_layer, rec, w.batch, w.hkv, ng, idx, staging)
-                ev2 = torch.cuda.Event()
-                ev2.record(side)
-            with torch.cuda.stream(main):
-                main.wait_event(ev2)
-                hsq.step_attend(ly.q, ly.tiers, w.beta, ly.dks, ly.dvs, cb["cb4"], ly.ws, ly.out,
-                                l3=staging.data_ptr(), l3_staged=True)
+            hsq.step_route(ly.q, ly.tiers, w.beta, ly.dks, cb["cb3"], ly.ws, idx=ly.ws_idx)
+            hsq.gather_l3(arch.dev_ptr + i * per_layer, rec, w.batch, w.hkv, ng, ly.ws_idx,
+                          staging)
+            hsq.step_attend(ly.q, ly.tiers, w.beta, ly.dks, ly.dvs, cb["cb4"], ly.ws, ly.out,
+                            l3=staging.data_ptr(), l3_staged=True)
 
-    one_step()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(main)
-    for _ in range(steps):
+    with torch.cuda.stream(main):
         one_step()
-    e1.record(main)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+        main.synchronize()
+    g = capture(torch, main, one_step)
+    time_graph(torch, g, 1, main)
+    ms = float(np.median(time_reps(torch, g, reps, main)))
     link_bytes = w.layers * w.batch * w.hkv * beta * rec
     # measured pinned host -> device copy rate, for context
     hbuf = arch.view(0, min(per_layer, 1 << 30))
@@ -344,9 +428,11 @@ def host_archive(torch, hsq, W, steps=3):
         "pcie_bytes_per_step": link_bytes,
         "pcie_gbs": link_bytes / (ms * 1e-3) / 1e9,
         "pinned_h2d_copy_gbs": h2d,
+        "frac_of_pinned_copy": link_bytes / (ms * 1e-3) / 1e9 / h2d,
         "archive_gib": per_layer * w.layers / 2 ** 30,
     }
-    del layers, arch
+    del layers, arch, g
+    torch.cuda.empty_cache()
     return res
 
 
@@ -484,53 +570,111 @@ def _host_layer(w, layer, dev, hsq, W, cb, l3_dev_ptr):
     return ly
 
 
-def cpu_baseline(torch, W, layers, budget_s=12.0):
-    """The oracle (fp64 numpy) on a bounded sample of the headline workload."""
+# ---- CPU oracle baseline -------------------------------------------------
+# The worker pool is forked at start-up, before anything touches the GPU, so
+# no child ever inherits a GPU context; each worker runs the oracle on one
+# thread (one unit per host core).
+
+def _cpu_init():
+    os.environ["OMP_NUM_THREADS"] = "1"
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        pass
+
+
+def _cpu_build(arg):
+    """Oracle tiers of one unit from its raw K and V (compress time, untimed)."""
+    from oracle import codebook as ocb
+    from oracle import tiers as otiers
+    k, v, l1, g, ksg, vsg, d = arg
+    u = otiers.build_unit(k, v, l1, g, ksg, vsg, ocb.codebook_f32(d, 4), ocb.codebook_f32(d, 3))
+    return {n: u[n] for n in ("l1k", "l1k_n", "l1v", "l1v_n", "l2k", "l2k_n", "l2v", "l2v_n",
+                              "l3")}
+
+
+def _cpu_steps(arg):
+    """Oracle decode steps (route + top-beta + attention) of one unit for
+    `budget` seconds of wall time; returns (steps, start, end)."""
     from oracle import codebook as ocb
     from oracle import decode as odec
-    from oracle import tiers as otiers
+    unit, q, ksg, vsg, gn, d, beta, budget = arg
+    c4, c3 = ocb.codebook_f32(d, 4), ocb.codebook_f32(d, 3)
+    n, t0 = 0, time.time()
+    while True:
+        odec.decode_step_unit(q, unit, gn, d, ksg, vsg, c4, c3, beta, 1.0 / math.sqrt(d))
+        n += 1
+        t1 = time.time()
+        if t1 - t0 >= budget:
+            return n, t0, t1
+
+
+def cpu_workers():
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))  # at most the host share of one GPU
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def start_cpu_pool():
+    import multiprocessing as mp
+    n = cpu_workers()
+    return mp.get_context("fork").Pool(processes=n, initializer=_cpu_init), n
+
+
+def cpu_baseline(torch, W, layers, pool, n_workers, budget_s=10.0):
+    """The oracle (fp64 numpy) on n_workers units of the headline workload's
+    layer 0, one unit per host core, all running at once for budget_s."""
     w = W.QWEN3_14B_16K
-    c4, c3 = ocb.codebook_f32(w.d, 4), ocb.codebook_f32(w.d, 3)
     ly = layers[0]
-    sample = [(0, 0), (17, 3), (42, 7)]
-    units = []
+    sample = [((37 * i) % w.batch, i % w.hkv) for i in range(n_workers)]
     k, v = W.kv(w, 0, "cuda")  # layer 0 of the timed workload, regenerated from its seed
-    raw = {(b, h): (k[b, h].cpu(), v[b, h].cpu()) for (b, h) in sample}
+    build_args = []
+    for (b, h) in sample:
+        from oracle import tiers as otiers
+        l1, g = otiers.tier_plan(w.T, w.n_sink, w.n_recent, W.marked(w, b), w.group_n)
+        build_args.append((k[b, h].float().cpu().numpy(), v[b, h].float().cpu().numpy(), l1, g,
+                           ly.k_signs[h], ly.v_signs[h], w.d))
     del k, v
     torch.cuda.empty_cache()
-    for (b, h) in sample:
-        kb, vb = raw[(b, h)]
-        l1, g = otiers.tier_plan(w.T, w.n_sink, w.n_recent, W.marked(w, b), w.group_n)
-        unit = otiers.build_unit(kb, vb, l1, g, ly.k_signs[h], ly.v_signs[h], c4, c3)
-        qh = ly.q[b, h * w.G:(h + 1) * w.G].double().cpu().numpy()
-        units.append((unit, qh, h))
-    done = 0
-    t0 = time.perf_counter()
-    while True:
-        unit, qh, h = units[done % len(units)]
-        odec.decode_step_unit(qh, unit, w.group_n, w.d, ly.k_signs[h], ly.v_signs[h], c4, c3, w.beta,
-                              1.0 / math.sqrt(w.d))
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    el = time.perf_counter() - t0
-    return {"value": done * w.T / el, "unit": "heads*tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} (sequence, kv-head) decode steps of the {w.name} workload "
-                      f"(route + top-beta + attention over T={w.T}), cycling over units {sample}, "
-                      f"{el:.1f} s; fp64 numpy oracle"}
+    units = pool.map(_cpu_build, build_args, chunksize=1)
+    del build_args
+    run_args = [(u, ly.q[b, h * w.G:(h + 1) * w.G].double().cpu().numpy(), ly.k_signs[h],
+                 ly.v_signs[h], w.group_n, w.d, w.beta, budget_s)
+                for u, (b, h) in zip(units, sample)]
+    res = pool.map(_cpu_steps, run_args, chunksize=1)
+    steps = sum(r[0] for r in res)
+    el = max(r[2] for r in res) - min(r[1] for r in res)
+    return {"value": steps * w.T / el, "unit": "heads*tokens/s", "cores": n_workers,
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": f"{steps} (sequence, kv-head) decode steps of the {w.name} workload "
+                      f"(route + top-beta + attention over T={w.T}, tiers built beforehand) on "
+                      f"{n_workers} units {sample}, one per worker process and core, all "
+                      f"running for {el:.1f} s; fp64 numpy oracle"}
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; multi-GPU runs are not part of it",
-                          "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this build measures one GPU; runs on several GPUs are not "
+                                   "part of it (--gpus must be 1)", "n_gpus": args.gpus}))
         sys.exit(2)
+    pool = n_workers = None
+    if not args.only_step and not args.no_cpu:
+        pool, n_workers = start_cpu_pool()  # before the GPU is touched
     import torch
     from compressed_decode_attention_turboquant_amd import hsq
     from compressed_decode_attention_turboquant_amd import workloads as W
@@ -549,6 +693,7 @@ def main():
         "n_gpus": 1,
         "steps": res["steps"],
         "warmup": args.warmup,
+        "reps": res["reps"],
         "ms_per_step": res["ms_step"],
         "higher_is_better": True,
         "scaling": "weak",
@@ -559,6 +704,8 @@ def main():
                    "head_dim": w.d, "context": w.T, "group_n": w.group_n, "beta": w.beta,
                    "n_l1": res["n1"], "n_groups": res["ng"], "archive": "hbm",
                    "layer_instances": args.layers, "parallelism": "single-gpu"},
+        "timing": {"per_rep_steps": res["steps"], "reps": res["reps"],
+                   "ms_per_step": res["rep_ms_per_step"], "statistic": "median over reps"},
         "step_hbm_gbs": res["step_gbs"],
         "step_hbm_frac": res["step_gbs"] / HBM_PEAK_GBS,
         "kernels": k,
@@ -567,6 +714,8 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": res["achieved"] / HBM_PEAK_GBS,
                      "traffic": measured_traffic(dom)},
     }
+    print(json.dumps({"progress": "headline", "ms_per_step": res["ms_step"]}), file=sys.stderr,
+          flush=True)
     if args.calib_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
         dst = torch.empty_like(src)
@@ -575,10 +724,18 @@ def main():
         torch.cuda.synchronize()
         line["calib_copy_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
         del src, dst
+    if not args.only_step and not args.no_configs:
+        line["qwen3_8b_8k"] = layer_chain(args, torch, hsq, W, W.QWEN3_8B_8K, 512,
+                                          "512 independent layer instances, one launch each")
+        print(json.dumps({"progress": "qwen3-8b-8k"}), file=sys.stderr, flush=True)
+        line["qwen3_8b_32k_hbm"] = layer_chain(args, torch, hsq, W, W.QWEN3_8B_32K,
+                                               W.QWEN3_8B_32K.layers,
+                                               "one decode step: 36 layers, archive in HBM")
+        print(json.dumps({"progress": "qwen3-8b-32k-hbm"}), file=sys.stderr, flush=True)
     if not args.only_step and not args.no_codec:
         line["codec"] = codec_rates(torch, hsq, W)
-    if not args.only_step and not args.no_codec:
         line["qjl"] = qjl_rates(torch, hsq, W)
+        print(json.dumps({"progress": "codec"}), file=sys.stderr, flush=True)
     if not args.only_step and not args.no_cache:
         line["cache_append"] = cache_append_rate(torch, hsq, W)
     if not args.only_step and not args.no_host:
@@ -586,8 +743,11 @@ def main():
             line["host_archive"] = host_archive(torch, hsq, W)
         except Exception as e:  # reported, never hides the headline
             line["host_archive"] = {"error": repr(e)}
-    if not args.only_step and not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(torch, W, layers)
+        print(json.dumps({"progress": "host archive"}), file=sys.stderr, flush=True)
+    if pool is not None:
+        line["cpu_baseline"] = cpu_baseline(torch, W, layers, pool, n_workers)
+        pool.close()
+        pool.join()
     print(json.dumps(line), flush=True)
 
 

@@ -191,14 +191,21 @@ int step_common(const char* fn, const StepShape& s, void* workspace, size_t ws_b
                 Workspace& w) {
   if (!step_limits_ok(s))
     return fail(HSQ_ERR_UNSUPPORTED,
-                std::string(fn) + ": n_groups, G * n_groups or the L1/L3 sizes exceed the "
-                                  "kernels' limits (n_groups <= 16384, G * n_groups <= 12288, "
-                                  "per-unit L1/L3 bytes < 2 GiB)");
+                std::string(fn) + ": n_groups or the L1/L3 sizes exceed the kernels' limits "
+                                  "(n_groups <= 16384, per-unit L1/L3 bytes < 2 GiB)");
   w = plan_workspace(s);
   if (!workspace || ws_bytes < w.total)
     return fail(HSQ_ERR_WORKSPACE, std::string(fn) + ": workspace missing or smaller than hsq_workspace_bytes()");
   if (reinterpret_cast<uintptr_t>(workspace) % 256)
     return fail(HSQ_ERR_ARG, std::string(fn) + ": workspace must be 256-byte aligned");
+  return HSQ_OK;
+}
+
+int need_route_lds(const char* fn, const StepShape& s) {
+  if (s.n_groups > 0 && !route_lds_ok(s))
+    return fail(HSQ_ERR_UNSUPPORTED,
+                std::string(fn) + ": G * n_groups exceeds 12288 (the router logits this call "
+                                  "holds on chip); hsq_decode_step serves such shapes");
   return HSQ_OK;
 }
 
@@ -266,6 +273,7 @@ extern "C" int hsq_decode_attn(const float* q, int B, int Hq, int Hkv, int d, co
   StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, beta};
   Workspace w;
   if ((rc = step_common("hsq_decode_attn", s, workspace, ws_bytes, w))) return rc;
+  if ((rc = need_route_lds("hsq_decode_attn", s))) return rc;
   StepTensors t{q, l1k, l1k_n, l1v, l1v_n, l2k, l2k_n, l2v, l2v_n, l3, l3_staged ? 1 : 0,
                 k_signs, v_signs, cb4, cb3, scale, summary_bias, HSQ_AGG_MAX, out};
   char* ws = static_cast<char*>(workspace);
@@ -291,6 +299,7 @@ extern "C" int hsq_step_route(const float* q, int B, int Hq, int Hkv, int d, int
   StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, b};
   Workspace w;
   if ((rc = step_common("hsq_step_route", s, workspace, ws_bytes, w))) return rc;
+  if ((rc = need_route_lds("hsq_step_route", s))) return rc;
   StepTensors t{};
   t.q = q; t.l2k = l2k; t.l2k_n = l2k_n; t.l2v = l2v; t.l2v_n = l2v_n; t.k_signs = k_signs;
   t.cb3 = cb3; t.scale = scale; t.summary_bias = summary_bias; t.agg = agg;
@@ -325,6 +334,7 @@ extern "C" int hsq_step_attend(const float* q, int B, int Hq, int Hkv, int d, co
   StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, b};
   Workspace w;
   if ((rc = step_common("hsq_step_attend", s, workspace, ws_bytes, w))) return rc;
+  if ((rc = need_route_lds("hsq_step_attend", s))) return rc;
   StepTensors t{};
   t.q = q; t.l1k = l1k; t.l1k_n = l1k_n; t.l1v = l1v; t.l1v_n = l1v_n; t.l3 = l3;
   t.l3_staged = l3_staged ? 1 : 0; t.k_signs = k_signs; t.v_signs = v_signs; t.cb4 = cb4;
@@ -354,15 +364,18 @@ extern "C" int hsq_decode_step(const float* q, int B, int Hq, int Hkv, int d, co
   StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, b};
   Workspace w;
   if ((rc = step_common("hsq_decode_step", s, workspace, ws_bytes, w))) return rc;
-  if (step_fused_ok(s)) {  // one launch: route and attend on the same work-group
-    StepTensors t{};
-    t.q = q; t.l1k = l1k; t.l1k_n = l1k_n; t.l1v = l1v; t.l1v_n = l1v_n;
-    t.l2k = l2k; t.l2k_n = l2k_n; t.l2v = l2v; t.l2v_n = l2v_n; t.l3 = l3; t.l3_staged = 0;
-    t.k_signs = k_signs; t.v_signs = v_signs; t.cb4 = cb4; t.cb3 = cb3; t.scale = scale;
-    t.summary_bias = summary_bias; t.agg = agg; t.out = out;
+  StepTensors t{};
+  t.q = q; t.l1k = l1k; t.l1k_n = l1k_n; t.l1v = l1v; t.l1v_n = l1v_n;
+  t.l2k = l2k; t.l2k_n = l2k_n; t.l2v = l2v; t.l2v_n = l2v_n; t.l3 = l3; t.l3_staged = 0;
+  t.k_signs = k_signs; t.v_signs = v_signs; t.cb4 = cb4; t.cb3 = cb3; t.scale = scale;
+  t.summary_bias = summary_bias; t.agg = agg; t.out = out;
+  if (use_split(s))  // few units or many groups: each unit over many work-groups
+    return check_hip(launch_split_step(s, t, w, static_cast<char*>(workspace),
+                                       b > 0 ? topk_idx : nullptr, as_stream(stream)),
+                     "hsq_decode_step (split)");
+  if (step_fused_ok(s))  // one launch: route and attend on the same work-group
     return check_hip(launch_step(s, t, b > 0 ? topk_idx : nullptr, as_stream(stream)),
                      "hsq_decode_step");
-  }
   if ((rc = hsq_step_route(q, B, Hq, Hkv, d, n_l1, l2k, l2k_n, l2v, l2v_n, n_groups, group_n, beta,
                            agg, k_signs, cb3, scale, summary_bias, topk_idx, workspace, ws_bytes,
                            stream)))
@@ -449,6 +462,9 @@ extern "C" int hsq_cache_decode_step(const float* q, int B, int Hq, int Hkv, int
   StepTensors t{q, l1k, l1k_n, l1v, l1v_n, l2k, l2k_n, l2v, l2v_n, l3, 0,
                 k_signs, v_signs, cb4, cb3, scale, summary_bias, agg, out};
   const hipStream_t st = as_stream(stream);
+  if (use_split(s))
+    return check_hip(launch_split_step(s, t, w, static_cast<char*>(workspace),
+                                       b > 0 ? topk_idx : nullptr, st), fn);
   if (step_fused_ok(s))
     return check_hip(launch_step(s, t, b > 0 ? topk_idx : nullptr, st), fn);
   char* ws = static_cast<char*>(workspace);

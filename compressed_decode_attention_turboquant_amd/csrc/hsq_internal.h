@@ -89,11 +89,21 @@ struct StepTensors {
 struct Workspace {
   size_t idx_off;      // int32 [B*Hkv][beta]   selection
   size_t part_off;     // fp32  [B*Hkv][G][d+2] summary-attention partial (m, l, O)
+  // split step only (use_split): per-head logits, router keys, largest key
+  // norm per score chunk, selection bitmap, partials of the attend chunks
+  size_t lgt_off, keys_off, rn_off, bits_off, parts_off;
   size_t total;
 };
 Workspace plan_workspace(const StepShape& s);
-// shapes the step kernels can hold in LDS / 32-bit buffer offsets
+// shapes the step kernels can address (group count, 32-bit buffer offsets)
 int step_limits_ok(const StepShape& s);
+// shapes whose router logits fit in LDS (one-launch step, two-launch route)
+int route_lds_ok(const StepShape& s);
+// shapes hsq_decode_step runs as the split step: few units, or router
+// logits beyond LDS
+int use_split(const StepShape& s);
+hipError_t launch_split_step(const StepShape& s, const StepTensors& t, const Workspace& w,
+                             char* ws, int32_t* idx_out, hipStream_t st);
 
 // mode bits for the summary kernel
 enum { ROUTE_TOPK = 1, ROUTE_PARTIALS = 2 };

@@ -70,7 +70,8 @@ constexpr int kMaxG = 8;
 constexpr int kNC3 = 32;                 // 3-bit table copies (lanes l, l+32 share)
 constexpr int kNC4 = 64;                 // 4-bit table copies (one per lane)
 constexpr int kMaxGroups = 16384;
-constexpr int kMaxLogits = 12288;        // G * n_groups kept in LDS
+constexpr int kMaxLogits = 12288;        // G * n_groups kept in LDS (one-launch step, route)
+constexpr int kSplitUnits = 128;         // fewer units than this: the split step
 constexpr size_t kMaxFusedLds = 92 * 1024;  // dynamic LDS of the one-launch step (64 KB static)
 constexpr uint32_t kFar = 0x80000000u;   // buffer offset that reads as zero
 constexpr float kNegInf = -INFINITY;
@@ -177,6 +178,28 @@ __device__ __forceinline__ float wave_max(float x) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 __device__ __forceinline__ float wave_min(float x) { return -wave_max(-x); }
+// Wave-wide unsigned minimum / maximum (butterfly: every lane gets it).
+__device__ __forceinline__ uint32_t wave_umin(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, o, 64));
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o, 64));
+  return x;
+}
+// Sum over aligned groups of LANES (8 or 16) consecutive lanes by DPP row
+// operations; every lane of a group gets its group's sum.
+template <int LANES>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(LANES == 8 || LANES == 16, "8 or 16 lanes");
+  x += dpp_f<0xb1>(x);   // quad_perm 1,0,3,2
+  x += dpp_f<0x4e>(x);   // quad_perm 2,3,0,1
+  x += dpp_f<0x141>(x);  // row_half_mirror: the other quad of the half row
+  if constexpr (LANES == 16) x += dpp_f<0x140>(x);  // row_mirror: the other half
+  return x;
+}
 
 // Three-way minimum / maximum as one VALU instruction.  fminf/fmaxf would
 // first quiet every operand the compiler cannot prove canonical (one more
@@ -279,17 +302,28 @@ __device__ __forceinline__ void load_query(const float* q, const uint32_t* mask,
     Q.sb = 0u;
   }
 }
+// qn, if not null, receives ||q'_h||_1 of each row (the router's error bound).
 template <int D>
-__device__ __forceinline__ void rotate_query(QueryIn& Q, float mult, float* qf, int tid) {
+__device__ __forceinline__ void rotate_query(QueryIn& Q, float mult, float* qf, int tid,
+                                             float* qn = nullptr) {
   constexpr int LPV = D / 8;
   if (tid < kMaxG * LPV) {
     const int h = tid / LPV, sub = tid % LPV;
 #pragma unroll
     for (int k = 0; k < 8; ++k) Q.v[k] = flip(Q.v[k], (Q.sb >> k) & 1u);
     fwht8xlanes<LPV>(Q.v, sub);
+    const f32x4 a = f32x4{Q.v[0], Q.v[1], Q.v[2], Q.v[3]} * mult;
+    const f32x4 b = f32x4{Q.v[4], Q.v[5], Q.v[6], Q.v[7]} * mult;
     f32x4* dst = reinterpret_cast<f32x4*>(qf + h * kQS<D> + 8 * sub);
-    dst[0] = f32x4{Q.v[0], Q.v[1], Q.v[2], Q.v[3]} * mult;
-    dst[1] = f32x4{Q.v[4], Q.v[5], Q.v[6], Q.v[7]} * mult;
+    dst[0] = a;
+    dst[1] = b;
+    if (qn) {
+      float s = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) s += fabsf(a[k]) + fabsf(b[k]);
+      s = group_sum<LPV>(s);
+      if (sub == 0) qn[h] = s;
+    }
   }
 }
 
@@ -721,8 +755,7 @@ __device__ __forceinline__ float exact_score(rsrc_t rk, rsrc_t rkn, int g, int s
     float acc = 0.f;
 #pragma unroll
     for (int k = 0; k < PER; ++k) acc = __builtin_fmaf(qr[k], cv[k], acc);
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o, 64);
+    acc = group_sum<16>(acc);
     const float lg = acc * r;
     best = fmaxf(best, lg);
     sum += lg;
@@ -856,6 +889,283 @@ __device__ __forceinline__ RouteLds route_lds(char* base, const RouteLayout& r, 
   return L;
 }
 
+// Top-beta of the unit's router keys by one wave, emitted in ascending
+// order (see the band rule above): into io.keys[0..beta) (the keys array is
+// reused), io.idx, io.recoff (record offsets) and io.bits (bitmap of the
+// selected groups, whole words) when those are set.  Without hsel the
+// selection is io.fmask.  Returns the number of groups selected.
+struct SelIo {
+  uint32_t* keys;          // LDS [ng] order-preserving keys; receives the selection
+  int* hist;               // LDS [256], the score histogram over [lo, hi]
+  uint2* cand;             // LDS [64]
+  const uint32_t* fmask;   // LDS bitmap: the selection when !hsel
+  int words, ng, beta, G;
+  float lo, bscale, bnd;
+  bool hsel, mean;
+  rsrc_t rk, rkn;          // summary key codes and norms of the unit (rescoring)
+  const float* qf;         // rotated query rows
+  const float* cb;         // the eight fp32 centroids
+  int32_t* idx;            // out [beta] or null
+  int32_t* recoff;         // LDS out [beta] or null
+  uint32_t rec;            // record bytes (recoff = g * rec)
+  uint32_t* bits;          // out [words] bitmap or null
+};
+template <int D, bool EXACT>
+__device__ int select_wave(const SelIo& io, int lane) {
+  const int sub = lane & 15, row = lane >> 4;
+  const float bnd = io.bnd;
+  // keys of the band's edges around theta (a bound that is not finite,
+  // from overflowing inputs, puts every group in the band)
+  auto band_keys = [&](uint32_t theta, uint32_t& khi, uint32_t& klo) {
+    if constexpr (EXACT) {
+      khi = klo = theta;
+    } else {
+      const float tf = key_float(theta);
+      const float tup = tf + 2.f * bnd, tdn = tf - 2.f * bnd;
+      const bool fin = __builtin_isfinite(tup) && __builtin_isfinite(tdn);
+      khi = fin ? fkey(tup) : 0xffffffffu;
+      klo = fin ? fkey(tdn) : 0u;
+    }
+  };
+  // exact keys of up to 64 listed groups io.cand[0..n) (into io.cand[j].y), four
+  // groups per pass (16 lanes each); the exact router's keys are exact
+  auto rescore = [&](int n) {
+    if constexpr (!EXACT) {
+      for (int j0 = 0; j0 < n; j0 += 4) {
+        const int j = min(j0 + row, n - 1);
+        const int g = (int)io.cand[j].x;
+        const uint32_t k = fkey(exact_score<D>(io.rk, io.rkn, g, sub, io.qf, io.cb, io.G, io.mean));
+        if (sub == 0 && j0 + row < n) io.cand[j].y = k;
+      }
+      wave_lds_sync();
+    }
+  };
+  // rank of this lane's (key, id) among lanes [0, n): (key desc, id asc)
+  auto rank_of = [&](uint2 me, int n) {
+    int rank = 0;
+    for (int j = 0; j < n; ++j) {
+      const uint32_t og = __builtin_amdgcn_readlane(me.x, j);
+      const uint32_t ok = __builtin_amdgcn_readlane(me.y, j);
+      rank += (ok > me.y) || (ok == me.y && og < me.x);
+    }
+    return rank;
+  };
+  // Fast path.  The threshold bucket bt (histogram); C = the groups of
+  // buckets bt-1 .. bt+1, one per lane (at most 64); theta from ranking C.
+  // Every group above C is above the band and every group below C below
+  // it when the smallest key above C exceeds theta + 2 bnd and the largest
+  // below C is under theta - 2 bnd, so the band is inside C.
+  uint2 me = make_uint2(0u, 0u), bme = make_uint2(0u, 0u);
+  uint64_t mask_a = 0u, mask_b = 0u;  // chosen lanes of me (above the band) / of bme (band)
+  uint32_t above0 = 0u;
+  int bhi = 255;
+  bool fast = false;
+  if (io.hsel) {
+    int bt, need;
+    hist_threshold(io.hist, io.beta, lane, bt, need);
+    bhi = min(bt + 1, 255);
+    const int blb = max(bt - 1, 0);
+    int n_hi = 0;  // groups in buckets above bhi
+    {
+      int cnt = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int b = 255 - 4 * lane - k;
+        cnt += b > bhi ? io.hist[b] : 0;
+      }
+      wave_excl_scan(cnt, lane, n_hi);
+    }
+    uint32_t amin = 0xffffffffu, bmax = 0u;
+    int nc = 0;
+    for (int w0 = 0; w0 < io.words; w0 += 64) {
+      const int w = w0 + lane, wr = min(w, io.words - 1);
+      u32x4 k4[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) k4[q] = *reinterpret_cast<const u32x4*>(io.keys + 32 * wr + 4 * q);
+      __builtin_amdgcn_sched_barrier(0);
+      uint32_t above = 0u, inc = 0u;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t k = k4[q][e];
+          const bool in = 32 * w + 4 * q + e < io.ng;
+          const int b = score_bucket(k, io.lo, io.bscale);
+          above |= (in && b > bhi) ? 1u << (4 * q + e) : 0u;
+          inc |= (in && b >= blb && b <= bhi) ? 1u << (4 * q + e) : 0u;
+          amin = (in && b > bhi) ? min(amin, k) : amin;
+          bmax = (in && b < blb) ? max(bmax, k) : bmax;
+        }
+      if (w0 == 0) above0 = above;
+      int total;
+      int pos = nc + wave_excl_scan(__popc(inc), lane, total);
+      while (inc) {
+        const int g = 32 * w + __ffs(inc) - 1;
+        if (pos < 64) io.cand[pos] = make_uint2((uint32_t)g, io.keys[g]);
+        ++pos;
+        inc &= inc - 1u;
+      }
+      nc += total;
+    }
+    const uint32_t amin_all = wave_umin(amin), bmax_all = wave_umax(bmax);
+    wave_lds_sync();
+    if (nc <= 64) {
+      me = lane < nc ? io.cand[lane] : make_uint2(0u, 0u);
+      const int rank = rank_of(me, nc);
+      const uint64_t at = __builtin_amdgcn_ballot_w64(lane < nc && rank == io.beta - n_hi - 1);
+      const uint32_t theta = __builtin_amdgcn_readlane(me.y, __ffsll((unsigned long long)at) - 1);
+      uint32_t khi, klo;
+      band_keys(theta, khi, klo);
+      fast = amin_all > khi && bmax_all < klo;
+      if (fast) {
+        const bool abv = lane < nc && me.y > khi;
+        const bool inb = lane < nc && me.y >= klo && me.y <= khi;
+        mask_a = __builtin_amdgcn_ballot_w64(abv);
+        const int need2 = io.beta - n_hi - __popcll(mask_a);
+        // the band's groups, listed in cand and rescored
+        int nb;
+        const int pos = wave_excl_scan(inb ? 1 : 0, lane, nb);
+        wave_lds_sync();
+        if (inb) io.cand[pos] = make_uint2(me.x, me.y);
+        wave_lds_sync();
+        rescore(nb);
+        bme = lane < nb ? io.cand[lane] : make_uint2(0u, 0u);
+        const int rb = rank_of(bme, nb);
+        mask_b = __builtin_amdgcn_ballot_w64(lane < nb && rb < need2);
+      }
+    }
+  }
+  // General path (heavy ties, or a band reaching past C): theta by radix
+  // select over all keys and the band by a scan of all keys; a band of
+  // more than 64 groups rescores every group, and the radix select over
+  // the exact keys emits the selection.
+  bool by_key = false, radix = false;
+  uint32_t khi_e = 0u;
+  if (io.hsel && !fast) {
+    int nd;
+    const uint32_t theta = radix_kth(io.keys, io.ng, io.beta, io.hist, lane, nd);
+    uint32_t klo;
+    band_keys(theta, khi_e, klo);
+    by_key = true;
+    int n_above = 0, nb = 0;
+    for (int w0 = 0; w0 < io.words; w0 += 64) {
+      const int w = w0 + lane, wr = min(w, io.words - 1);
+      u32x4 k4[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) k4[q] = *reinterpret_cast<const u32x4*>(io.keys + 32 * wr + 4 * q);
+      __builtin_amdgcn_sched_barrier(0);
+      uint32_t above = 0u, inb = 0u;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t k = k4[q][e];
+          const bool in = 32 * w + 4 * q + e < io.ng;
+          above |= (in && k > khi_e) ? 1u << (4 * q + e) : 0u;
+          inb |= (in && k >= klo && k <= khi_e) ? 1u << (4 * q + e) : 0u;
+        }
+      if (w0 == 0) above0 = above;
+      int tot_a;
+      wave_excl_scan(__popc(above), lane, tot_a);
+      n_above += tot_a;
+      int total;
+      int pos = nb + wave_excl_scan(__popc(inb), lane, total);
+      while (inb) {
+        if (pos < 64) io.cand[pos] = make_uint2((uint32_t)(32 * w + __ffs(inb) - 1), 0u);
+        ++pos;
+        inb &= inb - 1u;
+      }
+      nb += total;
+    }
+    wave_lds_sync();
+    if (nb <= 64) {
+      if constexpr (EXACT) {
+        if (lane < nb) io.cand[lane].y = io.keys[io.cand[lane].x];
+        wave_lds_sync();
+      }
+      rescore(nb);
+      bme = lane < nb ? io.cand[lane] : make_uint2(0u, 0u);
+      const int rb = rank_of(bme, nb);
+      mask_b = __builtin_amdgcn_ballot_w64(lane < nb && rb < io.beta - n_above);
+    } else {
+      if constexpr (!EXACT) {
+        for (int g0 = 0; g0 < io.ng; g0 += 4) {
+          const int g = min(g0 + row, io.ng - 1);
+          const uint32_t k = fkey(exact_score<D>(io.rk, io.rkn, g, sub, io.qf, io.cb, io.G, io.mean));
+          if (sub == 0 && g0 + row < io.ng) io.keys[g] = k;
+        }
+        wave_lds_sync();
+      }
+      top_beta_wave(io.keys, io.ng, io.beta, io.hist, reinterpret_cast<int32_t*>(io.keys), lane);
+      radix = true;
+    }
+  }
+  // emit the selection in ascending order (the radix select already did):
+  // word w's bits are the groups above C (fast path) or above the band
+  // (general path), plus the chosen lanes of me and bme
+  auto above_bits = [&](int w) {
+    const int wr = min(w, io.words - 1);
+    u32x4 k4[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) k4[q] = *reinterpret_cast<const u32x4*>(io.keys + 32 * wr + 4 * q);
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t above = 0u;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t k = k4[q][e];
+        const bool in = 32 * w + 4 * q + e < io.ng;
+        const bool up = by_key ? k > khi_e : score_bucket(k, io.lo, io.bscale) > bhi;
+        above |= (in && up) ? 1u << (4 * q + e) : 0u;
+      }
+    return above;
+  };
+  int nsel = 0;
+  if (radix) {
+    nsel = io.beta;
+    for (int pos = lane; pos < nsel; pos += 64) {
+      const int g = (int)io.keys[pos];
+      if (io.idx) io.idx[pos] = g;
+      if (io.recoff) io.recoff[pos] = (int32_t)((uint32_t)g * io.rec);
+      if (io.bits) atomicOr(&io.bits[g >> 5], 1u << (g & 31));
+    }
+  } else {
+    for (int w0 = 0; w0 < io.words; w0 += 64) {
+      const int w = w0 + lane;
+      uint32_t bits;
+      if (io.hsel) {
+        bits = (w0 == 0) ? above0 : above_bits(w);
+        for (uint64_t m = mask_a; m; m &= m - 1u) {
+          const uint32_t g = __builtin_amdgcn_readlane(me.x, __ffsll((unsigned long long)m) - 1);
+          bits |= ((int)(g >> 5) == w) ? 1u << (g & 31) : 0u;
+        }
+        for (uint64_t m = mask_b; m; m &= m - 1u) {
+          const uint32_t g = __builtin_amdgcn_readlane(bme.x, __ffsll((unsigned long long)m) - 1);
+          bits |= ((int)(g >> 5) == w) ? 1u << (g & 31) : 0u;
+        }
+      } else {
+        bits = (w < io.words) ? io.fmask[w] : 0u;
+      }
+      if (io.bits && w < io.words) io.bits[w] = bits;
+      int total;
+      int pos = nsel + wave_excl_scan(__popc(bits), lane, total);
+      while (bits) {
+        const int g = 32 * w + __ffs(bits) - 1;
+        io.keys[pos] = (uint32_t)g;
+        if (io.idx) io.idx[pos] = g;
+        if (io.recoff) io.recoff[pos] = (int32_t)((uint32_t)g * io.rec);
+        ++pos;
+        bits &= bits - 1u;
+      }
+      nsel += total;
+    }
+  }
+  wave_lds_sync();
+
+  return nsel;
+}
+
 // Router, top-beta and summary partial of one unit (the whole work-group).
 // The summary partial goes either, combined over the waves, to part_out
 // ([G][D+2] (m, l, O), global memory), or, when st_out is not null, stays
@@ -871,6 +1181,7 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   __shared__ float s_lo[kWaves], s_hi[kWaves];
   __shared__ float s_mh[kWaves][kMaxG];
   __shared__ float s_rn[kWaves];  // largest key norm seen by each wave
+  __shared__ float s_qn[kMaxG];   // ||q'_h||_1 of each head's rotated query
   const int ngp = (a.ng + 15) & ~15;
   float* qf = L.qf;
   float* logits = L.logits;
@@ -909,7 +1220,7 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
     load_keys<D>(rk, rkn, wave + j * kWaves, lane, kt[j]);
 
   if (tid < 8) s_cb[tid] = cbv;
-  rotate_query<D>(qin, a.scale * rsqrtf((float)D), qf, tid);
+  rotate_query<D>(qin, a.scale * rsqrtf((float)D), qf, tid, s_qn);
   const int words = (ngp + 31) >> 5;
   for (int w = tid; w < words; w += kThreads) fmask[w] = 0u;
   for (int b = tid; b < 256; b += kThreads) hist[b] = 0;
@@ -964,12 +1275,14 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
     s_rn[wave] = rn;
   }
   if (gq == 0 && writer) s_mh[wave][c] = cmax;
-  // Phase 2.  Seven waves stream the values of ALL summaries into their
-  // softmax partials (tiles w, w + 7, ...); the fetched ones are subtracted
-  // at the end with the same weights.  The eighth wave meanwhile forms the
-  // router scores and their histogram, finds the threshold, ranks the
-  // threshold bucket, emits the selection and subtracts the fetched
-  // summaries.  No barrier until the end.
+  // Phase 2.  (2a) All eight waves form the router scores of a share of the
+  // groups (max or mean over the G heads) as order-preserving keys, with
+  // their histogram over [lo, hi]; one barrier.  Then seven waves stream the
+  // values of ALL summaries into their softmax partials (tiles w, w + 7,
+  // ...); the fetched ones are subtracted at the end with the same weights.
+  // The eighth wave meanwhile finds the threshold, settles the groups near
+  // it, emits the selection and subtracts the fetched summaries.  No other
+  // barrier until the end.
   constexpr int K = kValDepth;
   constexpr int kSel = kWaves - 1;  // the selecting wave
   const bool stream = a.want_partial && a.beta < a.ng;  // else the partial is empty
@@ -980,6 +1293,71 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   if (wave != kSel) {
 #pragma unroll
     for (int j = 0; j < K - 1; ++j) load_vals<D>(rv, rvn, tile(j), lane, vt[j]);
+  }
+  lds_barrier();
+
+  // (2a) scores and histogram, 4 groups per lane and pass, passes dealt to
+  // the waves in turn
+  const bool hsel = a.want_topk && a.beta > 0 && a.beta < a.ng;
+  float lo = kPosInf, hi = kNegInf;
+  for (int w = 0; w < kWaves; ++w) {
+    lo = fminf(lo, s_lo[w]);
+    hi = fmaxf(hi, s_hi[w]);
+  }
+  const float bscale = (hi > lo) ? 256.f / (hi - lo) : 0.f;
+  const bool want_mean = a.agg != HSQ_AGG_MAX;
+  if (a.want_topk) {
+    const float inv_g = 1.f / (float)a.G;
+    const int hl = a.G - 1;
+    for (int g0 = 4 * lane + 256 * wave; g0 < 32 * words; g0 += 256 * kWaves) {
+      // every head's row is read before the first use (one LDS round trip
+      // per pass); the loop reads only the G rows of real heads
+      f32x4 x[kMaxG];
+#pragma unroll
+      for (int h = 0; h < kMaxG; ++h)
+        if (h <= hl) x[h] = *reinterpret_cast<const f32x4*>(logits + h * ngp + g0);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 vmax = x[0], vsum = x[0];
+#pragma unroll
+      for (int h = 1; h < kMaxG; ++h) {
+        if (h <= hl) {  // wave-uniform
+          vmax = f32x4{__builtin_amdgcn_fmed3f(vmax[0], x[h][0], kPosInf),
+                       __builtin_amdgcn_fmed3f(vmax[1], x[h][1], kPosInf),
+                       __builtin_amdgcn_fmed3f(vmax[2], x[h][2], kPosInf),
+                       __builtin_amdgcn_fmed3f(vmax[3], x[h][3], kPosInf)};
+          vsum += x[h];
+        }
+      }
+      u32x4 k4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = g0 + e < a.ng;
+        const float v = want_mean ? vsum[e] * inv_g : vmax[e];
+        k4[e] = ok ? fkey(v) : 0u;
+        // branch-free: a slot past the end adds 0 to bucket 0
+        if (hsel) atomicAdd(&hist[ok ? score_bucket(k4[e], lo, bscale) : 0], ok ? 1 : 0);
+      }
+      if (EXACT && a.scores_out) {  // only the exact router's scores are written
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (g0 + e < a.ng)
+            a.scores_out[(size_t)unit * a.ng + g0 + e] = want_mean ? vsum[e] * inv_g : vmax[e];
+      }
+      *reinterpret_cast<u32x4*>(keys + g0) = k4;
+    }
+  }
+  if (wave == kSel) {
+    if (a.want_topk && a.beta >= a.ng) {  // every group fetched
+      for (int w = lane; w < words; w += 64) {
+        const int left = a.ng - 32 * w;
+        fmask[w] = left >= 32 ? 0xffffffffu : (left <= 0 ? 0u : ((1u << left) - 1u));
+      }
+    } else if (!a.want_topk && a.given) {  // the given selection
+      for (int i = lane; i < a.beta; i += 64) {
+        const int g = a.given[(size_t)unit * a.beta + i];
+        if (g >= 0 && g < a.ng) atomicOr(&fmask[g >> 5], 1u << (g & 31));
+      }
+    }
   }
   lds_barrier();
 
@@ -1023,284 +1401,36 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   } else {
     // this wave gates the work-group's finish: its selection goes first
     __builtin_amdgcn_s_setprio(3);
-    // (2a) router scores (max or mean over the G heads) as order-preserving
-    // keys, 4 groups per lane and pass; their histogram over [lo, hi]
-    const bool hsel = a.want_topk && a.beta > 0 && a.beta < a.ng;
-    float lo = kPosInf, hi = kNegInf;
-    for (int w = 0; w < kWaves; ++w) {
-      lo = fminf(lo, s_lo[w]);
-      hi = fmaxf(hi, s_hi[w]);
-    }
-    const float bscale = (hi > lo) ? 256.f / (hi - lo) : 0.f;
-    if (a.want_topk) {
-      const float inv_g = 1.f / (float)a.G;
-      const int hl = a.G - 1;
-      for (int g0 = 4 * lane; g0 < 32 * words; g0 += 256) {
-        // every head's row is read before the first use (one LDS round trip
-        // per pass); rows past the last head repeat it, and the sum skips them
-        f32x4 x[kMaxG];
-#pragma unroll
-        for (int h = 0; h < kMaxG; ++h)
-          if (h <= hl) x[h] = *reinterpret_cast<const f32x4*>(logits + h * ngp + g0);
-        __builtin_amdgcn_sched_barrier(0);
-        f32x4 vmax = x[0], vsum = x[0];
-#pragma unroll
-        for (int h = 1; h < kMaxG; ++h) {
-          if (h <= hl) {  // wave-uniform
-            vmax = f32x4{__builtin_amdgcn_fmed3f(vmax[0], x[h][0], kPosInf),
-                         __builtin_amdgcn_fmed3f(vmax[1], x[h][1], kPosInf),
-                         __builtin_amdgcn_fmed3f(vmax[2], x[h][2], kPosInf),
-                         __builtin_amdgcn_fmed3f(vmax[3], x[h][3], kPosInf)};
-            vsum += x[h];
-          }
-        }
-        u32x4 k4;
-        const bool want_mean = a.agg != HSQ_AGG_MAX;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool ok = g0 + e < a.ng;
-          const float v = want_mean ? vsum[e] * inv_g : vmax[e];
-          k4[e] = ok ? fkey(v) : 0u;
-          // branch-free: a slot past the end adds 0 to bucket 0
-          if (hsel) atomicAdd(&hist[ok ? score_bucket(k4[e], lo, bscale) : 0], ok ? 1 : 0);
-        }
-        if (EXACT && a.scores_out) {  // only the exact router's scores are written
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (g0 + e < a.ng)
-              a.scores_out[(size_t)unit * a.ng + g0 + e] =
-                  want_mean ? vsum[e] * inv_g : vmax[e];
-        }
-        *reinterpret_cast<u32x4*>(keys + g0) = k4;
-      }
-      if (a.beta >= a.ng)  // every group fetched
-        for (int w = lane; w < words; w += 64) {
-          const int left = a.ng - 32 * w;
-          fmask[w] = left >= 32 ? 0xffffffffu : (left <= 0 ? 0u : ((1u << left) - 1u));
-        }
-    } else if (a.given) {  // the given selection
-      for (int i = lane; i < a.beta; i += 64) {
-        const int g = a.given[(size_t)unit * a.beta + i];
-        if (g >= 0 && g < a.ng) atomicOr(&fmask[g >> 5], 1u << (g & 31));
-      }
-    }
-    wave_lds_sync();
-
-    // (2b) theta: the key of the beta-th largest computed score.  The
-    // histogram gives its bucket; the bucket's groups (at most 64) are
-    // ranked exactly by (key descending, index ascending); more (heavy
-    // ties): radix select.
-    uint32_t theta = 0u;
-    if (hsel) {
-      int bt, need;
-      hist_threshold(hist, a.beta, lane, bt, need);
-      if (__builtin_amdgcn_readfirstlane(hist[bt]) > 64) {
-        int nd;
-        theta = radix_kth(keys, a.ng, a.beta, hist, lane, nd);
-      } else {
-        int nc = 0;
-        for (int w0 = 0; w0 < words; w0 += 64) {
-          // the word's eight reads go out together (lanes past the last
-          // word read the last one and keep no bits)
-          const int w = w0 + lane, wr = min(w, words - 1);
-          u32x4 k4[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) k4[q] = *reinterpret_cast<const u32x4*>(keys + 32 * wr + 4 * q);
-          __builtin_amdgcn_sched_barrier(0);
-          uint32_t inb = 0u;
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const bool in = 32 * w + 4 * q + e < a.ng;
-              inb |= (in && score_bucket(k4[q][e], lo, bscale) == bt) ? 1u << (4 * q + e) : 0u;
-            }
-          int total;
-          int pos = nc + wave_excl_scan(__popc(inb), lane, total);
-          while (inb) {
-            const int g = 32 * w + __ffs(inb) - 1;
-            cand[pos++] = make_uint2((uint32_t)g, keys[g]);
-            inb &= inb - 1u;
-          }
-          nc += total;
-        }
-        wave_lds_sync();
-        const uint2 me = lane < nc ? cand[lane] : make_uint2(0u, 0u);
-        int rank = 0;
-        for (int j = 0; j < nc; ++j) {
-          const uint32_t og = __builtin_amdgcn_readlane(me.x, j);
-          const uint32_t ok = __builtin_amdgcn_readlane(me.y, j);
-          rank += (ok > me.y) || (ok == me.y && og < me.x);
-        }
-        const uint64_t at = __builtin_amdgcn_ballot_w64(lane < nc && rank == need - 1);
-        theta = __builtin_amdgcn_readlane(me.y, __ffsll((unsigned long long)at) - 1);
-        wave_lds_sync();
-      }
-    }
-    // (2c) The band.  Without the exact router a computed score s differs
-    // from the exact one by at most bnd, so the beta-th exact score lies
-    // within bnd of theta: groups above theta + 2 bnd are taken, groups below
-    // theta - 2 bnd are not, and the groups between (the band; with the
-    // exact router, bnd = 0 and the band is theta's ties) are ranked by
-    // their exact scores (key descending, index ascending).
-    const bool mean = a.agg != HSQ_AGG_MAX;
+    const int sub = lane & 15, row = lane >> 4;
+    // The computed scores differ from the exact ones by at most bnd (zero
+    // with the exact router): r_max * max_h ||q'_h||_1 * (max |c - fp16(c)|
+    // + c_max 2^-14), the fp16 centroids plus the fp32 rounding of the MFMA
+    // sums and of the query split (both far below 2^-14 of the terms).  So
+    // the beta-th exact score lies within bnd of the beta-th computed one,
+    // theta: groups above theta + 2 bnd are taken, groups below theta - 2 bnd
+    // are not, and those between (the band) are ranked by exact scores
+    // (fp32 centroids and sums), then by index.
     float bnd = 0.f;
     if constexpr (!EXACT) {
       if (hsel) {
-        // bnd = r_max * max_h ||q'_h||_1 * (max |c - fp16(c)| + c_max 2^-14):
-        // the fp16 centroids, plus the fp32 rounding of the MFMA sums and of
-        // the query split (both far below 2^-14 of the terms' magnitudes)
-        float rmax = 0.f;
+        float rmax = 0.f, qn = 0.f;
         for (int w = 0; w < kWaves; ++w) rmax = fmaxf(rmax, s_rn[w]);
-        float qn = 0.f;
-        for (int h = 0; h < a.G; ++h) {
-          float sabs = 0.f;
-          for (int i = lane; i < D; i += 64) sabs += fabsf(qf[h * kQS<D> + i]);
-#pragma unroll
-          for (int o = 1; o < 64; o <<= 1) sabs += __shfl_xor(sabs, o, 64);
-          qn = fmaxf(qn, sabs);
-        }
+        for (int h = 0; h < a.G; ++h) qn = fmaxf(qn, s_qn[h]);
         const float cl = lane < 8 ? s_cb[lane] : 0.f;
         const float dl = wave_max(fabsf(cl - (float)(_Float16)cl));
         const float cm = wave_max(fabsf(cl));
         bnd = rmax * qn * (dl + cm * 0x1p-14f) * 1.0625f;
       }
     }
-    const float tf = key_float(theta);
-    const float tup = tf + 2.f * bnd, tdn = tf - 2.f * bnd;
-    // a bound that is not finite (overflowing inputs) puts every group in
-    // the band
-    const bool fin = __builtin_isfinite(tup) && __builtin_isfinite(tdn);
-    const uint32_t khi = EXACT ? theta : (fin ? fkey(tup) : 0xffffffffu);
-    const uint32_t klo = EXACT ? theta : (fin ? fkey(tdn) : 0u);
-    // bitmap word w (lane w % 64): groups above the band, and the band's
-    auto word_bits = [&](int w, uint32_t& above, uint32_t& inb) {
-      above = 0u;
-      inb = 0u;
-      const int wr = min(w, words - 1);
-      u32x4 k4[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) k4[q] = *reinterpret_cast<const u32x4*>(keys + 32 * wr + 4 * q);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t k = k4[q][e];
-          const bool in = 32 * w + 4 * q + e < a.ng;
-          above |= (in && k > khi) ? 1u << (4 * q + e) : 0u;
-          inb |= (in && k >= klo && k <= khi) ? 1u << (4 * q + e) : 0u;
-        }
-      }
-    };
-    // the band's groups, lane i holding the i-th (when at most 64); the
-    // first 64 words' above-band bits are kept for the emission
-    uint2 me = make_uint2(0u, 0u);
-    uint32_t above0 = 0u;
-    int nb = 0, n_above = 0;
-    if (hsel) {
-      for (int w0 = 0; w0 < words; w0 += 64) {
-        uint32_t above, inb;
-        word_bits(w0 + lane, above, inb);
-        if (w0 == 0) above0 = above;
-        int tot_a;
-        wave_excl_scan(__popc(above), lane, tot_a);
-        n_above += tot_a;
-        int total;
-        int pos = nb + wave_excl_scan(__popc(inb), lane, total);
-        while (inb) {
-          if (pos < 64) cand[pos] = make_uint2((uint32_t)(32 * (w0 + lane) + __ffs(inb) - 1), 0u);
-          ++pos;
-          inb &= inb - 1u;
-        }
-        nb += total;
-      }
-      wave_lds_sync();
-    }
-    const bool fallback = hsel && nb > 64;
-    const int sub = lane & 15, row = lane >> 4;
-    if (hsel && !fallback) {
-      // exact keys of the band's groups, four groups per pass (16 lanes each)
-      for (int j0 = 0; j0 < nb; j0 += 4) {
-        const int j = min(j0 + row, nb - 1);
-        const int g = (int)cand[j].x;
-        uint32_t k;
-        if constexpr (EXACT)
-          k = keys[g];
-        else
-          k = fkey(exact_score<D>(rk, rkn, g, sub, qf, s_cb, a.G, mean));
-        if (sub == 0 && j0 + row < nb) cand[j].y = k;
-      }
-      wave_lds_sync();
-      if (lane < nb) me = cand[lane];
-    } else if (fallback) {
-      // heavy ties: every group's exact key, then the radix select emits
-      if constexpr (!EXACT) {
-        for (int g0 = 0; g0 < a.ng; g0 += 4) {
-          const int g = min(g0 + row, a.ng - 1);
-          const uint32_t k = fkey(exact_score<D>(rk, rkn, g, sub, qf, s_cb, a.G, mean));
-          if (sub == 0 && g0 + row < a.ng) keys[g] = k;
-        }
-        wave_lds_sync();
-      }
-      top_beta_wave(keys, a.ng, a.beta, hist, sel, lane);
-    }
-    // rank the band by (exact key descending, index ascending): the first
-    // beta - n_above are taken
-    bool chosen = false;
-    if (hsel && !fallback) {
-      int rank = 0;
-      for (int j = 0; j < nb; ++j) {
-        const uint32_t og = __builtin_amdgcn_readlane(me.x, j);
-        const uint32_t ok = __builtin_amdgcn_readlane(me.y, j);
-        rank += (ok > me.y) || (ok == me.y && og < me.x);
-      }
-      chosen = lane < nb && rank < a.beta - n_above;
-    }
-    const uint64_t chosen_mask = __builtin_amdgcn_ballot_w64(chosen);
-    const bool rank_here = hsel && !fallback;
-    // emit the selection in ascending order (the radix select already did)
-    int nsel = 0;
-    if (fallback) {
-      nsel = a.beta;
-      for (int pos = lane; pos < nsel; pos += 64) {
-        const int g = sel[pos];
-        if (a.want_topk && a.idx) a.idx[(size_t)unit * a.beta + pos] = g;
-        if (recoff) recoff[pos] = (int32_t)((uint32_t)g * rec);
-      }
-    } else {
-      for (int w0 = 0; w0 < words; w0 += 64) {
-        const int w = w0 + lane;
-        uint32_t bits;
-        if (rank_here) {
-          uint32_t inb;
-          if (w0 == 0)
-            bits = above0;
-          else
-            word_bits(w, bits, inb);
-          for (uint64_t m = chosen_mask; m; m &= m - 1u) {
-            const int j = __ffsll((unsigned long long)m) - 1;
-            const uint32_t g = __builtin_amdgcn_readlane(me.x, j);
-            bits |= ((int)(g >> 5) == w) ? 1u << (g & 31) : 0u;
-          }
-        } else {
-          bits = (w < words) ? fmask[w] : 0u;
-        }
-        int total;
-        int pos = nsel + wave_excl_scan(__popc(bits), lane, total);
-        while (bits) {
-          const int g = 32 * w + __ffs(bits) - 1;
-          sel[pos] = g;
-          if (a.want_topk && a.idx) a.idx[(size_t)unit * a.beta + pos] = g;
-          if (recoff) recoff[pos] = (int32_t)((uint32_t)g * rec);
-          ++pos;
-          bits &= bits - 1u;
-        }
-        nsel += total;
-      }
-    }
+    SelIo io;
+    io.keys = keys; io.hist = hist; io.cand = cand; io.fmask = fmask;
+    io.words = words; io.ng = a.ng; io.beta = a.beta; io.G = a.G;
+    io.lo = lo; io.bscale = bscale; io.bnd = bnd; io.hsel = hsel; io.mean = want_mean;
+    io.rk = rk; io.rkn = rkn; io.qf = qf; io.cb = s_cb;
+    io.idx = (a.want_topk && a.idx) ? a.idx + (size_t)unit * a.beta : nullptr;
+    io.recoff = recoff; io.rec = rec; io.bits = nullptr;
+    const int nsel = select_wave<D, EXACT>(io, lane);
     wave_lds_sync();
-
     __builtin_amdgcn_s_setprio(2);
     // subtract the fetched summaries (list tiles of 16) with the same
     // arithmetic as they were added; rows past the list read nothing
@@ -1570,7 +1700,8 @@ template <int D, int N>
 __device__ __forceinline__ void attend_unit(const TokArgs& a, const AttendLds& L,
                                             TokTile (&tt)[kTokDepth], bool l1_issued,
                                             const int* bad_flag, const Softmax<D>* st_in,
-                                            int unit) {
+                                            int unit, int tile0 = 0, int tstride = 1,
+                                            float* part_out = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const uint32_t lane4 = (uint32_t)lane << 2;
   const uint32_t* lut4 = L.lut4;
@@ -1581,11 +1712,20 @@ __device__ __forceinline__ void attend_unit(const TokArgs& a, const AttendLds& L
   constexpr int LPV = D / 8;
   __builtin_amdgcn_s_setprio(1);  // see route_unit
 
+  // The tiles of this call: tile0, tile0 + tstride, ... below total (all of
+  // them by default); wave w takes the w-th, (w+8)-th, ... of those.  Past
+  // its last tile a wave names tiles just past total, whose record slots
+  // read as zero.
+  const int n_ck = tile0 < total ? (total - tile0 + tstride - 1) / tstride : 0;
+  const int iters = wave_iters(n_ck, wave);
+  auto tile_of = [&](int i) {
+    return i < iters ? tile0 + tstride * (wave + i * kWaves) : total + wave + kWaves * (i - iters);
+  };
   // this wave's first tiles not issued yet, loading while the table is built
 #pragma unroll
   for (int j = 0; j < kTokDepth - 1; ++j)
     if (!(l1_issued && wave + j * kWaves < n1t))  // wave-uniform
-      load_tok<D, N>(B, L.recoff, wave + j * kWaves, n1t, a.n1, lane, tt[j]);
+      load_tok<D, N>(B, L.recoff, tile_of(j), n1t, a.n1, lane, tt[j]);
   build_lut4(L.lut4, L.cb, tid);
   half8 qh[D / 32], ql[D / 32];
   query_operands<D>(L.qf, lane, qh, ql);
@@ -1604,12 +1744,10 @@ __device__ __forceinline__ void attend_unit(const TokArgs& a, const AttendLds& L
     const int ragged = (a.n1 & 15) ? n1t - 1 : -1;
     const int half = (N == 8 && (a.beta & 1)) ? total - 1 : -1;
     pipeline<kTokDepth>(
-        wave_iters(total, wave), tt,
-        [&](int i, TokTile& T) {
-          load_tok<D, N>(B, L.recoff, wave + i * kWaves, n1t, a.n1, lane, T);
-        },
+        iters, tt,
+        [&](int i, TokTile& T) { load_tok<D, N>(B, L.recoff, tile_of(i), n1t, a.n1, lane, T); },
         [&](int i, const TokTile& T) {
-          const int t = wave + i * kWaves;
+          const int t = tile_of(i);
           const bool masked = t == ragged || t == half || (any_bad && t >= n1t);
           consume_tok<D>(
               T, masked,
@@ -1620,6 +1758,10 @@ __device__ __forceinline__ void attend_unit(const TokArgs& a, const AttendLds& L
   lds_barrier();  // the table is no longer needed: reuse as scratch
   __builtin_amdgcn_s_setprio(0);
   float* scratch = reinterpret_cast<float*>(L.lut4);
+  if (part_out) {  // this call's partial, combined over the waves
+    combine_waves<D>(st, a.G, scratch, part_out, tid);
+    return;
+  }
   float* mine = scratch + kWaves * kMaxG * (D + 2);  // [G][D+2] this unit's token partial
   combine_waves<D>(st, a.G, scratch, mine, tid);
 
@@ -1806,6 +1948,367 @@ void step_kernel(SumArgs ra, TokArgs ta) {
   attend_unit<D, N>(ta, L, tt, false, nullptr, &st, unit);
 }
 
+// ------------------------------------------------------ split decode step ---
+//
+// For few units, or more summaries than the one-launch step holds on chip,
+// the step runs as four launches that spread every unit over many
+// work-groups (no cross-work-group synchronisation inside a launch; the
+// workspace carries the hand-overs):
+//   split_scores_kernel  chunk c of a unit's summary keys: per-head logits
+//                        (the router arithmetic above) and each group's
+//                        router key, both to the workspace
+//   split_select_kernel  one work-group per unit: histogram of the keys,
+//                        the exact top-beta (select_wave), the selection and
+//                        its bitmap
+//   split_attend_kernel  two kinds of work-groups: summary-value chunks (the
+//                        unfetched summaries, logits from the workspace) and
+//                        token chunks (L1 and fetched tiles); each writes one
+//                        partial (m, l, O) per head
+//   split_merge_kernel   one work-group per unit: log-sum-exp merge of the
+//                        partials, inverse V rotation, output
+
+constexpr int kScoreWaves = 2;                 // scores kernel: 2 waves, one tile each
+constexpr int kScoreTiles = kScoreWaves;
+
+struct SplitPlan {
+  int ngp, words, n_vt, n_tt;   // groups padded to 16; bitmap words; value / token tiles
+  int s1, sv, st, vt, tt;       // score chunks; value / token chunks; tiles per chunk
+};
+__host__ __device__ inline SplitPlan split_plan(int units, int n1, int ng, int beta, int N) {
+  SplitPlan p;
+  p.ngp = (ng + 15) & ~15;
+  p.words = (p.ngp + 31) / 32;
+  p.n_vt = p.ngp / 16;
+  p.n_tt = (n1 + 15) / 16 + (N == 16 ? beta : (beta + 1) / 2);
+  p.s1 = (p.n_vt + kScoreTiles - 1) / kScoreTiles;
+  // about 16 attend work-groups per unit, 2 .. 16 tiles each; the chunks
+  // depend on the unit's own sizes only, so a unit's result does not depend
+  // on the batch it is run in
+  (void)units;
+  int per = (p.n_vt + p.n_tt + 15) / 16;
+  per = per < 2 ? 2 : (per > 16 ? 16 : per);
+  p.vt = p.tt = per;
+  p.sv = (p.n_vt + per - 1) / per;
+  p.st = (p.n_tt + per - 1) / per;
+  if (p.st < 1) p.st = 1;
+  return p;
+}
+
+struct SplitArgs {
+  SumArgs r;        // router inputs (q, L2, signs, cb3, scale, bias, agg, G, Hkv, ng, beta, ngs)
+  TokArgs t;        // attend inputs
+  SplitPlan p;
+  float* lgt;       // [units][G][ngp] per-head logits
+  uint32_t* keys;   // [units][ngp] router keys
+  float* rn;        // [units][s1] largest key norm per score chunk
+  uint32_t* bits;   // [units][words] selection bitmap
+  int32_t* sel;     // [units][beta] selection
+  int32_t* idx_out; // optional [units][beta]
+  float* parts;     // [units][sv + st][G][D+2]
+};
+
+// Scores of 16 * kScoreTiles summaries of one unit: logits to a.lgt, router
+// keys to a.keys (EXACT: the three-term router, scores also to scores_out).
+template <int D, bool EXACT>
+__global__ __launch_bounds__(64 * kScoreWaves) void split_scores_kernel(SplitArgs a) {
+  constexpr int CB3 = 3 * D / 8;
+  __shared__ __align__(16) uint32_t s_lut3[64 * kNC3];
+  __shared__ __align__(16) uint32_t s_lut3lo[EXACT ? 64 * kNC3 : 4];
+  __shared__ __align__(16) float s_qf[kMaxG * kQS<D>];
+  __shared__ float s_cb[8];
+  __shared__ float s_rnw[kScoreWaves];
+  const SumArgs& r = a.r;
+  const int unit = blockIdx.x / a.p.s1, chunk = blockIdx.x % a.p.s1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int kvh = unit % r.Hkv;
+  const uint32_t lane4 = (uint32_t)(lane & 31) << 2;
+  const int c = lane & 15, gq = lane >> 4;
+  const rsrc_t rk = make_rsrc(r.l2k + (size_t)unit * r.ngs * CB3, (uint32_t)r.ng * CB3);
+  const rsrc_t rkn = make_rsrc(r.l2k_n + (size_t)unit * r.ngs, (uint32_t)r.ng * 4);
+  const int t = chunk * kScoreTiles + wave;  // this wave's tile
+  KeyTile kt;
+  load_keys<D>(rk, rkn, t, lane, kt);
+  QueryIn qin;
+  // the query rows are rotated by the first 8 * D / 8 threads: with two
+  // waves and D = 128 that is all of them; each thread does its share
+  const float cbv = (tid < 8) ? r.cb3[tid] : 0.f;
+  if (tid < 8) s_cb[tid] = cbv;
+  for (int base = 0; base < kMaxG * (D / 8); base += 64 * kScoreWaves) {
+    load_query<D>(r.q + (size_t)unit * r.G * D, r.k_signs + kvh * (D / 32), r.G, base + tid, qin);
+    rotate_query<D>(qin, r.scale * rsqrtf((float)D), s_qf, base + tid);
+  }
+  lds_barrier();
+  for (int e = tid; e < 64 * 8; e += 64 * kScoreWaves) {
+    build_lut3(s_lut3, s_cb, e);
+    if constexpr (EXACT) build_lut3_lo(s_lut3lo, s_cb, e);
+  }
+  half8 qb[D / 32];
+  router_operands<D>(s_qf, lane, qb);
+  lds_barrier();
+  uint32_t kw[3];
+  key_bits<D>(kt.kw, lane, kw);
+  f32x4 lg = qk3<D, EXACT>(kw, qb, s_lut3, s_lut3lo, lane4) * kt.kn;
+  const float rn = wave_max(max3f(max3f(kt.kn[0], kt.kn[1], kt.kn[2]), kt.kn[3], 0.f));
+  const int g0 = 16 * t + 4 * gq;
+  const bool live = t < a.p.n_vt;  // wave-uniform: the last chunk may have a tile past the end
+  if (live && c < r.G) {
+    float* dst = a.lgt + ((size_t)unit * r.G + c) * a.p.ngp + g0;
+    *reinterpret_cast<f32x4*>(dst) = lg;
+  }
+  // router score of rows g0 .. g0+3: max (or mean) over the lanes c < G of
+  // this row of 16 lanes
+  const bool mean = r.agg != HSQ_AGG_MAX;
+  float sc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float x = (c < r.G) ? lg[i] : (mean ? 0.f : kNegInf);
+    if (mean) {
+      x = group_sum<16>(x) * (1.f / (float)r.G);
+    } else {
+      x = fmaxf(x, dpp_f<0xb1>(x));
+      x = fmaxf(x, dpp_f<0x4e>(x));
+      x = fmaxf(x, dpp_f<0x141>(x));
+      x = fmaxf(x, dpp_f<0x140>(x));
+    }
+    sc[i] = x;
+  }
+  if (live && c == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = g0 + i < r.ng;
+      a.keys[(size_t)unit * a.p.ngp + g0 + i] = ok ? fkey(sc[i]) : 0u;
+      if (EXACT && r.scores_out && ok) r.scores_out[(size_t)unit * r.ng + g0 + i] = sc[i];
+    }
+  }
+  if (lane == 0) s_rnw[wave] = rn;
+  lds_barrier();
+  if (tid == 0) {
+    float m = 0.f;
+    for (int w = 0; w < kScoreWaves; ++w) m = fmaxf(m, s_rnw[w]);
+    a.rn[(size_t)unit * a.p.s1 + chunk] = m;
+  }
+}
+
+// Selection of one unit from its router keys (eight waves: keys to LDS and
+// the histogram; then one wave selects).  LDS: [keys ngp][hist 256][cand 64]
+// [fmask words][qf].
+template <int D, bool EXACT>
+__global__ __launch_bounds__(kThreads) void split_select_kernel(SplitArgs a) {
+  constexpr int CB3 = 3 * D / 8;
+  extern __shared__ __align__(16) char smem[];
+  __shared__ float s_cb[8];
+  __shared__ float s_qn[kMaxG];
+  __shared__ float s_lo[kWaves], s_hi[kWaves];
+  const SumArgs& r = a.r;
+  const int unit = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int kvh = unit % r.Hkv;
+  const SplitPlan& p = a.p;
+  uint32_t* keys = reinterpret_cast<uint32_t*>(smem);
+  int* hist = reinterpret_cast<int*>(keys + ((p.ngp + 31) & ~31));
+  uint2* cand = reinterpret_cast<uint2*>(hist + 256);
+  uint32_t* fmask = reinterpret_cast<uint32_t*>(cand + 64);
+  float* qf = reinterpret_cast<float*>(fmask + ((p.words + 3) & ~3));
+  const rsrc_t rk = make_rsrc(r.l2k + (size_t)unit * r.ngs * CB3, (uint32_t)r.ng * CB3);
+  const rsrc_t rkn = make_rsrc(r.l2k_n + (size_t)unit * r.ngs, (uint32_t)r.ng * 4);
+  const float cbv = (tid < 8) ? r.cb3[tid] : 0.f;
+  QueryIn qin;
+  load_query<D>(r.q + (size_t)unit * r.G * D, r.k_signs + kvh * (D / 32), r.G, tid, qin);
+  float lo = kPosInf, hi = kNegInf;
+  const uint32_t* kin = a.keys + (size_t)unit * p.ngp;
+  for (int g = tid; g < p.ngp; g += kThreads) {
+    const uint32_t k = kin[g];
+    keys[g] = k;
+    if (g < r.ng) {
+      const float f = key_float(k);
+      lo = fminf(lo, f);
+      hi = fmaxf(hi, f);
+    }
+  }
+  for (int b = tid; b < 256; b += kThreads) hist[b] = 0;
+  for (int w = tid; w < p.words; w += kThreads) {
+    const int left = r.ng - 32 * w;
+    fmask[w] = (r.beta >= r.ng) ? (left >= 32 ? 0xffffffffu : (left <= 0 ? 0u : ((1u << left) - 1u)))
+                                : 0u;
+    a.bits[(size_t)unit * p.words + w] = 0u;
+  }
+  if (tid < 8) s_cb[tid] = cbv;
+  rotate_query<D>(qin, r.scale * rsqrtf((float)D), qf, tid, s_qn);
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  if (lane == 0) {
+    s_lo[wave] = lo;
+    s_hi[wave] = hi;
+  }
+  __syncthreads();  // also orders the bitmap's zeroing before its atomics below
+  lo = kPosInf;
+  hi = kNegInf;
+  for (int w = 0; w < kWaves; ++w) {
+    lo = fminf(lo, s_lo[w]);
+    hi = fmaxf(hi, s_hi[w]);
+  }
+  const float bscale = (hi > lo) ? 256.f / (hi - lo) : 0.f;
+  const bool hsel = r.beta > 0 && r.beta < r.ng;
+  if (hsel)
+    for (int g = tid; g < r.ng; g += kThreads) atomicAdd(&hist[score_bucket(keys[g], lo, bscale)], 1);
+  lds_barrier();
+  if (wave != 0) return;
+  float bnd = 0.f;
+  if constexpr (!EXACT) {
+    if (hsel) {
+      float rmax = 0.f, qn = 0.f;
+      for (int k = lane; k < p.s1; k += 64) rmax = fmaxf(rmax, a.rn[(size_t)unit * p.s1 + k]);
+      rmax = wave_max(rmax);
+      for (int h = 0; h < r.G; ++h) qn = fmaxf(qn, s_qn[h]);
+      const float cl = lane < 8 ? s_cb[lane] : 0.f;
+      const float dl = wave_max(fabsf(cl - (float)(_Float16)cl));
+      const float cm = wave_max(fabsf(cl));
+      bnd = rmax * qn * (dl + cm * 0x1p-14f) * 1.0625f;
+    }
+  }
+  SelIo io;
+  io.keys = keys; io.hist = hist; io.cand = cand; io.fmask = fmask;
+  io.words = p.words; io.ng = r.ng; io.beta = r.beta; io.G = r.G;
+  io.lo = lo; io.bscale = bscale; io.bnd = bnd; io.hsel = hsel;
+  io.mean = r.agg != HSQ_AGG_MAX;
+  io.rk = rk; io.rkn = rkn; io.qf = qf; io.cb = s_cb;
+  io.idx = a.sel + (size_t)unit * r.beta;
+  io.recoff = nullptr; io.rec = 0u;
+  io.bits = a.bits + (size_t)unit * p.words;
+  const int nsel = select_wave<D, EXACT>(io, lane);
+  if (a.idx_out)
+    for (int i = lane; i < nsel; i += 64) a.idx_out[(size_t)unit * r.beta + i] = (int32_t)keys[i];
+}
+
+// Attend work-groups.  blockIdx: unit * (sv + st) + k; k < sv: summary-value
+// chunk k (tiles k * vt ..), else token chunk k - sv (tiles k - sv, with
+// stride st, of the unit's L1 and fetched tiles).  Each writes its partial
+// (m, l, O) per head to parts[unit][k].
+template <int D, int N>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void split_attend_kernel(SplitArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  __shared__ __align__(16) uint32_t s_tab[kLut4Bytes / 4];
+  __shared__ float s_cb[16];
+  const SplitPlan& p = a.p;
+  const int per = p.sv + p.st;
+  const int unit = blockIdx.x / per, k = blockIdx.x % per;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int G = a.r.G;
+  float* part = a.parts + ((size_t)unit * per + k) * G * (D + 2);
+  if (k < p.sv) {
+    // summary values of tiles k * vt .. (k + 1) * vt - 1, unfetched rows only
+    constexpr int CB3 = 3 * D / 8;
+    const SumArgs& r = a.r;
+    const rsrc_t rv = make_rsrc(r.l2v + (size_t)unit * r.ngs * CB3, (uint32_t)r.ng * CB3);
+    const rsrc_t rvn = make_rsrc(r.l2v_n + (size_t)unit * r.ngs, (uint32_t)r.ng * 4);
+    const int t0 = k * p.vt, nt = min(p.vt, p.n_vt - t0);
+    const int iters = wave_iters(nt, wave);
+    constexpr int K = kValDepth;
+    auto tile = [&](int i) { return i < iters ? t0 + wave + i * kWaves : p.n_vt + wave; };
+    ValTile vt[K];
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j) load_vals<D>(rv, rvn, tile(j), lane, vt[j]);
+    const float cbv = (tid < 8) ? r.cb3[tid] : 0.f;
+    if (tid < 8) s_cb[tid] = cbv;
+    lds_barrier();
+    build_lut3(s_tab, s_cb, tid);
+    lds_barrier();
+    const int c = lane & 15, gq = lane >> 4, hcol = min(c >> 1, G - 1);
+    const uint32_t lane4 = (uint32_t)(lane & 31) << 2;
+    const float* lrow = a.lgt + ((size_t)unit * G + hcol) * p.ngp + 4 * gq;
+    const uint32_t* bw = a.bits + (size_t)unit * p.words;
+    const uint32_t vsh = val_shift<D>(lane);
+    Softmax<D> st;
+    st.init(kNegInf);
+    pipeline<K>(
+        iters, vt, [&](int i, ValTile& V) { load_vals<D>(rv, rvn, tile(i), lane, V); },
+        [&](int i, const ValTile& V) {
+          const int t = tile(i);
+          const f32x4 lg4 = *reinterpret_cast<const f32x4*>(lrow + 16 * t);
+          const uint32_t fw = bw[(16 * t + 4 * gq) >> 5] >> ((16 * t + 4 * gq) & 31);
+          float lg[4], pw[4];
+          bool live[4];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            live[rr] = 16 * t + 4 * gq + rr < r.ng && !((fw >> rr) & 1u);
+            lg[rr] = live[rr] ? lg4[rr] : kNegInf;
+          }
+          st.update(lg, pw);
+          float w[4];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            // a masked row weighs 0 (also while no live row has set the
+            // reference, where exp(-inf - -inf) is not a number)
+            pw[rr] = live[rr] ? pw[rr] : 0.f;
+            st.l += pw[rr];
+            w[rr] = pw[rr] * V.vn[rr];
+          }
+          pv3<D>(V.va, vsh, weight_operand(w, lane), lane4, s_tab, st.O);
+        });
+    st.m += r.bias;
+    lds_barrier();
+    combine_waves<D>(st, G, reinterpret_cast<float*>(s_tab), part, tid);
+    return;
+  }
+  // token chunk: the attend body over tiles (k - sv), (k - sv) + st, ...
+  const TokArgs& ta = a.t;
+  const int kvh = unit % ta.Hkv;
+  AttendLds L;
+  L.lut4 = s_tab;
+  L.qf = reinterpret_cast<float*>(smem);
+  L.part = nullptr;
+  L.recoff = reinterpret_cast<int32_t*>(L.qf + kMaxG * kQS<D>);
+  L.cb = s_cb;
+  L.vsb = nullptr;
+  const size_t rec = (size_t)N * (D + 8);
+  const float cbv = (tid < 16) ? ta.cb4[tid] : 0.f;
+  QueryIn qin;
+  load_query<D>(ta.q + (size_t)unit * G * D, ta.k_signs + kvh * (D / 32), G, tid, qin);
+  const int32_t* sel = a.sel + (size_t)unit * ta.beta;
+  for (int s = tid; s < tok_slots<N>(ta.beta); s += kThreads) {
+    const int g = s < ta.beta ? sel[s] : -1;
+    const bool ok = g >= 0 && g < ta.ng;
+    L.recoff[s] = ok ? (int32_t)((uint32_t)g * (uint32_t)rec) : (int32_t)kFar;
+  }
+  if (tid < 16) s_cb[tid] = cbv;
+  rotate_query<D>(qin, ta.scale * rsqrtf((float)D), L.qf, tid);
+  lds_barrier();
+  TokTile tt[kTokDepth];
+  attend_unit<D, N>(ta, L, tt, false, nullptr, nullptr, unit, k - p.sv, p.st, part);
+}
+
+// Merge of one unit's partials and the inverse V rotation (8 * D / 8
+// threads: head h, 8 coordinates per thread).
+template <int D>
+__global__ __launch_bounds__(kMaxG * (D / 8)) void split_merge_kernel(SplitArgs a) {
+  constexpr int LPV = D / 8;
+  const int unit = blockIdx.x, tid = threadIdx.x, h = tid / LPV, sub = tid % LPV;
+  const int G = a.r.G, per = a.p.sv + a.p.st;
+  const int kvh = unit % a.t.Hkv;
+  if (h >= G) return;  // whole row groups: the lanes of one head stay together
+  const float* base = a.parts + (size_t)unit * per * G * (D + 2) + h * (D + 2);
+  float M = kNegInf;
+  for (int k = 0; k < per; ++k) M = fmaxf(M, base[(size_t)k * G * (D + 2)]);
+  float L = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < per; ++k) {
+    const float* pk = base + (size_t)k * G * (D + 2);
+    const float m = pk[0];
+    const float w = (m == kNegInf) ? 0.f : __expf(m - M);
+    L += w * pk[1];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] += w * pk[2 + 8 * sub + e];
+  }
+  const float inv = (L > 0.f) ? 1.f / L : 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] *= inv;
+  fwht8xlanes<LPV>(o, sub);
+  const uint32_t sb = sign_byte(a.t.v_signs + kvh * (D / 32), sub);
+  const float sc = rsqrtf((float)D);
+  float* dst = a.t.out + ((size_t)unit * G + h) * D + 8 * sub;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dst[e] = flip(o[e] * sc, (sb >> e) & 1u);
+}
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t summary_smem(int D, const StepShape& s) {
@@ -1830,20 +2333,34 @@ size_t step_smem(const StepShape& s) {
 
 }  // namespace
 
+int route_lds_ok(const StepShape& s) { return s.G * ((s.n_groups + 15) & ~15) <= kMaxLogits; }
+
+int use_split(const StepShape& s) {
+  return s.n_groups > 0 && (s.B * s.Hkv < kSplitUnits || !route_lds_ok(s));
+}
+
 Workspace plan_workspace(const StepShape& s) {
   Workspace w{};
   const int units = s.B * s.Hkv;
   size_t off = 0;
   w.idx_off = off;  off = align256(off + (size_t)units * std::max(s.beta, 1) * 4);
   w.part_off = off; off = align256(off + (size_t)units * s.G * (s.d + 2) * 4);
+  if (use_split(s)) {
+    const SplitPlan p = split_plan(units, s.n_l1, s.n_groups, s.beta, s.group_n);
+    w.lgt_off = off;   off = align256(off + (size_t)units * s.G * p.ngp * 4);
+    w.keys_off = off;  off = align256(off + (size_t)units * p.ngp * 4);
+    w.rn_off = off;    off = align256(off + (size_t)units * p.s1 * 4);
+    w.bits_off = off;  off = align256(off + (size_t)units * p.words * 4);
+    w.parts_off = off; off = align256(off + (size_t)units * (p.sv + p.st) * s.G * (s.d + 2) * 4);
+  }
   w.total = off;
   return w;
 }
 
 int step_limits_ok(const StepShape& s) {
   const size_t rec = (size_t)s.group_n * (s.d + 8);
-  return s.n_groups <= kMaxGroups && s.G * ((s.n_groups + 15) & ~15) <= kMaxLogits &&
-         (size_t)s.n_groups * rec < 0x7fffffffu && (size_t)s.n_l1 * s.d < 0x7fffffffu;
+  return s.n_groups <= kMaxGroups && (size_t)s.n_groups * rec < 0x7fffffffu &&
+         (size_t)s.n_l1 * s.d < 0x7fffffffu;
 }
 
 SumArgs sum_args(const StepShape& s, const StepTensors& t) {
@@ -1888,11 +2405,87 @@ hipError_t summary_d(const StepShape& s, const StepTensors& t, const Workspace& 
   return hipGetLastError();
 }
 
+SplitArgs split_args(const StepShape& s, const StepTensors& t, const Workspace& w, char* ws) {
+  SplitArgs a{};
+  a.r = sum_args(s, t);
+  a.t = tok_args(s, t);
+  a.p = split_plan(s.B * s.Hkv, s.n_l1, s.n_groups, s.beta, s.group_n);
+  a.lgt = reinterpret_cast<float*>(ws + w.lgt_off);
+  a.keys = reinterpret_cast<uint32_t*>(ws + w.keys_off);
+  a.rn = reinterpret_cast<float*>(ws + w.rn_off);
+  a.bits = reinterpret_cast<uint32_t*>(ws + w.bits_off);
+  a.sel = reinterpret_cast<int32_t*>(ws + w.idx_off);
+  a.parts = reinterpret_cast<float*>(ws + w.parts_off);
+  return a;
+}
+
+size_t select_smem(const SplitPlan& p, int D) {
+  return (size_t)((p.ngp + 31) & ~31) * 4 + 256 * 4 + 64 * 8 + (size_t)((p.words + 3) & ~3) * 4 +
+         (size_t)kMaxG * (D + 4) * 4;
+}
+
+// Scores and selection of the split step (route only when attend is false).
+template <int D>
+hipError_t split_route_d(const SplitArgs& a, int units, bool exact, hipStream_t st) {
+  const SplitPlan& p = a.p;
+  if (exact)
+    hipLaunchKernelGGL((split_scores_kernel<D, true>), dim3((unsigned)(units * p.s1)),
+                       dim3(64 * kScoreWaves), 0, st, a);
+  else
+    hipLaunchKernelGGL((split_scores_kernel<D, false>), dim3((unsigned)(units * p.s1)),
+                       dim3(64 * kScoreWaves), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (exact)
+    hipLaunchKernelGGL((split_select_kernel<D, true>), dim3((unsigned)units), dim3(kThreads),
+                       select_smem(p, D), st, a);
+  else
+    hipLaunchKernelGGL((split_select_kernel<D, false>), dim3((unsigned)units), dim3(kThreads),
+                       select_smem(p, D), st, a);
+  return hipGetLastError();
+}
+
+template <int D, int N>
+hipError_t split_step_dn(const SplitArgs& a, int units, hipStream_t st) {
+  hipError_t e = split_route_d<D>(a, units, false, st);
+  if (e != hipSuccess) return e;
+  const SplitPlan& p = a.p;
+  const size_t smem = (size_t)kMaxG * kQS<D> * 4 + (size_t)tok_slots<N>(a.t.beta) * 4;
+  hipLaunchKernelGGL((split_attend_kernel<D, N>), dim3((unsigned)(units * (p.sv + p.st))),
+                     dim3(kThreads), smem, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((split_merge_kernel<D>), dim3((unsigned)units), dim3(kMaxG * (D / 8)), 0, st,
+                     a);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_step(const StepShape& s, const StepTensors& t, const Workspace& w,
+                             char* ws, int32_t* idx_out, hipStream_t st) {
+  if (!step_limits_ok(s) || !use_split(s)) return hipErrorInvalidValue;
+  SplitArgs a = split_args(s, t, w, ws);
+  a.idx_out = s.beta > 0 ? idx_out : nullptr;
+  const int units = s.B * s.Hkv;
+  if (s.d == 128)
+    return s.group_n == 16 ? split_step_dn<128, 16>(a, units, st)
+                           : split_step_dn<128, 8>(a, units, st);
+  return s.group_n == 16 ? split_step_dn<64, 16>(a, units, st) : split_step_dn<64, 8>(a, units, st);
+}
+
 hipError_t launch_route(const StepShape& s, const StepTensors& t, const Workspace& w, char* ws,
                         int mode, const int32_t* given, float* scores_out, int32_t* idx_out,
                         hipStream_t st) {
   if (s.n_groups == 0) return hipSuccess;
   if (!step_limits_ok(s)) return hipErrorInvalidValue;
+  if (!route_lds_ok(s)) {
+    // more router logits than LDS holds: the split route (scores to the
+    // workspace, then the selection) serves the router-only call
+    if (mode != ROUTE_TOPK || !use_split(s)) return hipErrorInvalidValue;
+    SplitArgs a = split_args(s, t, w, ws);
+    a.r.scores_out = scores_out;
+    a.idx_out = s.beta > 0 ? idx_out : nullptr;
+    return s.d == 128 ? split_route_d<128>(a, s.B * s.Hkv, scores_out != nullptr, st)
+                      : split_route_d<64>(a, s.B * s.Hkv, scores_out != nullptr, st);
+  }
   return s.d == 128 ? summary_d<128>(s, t, w, ws, mode, given, scores_out, idx_out, st)
                     : summary_d<64>(s, t, w, ws, mode, given, scores_out, idx_out, st);
 }
@@ -1914,7 +2507,7 @@ hipError_t token_d(const StepShape& s, const StepTensors& t, const Workspace& w,
 
 hipError_t launch_attn(const StepShape& s, const StepTensors& t, const Workspace& w, char* ws,
                        const int32_t* idx, hipStream_t st) {
-  if (!step_limits_ok(s)) return hipErrorInvalidValue;
+  if (!step_limits_ok(s) || (s.n_groups > 0 && !route_lds_ok(s))) return hipErrorInvalidValue;
   return s.d == 128 ? token_d<128>(s, t, w, ws, idx, st) : token_d<64>(s, t, w, ws, idx, st);
 }
 
@@ -1931,7 +2524,7 @@ hipError_t step_dn(const StepShape& s, const StepTensors& t, int32_t* idx_out, h
 }
 
 int step_fused_ok(const StepShape& s) {
-  return s.n_groups > 0 && step_limits_ok(s) && step_smem(s) <= kMaxFusedLds;
+  return s.n_groups > 0 && step_limits_ok(s) && route_lds_ok(s) && step_smem(s) <= kMaxFusedLds;
 }
 
 hipError_t launch_step(const StepShape& s, const StepTensors& t, int32_t* idx_out,

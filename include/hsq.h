@@ -79,11 +79,10 @@ const char* hsq_last_error(void);
  * proportional to (1 - y^2)^((d-3)/2) on [-1, 1].  Computed on the host in
  * double precision by Lloyd iteration to its fixed point (centroid =
  * conditional mean of its cell, threshold = midpoint of neighbouring
- * centroids), made exactly odd-symmetric.  Stored tables: each centroid
- * rounded to the nearest fp16 value (via fp32, ties to even), returned as
- * fp32; each threshold the exact midpoint of its two stored neighbours (an
- * fp32 value), so quantising with the thresholds is nearest-centroid
- * against the stored centroids.
+ * centroids), made exactly odd-symmetric.  Stored tables: the fixed
+ * point's centroids and its thresholds (midpoints formed in double
+ * precision), each rounded to the nearest fp32 value, so the tables satisfy
+ * both Lloyd conditions to fp32 rounding.
  *   d           3..4096 (any integer; the codec itself needs d in {64,128})
  *   bits        1..4
  *   centroids   host out, [2^bits] ascending
@@ -217,12 +216,22 @@ int hsq_build_tiers(const void* k, const void* v, int dtype, int B, int Hkv, int
  *   agg         HSQ_AGG_MAX or HSQ_AGG_MEAN
  *   beta        >= 0, clamped to n_groups
  *   topk_idx    out int32 [B][Hkv][min(beta, n_groups)]
- *   scores      optional out fp32 [B][Hkv][n_groups] (NULL = not written)
+ *   scores      optional out fp32 [B][Hkv][n_groups] (NULL = not written).
+ *               When asked for, the router adds the centroids' low parts and
+ *               the scores are fp32-accurate; otherwise the selection is
+ *               still exact: groups whose computed score lies within the
+ *               computed scores' error bound of the beta-th are re-scored with
+ *               the fp32 centroids before the tie-break.
  *   workspace   device, >= hsq_workspace_bytes(...) bytes, 256-byte aligned;
  *               holds the selection and the summary-attention partials
  *               between the launches of one call.  No initial contents are
  *               needed.  Calls that share a workspace must be ordered on one
  *               stream.
+ * When G * n_groups exceeds 12288 (more router logits than one work-group
+ * holds on chip) the scores go through the workspace (two launches).
+ * Errors: HSQ_ERR_ARG (null pointers, negative sizes, bad agg),
+ * HSQ_ERR_UNSUPPORTED (d, G > 8, n_groups > 16384), HSQ_ERR_WORKSPACE,
+ * HSQ_ERR_HIP.
  */
 int hsq_route_topk(const float* q, int B, int Hq, int Hkv, int d, const uint8_t* l2k,
                    const float* l2k_n, int n_groups, const uint32_t* k_signs, const float* cb3,
@@ -243,6 +252,8 @@ int hsq_route_topk(const float* q, int B, int Hq, int Hkv, int d, const uint8_t*
  *               [B][Hkv][beta] in topk_idx order (hsq_gather_l3 output)
  *   cb4, cb3    fp32 centroids [16], [8] (device)
  *   out         fp32 [B][Hq][d]; a unit with no entries at all gets zeros
+ * Errors: as hsq_route_topk; HSQ_ERR_UNSUPPORTED also when G * n_groups
+ * exceeds 12288 (hsq_decode_step serves such shapes).
  */
 int hsq_decode_attn(const float* q, int B, int Hq, int Hkv, int d, const uint8_t* l1k,
                     const float* l1k_n, const uint8_t* l1v, const float* l1v_n, int n_l1,
@@ -257,11 +268,15 @@ int hsq_decode_attn(const float* q, int B, int Hq, int Hkv, int d, const uint8_t
  * hsq_decode_step -- the whole decode step of one layer: route, top-beta and
  * attention [HSQ "Decode process" steps 1-3]: hsq_route_topk followed by
  * hsq_decode_attn with l3_staged == 0 (the same selection; the output to
- * fp32 rounding of the order in which the partials merge).  Runs as
- * one launch, one work-group per (b, kvh) with the selection and the
- * summary partial kept on chip; when n_groups == 0 or the shape needs more
- * on-chip memory than that launch has, as two launches through the
- * workspace.
+ * fp32 rounding of the order in which the partials merge).  With 128 or
+ * more units (b, kvh) and G * n_groups <= 12288 it runs as one launch, one
+ * work-group per unit with the selection and the summary partial kept on
+ * chip.  With fewer units, or more groups, it runs as the split step: four
+ * launches that spread each unit over many work-groups (router logits and
+ * keys, the selection, summary-value and token chunks as partials, a
+ * log-sum-exp merge), with the hand-overs in the workspace; a unit's result
+ * depends only on its own inputs, not on the batch.  With n_groups == 0 it
+ * runs as two launches.
  *   topk_idx    optional out int32 [B][Hkv][min(beta, n_groups)] (NULL = not
  *               returned)
  *   other arguments as in hsq_route_topk / hsq_decode_attn
@@ -289,6 +304,7 @@ int hsq_decode_step(const float* q, int B, int Hq, int Hkv, int d, const uint8_t
  *                    from the workspace written by the preceding
  *                    hsq_step_route with the same sizes and workspace.
  * Both take n_l1 and n_groups so they size the workspace identically.
+ * Errors: as hsq_decode_attn (G * n_groups at most 12288).
  */
 int hsq_step_route(const float* q, int B, int Hq, int Hkv, int d, int n_l1, const uint8_t* l2k,
                    const float* l2k_n, const uint8_t* l2v, const float* l2v_n, int n_groups,

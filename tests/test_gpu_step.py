@@ -287,10 +287,14 @@ def oracle_tiers(sc):
     return t
 
 
+# Fewer than 128 (sequence, kv-head) units run the split step (four
+# launches); 128 or more the one-launch step.  Both kinds are here.
 SMALL = [
     ("tiny", W.TINY),
     ("q8-2k", W.QWEN3_8B_8K.smaller(T=2048, batch=2, n_marked=41)),
     ("q14-2k", W.QWEN3_14B_16K.smaller(T=2048, batch=2, n_marked=20)),
+    ("q14-1k-b16", W.QWEN3_14B_16K.smaller(T=1024, batch=16, n_marked=10)),
+    ("q8-1k-b16", W.QWEN3_8B_8K.smaller(T=1100, batch=16, n_marked=11, beta=9)),
 ]
 
 
@@ -589,6 +593,25 @@ def test_qwen3_8b_8k_full_size():
     sc = Scenario(w)
     worst, n_codes, n_diff = check_full(sc, w.beta)
     print(f"  worst rel L2 {worst:.3e}, {n_codes} code / {n_diff} set differences", flush=True)
+
+
+def test_long_context_beyond_on_chip_logits():
+    # 40/8 heads (G = 5), N = 8, T = 32768: about 4050 groups, so G * n_groups
+    # is beyond what the one-launch step keeps on chip; the split step
+    # streams the router logits through the workspace
+    w = W.QWEN3_14B_16K.smaller(T=32768, batch=2, n_marked=328)
+    print("long context G=5 N=8 T=32768", flush=True)
+    sc = Scenario(w)
+    assert w.G * ((sc.tiers.ng + 15) // 16 * 16) > 12288
+    worst, n_codes, n_diff = check_full(sc, w.beta)
+    print(f"  worst rel L2 {worst:.3e}, {n_codes} code / {n_diff} set differences", flush=True)
+    # the router alone (exact scores through the workspace) agrees with the
+    # step's selection and with the oracle's scores
+    idx, scores = hsq.route_topk(sc.q, sc.tiers, sc.dks, sc.cb3, w.beta, want_scores=True)
+    _, idx2 = hsq.decode_step(sc.q, sc.tiers, w.beta, sc.dks, sc.dvs, sc.cb4, sc.cb3)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+    check_route(sc, idx, scores, [(0, 0), (1, 7)], w.beta)
 
 
 @pytest.mark.parametrize("layer", [0, 35])
