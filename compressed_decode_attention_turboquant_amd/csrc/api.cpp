@@ -384,6 +384,36 @@ extern "C" int hsq_decode_step(const float* q, int B, int Hq, int Hkv, int d, co
                          beta, k_signs, v_signs, cb4, scale, workspace, ws_bytes, out, stream);
 }
 
+extern "C" int hsq_decode_step_static(const float* q, int B, int Hq, int Hkv, int d,
+                                      const uint8_t* l1k, const float* l1k_n, const uint8_t* l1v,
+                                      const float* l1v_n, int n_l1, const uint8_t* l2k,
+                                      const float* l2k_n, const uint8_t* l2v, const float* l2v_n,
+                                      int n_groups, const uint8_t* l3, int group_n, int beta,
+                                      int agg, const uint32_t* k_signs, const uint32_t* v_signs,
+                                      const float* cb4, const float* cb3, float scale,
+                                      float summary_bias, int32_t* topk_idx, float* out,
+                                      void* stream) {
+  const char* fn = "hsq_decode_step_static";
+  int rc = check_step_shape(fn, B, Hq, Hkv, d, n_l1, n_groups, group_n, beta);
+  if (rc) return rc;
+  const int b = beta < n_groups ? beta : n_groups;
+  StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, b};
+  if (!step_limits_ok(s))
+    return fail(HSQ_ERR_UNSUPPORTED, std::string(fn) + ": n_groups, G * n_groups or the L1/L3 "
+                                     "sizes exceed the kernels' limits");
+  const size_t need = plan_workspace(s).total;
+  if (need > kStaticScratchBytes)
+    return fail(HSQ_ERR_UNSUPPORTED,
+                std::string(fn) + ": these sizes need " + std::to_string(need) +
+                    " bytes of scratch; the static scratch holds " +
+                    std::to_string(kStaticScratchBytes) + " (use hsq_decode_step with a workspace)");
+  void* scratch = nullptr;
+  if ((rc = static_scratch(&scratch))) return rc;
+  return hsq_decode_step(q, B, Hq, Hkv, d, l1k, l1k_n, l1v, l1v_n, n_l1, l2k, l2k_n, l2v, l2v_n,
+                         n_groups, l3, group_n, beta, agg, k_signs, v_signs, cb4, cb3, scale,
+                         summary_bias, topk_idx, scratch, kStaticScratchBytes, out, stream);
+}
+
 extern "C" int hsq_gather_l3(const uint8_t* l3_src, size_t rec_bytes, int B, int Hkv,
                              int n_groups, const int32_t* topk_idx, int beta, uint8_t* staging,
                              void* stream) {

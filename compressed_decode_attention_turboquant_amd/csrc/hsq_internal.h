@@ -152,6 +152,12 @@ struct QjlLogitsJob {
 };
 hipError_t launch_qjl_logits(const QjlLogitsJob& j, hipStream_t s);
 
+// ---- device scratch of the entry points that allocate nothing (scratch.hip) --
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+// Address of this device's scratch array (looked up on the first call on
+// each device, with that device current).
+int static_scratch(void** out);
+
 // ---- host-side method pieces (host.cpp) -------------------------------------
 int codebook(int d, int bits, float* centroids, float* thresholds);
 

@@ -290,6 +290,28 @@ int hsq_decode_step(const float* q, int B, int Hq, int Hkv, int d, const uint8_t
                     void* workspace, size_t ws_bytes, float* out, void* stream);
 
 /*
+ * hsq_decode_step_static -- hsq_decode_step without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * workspace is a file-scope device array of 8 MiB per GPU, kept until the
+ * process ends; the call allocates nothing and calls no allocating routine.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other host threads) race; calls on one stream are
+ * ordered and safe.  The array needs no initial contents (each call writes
+ * what it later reads).
+ * Errors: as hsq_decode_step; HSQ_ERR_UNSUPPORTED when the sizes need more
+ * than 8 MiB of workspace (hsq_workspace_bytes) or the device ordinal is
+ * above 63; HSQ_ERR_HIP when the array's address cannot be looked up.
+ */
+int hsq_decode_step_static(const float* q, int B, int Hq, int Hkv, int d, const uint8_t* l1k,
+                           const float* l1k_n, const uint8_t* l1v, const float* l1v_n, int n_l1,
+                           const uint8_t* l2k, const float* l2k_n, const uint8_t* l2v,
+                           const float* l2v_n, int n_groups, const uint8_t* l3, int group_n,
+                           int beta, int agg, const uint32_t* k_signs, const uint32_t* v_signs,
+                           const float* cb4, const float* cb3, float scale, float summary_bias,
+                           int32_t* topk_idx, float* out, void* stream);
+
+/*
  * hsq_step_route / hsq_step_attend -- the two launches of hsq_decode_step,
  * exposed so a caller can put work between them: the host-archive path runs
  * hsq_step_route, then hsq_gather_l3 (PCIe, side stream), then
