@@ -178,15 +178,45 @@ __device__ __forceinline__ float wave_max(float x) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 __device__ __forceinline__ float wave_min(float x) { return -wave_max(-x); }
-// Wave-wide unsigned minimum / maximum (butterfly: every lane gets it).
+// Wave-wide unsigned minimum / maximum by the same DPP steps (no LDS
+// traffic); wave-uniform result.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, ROWS, 0xf, false);
+}
 __device__ __forceinline__ uint32_t wave_umin(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, o, 64));
-  return x;
+  x = min(x, dpp_u<0xb1>(x));
+  x = min(x, dpp_u<0x4e>(x));
+  x = min(x, dpp_u<0x141>(x));
+  x = min(x, dpp_u<0x140>(x));
+  x = min(x, dpp_u<0x142, 0xa>(x));
+  x = min(x, dpp_u<0x143, 0xc>(x));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 __device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o, 64));
+  x = max(x, dpp_u<0xb1>(x));
+  x = max(x, dpp_u<0x4e>(x));
+  x = max(x, dpp_u<0x141>(x));
+  x = max(x, dpp_u<0x140>(x));
+  x = max(x, dpp_u<0x142, 0xa>(x));
+  x = max(x, dpp_u<0x143, 0xc>(x));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+// Inclusive prefix sum over the lanes of a wave by DPP steps (no LDS
+// traffic): row shifts by 1, 2, 4, 8 sum each row of 16 lanes, then the row
+// broadcasts of lanes 15 and 31 carry the totals of the lower rows.  A lane
+// whose source is outside its row, or whose row is masked off, adds 0.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ int dpp_z(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xf, false);
+}
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp_z<0x111>(x);       // row_shr:1
+  x += dpp_z<0x112>(x);       // row_shr:2
+  x += dpp_z<0x114>(x);       // row_shr:4
+  x += dpp_z<0x118>(x);       // row_shr:8
+  x += dpp_z<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_z<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
   return x;
 }
 // Sum over aligned groups of LANES (8 or 16) consecutive lanes by DPP row
@@ -516,9 +546,6 @@ __device__ __forceinline__ uint32_t fkey(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum over the work-group.
-
-
 // Inverse of fkey.
 __device__ __forceinline__ float key_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
@@ -532,11 +559,11 @@ __device__ __forceinline__ int score_bucket(uint32_t key, float lo, float scale)
 }
 
 
-// Top-beta by a score histogram (0 < beta < ng).  The scores are bucketed
-// over [lo, hi] (any bounds of the scores) in 256 equal steps; every bucket
-// above the one holding the beta-th largest score is taken whole, and the
-// scores of that bucket are ranked exactly by (key descending, index
-// ascending), which is the order of the full sort.
+// Top-beta (0 < beta < ng) starts from a histogram of the scores over
+// [lo, hi] (any bounds of the scores) in 256 equal steps, which places the
+// beta-th largest score in one bucket; select_wave then counts and ranks
+// keys against bounds around that bucket, so the result is the order of the
+// full sort by (key descending, index ascending).
 
 // The threshold bucket and how many of its scores to take, from the full
 // histogram; every wave computes it (no barrier needed).
@@ -548,12 +575,7 @@ __device__ __forceinline__ void hist_threshold(const int* hist, int beta, int la
     cnt[k] = hist[255 - 4 * lane - k];
     sum += cnt[k];
   }
-  int incl = sum;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
+  const int incl = wave_incl_scan(sum);
   int my_bt = 0, my_need = 0, acc = incl - sum;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -571,12 +593,8 @@ __device__ __forceinline__ void hist_threshold(const int* hist, int beta, int la
 
 // Exclusive prefix sum of v over the lanes of a wave, plus the wave total.
 __device__ __forceinline__ int wave_excl_scan(int v, int lane, int& total) {
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
+  (void)lane;
+  const int incl = wave_incl_scan(v);
   total = __builtin_amdgcn_readlane(incl, 63);
   return incl - v;
 }
@@ -737,18 +755,32 @@ __device__ __forceinline__ f32x4 qk3(const uint32_t (&kw)[3], const half8 (&b)[D
 // selection's tie-break for groups near the beta-th score).  The 16 lanes of
 // a row (sub = lane & 15) share the work, D/16 coordinates each; every lane
 // of the row returns the score.  qf: rotated, scaled query rows; cb: the
-// eight fp32 centroids.
+// eight fp32 centroids.  exact_load issues the group's loads and
+// exact_from does the arithmetic, so that several groups' loads can be in
+// flight together.
 template <int D>
-__device__ __forceinline__ float exact_score(rsrc_t rk, rsrc_t rkn, int g, int sub, const float* qf,
-                                             const float* cb, int G, bool mean) {
+struct ExactRaw {
+  uint32_t w;  // this lane's code bits (D/16 codes from bit 0)
+  float r;     // the key norm
+};
+template <int D>
+__device__ __forceinline__ ExactRaw<D> exact_load(rsrc_t rk, rsrc_t rkn, int g, int sub) {
   constexpr int CB3 = 3 * D / 8, PER = D / 16;
   const uint32_t bit = 3u * PER * (uint32_t)sub;
   const uint32_t byte = min(bit >> 3, (uint32_t)(CB3 - 4));  // the dword stays inside the row
-  const uint32_t w = ld32(rk, (uint32_t)g * CB3 + byte) >> (bit - 8u * byte);
-  const float r = __uint_as_float(ld32(rkn, (uint32_t)g * 4u));
+  ExactRaw<D> x;
+  x.w = ld32(rk, (uint32_t)g * CB3 + byte);
+  x.r = __uint_as_float(ld32(rkn, (uint32_t)g * 4u));
+  x.w >>= bit - 8u * byte;
+  return x;
+}
+template <int D>
+__device__ __forceinline__ float exact_from(const ExactRaw<D>& x, int sub, const float* qf,
+                                            const float* cb, int G, bool mean) {
+  constexpr int PER = D / 16;
   float cv[PER];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) cv[k] = cb[(w >> (3 * k)) & 7u];
+  for (int k = 0; k < PER; ++k) cv[k] = cb[(x.w >> (3 * k)) & 7u];
   float best = kNegInf, sum = 0.f;
   for (int h = 0; h < G; ++h) {
     const float* qr = qf + h * kQS<D> + PER * sub;
@@ -756,11 +788,52 @@ __device__ __forceinline__ float exact_score(rsrc_t rk, rsrc_t rkn, int g, int s
 #pragma unroll
     for (int k = 0; k < PER; ++k) acc = __builtin_fmaf(qr[k], cv[k], acc);
     acc = group_sum<16>(acc);
-    const float lg = acc * r;
+    const float lg = acc * x.r;
     best = fmaxf(best, lg);
     sum += lg;
   }
   return mean ? sum * (1.f / (float)G) : best;
+}
+template <int D>
+__device__ __forceinline__ float exact_score(rsrc_t rk, rsrc_t rkn, int g, int sub, const float* qf,
+                                             const float* cb, int G, bool mean) {
+  return exact_from<D>(exact_load<D>(rk, rkn, g, sub), sub, qf, cb, G, mean);
+}
+// exact_from for P groups at once (P passes of four): each head's query
+// slice is read once for all of them.
+template <int D, int P>
+__device__ __forceinline__ void exact_from_p(const ExactRaw<D> (&x)[P], int sub, const float* qf,
+                                             const float* cb, int G, bool mean, float (&out)[P]) {
+  constexpr int PER = D / 16;
+  float cv[P][PER];
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+#pragma unroll
+    for (int k = 0; k < PER; ++k) cv[p][k] = cb[(x[p].w >> (3 * k)) & 7u];
+  float best[P], sum[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    best[p] = kNegInf;
+    sum[p] = 0.f;
+  }
+  for (int h = 0; h < G; ++h) {
+    const float* qr = qf + h * kQS<D> + PER * sub;
+    float q[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) q[k] = qr[k];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) acc = __builtin_fmaf(q[k], cv[p][k], acc);
+      acc = group_sum<16>(acc);
+      const float lg = acc * x[p].r;
+      best[p] = fmaxf(best[p], lg);
+      sum[p] += lg;
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < P; ++p) out[p] = mean ? sum[p] * (1.f / (float)G) : best[p];
 }
 
 // Keys of tile t (16 summaries): this lane's raw key words (D = 128: 96 bits
@@ -889,8 +962,9 @@ __device__ __forceinline__ RouteLds route_lds(char* base, const RouteLayout& r, 
   return L;
 }
 
-// Top-beta of the unit's router keys by one wave, emitted in ascending
-// order (see the band rule above): into io.keys[0..beta) (the keys array is
+// Top-beta of the unit's router keys by one wave (groups within bnd of the
+// threshold are ranked by their exact scores), emitted in ascending
+// order: into io.keys[0..beta) (the keys array is
 // reused), io.idx, io.recoff (record offsets) and io.bits (bitmap of the
 // selected groups, whole words) when those are set.  Without hsel the
 // selection is io.fmask.  Returns the number of groups selected.
@@ -910,10 +984,27 @@ struct SelIo {
   uint32_t rec;            // record bytes (recoff = g * rec)
   uint32_t* bits;          // out [words] bitmap or null
 };
+// Key bounds [Klo, Khi) of the scores in buckets bt-1 .. bt+1 of the
+// histogram over [lo, lo + 256 / bscale]; false when the histogram's range is
+// degenerate.  Keys at the bounds may land one bucket off the histogram's own
+// rounding; the selection counts keys against the bounds, never the
+// histogram's counts, so only the bounds' order matters.
+__device__ __forceinline__ bool c_bounds(int bt, float lo, float bscale, uint32_t& Klo,
+                                         uint32_t& Khi) {
+  const float step = 1.f / bscale;
+  if (!(bscale > 0.f && __builtin_isfinite(step) && __builtin_isfinite(lo))) return false;
+  const int blb = max(bt - 1, 0), bup = bt + 2;
+  Klo = blb == 0 ? 0u : fkey(lo + (float)blb * step);
+  Khi = bup > 255 ? 0xffffffffu : fkey(lo + (float)bup * step);
+  return true;
+}
+
 template <int D, bool EXACT>
 __device__ int select_wave(const SelIo& io, int lane) {
   const int sub = lane & 15, row = lane >> 4;
   const float bnd = io.bnd;
+  constexpr uint32_t kMark = 0xffffffffu;  // key of a chosen group (see below)
+  const int nkey = 32 * io.words;          // entries of the keys array
   // keys of the band's edges around theta (a bound that is not finite,
   // from overflowing inputs, puts every group in the band)
   auto band_keys = [&](uint32_t theta, uint32_t& khi, uint32_t& klo) {
@@ -927,15 +1018,27 @@ __device__ int select_wave(const SelIo& io, int lane) {
       klo = fin ? fkey(tdn) : 0u;
     }
   };
-  // exact keys of up to 64 listed groups io.cand[0..n) (into io.cand[j].y), four
-  // groups per pass (16 lanes each); the exact router's keys are exact
+  // exact keys of listed groups io.cand[0..n) (into io.cand[j].y), four
+  // groups per pass (16 lanes each), the loads of four passes issued
+  // together; the exact router's keys are exact already
   auto rescore = [&](int n) {
     if constexpr (!EXACT) {
-      for (int j0 = 0; j0 < n; j0 += 4) {
-        const int j = min(j0 + row, n - 1);
-        const int g = (int)io.cand[j].x;
-        const uint32_t k = fkey(exact_score<D>(io.rk, io.rkn, g, sub, io.qf, io.cb, io.G, io.mean));
-        if (sub == 0 && j0 + row < n) io.cand[j].y = k;
+      constexpr int P = 4;
+      for (int j0 = 0; j0 < n; j0 += 4 * P) {
+        ExactRaw<D> raw[P];
+        int jj[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          jj[p] = min(j0 + 4 * p + row, n - 1);
+          raw[p] = ExactRaw<D>{0u, 0.f};
+          if (j0 + 4 * p < n)  // wave-uniform
+            raw[p] = exact_load<D>(io.rk, io.rkn, (int)io.cand[jj[p]].x, sub);
+        }
+        float sc[P];
+        exact_from_p<D, P>(raw, sub, io.qf, io.cb, io.G, io.mean, sc);
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+          if (sub == 0 && j0 + 4 * p + row < n) io.cand[jj[p]].y = fkey(sc[p]);
       }
       wave_lds_sync();
     }
@@ -950,88 +1053,81 @@ __device__ int select_wave(const SelIo& io, int lane) {
     }
     return rank;
   };
-  // Fast path.  The threshold bucket bt (histogram); C = the groups of
-  // buckets bt-1 .. bt+1, one per lane (at most 64); theta from ranking C.
-  // Every group above C is above the band and every group below C below
-  // it when the smallest key above C exceeds theta + 2 bnd and the largest
-  // below C is under theta - 2 bnd, so the band is inside C.
+  // Every path below ends in the same form: the selection is the groups
+  // whose key is >= kth once the chosen groups near the threshold have had
+  // their key replaced by kMark (none of them compares >= kth before).
   uint2 me = make_uint2(0u, 0u), bme = make_uint2(0u, 0u);
-  uint64_t mask_a = 0u, mask_b = 0u;  // chosen lanes of me (above the band) / of bme (band)
-  uint32_t above0 = 0u;
-  int bhi = 255;
+  uint64_t mask_a = 0u, mask_b = 0u;  // chosen lanes of me / of bme
+  uint32_t kth = kMark;
   bool fast = false;
+  // Fast path.  The histogram's threshold bucket bt gives key bounds
+  // [Klo, Khi) around buckets bt-1 .. bt+1; one pass over the keys counts
+  // the groups at or above Khi exactly and lists C, those in [Klo, Khi).
+  // When the beta-th key lies in C (and C fits a wave), theta = that key is
+  // found bit by bit from C's keys, and if the band [theta - 2 bnd,
+  // theta + 2 bnd] lies inside [Klo, Khi), every group at or above Khi is
+  // above the band and every group below Klo below it; only the band's
+  // groups need their exact keys.
   if (io.hsel) {
-    int bt, need;
-    hist_threshold(io.hist, io.beta, lane, bt, need);
-    bhi = min(bt + 1, 255);
-    const int blb = max(bt - 1, 0);
-    int n_hi = 0;  // groups in buckets above bhi
-    {
-      int cnt = 0;
+    int bt, need_h;
+    hist_threshold(io.hist, io.beta, lane, bt, need_h);
+    uint32_t Klo = 0u, Khi = 0u;
+    int n_hi = 0, nc = 0;
+    const bool have = c_bounds(bt, io.lo, io.bscale, Klo, Khi);
+    if (have) {
+      for (int b0 = 0; b0 < io.ng; b0 += 2048) {  // 8 reads of 4 keys per lane
+        u32x4 k4[8];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int b = 255 - 4 * lane - k;
-        cnt += b > bhi ? io.hist[b] : 0;
+        for (int q = 0; q < 8; ++q)
+          k4[q] = *reinterpret_cast<const u32x4*>(io.keys + min(b0 + 256 * q + 4 * lane, nkey - 4));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int g = b0 + 256 * q + 4 * lane + e;
+            const uint32_t k = k4[q][e];
+            const bool in = g < io.ng;
+            n_hi += __popcll(__builtin_amdgcn_ballot_w64(in && k >= Khi));
+            const uint64_t inc = __builtin_amdgcn_ballot_w64(in && k >= Klo && k < Khi);
+            if (inc) {  // wave-uniform
+              const int p = nc + (int)__builtin_amdgcn_mbcnt_hi(
+                                     (uint32_t)(inc >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)inc, 0u));
+              if (((inc >> lane) & 1u) && p < 64) io.cand[p] = make_uint2((uint32_t)g, k);
+              nc += __popcll(inc);
+            }
+          }
       }
-      wave_excl_scan(cnt, lane, n_hi);
-    }
-    uint32_t amin = 0xffffffffu, bmax = 0u;
-    int nc = 0;
-    for (int w0 = 0; w0 < io.words; w0 += 64) {
-      const int w = w0 + lane, wr = min(w, io.words - 1);
-      u32x4 k4[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) k4[q] = *reinterpret_cast<const u32x4*>(io.keys + 32 * wr + 4 * q);
-      __builtin_amdgcn_sched_barrier(0);
-      uint32_t above = 0u, inc = 0u;
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t k = k4[q][e];
-          const bool in = 32 * w + 4 * q + e < io.ng;
-          const int b = score_bucket(k, io.lo, io.bscale);
-          above |= (in && b > bhi) ? 1u << (4 * q + e) : 0u;
-          inc |= (in && b >= blb && b <= bhi) ? 1u << (4 * q + e) : 0u;
-          amin = (in && b > bhi) ? min(amin, k) : amin;
-          bmax = (in && b < blb) ? max(bmax, k) : bmax;
+      wave_lds_sync();
+      const int need = io.beta - n_hi;
+      if (need > 0 && need <= nc && nc <= 64) {
+        me = lane < nc ? io.cand[lane] : make_uint2(0u, 0u);
+        // theta: the largest t with at least `need` keys of C >= t
+        uint32_t t = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t c = t | (1u << bit);
+          if (__popcll(__builtin_amdgcn_ballot_w64(lane < nc && me.y >= c)) >= need) t = c;
         }
-      if (w0 == 0) above0 = above;
-      int total;
-      int pos = nc + wave_excl_scan(__popc(inc), lane, total);
-      while (inc) {
-        const int g = 32 * w + __ffs(inc) - 1;
-        if (pos < 64) io.cand[pos] = make_uint2((uint32_t)g, io.keys[g]);
-        ++pos;
-        inc &= inc - 1u;
-      }
-      nc += total;
-    }
-    const uint32_t amin_all = wave_umin(amin), bmax_all = wave_umax(bmax);
-    wave_lds_sync();
-    if (nc <= 64) {
-      me = lane < nc ? io.cand[lane] : make_uint2(0u, 0u);
-      const int rank = rank_of(me, nc);
-      const uint64_t at = __builtin_amdgcn_ballot_w64(lane < nc && rank == io.beta - n_hi - 1);
-      const uint32_t theta = __builtin_amdgcn_readlane(me.y, __ffsll((unsigned long long)at) - 1);
-      uint32_t khi, klo;
-      band_keys(theta, khi, klo);
-      fast = amin_all > khi && bmax_all < klo;
-      if (fast) {
-        const bool abv = lane < nc && me.y > khi;
-        const bool inb = lane < nc && me.y >= klo && me.y <= khi;
-        mask_a = __builtin_amdgcn_ballot_w64(abv);
-        const int need2 = io.beta - n_hi - __popcll(mask_a);
-        // the band's groups, listed in cand and rescored
-        int nb;
-        const int pos = wave_excl_scan(inb ? 1 : 0, lane, nb);
-        wave_lds_sync();
-        if (inb) io.cand[pos] = make_uint2(me.x, me.y);
-        wave_lds_sync();
-        rescore(nb);
-        bme = lane < nb ? io.cand[lane] : make_uint2(0u, 0u);
-        const int rb = rank_of(bme, nb);
-        mask_b = __builtin_amdgcn_ballot_w64(lane < nb && rb < need2);
+        uint32_t khi, klo;
+        band_keys(t, khi, klo);
+        fast = Klo <= klo && khi < Khi;
+        if (fast) {
+          mask_a = __builtin_amdgcn_ballot_w64(lane < nc && me.y > khi);
+          const int need2 = need - __popcll(mask_a);
+          const uint64_t bm = __builtin_amdgcn_ballot_w64(lane < nc && me.y >= klo && me.y <= khi);
+          const int nb = __popcll(bm);
+          const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+          // the band's groups, listed in cand and rescored
+          wave_lds_sync();
+          if ((bm >> lane) & 1u) io.cand[pos] = me;
+          wave_lds_sync();
+          rescore(nb);
+          bme = lane < nb ? io.cand[lane] : make_uint2(0u, 0u);
+          const int rb = rank_of(bme, nb);
+          mask_b = __builtin_amdgcn_ballot_w64(lane < nb && rb < need2);
+          kth = Khi;
+        }
       }
     }
   }
@@ -1039,14 +1135,12 @@ __device__ int select_wave(const SelIo& io, int lane) {
   // select over all keys and the band by a scan of all keys; a band of
   // more than 64 groups rescores every group, and the radix select over
   // the exact keys emits the selection.
-  bool by_key = false, radix = false;
-  uint32_t khi_e = 0u;
+  bool radix = false;
   if (io.hsel && !fast) {
     int nd;
     const uint32_t theta = radix_kth(io.keys, io.ng, io.beta, io.hist, lane, nd);
-    uint32_t klo;
+    uint32_t khi_e, klo;
     band_keys(theta, khi_e, klo);
-    by_key = true;
     int n_above = 0, nb = 0;
     for (int w0 = 0; w0 < io.words; w0 += 64) {
       const int w = w0 + lane, wr = min(w, io.words - 1);
@@ -1064,7 +1158,6 @@ __device__ int select_wave(const SelIo& io, int lane) {
           above |= (in && k > khi_e) ? 1u << (4 * q + e) : 0u;
           inb |= (in && k >= klo && k <= khi_e) ? 1u << (4 * q + e) : 0u;
         }
-      if (w0 == 0) above0 = above;
       int tot_a;
       wave_excl_scan(__popc(above), lane, tot_a);
       n_above += tot_a;
@@ -1087,6 +1180,7 @@ __device__ int select_wave(const SelIo& io, int lane) {
       bme = lane < nb ? io.cand[lane] : make_uint2(0u, 0u);
       const int rb = rank_of(bme, nb);
       mask_b = __builtin_amdgcn_ballot_w64(lane < nb && rb < io.beta - n_above);
+      kth = khi_e == kMark ? kMark : khi_e + 1u;
     } else {
       if constexpr (!EXACT) {
         for (int g0 = 0; g0 < io.ng; g0 += 4) {
@@ -1100,27 +1194,13 @@ __device__ int select_wave(const SelIo& io, int lane) {
       radix = true;
     }
   }
-  // emit the selection in ascending order (the radix select already did):
-  // word w's bits are the groups above C (fast path) or above the band
-  // (general path), plus the chosen lanes of me and bme
-  auto above_bits = [&](int w) {
-    const int wr = min(w, io.words - 1);
-    u32x4 k4[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) k4[q] = *reinterpret_cast<const u32x4*>(io.keys + 32 * wr + 4 * q);
-    __builtin_amdgcn_sched_barrier(0);
-    uint32_t above = 0u;
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t k = k4[q][e];
-        const bool in = 32 * w + 4 * q + e < io.ng;
-        const bool up = by_key ? k > khi_e : score_bucket(k, io.lo, io.bscale) > bhi;
-        above |= (in && up) ? 1u << (4 * q + e) : 0u;
-      }
-    return above;
-  };
+  // the chosen groups near the threshold take the key kMark
+  if (io.hsel && !radix) {
+    if ((mask_a >> lane) & 1u) io.keys[me.x] = kMark;
+    if ((mask_b >> lane) & 1u) io.keys[bme.x] = kMark;
+    wave_lds_sync();
+  }
+  // emit the selection in ascending order (the radix select already did)
   int nsel = 0;
   if (radix) {
     nsel = io.beta;
@@ -1131,19 +1211,24 @@ __device__ int select_wave(const SelIo& io, int lane) {
       if (io.bits) atomicOr(&io.bits[g >> 5], 1u << (g & 31));
     }
   } else {
+    // lane w holds word w's bits (groups 32w .. 32w+31); an id is written at
+    // or below the position of the keys still to be read
     for (int w0 = 0; w0 < io.words; w0 += 64) {
       const int w = w0 + lane;
-      uint32_t bits;
+      uint32_t bits = 0u;
       if (io.hsel) {
-        bits = (w0 == 0) ? above0 : above_bits(w);
-        for (uint64_t m = mask_a; m; m &= m - 1u) {
-          const uint32_t g = __builtin_amdgcn_readlane(me.x, __ffsll((unsigned long long)m) - 1);
-          bits |= ((int)(g >> 5) == w) ? 1u << (g & 31) : 0u;
-        }
-        for (uint64_t m = mask_b; m; m &= m - 1u) {
-          const uint32_t g = __builtin_amdgcn_readlane(bme.x, __ffsll((unsigned long long)m) - 1);
-          bits |= ((int)(g >> 5) == w) ? 1u << (g & 31) : 0u;
-        }
+        const int wr = min(w, io.words - 1);
+        u32x4 k4[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) k4[q] = *reinterpret_cast<const u32x4*>(io.keys + 32 * wr + 4 * q);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool in = 32 * w + 4 * q + e < io.ng;
+            bits |= (in && k4[q][e] >= kth) ? 1u << (4 * q + e) : 0u;
+          }
       } else {
         bits = (w < io.words) ? io.fmask[w] : 0u;
       }
@@ -1172,12 +1257,16 @@ __device__ int select_wave(const SelIo& io, int lane) {
 // per wave in *st_out (reference maximum including the summary bias) for
 // the attend phase of the same work-group to continue.
 // recoff: if not null, LDS table that receives g * rec for selection slot s.
-template <int D, bool EXACT>
+// pre(): called by every wave once its share of the stream (or the
+// selection) is done, before the work-group waits for the selection; the
+// caller issues the first loads of its next phase there.
+template <int D, bool EXACT, typename PreF>
 __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, float* part_out,
                                            Softmax<D>* st_out, int32_t* recoff, uint32_t rec,
-                                           int unit) {
+                                           int unit, PreF pre) {
   constexpr int CB3 = 3 * D / 8;
   __shared__ float s_cb[8];
+  __shared__ int s_nsel;   // size of the selection
   __shared__ float s_lo[kWaves], s_hi[kWaves];
   __shared__ float s_mh[kWaves][kMaxG];
   __shared__ float s_rn[kWaves];  // largest key norm seen by each wave
@@ -1281,8 +1370,8 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   // values of ALL summaries into their softmax partials (tiles w, w + 7,
   // ...); the fetched ones are subtracted at the end with the same weights.
   // The eighth wave meanwhile finds the threshold, settles the groups near
-  // it, emits the selection and subtracts the fetched summaries.  No other
-  // barrier until the end.
+  // it and emits the selection.  (3) After one barrier all eight waves
+  // subtract the fetched summaries, and a last barrier ends the route.
   constexpr int K = kValDepth;
   constexpr int kSel = kWaves - 1;  // the selecting wave
   const bool stream = a.want_partial && a.beta < a.ng;  // else the partial is empty
@@ -1430,28 +1519,39 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
     io.idx = (a.want_topk && a.idx) ? a.idx + (size_t)unit * a.beta : nullptr;
     io.recoff = recoff; io.rec = rec; io.bits = nullptr;
     const int nsel = select_wave<D, EXACT>(io, lane);
-    wave_lds_sync();
+    if (lane == 0) s_nsel = nsel;
     __builtin_amdgcn_s_setprio(2);
-    // subtract the fetched summaries (list tiles of 16) with the same
-    // arithmetic as they were added; rows past the list read nothing
+  }
+  // the caller's first loads of its next phase, in flight across the barrier
+  pre();
+  if (!a.want_partial) return;
+  lds_barrier();  // the selection is visible to every wave
+  if (stream) {
+    // (3) subtract the fetched summaries (list tiles of 16, dealt to the
+    // waves in turn) with the same arithmetic as they were added; rows past
+    // the list read nothing
+    const int nsel = __builtin_amdgcn_readfirstlane(s_nsel);
     constexpr int RB = 3 * D / 8;
     const uint32_t vb = val_byte<D>(lane);
-    const int ntl = stream ? (nsel + 15) / 16 : 0;
+    const int ntl = (nsel + 15) / 16;
+    const int nci = wave_iters(ntl, wave);
     struct CorrTile {
       ValTile V;
       float lg[4];
     };
-    // The list rows of tile j + 1 are read while tile j's loads are issued
-    // (the list's last tile is reread past its end; sel holds 16 * ntl
-    // entries); the logits are masked at their use, so no load waits on LDS.
+    // The list rows of the wave's next tile are read while the current
+    // tile's loads are issued (a tile past the list rereads the last one);
+    // the logits are masked at their use, so no load waits on LDS.
     const float* lcol = logits + hcol * ngp;
-    auto sel_rows = [&](int j) {
-      return *reinterpret_cast<const u32x4*>(sel + 16 * min(j, max(ntl - 1, 0)) + 4 * gq);
+    auto sel_rows = [&](int i) {
+      const int j = min(wave + i * kWaves, max(ntl - 1, 0));
+      return *reinterpret_cast<const u32x4*>(sel + 16 * j + 4 * gq);
     };
     u32x4 gnext = sel_rows(0);
-    auto corr_load = [&](int j, CorrTile& C) {
+    auto corr_load = [&](int i, CorrTile& C) {
       const u32x4 g4 = gnext;
-      gnext = sel_rows(j + 1);
+      gnext = sel_rows(i + 1);
+      const int j = wave + i * kWaves;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool in = 16 * j + 4 * gq + r < nsel;
@@ -1464,17 +1564,18 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
         C.lg[r] = lcol[g];
       }
     };
-    CorrTile ct[K];
+    constexpr int KC = 2;
+    CorrTile ct[KC];
 #pragma unroll
-    for (int j = 0; j < K - 1; ++j) corr_load(j, ct[j]);
-    pipeline<K>(ntl, ct, corr_load, [&](int j, const CorrTile& C) {
+    for (int j = 0; j < KC - 1; ++j) corr_load(j, ct[j]);
+    pipeline<KC>(nci, ct, corr_load, [&](int i, const CorrTile& C) {
+      const int j = wave + i * kWaves;
       float lg[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) lg[r] = (16 * j + 4 * gq + r < nsel) ? C.lg[r] : kNegInf;
       consume(lg, C.V, -1.f);
     });
   }
-  if (!a.want_partial) return;
   lds_barrier();  // the logits are no longer needed: reuse as scratch
   st.m += a.bias;
   if (st_out) {
@@ -1504,7 +1605,8 @@ __global__ __launch_bounds__(kThreads) void summary_kernel(SumArgs a) {
   RouteLds L = route_lds<D>(smem, r, s_lut3, qf, dummy, qf);
   L.lut3lo = s_lut3lo;
   const int unit = blockIdx.x;
-  route_unit<D, EXACT>(a, L, a.part + (size_t)unit * a.G * (D + 2), nullptr, nullptr, 0u, unit);
+  route_unit<D, EXACT>(a, L, a.part + (size_t)unit * a.G * (D + 2), nullptr, nullptr, 0u, unit,
+                       [] {});
 }
 
 // ----------------------------------------------------------- token kernel ---
@@ -1934,8 +2036,20 @@ void step_kernel(SumArgs ra, TokArgs ta) {
                                   reinterpret_cast<float*>(rbase + S.dummy), nullptr);
   // ends with a barrier: the selection and record offsets are visible and
   // the union is free; each wave's summary partial stays in st
+  // this wave's first L1 tiles (they need no selection) are issued before
+  // the route's last barrier, so they load during its end and the table set-up
+  const TokBufs TB = tok_bufs<D, N>(ta, unit);
+  const int n1t = (ta.n1 + 15) / 16;
+  const int wave = wave_id();
+  TokTile tt[kTokDepth];
+  auto pre = [&] {
+#pragma unroll
+    for (int j = 0; j < kTokDepth - 1; ++j)
+      if (wave + j * kWaves < n1t)  // wave-uniform
+        load_tok_at<D, N>(TB, wave + j * kWaves, n1t, ta.n1, kFar, kFar, tid & 63, tt[j]);
+  };
   Softmax<D> st;
-  route_unit<D, false>(ra, R, nullptr, &st, recoff, (uint32_t)(N * (D + 8)), unit);
+  route_unit<D, false>(ra, R, nullptr, &st, recoff, (uint32_t)(N * (D + 8)), unit, pre);
 
   AttendLds L;
   L.lut4 = tab;
@@ -1944,8 +2058,7 @@ void step_kernel(SumArgs ra, TokArgs ta) {
   L.recoff = recoff;
   L.cb = s_cb4;
   L.vsb = s_vsb;
-  TokTile tt[kTokDepth];
-  attend_unit<D, N>(ta, L, tt, false, nullptr, &st, unit);
+  attend_unit<D, N>(ta, L, tt, true, nullptr, &st, unit);
 }
 
 // ------------------------------------------------------ split decode step ---
