@@ -101,7 +101,7 @@ __global__ __launch_bounds__(64) void append_kernel(AppendJob a, Div32 one) {
     j.group_n = 1;
     j.codes = (isv ? a.l1v : a.l1k) + (l1u + a.n_fix + a.slot) * (D / 2);
     j.norms = (isv ? a.l1v_n : a.l1k_n) + l1u + a.n_fix + a.slot;
-    encode_one<D, 4, true, 64>(j, q, 0u, sub, v, sword, tpos, false, nullptr);
+    encode_one<D, 4, true>(j, q, 0u, sub, v, sword, tpos, false, nullptr);
   } else if (grp < 4 && a.seal) {
     const bool isv = grp == 3;
     const void* x = isv ? a.raw_v : a.raw_k;
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(64) void append_kernel(AppendJob a, Div32 one) {
     j.group_n = a.group_n;
     j.codes = (isv ? a.l2v : a.l2k) + ((size_t)u * a.ng_cap + a.ng) * (3 * D / 8);
     j.norms = (isv ? a.l2v_n : a.l2k_n) + (size_t)u * a.ng_cap + a.ng;
-    encode_one<D, 3, true, 64>(j, q, 0u, sub, v, sword, tpos, false, nullptr);
+    encode_one<D, 3, true>(j, q, 0u, sub, v, sword, tpos, false, nullptr);
   }
 }
 

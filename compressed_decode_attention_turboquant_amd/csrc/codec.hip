@@ -71,58 +71,53 @@ __global__ __launch_bounds__(kWG) void encode_kernel(EncodeJob j, EncodeDivs q) 
     }
   }
 
-  // 4 bits: a table of kBins equal bins of |y| over [0, 1) (the last one open
-  // above) replaces the seven compares.  Bin b holds the number of positive
-  // thresholds below its start and the threshold inside it, if any; the count
-  // for a key in the bin is then that number plus one compare.  It is exact
-  // when no bin holds two thresholds (true for the Beta codebooks at d = 64
-  // and 128, whose closest thresholds are >= 0.022 apart); otherwise the
-  // work-group counts all seven.  Built while the loads above are in flight.
-  constexpr int kBins = 64;
-  __shared__ uint2 s_bin[kBins];
-  __shared__ int s_two_in_a_bin;
-  bool binned = false;
-  if constexpr (BITS == 4) {
-    if (threadIdx.x == 0) s_two_in_a_bin = 0;
-    lds_barrier();
-    if (threadIdx.x < kBins) {
-      const uint32_t lo = __float_as_uint((float)threadIdx.x * (1.f / kBins));
-      const uint32_t hi = threadIdx.x == kBins - 1 ? 0xffffffffu
-                                                   : __float_as_uint((float)(threadIdx.x + 1) * (1.f / kBins));
-      uint32_t below = 0, inside = 0xffffffffu;
-      int n_in = 0;
-#pragma unroll
-      for (int h = 0; h < NPOS; ++h) {
-        below += tpos[h] < lo ? 1u : 0u;
-        if (tpos[h] >= lo && tpos[h] < hi) {
-          inside = tpos[h];
-          ++n_in;
-        }
-      }
-      s_bin[threadIdx.x] = make_uint2(below, inside);
-      if (n_in > 1) s_two_in_a_bin = 1;
-    }
-    lds_barrier();
-    binned = s_two_in_a_bin == 0;
-  }
+  // the bin table of the quantiser, built while the loads above are in
+  // flight; a codebook with two thresholds in one bin falls back to counting
+  // the thresholds (work-group uniform)
+  static_assert(kWG == kSBins, "one bin per thread");
+  __shared__ uint2 s_bin[kSBins];
+  __shared__ int s_two;
+  if (threadIdx.x == 0) s_two = 0;
+  lds_barrier();
+  build_sbins(j.thr, L - 1, threadIdx.x, s_bin, &s_two);
+  lds_barrier();
+  const bool binned = s_two == 0;
 
 #pragma unroll
   for (int u = 0; u < kVPT; ++u)
-    encode_one<D, BITS, ROT, kBins>(j, q, i0 + u * VPB, sub, v[u], sword[u], tpos, binned, s_bin);
+    encode_one<D, BITS, ROT>(j, q, i0 + u * VPB, sub, v[u], sword[u], tpos, binned, s_bin);
 }
 
+// Code table of the decoder: one entry per byte of codes (BITS = 4: two
+// centroids, BITS = 2: four) or per 6-bit field (BITS = 3: two), so one LDS
+// read dequantises 2 or 4 coordinates.
+template <int BITS>
+struct DecTab {
+  static constexpr int kEntries = BITS == 3 ? 64 : 256;
+  static constexpr int kPer = BITS == 2 ? 4 : 2;  // coordinates per entry
+};
+
+constexpr int kDecVPT = 4;  // vectors per thread in the decoder, loads issued together
 
 template <int D, int BITS, int OUT, bool ROT, bool ROPE>
 __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j, Div32 per_rot, Div32 n_rot) {
   constexpr int LPV = D / 8;
   constexpr int VPB = kWG / LPV;
+  constexpr int U = kDecVPT;
   constexpr int CB = D * BITS / 8;
-  __shared__ float cent[1 << BITS];
+  constexpr int CW = BITS == 3 ? 2 : 1;  // code dwords loaded per lane and vector
+  constexpr int NE = DecTab<BITS>::kEntries, PER = DecTab<BITS>::kPer;
+  __shared__ __align__(16) float tab[NE * PER];
   // RoPE: turns per position of each coordinate pair, base^(-2f/d) / (2 pi),
   // as a 64-bit binary fraction (low and high words), so that the fraction of
   // a turn at any int32 position is one wrapping integer product
   __shared__ uint32_t turns_lo[ROPE ? D / 2 : 1], turns_hi[ROPE ? D / 2 : 1];
-  if (threadIdx.x < (1 << BITS)) cent[threadIdx.x] = j.centroids[threadIdx.x];
+  if (threadIdx.x < NE) {
+    constexpr uint32_t M = (1u << BITS) - 1;
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+      tab[threadIdx.x * PER + k] = j.centroids[(threadIdx.x >> (BITS * k)) & M];
+  }
   if constexpr (ROPE) {
     if (threadIdx.x < D / 2) {
       const double t = pow(j.rope_base, -2.0 * threadIdx.x / D) * (0.5 / 3.141592653589793);
@@ -148,81 +143,120 @@ __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j, Div32 per_rot,
       thi[k] = turns_hi[f];
     }
   }
-  // one block of VPB vectors per work-group; the RoPE variant, whose table
-  // costs a set-up per work-group, strides over blocks with a smaller grid
-  const uint32_t nblk = ROPE ? (uint32_t)((j.n_vec + VPB - 1) / VPB) : blockIdx.x + 1;
-  for (uint32_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
-    const uint64_t i64 = (uint64_t)blk * VPB + threadIdx.x / LPV;
-    const bool valid = i64 < (uint64_t)j.n_vec;
-    const uint32_t i = (uint32_t)i64;
-    uint32_t codes = 0;
-    float r = 0.f;
-    uint32_t sbyte = 0;
-    if (valid) {
+  // This lane's code bits of a row: BITS = 4 one dword; 2: half a dword;
+  // 3: 24 bits from bit 24 sub (two dwords, the second inside the row).
+  const int bit = BITS * 8 * sub;
+  const int w0 = bit >> 5, sh = bit & 31;
+  const int w1 = min(w0 + 1, CB / 4 - 1);
+  // Blocks of U * VPB vectors, one per work-group (the RoPE variant, whose
+  // table costs a set-up per work-group, strides over them with a grid of at
+  // most the resident work-groups); every load of a block (codes, norm, sign
+  // word, position) is issued before the first vector is decoded.
+  const uint64_t nblk = ((uint64_t)j.n_vec + U * VPB - 1) / (U * VPB);
+  for (uint64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    uint32_t cw[U][CW];
+    float r[U];
+    uint32_t sw[U];
+    int32_t ps[U];
+    bool valid[U];
+    uint32_t idx[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t i64 = blk * (U * VPB) + (uint64_t)(u * VPB) + threadIdx.x / LPV;
+      valid[u] = i64 < (uint64_t)j.n_vec;
+      const uint32_t i = valid[u] ? (uint32_t)i64 : (uint32_t)(j.n_vec - 1);  // reread the last
+      idx[u] = i;
       const uint32_t* row = reinterpret_cast<const uint32_t*>(j.codes + (int64_t)i * CB);
+      cw[u][0] = row[w0];
+      if constexpr (CW == 2) cw[u][1] = row[w1];
+      r[u] = j.norms[i];
+      sw[u] = 0u;
+      if constexpr (ROT) sw[u] = j.signs[rot_of(i, per_rot, n_rot) * (D / 32) + sub / 4];
+      ps[u] = 0;
+      if constexpr (ROPE) ps[u] = j.pos[i];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint32_t codes;
       if constexpr (BITS == 4) {
-        codes = row[sub];
+        codes = cw[u][0];
       } else if constexpr (BITS == 2) {
-        codes = (row[sub >> 1] >> (16 * (sub & 1))) & 0xffffu;
+        codes = cw[u][0] >> sh;
       } else {
-        const int bit = 24 * sub;
-        const uint32_t w0 = row[bit >> 5];
-        const int off = bit & 31;
-        codes = w0 >> off;
-        if (off > 8) codes |= row[(bit >> 5) + 1] << (32 - off);
-        codes &= 0xffffffu;
+        codes = (uint32_t)(((uint64_t)cw[u][1] << 32 | cw[u][0]) >> sh);
       }
-      r = j.norms[i];
-      if constexpr (ROT)
-        sbyte = (j.signs[rot_of(i, per_rot, n_rot) * (D / 32) + sub / 4] >> (8 * (sub % 4))) & 0xffu;
-    }
-    float v[8];
+      float v[8];
+      if constexpr (BITS == 4) {
 #pragma unroll
-    for (int a = 0; a < 8; ++a) v[a] = cent[(codes >> (BITS * a)) & ((1u << BITS) - 1)];
-    if constexpr (ROT) fwht8xlanes<LPV>(v, sub);
-    // 1 / sqrt(d) is a compile-time constant: one multiply, not a division
-    const float s = ROT ? r * (1.f / __builtin_sqrtf((float)D)) : r;
+        for (int k = 0; k < 4; ++k) {
+          const float2 c = reinterpret_cast<const float2*>(tab)[(codes >> (8 * k)) & 0xffu];
+          v[2 * k] = c.x;
+          v[2 * k + 1] = c.y;
+        }
+      } else if constexpr (BITS == 2) {
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
-      v[a] = __uint_as_float(__float_as_uint(v[a] * s) ^ (((sbyte >> a) & 1u) << 31));
-    if constexpr (ROPE) {
-      const int32_t p = valid ? j.pos[i] : 0;
-      const uint32_t pu = (uint32_t)p;
-      float sn[8], cs[8];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        // top word of p * turns mod 2^64: the fraction of a turn in units
-        // of 2^-32 (a negative p is pu - 2^32, which takes tlo off that word)
-        const uint32_t top = __umulhi(pu, tlo[k]) + pu * thi[k] - (p < 0 ? tlo[k] : 0u);
-        const float rev = (float)top * 0x1p-32f;
-        // the hardware sine and cosine take their argument in turns
-        const float s1 = __builtin_amdgcn_sinf(rev), c1 = __builtin_amdgcn_cosf(rev);
-        const float s2 = xor_lane<HALF>(s1), c2 = xor_lane<HALF>(c1);
-        sn[k] = upper ? s2 : s1;
-        cs[k] = upper ? c2 : c1;
-        sn[k + 4] = upper ? s1 : s2;
-        cs[k + 4] = upper ? c1 : c2;
-      }
-#pragma unroll
-      for (int a = 0; a < 8; ++a) {
-        const float partner = xor_lane<HALF>(v[a]);
-        v[a] = v[a] * cs[a] + (upper ? partner : -partner) * sn[a];
-      }
-    }
-    if (valid) {
-      if constexpr (OUT == HSQ_F32) {
-        float4* o = reinterpret_cast<float4*>(static_cast<float*>(j.out) + (int64_t)i * D + 8 * sub);
-        o[0] = make_float4(v[0], v[1], v[2], v[3]);
-        o[1] = make_float4(v[4], v[5], v[6], v[7]);
+        for (int k = 0; k < 2; ++k) {
+          const float4 c = reinterpret_cast<const float4*>(tab)[(codes >> (8 * k)) & 0xffu];
+          v[4 * k] = c.x;
+          v[4 * k + 1] = c.y;
+          v[4 * k + 2] = c.z;
+          v[4 * k + 3] = c.w;
+        }
       } else {
-        // round to nearest even, two values per conversion instruction
-        uint32_t w[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          w[k] = __builtin_bit_cast(uint32_t,
-                                    __builtin_convertvector(f32x2{v[2 * k], v[2 * k + 1]}, bf16x2));
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(j.out) + (int64_t)i * D + 8 * sub) =
-            make_uint4(w[0], w[1], w[2], w[3]);
+        for (int k = 0; k < 4; ++k) {
+          const float2 c = reinterpret_cast<const float2*>(tab)[(codes >> (6 * k)) & 63u];
+          v[2 * k] = c.x;
+          v[2 * k + 1] = c.y;
+        }
+      }
+      if constexpr (ROT) fwht8xlanes<LPV>(v, sub);
+      // 1 / sqrt(d) is a compile-time constant: one multiply, not a division
+      const float s = ROT ? r[u] * (1.f / __builtin_sqrtf((float)D)) : r[u];
+      const uint32_t sbyte = ROT ? (sw[u] >> (8 * (sub % 4))) & 0xffu : 0u;
+#pragma unroll
+      for (int a = 0; a < 8; ++a)
+        v[a] = __uint_as_float(__float_as_uint(v[a] * s) ^ (((sbyte >> a) & 1u) << 31));
+      if constexpr (ROPE) {
+        const int32_t p = ps[u];
+        const uint32_t pu = (uint32_t)p;
+        float sn[8], cs[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          // top word of p * turns mod 2^64: the fraction of a turn in units
+          // of 2^-32 (a negative p is pu - 2^32, which takes tlo off that word)
+          const uint32_t top = __umulhi(pu, tlo[k]) + pu * thi[k] - (p < 0 ? tlo[k] : 0u);
+          const float rev = (float)top * 0x1p-32f;
+          // the hardware sine and cosine take their argument in turns
+          const float s1 = __builtin_amdgcn_sinf(rev), c1 = __builtin_amdgcn_cosf(rev);
+          const float s2 = xor_lane<HALF>(s1), c2 = xor_lane<HALF>(c1);
+          sn[k] = upper ? s2 : s1;
+          cs[k] = upper ? c2 : c1;
+          sn[k + 4] = upper ? s1 : s2;
+          cs[k + 4] = upper ? c1 : c2;
+        }
+#pragma unroll
+        for (int a = 0; a < 8; ++a) {
+          const float partner = xor_lane<HALF>(v[a]);
+          v[a] = v[a] * cs[a] + (upper ? partner : -partner) * sn[a];
+        }
+      }
+      if (valid[u]) {
+        const uint32_t i = idx[u];
+        if constexpr (OUT == HSQ_F32) {
+          float4* o = reinterpret_cast<float4*>(static_cast<float*>(j.out) + (int64_t)i * D + 8 * sub);
+          o[0] = make_float4(v[0], v[1], v[2], v[3]);
+          o[1] = make_float4(v[4], v[5], v[6], v[7]);
+        } else {
+          // round to nearest even, two values per conversion instruction
+          uint32_t w[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            w[k] = __builtin_bit_cast(uint32_t,
+                                      __builtin_convertvector(f32x2{v[2 * k], v[2 * k + 1]}, bf16x2));
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(j.out) + (int64_t)i * D + 8 * sub) =
+              make_uint4(w[0], w[1], w[2], w[3]);
+        }
       }
     }
   }
@@ -253,10 +287,11 @@ hipError_t encode_dt(const EncodeJob& j, hipStream_t s) {
 template <int D, int BITS, bool ROT, bool ROPE>
 hipError_t decode_out(const DecodeJob& j, hipStream_t s) {
   constexpr int VPB = kWG / (D / 8);
-  // the RoPE variant: at most a full chip of resident work-groups (256 CUs,
-  // 8 work-groups of 4 waves each), each striding over the blocks
-  const int64_t blocks = (j.n_vec + VPB - 1) / VPB;
-  const int64_t grid = ROPE ? std::min<int64_t>(blocks, 256 * 8) : blocks;
+  // the RoPE variant: at most a chip of resident work-groups (256 CUs, 4
+  // work-groups of 4 waves each: its register use allows 5 or 6), each
+  // striding over the blocks
+  const int64_t blocks = (j.n_vec + kDecVPT * VPB - 1) / (kDecVPT * VPB);
+  const int64_t grid = ROPE ? std::min<int64_t>(blocks, 256 * 4) : blocks;
   const Div32 per_rot = make_div32(j.vecs_per_rot), n_rot = make_div32(j.n_rot);
   if (j.out_dtype == HSQ_F32)
     hipLaunchKernelGGL((decode_kernel<D, BITS, HSQ_F32, ROT, ROPE>), dim3((unsigned)grid), dim3(kWG),

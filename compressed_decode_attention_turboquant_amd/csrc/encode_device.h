@@ -103,9 +103,35 @@ __device__ __forceinline__ void norm_scale(float ss_lane, float& r, float& inv) 
   inv = r > 0.f ? __builtin_amdgcn_rcpf(den) : 0.f;
 }
 
+// Quantisation by a bin table.  kSBins equal bins of y * 128 over [-128, 128)
+// (unit steps of y * 128, so the bin of a value is the floor of an exactly
+// scaled value; values outside go to the end bins); bin b holds the number of
+// thresholds below its start and the threshold inside it (times 128, +inf if
+// none).  The code of y is that number plus one compare, exact when no bin
+// holds two thresholds (true for the Beta codebooks at d = 64 and 128: their
+// closest thresholds are >= 0.022 apart, a bin is 1/128 wide).
+constexpr int kSBins = 256;
+__device__ __forceinline__ void build_sbins(const float* thr, int n_thr, int b, uint2* s_bin,
+                                            int* s_two) {
+  const float start = (float)(b - kSBins / 2), end = start + 1.f;
+  uint32_t below = 0u, inside = 0x7f800000u;
+  int n_in = 0;
+  for (int h = 0; h < n_thr; ++h) {
+    const float t = thr[h] * 128.f;
+    below += t < start ? 1u : 0u;
+    if (t >= start && t < end) {
+      inside = __float_as_uint(t);
+      ++n_in;
+    }
+  }
+  s_bin[b] = make_uint2(below, inside);
+  if (n_in > 1) *s_two = 1;
+}
+
 // Norm, rotation, quantisation and packing of vector i, whose 8 coordinates
-// of this lane are in v (LPV lanes per vector).
-template <int D, int BITS, bool ROT, int kBins>
+// of this lane are in v (LPV lanes per vector).  binned: codes from the bin
+// table s_bin (build_sbins); else from the positive thresholds tpos.
+template <int D, int BITS, bool ROT>
 __device__ __forceinline__ void encode_one(const EncodeJob& j, const EncodeDivs& q, uint32_t i,
                                            int sub, float (&v)[8], uint32_t sword,
                                            const uint32_t (&tpos)[(1 << BITS) / 2 - 1], bool binned,
@@ -130,16 +156,16 @@ __device__ __forceinline__ void encode_one(const EncodeJob& j, const EncodeDivs&
 
   uint32_t packed = 0;
   if (binned) {  // work-group uniform
+    // y * 128 = v * (inv * 128): scaling by 128 is exact, so this is the
+    // rounded y scaled, and its compares with the scaled thresholds are those
+    // of y with the thresholds
+    const float inv128 = inv * 128.f;
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
-      const float y = v[a] * inv;
-      const bool pos = y > 0.f;
-      const float ay = fabsf(y);
-      const uint32_t key = __float_as_uint(ay) + (pos ? 0u : 1u);
-      const uint32_t b = min((uint32_t)(ay * (float)kBins), (uint32_t)(kBins - 1));
+      const float y128 = v[a] * inv128;
+      const int b = min(max((int)__builtin_floorf(y128), -kSBins / 2), kSBins / 2 - 1) + kSBins / 2;
       const uint2 e = s_bin[b];
-      const uint32_t cnt = e.x + (e.y < key ? 1u : 0u);
-      const uint32_t code = pos ? (uint32_t)(L / 2) + cnt : (uint32_t)(L / 2 - 1) - cnt;
+      const uint32_t code = e.x + (__uint_as_float(e.y) < y128 ? 1u : 0u);
       packed |= code << (BITS * a);
     }
   } else {
