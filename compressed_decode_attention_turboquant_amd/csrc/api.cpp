@@ -299,12 +299,15 @@ extern "C" int hsq_step_route(const float* q, int B, int Hq, int Hkv, int d, int
   StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, b};
   Workspace w;
   if ((rc = step_common("hsq_step_route", s, workspace, ws_bytes, w))) return rc;
-  if ((rc = need_route_lds("hsq_step_route", s))) return rc;
   StepTensors t{};
   t.q = q; t.l2k = l2k; t.l2k_n = l2k_n; t.l2v = l2v; t.l2v_n = l2v_n; t.k_signs = k_signs;
   t.cb3 = cb3; t.scale = scale; t.summary_bias = summary_bias; t.agg = agg;
   char* ws = static_cast<char*>(workspace);
   const hipStream_t st = as_stream(stream);
+  if (s.n_groups > 0 && !route_lds_ok(s))  // router logits beyond LDS: the split step's first half
+    return check_hip(launch_split_half(s, t, w, ws, true, b > 0 ? topk_idx : nullptr, st),
+                     "hsq_step_route (split)");
+  if ((rc = need_route_lds("hsq_step_route", s))) return rc;
   int32_t* idx = reinterpret_cast<int32_t*>(ws + w.idx_off);
   if ((rc = check_hip(launch_route(s, t, w, ws, ROUTE_TOPK | ROUTE_PARTIALS, nullptr, nullptr,
                                    idx, st),
@@ -334,12 +337,15 @@ extern "C" int hsq_step_attend(const float* q, int B, int Hq, int Hkv, int d, co
   StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, b};
   Workspace w;
   if ((rc = step_common("hsq_step_attend", s, workspace, ws_bytes, w))) return rc;
-  if ((rc = need_route_lds("hsq_step_attend", s))) return rc;
   StepTensors t{};
   t.q = q; t.l1k = l1k; t.l1k_n = l1k_n; t.l1v = l1v; t.l1v_n = l1v_n; t.l3 = l3;
   t.l3_staged = l3_staged ? 1 : 0; t.k_signs = k_signs; t.v_signs = v_signs; t.cb4 = cb4;
   t.scale = scale; t.out = out;
   char* ws = static_cast<char*>(workspace);
+  if (s.n_groups > 0 && !route_lds_ok(s))  // the split step's second half, after hsq_step_route's
+    return check_hip(launch_split_half(s, t, w, ws, false, nullptr, as_stream(stream)),
+                     "hsq_step_attend (split)");
+  if ((rc = need_route_lds("hsq_step_attend", s))) return rc;
   return check_hip(launch_attn(s, t, w, ws, reinterpret_cast<int32_t*>(ws + w.idx_off),
                                as_stream(stream)),
                    "hsq_step_attend");

@@ -104,6 +104,12 @@ int route_lds_ok(const StepShape& s);
 int use_split(const StepShape& s);
 hipError_t launch_split_step(const StepShape& s, const StepTensors& t, const Workspace& w,
                              char* ws, int32_t* idx_out, hipStream_t st);
+// The split step in two calls (use_split shapes): first = scores, selection
+// (idx_out optional) and the summary-value chunks, from t's router inputs;
+// else the token chunks (L1 and the fetched records; staged ones by slot)
+// and the merge, from t's attend inputs.  Same shape and workspace in both.
+hipError_t launch_split_half(const StepShape& s, const StepTensors& t, const Workspace& w,
+                             char* ws, bool first, int32_t* idx_out, hipStream_t st);
 
 // mode bits for the summary kernel
 enum { ROUTE_TOPK = 1, ROUTE_PARTIALS = 2 };

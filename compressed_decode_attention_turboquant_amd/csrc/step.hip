@@ -2118,6 +2118,7 @@ struct SplitArgs {
   int32_t* sel;     // [units][beta] selection
   int32_t* idx_out; // optional [units][beta]
   float* parts;     // [units][sv + st][G][D+2]
+  int chunk0, nchunk;  // split_attend_kernel: chunks chunk0 .. chunk0 + nchunk - 1 of each unit
 };
 
 // Scores of 16 * kScoreTiles summaries of one unit: logits to a.lgt, router
@@ -2304,7 +2305,7 @@ void split_attend_kernel(SplitArgs a) {
   __shared__ float s_cb[16];
   const SplitPlan& p = a.p;
   const int per = p.sv + p.st;
-  const int unit = blockIdx.x / per, k = blockIdx.x % per;
+  const int unit = blockIdx.x / a.nchunk, k = a.chunk0 + blockIdx.x % a.nchunk;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int G = a.r.G;
   float* part = a.parts + ((size_t)unit * per + k) * G * (D + 2);
@@ -2377,11 +2378,14 @@ void split_attend_kernel(SplitArgs a) {
   const float cbv = (tid < 16) ? ta.cb4[tid] : 0.f;
   QueryIn qin;
   load_query<D>(ta.q + (size_t)unit * G * D, ta.k_signs + kvh * (D / 32), G, tid, qin);
+  // record of slot s: group sel[s] of the archive, or slot s of the staging
+  // buffer when the records were gathered there (l3_staged)
   const int32_t* sel = a.sel + (size_t)unit * ta.beta;
   for (int s = tid; s < tok_slots<N>(ta.beta); s += kThreads) {
     const int g = s < ta.beta ? sel[s] : -1;
     const bool ok = g >= 0 && g < ta.ng;
-    L.recoff[s] = ok ? (int32_t)((uint32_t)g * (uint32_t)rec) : (int32_t)kFar;
+    const uint32_t r = ta.l3_staged ? (uint32_t)s : (uint32_t)g;
+    L.recoff[s] = ok ? (int32_t)(r * (uint32_t)rec) : (int32_t)kFar;
   }
   if (tid < 16) s_cb[tid] = cbv;
   rotate_query<D>(qin, ta.scale * rsqrtf((float)D), L.qf, tid);
@@ -2558,18 +2562,42 @@ hipError_t split_route_d(const SplitArgs& a, int units, bool exact, hipStream_t 
   return hipGetLastError();
 }
 
+// Attend chunks [k0, k0 + n) of every unit; with merge, then the merge.
+template <int D, int N>
+hipError_t split_attend_dn(SplitArgs a, int units, int k0, int n, bool merge, hipStream_t st) {
+  a.chunk0 = k0;
+  a.nchunk = n;
+  if (n > 0) {
+    const size_t smem = (size_t)kMaxG * kQS<D> * 4 + (size_t)tok_slots<N>(a.t.beta) * 4;
+    hipLaunchKernelGGL((split_attend_kernel<D, N>), dim3((unsigned)(units * n)), dim3(kThreads),
+                       smem, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (merge)
+    hipLaunchKernelGGL((split_merge_kernel<D>), dim3((unsigned)units), dim3(kMaxG * (D / 8)), 0,
+                       st, a);
+  return hipGetLastError();
+}
+
 template <int D, int N>
 hipError_t split_step_dn(const SplitArgs& a, int units, hipStream_t st) {
   hipError_t e = split_route_d<D>(a, units, false, st);
   if (e != hipSuccess) return e;
-  const SplitPlan& p = a.p;
-  const size_t smem = (size_t)kMaxG * kQS<D> * 4 + (size_t)tok_slots<N>(a.t.beta) * 4;
-  hipLaunchKernelGGL((split_attend_kernel<D, N>), dim3((unsigned)(units * (p.sv + p.st))),
-                     dim3(kThreads), smem, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((split_merge_kernel<D>), dim3((unsigned)units), dim3(kMaxG * (D / 8)), 0, st,
-                     a);
-  return hipGetLastError();
+  return split_attend_dn<D, N>(a, units, 0, a.p.sv + a.p.st, true, st);
+}
+
+// The split step as two calls with work between them (the host-archive
+// path gathers the fetched records in between): scores, selection and the
+// summary-value chunks; then the token chunks and the merge.
+template <int D, int N>
+hipError_t split_halves_dn(const SplitArgs& a, int units, bool first, hipStream_t st) {
+  if (first) {
+    const hipError_t e = split_route_d<D>(a, units, false, st);
+    if (e != hipSuccess) return e;
+    return split_attend_dn<D, N>(a, units, 0, a.p.sv, false, st);
+  }
+  return split_attend_dn<D, N>(a, units, a.p.sv, a.p.st, true, st);
 }
 
 hipError_t launch_split_step(const StepShape& s, const StepTensors& t, const Workspace& w,
@@ -2582,6 +2610,19 @@ hipError_t launch_split_step(const StepShape& s, const StepTensors& t, const Wor
     return s.group_n == 16 ? split_step_dn<128, 16>(a, units, st)
                            : split_step_dn<128, 8>(a, units, st);
   return s.group_n == 16 ? split_step_dn<64, 16>(a, units, st) : split_step_dn<64, 8>(a, units, st);
+}
+
+hipError_t launch_split_half(const StepShape& s, const StepTensors& t, const Workspace& w,
+                             char* ws, bool first, int32_t* idx_out, hipStream_t st) {
+  if (!step_limits_ok(s) || !use_split(s)) return hipErrorInvalidValue;
+  SplitArgs a = split_args(s, t, w, ws);
+  a.idx_out = s.beta > 0 ? idx_out : nullptr;
+  const int units = s.B * s.Hkv;
+  if (s.d == 128)
+    return s.group_n == 16 ? split_halves_dn<128, 16>(a, units, first, st)
+                           : split_halves_dn<128, 8>(a, units, first, st);
+  return s.group_n == 16 ? split_halves_dn<64, 16>(a, units, first, st)
+                         : split_halves_dn<64, 8>(a, units, first, st);
 }
 
 hipError_t launch_route(const StepShape& s, const StepTensors& t, const Workspace& w, char* ws,

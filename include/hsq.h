@@ -319,14 +319,22 @@ int hsq_decode_step_static(const float* q, int B, int Hq, int Hkv, int d, const 
  * fetching from the CPU archive, then attention].
  *   hsq_step_route   router scores, top-beta and the summary-attention
  *                    partials (all summaries, then the fetched ones removed)
- *                    into the workspace; topk_idx (optional) receives a copy
- *                    of the selection.
+ *                    into the workspace.  The selection stays at the start
+ *                    of the workspace, int32 [B*Hkv][min(beta, n_groups)]
+ *                    ascending per unit, where a device-side consumer such
+ *                    as hsq_gather_l3 can read it in place; topk_idx
+ *                    (optional) receives a copy.
  *   hsq_step_attend  L1 and fetched-token attention, merge with the summary
  *                    partials, inverse V rotation, out.  Reads the selection
  *                    from the workspace written by the preceding
  *                    hsq_step_route with the same sizes and workspace.
  * Both take n_l1 and n_groups so they size the workspace identically.
- * Errors: as hsq_decode_attn (G * n_groups at most 12288).
+ * Shapes with G * n_groups above 12288 (more router logits than these
+ * launches hold on chip) run as the two halves of the split decode step (see
+ * hsq_decode_step): hsq_step_route launches the score chunks, the selection
+ * and the summary-value chunks, hsq_step_attend the token chunks (L1 and the
+ * fetched records, staged ones read by slot) and the merge.
+ * Errors: as hsq_decode_attn, without its G * n_groups limit.
  */
 int hsq_step_route(const float* q, int B, int Hq, int Hkv, int d, int n_l1, const uint8_t* l2k,
                    const float* l2k_n, const uint8_t* l2v, const float* l2v_n, int n_groups,

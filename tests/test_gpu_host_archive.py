@@ -84,3 +84,111 @@ def test_host_archive_step_matches_the_device_archive_step():
     check_route(sc, idx, None, units, w.beta)
     worst = check_attn(sc, out_host, idx, units)
     print(f"  worst rel L2 vs oracle on {units}: {worst:.2e}", flush=True)
+
+
+def test_gather_leaves_invalid_slots_untouched():
+    # 5 units x 9 slots = 45 slots: two full work-groups of 16 records and a
+    # partial one; some slots name no record (negative or past n_groups)
+    print("[gather] invalid slots, ragged last work-group", flush=True)
+    B, Hkv, ng, beta, rec = 5, 1, 40, 9, 8 * (64 + 8)
+    g = torch.Generator().manual_seed(11)
+    src = torch.randint(0, 256, (B, Hkv, ng, rec), dtype=torch.uint8, generator=g).to(DEV)
+    idx = torch.randint(0, ng, (B, Hkv, beta), dtype=torch.int32, generator=g)
+    idx[0, 0, 3] = -1
+    idx[2, 0, 8] = ng
+    idx[4, 0, 0] = -7
+    staging = torch.full((B, Hkv, beta, rec), 0xAB, dtype=torch.uint8, device=DEV)
+    hsq.gather_l3(src.data_ptr(), rec, B, Hkv, ng, idx.to(DEV), staging)
+    torch.cuda.synchronize()
+    s, x = staging.cpu(), src.cpu()
+    for b in range(B):
+        for i in range(beta):
+            gi = int(idx[b, 0, i])
+            if 0 <= gi < ng:
+                assert torch.equal(s[b, 0, i], x[b, 0, gi]), (b, i)
+            else:
+                assert bool((s[b, 0, i] == 0xAB).all()), (b, i)
+
+
+def test_selection_is_left_at_the_start_of_the_workspace():
+    w = W.QWEN3_8B_32K.smaller(T=4096, batch=2, n_marked=80)
+    print(f"[workspace selection] {w.name} T={w.T} B={w.batch}", flush=True)
+    sc = Scenario(w)
+    t = sc.tiers
+    beta = min(w.beta, t.ng)
+    ws = hsq.make_workspace(w.batch, w.hq, w.hkv, w.d, t.n1, t.ng, beta, w.group_n, DEV)
+    idx = torch.empty((w.batch, w.hkv, beta), dtype=torch.int32, device=DEV)
+    hsq.step_route(sc.q, t, w.beta, sc.dks, sc.cb3, ws, idx=idx)
+    torch.cuda.synchronize()
+    n = w.batch * w.hkv * beta
+    head = ws.buf[ws.ptr - ws.buf.data_ptr():][:4 * n].view(torch.int32).reshape(idx.shape)
+    assert torch.equal(head, idx)
+
+
+def test_two_micro_batches_on_two_streams_match_one_batch():
+    # as the bench runs the host archive: each half of the batch takes route,
+    # gather (selection read in place) and attend on its own stream
+    w = W.QWEN3_8B_32K.smaller(T=8192, batch=4, n_marked=160)
+    print(f"[micro-batches] {w.name} T={w.T} B={w.batch}", flush=True)
+    sc = Scenario(w)
+    t = sc.tiers
+    rec, beta = t.rec_bytes, min(w.beta, t.ng)
+    arch = hsq.HostArchive(t.l3.numel())
+    arch.host.copy_(t.l3.reshape(-1).cpu())
+    lib = hsq.lib()
+    # the same two launches over the whole batch, archive in device memory
+    out_full = torch.empty((w.batch, w.hq, w.d), dtype=torch.float32, device=DEV)
+    ws = hsq.make_workspace(w.batch, w.hq, w.hkv, w.d, t.n1, t.ng, beta, w.group_n, DEV)
+    hsq.step_route(sc.q, t, w.beta, sc.dks, sc.cb3, ws)
+    hsq.step_attend(sc.q, t, w.beta, sc.dks, sc.dvs, sc.cb4, ws, out_full)
+    out = torch.empty_like(out_full)
+    nb = w.batch // 2
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    per_seq = w.hkv * t.ng * rec
+    keep = []
+    torch.cuda.synchronize()
+    for h, (b0, n) in enumerate([(0, nb), (nb, w.batch - nb)]):
+        tv = hsq.Tiers(n, w.hkv, w.d, t.n1, t.ng, w.group_n,
+                       *[getattr(t, f)[b0:b0 + n] for f in
+                         ("l1k", "l1k_n", "l1v", "l1v_n", "l2k", "l2k_n", "l2v", "l2v_n")], t.l3)
+        wsh = hsq.make_workspace(n, w.hq, w.hkv, w.d, t.n1, t.ng, beta, w.group_n, DEV)
+        stg = torch.empty((n, w.hkv, beta, rec), dtype=torch.uint8, device=DEV)
+        keep += [wsh, stg]
+        with torch.cuda.stream(streams[h]):
+            q = sc.q[b0:b0 + n]
+            hsq.step_route(q, tv, w.beta, sc.dks, sc.cb3, wsh)
+            hsq._check(lib.hsq_gather_l3(arch.dev_ptr + b0 * per_seq, rec, n, w.hkv, t.ng,
+                                         wsh.ptr, beta, stg.data_ptr(),
+                                         streams[h].cuda_stream))
+            hsq.step_attend(q, tv, w.beta, sc.dks, sc.dvs, sc.cb4, wsh, out[b0:b0 + n],
+                            l3=stg.data_ptr(), l3_staged=True)
+    torch.cuda.synchronize()
+    # one work-group per unit: a unit's result does not depend on the batch
+    # it runs in, nor on where its records were read from
+    assert torch.equal(out, out_full)
+
+
+def test_two_launches_beyond_on_chip_logits_match_the_split_step():
+    # G * n_groups above what the two-launch kernels hold on chip: hsq_step_route
+    # and hsq_step_attend run as the split step's two halves, with the fetched
+    # records staged by a gather in between (read by slot), and give the
+    # one-call step's result exactly
+    w = W.QWEN3_14B_16K.smaller(T=32768, batch=2, n_marked=328)
+    print(f"[split halves] {w.name} T={w.T} B={w.batch}", flush=True)
+    sc = Scenario(w)
+    t = sc.tiers
+    assert w.G * t.ng > 12288
+    rec, beta = t.rec_bytes, min(w.beta, t.ng)
+    ws = hsq.make_workspace(w.batch, w.hq, w.hkv, w.d, t.n1, t.ng, beta, w.group_n, DEV)
+    out_one, idx_one = hsq.decode_step(sc.q, t, w.beta, sc.dks, sc.dvs, sc.cb4, sc.cb3, ws=ws)
+    ws2 = hsq.make_workspace(w.batch, w.hq, w.hkv, w.d, t.n1, t.ng, beta, w.group_n, DEV)
+    idx = torch.empty((w.batch, w.hkv, beta), dtype=torch.int32, device=DEV)
+    staging = torch.empty((w.batch, w.hkv, beta, rec), dtype=torch.uint8, device=DEV)
+    out_two = torch.empty_like(out_one)
+    hsq.step_route(sc.q, t, w.beta, sc.dks, sc.cb3, ws2, idx=idx)
+    hsq.gather_l3(t.l3.data_ptr(), rec, w.batch, w.hkv, t.ng, idx, staging)
+    hsq.step_attend(sc.q, t, w.beta, sc.dks, sc.dvs, sc.cb4, ws2, out_two,
+                    l3=staging.data_ptr(), l3_staged=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_one)
+    assert torch.equal(out_two, out_one)
