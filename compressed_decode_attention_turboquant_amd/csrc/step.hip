@@ -47,12 +47,15 @@
 //     A[pair r][(n, e)] = V[n][2r + e],  B[(n, e)][(h, e')] = P[h][n] [e == e']
 // so C[r][(h, e')] = O[h][2r + e'].  A lane then needs, per token, a byte (two
 // 4-bit codes = two dims) straight from the token's code row, and B's columns
-// (h, e') are exactly the QK output columns when each head's query is placed
-// in two columns (2h, 2h+1).  G <= 8 heads fill the 16 columns.
+// are exactly the QK output columns when each head's query is placed in two
+// columns: column c holds (h, e') = (c & 7, c >> 3).  G <= 8 heads fill the 16
+// columns.
 #include <cmath>
+#include <type_traits>
 
 #include "hsq_device.h"
 #include "hsq_internal.h"
+
 
 namespace hsq {
 namespace {
@@ -69,6 +72,7 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kMaxG = 8;
 constexpr int kNC3 = 32;                 // 3-bit table copies (lanes l, l+32 share)
 constexpr int kNC4 = 64;                 // 4-bit table copies (one per lane)
+constexpr int kLut4Bytes = 256 * kNC4 * 4;  // 4-bit table of the two-launch kernels
 constexpr int kMaxGroups = 16384;
 constexpr int kMaxLogits = 12288;        // G * n_groups kept in LDS (one-launch step, route)
 constexpr int kSplitUnits = 128;         // fewer units than this: the split step
@@ -119,6 +123,22 @@ __device__ __forceinline__ half8 as_h8(uint32_t a, uint32_t b, uint32_t c, uint3
 __device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
+// Row norms.  Lane (c, gq) handles rows 4gq .. 4gq+3 of a tile and loads the
+// norm of row 4gq + (c & 3) only; lane c & 3 == i of each quad then holds row
+// 4gq + i, so quad_perm [i,i,i,i] gives every lane row i's norm, and the DPP
+// move fuses into the multiply that uses it (one register per tile, not four).
+template <int I>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), I * 0x55, 0xf, 0xf, true));
+}
+__device__ __forceinline__ f32x4 mul_rows(f32x4 a, float nrm) {
+  return f32x4{a[0] * quad_bcast<0>(nrm), a[1] * quad_bcast<1>(nrm), a[2] * quad_bcast<2>(nrm),
+               a[3] * quad_bcast<3>(nrm)};
+}
+__device__ __forceinline__ float row_norm(float nrm, int r) {
+  return r == 0 ? quad_bcast<0>(nrm)
+                : (r == 1 ? quad_bcast<1>(nrm) : (r == 2 ? quad_bcast<2>(nrm) : quad_bcast<3>(nrm)));
+}
 
 // Runs use(i, B[i % K]) for i in [0, iters) with each buffer's loads
 // issued K-1 iterations before its use, so every wave keeps K-1 tiles in
@@ -153,12 +173,22 @@ __device__ __forceinline__ void pipeline(int iters, Buf (&B)[K], LoadF load, Use
   pipeline_seg<K>(0, (iters + K - 1) / K, iters, B, load, use);
 }
 
+// Lane index, read afresh at each use (the asm is volatile, so the
+// compiler neither hoists nor keeps it): the per-lane parts of the tile
+// addresses are a few VALU from it, cheaper than registers held across a
+// loop or spilled (a reload waits for every load in flight).
+__device__ __forceinline__ int lane_now() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
 // Wave index as a scalar (wave-uniform for the compiler).
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
+template <int NW = kWaves>
 __device__ __forceinline__ int wave_iters(int n_tiles, int wave) {
-  return wave < n_tiles ? (n_tiles - wave + kWaves - 1) / kWaves : 0;
+  return wave < n_tiles ? (n_tiles - wave + NW - 1) / NW : 0;
 }
 
 // Wave-wide maximum / minimum by DPP row operations (GFX9 row broadcasts);
@@ -301,6 +331,14 @@ __device__ __forceinline__ uint32_t lut3_addr(uint32_t e, uint32_t lane4) {
   return (e << 7) | lane4;
 }
 
+// Columns of the MFMA products.  Column c of a QK or PV tile belongs to
+// head c & 7 and, in the value products, to element c >> 3 of each
+// dimension pair; so columns c and c + 8 carry the same head, and the two
+// halves of the router's query split (columns h and h + 8) add up by one row
+// rotation into a value that both columns then hold.
+__device__ __forceinline__ int col_head(int c) { return c & 7; }
+__device__ __forceinline__ int col_elem(int c) { return c >> 3; }
+
 // -------------------------------------------------------- query rotation ---
 
 // Query rotation in two steps so that its global loads can be issued with
@@ -357,12 +395,12 @@ __device__ __forceinline__ void rotate_query(QueryIn& Q, float mult, float* qf, 
   }
 }
 
-// B operand of the QK products: lane (c, gq) holds head c/2, dims
+// B operand of the QK products: lane (c, gq) holds head col_head(c), dims
 // gq*D/4 + 8m + j for k-chunk m; hi/lo fp16 split of the fp32 rotated query.
 template <int D>
 __device__ void query_operands(const float* qf, int lane, half8 (&hi)[D / 32],
                                half8 (&lo)[D / 32]) {
-  const int c = lane & 15, gq = lane >> 4, h = c >> 1;
+  const int c = lane & 15, gq = lane >> 4, h = col_head(c);
   const f32x4* src = reinterpret_cast<const f32x4*>(qf + h * kQS<D> + gq * (D / 4));
 #pragma unroll
   for (int m = 0; m < D / 32; ++m) {
@@ -454,7 +492,7 @@ struct Softmax {
 // B operand of the value products from 4 weights of this lane's column
 // (h, e'): token 4gq+j, element e' of each dimension pair.
 __device__ __forceinline__ half8 weight_operand(const float (&w)[4], int lane) {
-  const uint32_t sh = (lane & 1) ? 16u : 0u;
+  const uint32_t sh = col_elem(lane & 15) ? 16u : 0u;
   uint32_t pb[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) pb[j] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)w[j]) << sh;
@@ -499,35 +537,35 @@ __device__ __forceinline__ void pv3(const uint32_t (&va)[4], uint32_t sh, half8 
 
 // Combine the waves' states; result per head written to dst[h][D+2] as
 // [m, l, O[0..D)] (dst may be LDS or global).  scratch: kWaves*kMaxG*(D+2) floats.
-template <int D>
+template <int D, int NW = kWaves>
 __device__ void combine_waves(const Softmax<D>& st, int G, float* scratch, float* dst, int tid) {
   const int lane = tid & 63, wave = tid >> 6, c = lane & 15, gq = lane >> 4;
   float l = st.l;
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
   constexpr int T = D / 32;
-  const int h = c >> 1;
+  const int h = col_head(c), e = col_elem(c);
   float* w = scratch + (wave * kMaxG + h) * (D + 2);
   if (h < G) {
-    if (gq == 0 && !(c & 1)) {
+    if (gq == 0 && e == 0) {
       w[0] = st.m;
       w[1] = l;
     }
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[2 + 2 * (T * (4 * gq + i) + t) + (c & 1)] = st.O[t][i];
+      for (int i = 0; i < 4; ++i) w[2 + 2 * (T * (4 * gq + i) + t) + e] = st.O[t][i];
   }
   lds_barrier();
-  for (int k = tid; k < G * (D + 2); k += kThreads) {
+  for (int k = tid; k < G * (D + 2); k += (NW * 64)) {
     const int hh = k / (D + 2), e = k % (D + 2);
     float M = kNegInf;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, scratch[(v * kMaxG + hh) * (D + 2)]);
+    for (int v = 0; v < NW; ++v) M = fmaxf(M, scratch[(v * kMaxG + hh) * (D + 2)]);
     float acc = 0.f;
     if (e > 0) {
 #pragma unroll
-      for (int v = 0; v < kWaves; ++v) {
+      for (int v = 0; v < NW; ++v) {
         const float* s = scratch + (v * kMaxG + hh) * (D + 2);
         const float wgt = (s[0] == kNegInf) ? 0.f : __expf(s[0] - M);
         acc += wgt * s[e];
@@ -607,19 +645,19 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
-// Radix select of the beta-th largest of keys[0..ng) by one wave: 4 passes
+// Radix select of the beta-th largest of the keys key(0 .. ng-1) by one wave: 4 passes
 // of 8 bits, most significant first, histogram in LDS.  Returns that key;
 // need = how many of the keys equal to it rank among the beta largest.
 // 0 < beta < ng.
-__device__ uint32_t radix_kth(const uint32_t* keys, int ng, int beta, int* hist, int lane,
-                              int& need_out) {
+template <typename KeyF>
+__device__ uint32_t radix_kth_f(KeyF key, int ng, int beta, int* hist, int lane, int& need_out) {
   uint32_t pre = 0u, msk = 0u;
   int need = beta;
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int b = lane; b < 256; b += 64) hist[b] = 0;
     wave_lds_sync();
     for (int g = lane; g < ng; g += 64) {
-      const uint32_t k = keys[g];
+      const uint32_t k = key(g);
       if ((k & msk) == pre) atomicAdd(&hist[(k >> shift) & 255u], 1);
     }
     wave_lds_sync();
@@ -651,6 +689,10 @@ __device__ uint32_t radix_kth(const uint32_t* keys, int ng, int beta, int* hist,
   }
   need_out = need;
   return pre;
+}
+__device__ uint32_t radix_kth(const uint32_t* keys, int ng, int beta, int* hist, int lane,
+                              int& need_out) {
+  return radix_kth_f([&](int g) { return keys[g]; }, ng, beta, hist, lane, need_out);
 }
 
 // Top-beta of keys[0..ng) by one wave: sel[0..beta) ascending group ids.
@@ -838,10 +880,10 @@ __device__ __forceinline__ void exact_from_p(const ExactRaw<D> (&x)[P], int sub,
 
 // Keys of tile t (16 summaries): this lane's raw key words (D = 128: 96 bits
 // at byte 12gq of row lane&15; D = 64: 64 bits from the dword holding bit
-// 48gq, aligned by key_bits) and the key norms of rows 4gq .. 4gq+3.
+// 48gq, aligned by key_bits) and the key norm of row 4gq + (lane & 3).
 struct KeyTile {
   uint32_t kw[3];
-  f32x4 kn;
+  float kn;  // norm of row 4gq + (lane & 3) (see mul_rows)
 };
 template <int D>
 __device__ __forceinline__ void load_keys(rsrc_t rk, rsrc_t rn, int t, int lane,
@@ -856,7 +898,7 @@ __device__ __forceinline__ void load_keys(rsrc_t rk, rsrc_t rn, int t, int lane,
     const u32x2 w = ld64(rk, row + 4 * ((3 * gq) >> 1));
     T.kw[0] = w.x; T.kw[1] = w.y; T.kw[2] = 0u;
   }
-  T.kn = ldf4(rn, (uint32_t)(16 * t + 4 * gq) * 4);
+  T.kn = __uint_as_float(ld32(rn, (uint32_t)(16 * t + 4 * gq + (lane & 3)) * 4));
 }
 // This lane's key bits from the words load_keys left (the loads stay free of
 // arithmetic so that no wait is forced before the tile is used).
@@ -874,10 +916,10 @@ __device__ __forceinline__ void key_bits(const uint32_t (&w)[3], int lane, uint3
 
 // Values of tile t: the dword of row 4gq+j that holds this lane's value bits
 // (dims [2T*rho, 2T*rho + 2T), T = D/32; the bits start at val_shift) and the
-// rows' norms.
+// norm of row 4gq + (lane & 3).
 struct ValTile {
   uint32_t va[4];
-  f32x4 vn;
+  float vn;  // norm of row 4gq + (lane & 3) (see mul_rows)
 };
 // The dword holding this lane's value bits starts at byte min(bit/8, RB-4)
 // (so it never crosses the end of the row; buffer loads need only byte
@@ -907,7 +949,7 @@ __device__ __forceinline__ void load_vals(rsrc_t rv, rsrc_t rvn, int t, int lane
   asm("" : "+v"(base));
 #pragma unroll
   for (int j = 0; j < 4; ++j) T.va[j] = ld32(rv, base + j * RB);
-  T.vn = ldf4(rvn, tn + (uint32_t)(16 * gq));
+  T.vn = __uint_as_float(ld32(rvn, tn + (uint32_t)(16 * gq + 4 * (lane & 3))));
 }
 
 // Byte offsets of the route body's LDS arrays after `base` (16-byte aligned):
@@ -1320,7 +1362,7 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
   router_operands<D>(qf, lane, qb);
   lds_barrier();
 
-  // (1) keys -> per-head logits in LDS (column 2h holds head h)
+  // (1) keys -> per-head logits in LDS (column h < 8 holds head h)
   const int n_tiles = ngp >> 4;
   // lanes that hold no head's logits store into a dummy slot (no branch)
   const bool writer = c < a.G;
@@ -1339,8 +1381,8 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
           const int t = wave + i * kWaves;
           uint32_t kw[3];
           key_bits<D>(T.kw, lane, kw);
-          f32x4 lg = qk3<D, EXACT>(kw, qb, lut3, L.lut3lo, lane4) * T.kn;
-          if constexpr (!EXACT) rn = max3f(max3f(rn, T.kn[0], T.kn[1]), T.kn[2], T.kn[3]);
+          f32x4 lg = mul_rows(qk3<D, EXACT>(kw, qb, lut3, L.lut3lo, lane4), T.kn);
+          if constexpr (!EXACT) rn = fmaxf(rn, T.kn);
           *reinterpret_cast<f32x4*>(lw + (writer ? 16 * t : 0)) = lg;
           // a lower bound of every score (max or mean over heads of these
           // logits); the heads' maxima below bound them from above
@@ -1452,7 +1494,7 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
 
   __builtin_amdgcn_s_setprio(2);
   // every weight exp(logit + bias - m) <= 1 with m the head's maximum logit
-  const int hcol = min(c >> 1, a.G - 1);
+  const int hcol = min(col_head(c), a.G - 1);
   float m0 = kNegInf;
   for (int w = 0; w < kWaves; ++w) m0 = fmaxf(m0, s_mh[w][hcol]);
   Softmax<D> st;
@@ -1467,7 +1509,7 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       st.l += sign * p[r];
-      w[r] = sign * p[r] * V.vn[r];
+      w[r] = sign * p[r] * row_norm(V.vn, r);
     }
     pv3<D>(V.va, vsh, weight_operand(w, lane), lane4, lut3, st.O);
   };
@@ -1552,17 +1594,19 @@ __device__ __forceinline__ void route_unit(const SumArgs& a, const RouteLds& L, 
       const u32x4 g4 = gnext;
       gnext = sel_rows(i + 1);
       const int j = wave + i * kWaves;
+      uint32_t nof = kFar;  // this lane's norm row: 4gq + (lane & 3)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool in = 16 * j + 4 * gq + r < nsel;
         const uint32_t g = in ? g4[r] : 0u;
         const uint32_t far = in ? 0u : kFar;
-        uint32_t vo = (g * RB + vb) | far, no = (g * 4u) | far;
-        asm("" : "+v"(vo), "+v"(no));  // one load at one address per row
+        uint32_t vo = (g * RB + vb) | far;
+        asm("" : "+v"(vo));  // one load at one address per row
         C.V.va[r] = ld32(rv, vo);
-        C.V.vn[r] = __uint_as_float(ld32(rvn, no));
+        nof = (r == (lane & 3)) ? ((g * 4u) | far) : nof;
         C.lg[r] = lcol[g];
       }
+      C.V.vn = __uint_as_float(ld32(rvn, nof));
     };
     constexpr int KC = 2;
     CorrTile ct[KC];
@@ -1626,8 +1670,8 @@ struct TokArgs {
 
 struct TokTile {
   u32x4 kw;        // key code dwords of token row lane&15 (D=64 uses .x, .y)
-  f32x4 kn;        // key norms of rows 4gq+i
-  f32x4 vn;        // value norms of rows 4gq+i
+  float kn;        // key norm of row 4gq + (lane & 3) (see mul_rows)
+  float vn;        // value norm of row 4gq + (lane & 3)
   uint32_t va[4];  // value bits of rows 4gq+j for lane rho = lane&15
 };
 
@@ -1661,11 +1705,14 @@ __device__ __forceinline__ TokBufs tok_bufs(const TokArgs& a, int unit) {
 // picks the buffers, per-lane selects pick the offsets).
 // Loads of tile t given the record offsets bk (key rows) and br (value
 // rows, norms) of its archive slot(s); an L1 tile ignores them.
-template <int D, int N>
+// FRESH: the lane's address parts are recomputed from lane_now() (for
+// kernels whose pipelines run at the register limit).
+template <int D, int N, bool FRESH = false>
 __device__ __forceinline__ void load_tok_at(const TokBufs& B, int t, int n1t, int n1, uint32_t bk,
                                             uint32_t br, int lane, TokTile& T) {
   constexpr int CB = D / 2;
   constexpr uint32_t KB = D / 8;  // key code bytes per lane
+  if constexpr (FRESH) lane = lane_now();
   const int n = lane & 15, gq = lane >> 4;
   const int tk = (N == 16) ? n : (n & 7);            // key row within the group
   const int tr = (N == 16) ? 4 * gq : 4 * (gq & 1);  // first value row within the group
@@ -1684,8 +1731,8 @@ __device__ __forceinline__ void load_tok_at(const TokBufs& B, int t, int n1t, in
       const u32x2 w = ld64(B.l1k, tc + (uint32_t)(n * CB) + KB * gq);
       T.kw = u32x4{w.x, w.y, 0u, 0u};
     }
-    T.kn = ldf4(B.l1kn, tn + (uint32_t)(16 * gq));
-    T.vn = ldf4(B.l1vn, tn + (uint32_t)(16 * gq));
+    T.kn = __uint_as_float(ld32(B.l1kn, tn + (uint32_t)(16 * gq + 4 * (lane & 3))));
+    T.vn = __uint_as_float(ld32(B.l1vn, tn + (uint32_t)(16 * gq + 4 * (lane & 3))));
 #pragma unroll
     for (int j = 0; j < 4; ++j) T.va[j] = ld32(B.l1v, vo + j * CB);
   } else {
@@ -1697,8 +1744,8 @@ __device__ __forceinline__ void load_tok_at(const TokBufs& B, int t, int n1t, in
       const u32x2 w = ld64(B.l3, bk + (uint32_t)(tk * CB) + KB * gq);
       T.kw = u32x4{w.x, w.y, 0u, 0u};
     }
-    T.kn = ldf4(B.l3, br + (uint32_t)(N * CB + 4 * tr));
-    T.vn = ldf4(B.l3, br + (uint32_t)(N * (2 * CB + 4) + 4 * tr));
+    T.kn = __uint_as_float(ld32(B.l3, br + (uint32_t)(N * CB + 4 * (tr + (lane & 3)))));
+    T.vn = __uint_as_float(ld32(B.l3, br + (uint32_t)(N * (2 * CB + 4) + 4 * (tr + (lane & 3)))));
 #pragma unroll
     for (int j = 0; j < 4; ++j) T.va[j] = ld32(B.l3, vo + j * CB);
   }
@@ -1711,22 +1758,23 @@ __device__ __forceinline__ int tile_slot(int t, int n1t) {
 }
 // Loads of tile t, the record offsets read from recoff (which covers every
 // slot a tile of the pipeline can name, see tok_slots).
-template <int D, int N>
+template <int D, int N, bool FRESH = false>
 __device__ __forceinline__ void load_tok(const TokBufs& B, const int32_t* recoff, int t, int n1t,
                                          int n1, int lane, TokTile& T) {
+  if constexpr (FRESH) lane = lane_now();
   const int n = lane & 15, gq = lane >> 4;
   const int xk = (N == 16) ? 0 : (n >> 3), xr = (N == 16) ? 0 : (gq >> 1);
   const int32_t* rs = recoff + tile_slot<N>(t, n1t);
   const uint32_t bk = (uint32_t)rs[xk];
   const uint32_t br = (uint32_t)rs[xr];
-  load_tok_at<D, N>(B, t, n1t, n1, bk, br, lane, T);
+  load_tok_at<D, N, FRESH>(B, t, n1t, n1, bk, br, lane, T);
 }
 // Entries of the record-offset table: every slot of the fetched tiles and of
 // the tiles the pipeline loads past the last one (they read kFar).  A wave's
 // loads run at most 2K-2 of its tiles (8 tile indices apart) past its last.
-template <int N>
+template <int N, int NW = kWaves, int TD = kTokDepth>
 __host__ __device__ constexpr int tok_slots(int beta) {
-  return (N == 16 ? 1 : 2) * ((N == 16 ? beta : (beta + 1) / 2) + 2 * kWaves * kTokDepth);
+  return (N == 16 ? 1 : 2) * ((N == 16 ? beta : (beta + 1) / 2) + 2 * NW * TD);
 }
 
 // Rows of tile t that hold no token: lg = -inf.  Only the ragged last L1
@@ -1748,7 +1796,10 @@ __device__ __forceinline__ void mask_rows(float (&lg)[4], int t, int n1t, int n1
   for (int i = 0; i < 4; ++i) lg[i] = ((ok >> i) & 1u) ? lg[i] : kNegInf;
 }
 
-template <int D, typename MaskF>
+// SPLITQ: qh is the router operand (fp16 high parts of the query in columns
+// c < 8, low parts in c + 8), so one row rotation completes fp32-accurate
+// query products in every column.
+template <int D, bool SPLITQ = false, typename MaskF>
 __device__ __forceinline__ void consume_tok(const TokTile& T, bool masked, MaskF mask,
                                             const half8 (&qh)[D / 32], const uint32_t* lut4,
                                             int lane, uint32_t lane4, Softmax<D>& st) {
@@ -1761,17 +1812,24 @@ __device__ __forceinline__ void consume_tok(const TokTile& T, bool masked, MaskF
                            lds_at(lut4, lut4_addr<2>(w, lane4)), lds_at(lut4, lut4_addr<3>(w, lane4)));
     acc2[m & 1] = mfma16(av, qh[m], acc2[m & 1]);
   }
-  const f32x4 acc = acc2[0] + acc2[1];
+  f32x4 acc = acc2[0] + acc2[1];
+  if constexpr (SPLITQ) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = __float_as_int(acc[i]);
+      acc[i] += __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x128, 0xf, 0xf, true));
+    }
+  }
   float lg[4], p[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lg[i] = acc[i] * T.kn[i];
+  for (int i = 0; i < 4; ++i) lg[i] = acc[i] * row_norm(T.kn, i);
   if (masked) mask(lg);  // wave-uniform
   st.update(lg, p);
   float w[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     st.l += p[i];
-    w[i] = p[i] * T.vn[i];
+    w[i] = p[i] * row_norm(T.vn, i);
   }
   uint32_t va[4];
 #pragma unroll
@@ -1973,92 +2031,598 @@ void token_kernel(TokArgs a) {
   attend_unit<D, N>(a, L, tt, true, &s_bad, nullptr, unit);
 }
 
-// LDS of the one-launch step.  A static 64 KB table region holds the 4-bit
-// table in the attend phase (and its combine scratch after the tiles) and,
-// in the route phase, the 3-bit table (first kLut3Bytes), then the route
-// arrays and the landing slot of lanes without a head when they fit (else
-// those go to the front of the dynamic LDS).  The tables sit at fixed
-// addresses, so the table reads fold them into their offsets.  The dynamic
-// LDS then holds the arrays both phases use: [qf][record offsets].
-constexpr int kLut4Bytes = 256 * kNC4 * 4;
-constexpr int kLut3Bytes = 64 * kNC3 * 4;
-struct StepLayout {
-  RouteLayout r;   // offsets from the table (in_tab) or from the dynamic LDS
-  bool in_tab;
-  int dummy, qf, recoff, end;  // end: dynamic LDS bytes
+// ------------------------------------------------------- one-launch step ---
+//
+// The whole decode step on one work-group per unit (archive in device-visible
+// memory, 0 < n_groups <= kFusedMaxGroups).
+//   (1) One stream over the summaries.  A tile brings the keys and values of
+//       16 summaries; the three-term router (fp16 centroid parts and query
+//       parts, fp32 sums) forms fp32-accurate per-head logits.  Their maximum
+//       (or mean) over the heads is the router score, kept in LDS; the same
+//       logits weight the values in each wave's online softmax.  Nothing else
+//       of a tile outlives it.
+//   (2) Top-beta over the scores by all eight waves: a 256-bucket histogram
+//       over the scores' range, the groups above the threshold bucket taken,
+//       those inside it ranked exactly by (score descending, index
+//       ascending); then the selection in ascending order as record offsets.
+//       The first L1 token tiles load meanwhile.
+//   (3) The fetched groups' summaries are streamed again, 16 per tile, and
+//       subtracted with the same logits; the L1 tiles and the fetched tokens
+//       continue the same softmax states.
+//   (4) The waves' states combine; inverse V rotation; output.
+//
+// LDS: one static 64 KB region of 256 blocks of 256 bytes.  The low half of
+// block e holds entry e of the 4-bit table (a code byte -> fp16 centroid
+// pair) in 32 copies, so lane l reads copy l % 32 at (e << 8) | (l % 32) << 2,
+// an address one v_perm builds from the code dword.  The high halves hold,
+// again in 32 copies at (f << 8) | 128 | (l % 32) << 2, the 3-bit table
+// (blocks 0..63, 6-bit field f), its low parts (blocks 64..127, one
+// immediate offset away, so a field's two reads share an address) and the
+// router scores (blocks 128..191, 32 per block).  Each 32-lane half of a wave
+// then reads 32 different banks from any table.  Once the tiles are done the
+// region is the wave-combine scratch.
+constexpr int kTabBytes = 256 * 256;
+constexpr uint32_t kHiHalf = 128u;
+constexpr uint32_t kLoOff = 64u * 256u;  // low-part table, from the 3-bit table
+constexpr int kScoreBlock = 128;
+constexpr int kFusedMaxGroups = 64 * 32;
+constexpr int kCandCap = 256;  // threshold-bucket groups ranked in parallel
+// Waves per work-group and the pipeline depths (tiles per wave: SD in the
+// summary stream, TD in the token pipeline) that its register budget allows:
+// two work-groups share a CU (the LDS limit), so eight waves leave each 128
+// registers per lane (WPE waves per SIMD).  Measured on the 16K-context,
+// 40/8-head layer: four or five tiles deep were no faster, and four waves
+// with 200 registers each streamed slower (fewer waves to hide latencies).
+template <int NW> struct FusedCfg;
+template <> struct FusedCfg<8> { static constexpr int SD = 3, TD = 3, WPE = 4; };
+constexpr int kFusedWaves = 8;
+static_assert((8 + 1) * kMaxG * (128 + 2) * 4 + kMaxG * 128 * 4 <= kTabBytes,
+              "the epilogue's scratch must fit in the table region");
+
+// Both tables: the 4-bit one into the low halves (thread t writes 16-byte
+// chunks t, t + 512, ..., eight per entry), the 3-bit one and its low parts
+// into the high halves of blocks 0..127.
+template <int NT>
+__device__ void build_tables(uint32_t* tab, const float* cb4, const float* cb3, int tid) {
+  u32x4* dst = reinterpret_cast<u32x4*>(tab);
+  for (int c = tid; c < 2048; c += NT) {
+    const int e = c >> 3;
+    const uint32_t v = h2u((_Float16)cb4[e & 15], (_Float16)cb4[e >> 4]);
+    dst[16 * e + (c & 7)] = u32x4{v, v, v, v};
+  }
+  for (int c = tid; c < 1024; c += NT) {
+    const int b = c >> 3, f = b & 63;
+    const float c0 = cb3[f & 7], c1 = cb3[f >> 3];
+    const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
+    const uint32_t v = b < 64 ? h2u(h0, h1)
+                              : h2u((_Float16)((c0 - (float)h0) * kLoScale),
+                                    (_Float16)((c1 - (float)h1) * kLoScale));
+    dst[16 * b + 8 + (c & 7)] = u32x4{v, v, v, v};
+  }
+}
+// LDS byte address of router score g (scores of 4-aligned g .. g+3 are
+// contiguous).
+__device__ __forceinline__ uint32_t score_addr(int g) {
+  return ((uint32_t)(kScoreBlock + (g >> 5)) << 8) | kHiHalf | ((uint32_t)(g & 31) << 2);
+}
+__device__ __forceinline__ f32x4 scores4(const uint32_t* tab, int g) {
+  return *reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(tab) + score_addr(g));
+}
+
+// B operand of the one-launch router: column c < 8 holds the fp16 high part
+// of head c's rotated query, column 8 + c its low part.  Columns of absent
+// heads copy head 0 for the maximum (it does not change a maximum) and stay
+// zero for the mean (they add nothing to a sum).
+template <int D>
+__device__ void router_operands_pad(const float* qf, int lane, int G, bool mean,
+                                    half8 (&b)[D / 32]) {
+  const int c = lane & 15, gq = lane >> 4, hc = col_head(c);
+  const int h = (hc >= G && !mean) ? 0 : hc;
+  const bool low = c >= 8;
+  const f32x4* src = reinterpret_cast<const f32x4*>(qf + h * kQS<D> + gq * (D / 4));
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m) {
+    const f32x4 x0 = src[2 * m], x1 = src[2 * m + 1];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float x = (j < 4) ? x0[j] : x1[j - 4];
+      const _Float16 xh = (_Float16)x;
+      b[m][j] = low ? (_Float16)(x - (float)xh) : xh;
+    }
+  }
+}
+
+// Per-head logits of 16 summaries, fp32-accurate: the fp16 centroid parts
+// (hi, and lo scaled by kLoScale) against both query parts.  Lane (c, gq)
+// returns head col_head(c)'s scaled logits of rows 4gq .. 4gq+3 before the
+// key norm.  kw: this lane's 3D/4 key bits from bit 0.
+template <int D>
+__device__ __forceinline__ f32x4 qk3_exact(const uint32_t (&kw)[3], const half8 (&b)[D / 32],
+                                           const uint32_t* tabh, uint32_t lane4) {
+  uint32_t a[D / 8];
+#define HSQ_FIELD_ADDR(P) a[P] = (field6<6 * (P)>(kw) << 8) | lane4
+  HSQ_FIELD_ADDR(0); HSQ_FIELD_ADDR(1); HSQ_FIELD_ADDR(2); HSQ_FIELD_ADDR(3);
+  HSQ_FIELD_ADDR(4); HSQ_FIELD_ADDR(5); HSQ_FIELD_ADDR(6); HSQ_FIELD_ADDR(7);
+  if constexpr (D == 128) {
+    HSQ_FIELD_ADDR(8); HSQ_FIELD_ADDR(9); HSQ_FIELD_ADDR(10); HSQ_FIELD_ADDR(11);
+    HSQ_FIELD_ADDR(12); HSQ_FIELD_ADDR(13); HSQ_FIELD_ADDR(14); HSQ_FIELD_ADDR(15);
+  }
+#undef HSQ_FIELD_ADDR
+  const uint32_t* lo = tabh + kLoOff / 4;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, accl = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m) {
+    const half8 ak = as_h8(lds_at(tabh, a[4 * m]), lds_at(tabh, a[4 * m + 1]),
+                           lds_at(tabh, a[4 * m + 2]), lds_at(tabh, a[4 * m + 3]));
+    // kept apart from the high parts' reads: merged into two-address reads
+    // they would land interleaved and need moves into the operand registers
+    asm volatile("" ::: "memory");
+    const half8 al = as_h8(lds_at(lo, a[4 * m]), lds_at(lo, a[4 * m + 1]),
+                           lds_at(lo, a[4 * m + 2]), lds_at(lo, a[4 * m + 3]));
+    acc = mfma16(ak, b[m], acc);
+    accl = mfma16(al, b[m], accl);
+  }
+  acc += accl * (1.f / kLoScale);
+  f32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // row_ror:8 adds the query parts (columns c and c + 8)
+    const int v = __float_as_int(acc[i]);
+    r[i] = acc[i] + __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x128, 0xf, 0xf, true));
+  }
+  return r;
+}
+
+// PV with 3-bit values from the one-launch step's table (see pv3).
+template <int D>
+__device__ __forceinline__ void pv3_tab(const uint32_t (&va)[4], uint32_t sh, half8 b,
+                                        uint32_t lane4, const uint32_t* tabh, f32x4 (&O)[D / 32]) {
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+    uint32_t a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      a[j] = lds_at(tabh, (__builtin_amdgcn_ubfe(va[j], sh + 6 * t, 6) << 8) | lane4);
+    O[t] = mfma16(as_h8(a[0], a[1], a[2], a[3]), b, O[t]);
+  }
+}
+
+// Router score of this lane's four rows: the maximum (or the sum) over the
+// 16 columns of its row group; columns c and c + 8 hold the same head and
+// absent heads repeat head 0 (maximum) or are zero (sum), so three row steps
+// cover every head: quad_perm 1,0,3,2 and 2,3,0,1, then row_ror:4.  The
+// maximum is one v_max_f32 with a DPP operand per step (fmaxf would first
+// quiet both operands); the s_nop gives the DPP read of a just-written
+// register its two wait states.
+__device__ __forceinline__ float max_dpp_q1(float x) {
+  float r;
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+      : "=v"(r) : "v"(x));
+  return r;
+}
+__device__ __forceinline__ float max_dpp_q2(float x) {
+  float r;
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+      : "=v"(r) : "v"(x));
+  return r;
+}
+__device__ __forceinline__ float max_dpp_r4(float x) {
+  float r;
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 row_ror:4 row_mask:0xf bank_mask:0xf"
+      : "=v"(r) : "v"(x));
+  return r;
+}
+template <int CTRL>
+__device__ __forceinline__ float add_dpp(float x) {
+  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+template <bool MEAN>
+__device__ __forceinline__ f32x4 row_agg(f32x4 x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (MEAN)
+      x[i] = add_dpp<0x124>(add_dpp<0x4e>(add_dpp<0xb1>(x[i])));
+    else
+      x[i] = max_dpp_r4(max_dpp_q2(max_dpp_q1(x[i])));
+  }
+  return x;
+}
+
+// Summary tile: the keys and values of 16 summaries.
+struct SumTile {
+  KeyTile k;
+  ValTile v;
 };
-template <int D, int N>
-__host__ __device__ inline StepLayout step_layout(int G, int ng, int beta) {
-  StepLayout L;
-  L.r = route_layout(G, ng, beta, kLut3Bytes);
-  L.in_tab = L.r.end + 64 * 16 <= kLut4Bytes;
-  if (!L.in_tab) L.r = route_layout(G, ng, beta, 0);
-  L.dummy = L.r.end;
-  L.qf = L.in_tab ? 0 : L.dummy + 64 * 16;
+// Summary tile of 16 listed groups (list[16j .. 16j + 15], n entries in all;
+// rows past the list read zero).
+template <int D>
+__device__ __forceinline__ void load_sum_list(rsrc_t rk, rsrc_t rkn, rsrc_t rv, rsrc_t rvn,
+                                              const int32_t* list, int n, int j, int lane,
+                                              SumTile& T) {
+  constexpr int CB3 = 3 * D / 8;
+  const int r = lane & 15, gq = lane >> 4;
+  const int ik = 16 * j + r;
+  const uint32_t gk = ik < n ? (uint32_t)list[ik] : 0u;
+  const uint32_t fk = ik < n ? 0u : kFar;
+  uint32_t ko = (gk * CB3 + (D == 128 ? 12u * gq : 4u * ((3u * gq) >> 1))) | fk;
+  asm("" : "+v"(ko));
+  if constexpr (D == 128) {
+    const u32x3 w = ld96(rk, ko);
+    T.k.kw[0] = w.x; T.k.kw[1] = w.y; T.k.kw[2] = w.z;
+  } else {
+    const u32x2 w = ld64(rk, ko);
+    T.k.kw[0] = w.x; T.k.kw[1] = w.y; T.k.kw[2] = 0u;
+  }
+  const uint32_t vb = val_byte<D>(lane);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int ir = 16 * j + 4 * gq + q;
+    const uint32_t g = ir < n ? (uint32_t)list[ir] : 0u;
+    const uint32_t f = ir < n ? 0u : kFar;
+    uint32_t vo = (g * CB3 + vb) | f;
+    asm("" : "+v"(vo));  // one load at one address per row
+    T.v.va[q] = ld32(rv, vo);
+  }
+  // this lane's norm row, 4gq + (lane & 3)
+  const int in_ = 16 * j + 4 * gq + (lane & 3);
+  uint32_t no = in_ < n ? (uint32_t)list[in_] * 4u : kFar;
+  T.k.kn = __uint_as_float(ld32(rkn, no));
+  T.v.vn = __uint_as_float(ld32(rvn, no));
+}
+
+// Top-beta of the scores (0 < beta < ng) by the whole work-group, as a
+// bitmap of the selected groups in bits (LDS, zero on entry); hist (zero on
+// entry), cand and *nc are LDS scratch.  A 256-bucket histogram over [lo,
+// lo + 256 / bscale] (any bounds of the scores) places the beta-th largest
+// score in bucket bt; every wave finds bt, and the groups of higher buckets
+// are taken.  Wave 0 then ranks the groups of bucket bt exactly by (score
+// descending, index ascending) and takes the first `need`; with more than
+// kCandCap groups in bt (heavy exact ties) it runs a radix select over all
+// scores instead.  The same barriers run on every path; the bitmap is
+// complete for wave 0 on return, and for the other waves after their next
+// barrier.
+template <int NT>
+__device__ void select_bits(const uint32_t* tab, int ng, int beta, float lo, float bscale,
+                            int* hist, uint2* cand, int* nc, uint32_t* bits, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  for (int g = 4 * tid; g < ng; g += 4 * NT) {
+    const f32x4 s = scores4(tab, g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (g + e < ng) atomicAdd(&hist[score_bucket(fkey(s[e]), lo, bscale)], 1);
+  }
+  lds_barrier();
+  int bt, need;
+  hist_threshold(hist, beta, lane, bt, need);
+  const int nb = __builtin_amdgcn_readfirstlane(hist[bt]);
+  const bool fast = nb <= kCandCap;
+  if (fast) {
+    for (int g = 4 * tid; g < ng; g += 4 * NT) {
+      const f32x4 s = scores4(tab, g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (g + e >= ng) break;
+        const uint32_t k = fkey(s[e]);
+        const int b = score_bucket(k, lo, bscale);
+        if (b > bt) atomicOr(&bits[(g + e) >> 5], 1u << ((g + e) & 31));
+        if (b == bt) cand[atomicAdd(nc, 1)] = make_uint2((uint32_t)(g + e), k);
+      }
+    }
+  }
+  lds_barrier();
+  if (wave != 0) return;
+  if (fast) {
+    for (int i0 = 0; i0 < nb; i0 += 64) {
+      const uint2 me = i0 + lane < nb ? cand[i0 + lane] : make_uint2(0u, 0u);
+      int rank = 0;
+      for (int j = 0; j < nb; ++j) {
+        const uint2 o = cand[j];
+        rank += (o.y > me.y) || (o.y == me.y && o.x < me.x);
+      }
+      if (i0 + lane < nb && rank < need) atomicOr(&bits[me.x >> 5], 1u << (me.x & 31));
+    }
+  } else {
+    auto key = [&](int g) {
+      return fkey(*reinterpret_cast<const float*>(reinterpret_cast<const char*>(tab) + score_addr(g)));
+    };
+    int nd;
+    const uint32_t kth = radix_kth_f(key, ng, beta, hist, lane, nd);
+    int eq_before = 0;
+    for (int g0 = 0; g0 < ng; g0 += 64) {
+      const int g = g0 + lane;
+      const uint32_t k = g < ng ? key(g) : 0u;
+      const bool eq = g < ng && k == kth;
+      int n_eq;
+      const int eq_excl = wave_excl_scan(eq ? 1 : 0, lane, n_eq);
+      if ((g < ng && k > kth) || (eq && eq_before + eq_excl < nd))
+        atomicOr(&bits[g >> 5], 1u << (g & 31));
+      eq_before += n_eq;
+    }
+  }
+  wave_lds_sync();
+}
+
+// The one-launch step's small LDS arrays after the static table: [qf]
+// [record offsets][selection list][histogram][threshold-bucket groups]
+// [selection bitmap].
+struct FusedLayout {
+  int qf, recoff, sel, hist, cand, bits, end;
+};
+template <int D, int N, int NW>
+__host__ __device__ inline FusedLayout fused_layout(int beta) {
+  FusedLayout L;
+  L.qf = 0;
   L.recoff = L.qf + kMaxG * kQS<D> * 4;
-  L.end = L.recoff + ((tok_slots<N>(beta) * 4 + 15) & ~15);
+  L.sel = L.recoff + ((tok_slots<N, NW, FusedCfg<NW>::TD>(beta) * 4 + 15) & ~15);
+  L.hist = L.sel + ((max(beta, 1) * 4 + 15) & ~15);
+  L.cand = L.hist + 256 * 4;
+  L.bits = L.cand + kCandCap * 8;
+  L.end = L.bits + (kFusedMaxGroups / 32) * 4;
   return L;
 }
-static_assert((kWaves + 2) * kMaxG * (128 + 2) * 4 <= kLut4Bytes,
-              "the attend phase's combine scratch must fit in the table region");
 
-// The whole decode step in one launch (archive in device-visible memory,
-// n_groups > 0): route_unit, then attend_unit on the same work-group.  The
-// selection reaches the attend phase as record offsets in LDS, and each
-// wave's softmax state of the summary partial carries on into the token
-// tiles, so the partial is combined over the waves only once, at the end.
-template <int D, int N>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+// the register budget of FusedCfg<NW> so that two work-groups (the LDS
+// limit) fit on a CU
+template <int D, int N, bool MEAN, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FusedCfg<NW>::WPE)))
 void step_kernel(SumArgs ra, TokArgs ta) {
+  constexpr int NT = NW * 64, SD = FusedCfg<NW>::SD, TD = FusedCfg<NW>::TD;
   extern __shared__ __align__(16) char smem[];
-  __shared__ __align__(16) uint32_t s_tab[kLut4Bytes / 4];
-  __shared__ float s_cb4[16];
+  __shared__ __align__(16) uint32_t tab[kTabBytes / 4];
+  __shared__ float s_cb3[8], s_cb4[16];
   __shared__ uint32_t s_vsb[kMaxG * (D / 8)];
-  const StepLayout S = step_layout<D, N>(ra.G, ra.ng, ra.beta);
-  uint32_t* tab = s_tab;
-  char* rbase = S.in_tab ? reinterpret_cast<char*>(s_tab) : smem;
-  float* qf = reinterpret_cast<float*>(smem + S.qf);
-  int32_t* recoff = reinterpret_cast<int32_t*>(smem + S.recoff);
-  const int tid = threadIdx.x;
-  const int unit = blockIdx.x;
-  const int kvh = unit % ta.Hkv;
+  __shared__ float s_lo[NW], s_hi[NW];
+  __shared__ int s_nc;
+  constexpr int CB3 = 3 * D / 8;
   constexpr int LPV = D / 8;
+  const FusedLayout FL = fused_layout<D, N, NW>(ra.beta);
+  float* qf = reinterpret_cast<float*>(smem + FL.qf);
+  int32_t* recoff = reinterpret_cast<int32_t*>(smem + FL.recoff);
+  int32_t* sel = reinterpret_cast<int32_t*>(smem + FL.sel);
+  int* hist = reinterpret_cast<int*>(smem + FL.hist);
+  uint2* cand = reinterpret_cast<uint2*>(smem + FL.cand);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(smem + FL.bits);
 
-  // the attend phase's small inputs; the empty slots past beta
-  const float cbv = (tid < 16) ? ta.cb4[tid] : 0.f;
-  const uint32_t vsb =
-      (tid < kMaxG * LPV) ? sign_byte(ta.v_signs + kvh * (D / 32), tid % LPV) : 0u;
-  for (int s = ra.beta + tid; s < tok_slots<N>(ra.beta); s += kThreads) recoff[s] = (int32_t)kFar;
-  if (tid < 16) s_cb4[tid] = cbv;
-  if (tid < kMaxG * LPV) s_vsb[tid] = vsb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int c = lane & 15, gq = lane >> 4;
+  const int unit = blockIdx.x;
+  const int kvh = unit % ra.Hkv;
+  const int ng = ra.ng, beta = ra.beta;
+  const uint32_t lane4 = (uint32_t)(lane & 31) << 2;
+  const uint32_t* tabh = tab + kHiHalf / 4;  // the high halves
+  const uint32_t rec = (uint32_t)(N * (D + 8));
+  // the summary partial is empty when every group is fetched; the router
+  // runs whenever it is not
+  const bool stream = beta < ng;
+  const int n_tiles = stream ? (ng + 15) >> 4 : 0;
 
-  const RouteLds R = route_lds<D>(rbase, S.r, tab, qf,
-                                  reinterpret_cast<float*>(rbase + S.dummy), nullptr);
-  // ends with a barrier: the selection and record offsets are visible and
-  // the union is free; each wave's summary partial stays in st
-  // this wave's first L1 tiles (they need no selection) are issued before
-  // the route's last barrier, so they load during its end and the table set-up
+  const rsrc_t rk = make_rsrc(ra.l2k + (size_t)unit * ra.ngs * CB3, (uint32_t)ng * CB3);
+  const rsrc_t rkn = make_rsrc(ra.l2k_n + (size_t)unit * ra.ngs, (uint32_t)ng * 4);
+  const rsrc_t rv = make_rsrc(ra.l2v + (size_t)unit * ra.ngs * CB3, (uint32_t)ng * CB3);
+  const rsrc_t rvn = make_rsrc(ra.l2v_n + (size_t)unit * ra.ngs, (uint32_t)ng * 4);
   const TokBufs TB = tok_bufs<D, N>(ta, unit);
   const int n1t = (ta.n1 + 15) / 16;
-  const int wave = wave_id();
-  TokTile tt[kTokDepth];
-  auto pre = [&] {
-#pragma unroll
-    for (int j = 0; j < kTokDepth - 1; ++j)
-      if (wave + j * kWaves < n1t)  // wave-uniform
-        load_tok_at<D, N>(TB, wave + j * kWaves, n1t, ta.n1, kFar, kFar, tid & 63, tt[j]);
-  };
-  Softmax<D> st;
-  route_unit<D, false>(ra, R, nullptr, &st, recoff, (uint32_t)(N * (D + 8)), unit, pre);
 
-  AttendLds L;
-  L.lut4 = tab;
-  L.qf = qf;
-  L.part = nullptr;
-  L.recoff = recoff;
-  L.cb = s_cb4;
-  L.vsb = s_vsb;
-  attend_unit<D, N>(ta, L, tt, true, nullptr, &st, unit);
+  // (0) global loads first: the set-up inputs and this wave's first summary
+  // tiles, whose latency the set-up below overlaps
+  const float cb3v = (tid < 8) ? ra.cb3[tid] : 0.f;
+  const float cb4v = (tid < 16) ? ta.cb4[tid] : 0.f;
+  QueryIn qin;
+  load_query<D>(ra.q + (size_t)unit * ra.G * D, ra.k_signs + kvh * (D / 32), ra.G, tid, qin);
+  const uint32_t vsb =
+      (tid < kMaxG * LPV) ? sign_byte(ta.v_signs + kvh * (D / 32), tid % LPV) : 0u;
+  auto load_tile = [&](int t, SumTile& T) {
+    load_keys<D>(rk, rkn, t, lane, T.k);
+    load_vals<D>(rv, rvn, t, lane, T.v);
+  };
+  SumTile ft[SD];
+#pragma unroll
+  for (int j = 0; j < SD - 1; ++j) load_tile(wave + j * NW, ft[j]);
+
+  for (int s = beta + tid; s < tok_slots<N, NW, TD>(beta); s += NT) recoff[s] = (int32_t)kFar;
+  for (int b = tid; b < 256; b += NT) hist[b] = 0;
+  if (tid < kFusedMaxGroups / 32) bits[tid] = 0u;
+  if (tid == 0) s_nc = 0;
+  if (tid < 8) s_cb3[tid] = cb3v;
+  if (tid < 16) s_cb4[tid] = cb4v;
+  if (tid < kMaxG * LPV) s_vsb[tid] = vsb;
+  rotate_query<D>(qin, ra.scale * rsqrtf((float)D), qf, tid);
+  lds_barrier();
+  build_tables<NT>(tab, s_cb4, s_cb3, tid);
+  lds_barrier();
+
+  // (1) the summary stream
+  // wave priorities: the stream 2, the selection 3 (the work-group waits on
+  // it), the tokens 1, the epilogue 0; where two work-groups share a CU, the
+  // one that is behind gets the issue slots first
+  __builtin_amdgcn_s_setprio(2);
+  Softmax<D> st;
+  st.init(kNegInf);
+  float lo = kPosInf, hi = kNegInf;
+  if (stream) {
+    half8 qb[D / 32];
+    router_operands_pad<D>(qf, lane, ra.G, MEAN, qb);
+    const float inv_g = 1.f / (float)ra.G;
+    const uint32_t vsh = val_shift<D>(lane);
+    const int last = n_tiles - 1;
+    const int tail = ng - 16 * last - 4 * gq;  // rows of the last tile for this lane
+    const int n_iters = wave_iters<NW>(n_tiles, wave);
+    pipeline<SD>(
+        n_iters, ft,
+        [&](int i, SumTile& T) { load_tile(wave + i * NW, T); },
+        [&](int i, const SumTile& T) {
+          const int t = wave + i * NW;
+          uint32_t kw[3];
+          key_bits<D>(T.k.kw, lane, kw);
+          const f32x4 lg4 = mul_rows(qk3_exact<D>(kw, qb, tabh, lane4), T.k.kn);
+          f32x4 s = row_agg<MEAN>(lg4);
+          if constexpr (MEAN) s *= inv_g;
+          // rows past the last group score 0 (norm 0): still bounds of the scores
+          lo = min3f(min3f(lo, s[0], s[1]), s[2], s[3]);
+          hi = max3f(max3f(hi, s[0], s[1]), s[2], s[3]);
+          if (c == 0) {  // scores 16t + 4gq .. +3 (see score_addr)
+            const uint32_t sa = ((uint32_t)(kScoreBlock + (t >> 1)) << 8) + 64u * (t & 1);
+            *reinterpret_cast<f32x4*>(reinterpret_cast<char*>(tab) + kHiHalf + sa + 16 * gq) = s;
+          }
+          float lg[4] = {lg4[0], lg4[1], lg4[2], lg4[3]};
+          if (t == last) {  // wave-uniform: rows past the last group weigh nothing
+            // (the empty asm keeps this a branch: selects would cost every tile)
+            asm volatile("");
+#pragma unroll
+            for (int r = 0; r < 4; ++r) lg[r] = r < tail ? lg[r] : kNegInf;
+          }
+          float p[4], w[4];
+          st.update(lg, p);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            st.l += p[r];
+            w[r] = p[r] * row_norm(T.v.vn, r);
+          }
+          pv3_tab<D>(T.v.va, vsh, weight_operand(w, lane), lane4, tabh, st.O);
+        });
+  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  if (lane == 0) {
+    s_lo[wave] = lo;
+    s_hi[wave] = hi;
+  }
+  // this wave's first L1 token tiles (they need no selection) load during
+  // the selection
+  TokTile tt[TD];
+#pragma unroll
+  for (int j = 0; j < TD - 1; ++j)
+    if (wave + j * NW < n1t)  // wave-uniform
+      load_tok_at<D, N>(TB, wave + j * NW, n1t, ta.n1, kFar, kFar, lane, tt[j]);
+  lds_barrier();  // the scores are complete
+
+  // (2) the selection, as a bitmap, then in ascending order
+  __builtin_amdgcn_s_setprio(3);
+  if (beta > 0 && beta < ng) {
+    lo = kPosInf;
+    hi = kNegInf;
+    for (int w = 0; w < NW; ++w) {
+      lo = fminf(lo, s_lo[w]);
+      hi = fmaxf(hi, s_hi[w]);
+    }
+    const float bs = 256.f / (hi - lo);
+    const float bscale = (hi > lo && __builtin_isfinite(bs)) ? bs : 0.f;
+    select_bits<NT>(tab, ng, beta, lo, bscale, hist, cand, &s_nc, bits, tid);
+    if (wave == 0) {
+      int32_t* idx = ra.idx ? ra.idx + (size_t)unit * beta : nullptr;
+      int pos0 = 0;
+      for (int w0 = 0; w0 < (ng + 31) >> 5; w0 += 64) {
+        const int wd = w0 + lane;
+        uint32_t b = wd < (ng + 31) >> 5 ? bits[wd] : 0u;
+        int total;
+        int pos = pos0 + wave_excl_scan(__popc(b), lane, total);
+        while (b) {
+          const int g = 32 * wd + __ffs(b) - 1;
+          if (pos < beta) {  // exactly beta bits are set; the test keeps the lists in bounds
+            sel[pos] = g;
+            recoff[pos] = (int32_t)((uint32_t)g * rec);
+            if (idx) idx[pos] = g;
+          }
+          ++pos;
+          b &= b - 1u;
+        }
+        pos0 += total;
+      }
+    }
+  } else if (beta > 0) {  // every group fetched
+    int32_t* idx = ra.idx ? ra.idx + (size_t)unit * beta : nullptr;
+    for (int g = tid; g < beta; g += NT) {
+      recoff[g] = (int32_t)((uint32_t)g * rec);
+      if (idx) idx[g] = g;
+    }
+  }
+  lds_barrier();  // the record offsets and the selection list are visible
+
+  // (3) The fetched groups' summaries come out first: 16 a tile, subtracted
+  // with the stream's own logits (the same code and operands).  Then one
+  // pipeline over the L1 tiles and the fetched tokens.  The summary bias
+  // shifts every summary logit and the reference alike: the stream took the
+  // weights without it, so it joins m now and the subtracted logits carry it.
+  __builtin_amdgcn_s_setprio(1);
+  st.m += ra.bias;
+  st.mL = st.m * kLog2e;
+  st.mth = st.m + kLazy;
+  const int ntc = (stream && beta > 0) ? (beta + 15) / 16 : 0;
+  const int nft = (N == 16) ? beta : (beta + 1) / 2;
+  const int total = n1t + nft;
+  const int iters = wave_iters<NW>(total, wave);
+  auto tile_of = [&](int i) { return i < iters ? wave + i * NW : total + wave + NW * (i - iters); };
+  SumTile ct;
+  if (wave < ntc) load_sum_list<D>(rk, rkn, rv, rvn, sel, beta, wave, lane, ct);
+#pragma unroll
+  for (int j = 0; j < TD - 1; ++j)
+    if (!(wave + j * NW < n1t))  // wave-uniform: the fetched tiles among the first
+      load_tok<D, N>(TB, recoff, tile_of(j), n1t, ta.n1, lane, tt[j]);
+  if (wave < ntc) {
+    half8 qb[D / 32];
+    router_operands_pad<D>(qf, lane, ra.G, MEAN, qb);
+    const uint32_t vsh = val_shift<D>(lane);
+    for (int j = wave; j < ntc; j += NW) {
+      if (j != wave) load_sum_list<D>(rk, rkn, rv, rvn, sel, beta, j, lane, ct);
+      uint32_t kw[3];
+      key_bits<D>(ct.k.kw, lane, kw);
+      const f32x4 lg4 = mul_rows(qk3_exact<D>(kw, qb, tabh, lane4), ct.k.kn);
+      float lg[4], p[4], w[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        lg[r] = (16 * j + 4 * gq + r < beta) ? lg4[r] + ra.bias : kNegInf;
+      st.update(lg, p);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        st.l -= p[r];
+        w[r] = -p[r] * row_norm(ct.v.vn, r);
+      }
+      pv3_tab<D>(ct.v.va, vsh, weight_operand(w, lane), lane4, tabh, st.O);
+    }
+  }
+  {
+    half8 qh[D / 32], ql[D / 32];
+    query_operands<D>(qf, lane, qh, ql);
+    const int ragged = (ta.n1 & 15) ? n1t - 1 : -1;
+    const int half = (N == 8 && (beta & 1)) ? total - 1 : -1;
+    pipeline<TD>(
+        iters, tt,
+        [&](int i, TokTile& T) { load_tok<D, N>(TB, recoff, tile_of(i), n1t, ta.n1, lane, T); },
+        [&](int i, const TokTile& T) {
+          const int t = tile_of(i);
+          consume_tok<D>(
+              T, t == ragged || t == half,
+              [&](float (&lg)[4]) { mask_rows<N>(lg, t, n1t, ta.n1, beta, recoff, lane); }, qh,
+              tab, lane, lane4, st);
+        });
+  }
+  lds_barrier();  // the tables are no longer needed: reuse as scratch
+
+  // (4) combine, normalise, inverse V rotation, output
+  __builtin_amdgcn_s_setprio(0);
+  float* scratch = reinterpret_cast<float*>(tab);
+  float* mine = scratch + NW * kMaxG * (D + 2);
+  combine_waves<D, NW>(st, ra.G, scratch, mine, tid);
+  float* o = mine + kMaxG * (D + 2);
+  for (int k = tid; k < ra.G * D; k += NT) {
+    const int h = k / D, e = k % D;
+    const float l = mine[h * (D + 2) + 1];
+    o[k] = l > 0.f ? mine[h * (D + 2) + 2 + e] / l : 0.f;
+  }
+  lds_barrier();
+  if (tid < kMaxG * LPV) {
+    const int h = tid / LPV, sub = tid % LPV;
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = (h < ra.G) ? o[h * D + 8 * sub + k] : 0.f;
+    fwht8xlanes<LPV>(v, sub);
+    if (h < ra.G) {
+      const uint32_t sb = s_vsb[tid];
+      const float sc = rsqrtf((float)D);
+      float* dst = ta.out + ((size_t)unit * ra.G + h) * D + 8 * sub;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) dst[k] = flip(v[k] * sc, (sb >> k) & 1u);
+    }
+  }
 }
 
 // ------------------------------------------------------ split decode step ---
@@ -2161,8 +2725,8 @@ __global__ __launch_bounds__(64 * kScoreWaves) void split_scores_kernel(SplitArg
   lds_barrier();
   uint32_t kw[3];
   key_bits<D>(kt.kw, lane, kw);
-  f32x4 lg = qk3<D, EXACT>(kw, qb, s_lut3, s_lut3lo, lane4) * kt.kn;
-  const float rn = wave_max(max3f(max3f(kt.kn[0], kt.kn[1], kt.kn[2]), kt.kn[3], 0.f));
+  f32x4 lg = mul_rows(qk3<D, EXACT>(kw, qb, s_lut3, s_lut3lo, lane4), kt.kn);
+  const float rn = wave_max(fmaxf(kt.kn, 0.f));
   const int g0 = 16 * t + 4 * gq;
   const bool live = t < a.p.n_vt;  // wave-uniform: the last chunk may have a tile past the end
   if (live && c < r.G) {
@@ -2327,7 +2891,7 @@ void split_attend_kernel(SplitArgs a) {
     lds_barrier();
     build_lut3(s_tab, s_cb, tid);
     lds_barrier();
-    const int c = lane & 15, gq = lane >> 4, hcol = min(c >> 1, G - 1);
+    const int c = lane & 15, gq = lane >> 4, hcol = min(col_head(c), G - 1);
     const uint32_t lane4 = (uint32_t)(lane & 31) << 2;
     const float* lrow = a.lgt + ((size_t)unit * G + hcol) * p.ngp + 4 * gq;
     const uint32_t* bw = a.bits + (size_t)unit * p.words;
@@ -2355,7 +2919,7 @@ void split_attend_kernel(SplitArgs a) {
             // reference, where exp(-inf - -inf) is not a number)
             pw[rr] = live[rr] ? pw[rr] : 0.f;
             st.l += pw[rr];
-            w[rr] = pw[rr] * V.vn[rr];
+            w[rr] = pw[rr] * row_norm(V.vn, rr);
           }
           pv3<D>(V.va, vsh, weight_operand(w, lane), lane4, s_tab, st.O);
         });
@@ -2441,11 +3005,12 @@ size_t token_smem(int D, const StepShape& s) {
 }
 
 size_t step_smem(const StepShape& s) {
+  constexpr int NW = kFusedWaves;
   if (s.d == 128)
-    return (size_t)(s.group_n == 16 ? step_layout<128, 16>(s.G, s.n_groups, s.beta).end
-                                    : step_layout<128, 8>(s.G, s.n_groups, s.beta).end);
-  return (size_t)(s.group_n == 16 ? step_layout<64, 16>(s.G, s.n_groups, s.beta).end
-                                  : step_layout<64, 8>(s.G, s.n_groups, s.beta).end);
+    return (size_t)(s.group_n == 16 ? fused_layout<128, 16, NW>(s.beta).end
+                                    : fused_layout<128, 8, NW>(s.beta).end);
+  return (size_t)(s.group_n == 16 ? fused_layout<64, 16, NW>(s.beta).end
+                                  : fused_layout<64, 8, NW>(s.beta).end);
 }
 
 }  // namespace
@@ -2672,13 +3237,19 @@ hipError_t step_dn(const StepShape& s, const StepTensors& t, int32_t* idx_out, h
   ra.want_partial = 1;
   ra.idx = idx_out;
   TokArgs ta = tok_args(s, t);
-  hipLaunchKernelGGL((step_kernel<D, N>), dim3((unsigned)(s.B * s.Hkv)), dim3(kThreads),
-                     step_smem(s), st, ra, ta);
+  constexpr int NW = kFusedWaves;
+  if (t.agg == HSQ_AGG_MAX)
+    hipLaunchKernelGGL((step_kernel<D, N, false, NW>), dim3((unsigned)(s.B * s.Hkv)),
+                       dim3(NW * 64), step_smem(s), st, ra, ta);
+  else
+    hipLaunchKernelGGL((step_kernel<D, N, true, NW>), dim3((unsigned)(s.B * s.Hkv)),
+                       dim3(NW * 64), step_smem(s), st, ra, ta);
   return hipGetLastError();
 }
 
 int step_fused_ok(const StepShape& s) {
-  return s.n_groups > 0 && step_limits_ok(s) && route_lds_ok(s) && step_smem(s) <= kMaxFusedLds;
+  return s.n_groups > 0 && s.n_groups <= kFusedMaxGroups && step_limits_ok(s) &&
+         step_smem(s) <= kMaxFusedLds;
 }
 
 hipError_t launch_step(const StepShape& s, const StepTensors& t, int32_t* idx_out,
