@@ -83,6 +83,7 @@ def parse():
     p.add_argument("--no-configs", action="store_true",
                    help="skip the Qwen3-8B 8K and 32K (HBM archive) lines")
     p.add_argument("--only-step", action="store_true", help="headline step only (for profiling)")
+    p.add_argument("--only-codec", action="store_true", help="codec loop only (for profiling)")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (calibrates HBM byte counters)")
     return p.parse_args()
@@ -706,7 +707,7 @@ def main():
                                    "part of it (--gpus must be 1)", "n_gpus": args.gpus}))
         sys.exit(2)
     pool = n_workers = None
-    if not args.only_step and not args.no_cpu:
+    if not (args.only_step or args.only_codec) and not args.no_cpu:
         pool, n_workers = start_cpu_pool()  # before the GPU is touched
     import torch
     from compressed_decode_attention_turboquant_amd import hsq
@@ -715,6 +716,9 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     hsq.lib()
+    if args.only_codec:
+        print(json.dumps({"codec": codec_rates(torch, hsq, W, reps=args.reps)}))
+        return
     res, layers = headline(args, torch, hsq, W)
     w = res["w"]
     k = res["kernels"]

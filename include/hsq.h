@@ -269,9 +269,13 @@ int hsq_decode_attn(const float* q, int B, int Hq, int Hkv, int d, const uint8_t
  * attention [HSQ "Decode process" steps 1-3]: hsq_route_topk followed by
  * hsq_decode_attn with l3_staged == 0 (the same selection; the output to
  * fp32 rounding of the order in which the partials merge).  With 128 or
- * more units (b, kvh) and G * n_groups <= 12288 it runs as one launch, one
- * work-group per unit with the selection and the summary partial kept on
- * chip.  With fewer units, or more groups, it runs as the split step: four
+ * more units (b, kvh), n_groups <= 2048 and G * n_groups <= 12288 it runs as
+ * one launch, one work-group per unit: one stream over the summaries (router
+ * scores and the summary attention together), the selection on chip, then
+ * the fetched summaries taken out again and the tokens attended.  With more
+ * than 2048 groups (and G * n_groups <= 12288) it runs as the two launches of
+ * hsq_route_topk and hsq_decode_attn.  With fewer units, or
+ * G * n_groups > 12288, it runs as the split step: four
  * launches that spread each unit over many work-groups (router logits and
  * keys, the selection, summary-value and token chunks as partials, a
  * log-sum-exp merge), with the hand-overs in the workspace; a unit's result

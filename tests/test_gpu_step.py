@@ -312,9 +312,10 @@ def test_route_topk_parity(name, w):
 def test_route_strict_on_oracle_records(name, w):
     # The GPU router on the oracle's own L2 records: no code can differ, so
     # the rules apply with no slack at all.  hsq_route_topk with scores (the
-    # exact router): scores within 2e-6 of the oracle's; both it and the
-    # one-launch step (computed scores, band rescoring): sets exact except
-    # groups within 1e-5 of the beta-th score.
+    # exact router): scores within 2e-6 of the oracle's; both it and
+    # hsq_decode_step (the one-launch step's exact router, or the split
+    # step's band rescoring): sets exact except groups within 1e-5 of the
+    # beta-th score.
     print(f"strict route {name}", flush=True)
     sc = Scenario(w)
     t = oracle_tiers(sc)
