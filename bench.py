@@ -84,6 +84,9 @@ def parse():
                    help="skip the Qwen3-8B 8K and 32K (HBM archive) lines")
     p.add_argument("--only-step", action="store_true", help="headline step only (for profiling)")
     p.add_argument("--only-codec", action="store_true", help="codec loop only (for profiling)")
+    p.add_argument("--only-host", action="store_true", help="pinned-host archive run only")
+    p.add_argument("--host-mb", type=int, default=2,
+                   help="micro-batches (and streams) of the pinned-host archive run")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (calibrates HBM byte counters)")
     return p.parse_args()
@@ -372,14 +375,14 @@ def codec_rates(torch, hsq, W, n_sets=3, reps=20):
     return out
 
 
-def host_archive(torch, hsq, W, reps=5):
+def host_archive(torch, hsq, W, reps=5, n_mb=2):
     """Decode step of 36 layers with the L3 archive in pinned host memory.
     Per layer: the route launch, the gather of the selected records over PCIe
     (through the device alias of the pinned archive) into HBM staging, and the
-    attend launch.  The batch runs as two micro-batches of half the sequences
-    on two streams: every sequence still takes its layers in order, and one
-    half's PCIe gather overlaps the other half's route and attend.  One
-    captured graph per decode step."""
+    attend launch.  The batch runs as n_mb micro-batches of its sequences on
+    n_mb streams: every sequence still takes its layers in order, the gathers
+    take the PCIe link in turn, and one micro-batch's gather overlaps the
+    others' route and attend.  One captured graph per decode step."""
     dev = "cuda"
     w = W.QWEN3_8B_32K
     cb = codebooks(hsq, w.d, dev)
@@ -393,8 +396,8 @@ def host_archive(torch, hsq, W, reps=5):
               for i in range(w.layers)]
     torch.cuda.synchronize()
     beta = min(w.beta, ng)
-    nb = w.batch // 2
-    halves = [(0, nb), (nb, w.batch - nb)]
+    cuts = [w.batch * k // n_mb for k in range(n_mb + 1)]
+    halves = [(cuts[k], cuts[k + 1] - cuts[k]) for k in range(n_mb)]
     lib = hsq.lib()
     per_seq = w.hkv * ng * rec  # archive bytes of one sequence in one layer
     # per half: a workspace per layer (it carries the selection and the summary
@@ -409,27 +412,36 @@ def host_archive(torch, hsq, W, reps=5):
                           ("l1k", "l1k_n", "l1v", "l1v_n", "l2k", "l2k_n", "l2v", "l2v_n")],
                         ly.tiers.l3) for ly in layers]
         mb.append((b0, n, ws, stg, tv))
-    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    streams = [torch.cuda.Stream() for _ in halves]
     main = streams[0]
-
-    def half_step(h):
-        b0, n, ws, stg, tv = mb[h]
-        for i, ly in enumerate(layers):
-            q = ly.q[b0:b0 + n]
-            hsq.step_route(q, tv[i], w.beta, ly.dks, cb["cb3"], ws[i])
-            # the selection is read in place at the start of the workspace
-            hsq._check(lib.hsq_gather_l3(arch.dev_ptr + i * per_layer + b0 * per_seq, rec, n,
-                                         w.hkv, ng, ws[i].ptr, beta, stg.data_ptr(),
-                                         torch.cuda.current_stream().cuda_stream))
-            hsq.step_attend(q, tv[i], w.beta, ly.dks, ly.dvs, cb["cb4"], ws[i],
-                            ly.out[b0:b0 + n], l3=stg.data_ptr(), l3_staged=True)
+    turn = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def one_step():
-        streams[1].wait_stream(main)
-        half_step(0)
-        with torch.cuda.stream(streams[1]):
-            half_step(1)
-        main.wait_stream(streams[1])
+        # The gathers take the link in turn (micro-batch 0, 1, .. of layer 0,
+        # then of layer 1, ..), each after the one before it, so that a
+        # micro-batch's attend and next route run while another's records
+        # cross.  The turn is taken on the device (hsq_gather_l3_ordered): an
+        # event wait between two streams costs about 10 us per hand-over.
+        turn.zero_()  # a fill kernel, before the streams fork
+        for st in streams[1:]:
+            st.wait_stream(main)
+        after = 0
+        for i, ly in enumerate(layers):
+            for h, (b0, n, ws, stg, tv) in enumerate(mb):
+                st = streams[h]
+                with torch.cuda.stream(st):
+                    q = ly.q[b0:b0 + n]
+                    hsq.step_route(q, tv[i], w.beta, ly.dks, cb["cb3"], ws[i])
+                    # the selection is read in place at the start of the workspace
+                    hsq._check(lib.hsq_gather_l3_ordered(
+                        arch.dev_ptr + i * per_layer + b0 * per_seq, rec, n, w.hkv, ng, ws[i].ptr,
+                        beta, stg.data_ptr(), turn.data_ptr(), after & 0xFFFFFFFF,
+                        st.cuda_stream))
+                    after += n * w.hkv * beta
+                    hsq.step_attend(q, tv[i], w.beta, ly.dks, ly.dvs, cb["cb4"], ws[i],
+                                    ly.out[b0:b0 + n], l3=stg.data_ptr(), l3_staged=True)
+        for st in streams[1:]:
+            main.wait_stream(st)
 
     with torch.cuda.stream(main):
         one_step()
@@ -455,6 +467,25 @@ def host_archive(torch, hsq, W, reps=5):
         return n_copies * nbytes / (c0.elapsed_time(c1) * 1e-3) / 1e9
     h2d = h2d_rate(min(per_layer, 1 << 30))
     h2d_layer = h2d_rate(w.batch * w.hkv * beta * rec, 20)
+
+    # the gather alone, for context: the first micro-batch's records of
+    # layer 0 (its selection from the replays above), launched back to back
+    def gather_rate(n_launch=20):
+        b0, n, ws, stg, _ = mb[0]
+        sm = main.cuda_stream
+        args_ = (arch.dev_ptr + b0 * per_seq, rec, n, w.hkv, ng, ws[0].ptr, beta, stg.data_ptr(),
+                 sm)
+        hsq._check(lib.hsq_gather_l3(*args_))
+        torch.cuda.synchronize()
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record(main)
+        for _ in range(n_launch):
+            hsq._check(lib.hsq_gather_l3(*args_))
+        c1.record(main)
+        torch.cuda.synchronize()
+        return n_launch * n * w.hkv * beta * rec / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    gather_gbs = gather_rate()
     pcie = link_bytes / (ms * 1e-3) / 1e9
     res = {
         "workload": w.name, "layers": w.layers, "batch": w.batch, "T": w.T, "beta": beta,
@@ -467,6 +498,7 @@ def host_archive(torch, hsq, W, reps=5):
         "pinned_h2d_copy_gbs": h2d,
         "pinned_h2d_copy_gbs_layer_size": h2d_layer,
         "frac_of_pinned_copy": pcie / h2d,
+        "gather_alone_gbs": gather_gbs,
         "archive_gib": per_layer * w.layers / 2 ** 30,
     }
     del layers, arch, g, mb
@@ -703,11 +735,11 @@ def cpu_baseline(torch, W, layers, pool, n_workers, budget_s=10.0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; runs on several GPUs are not "
-                                   "part of it (--gpus must be 1)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "the decode step runs on one GPU and bench.py measures one "
+                                   "GPU (--gpus must be 1)", "n_gpus": args.gpus}))
         sys.exit(2)
     pool = n_workers = None
-    if not (args.only_step or args.only_codec) and not args.no_cpu:
+    if not (args.only_step or args.only_codec or args.only_host) and not args.no_cpu:
         pool, n_workers = start_cpu_pool()  # before the GPU is touched
     import torch
     from compressed_decode_attention_turboquant_amd import hsq
@@ -718,6 +750,9 @@ def main():
     hsq.lib()
     if args.only_codec:
         print(json.dumps({"codec": codec_rates(torch, hsq, W, reps=args.reps)}))
+        return
+    if args.only_host:
+        print(json.dumps({"host_archive": host_archive(torch, hsq, W, n_mb=args.host_mb)}))
         return
     res, layers = headline(args, torch, hsq, W)
     w = res["w"]
@@ -777,7 +812,7 @@ def main():
         line["cache_append"] = cache_append_rate(torch, hsq, W)
     if not args.only_step and not args.no_host:
         try:
-            line["host_archive"] = host_archive(torch, hsq, W)
+            line["host_archive"] = host_archive(torch, hsq, W, n_mb=args.host_mb)
         except Exception as e:  # reported, never hides the headline
             line["host_archive"] = {"error": repr(e)}
         print(json.dumps({"progress": "host archive"}), file=sys.stderr, flush=True)

@@ -420,17 +420,44 @@ extern "C" int hsq_decode_step_static(const float* q, int B, int Hq, int Hkv, in
                          summary_bias, topk_idx, scratch, kStaticScratchBytes, out, stream);
 }
 
+namespace {
+
+int gather_common(const char* fn, const uint8_t* l3_src, size_t rec_bytes, int B, int Hkv,
+                  int n_groups, const int32_t* topk_idx, int beta, uint8_t* staging,
+                  uint32_t* turn, uint32_t after, void* stream) {
+  if (B < 1 || Hkv < 1 || n_groups < 0 || beta < 0 || beta > n_groups)
+    return fail(HSQ_ERR_ARG, std::string(fn) + ": bad sizes");
+  if (rec_bytes == 0 || rec_bytes % 16)
+    return fail(HSQ_ERR_ARG, std::string(fn) + ": rec_bytes must be a positive multiple of 16");
+  if (rec_bytes > (size_t(1) << 20))
+    return fail(HSQ_ERR_UNSUPPORTED, std::string(fn) + ": rec_bytes above 1 MiB");
+  if ((int64_t)B * Hkv * beta > (int64_t)UINT32_MAX)
+    return fail(HSQ_ERR_UNSUPPORTED, std::string(fn) + ": B * Hkv * beta must be < 2^32");
+  if (beta == 0) return HSQ_OK;
+  if (!l3_src || !topk_idx || !staging) return fail(HSQ_ERR_ARG, std::string(fn) + ": null pointer");
+  return check_hip(launch_gather(l3_src, rec_bytes, B * Hkv, n_groups, topk_idx, beta, staging,
+                                 turn, after, as_stream(stream)),
+                   (std::string(fn) + " launch").c_str());
+}
+
+}  // namespace
+
 extern "C" int hsq_gather_l3(const uint8_t* l3_src, size_t rec_bytes, int B, int Hkv,
                              int n_groups, const int32_t* topk_idx, int beta, uint8_t* staging,
                              void* stream) {
-  if (B < 1 || Hkv < 1 || n_groups < 0 || beta < 0 || beta > n_groups)
-    return fail(HSQ_ERR_ARG, "hsq_gather_l3: bad sizes");
-  if (rec_bytes == 0 || rec_bytes % 16) return fail(HSQ_ERR_ARG, "hsq_gather_l3: rec_bytes must be a positive multiple of 16");
-  if (beta == 0) return HSQ_OK;
-  if (!l3_src || !topk_idx || !staging) return fail(HSQ_ERR_ARG, "hsq_gather_l3: null pointer");
-  return check_hip(launch_gather(l3_src, rec_bytes, B * Hkv, n_groups, topk_idx, beta, staging,
-                                 as_stream(stream)),
-                   "hsq_gather_l3 launch");
+  return gather_common("hsq_gather_l3", l3_src, rec_bytes, B, Hkv, n_groups, topk_idx, beta,
+                       staging, nullptr, 0u, stream);
+}
+
+extern "C" int hsq_gather_l3_ordered(const uint8_t* l3_src, size_t rec_bytes, int B, int Hkv,
+                                     int n_groups, const int32_t* topk_idx, int beta,
+                                     uint8_t* staging, uint32_t* turn, uint32_t after,
+                                     void* stream) {
+  if (!turn) return fail(HSQ_ERR_ARG, "hsq_gather_l3_ordered: null turn");
+  if (reinterpret_cast<uintptr_t>(turn) % 4)
+    return fail(HSQ_ERR_ARG, "hsq_gather_l3_ordered: turn must be 4-byte aligned");
+  return gather_common("hsq_gather_l3_ordered", l3_src, rec_bytes, B, Hkv, n_groups, topk_idx,
+                       beta, staging, turn, after, stream);
 }
 
 extern "C" int hsq_cache_append(const void* k_new, const void* v_new, int dtype, int B, int Hkv,

@@ -124,8 +124,11 @@ hipError_t launch_attn(const StepShape& s, const StepTensors& t, const Workspace
 int step_fused_ok(const StepShape& s);
 hipError_t launch_step(const StepShape& s, const StepTensors& t, int32_t* idx_out,
                        hipStream_t st);
+// turn == nullptr: plain gather; else wait (bounded) for *turn >= after,
+// then add the records moved to *turn
 hipError_t launch_gather(const uint8_t* src, size_t rec_bytes, int units, int n_groups,
-                         const int32_t* idx, int beta, uint8_t* dst, hipStream_t st);
+                         const int32_t* idx, int beta, uint8_t* dst, uint32_t* turn,
+                         uint32_t after, hipStream_t st);
 
 // ---- decode-time tier maintenance (cache.hip) -------------------------------
 // One token appended per unit; layouts as in include/hsq.h ("Cache layout").

@@ -47,6 +47,7 @@ _SIGNATURES = {
     "hsq_step_attend": ([_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _vp, _i, _i, _i, _vp,
                          _vp, _vp, _f, _vp, _sz, _vp, _vp], _i),
     "hsq_gather_l3": ([_vp, _sz, _i, _i, _i, _vp, _i, _vp, _vp], _i),
+    "hsq_gather_l3_ordered": ([_vp, _sz, _i, _i, _i, _vp, _i, _vp, _vp, _c.c_uint32, _vp], _i),
     "hsq_cache_append": ([_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i64, _i, _i, _i, _i]
                          + [_vp] * 16, _i),
     "hsq_encode_qjl": ([_vp, _i, _i64, _i, _i] + [_vp] * 9, _i),
@@ -372,6 +373,17 @@ def gather_l3(l3_src_ptr, rec_bytes, B, Hkv, ng, idx, staging):
     beta = idx.shape[-1]
     _check(lib().hsq_gather_l3(l3_src_ptr, rec_bytes, B, Hkv, ng, _dev(idx, torch.int32, "idx"),
                                beta, _dev(staging, torch.uint8, "staging"), _stream()))
+    return staging
+
+
+def gather_l3_ordered(l3_src_ptr, rec_bytes, B, Hkv, ng, idx, staging, turn, after):
+    """gather_l3 after the gathers before it in a chain (turn: int32 [1] on
+    the device, zeroed before the chain; after: records of those gathers)."""
+    beta = idx.shape[-1]
+    _check(lib().hsq_gather_l3_ordered(
+        l3_src_ptr, rec_bytes, B, Hkv, ng, _dev(idx, torch.int32, "idx"), beta,
+        _dev(staging, torch.uint8, "staging"), _dev(turn, torch.int32, "turn"),
+        after & 0xFFFFFFFF, _stream()))
     return staging
 
 

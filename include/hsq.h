@@ -358,11 +358,38 @@ int hsq_step_attend(const float* q, int B, int Hq, int Hkv, int d, const uint8_t
  * device alias of pinned mapped host memory, so the copy crosses PCIe with
  * indices that never leave the device) and writes
  * staging[u][i] = l3_src[u][topk_idx[u][i]] for units u < B*Hkv, i < beta.
- *   rec_bytes   bytes per record, N*(d+8); must be a multiple of 16
- * Errors: HSQ_ERR_ARG (null, sizes), HSQ_ERR_HIP.
+ *   rec_bytes   bytes per record, N*(d+8); a multiple of 16, at most 1 MiB
+ * A selection index outside [0, n_groups) leaves its staging record as it
+ * was.  The launch uses few work-groups (128 records each), so that route
+ * and attend launches of other micro-batches keep most CUs to themselves.
+ * Errors: HSQ_ERR_ARG (null, sizes), HSQ_ERR_UNSUPPORTED (rec_bytes above
+ * 1 MiB, B*Hkv*beta >= 2^32), HSQ_ERR_HIP.
  */
 int hsq_gather_l3(const uint8_t* l3_src, size_t rec_bytes, int B, int Hkv, int n_groups,
                   const int32_t* topk_idx, int beta, uint8_t* staging, void* stream);
+
+/*
+ * hsq_gather_l3_ordered -- hsq_gather_l3 that takes its turn on the PCIe
+ * link after other gathers, for callers that split a batch into
+ * micro-batches on several streams [HSQ "Decode process" step 2; the
+ * pages put long-context decode time on the fetch from CPU memory, HSQ
+ * section 4 "Results"].  Before copying, the call's work-groups wait on the
+ * device until *turn >= after (compared modulo 2^32), for at most about
+ * 2 ms, and then copy regardless: the wait orders use of the link and never
+ * the data, so a wrong `after` costs time, not correctness.  Each
+ * work-group adds its records to *turn when its reads are done: once the
+ * call completes, *turn has grown by B*Hkv*beta.  A chain of gathers on
+ * any streams passes after = the running total of B*Hkv*beta of the gathers
+ * before it, with *turn zeroed (on the device, before the first) by the
+ * caller; the gathers then run one after the other without host-side
+ * events between the streams.
+ *   turn        device uint32, 4-byte aligned, owned by the caller
+ * Errors: as hsq_gather_l3; HSQ_ERR_ARG for a null or misaligned turn;
+ * HSQ_ERR_UNSUPPORTED when B*Hkv*beta >= 2^32.
+ */
+int hsq_gather_l3_ordered(const uint8_t* l3_src, size_t rec_bytes, int B, int Hkv, int n_groups,
+                          const int32_t* topk_idx, int beta, uint8_t* staging, uint32_t* turn,
+                          uint32_t after, void* stream);
 
 /* ------------------------------------------ decode-time tier maintenance -- */
 

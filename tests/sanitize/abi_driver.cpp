@@ -209,6 +209,18 @@ void run_errors() {
          HSQ_ERR_ARG, "L1");
   expect("gather rec_bytes", hsq_gather_l3(u8, 100, 1, 1, 4, i32, 2, u8, nullptr), HSQ_ERR_ARG);
   expect("gather beta>ng", hsq_gather_l3(u8, 1088, 1, 1, 4, i32, 5, u8, nullptr), HSQ_ERR_ARG);
+  expect("gather rec > 1 MiB", hsq_gather_l3(u8, (1u << 20) + 16, 1, 1, 4, i32, 2, u8, nullptr),
+         HSQ_ERR_UNSUPPORTED, "1 MiB");
+  expect("ordered gather null turn",
+         hsq_gather_l3_ordered(u8, 1088, 1, 1, 4, i32, 2, u8, nullptr, 0u, nullptr), HSQ_ERR_ARG,
+         "turn");
+  expect("ordered gather misaligned turn",
+         hsq_gather_l3_ordered(u8, 1088, 1, 1, 4, i32, 2, u8, reinterpret_cast<uint32_t*>(18), 0u,
+                               nullptr),
+         HSQ_ERR_ARG, "aligned");
+  expect("ordered gather beta>ng", hsq_gather_l3_ordered(u8, 1088, 1, 1, 4, i32, 5, u8, u32, 0u,
+                                                         nullptr),
+         HSQ_ERR_ARG);
   expect("tier_plan null marks", hsq_tier_plan(10, 1, 1, nullptr, 3, 8, nullptr, nullptr, nullptr,
                                                nullptr),
          HSQ_ERR_ARG);

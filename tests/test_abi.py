@@ -103,6 +103,11 @@ def test_argument_errors_are_reported_without_launch():
                               None, None, 0, None) == -1
     assert lib.hsq_gather_l3(p, 100, 1, 1, 4, p, 2, p, None) == -1
     assert lib.hsq_gather_l3(p, 1088, 1, 1, 4, p, 5, p, None) == -1
+    assert lib.hsq_gather_l3(p, (1 << 20) + 16, 1, 1, 4, p, 2, p, None) == -2
+    assert lib.hsq_gather_l3_ordered(p, 1088, 1, 1, 4, p, 2, p, None, 0, None) == -1
+    assert "turn" in lib.hsq_last_error().decode()
+    assert lib.hsq_gather_l3_ordered(p, 1088, 1, 1, 4, p, 2, p, ctypes.c_void_p(18), 0, None) == -1
+    assert lib.hsq_gather_l3_ordered(p, 1088, 1, 1, 4, p, 5, p, p, 0, None) == -1
     assert lib.hsq_tier_plan(10, 1, 1, None, 3, 8, None, None, None, None) == -1
 
 

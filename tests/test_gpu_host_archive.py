@@ -87,27 +87,83 @@ def test_host_archive_step_matches_the_device_archive_step():
 
 
 def test_gather_leaves_invalid_slots_untouched():
-    # 5 units x 9 slots = 45 slots: two full work-groups of 16 records and a
-    # partial one; some slots name no record (negative or past n_groups)
+    # 20 units x 13 slots = 260 slots: two full work-groups of 128 records
+    # and a partial one of 4; some slots name no record (negative or past
+    # n_groups), in full work-groups and in the partial one
     print("[gather] invalid slots, ragged last work-group", flush=True)
-    B, Hkv, ng, beta, rec = 5, 1, 40, 9, 8 * (64 + 8)
+    B, Hkv, ng, beta, rec = 5, 4, 40, 13, 8 * (64 + 8)
     g = torch.Generator().manual_seed(11)
     src = torch.randint(0, 256, (B, Hkv, ng, rec), dtype=torch.uint8, generator=g).to(DEV)
     idx = torch.randint(0, ng, (B, Hkv, beta), dtype=torch.int32, generator=g)
     idx[0, 0, 3] = -1
-    idx[2, 0, 8] = ng
-    idx[4, 0, 0] = -7
+    idx[2, 1, 8] = ng
+    idx[4, 3, 12] = -7   # slot 259, in the partial work-group
+    idx[4, 3, 9] = ng + 5
     staging = torch.full((B, Hkv, beta, rec), 0xAB, dtype=torch.uint8, device=DEV)
     hsq.gather_l3(src.data_ptr(), rec, B, Hkv, ng, idx.to(DEV), staging)
     torch.cuda.synchronize()
     s, x = staging.cpu(), src.cpu()
     for b in range(B):
-        for i in range(beta):
-            gi = int(idx[b, 0, i])
-            if 0 <= gi < ng:
-                assert torch.equal(s[b, 0, i], x[b, 0, gi]), (b, i)
-            else:
-                assert bool((s[b, 0, i] == 0xAB).all()), (b, i)
+        for h in range(Hkv):
+            for i in range(beta):
+                gi = int(idx[b, h, i])
+                if 0 <= gi < ng:
+                    assert torch.equal(s[b, h, i], x[b, h, gi]), (b, h, i)
+                else:
+                    assert bool((s[b, h, i] == 0xAB).all()), (b, h, i)
+
+
+def _gather_case(seed, B=4, Hkv=8, ng=300, beta=64, rec=16 * (128 + 8)):
+    g = torch.Generator().manual_seed(seed)
+    src = torch.randint(0, 256, (B, Hkv, ng, rec), dtype=torch.uint8, generator=g)
+    idx = torch.stack([torch.sort(torch.randperm(ng, generator=g)[:beta])[0]
+                       for _ in range(B * Hkv)]).reshape(B, Hkv, beta).to(torch.int32)
+    want = torch.stack([src[b, h, idx[b, h].long()] for b in range(B) for h in range(Hkv)])
+    return src, idx, want.reshape(B, Hkv, beta, rec)
+
+
+def test_ordered_gathers_on_two_streams():
+    # a chain of four ordered gathers over two streams, issued in turn order
+    # (as the pinned-host step issues them): every staging buffer holds its
+    # records, and the turn counter ends at the total record count
+    print("[gather ordered] 4 gathers, 2 streams", flush=True)
+    cases = [_gather_case(20 + k) for k in range(4)]
+    arch = hsq.HostArchive(sum(c[0].numel() for c in cases))
+    ptrs, off = [], 0
+    for src, _, _ in cases:
+        arch.host[off:off + src.numel()].copy_(src.reshape(-1))
+        ptrs.append(arch.dev_ptr + off)
+        off += src.numel()
+    turn = torch.zeros(1, dtype=torch.int32, device=DEV)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    stg = [torch.zeros_like(c[2], device=DEV) for c in cases]
+    idx = [c[1].to(DEV) for c in cases]
+    torch.cuda.synchronize()
+    after = 0
+    for k, (src, ix, want) in enumerate(cases):
+        B, Hkv, ng, rec = src.shape
+        with torch.cuda.stream(streams[k % 2]):
+            hsq.gather_l3_ordered(ptrs[k], rec, B, Hkv, ng, idx[k], stg[k], turn, after)
+        after += B * Hkv * ix.shape[-1]
+    torch.cuda.synchronize()
+    for k, (_, _, want) in enumerate(cases):
+        assert torch.equal(stg[k].cpu(), want), k
+    assert int(turn.item()) == after
+
+
+def test_ordered_gather_goes_ahead_when_its_turn_never_comes():
+    # the host passes a turn that no gather will reach: the bounded wait on
+    # the device ends (about 2 ms) and the records are copied regardless
+    print("[gather ordered] turn never reached: bounded wait", flush=True)
+    src, ix, want = _gather_case(31, B=2, Hkv=2, ng=50, beta=9, rec=8 * (64 + 8))
+    B, Hkv, ng, rec = src.shape
+    dsrc = src.to(DEV)
+    turn = torch.zeros(1, dtype=torch.int32, device=DEV)
+    staging = torch.zeros_like(want, device=DEV)
+    hsq.gather_l3_ordered(dsrc.data_ptr(), rec, B, Hkv, ng, ix.to(DEV), staging, turn, 1 << 30)
+    torch.cuda.synchronize()
+    assert torch.equal(staging.cpu(), want)
+    assert int(turn.item()) == B * Hkv * 9
 
 
 def test_selection_is_left_at_the_start_of_the_workspace():

@@ -615,6 +615,20 @@ def test_long_context_beyond_on_chip_logits():
     check_route(sc, idx, scores, [(0, 0), (1, 7)], w.beta)
 
 
+def test_two_launch_step_beyond_one_launch_groups():
+    # 40/8 heads (G = 5), N = 8, T = 18432, batch 16: 128 units of about 2270
+    # groups, more than the one-launch step takes (2048) while G * n_groups
+    # still fits the router's on-chip logits, so hsq_decode_step runs the
+    # route and attend launches; every unit against the oracle
+    w = W.QWEN3_14B_16K.smaller(T=18432, batch=16, n_marked=184)
+    print("two-launch step G=5 N=8 T=18432 batch 16", flush=True)
+    sc = Scenario(w)
+    ng = sc.tiers.ng
+    assert ng > 2048 and w.G * ((ng + 15) // 16 * 16) <= 12288 and w.batch * w.hkv >= 128
+    worst, n_codes, n_diff = check_full(sc, w.beta, agg="mean", bias=-0.4)
+    print(f"  worst rel L2 {worst:.3e}, {n_codes} code / {n_diff} set differences", flush=True)
+
+
 @pytest.mark.parametrize("layer", [0, 35])
 def test_qwen3_8b_32k_layer_full_size(layer):
     # one layer of the 36-layer, T=32768, batch-8, N=16, beta=64 workload at
