@@ -2080,25 +2080,40 @@ static_assert((8 + 1) * kMaxG * (128 + 2) * 4 + kMaxG * 128 * 4 <= kTabBytes,
               "the epilogue's scratch must fit in the table region");
 
 // Both tables: the 4-bit one into the low halves (thread t writes 16-byte
-// chunks t, t + 512, ..., eight per entry), the 3-bit one and its low parts
-// into the high halves of blocks 0..127.
-template <int NT>
-__device__ void build_tables(uint32_t* tab, const float* cb4, const float* cb3, int tid) {
+// chunks t, t + 512, t + 1024, t + 1536 of entries t/8 + 64k, eight chunks
+// per entry), the 3-bit one into the high halves of blocks 0..63 (chunk t)
+// and its low parts into those of blocks 64..127 (chunk t + 512).  A
+// thread's codebook values come straight from global memory (the loads are
+// issued with the kernel's first loads), so no barrier precedes the build.
+struct TabIn {
+  float lo4, hi4[4];  // cb4[(t/8) % 16], cb4[t/128 + 4k]
+  float c0, c1;       // cb3[(t/8) % 8], cb3[(t/64) % 8]
+};
+__device__ __forceinline__ TabIn load_tab_in(const float* cb4, const float* cb3, int tid) {
+  TabIn in;
+  in.lo4 = cb4[(tid >> 3) & 15];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) in.hi4[k] = cb4[(tid >> 7) + 4 * k];
+  in.c0 = cb3[(tid >> 3) & 7];
+  in.c1 = cb3[(tid >> 6) & 7];
+  return in;
+}
+__device__ void build_tables(uint32_t* tab, const TabIn& in, int tid) {
   u32x4* dst = reinterpret_cast<u32x4*>(tab);
-  for (int c = tid; c < 2048; c += NT) {
-    const int e = c >> 3;
-    const uint32_t v = h2u((_Float16)cb4[e & 15], (_Float16)cb4[e >> 4]);
+  const _Float16 lo = (_Float16)in.lo4;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = tid + 512 * k, e = c >> 3;  // e = t/8 + 64k: e % 16 = t/8 % 16, e / 16 = t/128 + 4k
+    const uint32_t v = h2u(lo, (_Float16)in.hi4[k]);
     dst[16 * e + (c & 7)] = u32x4{v, v, v, v};
   }
-  for (int c = tid; c < 1024; c += NT) {
-    const int b = c >> 3, f = b & 63;
-    const float c0 = cb3[f & 7], c1 = cb3[f >> 3];
-    const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
-    const uint32_t v = b < 64 ? h2u(h0, h1)
-                              : h2u((_Float16)((c0 - (float)h0) * kLoScale),
-                                    (_Float16)((c1 - (float)h1) * kLoScale));
-    dst[16 * b + 8 + (c & 7)] = u32x4{v, v, v, v};
-  }
+  const _Float16 h0 = (_Float16)in.c0, h1 = (_Float16)in.c1;
+  const int b = tid >> 3;  // f = b: cb3[f % 8], cb3[f / 8]
+  const uint32_t vh = h2u(h0, h1);
+  const uint32_t vl = h2u((_Float16)((in.c0 - (float)h0) * kLoScale),
+                          (_Float16)((in.c1 - (float)h1) * kLoScale));
+  dst[16 * b + 8 + (tid & 7)] = u32x4{vh, vh, vh, vh};
+  dst[16 * (b + 64) + 8 + (tid & 7)] = u32x4{vl, vl, vl, vl};
 }
 // LDS byte address of router score g (scores of 4-aligned g .. g+3 are
 // contiguous).
@@ -2368,7 +2383,6 @@ void step_kernel(SumArgs ra, TokArgs ta) {
   constexpr int NT = NW * 64, SD = FusedCfg<NW>::SD, TD = FusedCfg<NW>::TD;
   extern __shared__ __align__(16) char smem[];
   __shared__ __align__(16) uint32_t tab[kTabBytes / 4];
-  __shared__ float s_cb3[8], s_cb4[16];
   __shared__ uint32_t s_vsb[kMaxG * (D / 8)];
   __shared__ float s_lo[NW], s_hi[NW];
   __shared__ int s_nc;
@@ -2404,8 +2418,8 @@ void step_kernel(SumArgs ra, TokArgs ta) {
 
   // (0) global loads first: the set-up inputs and this wave's first summary
   // tiles, whose latency the set-up below overlaps
-  const float cb3v = (tid < 8) ? ra.cb3[tid] : 0.f;
-  const float cb4v = (tid < 16) ? ta.cb4[tid] : 0.f;
+  static_assert(NT == 512, "the table build assigns 16-byte chunks to 512 threads");
+  const TabIn tin = load_tab_in(ta.cb4, ra.cb3, tid);
   QueryIn qin;
   load_query<D>(ra.q + (size_t)unit * ra.G * D, ra.k_signs + kvh * (D / 32), ra.G, tid, qin);
   const uint32_t vsb =
@@ -2422,12 +2436,9 @@ void step_kernel(SumArgs ra, TokArgs ta) {
   for (int b = tid; b < 256; b += NT) hist[b] = 0;
   if (tid < kFusedMaxGroups / 32) bits[tid] = 0u;
   if (tid == 0) s_nc = 0;
-  if (tid < 8) s_cb3[tid] = cb3v;
-  if (tid < 16) s_cb4[tid] = cb4v;
   if (tid < kMaxG * LPV) s_vsb[tid] = vsb;
+  build_tables(tab, tin, tid);
   rotate_query<D>(qin, ra.scale * rsqrtf((float)D), qf, tid);
-  lds_barrier();
-  build_tables<NT>(tab, s_cb4, s_cb3, tid);
   lds_barrier();
 
   // (1) the summary stream
@@ -2486,6 +2497,12 @@ void step_kernel(SumArgs ra, TokArgs ta) {
     s_lo[wave] = lo;
     s_hi[wave] = hi;
   }
+  // The summary bias shifts every summary logit and the reference alike: the
+  // stream took the weights without it, so it joins m now, before any token
+  // comes in, and the subtracted logits carry it.
+  st.m += ra.bias;
+  st.mL = st.m * kLog2e;
+  st.mth = st.m + kLazy;
   // this wave's first L1 token tiles (they need no selection) load during
   // the selection
   TokTile tt[TD];
@@ -2539,13 +2556,8 @@ void step_kernel(SumArgs ra, TokArgs ta) {
 
   // (3) The fetched groups' summaries come out first: 16 a tile, subtracted
   // with the stream's own logits (the same code and operands).  Then one
-  // pipeline over the L1 tiles and the fetched tokens.  The summary bias
-  // shifts every summary logit and the reference alike: the stream took the
-  // weights without it, so it joins m now and the subtracted logits carry it.
+  // pipeline over the L1 tiles and the fetched tokens.
   __builtin_amdgcn_s_setprio(1);
-  st.m += ra.bias;
-  st.mL = st.m * kLog2e;
-  st.mth = st.m + kLazy;
   const int ntc = (stream && beta > 0) ? (beta + 15) / 16 : 0;
   const int nft = (N == 16) ? beta : (beta + 1) / 2;
   const int total = n1t + nft;

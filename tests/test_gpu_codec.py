@@ -43,7 +43,7 @@ def test_encode_parity(d, bits, dtype, n):
     signs = _rand_signs(rng, n_rot, d)
     x = _inputs(n, d, dtype, seed=n + d + bits)
     c32, t32 = ocb.codebook_f32(d, bits)
-    codes, norms = hsq.encode(x.to(DEV), bits, signs_to_dev(signs), torch.from_numpy(t32).to(DEV),
+    codes, norms = hsq.encode(x.to(DEV), bits, signs_to_dev(signs), torch.from_numpy(np.array(t32)).to(DEV),
                               vecs_per_rot=vpr, n_rot=n_rot)
     torch.cuda.synchronize()
     gc, gn = codes.cpu().numpy(), norms.cpu().numpy()
@@ -66,7 +66,7 @@ def test_encode_group_mean_and_row_index(d, bits, gn):
     idx = rng.choice(rows, size=n_vec * gn, replace=False).astype(np.int64)
     signs = _rand_signs(rng, 1, d)
     c32, t32 = ocb.codebook_f32(d, bits)
-    codes, norms = hsq.encode(x.to(DEV), bits, signs_to_dev(signs), torch.from_numpy(t32).to(DEV),
+    codes, norms = hsq.encode(x.to(DEV), bits, signs_to_dev(signs), torch.from_numpy(np.array(t32)).to(DEV),
                               row_idx=torch.from_numpy(idx).to(DEV), group_n=gn)
     torch.cuda.synchronize()
     mean = codec.to_f64(x)[idx].reshape(n_vec, gn, d).mean(axis=1)
@@ -91,7 +91,7 @@ def test_decode_parity(d, bits, out):
     od = np.concatenate([codec.decode(codes[:500], norms[:500], signs[0], c32),
                          codec.decode(codes[500:], norms[500:], signs[1], c32)])
     g = hsq.decode(torch.from_numpy(packed).to(DEV), torch.from_numpy(norms).to(DEV), bits, d,
-                   signs_to_dev(signs), torch.from_numpy(c32).to(DEV), vecs_per_rot=500, n_rot=2,
+                   signs_to_dev(signs), torch.from_numpy(np.array(c32)).to(DEV), vecs_per_rot=500, n_rot=2,
                    out_dtype=torch.float32 if out == "f32" else torch.bfloat16)
     g = g.float().cpu().numpy().astype(np.float64)
     if out == "f32":
@@ -159,9 +159,9 @@ def test_codec_workload_all_heads(bits):
     total_bad = total = 0
     for name, x, sg in (("K", k, ks), ("V", v, vs)):
         codes, norms = hsq.encode(x.view(n, c.d), bits, signs_to_dev(sg),
-                                  torch.from_numpy(t32).to(DEV), vecs_per_rot=c.tokens,
+                                  torch.from_numpy(np.array(t32)).to(DEV), vecs_per_rot=c.tokens,
                                   n_rot=c.heads)
-        dec = hsq.decode(codes, norms, bits, c.d, signs_to_dev(sg), torch.from_numpy(c32).to(DEV),
+        dec = hsq.decode(codes, norms, bits, c.d, signs_to_dev(sg), torch.from_numpy(np.array(c32)).to(DEV),
                          vecs_per_rot=c.tokens, n_rot=c.heads, out_dtype=torch.bfloat16)
         torch.cuda.synchronize()
         gc = codes.view(c.heads, c.tokens, -1).cpu().numpy()

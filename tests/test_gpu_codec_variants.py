@@ -41,7 +41,7 @@ def test_encode_variant_parity(bits, rot, d, dtype, n):
     x = _inputs(n, d, dtype, seed=n + d + bits + 2 * rot)
     _, t32 = ocb.codebook_f32(d, bits)
     codes, norms = hsq.encode(x.to(DEV), bits, signs_to_dev(signs) if rot else None,
-                              torch.from_numpy(t32).to(DEV))
+                              torch.from_numpy(np.array(t32)).to(DEV))
     torch.cuda.synchronize()
     assert codes.shape == (n, bits * d // 8)
     oc, on, oy = codec.encode(x, signs[0] if rot else None, t32)
@@ -64,7 +64,7 @@ def test_decode_variant_parity(bits, rot, d, out):
     od = codec.decode(codes, norms, signs[0] if rot else None, c32)
     g = hsq.decode(torch.from_numpy(codec.pack(codes, bits)).to(DEV),
                    torch.from_numpy(norms).to(DEV), bits, d,
-                   signs_to_dev(signs) if rot else None, torch.from_numpy(c32).to(DEV),
+                   signs_to_dev(signs) if rot else None, torch.from_numpy(np.array(c32)).to(DEV),
                    out_dtype=torch.float32 if out == "f32" else torch.bfloat16)
     g = g.float().cpu().numpy().astype(np.float64)
     if out == "f32":
@@ -88,8 +88,8 @@ def test_plain_round_trip_on_codec_workload_shape(bits):
     z[:, :4] *= 20.0
     x = z.to(torch.bfloat16)
     c32, t32 = ocb.codebook_f32(d, bits)
-    codes, norms = hsq.encode(x.to(DEV), bits, None, torch.from_numpy(t32).to(DEV))
-    xh = hsq.decode(codes, norms, bits, d, None, torch.from_numpy(c32).to(DEV))
+    codes, norms = hsq.encode(x.to(DEV), bits, None, torch.from_numpy(np.array(t32)).to(DEV))
+    xh = hsq.decode(codes, norms, bits, d, None, torch.from_numpy(np.array(c32)).to(DEV))
     torch.cuda.synchronize()
     oc, on, oy = codec.encode(x, None, t32)
     compare_codes(codes.cpu().numpy(), oc, oy, t32, bits, d, "plain round trip")
@@ -112,9 +112,9 @@ def test_rotation_index_for_many_divisors(vpr, n_rot):
     signs = rng.integers(0, 1 << 32, size=(n_rot, d // 32), dtype=np.uint64).astype(np.uint32)
     x = _inputs(n, d, "f32", seed=vpr + n_rot)
     c32, t32 = ocb.codebook_f32(d, bits)
-    codes, norms = hsq.encode(x.to(DEV), bits, signs_to_dev(signs), torch.from_numpy(t32).to(DEV),
+    codes, norms = hsq.encode(x.to(DEV), bits, signs_to_dev(signs), torch.from_numpy(np.array(t32)).to(DEV),
                               vecs_per_rot=vpr, n_rot=n_rot)
-    xh = hsq.decode(codes, norms, bits, d, signs_to_dev(signs), torch.from_numpy(c32).to(DEV),
+    xh = hsq.decode(codes, norms, bits, d, signs_to_dev(signs), torch.from_numpy(np.array(c32)).to(DEV),
                     vecs_per_rot=vpr, n_rot=n_rot)
     torch.cuda.synchronize()
     rot = (np.arange(n) // vpr) % n_rot

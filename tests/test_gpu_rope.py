@@ -110,7 +110,7 @@ def test_one_vector_and_empty():
           rope.decode_rope(codes, norms, signs[0], c32, pos, BASE), torch.float32)
     e = hsq.decode_rope(torch.zeros((0, 64), dtype=torch.uint8, device=DEV),
                         torch.zeros(0, device=DEV), 4, 128, signs_to_dev(signs),
-                        torch.from_numpy(c32).to(DEV), torch.zeros(0, dtype=torch.int32,
+                        torch.from_numpy(np.array(c32)).to(DEV), torch.zeros(0, dtype=torch.int32,
                                                                     device=DEV), BASE)
     assert e.shape == (0, 128)
 
