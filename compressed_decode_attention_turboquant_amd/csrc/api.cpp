@@ -375,7 +375,7 @@ extern "C" int hsq_decode_step(const float* q, int B, int Hq, int Hkv, int d, co
   t.l2k = l2k; t.l2k_n = l2k_n; t.l2v = l2v; t.l2v_n = l2v_n; t.l3 = l3; t.l3_staged = 0;
   t.k_signs = k_signs; t.v_signs = v_signs; t.cb4 = cb4; t.cb3 = cb3; t.scale = scale;
   t.summary_bias = summary_bias; t.agg = agg; t.out = out;
-  if (use_split(s))  // few units or many groups: each unit over many work-groups
+  if (use_split(s))  // beyond the one-launch step: each unit over many work-groups
     return check_hip(launch_split_step(s, t, w, static_cast<char*>(workspace),
                                        b > 0 ? topk_idx : nullptr, as_stream(stream)),
                      "hsq_decode_step (split)");

@@ -89,7 +89,7 @@ struct StepTensors {
 struct Workspace {
   size_t idx_off;      // int32 [B*Hkv][beta]   selection
   size_t part_off;     // fp32  [B*Hkv][G][d+2] summary-attention partial (m, l, O)
-  // split step only (use_split): per-head logits, router keys, largest key
+  // split step only (split_shape): per-head logits, router keys, largest key
   // norm per score chunk, selection bitmap, partials of the attend chunks
   size_t lgt_off, keys_off, rn_off, bits_off, parts_off;
   size_t total;
@@ -99,12 +99,15 @@ Workspace plan_workspace(const StepShape& s);
 int step_limits_ok(const StepShape& s);
 // shapes whose router logits fit in LDS (one-launch step, two-launch route)
 int route_lds_ok(const StepShape& s);
-// shapes hsq_decode_step runs as the split step: few units, or router
-// logits beyond LDS
+// shapes the split kernels serve (and whose workspace holds their buffers):
+// few units, or router logits beyond LDS
+int split_shape(const StepShape& s);
+// shapes hsq_decode_step runs as the split step: split shapes the one-launch
+// step cannot take (more than 2048 groups, or LDS)
 int use_split(const StepShape& s);
 hipError_t launch_split_step(const StepShape& s, const StepTensors& t, const Workspace& w,
                              char* ws, int32_t* idx_out, hipStream_t st);
-// The split step in two calls (use_split shapes): first = scores, selection
+// The split step in two calls (split_shape shapes): first = scores, selection
 // (idx_out optional) and the summary-value chunks, from t's router inputs;
 // else the token chunks (L1 and the fetched records; staged ones by slot)
 // and the merge, from t's attend inputs.  Same shape and workspace in both.

@@ -3029,9 +3029,11 @@ size_t step_smem(const StepShape& s) {
 
 int route_lds_ok(const StepShape& s) { return s.G * ((s.n_groups + 15) & ~15) <= kMaxLogits; }
 
-int use_split(const StepShape& s) {
+int split_shape(const StepShape& s) {
   return s.n_groups > 0 && (s.B * s.Hkv < kSplitUnits || !route_lds_ok(s));
 }
+
+int use_split(const StepShape& s) { return split_shape(s) && !step_fused_ok(s); }
 
 Workspace plan_workspace(const StepShape& s) {
   Workspace w{};
@@ -3039,7 +3041,7 @@ Workspace plan_workspace(const StepShape& s) {
   size_t off = 0;
   w.idx_off = off;  off = align256(off + (size_t)units * std::max(s.beta, 1) * 4);
   w.part_off = off; off = align256(off + (size_t)units * s.G * (s.d + 2) * 4);
-  if (use_split(s)) {
+  if (split_shape(s)) {
     const SplitPlan p = split_plan(units, s.n_l1, s.n_groups, s.beta, s.group_n);
     w.lgt_off = off;   off = align256(off + (size_t)units * s.G * p.ngp * 4);
     w.keys_off = off;  off = align256(off + (size_t)units * p.ngp * 4);
@@ -3179,7 +3181,7 @@ hipError_t split_halves_dn(const SplitArgs& a, int units, bool first, hipStream_
 
 hipError_t launch_split_step(const StepShape& s, const StepTensors& t, const Workspace& w,
                              char* ws, int32_t* idx_out, hipStream_t st) {
-  if (!step_limits_ok(s) || !use_split(s)) return hipErrorInvalidValue;
+  if (!step_limits_ok(s) || !split_shape(s)) return hipErrorInvalidValue;
   SplitArgs a = split_args(s, t, w, ws);
   a.idx_out = s.beta > 0 ? idx_out : nullptr;
   const int units = s.B * s.Hkv;
@@ -3191,7 +3193,7 @@ hipError_t launch_split_step(const StepShape& s, const StepTensors& t, const Wor
 
 hipError_t launch_split_half(const StepShape& s, const StepTensors& t, const Workspace& w,
                              char* ws, bool first, int32_t* idx_out, hipStream_t st) {
-  if (!step_limits_ok(s) || !use_split(s)) return hipErrorInvalidValue;
+  if (!step_limits_ok(s) || !split_shape(s)) return hipErrorInvalidValue;
   SplitArgs a = split_args(s, t, w, ws);
   a.idx_out = s.beta > 0 ? idx_out : nullptr;
   const int units = s.B * s.Hkv;
@@ -3210,7 +3212,7 @@ hipError_t launch_route(const StepShape& s, const StepTensors& t, const Workspac
   if (!route_lds_ok(s)) {
     // more router logits than LDS holds: the split route (scores to the
     // workspace, then the selection) serves the router-only call
-    if (mode != ROUTE_TOPK || !use_split(s)) return hipErrorInvalidValue;
+    if (mode != ROUTE_TOPK || !split_shape(s)) return hipErrorInvalidValue;
     SplitArgs a = split_args(s, t, w, ws);
     a.r.scores_out = scores_out;
     a.idx_out = s.beta > 0 ? idx_out : nullptr;

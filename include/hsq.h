@@ -268,19 +268,19 @@ int hsq_decode_attn(const float* q, int B, int Hq, int Hkv, int d, const uint8_t
  * hsq_decode_step -- the whole decode step of one layer: route, top-beta and
  * attention [HSQ "Decode process" steps 1-3]: hsq_route_topk followed by
  * hsq_decode_attn with l3_staged == 0 (the same selection; the output to
- * fp32 rounding of the order in which the partials merge).  With 128 or
- * more units (b, kvh), n_groups <= 2048 and G * n_groups <= 12288 it runs as
- * one launch, one work-group per unit: one stream over the summaries (router
+ * fp32 rounding of the order in which the partials merge).  With
+ * 1 <= n_groups <= 2048 it runs as one launch, one work-group per unit (b,
+ * kvh), for any number of units: one stream over the summaries (router
  * scores and the summary attention together), the selection on chip, then
  * the fetched summaries taken out again and the tokens attended.  With more
- * than 2048 groups (and G * n_groups <= 12288) it runs as the two launches of
- * hsq_route_topk and hsq_decode_attn.  With fewer units, or
- * G * n_groups > 12288, it runs as the split step: four
- * launches that spread each unit over many work-groups (router logits and
- * keys, the selection, summary-value and token chunks as partials, a
- * log-sum-exp merge), with the hand-overs in the workspace; a unit's result
- * depends only on its own inputs, not on the batch.  With n_groups == 0 it
- * runs as two launches.
+ * than 2048 groups it runs as the split step when there are fewer than 128
+ * units or G * n_groups > 12288: four launches that spread each unit over
+ * many work-groups (router logits and keys, the selection, summary-value and
+ * token chunks as partials, a log-sum-exp merge), with the hand-overs in the
+ * workspace; a unit's result depends only on its own inputs, not on the
+ * batch.  Otherwise (more than 2048 groups, 128 or more units,
+ * G * n_groups <= 12288), and with n_groups == 0, it runs as the two
+ * launches of hsq_route_topk and hsq_decode_attn.
  *   topk_idx    optional out int32 [B][Hkv][min(beta, n_groups)] (NULL = not
  *               returned)
  *   other arguments as in hsq_route_topk / hsq_decode_attn

@@ -116,7 +116,7 @@ def test_build_tiers_parity(wl, T, B):
     gp = torch.from_numpy(np.stack([p[1].reshape(-1) for p in plans])).to(DEV)
     c4, c3 = ocb.codebook_f32(w.d, 4), ocb.codebook_f32(w.d, 3)
     t = hsq.build_tiers(k, v, l1, gp, w.group_n, signs_to_dev(ks), signs_to_dev(vs),
-                        torch.from_numpy(c4[1]).to(DEV), torch.from_numpy(c3[1]).to(DEV))
+                        torch.from_numpy(np.array(c4[1])).to(DEV), torch.from_numpy(np.array(c3[1])).to(DEV))
     torch.cuda.synchronize()
     kc, vc = k.cpu(), v.cpu()
     host = {name: getattr(t, name).cpu().numpy() for name in

@@ -287,8 +287,9 @@ def oracle_tiers(sc):
     return t
 
 
-# Fewer than 128 (sequence, kv-head) units run the split step (four
-# launches); 128 or more the one-launch step.  Both kinds are here.
+# Up to 2048 groups the step runs as one launch for any number of units;
+# the split step (four launches) takes more groups with few units, and is
+# covered by the tests further down.
 SMALL = [
     ("tiny", W.TINY),
     ("q8-2k", W.QWEN3_8B_8K.smaller(T=2048, batch=2, n_marked=41)),
@@ -613,6 +614,25 @@ def test_long_context_beyond_on_chip_logits():
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2)
     check_route(sc, idx, scores, [(0, 0), (1, 7)], w.beta)
+
+
+@pytest.mark.parametrize("case", ["q8_b1_n16", "q14_b2_n8"])
+def test_split_step_few_units_many_groups(case):
+    # fewer than 128 units with more than 2048 groups (and G * n_groups within
+    # the on-chip logits): hsq_decode_step runs the split step; every unit
+    # against the oracle, max and mean routers
+    if case == "q8_b1_n16":
+        w = W.QWEN3_8B_8K.smaller(T=36864, batch=1, n_marked=600)
+        agg, bias = "max", 0.0
+    else:
+        w = W.QWEN3_14B_16K.smaller(T=17408, batch=2, n_marked=170)
+        agg, bias = "mean", 0.8
+    print(f"split step {case}: T={w.T} B={w.batch} G={w.G} N={w.group_n}", flush=True)
+    sc = Scenario(w)
+    ng = sc.tiers.ng
+    assert ng > 2048 and w.batch * w.hkv < 128 and w.G * ((ng + 15) // 16 * 16) <= 12288
+    worst, n_codes, n_diff = check_full(sc, w.beta, agg=agg, bias=bias)
+    print(f"  worst rel L2 {worst:.3e}, {n_codes} code / {n_diff} set differences", flush=True)
 
 
 def test_two_launch_step_beyond_one_launch_groups():
