@@ -538,14 +538,15 @@ __device__ __forceinline__ void pv3(const uint32_t (&va)[4], uint32_t sh, half8 
 // Combine the waves' states; result per head written to dst[h][D+2] as
 // [m, l, O[0..D)] (dst may be LDS or global).  scratch: kWaves*kMaxG*(D+2) floats.
 template <int D, int NW = kWaves>
-__device__ void combine_waves(const Softmax<D>& st, int G, float* scratch, float* dst, int tid) {
+__device__ void combine_waves(const Softmax<D>& st, int G, float* scratch, float* dst, int tid,
+                              int gs = kMaxG) {
   const int lane = tid & 63, wave = tid >> 6, c = lane & 15, gq = lane >> 4;
   float l = st.l;
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
   constexpr int T = D / 32;
   const int h = col_head(c), e = col_elem(c);
-  float* w = scratch + (wave * kMaxG + h) * (D + 2);
+  float* w = scratch + (wave * gs + h) * (D + 2);
   if (h < G) {
     if (gq == 0 && e == 0) {
       w[0] = st.m;
@@ -561,12 +562,12 @@ __device__ void combine_waves(const Softmax<D>& st, int G, float* scratch, float
     const int hh = k / (D + 2), e = k % (D + 2);
     float M = kNegInf;
 #pragma unroll
-    for (int v = 0; v < NW; ++v) M = fmaxf(M, scratch[(v * kMaxG + hh) * (D + 2)]);
+    for (int v = 0; v < NW; ++v) M = fmaxf(M, scratch[(v * gs + hh) * (D + 2)]);
     float acc = 0.f;
     if (e > 0) {
 #pragma unroll
       for (int v = 0; v < NW; ++v) {
-        const float* s = scratch + (v * kMaxG + hh) * (D + 2);
+        const float* s = scratch + (v * gs + hh) * (D + 2);
         const float wgt = (s[0] == kNegInf) ? 0.f : __expf(s[0] - M);
         acc += wgt * s[e];
       }
@@ -2075,7 +2076,12 @@ constexpr int kCandCap = 256;  // threshold-bucket groups ranked in parallel
 // with 200 registers each streamed slower (fewer waves to hide latencies).
 template <int NW> struct FusedCfg;
 template <> struct FusedCfg<8> { static constexpr int SD = 3, TD = 3, WPE = 4; };
+// 16 waves, one work-group per CU: layers of at most 256 units
+template <> struct FusedCfg<16> { static constexpr int SD = 3, TD = 3, WPE = 4; };
 constexpr int kFusedWaves = 8;
+constexpr int kFusedWavesFew = 16;
+constexpr int kFewUnits = 256;
+constexpr int kFewGroups = 1024;
 static_assert((8 + 1) * kMaxG * (128 + 2) * 4 + kMaxG * 128 * 4 <= kTabBytes,
               "the epilogue's scratch must fit in the table region");
 
@@ -2418,8 +2424,9 @@ void step_kernel(SumArgs ra, TokArgs ta) {
 
   // (0) global loads first: the set-up inputs and this wave's first summary
   // tiles, whose latency the set-up below overlaps
-  static_assert(NT == 512, "the table build assigns 16-byte chunks to 512 threads");
-  const TabIn tin = load_tab_in(ta.cb4, ra.cb3, tid);
+  // the tables are built by the first 512 threads (8 waves)
+  TabIn tin{};
+  if (tid < 512) tin = load_tab_in(ta.cb4, ra.cb3, tid);
   QueryIn qin;
   load_query<D>(ra.q + (size_t)unit * ra.G * D, ra.k_signs + kvh * (D / 32), ra.G, tid, qin);
   const uint32_t vsb =
@@ -2437,7 +2444,7 @@ void step_kernel(SumArgs ra, TokArgs ta) {
   if (tid < kFusedMaxGroups / 32) bits[tid] = 0u;
   if (tid == 0) s_nc = 0;
   if (tid < kMaxG * LPV) s_vsb[tid] = vsb;
-  build_tables(tab, tin, tid);
+  if (tid < 512) build_tables(tab, tin, tid);
   rotate_query<D>(qin, ra.scale * rsqrtf((float)D), qf, tid);
   lds_barrier();
 
@@ -2612,9 +2619,12 @@ void step_kernel(SumArgs ra, TokArgs ta) {
   // (4) combine, normalise, inverse V rotation, output
   __builtin_amdgcn_s_setprio(0);
   float* scratch = reinterpret_cast<float*>(tab);
-  float* mine = scratch + NW * kMaxG * (D + 2);
-  combine_waves<D, NW>(st, ra.G, scratch, mine, tid);
-  float* o = mine + kMaxG * (D + 2);
+  // head stride of the scratch: kMaxG, or G with 16 waves (so that 17
+  // partials and the output fit in the 64 KB region; the launch checks it)
+  const int gs = NW > 8 ? ra.G : kMaxG;
+  float* mine = scratch + NW * gs * (D + 2);
+  combine_waves<D, NW>(st, ra.G, scratch, mine, tid, gs);
+  float* o = mine + gs * (D + 2);
   for (int k = tid; k < ra.G * D; k += NT) {
     const int h = k / D, e = k % D;
     const float l = mine[h * (D + 2) + 1];
@@ -3016,13 +3026,32 @@ size_t token_smem(int D, const StepShape& s) {
   return (size_t)kMaxG * (D + 4) * 4 + (size_t)kMaxG * (D + 2) * 4 + (size_t)slots * 4;
 }
 
-size_t step_smem(const StepShape& s) {
-  constexpr int NW = kFusedWaves;
+// Waves per work-group of the one-launch step: 16 (one work-group per CU)
+// for layers of at most kFewUnits units with at least kFewGroups groups (a
+// stream long enough to split further) whose epilogue scratch (17 wave
+// partials at head stride G, this unit's partial and the output) fits the
+// 64 KB table region, else 8 (two work-groups per CU).  Measured: 64 units
+// of 2002 groups 34.4 -> 31.2 us with 16 waves; 8 units of 497 groups 18.1
+// -> 19.0 us (a short stream gains nothing from more waves).
+int fused_waves(const StepShape& s) {
+  const size_t scratch = (size_t)(17 * s.G * (s.d + 2) + s.G * (s.d + 2) + s.G * s.d) * 4;
+  return (s.B * s.Hkv <= kFewUnits && s.n_groups >= kFewGroups && scratch <= (size_t)kTabBytes)
+             ? kFusedWavesFew
+             : kFusedWaves;
+}
+
+template <int NW>
+size_t step_smem_nw(const StepShape& s) {
   if (s.d == 128)
     return (size_t)(s.group_n == 16 ? fused_layout<128, 16, NW>(s.beta).end
                                     : fused_layout<128, 8, NW>(s.beta).end);
   return (size_t)(s.group_n == 16 ? fused_layout<64, 16, NW>(s.beta).end
                                   : fused_layout<64, 8, NW>(s.beta).end);
+}
+
+size_t step_smem(const StepShape& s) {
+  return fused_waves(s) == kFusedWavesFew ? step_smem_nw<kFusedWavesFew>(s)
+                                          : step_smem_nw<kFusedWaves>(s);
 }
 
 }  // namespace
@@ -3251,13 +3280,21 @@ hipError_t step_dn(const StepShape& s, const StepTensors& t, int32_t* idx_out, h
   ra.want_partial = 1;
   ra.idx = idx_out;
   TokArgs ta = tok_args(s, t);
-  constexpr int NW = kFusedWaves;
-  if (t.agg == HSQ_AGG_MAX)
-    hipLaunchKernelGGL((step_kernel<D, N, false, NW>), dim3((unsigned)(s.B * s.Hkv)),
-                       dim3(NW * 64), step_smem(s), st, ra, ta);
-  else
-    hipLaunchKernelGGL((step_kernel<D, N, true, NW>), dim3((unsigned)(s.B * s.Hkv)),
-                       dim3(NW * 64), step_smem(s), st, ra, ta);
+  const dim3 grid((unsigned)(s.B * s.Hkv));
+  const size_t smem = step_smem(s);
+  if (fused_waves(s) == kFusedWavesFew) {
+    constexpr int NW = kFusedWavesFew;
+    if (t.agg == HSQ_AGG_MAX)
+      hipLaunchKernelGGL((step_kernel<D, N, false, NW>), grid, dim3(NW * 64), smem, st, ra, ta);
+    else
+      hipLaunchKernelGGL((step_kernel<D, N, true, NW>), grid, dim3(NW * 64), smem, st, ra, ta);
+  } else {
+    constexpr int NW = kFusedWaves;
+    if (t.agg == HSQ_AGG_MAX)
+      hipLaunchKernelGGL((step_kernel<D, N, false, NW>), grid, dim3(NW * 64), smem, st, ra, ta);
+    else
+      hipLaunchKernelGGL((step_kernel<D, N, true, NW>), grid, dim3(NW * 64), smem, st, ra, ta);
+  }
   return hipGetLastError();
 }
 

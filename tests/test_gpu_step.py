@@ -616,6 +616,19 @@ def test_long_context_beyond_on_chip_logits():
     check_route(sc, idx, scores, [(0, 0), (1, 7)], w.beta)
 
 
+@pytest.mark.parametrize("agg,bias", [("max", 0.0), ("mean", 0.5)])
+def test_one_launch_step_sixteen_waves(agg, bias):
+    # 16 units of about 1500 groups: at most 256 units and at least 1024
+    # groups, so the one-launch step runs 16-wave work-groups (one per CU);
+    # every unit against the oracle
+    w = W.QWEN3_14B_16K.smaller(T=12288, batch=2, n_marked=120)
+    print(f"one-launch step, 16 waves: T={w.T} B={w.batch} {agg} bias {bias}", flush=True)
+    sc = Scenario(w)
+    assert 1024 <= sc.tiers.ng <= 2048 and w.batch * w.hkv <= 256
+    worst, n_codes, n_diff = check_full(sc, w.beta, agg=agg, bias=bias)
+    print(f"  worst rel L2 {worst:.3e}, {n_codes} code / {n_diff} set differences", flush=True)
+
+
 @pytest.mark.parametrize("case", ["q8_b1_n16", "q14_b2_n8"])
 def test_split_step_few_units_many_groups(case):
     # fewer than 128 units with more than 2048 groups (and G * n_groups within
