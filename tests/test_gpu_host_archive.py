@@ -166,6 +166,84 @@ def test_ordered_gather_goes_ahead_when_its_turn_never_comes():
     assert int(turn.item()) == B * Hkv * 9
 
 
+def test_ordered_pipeline_graph_replays():
+    # the pinned-host step as the bench runs it: two micro-batches on two
+    # streams, route -> ordered gather -> attend per micro-batch and layer
+    # pass, the turn counter zeroed by a fill kernel inside the graph.  Every
+    # replay (with eager work between them) equals the eager run bit for
+    # bit, and the staged outputs equal the two launches on the archive in
+    # device memory.
+    w = W.QWEN3_8B_32K.smaller(layers=1, T=8192, batch=4, n_marked=160)
+    print(f"[ordered pipeline graph] {w.name} T={w.T} B={w.batch}", flush=True)
+    sc = Scenario(w)
+    t = sc.tiers
+    rec, beta = t.rec_bytes, min(w.beta, t.ng)
+    arch = hsq.HostArchive(t.l3.numel())
+    arch.host.copy_(t.l3.reshape(-1).cpu())
+    per_seq = w.hkv * t.ng * rec
+    names = ("l1k", "l1k_n", "l1v", "l1v_n", "l2k", "l2k_n", "l2v", "l2v_n")
+    mb = []
+    for b0, n in ((0, 2), (2, 2)):
+        tv = hsq.Tiers(n, w.hkv, w.d, t.n1, t.ng, w.group_n,
+                       *[getattr(t, f)[b0:b0 + n] for f in names], t.l3)
+        ws = hsq.make_workspace(n, w.hq, w.hkv, w.d, t.n1, t.ng, beta, w.group_n, DEV)
+        stg = torch.empty((n, w.hkv, beta, rec), dtype=torch.uint8, device=DEV)
+        outs = [torch.empty((n, w.hq, w.d), dtype=torch.float32, device=DEV) for _ in range(2)]
+        mb.append((b0, n, tv, ws, stg, outs))
+    turn = torch.zeros(1, dtype=torch.int32, device=DEV)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+
+    def one_step():
+        turn.zero_()
+        streams[1].wait_stream(streams[0])
+        after = 0
+        for rep in range(2):  # two passes over the layer, as two layers
+            for h, (b0, n, tv, ws, stg, outs) in enumerate(mb):
+                with torch.cuda.stream(streams[h]):
+                    q = sc.q[b0:b0 + n]
+                    hsq.step_route(q, tv, w.beta, sc.dks, sc.cb3, ws)
+                    idx = ws.buf[ws.ptr - ws.buf.data_ptr():][:4 * n * w.hkv * beta]
+                    hsq.gather_l3_ordered(arch.dev_ptr + b0 * per_seq, rec, n, w.hkv, t.ng,
+                                          idx.view(torch.int32).reshape(n, w.hkv, beta), stg,
+                                          turn, after)
+                    after += n * w.hkv * beta
+                    hsq.step_attend(q, tv, w.beta, sc.dks, sc.dvs, sc.cb4, ws, outs[rep],
+                                    l3=stg.data_ptr(), l3_staged=True)
+        streams[0].wait_stream(streams[1])
+
+    with torch.cuda.stream(streams[0]):
+        one_step()
+    torch.cuda.synchronize()
+    eager = [o.clone() for (_, _, _, _, _, outs) in mb for o in outs]
+    assert int(turn.item()) == 2 * w.batch * w.hkv * beta
+    ref = torch.empty((w.batch, w.hq, w.d), dtype=torch.float32, device=DEV)
+    wsd = hsq.make_workspace(w.batch, w.hq, w.hkv, w.d, t.n1, t.ng, beta, w.group_n, DEV)
+    hsq.step_route(sc.q, t, w.beta, sc.dks, sc.cb3, wsd)
+    hsq.step_attend(sc.q, t, w.beta, sc.dks, sc.dvs, sc.cb4, wsd, ref)
+    torch.cuda.synchronize()
+    for (b0, n, _, _, _, outs) in mb:
+        for o in outs:
+            assert torch.equal(o, ref[b0:b0 + n])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(streams[0]):
+        with torch.cuda.graph(g, stream=streams[0]):
+            one_step()
+    for r in range(3):
+        for (_, _, _, _, stg, outs) in mb:
+            stg.zero_()
+            for o in outs:
+                o.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device=DEV).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [o for (_, _, _, _, _, outs) in mb for o in outs]
+        for k, (a, e) in enumerate(zip(got, eager)):
+            assert torch.equal(a, e), f"replay {r}, output {k}"
+        assert int(turn.item()) == 2 * w.batch * w.hkv * beta
+        del junk
+
+
 def test_selection_is_left_at_the_start_of_the_workspace():
     w = W.QWEN3_8B_32K.smaller(T=4096, batch=2, n_marked=80)
     print(f"[workspace selection] {w.name} T={w.T} B={w.batch}", flush=True)

@@ -632,6 +632,50 @@ def test_long_context_beyond_on_chip_logits():
     check_route(sc, idx, scores, [(0, 0), (1, 7)], w.beta)
 
 
+@pytest.mark.parametrize("case", ["split", "sixteen_waves"])
+def test_graph_replays_match_eager(case):
+    # the split step (four launches, hand-overs through the workspace) and
+    # the 16-wave one-launch step captured in a graph: three replays with
+    # eager work between them equal the eager call bit for bit
+    if case == "split":
+        w = W.QWEN3_8B_8K.smaller(T=4 + 64 + 2100 * 16, batch=1, n_marked=0)
+    else:
+        w = W.QWEN3_14B_16K.smaller(T=12288, batch=2, n_marked=120)
+    print(f"graph replays: {case}", flush=True)
+    sc = Scenario(w)
+    t = sc.tiers
+    beta = min(w.beta, t.ng)
+    ws = hsq.make_workspace(w.batch, w.hq, w.hkv, w.d, t.n1, t.ng, beta, w.group_n, DEV)
+    out = torch.empty((w.batch, w.hq, w.d), dtype=torch.float32, device=DEV)
+    idx = torch.empty((w.batch, w.hkv, beta), dtype=torch.int32, device=DEV)
+
+    def step():
+        hsq.decode_step(sc.q, t, w.beta, sc.dks, sc.dvs, sc.cb4, sc.cb3, ws=ws, out=out, idx=idx)
+
+    step()
+    torch.cuda.synchronize()
+    out0, idx0 = out.clone(), idx.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        step()
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            step()
+    for r in range(3):
+        out.fill_(float("nan"))
+        idx.fill_(-1)
+        ws.buf.fill_(0x5A)  # the workspace's contents must not matter
+        junk = torch.randn(1 << 20, device=DEV).sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, idx0), f"replay {r}: selection differs"
+        assert torch.equal(out, out0), f"replay {r}: output differs"
+        del junk
+
+
 @pytest.mark.parametrize("agg,bias", [("max", 0.0), ("mean", 0.5)])
 def test_one_launch_step_sixteen_waves(agg, bias):
     # 16 units of about 1500 groups: at most 256 units and at least 1024
