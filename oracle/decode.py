@@ -26,7 +26,7 @@ Readings taken:
 """
 import numpy as np
 
-from . import codec, tiers
+from . import codec, rope, tiers
 
 
 def dequant_unit(unit, d, group_n, k_signs, v_signs, cb4, cb3):
@@ -89,17 +89,25 @@ def softmax_attention(q, keys, values, scale, bias=None):
 
 
 def hsq_attention_unit(q_heads, deq, l3_records, sel, group_n, d, k_signs, v_signs,
-                       cb4, scale, summary_bias=0.0):
+                       cb4, scale, summary_bias=0.0, group_pos=None, rope_base=None):
     """HSQ attention for the G query heads of one unit, given the fetched set sel.
 
     Entries: L1 tokens, summaries of unfetched groups, tokens of fetched groups.
-    Returns [G, d].
+    Pre-RoPE archive (group_pos given, [ng, N] token positions of each group):
+    the archive holds keys before the rotary position embedding, so each
+    fetched key is dequantised and then rotated to its token's position
+    (rope.rope with rope_base) before its logit is formed ("rotated to their
+    semantic positions", read as re-applying RoPE); L1 and L2 hold the
+    embedded keys as usual.  Returns [G, d].
     """
     ng = deq["l2k"].shape[0]
     sel = np.asarray(sel, dtype=np.int64)
     fetched = np.zeros(ng, dtype=bool)
     fetched[sel] = True
     kf, vf = dequant_l3_groups(l3_records, sel, group_n, d, k_signs, v_signs, cb4)
+    if group_pos is not None:
+        pos = np.asarray(group_pos, dtype=np.int64)[sel].reshape(-1)
+        kf = rope.rope(kf, pos, rope_base)
     keys = np.concatenate([deq["l1k"], deq["l2k"][~fetched], kf], axis=0)
     vals = np.concatenate([deq["l1v"], deq["l2v"][~fetched], vf], axis=0)
     bias = np.concatenate([

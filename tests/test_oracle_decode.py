@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from oracle import codebook as cb
-from oracle import codec, decode, tiers
+from oracle import codec, decode, rope, tiers
 
 
 def make_unit(T=200, d=64, n_sink=4, n_recent=16, n_marked=10, gn=8, seed=0):
@@ -360,3 +360,88 @@ def test_brute_force_tiny_end_to_end(agg, bias):
         w = [math.exp(e[0] - m) for e in ents]
         o = [sum(wi * e[1][i] for wi, e in zip(w, ents)) / sum(w) for i in range(d)]
         np.testing.assert_allclose(out[h], o, rtol=1e-11, atol=1e-12)
+
+
+# ---- pre-RoPE archive: the fetched keys are rotated to their positions ----
+
+def _prerope_unit(T=240, d=64, gn=8, seed=21, base=1e4):
+    """A unit whose L1 and L2 come from embedded keys and whose L3 archive
+    holds the keys before the rotary embedding (k_pre); k_post = RoPE(k_pre)
+    at positions 0 .. T-1 (oracle.rope)."""
+    u = make_unit(T=T, d=d, gn=gn, seed=seed)
+    k_pre = u["k"]
+    k_post = rope.rope(k_pre, np.arange(T), base)
+    post = tiers.build_unit(k_post, u["v"], u["l1"], u["groups"], u["ks"], u["vs"], u["cb4"],
+                            u["cb3"])
+    pre = tiers.build_unit(k_pre, u["v"], u["l1"], u["groups"], u["ks"], u["vs"], u["cb4"],
+                           u["cb3"])
+    unit = dict(post)
+    unit["l3"] = pre["l3"]
+    return dict(u, unit=unit, k_pre=k_pre, k_post=k_post, base=base)
+
+
+def test_prerope_positions_zero_is_the_plain_step():
+    # RoPE at position 0 is the identity: with every group at position 0 the
+    # pre-RoPE attention is the plain one on the same archive
+    u = _prerope_unit()
+    d, gn = u["d"], u["gn"]
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((2, d))
+    deq = decode.dequant_unit(u["unit"], d, gn, u["ks"], u["vs"], u["cb4"], u["cb3"])
+    sel = np.array([0, 3, 7, 11])
+    zero = np.zeros_like(u["groups"])
+    a = decode.hsq_attention_unit(q, deq, u["unit"]["l3"], sel, gn, d, u["ks"], u["vs"], u["cb4"],
+                                  1 / math.sqrt(d), group_pos=zero, rope_base=u["base"])
+    b = decode.hsq_attention_unit(q, deq, u["unit"]["l3"], sel, gn, d, u["ks"], u["vs"], u["cb4"],
+                                  1 / math.sqrt(d))
+    np.testing.assert_array_equal(a, b)
+
+
+def test_prerope_all_fetched_equals_dense_attention():
+    # beta = ng: the L1 tokens (embedded keys, each encoded at 4 bits) and every
+    # grouped token (its pre-embedding key encoded at 4 bits, decoded, then
+    # rotated to its position with the textbook pair rotation written out
+    # here) in one dense softmax
+    u = _prerope_unit()
+    d, gn, base = u["d"], u["gn"], u["base"]
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((3, d)) * 2
+    scale = 1 / math.sqrt(d)
+    ng = u["groups"].shape[0]
+    deq = decode.dequant_unit(u["unit"], d, gn, u["ks"], u["vs"], u["cb4"], u["cb3"])
+    got = decode.hsq_attention_unit(q, deq, u["unit"]["l3"], np.arange(ng), gn, d, u["ks"],
+                                    u["vs"], u["cb4"], scale, group_pos=u["groups"],
+                                    rope_base=base)
+
+    def enc_dec(x, signs):
+        c, n, _ = codec.encode(x, signs, u["cb4"][1])
+        return codec.decode(c, n, signs, u["cb4"][0])
+
+    gpos = u["groups"].reshape(-1)
+    kg = enc_dec(u["k_pre"][gpos], u["ks"])
+    half = d // 2
+    out = np.empty_like(kg)
+    for r, p in enumerate(gpos):
+        for i in range(half):
+            a = p * base ** (-2.0 * i / d)
+            out[r, i] = kg[r, i] * math.cos(a) - kg[r, i + half] * math.sin(a)
+            out[r, i + half] = kg[r, i + half] * math.cos(a) + kg[r, i] * math.sin(a)
+    keys = np.concatenate([enc_dec(u["k_post"][u["l1"]], u["ks"]), out])
+    vals = np.concatenate([enc_dec(u["v"][u["l1"]], u["vs"]), enc_dec(u["v"][gpos], u["vs"])])
+    want = np.stack([decode.softmax_attention(qh, keys, vals, scale) for qh in q])
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_prerope_rotation_matters():
+    # the embedding is not a no-op: at real positions the fetched keys, and so
+    # the output, differ from the plain step on the same archive
+    u = _prerope_unit()
+    d, gn = u["d"], u["gn"]
+    q = np.random.default_rng(5).standard_normal((1, d)) * 3
+    deq = decode.dequant_unit(u["unit"], d, gn, u["ks"], u["vs"], u["cb4"], u["cb3"])
+    sel = np.arange(u["groups"].shape[0])
+    a = decode.hsq_attention_unit(q, deq, u["unit"]["l3"], sel, gn, d, u["ks"], u["vs"], u["cb4"],
+                                  1 / math.sqrt(d), group_pos=u["groups"], rope_base=u["base"])
+    b = decode.hsq_attention_unit(q, deq, u["unit"]["l3"], sel, gn, d, u["ks"], u["vs"], u["cb4"],
+                                  1 / math.sqrt(d))
+    assert np.linalg.norm(a - b) > 1e-3 * np.linalg.norm(b)
