@@ -390,6 +390,88 @@ extern "C" int hsq_decode_step(const float* q, int B, int Hq, int Hkv, int d, co
                          beta, k_signs, v_signs, cb4, scale, workspace, ws_bytes, out, stream);
 }
 
+namespace {
+
+// fp16 fetched-key rows of the pre-RoPE step, after the step's own workspace
+size_t prerope_rows_off(const Workspace& w) { return (w.total + 255) / 256 * 256; }
+size_t prerope_rows_bytes(const StepShape& s) {
+  return (size_t)s.B * s.Hkv * s.beta * s.group_n * s.d * 2;
+}
+
+}  // namespace
+
+extern "C" size_t hsq_prerope_workspace_bytes(int B, int Hq, int Hkv, int d, int n_l1,
+                                              int n_groups, int beta, int group_n) {
+  if (check_step_shape("hsq_prerope_workspace_bytes", B, Hq, Hkv, d, n_l1, n_groups, group_n,
+                       beta))
+    return 0;
+  StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, beta < n_groups ? beta : n_groups};
+  return prerope_rows_off(plan_workspace(s)) + prerope_rows_bytes(s);
+}
+
+extern "C" int hsq_decode_step_prerope(const float* q, int B, int Hq, int Hkv, int d,
+                                       const uint8_t* l1k, const float* l1k_n, const uint8_t* l1v,
+                                       const float* l1v_n, int n_l1, const uint8_t* l2k,
+                                       const float* l2k_n, const uint8_t* l2v, const float* l2v_n,
+                                       int n_groups, const uint8_t* l3, int group_n, int beta,
+                                       int agg, const uint32_t* k_signs, const uint32_t* v_signs,
+                                       const float* cb4, const float* cb3, float scale,
+                                       float summary_bias, const int32_t* group_pos,
+                                       double rope_base, int32_t* topk_idx, void* workspace,
+                                       size_t ws_bytes, float* out, void* stream) {
+  const char* fn = "hsq_decode_step_prerope";
+  int rc = check_step_shape(fn, B, Hq, Hkv, d, n_l1, n_groups, group_n, beta);
+  if (rc) return rc;
+  if ((rc = attn_args(fn, q, l1k, l1k_n, l1v, l1v_n, n_l1, l2k, l2k_n, l2v, l2v_n, n_groups, l3,
+                      k_signs, v_signs, cb4, cb3, out)))
+    return rc;
+  if (agg != HSQ_AGG_MAX && agg != HSQ_AGG_MEAN) return fail(HSQ_ERR_ARG, std::string(fn) + ": bad agg");
+  if (n_groups > 0 && !group_pos) return fail(HSQ_ERR_ARG, std::string(fn) + ": null group_pos");
+  if (!(rope_base > 0.0) || !std::isfinite(rope_base))
+    return fail(HSQ_ERR_ARG, std::string(fn) + ": rope_base must be finite and > 0");
+  const int b = beta < n_groups ? beta : n_groups;
+  StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, b};
+  Workspace w;
+  if ((rc = step_common(fn, s, workspace, ws_bytes, w))) return rc;
+  if (s.n_groups > 0 && !route_lds_ok(s))
+    return fail(HSQ_ERR_UNSUPPORTED,
+                std::string(fn) + ": G * n_groups exceeds 12288 (router logits beyond LDS)");
+  const size_t kd_off = prerope_rows_off(w);
+  if (ws_bytes < kd_off + prerope_rows_bytes(s))
+    return fail(HSQ_ERR_WORKSPACE,
+                std::string(fn) + ": workspace smaller than hsq_prerope_workspace_bytes()");
+  StepTensors t{};
+  t.q = q; t.l1k = l1k; t.l1k_n = l1k_n; t.l1v = l1v; t.l1v_n = l1v_n;
+  t.l2k = l2k; t.l2k_n = l2k_n; t.l2v = l2v; t.l2v_n = l2v_n; t.l3 = l3; t.l3_staged = 0;
+  t.k_signs = k_signs; t.v_signs = v_signs; t.cb4 = cb4; t.cb3 = cb3; t.scale = scale;
+  t.summary_bias = summary_bias; t.agg = agg; t.out = out;
+  char* ws = static_cast<char*>(workspace);
+  const hipStream_t st = as_stream(stream);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + w.idx_off);
+  uint16_t* rows = reinterpret_cast<uint16_t*>(ws + kd_off);
+  if (s.n_groups > 0) {
+    if ((rc = check_hip(launch_route(s, t, w, ws, ROUTE_TOPK | ROUTE_PARTIALS, nullptr, nullptr,
+                                     idx, st),
+                        "hsq_decode_step_prerope route")))
+      return rc;
+    RopeKeysJob j{};
+    j.l3 = l3; j.unit_recs = n_groups; j.idx = idx; j.group_pos = group_pos;
+    j.pos_per_seq = (int64_t)n_groups * group_n; j.units = B * Hkv; j.Hkv = Hkv; j.d = d;
+    j.n_groups = n_groups; j.group_n = group_n; j.beta = b; j.k_signs = k_signs; j.cb4 = cb4;
+    j.rope_base = rope_base; j.out = rows;
+    if ((rc = check_hip(launch_rope_keys(j, st), "hsq_decode_step_prerope fetched keys")))
+      return rc;
+  }
+  if ((rc = check_hip(launch_attn_prerope(s, t, w, ws, idx, b > 0 ? rows : nullptr, st),
+                      "hsq_decode_step_prerope attention")))
+    return rc;
+  if (topk_idx && b > 0)
+    return check_hip(hipMemcpyAsync(topk_idx, idx, sizeof(int32_t) * (size_t)B * Hkv * b,
+                                    hipMemcpyDeviceToDevice, st),
+                     "hsq_decode_step_prerope topk copy");
+  return HSQ_OK;
+}
+
 extern "C" int hsq_decode_step_static(const float* q, int B, int Hq, int Hkv, int d,
                                       const uint8_t* l1k, const float* l1k_n, const uint8_t* l1v,
                                       const float* l1v_n, int n_l1, const uint8_t* l2k,

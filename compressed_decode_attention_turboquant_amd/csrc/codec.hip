@@ -99,6 +99,64 @@ struct DecTab {
 
 constexpr int kDecVPT = 4;  // vectors per thread in the decoder, loads issued together
 
+// RoPE turns per position of each coordinate pair f < d/2, base^(-2f/d) /
+// (2 pi), as a 64-bit binary fraction (low and high words), so that the
+// fraction of a turn at any int32 position is one wrapping integer product.
+// Written by threads 0 .. d/2 - 1 of the work-group.
+template <int D>
+__device__ __forceinline__ void rope_turns(double base, uint32_t* lo, uint32_t* hi) {
+  if (threadIdx.x < D / 2) {
+    const double t = pow(base, -2.0 * threadIdx.x / D) * (0.5 / 3.141592653589793);
+    const uint64_t fx = (uint64_t)((t - __builtin_floor(t)) * 0x1p64);
+    lo[threadIdx.x] = (uint32_t)fx;
+    hi[threadIdx.x] = (uint32_t)(fx >> 32);
+  }
+}
+// Lane sub holds coordinates 8 sub .. 8 sub + 7; coordinate f < d/2 pairs
+// with f + d/2, in the same slot of lane sub ^ LPV/2.  Both lanes of a pair
+// need the same angles: the lower one takes slots 0..3, the upper one slots
+// 4..7, and they swap the results.  This lane's four turns:
+template <int LPV>
+__device__ __forceinline__ void rope_lane_turns(const uint32_t* lo, const uint32_t* hi, int sub,
+                                                uint32_t (&tlo)[4], uint32_t (&thi)[4]) {
+  constexpr int HALF = LPV / 2;
+  const bool upper = sub >= HALF;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int f = 8 * (sub % HALF) + (upper ? 4 : 0) + k;
+    tlo[k] = lo[f];
+    thi[k] = hi[f];
+  }
+}
+// Rotate the lane's 8 coordinates (with the partner lane's) to position p.
+template <int LPV>
+__device__ __forceinline__ void rope8(float (&v)[8], int32_t p, const uint32_t (&tlo)[4],
+                                      const uint32_t (&thi)[4], int sub) {
+  constexpr int HALF = LPV / 2;
+  const bool upper = sub >= HALF;
+  const uint32_t pu = (uint32_t)p;
+  float sn[8], cs[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    // top word of p * turns mod 2^64: the fraction of a turn in units of
+    // 2^-32 (a negative p is pu - 2^32, which takes tlo off that word)
+    const uint32_t top = __umulhi(pu, tlo[k]) + pu * thi[k] - (p < 0 ? tlo[k] : 0u);
+    const float rev = (float)top * 0x1p-32f;
+    // the hardware sine and cosine take their argument in turns
+    const float s1 = __builtin_amdgcn_sinf(rev), c1 = __builtin_amdgcn_cosf(rev);
+    const float s2 = xor_lane<HALF>(s1), c2 = xor_lane<HALF>(c1);
+    sn[k] = upper ? s2 : s1;
+    cs[k] = upper ? c2 : c1;
+    sn[k + 4] = upper ? s1 : s2;
+    cs[k + 4] = upper ? c1 : c2;
+  }
+#pragma unroll
+  for (int a = 0; a < 8; ++a) {
+    const float partner = xor_lane<HALF>(v[a]);
+    v[a] = v[a] * cs[a] + (upper ? partner : -partner) * sn[a];
+  }
+}
+
 template <int D, int BITS, int OUT, bool ROT, bool ROPE>
 __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j, Div32 per_rot, Div32 n_rot) {
   constexpr int LPV = D / 8;
@@ -108,9 +166,7 @@ __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j, Div32 per_rot,
   constexpr int CW = BITS == 3 ? 2 : 1;  // code dwords loaded per lane and vector
   constexpr int NE = DecTab<BITS>::kEntries, PER = DecTab<BITS>::kPer;
   __shared__ __align__(16) float tab[NE * PER];
-  // RoPE: turns per position of each coordinate pair, base^(-2f/d) / (2 pi),
-  // as a 64-bit binary fraction (low and high words), so that the fraction of
-  // a turn at any int32 position is one wrapping integer product
+  // RoPE: turns per position of each coordinate pair (rope_turns)
   __shared__ uint32_t turns_lo[ROPE ? D / 2 : 1], turns_hi[ROPE ? D / 2 : 1];
   if (threadIdx.x < NE) {
     constexpr uint32_t M = (1u << BITS) - 1;
@@ -118,31 +174,11 @@ __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j, Div32 per_rot,
     for (int k = 0; k < PER; ++k)
       tab[threadIdx.x * PER + k] = j.centroids[(threadIdx.x >> (BITS * k)) & M];
   }
-  if constexpr (ROPE) {
-    if (threadIdx.x < D / 2) {
-      const double t = pow(j.rope_base, -2.0 * threadIdx.x / D) * (0.5 / 3.141592653589793);
-      const uint64_t fx = (uint64_t)((t - __builtin_floor(t)) * 0x1p64);
-      turns_lo[threadIdx.x] = (uint32_t)fx;
-      turns_hi[threadIdx.x] = (uint32_t)(fx >> 32);
-    }
-  }
+  if constexpr (ROPE) rope_turns<D>(j.rope_base, turns_lo, turns_hi);
   __syncthreads();
   const int sub = threadIdx.x % LPV;
-  // RoPE: lane sub holds coordinates 8 sub .. 8 sub + 7; coordinate f < d/2
-  // pairs with f + d/2, in the same slot of lane sub ^ LPV/2.  Both lanes of
-  // a pair need the same angles: the lower one takes slots 0..3, the upper
-  // one slots 4..7, and they swap the results.
-  constexpr int HALF = LPV / 2;
-  const bool upper = sub >= HALF;
   uint32_t tlo[4] = {}, thi[4] = {};
-  if constexpr (ROPE) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int f = 8 * (sub % HALF) + (upper ? 4 : 0) + k;
-      tlo[k] = turns_lo[f];
-      thi[k] = turns_hi[f];
-    }
-  }
+  if constexpr (ROPE) rope_lane_turns<LPV>(turns_lo, turns_hi, sub, tlo, thi);
   // This lane's code bits of a row: BITS = 4 one dword; 2: half a dword;
   // 3: 24 bits from bit 24 sub (two dwords, the second inside the row).
   const int bit = BITS * 8 * sub;
@@ -217,30 +253,7 @@ __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j, Div32 per_rot,
 #pragma unroll
       for (int a = 0; a < 8; ++a)
         v[a] = __uint_as_float(__float_as_uint(v[a] * s) ^ (((sbyte >> a) & 1u) << 31));
-      if constexpr (ROPE) {
-        const int32_t p = ps[u];
-        const uint32_t pu = (uint32_t)p;
-        float sn[8], cs[8];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          // top word of p * turns mod 2^64: the fraction of a turn in units
-          // of 2^-32 (a negative p is pu - 2^32, which takes tlo off that word)
-          const uint32_t top = __umulhi(pu, tlo[k]) + pu * thi[k] - (p < 0 ? tlo[k] : 0u);
-          const float rev = (float)top * 0x1p-32f;
-          // the hardware sine and cosine take their argument in turns
-          const float s1 = __builtin_amdgcn_sinf(rev), c1 = __builtin_amdgcn_cosf(rev);
-          const float s2 = xor_lane<HALF>(s1), c2 = xor_lane<HALF>(c1);
-          sn[k] = upper ? s2 : s1;
-          cs[k] = upper ? c2 : c1;
-          sn[k + 4] = upper ? s1 : s2;
-          cs[k + 4] = upper ? c1 : c2;
-        }
-#pragma unroll
-        for (int a = 0; a < 8; ++a) {
-          const float partner = xor_lane<HALF>(v[a]);
-          v[a] = v[a] * cs[a] + (upper ? partner : -partner) * sn[a];
-        }
-      }
+      if constexpr (ROPE) rope8<LPV>(v, ps[u], tlo, thi, sub);
       if (valid[u]) {
         const uint32_t i = idx[u];
         if constexpr (OUT == HSQ_F32) {
@@ -282,6 +295,74 @@ hipError_t encode_dt(const EncodeJob& j, hipStream_t s) {
       hipLaunchKernelGGL((encode_kernel<D, BITS, HSQ_BF16, ROT, false>), g, b, 0, s, j, q);
   }
   return hipGetLastError();
+}
+
+// Fetched keys of a pre-RoPE archive (RopeKeysJob): one vector per D/8
+// lanes, blocks of VPB vectors strided over a grid of at most the resident
+// work-groups (the turns table costs a set-up per work-group).  A slot whose
+// selection names no group gets a zero row.  Indices past the end are
+// clamped to the last vector (recomputed, not stored), so every lane runs
+// the cross-lane steps.
+template <int D>
+__global__ __launch_bounds__(kWG) void rope_keys_kernel(RopeKeysJob j) {
+  constexpr int LPV = D / 8, VPB = kWG / LPV, CB = D / 2;
+  __shared__ __align__(16) float tab[256 * 2];  // code byte -> its two centroids
+  __shared__ uint32_t turns_lo[D / 2], turns_hi[D / 2];
+  if (threadIdx.x < 256) {
+    tab[2 * threadIdx.x] = j.cb4[threadIdx.x & 15];
+    tab[2 * threadIdx.x + 1] = j.cb4[threadIdx.x >> 4];
+  }
+  rope_turns<D>(j.rope_base, turns_lo, turns_hi);
+  __syncthreads();
+  const int sub = threadIdx.x % LPV;
+  uint32_t tlo[4], thi[4];
+  rope_lane_turns<LPV>(turns_lo, turns_hi, sub, tlo, thi);
+  const int N = j.group_n;
+  const uint64_t rec = (uint64_t)N * (D + 8);
+  const uint64_t n_vec = (uint64_t)j.units * j.beta * N;
+  const uint64_t nblk = (n_vec + VPB - 1) / VPB;
+  const float isd = 1.f / __builtin_sqrtf((float)D);
+  for (uint64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    const uint64_t i64 = blk * VPB + threadIdx.x / LPV;
+    const bool valid = i64 < n_vec;
+    const uint64_t i = valid ? i64 : n_vec - 1;
+    const uint32_t t = (uint32_t)(i % N);
+    const uint64_t us = i / N;            // u * beta + s
+    const uint64_t u = us / j.beta;
+    const int g0 = j.idx[us];
+    const bool ok = g0 >= 0 && g0 < j.n_groups;
+    const int g = ok ? g0 : 0;
+    const uint32_t codes = *reinterpret_cast<const uint32_t*>(
+        j.l3 + (u * j.unit_recs + (uint64_t)g) * rec + (uint64_t)t * CB + 4 * sub);
+    const int32_t p = j.group_pos[(u / j.Hkv) * j.pos_per_seq + (uint64_t)g * N + t];
+    const uint32_t sbyte = sign_byte(j.k_signs + (u % j.Hkv) * (D / 32), sub);
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float2 c = reinterpret_cast<const float2*>(tab)[(codes >> (8 * k)) & 0xffu];
+      v[2 * k] = c.x;
+      v[2 * k + 1] = c.y;
+    }
+    // back to the model's domain: x = D H c / sqrt(d)
+    fwht8xlanes<LPV>(v, sub);
+#pragma unroll
+    for (int a = 0; a < 8; ++a) v[a] = flip(v[a] * isd, (sbyte >> a) & 1u);
+    rope8<LPV>(v, p, tlo, thi, sub);
+    // forward again: y = H D x / sqrt(d)
+#pragma unroll
+    for (int a = 0; a < 8; ++a) v[a] = flip(v[a], (sbyte >> a) & 1u);
+    fwht8xlanes<LPV>(v, sub);
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const _Float16 lo = ok ? (_Float16)(v[2 * k] * isd) : (_Float16)0.f;
+      const _Float16 hi = ok ? (_Float16)(v[2 * k + 1] * isd) : (_Float16)0.f;
+      w[k] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    if (valid)
+      *reinterpret_cast<uint4*>(j.out + i * D + 8 * sub) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
 }
 
 template <int D, int BITS, bool ROT, bool ROPE>
@@ -330,6 +411,18 @@ hipError_t launch_encode(const EncodeJob& j, hipStream_t s) {
   const bool rot = j.signs != nullptr;
   if (j.d == 128) return rot ? encode_bits<128, true>(j, s) : encode_bits<128, false>(j, s);
   return rot ? encode_bits<64, true>(j, s) : encode_bits<64, false>(j, s);
+}
+
+hipError_t launch_rope_keys(const RopeKeysJob& j, hipStream_t s) {
+  const int64_t n_vec = (int64_t)j.units * j.beta * j.group_n;
+  if (n_vec <= 0) return hipSuccess;
+  const int64_t vpb = kWG / (j.d / 8);
+  const int64_t grid = std::min<int64_t>((n_vec + vpb - 1) / vpb, 256 * 4);
+  if (j.d == 128)
+    hipLaunchKernelGGL(rope_keys_kernel<128>, dim3((unsigned)grid), dim3(kWG), 0, s, j);
+  else
+    hipLaunchKernelGGL(rope_keys_kernel<64>, dim3((unsigned)grid), dim3(kWG), 0, s, j);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeJob& j, hipStream_t s) {

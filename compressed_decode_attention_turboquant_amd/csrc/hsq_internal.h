@@ -63,6 +63,25 @@ struct DecodeJob {
 };
 hipError_t launch_decode(const DecodeJob& j, hipStream_t s);
 
+// Fetched keys of a pre-RoPE archive (codec.hip): for every selection slot s
+// of every unit u and token t of the group, the 4-bit key of the record in
+// the rotated domain (unit norm), taken back to the model's domain, rotated
+// to the token's position, rotated forward again: fp16 out[u][s][t][d], the
+// rows the attend kernel multiplies in place of the table lookups.
+struct RopeKeysJob {
+  const uint8_t* l3;        // archive records, N * (d + 8) bytes each
+  int64_t unit_recs;        // records between consecutive units (n_groups or a capacity)
+  const int32_t* idx;       // [units][beta] selected group per slot
+  const int32_t* group_pos; // [B][pos_per_seq] token positions, group-major
+  int64_t pos_per_seq;
+  int units, Hkv, d, n_groups, group_n, beta;
+  const uint32_t* k_signs;  // [Hkv][d/32]
+  const float* cb4;         // 16 centroids
+  double rope_base;
+  uint16_t* out;            // fp16 bits [units][beta][group_n][d]
+};
+hipError_t launch_rope_keys(const RopeKeysJob& j, hipStream_t s);
+
 // ---- decode step (route.hip / attn.hip) ------------------------------------
 struct StepShape {
   int B, Hq, Hkv, G, d;
@@ -122,6 +141,12 @@ hipError_t launch_route(const StepShape& s, const StepTensors& t, const Workspac
                         int32_t* idx_out, hipStream_t st);
 hipError_t launch_attn(const StepShape& s, const StepTensors& t, const Workspace& w, char* ws,
                        const int32_t* idx, hipStream_t st);
+// launch_attn over a pre-RoPE archive: the fetched tiles multiply the fp16
+// key rows kdense [units][beta][group_n][d] (launch_rope_keys) instead of
+// the records' key codes (kdense may be null when beta == 0)
+hipError_t launch_attn_prerope(const StepShape& s, const StepTensors& t, const Workspace& w,
+                               char* ws, const int32_t* idx, const uint16_t* kdense,
+                               hipStream_t st);
 // The whole step in one launch (route + attend per work-group); only for
 // shapes where step_fused_ok holds.  idx_out (optional): [units][beta].
 int step_fused_ok(const StepShape& s);

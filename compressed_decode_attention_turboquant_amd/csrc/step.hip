@@ -1694,6 +1694,10 @@ struct TokArgs {
   int n1s, ngs;            // rows / groups between consecutive units of L1 / L3
   const float* part;       // summary partial per unit, or null when there are none
   float* out;
+  // pre-RoPE archive: fp16 rows [units][beta][N][D] of the fetched keys in the
+  // rotated domain (RopeKeysJob), read in place of the key codes' table
+  // lookups by the fetched tiles (null otherwise)
+  const uint16_t* kdense;
 };
 
 struct TokTile {
@@ -1702,6 +1706,12 @@ struct TokTile {
   float vn;        // value norm of row 4gq + (lane & 3)
   uint32_t va[4];  // value bits of rows 4gq+j for lane rho = lane&15
 };
+// A tile that also carries the fetched keys' fp16 rows (pre-RoPE archive):
+// the lane's D/4 coordinates of token row lane&15, the MFMA operands as they
+// are (D=64 uses kd[0..1]).
+struct TokTileK : TokTile {
+  u32x4 kd[4];
+};
 
 // Per-unit buffers of the token tiles.  Tile t < n1t holds L1 rows 16t ..
 // 16t+15; tile n1t + f holds the fetched archive groups of slot f (N = 16) or
@@ -1709,6 +1719,7 @@ struct TokTile {
 // [K codes N*CB][K norms N*4][V codes N*CB][V norms N*4].
 struct TokBufs {
   rsrc_t l1k, l1kn, l1v, l1vn, l3;
+  rsrc_t kd;  // the unit's fetched-key rows (pre-RoPE archive), else empty
 };
 
 template <int D, int N>
@@ -1724,6 +1735,9 @@ __device__ __forceinline__ TokBufs tok_bufs(const TokArgs& a, int unit) {
   B.l1vn = make_rsrc(a.l1v_n + o1, (uint32_t)a.n1 * 4);
   B.l3 = make_rsrc(a.l3 + (size_t)unit * (a.l3_staged ? a.beta : a.ngs) * rec,
                    (uint32_t)(recs * rec));
+  const size_t kdu = (size_t)a.beta * N * D;  // fp16 values per unit
+  B.kd = make_rsrc(a.kdense ? a.kdense + (size_t)unit * kdu : nullptr,
+                   a.kdense ? (uint32_t)(kdu * 2) : 0u);
   return B;
 }
 
@@ -1735,9 +1749,9 @@ __device__ __forceinline__ TokBufs tok_bufs(const TokArgs& a, int unit) {
 // rows, norms) of its archive slot(s); an L1 tile ignores them.
 // FRESH: the lane's address parts are recomputed from lane_now() (for
 // kernels whose pipelines run at the register limit).
-template <int D, int N, bool FRESH = false>
+template <int D, int N, bool FRESH = false, typename TT = TokTile>
 __device__ __forceinline__ void load_tok_at(const TokBufs& B, int t, int n1t, int n1, uint32_t bk,
-                                            uint32_t br, int lane, TokTile& T) {
+                                            uint32_t br, int lane, TT& T, int s0 = 0) {
   constexpr int CB = D / 2;
   constexpr uint32_t KB = D / 8;  // key code bytes per lane
   if constexpr (FRESH) lane = lane_now();
@@ -1776,6 +1790,13 @@ __device__ __forceinline__ void load_tok_at(const TokBufs& B, int t, int n1t, in
     T.vn = __uint_as_float(ld32(B.l3, br + (uint32_t)(N * (2 * CB + 4) + 4 * (tr + (lane & 3)))));
 #pragma unroll
     for (int j = 0; j < 4; ++j) T.va[j] = ld32(B.l3, vo + j * CB);
+    if constexpr (std::is_same_v<TT, TokTileK>) {
+      // row slot * N + tk of the dense keys; a slot past beta reads zeros
+      const int slot = s0 + ((N == 16) ? 0 : (n >> 3));
+      const uint32_t ko = (uint32_t)((slot * N + tk) * (2 * D)) + (uint32_t)(gq * (D / 2));
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m) T.kd[m] = ld128(B.kd, ko + 16 * m);
+    }
   }
 }
 // First archive slot of tile t (wave-uniform; 0 for L1 tiles, whose loads
@@ -1786,16 +1807,17 @@ __device__ __forceinline__ int tile_slot(int t, int n1t) {
 }
 // Loads of tile t, the record offsets read from recoff (which covers every
 // slot a tile of the pipeline can name, see tok_slots).
-template <int D, int N, bool FRESH = false>
+template <int D, int N, bool FRESH = false, typename TT = TokTile>
 __device__ __forceinline__ void load_tok(const TokBufs& B, const int32_t* recoff, int t, int n1t,
-                                         int n1, int lane, TokTile& T) {
+                                         int n1, int lane, TT& T) {
   if constexpr (FRESH) lane = lane_now();
   const int n = lane & 15, gq = lane >> 4;
   const int xk = (N == 16) ? 0 : (n >> 3), xr = (N == 16) ? 0 : (gq >> 1);
-  const int32_t* rs = recoff + tile_slot<N>(t, n1t);
+  const int s0 = tile_slot<N>(t, n1t);
+  const int32_t* rs = recoff + s0;
   const uint32_t bk = (uint32_t)rs[xk];
   const uint32_t br = (uint32_t)rs[xr];
-  load_tok_at<D, N, FRESH>(B, t, n1t, n1, bk, br, lane, T);
+  load_tok_at<D, N, FRESH, TT>(B, t, n1t, n1, bk, br, lane, T, s0);
 }
 // Entries of the record-offset table: every slot of the fetched tiles and of
 // the tiles the pipeline loads past the last one (they read kFar).  A wave's
@@ -1827,18 +1849,28 @@ __device__ __forceinline__ void mask_rows(float (&lg)[4], int t, int n1t, int n1
 // SPLITQ: qh is the router operand (fp16 high parts of the query in columns
 // c < 8, low parts in c + 8), so one row rotation completes fp32-accurate
 // query products in every column.
-template <int D, bool SPLITQ = false, typename MaskF>
-__device__ __forceinline__ void consume_tok(const TokTile& T, bool masked, MaskF mask,
+template <int D, bool SPLITQ = false, typename MaskF, typename TT = TokTile>
+__device__ __forceinline__ void consume_tok(const TT& T, bool masked, MaskF mask,
                                             const half8 (&qh)[D / 32], const uint32_t* lut4,
-                                            int lane, uint32_t lane4, Softmax<D>& st) {
+                                            int lane, uint32_t lane4, Softmax<D>& st,
+                                            bool dense = false) {
   // two accumulators so that consecutive MFMAs do not wait on each other
   f32x4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  if constexpr (std::is_same_v<TT, TokTileK>) {
+    if (dense) {  // wave-uniform: a fetched tile of a pre-RoPE archive
 #pragma unroll
-  for (int m = 0; m < D / 32; ++m) {
-    const uint32_t w = T.kw[m];
-    const half8 av = as_h8(lds_at(lut4, lut4_addr<0>(w, lane4)), lds_at(lut4, lut4_addr<1>(w, lane4)),
-                           lds_at(lut4, lut4_addr<2>(w, lane4)), lds_at(lut4, lut4_addr<3>(w, lane4)));
-    acc2[m & 1] = mfma16(av, qh[m], acc2[m & 1]);
+      for (int m = 0; m < D / 32; ++m)
+        acc2[m & 1] = mfma16(__builtin_bit_cast(half8, T.kd[m]), qh[m], acc2[m & 1]);
+    }
+  }
+  if (!(std::is_same_v<TT, TokTileK> && dense)) {
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) {
+      const uint32_t w = T.kw[m];
+      const half8 av = as_h8(lds_at(lut4, lut4_addr<0>(w, lane4)), lds_at(lut4, lut4_addr<1>(w, lane4)),
+                             lds_at(lut4, lut4_addr<2>(w, lane4)), lds_at(lut4, lut4_addr<3>(w, lane4)));
+      acc2[m & 1] = mfma16(av, qh[m], acc2[m & 1]);
+    }
   }
   f32x4 acc = acc2[0] + acc2[1];
   if constexpr (SPLITQ) {
@@ -1884,9 +1916,9 @@ struct AttendLds {
 // this wave's softmax state of the summary partial, which the token tiles
 // continue (L.part is then not used); else the waves' states start empty
 // and the combined result is merged with L.part.
-template <int D, int N>
+template <int D, int N, typename TT = TokTile, int TD = kTokDepth>
 __device__ __forceinline__ void attend_unit(const TokArgs& a, const AttendLds& L,
-                                            TokTile (&tt)[kTokDepth], bool l1_issued,
+                                            TT (&tt)[TD], bool l1_issued,
                                             const int* bad_flag, const Softmax<D>* st_in,
                                             int unit, int tile0 = 0, int tstride = 1,
                                             float* part_out = nullptr) {
@@ -1911,9 +1943,9 @@ __device__ __forceinline__ void attend_unit(const TokArgs& a, const AttendLds& L
   };
   // this wave's first tiles not issued yet, loading while the table is built
 #pragma unroll
-  for (int j = 0; j < kTokDepth - 1; ++j)
+  for (int j = 0; j < TD - 1; ++j)
     if (!(l1_issued && wave + j * kWaves < n1t))  // wave-uniform
-      load_tok<D, N>(B, L.recoff, tile_of(j), n1t, a.n1, lane, tt[j]);
+      load_tok<D, N, false, TT>(B, L.recoff, tile_of(j), n1t, a.n1, lane, tt[j]);
   build_lut4(L.lut4, L.cb, tid);
   half8 qh[D / 32], ql[D / 32];
   query_operands<D>(L.qf, lane, qh, ql);
@@ -1931,16 +1963,20 @@ __device__ __forceinline__ void attend_unit(const TokArgs& a, const AttendLds& L
     const bool any_bad = bad_flag && __builtin_amdgcn_readfirstlane(*bad_flag) != 0;
     const int ragged = (a.n1 & 15) ? n1t - 1 : -1;
     const int half = (N == 8 && (a.beta & 1)) ? total - 1 : -1;
-    pipeline<kTokDepth>(
+    pipeline<TD>(
         iters, tt,
-        [&](int i, TokTile& T) { load_tok<D, N>(B, L.recoff, tile_of(i), n1t, a.n1, lane, T); },
-        [&](int i, const TokTile& T) {
+        [&](int i, TT& T) {
+          // the dense-key tiles run at the register limit: lane parts afresh
+          load_tok<D, N, std::is_same_v<TT, TokTileK>, TT>(B, L.recoff, tile_of(i), n1t, a.n1,
+                                                          lane, T);
+        },
+        [&](int i, const TT& T) {
           const int t = tile_of(i);
           const bool masked = t == ragged || t == half || (any_bad && t >= n1t);
           consume_tok<D>(
               T, masked,
               [&](float (&lg)[4]) { mask_rows<N>(lg, t, n1t, a.n1, a.beta, L.recoff, lane); },
-              qh, lut4, lane, lane4, st);
+              qh, lut4, lane, lane4, st, t >= n1t);
         });
   }
   lds_barrier();  // the table is no longer needed: reuse as scratch
@@ -1992,10 +2028,14 @@ __device__ __forceinline__ void attend_unit(const TokArgs& a, const AttendLds& L
   }
 }
 
-// at most 128 VGPRs so that two work-groups (the LDS limit) fit on a CU
-template <int D, int N>
+// at most 128 VGPRs so that two work-groups (the LDS limit) fit on a CU.
+// TT = TokTileK: the fetched tiles multiply dense fp16 key rows (a.kdense)
+// instead of looking their codes up; the pipeline is one tile shallower to
+// make room for them.
+template <int D, int N, typename TT = TokTile>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void token_kernel(TokArgs a) {
+  constexpr int TD = std::is_same_v<TT, TokTileK> ? kTokDepth - 1 : kTokDepth;
   extern __shared__ __align__(16) char smem[];
   __shared__ __align__(16) uint32_t s_lut4[256 * kNC4];
   __shared__ float s_cb[16];
@@ -2021,11 +2061,11 @@ void token_kernel(TokArgs a) {
   // global loads first: this wave's first L1 tiles (they need no record
   // offsets), the set-up inputs and the summary partial merged at the end
   const TokBufs B = tok_bufs<D, N>(a, unit);
-  TokTile tt[kTokDepth];
+  TT tt[TD];
 #pragma unroll
-  for (int j = 0; j < kTokDepth - 1; ++j)
+  for (int j = 0; j < TD - 1; ++j)
     if (wave + j * kWaves < n1t)  // wave-uniform
-      load_tok_at<D, N>(B, wave + j * kWaves, n1t, a.n1, kFar, kFar, tid & 63, tt[j]);
+      load_tok_at<D, N, false, TT>(B, wave + j * kWaves, n1t, a.n1, kFar, kFar, tid & 63, tt[j]);
   const float cbv = (tid < 16) ? a.cb4[tid] : 0.f;
   QueryIn qin;
   load_query<D>(a.q + (size_t)unit * a.G * D, a.k_signs + kvh * (D / 32), a.G, tid, qin);
@@ -2056,7 +2096,7 @@ void token_kernel(TokArgs a) {
   rotate_query<D>(qin, a.scale * rsqrtf((float)D), L.qf, tid);
   lds_barrier();
   if (bad) s_bad = 1;  // read after the next barrier
-  attend_unit<D, N>(a, L, tt, true, &s_bad, nullptr, unit);
+  attend_unit<D, N, TT, TD>(a, L, tt, true, &s_bad, nullptr, unit);
 }
 
 // ------------------------------------------------------- one-launch step ---
@@ -3280,17 +3320,18 @@ hipError_t launch_route(const StepShape& s, const StepTensors& t, const Workspac
                     : summary_d<64>(s, t, w, ws, mode, given, scores_out, idx_out, st);
 }
 
-template <int D>
+template <int D, typename TT = TokTile>
 hipError_t token_d(const StepShape& s, const StepTensors& t, const Workspace& w, char* ws,
-                   const int32_t* idx, hipStream_t st) {
+                   const int32_t* idx, const uint16_t* kdense, hipStream_t st) {
   TokArgs a = tok_args(s, t);
   a.idx = idx;
   a.part = s.n_groups > 0 ? reinterpret_cast<const float*>(ws + w.part_off) : nullptr;
+  a.kdense = kdense;
   if (s.group_n == 16)
-    hipLaunchKernelGGL((token_kernel<D, 16>), dim3((unsigned)(s.B * s.Hkv)), dim3(kThreads),
+    hipLaunchKernelGGL((token_kernel<D, 16, TT>), dim3((unsigned)(s.B * s.Hkv)), dim3(kThreads),
                        token_smem(D, s), st, a);
   else
-    hipLaunchKernelGGL((token_kernel<D, 8>), dim3((unsigned)(s.B * s.Hkv)), dim3(kThreads),
+    hipLaunchKernelGGL((token_kernel<D, 8, TT>), dim3((unsigned)(s.B * s.Hkv)), dim3(kThreads),
                        token_smem(D, s), st, a);
   return hipGetLastError();
 }
@@ -3298,7 +3339,18 @@ hipError_t token_d(const StepShape& s, const StepTensors& t, const Workspace& w,
 hipError_t launch_attn(const StepShape& s, const StepTensors& t, const Workspace& w, char* ws,
                        const int32_t* idx, hipStream_t st) {
   if (!step_limits_ok(s) || (s.n_groups > 0 && !route_lds_ok(s))) return hipErrorInvalidValue;
-  return s.d == 128 ? token_d<128>(s, t, w, ws, idx, st) : token_d<64>(s, t, w, ws, idx, st);
+  return s.d == 128 ? token_d<128>(s, t, w, ws, idx, nullptr, st)
+                    : token_d<64>(s, t, w, ws, idx, nullptr, st);
+}
+
+hipError_t launch_attn_prerope(const StepShape& s, const StepTensors& t, const Workspace& w,
+                               char* ws, const int32_t* idx, const uint16_t* kdense,
+                               hipStream_t st) {
+  if (!step_limits_ok(s) || (s.n_groups > 0 && !route_lds_ok(s)) || t.l3_staged ||
+      (s.beta > 0 && !kdense))
+    return hipErrorInvalidValue;
+  return s.d == 128 ? token_d<128, TokTileK>(s, t, w, ws, idx, kdense, st)
+                    : token_d<64, TokTileK>(s, t, w, ws, idx, kdense, st);
 }
 
 template <int D, int N>

@@ -294,6 +294,44 @@ int hsq_decode_step(const float* q, int B, int Hq, int Hkv, int d, const uint8_t
                     void* workspace, size_t ws_bytes, float* out, void* stream);
 
 /*
+ * hsq_prerope_workspace_bytes / hsq_decode_step_prerope -- the decode step
+ * over a pre-RoPE archive [HSQ "Decode process" step 2: the originals of the
+ * fetched groups are dequantised and rotated to their semantic positions
+ * before they are attended; RoPE as in Su et al., RoFormer (2021), pairing
+ * coordinate f < d/2 with f + d/2 as hsq_decode_rope does].  L1 and L2 hold
+ * keys with RoPE applied, as for hsq_decode_step; the L3 records hold the
+ * keys without it (values are never rotated).  The route, the selection, the
+ * summaries and L1 are as in hsq_decode_step (two launches); between them a
+ * third launch takes every fetched record's 4-bit key codes back to the
+ * model's domain, rotates each token to its position, rotates the result
+ * forward again into fp16 rows in the workspace, and the attention multiplies
+ * those rows where it would look the codes up (the norms, the values and
+ * everything else unchanged).
+ *   group_pos   int32 [B][n_groups*group_n] (device): position of token t of
+ *               group g of sequence b at [b][g*group_n + t], any value
+ *   rope_base   the rotary base (1e6 for the Qwen3 models), finite, > 0
+ *   workspace   hsq_prerope_workspace_bytes(...) bytes, 256-byte aligned:
+ *               hsq_workspace_bytes' plus B*Hkv*min(beta, n_groups)*group_n*d
+ *               fp16 rows
+ *   other arguments as in hsq_decode_step
+ * Errors: as hsq_decode_step, plus HSQ_ERR_ARG for a null group_pos (with
+ * n_groups > 0) or a bad rope_base, HSQ_ERR_UNSUPPORTED when
+ * G * n_groups > 12288 (router logits beyond the chip's LDS).
+ * hsq_prerope_workspace_bytes returns 0 for sizes hsq_workspace_bytes
+ * rejects.
+ */
+size_t hsq_prerope_workspace_bytes(int B, int Hq, int Hkv, int d, int n_l1, int n_groups,
+                                   int beta, int group_n);
+int hsq_decode_step_prerope(const float* q, int B, int Hq, int Hkv, int d, const uint8_t* l1k,
+                            const float* l1k_n, const uint8_t* l1v, const float* l1v_n, int n_l1,
+                            const uint8_t* l2k, const float* l2k_n, const uint8_t* l2v,
+                            const float* l2v_n, int n_groups, const uint8_t* l3, int group_n,
+                            int beta, int agg, const uint32_t* k_signs, const uint32_t* v_signs,
+                            const float* cb4, const float* cb3, float scale, float summary_bias,
+                            const int32_t* group_pos, double rope_base, int32_t* topk_idx,
+                            void* workspace, size_t ws_bytes, float* out, void* stream);
+
+/*
  * hsq_decode_step_static -- hsq_decode_step without a workspace argument,
  * for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc).  The

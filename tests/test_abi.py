@@ -104,6 +104,25 @@ def test_argument_errors_are_reported_without_launch():
     assert lib.hsq_gather_l3(p, 100, 1, 1, 4, p, 2, p, None) == -1
     assert lib.hsq_gather_l3(p, 1088, 1, 1, 4, p, 5, p, None) == -1
     assert lib.hsq_gather_l3(p, (1 << 20) + 16, 1, 1, 4, p, 2, p, None) == -2
+    # pre-RoPE step: workspace size (the plain one plus the fetched rows),
+    # null positions, bad rotary base, workspace of only the plain size
+    plain = lib.hsq_workspace_bytes(2, 32, 8, 128, 10, 10, 4, 16)
+    pre = lib.hsq_prerope_workspace_bytes(2, 32, 8, 128, 10, 10, 4, 16)
+    assert pre >= plain + 2 * 8 * 4 * 16 * 128 * 2
+    assert lib.hsq_prerope_workspace_bytes(1, 36, 4, 128, 10, 10, 2, 16) == 0
+
+    def pre_step(pos=p, base=1e6, ws_bytes=pre, ws=ctypes.c_void_p(256)):
+        f = ctypes.c_float(0.1)
+        return lib.hsq_decode_step_prerope(p, 2, 32, 8, 128, p, p, p, p, 10, p, p, p, p, 10, p,
+                                           16, 4, 0, p, p, p, p, f, f, pos, base, None, ws,
+                                           ws_bytes, p, None)
+
+    assert pre_step(pos=None) == -1
+    assert "group_pos" in lib.hsq_last_error().decode()
+    assert pre_step(base=0.0) == -1
+    assert pre_step(base=float("inf")) == -1
+    assert pre_step(ws_bytes=plain) == -4
+    assert pre_step(ws=None) == -4
     assert lib.hsq_gather_l3_ordered(p, 1088, 1, 1, 4, p, 2, p, None, 0, None) == -1
     assert "turn" in lib.hsq_last_error().decode()
     assert lib.hsq_gather_l3_ordered(p, 1088, 1, 1, 4, p, 2, p, ctypes.c_void_p(18), 0, None) == -1
