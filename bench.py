@@ -111,6 +111,7 @@ class Layer:
                  for b in range(w.batch)]
         l1 = torch.from_numpy(np.stack([p[0] for p in plans])).to(dev)
         gp = torch.from_numpy(np.stack([p[1].reshape(-1) for p in plans])).to(dev)
+        self.gp = gp  # token positions of the grouped tokens (RoPE positions)
         k, v = W.kv(w, layer, dev)
         self.tiers = hsq.build_tiers(k, v, l1, gp, w.group_n, self.dks, self.dvs, cb["thr4"],
                                      cb["thr3"], l3=l3)
@@ -217,6 +218,25 @@ def headline(args, torch, hsq, W):
         time_graph(torch, g, 2, stream)
         two[name] = float(np.median(time_reps(torch, g, 10, stream))) / L
         del g
+    # the same layers read as pre-RoPE archives (the fetched keys rotated to
+    # the grouped tokens' positions before attention): three launches
+    pre_ms = None
+    if not args.only_step:
+        pre_ws = hsq.Workspace(hsq.prerope_workspace_bytes(
+            w.batch, w.hq, w.hkv, w.d, layers[0].tiers.n1, layers[0].tiers.ng, layers[0].beta,
+            w.group_n), dev)
+
+        def pre(ly):
+            hsq.decode_step_prerope(ly.q, ly.tiers, w.beta, ly.dks, ly.dvs, cb["cb4"], cb["cb3"],
+                                    ly.gp, 1e6, ws=pre_ws, out=ly.out)
+
+        with torch.cuda.stream(stream):
+            pre(layers[0])
+            stream.synchronize()
+        g = capture(torch, stream, lambda: [pre(ly) for ly in layers])
+        time_graph(torch, g, 2, stream)
+        pre_ms = float(np.median(time_reps(torch, g, 10, stream))) / L
+        del g, pre_ws
     t = layers[0].tiers
     units = w.batch * w.hkv
     rb, ab = algorithmic_bytes(w, t.n1, t.ng, layers[0].beta)
@@ -231,6 +251,9 @@ def headline(args, torch, hsq, W):
         "kernels": {"step_kernel": {"us": ms_step * 1e3, "bytes": step_bytes, "gbs": achieved}},
         "two_launch": {k: {"us": two[k] * 1e3, "bytes": kb[k],
                            "gbs": kb[k] / (two[k] * 1e-3) / 1e9} for k in two},
+        "prerope_step": None if pre_ms is None else {
+            "us": pre_ms * 1e3, "vs_step": pre_ms / ms_step, "launches": 3,
+            "what": "same layers as pre-RoPE archives: route, fetched-key RoPE pass, attend"},
         "dominant": "step_kernel", "achieved": achieved, "n1": t.n1, "ng": t.ng,
         "step_bytes": step_bytes,
         "tier_bytes": t.nbytes(),
@@ -782,6 +805,7 @@ def main():
         "step_hbm_frac": res["step_gbs"] / HBM_PEAK_GBS,
         "kernels": k,
         "two_launch": res["two_launch"],
+        "prerope_step": res["prerope_step"],
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": res["achieved"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": res["achieved"] / HBM_PEAK_GBS,
                      "traffic": measured_traffic(dom)},

@@ -298,14 +298,15 @@ hipError_t encode_dt(const EncodeJob& j, hipStream_t s) {
 }
 
 // Fetched keys of a pre-RoPE archive (RopeKeysJob): one vector per D/8
-// lanes, blocks of VPB vectors strided over a grid of at most the resident
-// work-groups (the turns table costs a set-up per work-group).  A slot whose
-// selection names no group gets a zero row.  Indices past the end are
-// clamped to the last vector (recomputed, not stored), so every lane runs
-// the cross-lane steps.
+// lanes, kDecVPT vectors per lane group with their loads issued together
+// (each vector's address waits on its selection entry), in blocks strided
+// over a grid of at most the resident work-groups (the turns table costs a
+// set-up per work-group).  A slot whose selection names no group gets a zero
+// row.  Indices past the end are clamped to the last vector (recomputed, not
+// stored), so every lane runs the cross-lane steps.
 template <int D>
 __global__ __launch_bounds__(kWG) void rope_keys_kernel(RopeKeysJob j) {
-  constexpr int LPV = D / 8, VPB = kWG / LPV, CB = D / 2;
+  constexpr int LPV = D / 8, VPB = kWG / LPV, CB = D / 2, U = kDecVPT;
   __shared__ __align__(16) float tab[256 * 2];  // code byte -> its two centroids
   __shared__ uint32_t turns_lo[D / 2], turns_hi[D / 2];
   if (threadIdx.x < 256) {
@@ -317,51 +318,65 @@ __global__ __launch_bounds__(kWG) void rope_keys_kernel(RopeKeysJob j) {
   const int sub = threadIdx.x % LPV;
   uint32_t tlo[4], thi[4];
   rope_lane_turns<LPV>(turns_lo, turns_hi, sub, tlo, thi);
-  const int N = j.group_n;
+  const uint32_t N = (uint32_t)j.group_n, beta = (uint32_t)j.beta, Hkv = (uint32_t)j.Hkv;
   const uint64_t rec = (uint64_t)N * (D + 8);
-  const uint64_t n_vec = (uint64_t)j.units * j.beta * N;
-  const uint64_t nblk = (n_vec + VPB - 1) / VPB;
+  const uint32_t n_vec = (uint32_t)j.units * beta * N;  // < 2^31 (launch_rope_keys)
+  const uint32_t nblk = (n_vec + VPB * U - 1) / (VPB * U);
   const float isd = 1.f / __builtin_sqrtf((float)D);
-  for (uint64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
-    const uint64_t i64 = blk * VPB + threadIdx.x / LPV;
-    const bool valid = i64 < n_vec;
-    const uint64_t i = valid ? i64 : n_vec - 1;
-    const uint32_t t = (uint32_t)(i % N);
-    const uint64_t us = i / N;            // u * beta + s
-    const uint64_t u = us / j.beta;
-    const int g0 = j.idx[us];
-    const bool ok = g0 >= 0 && g0 < j.n_groups;
-    const int g = ok ? g0 : 0;
-    const uint32_t codes = *reinterpret_cast<const uint32_t*>(
-        j.l3 + (u * j.unit_recs + (uint64_t)g) * rec + (uint64_t)t * CB + 4 * sub);
-    const int32_t p = j.group_pos[(u / j.Hkv) * j.pos_per_seq + (uint64_t)g * N + t];
-    const uint32_t sbyte = sign_byte(j.k_signs + (u % j.Hkv) * (D / 32), sub);
-    float v[8];
+  for (uint32_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    uint32_t i[U];
+    bool valid[U], ok[U];
+    uint32_t codes[U], sbyte[U];
+    int32_t p[U];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float2 c = reinterpret_cast<const float2*>(tab)[(codes >> (8 * k)) & 0xffu];
-      v[2 * k] = c.x;
-      v[2 * k + 1] = c.y;
+    for (int k = 0; k < U; ++k) {
+      const uint32_t i0 = (blk * U + k) * VPB + threadIdx.x / LPV;
+      valid[k] = i0 < n_vec;
+      i[k] = valid[k] ? i0 : n_vec - 1;
     }
-    // back to the model's domain: x = D H c / sqrt(d)
-    fwht8xlanes<LPV>(v, sub);
 #pragma unroll
-    for (int a = 0; a < 8; ++a) v[a] = flip(v[a] * isd, (sbyte >> a) & 1u);
-    rope8<LPV>(v, p, tlo, thi, sub);
-    // forward again: y = H D x / sqrt(d)
-#pragma unroll
-    for (int a = 0; a < 8; ++a) v[a] = flip(v[a], (sbyte >> a) & 1u);
-    fwht8xlanes<LPV>(v, sub);
-    uint32_t w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const _Float16 lo = ok ? (_Float16)(v[2 * k] * isd) : (_Float16)0.f;
-      const _Float16 hi = ok ? (_Float16)(v[2 * k + 1] * isd) : (_Float16)0.f;
-      w[k] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-             ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    for (int k = 0; k < U; ++k) {
+      // 32-bit quotients (a 64-bit division is a long software sequence)
+      const uint32_t us = i[k] / N, t = i[k] - us * N;  // us = u * beta + s
+      const uint32_t u = us / beta, b = u / Hkv, h = u - b * Hkv;
+      const int g0 = j.idx[us];
+      ok[k] = g0 >= 0 && g0 < j.n_groups;
+      const uint32_t g = ok[k] ? (uint32_t)g0 : 0u;
+      codes[k] = *reinterpret_cast<const uint32_t*>(
+          j.l3 + ((uint64_t)u * j.unit_recs + g) * rec + t * CB + 4 * sub);
+      p[k] = j.group_pos[(uint64_t)b * j.pos_per_seq + g * N + t];
+      sbyte[k] = sign_byte(j.k_signs + h * (D / 32), sub);
     }
-    if (valid)
-      *reinterpret_cast<uint4*>(j.out + i * D + 8 * sub) = make_uint4(w[0], w[1], w[2], w[3]);
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      float v[8];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float2 e = reinterpret_cast<const float2*>(tab)[(codes[k] >> (8 * c)) & 0xffu];
+        v[2 * c] = e.x;
+        v[2 * c + 1] = e.y;
+      }
+      // back to the model's domain: x = D H c / sqrt(d)
+      fwht8xlanes<LPV>(v, sub);
+#pragma unroll
+      for (int a = 0; a < 8; ++a) v[a] = flip(v[a] * isd, (sbyte[k] >> a) & 1u);
+      rope8<LPV>(v, p[k], tlo, thi, sub);
+      // forward again: y = H D x / sqrt(d)
+#pragma unroll
+      for (int a = 0; a < 8; ++a) v[a] = flip(v[a], (sbyte[k] >> a) & 1u);
+      fwht8xlanes<LPV>(v, sub);
+      uint32_t w[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const _Float16 lo = ok[k] ? (_Float16)(v[2 * c] * isd) : (_Float16)0.f;
+        const _Float16 hi = ok[k] ? (_Float16)(v[2 * c + 1] * isd) : (_Float16)0.f;
+        w[c] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      }
+      if (valid[k])
+        *reinterpret_cast<uint4*>(j.out + (uint64_t)i[k] * D + 8 * sub) =
+            make_uint4(w[0], w[1], w[2], w[3]);
+    }
   }
 }
 
@@ -416,7 +431,8 @@ hipError_t launch_encode(const EncodeJob& j, hipStream_t s) {
 hipError_t launch_rope_keys(const RopeKeysJob& j, hipStream_t s) {
   const int64_t n_vec = (int64_t)j.units * j.beta * j.group_n;
   if (n_vec <= 0) return hipSuccess;
-  const int64_t vpb = kWG / (j.d / 8);
+  if (n_vec >= (int64_t(1) << 31)) return hipErrorInvalidValue;  // 32-bit vector index
+  const int64_t vpb = kWG / (j.d / 8) * kDecVPT;
   const int64_t grid = std::min<int64_t>((n_vec + vpb - 1) / vpb, 256 * 4);
   if (j.d == 128)
     hipLaunchKernelGGL(rope_keys_kernel<128>, dim3((unsigned)grid), dim3(kWG), 0, s, j);

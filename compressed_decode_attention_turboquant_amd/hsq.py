@@ -279,6 +279,10 @@ class Workspace:
         self.ptr = self.buf.data_ptr() + off
 
 
+def prerope_workspace_bytes(B, Hq, Hkv, d, n_l1, n_groups, beta, group_n):
+    return int(lib().hsq_prerope_workspace_bytes(B, Hq, Hkv, d, n_l1, n_groups, beta, group_n))
+
+
 def make_workspace(B, Hq, Hkv, d, n_l1, n_groups, beta, group_n, device):
     n = workspace_bytes(B, Hq, Hkv, d, n_l1, n_groups, beta, group_n)
     if n == 0:
@@ -362,8 +366,7 @@ def decode_step_prerope(q, tiers, beta, k_signs, v_signs, cb4, cb3, group_pos, r
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if ws is None:
-        n = int(lib().hsq_prerope_workspace_bytes(B, Hq, tiers.Hkv, d, tiers.n1, tiers.ng, b,
-                                                  tiers.group_n))
+        n = prerope_workspace_bytes(B, Hq, tiers.Hkv, d, tiers.n1, tiers.ng, b, tiers.group_n)
         if n == 0:
             raise HSQError(-1, "invalid sizes for hsq_prerope_workspace_bytes")
         ws = Workspace(n, q.device)
