@@ -26,7 +26,7 @@ Readings taken:
 """
 import numpy as np
 
-from . import codec, rope, tiers
+from . import codec, qjl as qjl_mod, rope, tiers
 
 
 def dequant_unit(unit, d, group_n, k_signs, v_signs, cb4, cb3):
@@ -89,7 +89,7 @@ def softmax_attention(q, keys, values, scale, bias=None):
 
 
 def hsq_attention_unit(q_heads, deq, l3_records, sel, group_n, d, k_signs, v_signs,
-                       cb4, scale, summary_bias=0.0, group_pos=None, rope_base=None):
+                       cb4, scale, summary_bias=0.0, group_pos=None, rope_base=None, qjl=None):
     """HSQ attention for the G query heads of one unit, given the fetched set sel.
 
     Entries: L1 tokens, summaries of unfetched groups, tokens of fetched groups.
@@ -98,7 +98,13 @@ def hsq_attention_unit(q_heads, deq, l3_records, sel, group_n, d, k_signs, v_sig
     fetched key is dequantised and then rotated to its token's position
     (rope.rope with rope_base) before its logit is formed ("rotated to their
     semantic positions", read as re-applying RoPE); L1 and L2 hold the
-    embedded keys as usual.  Returns [G, d].
+    embedded keys as usual.
+    TQ-QKV token keys (qjl given: dict of S [m, d] and the unit's sketches as
+    qjl.unit_sketches returns them): the logit of every L1 token and every
+    fetched token gains the QJL estimate of its key residual's share,
+    scale * qjl.correction (Ablation page, "Key contributions" 1: TQ-QKV adds
+    the 1-bit residual sketch on the key path); the summaries' logits are
+    unchanged.  Returns [G, d].
     """
     ng = deq["l2k"].shape[0]
     sel = np.asarray(sel, dtype=np.int64)
@@ -115,7 +121,18 @@ def hsq_attention_unit(q_heads, deq, l3_records, sel, group_n, d, k_signs, v_sig
         np.full(int((~fetched).sum()), float(summary_bias)),
         np.zeros(kf.shape[0]),
     ])
-    return np.stack([softmax_attention(qh, keys, vals, scale, bias) for qh in q_heads])
+    if qjl is None:
+        return np.stack([softmax_attention(qh, keys, vals, scale, bias) for qh in q_heads])
+    m = np.asarray(qjl["S"]).shape[0]
+    c1 = qjl_mod.correction(q_heads, qjl["l1_bits"], qjl["l1_gamma"], k_signs, qjl["S"])
+    cf = qjl_mod.correction(q_heads, np.asarray(qjl["l3_bits"])[sel].reshape(-1, m),
+                            np.asarray(qjl["l3_gamma"])[sel].reshape(-1), k_signs, qjl["S"])
+    n_sum = int((~fetched).sum())
+    out = []
+    for h, qh in enumerate(q_heads):
+        corr = np.concatenate([c1[h], np.zeros(n_sum), cf[h]])
+        out.append(softmax_attention(qh, keys, vals, scale, bias + scale * corr))
+    return np.stack(out)
 
 
 def decode_step_unit(q_heads, unit, group_n, d, k_signs, v_signs, cb4, cb3, beta,

@@ -69,14 +69,37 @@ def logits_tq(q, codes, norms, sign_words, centroids, scale):
     return scale * (np.asarray(q, dtype=np.float64) @ xh.T)
 
 
-def logits_qjl(q, codes, norms, bits, gamma, sign_words, centroids, S, scale):
-    """TQ-QKV logits: the TQ-KV logit plus the QJL estimate of the residual's
-    inner product.  q [G, d]; bits bool [n, m].  Returns [G, n]."""
+def correction(q, bits, gamma, sign_words, S):
+    """QJL estimate of the residual's share of q . x for query rows q [G, d]
+    and sketched keys (bits bool [n, m], gamma [n]):
+    sqrt(pi/2) / m * gamma * <S R q, 1 - 2 bits>, unscaled.  Returns [G, n]."""
     q = np.asarray(q, dtype=np.float64)
     S = np.asarray(S, dtype=np.float64)
     m, d = S.shape
     rq = q @ codec.rotation_matrix(sign_words, d).T        # R q, [G, d]
     sq = rq @ S.T                                          # S R q, [G, m]
     sgn = 1.0 - 2.0 * np.asarray(bits, dtype=np.float64)    # [n, m]
-    corr = np.sqrt(np.pi / 2) / m * (sq @ sgn.T) * np.asarray(gamma, dtype=np.float64)[None, :]
-    return logits_tq(q, codes, norms, sign_words, centroids, scale) + scale * corr
+    return np.sqrt(np.pi / 2) / m * (sq @ sgn.T) * np.asarray(gamma, dtype=np.float64)[None, :]
+
+
+def logits_qjl(q, codes, norms, bits, gamma, sign_words, centroids, S, scale):
+    """TQ-QKV logits: the TQ-KV logit plus the QJL estimate of the residual's
+    inner product.  q [G, d]; bits bool [n, m].  Returns [G, n]."""
+    return (logits_tq(q, codes, norms, sign_words, centroids, scale)
+            + scale * correction(q, bits, gamma, sign_words, S))
+
+
+def unit_sketches(k_raw, l1_pos, groups, sign_words, thresholds, centroids, S):
+    """Sketches of one unit's token keys, as the TQ-QKV decode step reads
+    them: the L1 keys (rows l1_pos) and every grouped token (groups [ng, N]),
+    each encoded on its own exactly as the 4-bit tiers encode it.
+    Returns dict: l1_bits bool [n1, m], l1_gamma fp32 [n1],
+    l3_bits bool [ng, N, m], l3_gamma fp32 [ng, N]."""
+    x = codec.to_f64(k_raw)
+    groups = np.asarray(groups, dtype=np.int64)
+    ng, gn = groups.shape
+    m = np.asarray(S).shape[0]
+    a = encode(x[np.asarray(l1_pos, dtype=np.int64)], sign_words, thresholds, centroids, S)
+    b = encode(x[groups.reshape(-1)], sign_words, thresholds, centroids, S)
+    return {"l1_bits": a["bits"], "l1_gamma": a["gamma"],
+            "l3_bits": b["bits"].reshape(ng, gn, m), "l3_gamma": b["gamma"].reshape(ng, gn)}

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from oracle import codebook as cb
-from oracle import codec, decode, rope, tiers
+from oracle import codec, decode, qjl, rope, tiers
 
 
 def make_unit(T=200, d=64, n_sink=4, n_recent=16, n_marked=10, gn=8, seed=0):
@@ -445,3 +445,86 @@ def test_prerope_rotation_matters():
     b = decode.hsq_attention_unit(q, deq, u["unit"]["l3"], sel, gn, d, u["ks"], u["vs"], u["cb4"],
                                   1 / math.sqrt(d))
     assert np.linalg.norm(a - b) > 1e-3 * np.linalg.norm(b)
+
+
+# ---- TQ-QKV token keys in the decode step ----------------------------------
+# Ablation page, "Key contributions" 1: TQ-QKV = TQ-KV plus a 1-bit QJL sketch
+# of the key residual.  Read for the step: every 4-bit token key (L1 and the
+# archive) carries its sketch and gamma; the summaries do not.
+
+def _qjl_unit(T=220, d=64, gn=8, seed=31):
+    u = make_unit(T=T, d=d, gn=gn, seed=seed)
+    S = np.random.default_rng(seed + 1).standard_normal((d, d))
+    sk = qjl.unit_sketches(u["k"], u["l1"], u["groups"], u["ks"], u["cb4"][1], u["cb4"][0], S)
+    return dict(u, S=S, sk=dict(sk, S=S))
+
+
+def _enc_dec(x, signs, c4):
+    c, n, _ = codec.encode(x, signs, c4[1])
+    return codec.decode(c, n, signs, c4[0])
+
+
+def test_qjl_zero_gamma_is_the_plain_step():
+    # gamma = 0 on every key: the correction vanishes and the step is TQ-KV
+    u = _qjl_unit()
+    d, gn = u["d"], u["gn"]
+    q = np.random.default_rng(2).standard_normal((3, d))
+    deq = decode.dequant_unit(u["unit"], d, gn, u["ks"], u["vs"], u["cb4"], u["cb3"])
+    sel = np.array([1, 4, 9])
+    sk = dict(u["sk"], l1_gamma=np.zeros_like(u["sk"]["l1_gamma"]),
+              l3_gamma=np.zeros_like(u["sk"]["l3_gamma"]))
+    a = decode.hsq_attention_unit(q, deq, u["unit"]["l3"], sel, gn, d, u["ks"], u["vs"], u["cb4"],
+                                  1 / math.sqrt(d), 0.3, qjl=sk)
+    b = decode.hsq_attention_unit(q, deq, u["unit"]["l3"], sel, gn, d, u["ks"], u["vs"], u["cb4"],
+                                  1 / math.sqrt(d), 0.3)
+    np.testing.assert_array_equal(a, b)
+
+
+def _dense(q, logits, vals):
+    s = logits - logits.max()
+    w = np.exp(s)
+    return (w[:, None] * vals).sum(axis=0) / w.sum()
+
+
+def test_qjl_all_fetched_equals_dense_attention_over_tq_qkv_logits():
+    # beta = ng: one softmax over the L1 tokens and every grouped token, each
+    # logit the codec-level TQ-QKV logit of its key (qjl.logits_qjl over the
+    # key's own encode and sketch), values dequantised at 4 bits
+    u = _qjl_unit()
+    d, gn, S = u["d"], u["gn"], u["S"]
+    q = np.random.default_rng(4).standard_normal((2, d)) * 2
+    scale = 1 / math.sqrt(d)
+    ng = u["groups"].shape[0]
+    deq = decode.dequant_unit(u["unit"], d, gn, u["ks"], u["vs"], u["cb4"], u["cb3"])
+    got = decode.hsq_attention_unit(q, deq, u["unit"]["l3"], np.arange(ng), gn, d, u["ks"],
+                                    u["vs"], u["cb4"], scale, qjl=u["sk"])
+    rows = np.concatenate([u["l1"], u["groups"].reshape(-1)])
+    e = qjl.encode(u["k"][rows], u["ks"], u["cb4"][1], u["cb4"][0], S)
+    lg = qjl.logits_qjl(q, e["codes"], e["norms"], e["bits"], e["gamma"], u["ks"], u["cb4"][0], S,
+                        scale)
+    vals = _enc_dec(u["v"][rows], u["vs"], u["cb4"])
+    want = np.stack([_dense(q[h], lg[h], vals) for h in range(q.shape[0])])
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_qjl_correction_enters_token_logits_only():
+    # nothing fetched: the L1 tokens take the TQ-QKV logit, every summary its
+    # plain logit plus the bias; and the correction is not a no-op
+    u = _qjl_unit(seed=37)
+    d, gn, S = u["d"], u["gn"], u["S"]
+    q = np.random.default_rng(6).standard_normal((1, d)) * 3
+    scale, bias = 1 / math.sqrt(d), -0.4
+    deq = decode.dequant_unit(u["unit"], d, gn, u["ks"], u["vs"], u["cb4"], u["cb3"])
+    none = np.zeros(0, dtype=np.int64)
+    got = decode.hsq_attention_unit(q, deq, u["unit"]["l3"], none, gn, d, u["ks"], u["vs"],
+                                    u["cb4"], scale, bias, qjl=u["sk"])
+    e = qjl.encode(u["k"][u["l1"]], u["ks"], u["cb4"][1], u["cb4"][0], S)
+    l1 = qjl.logits_qjl(q, e["codes"], e["norms"], e["bits"], e["gamma"], u["ks"], u["cb4"][0], S,
+                        scale)[0]
+    l2 = scale * (deq["l2k"] @ q[0]) + bias
+    vals = np.concatenate([_enc_dec(u["v"][u["l1"]], u["vs"], u["cb4"]), deq["l2v"]])
+    want = _dense(q[0], np.concatenate([l1, l2]), vals)
+    np.testing.assert_allclose(got[0], want, rtol=1e-12, atol=1e-12)
+    plain = decode.hsq_attention_unit(q, deq, u["unit"]["l3"], none, gn, d, u["ks"], u["vs"],
+                                      u["cb4"], scale, bias)
+    assert np.abs(got - plain).max() > 1e-4
