@@ -472,6 +472,59 @@ extern "C" int hsq_decode_step_prerope(const float* q, int B, int Hq, int Hkv, i
   return HSQ_OK;
 }
 
+extern "C" int hsq_decode_step_qjl(const float* q, int B, int Hq, int Hkv, int d,
+                                   const uint8_t* l1k, const float* l1k_n, const uint8_t* l1v,
+                                   const float* l1v_n, int n_l1, const uint8_t* l2k,
+                                   const float* l2k_n, const uint8_t* l2v, const float* l2v_n,
+                                   int n_groups, const uint8_t* l3, int group_n, int beta, int agg,
+                                   const uint32_t* k_signs, const uint32_t* v_signs,
+                                   const float* cb4, const float* cb3, float scale,
+                                   float summary_bias, const uint8_t* l1_sketch,
+                                   const float* l1_gamma, const uint8_t* l3_sketch,
+                                   const float* l3_gamma, const float* S, int32_t* topk_idx,
+                                   void* workspace, size_t ws_bytes, float* out, void* stream) {
+  const char* fn = "hsq_decode_step_qjl";
+  int rc = check_step_shape(fn, B, Hq, Hkv, d, n_l1, n_groups, group_n, beta);
+  if (rc) return rc;
+  if ((rc = attn_args(fn, q, l1k, l1k_n, l1v, l1v_n, n_l1, l2k, l2k_n, l2v, l2v_n, n_groups, l3,
+                      k_signs, v_signs, cb4, cb3, out)))
+    return rc;
+  if (agg != HSQ_AGG_MAX && agg != HSQ_AGG_MEAN) return fail(HSQ_ERR_ARG, std::string(fn) + ": bad agg");
+  if (!S) return fail(HSQ_ERR_ARG, std::string(fn) + ": null S");
+  if (n_l1 > 0 && (!l1_sketch || !l1_gamma))
+    return fail(HSQ_ERR_ARG, std::string(fn) + ": null L1 sketch or gamma");
+  if (n_groups > 0 && (!l3_sketch || !l3_gamma))
+    return fail(HSQ_ERR_ARG, std::string(fn) + ": null archive sketch or gamma");
+  const int b = beta < n_groups ? beta : n_groups;
+  StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, b};
+  Workspace w;
+  if ((rc = step_common(fn, s, workspace, ws_bytes, w))) return rc;
+  if (s.n_groups > 0 && !route_lds_ok(s))
+    return fail(HSQ_ERR_UNSUPPORTED,
+                std::string(fn) + ": G * n_groups exceeds 12288 (router logits beyond LDS)");
+  StepTensors t{};
+  t.q = q; t.l1k = l1k; t.l1k_n = l1k_n; t.l1v = l1v; t.l1v_n = l1v_n;
+  t.l2k = l2k; t.l2k_n = l2k_n; t.l2v = l2v; t.l2v_n = l2v_n; t.l3 = l3; t.l3_staged = 0;
+  t.k_signs = k_signs; t.v_signs = v_signs; t.cb4 = cb4; t.cb3 = cb3; t.scale = scale;
+  t.summary_bias = summary_bias; t.agg = agg; t.out = out;
+  char* ws = static_cast<char*>(workspace);
+  const hipStream_t st = as_stream(stream);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + w.idx_off);
+  if (s.n_groups > 0 &&
+      (rc = check_hip(launch_route(s, t, w, ws, ROUTE_TOPK | ROUTE_PARTIALS, nullptr, nullptr,
+                                   idx, st),
+                      "hsq_decode_step_qjl route")))
+    return rc;
+  const QjlKeys qk{l1_sketch, l1_gamma, l3_sketch, l3_gamma, S};
+  if ((rc = check_hip(launch_attn_qjl(s, t, w, ws, idx, qk, st), "hsq_decode_step_qjl attention")))
+    return rc;
+  if (topk_idx && b > 0)
+    return check_hip(hipMemcpyAsync(topk_idx, idx, sizeof(int32_t) * (size_t)B * Hkv * b,
+                                    hipMemcpyDeviceToDevice, st),
+                     "hsq_decode_step_qjl topk copy");
+  return HSQ_OK;
+}
+
 extern "C" int hsq_decode_step_static(const float* q, int B, int Hq, int Hkv, int d,
                                       const uint8_t* l1k, const float* l1k_n, const uint8_t* l1v,
                                       const float* l1v_n, int n_l1, const uint8_t* l2k,

@@ -147,6 +147,16 @@ hipError_t launch_attn(const StepShape& s, const StepTensors& t, const Workspace
 hipError_t launch_attn_prerope(const StepShape& s, const StepTensors& t, const Workspace& w,
                                char* ws, const int32_t* idx, const uint16_t* kdense,
                                hipStream_t st);
+// launch_attn over TQ-QKV token keys (dense tiers, device archive): every L1
+// and fetched token's logit gains its QJL residual estimate from the sketch
+// arrays and the sketch matrices S [Hkv][d][d]
+struct QjlKeys {
+  const uint8_t* l1_sk; const float* l1_gam;  // [units][n1][d/8], [units][n1]
+  const uint8_t* l3_sk; const float* l3_gam;  // [units][ng][N][d/8], [units][ng][N]
+  const float* S;
+};
+hipError_t launch_attn_qjl(const StepShape& s, const StepTensors& t, const Workspace& w, char* ws,
+                           const int32_t* idx, const QjlKeys& qk, hipStream_t st);
 // The whole step in one launch (route + attend per work-group); only for
 // shapes where step_fused_ok holds.  idx_out (optional): [units][beta].
 int step_fused_ok(const StepShape& s);

@@ -463,6 +463,50 @@ __device__ void router_operands(const float* qf, int lane, half8 (&b)[D / 32]) {
   }
 }
 
+// TQ-QKV: uf[h][j] = mult * sum_i S[j][i] qf[h][i] for h < G (rows of absent
+// heads are zero), S the unit's D x D sketch matrix (row j = direction j).
+// Each 16-lane group of a wave takes one row j at a time, D/16 coordinates
+// per lane (coalesced 16-byte loads), and sums over the group by DPP.
+template <int D>
+__device__ void qjl_project(const float* S, const float* qf, int G, float mult, float* uf,
+                            int tid, int nthreads) {
+  constexpr int PL = D / 16;  // coordinates per lane
+  const int l16 = tid & 15, grp = tid >> 4, ngrp = nthreads >> 4;
+  for (int j = grp; j < D; j += ngrp) {
+    float sv[PL];
+    const f32x4* sp = reinterpret_cast<const f32x4*>(S + (size_t)j * D + PL * l16);
+#pragma unroll
+    for (int c = 0; c < PL / 4; ++c) {
+      const f32x4 x = sp[c];
+      sv[4 * c] = x[0]; sv[4 * c + 1] = x[1]; sv[4 * c + 2] = x[2]; sv[4 * c + 3] = x[3];
+    }
+    for (int h = 0; h < kMaxG; ++h) {  // uniform within the group
+      float acc = 0.f;
+      if (h < G) {
+        const float* qp = qf + h * kQS<D> + PL * l16;
+#pragma unroll
+        for (int c = 0; c < PL; ++c) acc = fmaf(sv[c], qp[c], acc);
+      }
+      acc = group_sum<16>(acc);
+      if (l16 == 0) uf[h * kQS<D> + j] = acc * mult;
+    }
+  }
+}
+// B operand of the sketch products: lane (c, gq), chunk m, slot 2k + h holds
+// head col_head(c)'s u at coordinate gq*D/4 + 4m + k + (D/8) h (the order in
+// which consume_tok takes the sketch bits).
+template <int D>
+__device__ void qjl_operands(const float* uf, int lane, half8 (&u)[D / 32]) {
+  const int c = lane & 15, gq = lane >> 4, h = col_head(c);
+  const float* src = uf + h * kQS<D> + gq * (D / 4);
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) u[m][2 * k + hh] = (_Float16)src[4 * m + k + (D / 8) * hh];
+}
+
 // ---------------------------------------------------------- online softmax ---
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -1698,6 +1742,12 @@ struct TokArgs {
   // rotated domain (RopeKeysJob), read in place of the key codes' table
   // lookups by the fetched tiles (null otherwise)
   const uint16_t* kdense;
+  // TQ-QKV token keys: the QJL sketch bits and gamma of every L1 key
+  // ([units][n1][D/8], [units][n1]) and archive key ([units][ng][N][D/8],
+  // [units][ng][N]), and the sketch matrices S [Hkv][D][D] (null otherwise)
+  const uint8_t* l1_sk; const float* l1_gam;
+  const uint8_t* l3_sk; const float* l3_gam;
+  const float* S;
 };
 
 struct TokTile {
@@ -1712,6 +1762,13 @@ struct TokTile {
 struct TokTileK : TokTile {
   u32x4 kd[4];
 };
+// A tile of TQ-QKV keys: also the lane's D/4 sketch bits of token row
+// lane&15 (D = 64: 16 bits, spread to bits 0-7 and 16-23) and the gamma of
+// row 4gq + (lane & 3).
+struct TokTileQ : TokTile {
+  uint32_t sk;
+  float gm;
+};
 
 // Per-unit buffers of the token tiles.  Tile t < n1t holds L1 rows 16t ..
 // 16t+15; tile n1t + f holds the fetched archive groups of slot f (N = 16) or
@@ -1720,6 +1777,7 @@ struct TokTileK : TokTile {
 struct TokBufs {
   rsrc_t l1k, l1kn, l1v, l1vn, l3;
   rsrc_t kd;  // the unit's fetched-key rows (pre-RoPE archive), else empty
+  rsrc_t l1sk, l1gm, l3sk, l3gm;  // the unit's sketches and gammas (TQ-QKV), else empty
 };
 
 template <int D, int N>
@@ -1738,7 +1796,29 @@ __device__ __forceinline__ TokBufs tok_bufs(const TokArgs& a, int unit) {
   const size_t kdu = (size_t)a.beta * N * D;  // fp16 values per unit
   B.kd = make_rsrc(a.kdense ? a.kdense + (size_t)unit * kdu : nullptr,
                    a.kdense ? (uint32_t)(kdu * 2) : 0u);
+  const bool q = a.l1_sk != nullptr;
+  const size_t n3 = (size_t)a.ng * N;  // archive keys per unit
+  B.l1sk = make_rsrc(q ? a.l1_sk + o1 * (D / 8) : nullptr, q ? (uint32_t)a.n1 * (D / 8) : 0u);
+  B.l1gm = make_rsrc(q ? a.l1_gam + o1 : nullptr, q ? (uint32_t)a.n1 * 4 : 0u);
+  B.l3sk = make_rsrc(q ? a.l3_sk + (size_t)unit * a.ngs * N * (D / 8) : nullptr,
+                     q ? (uint32_t)(n3 * (D / 8)) : 0u);
+  B.l3gm = make_rsrc(q ? a.l3_gam + (size_t)unit * a.ngs * N : nullptr,
+                     q ? (uint32_t)(n3 * 4) : 0u);
   return B;
+}
+
+// The lane's sketch bits of a key row (D/8 bytes at row_off): coordinates
+// gq*D/4 .. gq*D/4 + D/4 - 1.  D = 64: 16 bits, spread so that bits 0-7
+// stay and bits 8-15 move to 16-23 (the pairs the operand builder takes).
+// Bit offsets past the buffer (kFar rows) read zero.
+template <int D>
+__device__ __forceinline__ uint32_t sketch_bits(rsrc_t r, uint32_t row_off, int gq) {
+  if constexpr (D == 128) {
+    return ld32(r, row_off + 4u * (uint32_t)gq);
+  } else {
+    const uint32_t w = ld32(r, row_off + 4u * (uint32_t)(gq >> 1)) >> (16 * (gq & 1));
+    return (w & 0xffu) | ((w & 0xff00u) << 8);
+  }
 }
 
 // recoff[s]: byte offset of slot s's record in the unit's archive buffer, or
@@ -1777,6 +1857,10 @@ __device__ __forceinline__ void load_tok_at(const TokBufs& B, int t, int n1t, in
     T.vn = __uint_as_float(ld32(B.l1vn, tn + (uint32_t)(16 * gq + 4 * (lane & 3))));
 #pragma unroll
     for (int j = 0; j < 4; ++j) T.va[j] = ld32(B.l1v, vo + j * CB);
+    if constexpr (std::is_same_v<TT, TokTileQ>) {
+      T.sk = sketch_bits<D>(B.l1sk, (uint32_t)((16 * t + n) * (D / 8)), gq);
+      T.gm = __uint_as_float(ld32(B.l1gm, tn + (uint32_t)(16 * gq + 4 * (lane & 3))));
+    }
   } else {
     uint32_t vo = br + (uint32_t)(N * (CB + 4) + tr * CB) + vl;
     asm("" : "+v"(vo));
@@ -1796,6 +1880,14 @@ __device__ __forceinline__ void load_tok_at(const TokBufs& B, int t, int n1t, in
       const uint32_t ko = (uint32_t)((slot * N + tk) * (2 * D)) + (uint32_t)(gq * (D / 2));
 #pragma unroll
       for (int m = 0; m < D / 32; ++m) T.kd[m] = ld128(B.kd, ko + 16 * m);
+    }
+    if constexpr (std::is_same_v<TT, TokTileQ>) {
+      // the group of a record offset (a constant divisor); kFar gives a
+      // group past every buffer, which reads zero
+      constexpr uint32_t REC = (uint32_t)(N * (D + 8));
+      const uint32_t gk = bk / REC, gr = br / REC;
+      T.sk = sketch_bits<D>(B.l3sk, (gk * N + (uint32_t)tk) * (D / 8), gq);
+      T.gm = __uint_as_float(ld32(B.l3gm, 4u * (gr * N + (uint32_t)(tr + (lane & 3)))));
     }
   }
 }
@@ -1853,7 +1945,7 @@ template <int D, bool SPLITQ = false, typename MaskF, typename TT = TokTile>
 __device__ __forceinline__ void consume_tok(const TT& T, bool masked, MaskF mask,
                                             const half8 (&qh)[D / 32], const uint32_t* lut4,
                                             int lane, uint32_t lane4, Softmax<D>& st,
-                                            bool dense = false) {
+                                            bool dense = false, const half8* uh = nullptr) {
   // two accumulators so that consecutive MFMAs do not wait on each other
   f32x4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   if constexpr (std::is_same_v<TT, TokTileK>) {
@@ -1883,6 +1975,24 @@ __device__ __forceinline__ void consume_tok(const TT& T, bool masked, MaskF mask
   float lg[4], p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) lg[i] = acc[i] * row_norm(T.kn, i);
+  if constexpr (std::is_same_v<TT, TokTileQ>) {
+    // the QJL estimate of the residual's share: <(1 - 2 bits), u> on MFMA
+    // with the +-1 operands built from the sketch bits (slot 2k + h of chunk
+    // m takes bit 4m + k + (D/8) h: a shift puts both at the fp16 sign bits)
+    // and u = scale sqrt(pi/2)/D S R q in the same coordinate order, times
+    // gamma of the row
+    f32x4 aq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) {
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        w[k] = ((T.sk << (15 - 4 * m - k)) & 0x80008000u) | 0x3c003c00u;
+      aq = mfma16(as_h8(w[0], w[1], w[2], w[3]), uh[m], aq);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lg[i] = fmaf(aq[i], row_norm(T.gm, i), lg[i]);
+  }
   if (masked) mask(lg);  // wave-uniform
   st.update(lg, p);
   float w[4];
@@ -1905,6 +2015,7 @@ struct AttendLds {
   int32_t* recoff;  // record offset per slot, tok_slots(beta) entries
   float* cb;        // 16 centroids of the 4-bit codebook
   uint32_t* vsb;    // V sign byte per (head, lane of the inverse rotation)
+  float* uf;        // TQ-QKV: scale sqrt(pi/2)/D S R q per head, kMaxG * kQS<D>
 };
 
 // L1 + fetched-token attention of one unit, merged with the summary partial,
@@ -1949,7 +2060,13 @@ __device__ __forceinline__ void attend_unit(const TokArgs& a, const AttendLds& L
   build_lut4(L.lut4, L.cb, tid);
   half8 qh[D / 32], ql[D / 32];
   query_operands<D>(L.qf, lane, qh, ql);
+  constexpr bool QJL = std::is_same_v<TT, TokTileQ>;
+  if constexpr (QJL)
+    qjl_project<D>(a.S + (size_t)(unit % a.Hkv) * D * D, L.qf, a.G, 1.2533141373155003f / D, L.uf,
+                   tid, kThreads);
   lds_barrier();
+  half8 uh[QJL ? D / 32 : 1];
+  if constexpr (QJL) qjl_operands<D>(L.uf, lane, uh);
 
   Softmax<D> st;
   if (st_in)
@@ -1976,7 +2093,7 @@ __device__ __forceinline__ void attend_unit(const TokArgs& a, const AttendLds& L
           consume_tok<D>(
               T, masked,
               [&](float (&lg)[4]) { mask_rows<N>(lg, t, n1t, a.n1, a.beta, L.recoff, lane); },
-              qh, lut4, lane, lane4, st, t >= n1t);
+              qh, lut4, lane, lane4, st, t >= n1t, uh);
         });
   }
   lds_barrier();  // the table is no longer needed: reuse as scratch
@@ -2035,14 +2152,14 @@ __device__ __forceinline__ void attend_unit(const TokArgs& a, const AttendLds& L
 template <int D, int N, typename TT = TokTile>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void token_kernel(TokArgs a) {
-  constexpr int TD = std::is_same_v<TT, TokTileK> ? kTokDepth - 1 : kTokDepth;
+  constexpr int TD = std::is_same_v<TT, TokTile> ? kTokDepth : kTokDepth - 1;
   extern __shared__ __align__(16) char smem[];
   __shared__ __align__(16) uint32_t s_lut4[256 * kNC4];
   __shared__ float s_cb[16];
   __shared__ uint32_t s_vsb[kMaxG * (D / 8)];
   __shared__ int s_bad;  // some slot names no record
   // dynamic layout: [qf 8*(D+4) f32][summary partial 8*(D+2) f32]
-  //   [recoff tok_slots(beta)]
+  //   [recoff tok_slots(beta)][TQ-QKV: uf 8*(D+4) f32]
   AttendLds L;
   L.lut4 = s_lut4;
   L.qf = reinterpret_cast<float*>(smem);
@@ -2050,6 +2167,7 @@ void token_kernel(TokArgs a) {
   L.recoff = reinterpret_cast<int32_t*>(L.part + kMaxG * (D + 2));
   L.cb = s_cb;
   L.vsb = s_vsb;
+  L.uf = reinterpret_cast<float*>(L.recoff + ((tok_slots<N>(a.beta) + 3) & ~3));
 
   const int tid = threadIdx.x, wave = wave_id();
   const int unit = blockIdx.x;
@@ -3089,9 +3207,10 @@ size_t summary_smem(int D, const StepShape& s) {
   return std::max(body, comb);
 }
 
-size_t token_smem(int D, const StepShape& s) {
+size_t token_smem(int D, const StepShape& s, bool qjl = false) {
   const int slots = s.group_n == 16 ? tok_slots<16>(s.beta) : tok_slots<8>(s.beta);
-  return (size_t)kMaxG * (D + 4) * 4 + (size_t)kMaxG * (D + 2) * 4 + (size_t)slots * 4;
+  return (size_t)kMaxG * (D + 4) * 4 + (size_t)kMaxG * (D + 2) * 4 +
+         (size_t)((slots + 3) & ~3) * 4 + (qjl ? (size_t)kMaxG * (D + 4) * 4 : 0);
 }
 
 // Waves per work-group of the one-launch step: 16 (one work-group per CU)
@@ -3322,17 +3441,23 @@ hipError_t launch_route(const StepShape& s, const StepTensors& t, const Workspac
 
 template <int D, typename TT = TokTile>
 hipError_t token_d(const StepShape& s, const StepTensors& t, const Workspace& w, char* ws,
-                   const int32_t* idx, const uint16_t* kdense, hipStream_t st) {
+                   const int32_t* idx, const uint16_t* kdense, hipStream_t st,
+                   const QjlKeys* qk = nullptr) {
   TokArgs a = tok_args(s, t);
   a.idx = idx;
   a.part = s.n_groups > 0 ? reinterpret_cast<const float*>(ws + w.part_off) : nullptr;
   a.kdense = kdense;
+  if (qk) {
+    a.l1_sk = qk->l1_sk; a.l1_gam = qk->l1_gam; a.l3_sk = qk->l3_sk; a.l3_gam = qk->l3_gam;
+    a.S = qk->S;
+  }
+  const size_t smem = token_smem(D, s, qk != nullptr);
   if (s.group_n == 16)
     hipLaunchKernelGGL((token_kernel<D, 16, TT>), dim3((unsigned)(s.B * s.Hkv)), dim3(kThreads),
-                       token_smem(D, s), st, a);
+                       smem, st, a);
   else
     hipLaunchKernelGGL((token_kernel<D, 8, TT>), dim3((unsigned)(s.B * s.Hkv)), dim3(kThreads),
-                       token_smem(D, s), st, a);
+                       smem, st, a);
   return hipGetLastError();
 }
 
@@ -3351,6 +3476,16 @@ hipError_t launch_attn_prerope(const StepShape& s, const StepTensors& t, const W
     return hipErrorInvalidValue;
   return s.d == 128 ? token_d<128, TokTileK>(s, t, w, ws, idx, kdense, st)
                     : token_d<64, TokTileK>(s, t, w, ws, idx, kdense, st);
+}
+
+hipError_t launch_attn_qjl(const StepShape& s, const StepTensors& t, const Workspace& w, char* ws,
+                           const int32_t* idx, const QjlKeys& qk, hipStream_t st) {
+  if (!step_limits_ok(s) || (s.n_groups > 0 && !route_lds_ok(s)) || t.l3_staged ||
+      s.l1_stride || s.ng_stride || !qk.S || (s.n_l1 > 0 && (!qk.l1_sk || !qk.l1_gam)) ||
+      (s.beta > 0 && (!qk.l3_sk || !qk.l3_gam)))
+    return hipErrorInvalidValue;
+  return s.d == 128 ? token_d<128, TokTileQ>(s, t, w, ws, idx, nullptr, st, &qk)
+                    : token_d<64, TokTileQ>(s, t, w, ws, idx, nullptr, st, &qk);
 }
 
 template <int D, int N>

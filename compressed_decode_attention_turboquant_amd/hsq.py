@@ -43,6 +43,9 @@ _SIGNATURES = {
     "hsq_decode_step_prerope": ([_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp,
                                  _i, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _f, _vp,
                                  _c.c_double, _vp, _vp, _sz, _vp, _vp], _i),
+    "hsq_decode_step_qjl": ([_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp,
+                             _i, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _f, _vp, _vp, _vp,
+                             _vp, _vp, _vp, _vp, _sz, _vp, _vp], _i),
     "hsq_decode_step_static": ([_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp,
                                 _i, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _f, _vp, _vp, _vp],
                                _i),
@@ -383,6 +386,37 @@ def decode_step_prerope(q, tiers, beta, k_signs, v_signs, cb4, cb3, group_pos, r
         _dev(group_pos, torch.int32, "group_pos") if tiers.ng > 0 else None, float(rope_base),
         idx.data_ptr() if idx is not None else None, ws.ptr, ws.nbytes, out.data_ptr(),
         _stream()))
+    return out, idx
+
+
+def decode_step_qjl(q, tiers, beta, k_signs, v_signs, cb4, cb3, l1_sketch, l1_gamma, l3_sketch,
+                    l3_gamma, S, scale=None, summary_bias=0.0, agg=HSQ_AGG_MAX, ws=None,
+                    out=None, idx=None):
+    """hsq_decode_step_qjl: the decode step with TQ-QKV token keys (sketches
+    and gammas of the L1 and archive keys, S [Hkv][d][d]).  Returns (out, idx)."""
+    B, Hq, d = q.shape
+    b = min(beta, tiers.ng)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if ws is None:
+        ws = make_workspace(B, Hq, tiers.Hkv, d, tiers.n1, tiers.ng, b, tiers.group_n, q.device)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if idx is None and b > 0:
+        idx = torch.empty((B, tiers.Hkv, b), dtype=torch.int32, device=q.device)
+    has1, has3 = tiers.n1 > 0, tiers.ng > 0
+    _check(lib().hsq_decode_step_qjl(
+        _dev(q, torch.float32, "q"), B, Hq, tiers.Hkv, d, _dev(tiers.l1k), _dev(tiers.l1k_n),
+        _dev(tiers.l1v), _dev(tiers.l1v_n), tiers.n1, _dev(tiers.l2k), _dev(tiers.l2k_n),
+        _dev(tiers.l2v), _dev(tiers.l2v_n), tiers.ng, tiers.l3.data_ptr(), tiers.group_n, beta,
+        agg, _dev(k_signs, torch.int32, "k_signs"), _dev(v_signs, torch.int32, "v_signs"),
+        _dev(cb4, torch.float32, "cb4"), _dev(cb3, torch.float32, "cb3"), scale, summary_bias,
+        _dev(l1_sketch, torch.uint8, "l1_sketch") if has1 else None,
+        _dev(l1_gamma, torch.float32, "l1_gamma") if has1 else None,
+        _dev(l3_sketch, torch.uint8, "l3_sketch") if has3 else None,
+        _dev(l3_gamma, torch.float32, "l3_gamma") if has3 else None,
+        _dev(S, torch.float32, "S"), idx.data_ptr() if idx is not None else None, ws.ptr,
+        ws.nbytes, out.data_ptr(), _stream()))
     return out, idx
 
 

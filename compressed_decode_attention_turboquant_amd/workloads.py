@@ -155,6 +155,13 @@ def signs(w_seed, layer, hkv, d):
     return np.ascontiguousarray(m[0]), np.ascontiguousarray(m[1])
 
 
+def sketch_matrices(w_seed, layer, hkv, d):
+    """QJL sketch matrices of the TQ-QKV keys: i.i.d. N(0, 1), fp32
+    [hkv, d, d] (row j = sketch direction j of kv-head h)."""
+    rng = np.random.default_rng([_seed(w_seed, layer, "qjl-S") & 0xFFFFFFFF, layer])
+    return rng.standard_normal((hkv, d, d)).astype(np.float32)
+
+
 def marked(w, b):
     """Reader-marked positions of sequence b (sorted int64)."""
     lo, hi = w.n_sink, w.T - w.n_recent

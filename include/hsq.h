@@ -332,6 +332,39 @@ int hsq_decode_step_prerope(const float* q, int B, int Hq, int Hkv, int d, const
                             void* workspace, size_t ws_bytes, float* out, void* stream);
 
 /*
+ * hsq_decode_step_qjl -- the decode step over TQ-QKV token keys [ABL "Key
+ * contributions" 1: TQ-QKV = TurboQuant plus a 1-bit QJL sketch of the key
+ * residual; estimator as hsq_qjl_logits].  Every 4-bit token key (L1 and the
+ * archive) carries its sketch and gamma, as hsq_encode_qjl writes them for
+ * that key (same signs, the 4-bit codebook, one S per kv-head); the L2
+ * summaries do not.  The route, the selection and the summaries are as in
+ * hsq_decode_step (two launches); the logit of every L1 token and every
+ * fetched token is
+ *   scale * (r <R q, c[code]> + sqrt(pi/2)/d * gamma * <S R q, 1 - 2 bits>),
+ * the correction formed on MFMA from the sketch bits (fp16 S R q operands).
+ *   l1_sketch   uint8 [B][Hkv][n_l1][d/8], l1_gamma fp32 [B][Hkv][n_l1]
+ *               (the L1 keys in L1 order)
+ *   l3_sketch   uint8 [B][Hkv][n_groups][group_n][d/8], l3_gamma fp32
+ *               [B][Hkv][n_groups][group_n] (the grouped keys in group order)
+ *   S           fp32 [Hkv][d][d], row j = sketch direction j of kv-head h
+ *   workspace   hsq_workspace_bytes(...) bytes, as hsq_decode_step
+ *   other arguments as in hsq_decode_step
+ * Errors: as hsq_decode_step, plus HSQ_ERR_ARG for a null S, or null
+ * sketches or gammas of a tier that has entries, HSQ_ERR_UNSUPPORTED when
+ * G * n_groups > 12288.
+ */
+int hsq_decode_step_qjl(const float* q, int B, int Hq, int Hkv, int d, const uint8_t* l1k,
+                        const float* l1k_n, const uint8_t* l1v, const float* l1v_n, int n_l1,
+                        const uint8_t* l2k, const float* l2k_n, const uint8_t* l2v,
+                        const float* l2v_n, int n_groups, const uint8_t* l3, int group_n,
+                        int beta, int agg, const uint32_t* k_signs, const uint32_t* v_signs,
+                        const float* cb4, const float* cb3, float scale, float summary_bias,
+                        const uint8_t* l1_sketch, const float* l1_gamma,
+                        const uint8_t* l3_sketch, const float* l3_gamma, const float* S,
+                        int32_t* topk_idx, void* workspace, size_t ws_bytes, float* out,
+                        void* stream);
+
+/*
  * hsq_decode_step_static -- hsq_decode_step without a workspace argument,
  * for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc).  The

@@ -123,6 +123,17 @@ def test_argument_errors_are_reported_without_launch():
     assert pre_step(base=float("inf")) == -1
     assert pre_step(ws_bytes=plain) == -4
     assert pre_step(ws=None) == -4
+    # TQ-QKV step: null S, null sketches of a tier that has entries
+    def qjl_step(l1s=p, l1g=p, l3s=p, l3g=p, S=p, n_l1=10, ng=10):
+        f = ctypes.c_float(0.1)
+        return lib.hsq_decode_step_qjl(p, 2, 32, 8, 128, p, p, p, p, n_l1, p, p, p, p, ng, p, 16,
+                                       4, 0, p, p, p, p, f, f, l1s, l1g, l3s, l3g, S, None,
+                                       ctypes.c_void_p(256), plain, p, None)
+
+    assert qjl_step(S=None) == -1
+    assert "S" in lib.hsq_last_error().decode()
+    assert qjl_step(l1s=None) == -1
+    assert qjl_step(l3g=None) == -1
     assert lib.hsq_gather_l3_ordered(p, 1088, 1, 1, 4, p, 2, p, None, 0, None) == -1
     assert "turn" in lib.hsq_last_error().decode()
     assert lib.hsq_gather_l3_ordered(p, 1088, 1, 1, 4, p, 2, p, ctypes.c_void_p(18), 0, None) == -1
