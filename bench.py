@@ -237,6 +237,36 @@ def headline(args, torch, hsq, W):
         time_graph(torch, g, 2, stream)
         pre_ms = float(np.median(time_reps(torch, g, 10, stream))) / L
         del g, pre_ws
+    # the same layers with TQ-QKV token keys: seeded sketch bits and gammas
+    # of every L1 and archive key (their values do not change the work)
+    qjl_ms = None
+    if not args.only_step:
+        t0_ = layers[0].tiers
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7)
+        sk = {
+            "l1s": torch.randint(0, 256, (w.batch, w.hkv, t0_.n1, w.d // 8), generator=gen,
+                                 device=dev, dtype=torch.uint8),
+            "l1g": torch.rand((w.batch, w.hkv, t0_.n1), generator=gen, device=dev) * 0.1,
+            "l3s": torch.randint(0, 256, (w.batch, w.hkv, t0_.ng, w.group_n, w.d // 8),
+                                 generator=gen, device=dev, dtype=torch.uint8),
+            "l3g": torch.rand((w.batch, w.hkv, t0_.ng, w.group_n), generator=gen,
+                              device=dev) * 0.1,
+            "S": torch.from_numpy(W.sketch_matrices(w.seed, 0, w.hkv, w.d)).to(dev),
+        }
+
+        def qjl(ly):
+            hsq.decode_step_qjl(ly.q, ly.tiers, w.beta, ly.dks, ly.dvs, cb["cb4"], cb["cb3"],
+                                sk["l1s"], sk["l1g"], sk["l3s"], sk["l3g"], sk["S"], ws=ly.ws,
+                                out=ly.out)
+
+        with torch.cuda.stream(stream):
+            qjl(layers[0])
+            stream.synchronize()
+        g = capture(torch, stream, lambda: [qjl(ly) for ly in layers])
+        time_graph(torch, g, 2, stream)
+        qjl_ms = float(np.median(time_reps(torch, g, 10, stream))) / L
+        del g, sk
     t = layers[0].tiers
     units = w.batch * w.hkv
     rb, ab = algorithmic_bytes(w, t.n1, t.ng, layers[0].beta)
@@ -254,6 +284,10 @@ def headline(args, torch, hsq, W):
         "prerope_step": None if pre_ms is None else {
             "us": pre_ms * 1e3, "vs_step": pre_ms / ms_step, "launches": 3,
             "what": "same layers as pre-RoPE archives: route, fetched-key RoPE pass, attend"},
+        "qjl_step": None if qjl_ms is None else {
+            "us": qjl_ms * 1e3, "vs_step": qjl_ms / ms_step, "launches": 2,
+            "what": "same layers with TQ-QKV token keys (QJL sketches of every L1 and "
+                    "archive key): route, attend with the sketch correction"},
         "dominant": "step_kernel", "achieved": achieved, "n1": t.n1, "ng": t.ng,
         "step_bytes": step_bytes,
         "tier_bytes": t.nbytes(),
@@ -806,6 +840,7 @@ def main():
         "kernels": k,
         "two_launch": res["two_launch"],
         "prerope_step": res["prerope_step"],
+        "qjl_step": res["qjl_step"],
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": res["achieved"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": res["achieved"] / HBM_PEAK_GBS,
                      "traffic": measured_traffic(dom)},
