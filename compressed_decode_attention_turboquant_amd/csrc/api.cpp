@@ -696,6 +696,49 @@ extern "C" int hsq_encode_qjl(const void* x, int x_dtype, int64_t n_vec, int d, 
   return check_hip(launch_qjl_encode(j, as_stream(stream)), "hsq_encode_qjl");
 }
 
+extern "C" int hsq_build_sketches(const void* k, int dtype, int B, int Hkv, int T, int d,
+                                  const int32_t* l1_pos, int n1, const int32_t* group_pos,
+                                  int n_groups, int group_n, const uint32_t* k_signs,
+                                  const float* thr4, const float* cb4, const float* S,
+                                  uint8_t* l1_sketch, float* l1_gamma, uint8_t* l3_sketch,
+                                  float* l3_gamma, void* stream) {
+  const char* fn = "hsq_build_sketches";
+  if (B < 1 || Hkv < 1 || T < 1 || n1 < 0 || n_groups < 0 || group_n < 1)
+    return fail(HSQ_ERR_ARG, std::string(fn) + ": bad sizes");
+  if ((int64_t)n1 + (int64_t)n_groups * group_n > T)
+    return fail(HSQ_ERR_ARG, std::string(fn) + ": n1 + n_groups * group_n exceeds T");
+  if (!supported_d(d)) return fail(HSQ_ERR_UNSUPPORTED, std::string(fn) + ": d must be 64 or 128");
+  if (dtype != HSQ_F32 && dtype != HSQ_BF16)
+    return fail(HSQ_ERR_UNSUPPORTED, std::string(fn) + ": dtype must be HSQ_F32 or HSQ_BF16");
+  if ((int64_t)B * Hkv * T >= (int64_t(1) << 32))
+    return fail(HSQ_ERR_UNSUPPORTED, std::string(fn) + ": B * Hkv * T must be below 2^32");
+  if (!k || !k_signs || !thr4 || !cb4 || !S)
+    return fail(HSQ_ERR_ARG, std::string(fn) + ": null pointer");
+  if (n1 > 0 && (!l1_pos || !l1_sketch || !l1_gamma))
+    return fail(HSQ_ERR_ARG, std::string(fn) + ": null L1 pointer");
+  if (n_groups > 0 && (!group_pos || !l3_sketch || !l3_gamma))
+    return fail(HSQ_ERR_ARG, std::string(fn) + ": null archive pointer");
+  const hipStream_t st = as_stream(stream);
+  for (int h = 0; h < Hkv; ++h) {
+    for (int tier = 0; tier < 2; ++tier) {
+      const int64_t per_seq = tier == 0 ? n1 : (int64_t)n_groups * group_n;
+      if (per_seq == 0) continue;
+      QjlJob j{};
+      j.x = k; j.dtype = dtype; j.n_vec = (int64_t)B * per_seq; j.d = d; j.bits = 4;
+      j.signs = k_signs + (size_t)h * (d / 32); j.thr = thr4; j.centroids = cb4;
+      j.S = S + (size_t)h * d * d;
+      j.sketch = tier == 0 ? l1_sketch : l3_sketch;
+      j.gamma = tier == 0 ? l1_gamma : l3_gamma;
+      j.pos = tier == 0 ? l1_pos : group_pos;
+      j.per_seq = per_seq; j.x_seq = (int64_t)Hkv * T; j.x_base = (int64_t)h * T;
+      j.out_seq = (int64_t)Hkv * per_seq; j.out_base = (int64_t)h * per_seq;
+      const int rc = check_hip(launch_qjl_encode(j, st), "hsq_build_sketches");
+      if (rc) return rc;
+    }
+  }
+  return HSQ_OK;
+}
+
 extern "C" int hsq_qjl_logits(const float* q, int n_q, int d, int bits, const uint8_t* codes,
                               const float* norms, const uint8_t* sketch, const float* gamma,
                               int64_t n_keys, const uint32_t* signs, const float* centroids,

@@ -188,6 +188,11 @@ struct QjlJob {
   const void* x; int dtype; int64_t n_vec; int d, bits;
   const uint32_t* signs; const float* thr; const float* centroids; const float* S;
   uint8_t* codes; float* norms; uint8_t* sketch; float* gamma;
+  // gathered rows (tier build), when pos is set: vector i = (s, t) with
+  // s = i / per_seq, t = i % per_seq reads row x_base + s * x_seq + pos[i]
+  // of x and writes its sketch and gamma at out_base + s * out_seq + t;
+  // codes and norms may be null (not written)
+  const int32_t* pos; int64_t per_seq, x_seq, x_base, out_seq, out_base;
 };
 hipError_t launch_qjl_encode(const QjlJob& j, hipStream_t s);
 struct QjlLogitsJob {

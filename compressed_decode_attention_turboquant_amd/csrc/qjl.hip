@@ -65,6 +65,7 @@ __global__ __launch_bounds__(kQWG) void qjl_encode_kernel(QjlJob j) {
   __shared__ float s_S[D * kSP<D>];
   __shared__ float s_u[VPP * kSP<D>];
   __shared__ float s_c[16];
+  __shared__ int64_t s_out[VPP];  // output row of each vector of the pass
   const int tid = threadIdx.x, sub = tid % LPV, vl = tid / LPV;
   stage_S<D>(s_S, j.S, tid);
   if (tid < L) s_c[tid] = j.centroids[tid];
@@ -78,9 +79,17 @@ __global__ __launch_bounds__(kQWG) void qjl_encode_kernel(QjlJob j) {
   for (int64_t p = blockIdx.x; p < passes; p += gridDim.x) {
     const int64_t i = p * VPP + vl;
     const bool valid = i < j.n_vec;
+    // input row and output row of this vector (gathered in a tier build)
+    int64_t xr = i, orow = i;
+    if (j.pos && valid) {
+      const int64_t sq = i / j.per_seq;
+      xr = j.x_base + sq * j.x_seq + j.pos[i];
+      orow = j.out_base + sq * j.out_seq + (i - sq * j.per_seq);
+    }
+    if (sub == 0) s_out[vl] = orow;
     float v[8];
     if (valid) {
-      load8<DT>(j.x, i * D + 8 * sub, v);
+      load8<DT>(j.x, xr * D + 8 * sub, v);
     } else {
 #pragma unroll
       for (int a = 0; a < 8; ++a) v[a] = 0.f;
@@ -112,19 +121,20 @@ __global__ __launch_bounds__(kQWG) void qjl_encode_kernel(QjlJob j) {
       s_u[vl * kSP<D> + 8 * sub + a] = u;
     }
     uu = lanes_sum<LPV>(uu);
-    uint8_t* crow = j.codes + i * CB;
+    const bool wc = valid && j.codes != nullptr;  // codes and norms wanted
+    uint8_t* crow = j.codes + (wc ? i : 0) * CB;
     if constexpr (BITS == 4) {
-      if (valid) reinterpret_cast<uint32_t*>(crow)[sub] = packed;
+      if (wc) reinterpret_cast<uint32_t*>(crow)[sub] = packed;
     } else {
       const uint32_t nxt = __shfl_down(packed, 1, 64);
       const int qd = sub & 3;
-      if (valid && qd < 3)
+      if (wc && qd < 3)
         reinterpret_cast<uint32_t*>(crow)[3 * (sub >> 2) + qd] =
             (packed >> (8 * qd)) | (nxt << (24 - 8 * qd));
     }
     if (valid && sub == 0) {
-      j.norms[i] = r;
-      j.gamma[i] = r * sqrtf(uu);
+      if (wc) j.norms[i] = r;
+      j.gamma[orow] = r * sqrtf(uu);
     }
     __syncthreads();
     // projections of the pass's residuals, P = U S^T (VPP x d), on fp32 MFMA
@@ -147,9 +157,10 @@ __global__ __launch_bounds__(kQWG) void qjl_encode_kernel(QjlJob j) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint64_t b = __builtin_amdgcn_ballot_w64(acc[e] < 0.f);
-        const int64_t vi = p * VPP + 16 * rt + 4 * lk + e;
+        const int vv = 16 * rt + 4 * lk + e;  // vector of the pass
+        const int64_t vi = p * VPP + vv;
         if (lr == 0 && vi < j.n_vec)
-          *reinterpret_cast<uint16_t*>(j.sketch + vi * (D / 8) + 2 * ct) =
+          *reinterpret_cast<uint16_t*>(j.sketch + s_out[vv] * (D / 8) + 2 * ct) =
               (uint16_t)(b >> (16 * lk));
       }
     }

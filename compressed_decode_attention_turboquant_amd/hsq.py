@@ -46,6 +46,8 @@ _SIGNATURES = {
     "hsq_decode_step_qjl": ([_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp,
                              _i, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _f, _vp, _vp, _vp,
                              _vp, _vp, _vp, _vp, _sz, _vp, _vp], _i),
+    "hsq_build_sketches": ([_vp, _i, _i, _i, _i, _i, _vp, _i, _vp, _i, _i, _vp, _vp, _vp, _vp,
+                            _vp, _vp, _vp, _vp, _vp], _i),
     "hsq_decode_step_static": ([_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp,
                                 _i, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _f, _vp, _vp, _vp],
                                _i),
@@ -418,6 +420,27 @@ def decode_step_qjl(q, tiers, beta, k_signs, v_signs, cb4, cb3, l1_sketch, l1_ga
         _dev(S, torch.float32, "S"), idx.data_ptr() if idx is not None else None, ws.ptr,
         ws.nbytes, out.data_ptr(), _stream()))
     return out, idx
+
+
+def build_sketches(k, l1_pos, group_pos, group_n, k_signs, thr4, cb4, S):
+    """hsq_build_sketches: QJL sketches and gammas of the L1 and grouped keys
+    of k [B][Hkv][T][d].  Returns (l1_sketch, l1_gamma, l3_sketch, l3_gamma)."""
+    B, Hkv, T, d = k.shape
+    dtype = HSQ_F32 if k.dtype == torch.float32 else HSQ_BF16
+    n1 = l1_pos.shape[1]
+    ng = group_pos.shape[1] // group_n
+    dev = k.device
+    l1s = torch.empty((B, Hkv, n1, d // 8), dtype=torch.uint8, device=dev)
+    l1g = torch.empty((B, Hkv, n1), dtype=torch.float32, device=dev)
+    l3s = torch.empty((B, Hkv, ng, group_n, d // 8), dtype=torch.uint8, device=dev)
+    l3g = torch.empty((B, Hkv, ng, group_n), dtype=torch.float32, device=dev)
+    _check(lib().hsq_build_sketches(
+        _dev(k, None, "k"), dtype, B, Hkv, T, d, _dev(l1_pos, torch.int32, "l1_pos"), n1,
+        _dev(group_pos, torch.int32, "group_pos"), ng, group_n,
+        _dev(k_signs, torch.int32, "k_signs"), _dev(thr4, torch.float32, "thr4"),
+        _dev(cb4, torch.float32, "cb4"), _dev(S, torch.float32, "S"), l1s.data_ptr(),
+        l1g.data_ptr(), l3s.data_ptr(), l3g.data_ptr(), _stream()))
+    return l1s, l1g, l3s, l3g
 
 
 def decode_step_static(q, tiers, beta, k_signs, v_signs, cb4, cb3, scale=None,

@@ -558,6 +558,31 @@ int hsq_encode_qjl(const void* x, int x_dtype, int64_t n_vec, int d, int bits,
                    void* stream);
 
 /*
+ * hsq_build_sketches -- the QJL sketches and gammas of a layer's 4-bit token
+ * keys, for hsq_decode_step_qjl [ABL "Key contributions" 1: TQ-QKV adds the
+ * sketch on the key path].  Each key is encoded as hsq_encode_qjl encodes it
+ * (4 bits, its kv-head's signs and S), read straight from k at the tier
+ * plan's rows; the codes themselves are hsq_build_tiers' and are not
+ * written again.
+ *   k           [B][Hkv][T][d] in dtype (HSQ_F32 or HSQ_BF16)
+ *   l1_pos      int32 [B][n1], group_pos int32 [B][n_groups*group_n]
+ *               (device; the rows hsq_build_tiers was given)
+ *   k_signs     uint32 [Hkv][d/32];  thr4, cb4  4-bit codebook (device)
+ *   S           fp32 [Hkv][d][d]
+ *   outputs     l1_sketch [B][Hkv][n1][d/8], l1_gamma [B][Hkv][n1],
+ *               l3_sketch [B][Hkv][n_groups][group_n][d/8],
+ *               l3_gamma [B][Hkv][n_groups][group_n]
+ * Two launches per kv-head.  n1 == 0 or n_groups == 0 skip that tier.
+ * Errors: HSQ_ERR_ARG (null pointers, bad sizes, n1 + n_groups*group_n > T),
+ * HSQ_ERR_UNSUPPORTED (d, dtype, B*Hkv*T >= 2^32), HSQ_ERR_HIP.
+ */
+int hsq_build_sketches(const void* k, int dtype, int B, int Hkv, int T, int d,
+                       const int32_t* l1_pos, int n1, const int32_t* group_pos, int n_groups,
+                       int group_n, const uint32_t* k_signs, const float* thr4, const float* cb4,
+                       const float* S, uint8_t* l1_sketch, float* l1_gamma, uint8_t* l3_sketch,
+                       float* l3_gamma, void* stream);
+
+/*
  * hsq_qjl_logits -- TQ-QKV logits of n_q query rows against n_keys keys
  * encoded by hsq_encode_qjl (same signs, centroids and S):
  *   out[h][k] = scale * (r_k <R q_h, c[code_k]> +

@@ -25,7 +25,7 @@ from oracle import codebook as ocb
 from oracle import decode as odec
 from oracle import qjl as oqjl
 from oracle import tiers as otiers
-from tests.gpu_util import ATTN_REL_L2, TIE_BAND, rel_l2, signs_to_dev
+from tests.gpu_util import ATTN_REL_L2, CODE_BAND, TIE_BAND, rel_l2, signs_to_dev
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -168,3 +168,93 @@ def test_qjl_step_full_size_sampled_units():
     units = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.batch, 8),
                                               rng.integers(0, w.hkv, 8))]
     run_case(w, w.beta, units=sorted(set(units)))
+
+
+PROJ_BAND = 1e-5  # |(S u)_j| below which fp32 and fp64 may take other signs
+
+
+@pytest.mark.parametrize("case", ["q8_2k", "d64_g3_n8"])
+def test_build_sketches_parity(case):
+    # hsq_build_sketches straight from the raw keys at the tier plan's rows
+    # against the oracle's per-key encode: on every key with no coordinate
+    # within the code band of a threshold (so its codes are the oracle's),
+    # the sketch bits match except at projections within 1e-5 of zero and
+    # gamma matches to 1e-5 relative.  About 1% of the keys have such a
+    # coordinate (128 coordinates, 15 thresholds); they are left out
+    w = CASES[case]
+    print(f"[build sketches] {case}", flush=True)
+    k, _ = W.kv(w, 0, DEV)
+    ks, _ = W.signs(w.seed, 0, w.hkv, w.d)
+    S = W.sketch_matrices(w.seed, 0, w.hkv, w.d)
+    c4 = ocb.codebook_f32(w.d, 4)
+    plans = [hsq.tier_plan(w.T, w.n_sink, w.n_recent, W.marked(w, b), w.group_n)
+             for b in range(w.batch)]
+    l1 = to_dev(np.stack([p[0] for p in plans]))
+    gp = to_dev(np.stack([p[1].reshape(-1) for p in plans]))
+    g = [a.cpu().numpy() for a in hsq.build_sketches(
+        k, l1, gp, w.group_n, signs_to_dev(ks), to_dev(np.array(c4[1])), to_dev(np.array(c4[0])),
+        to_dev(S))]
+    m = w.d
+    n_rows = n_near = 0
+    for b in range(w.batch):
+        for h in range(w.hkv):
+            rows = np.concatenate([plans[b][0], plans[b][1].reshape(-1)])
+            o = oqjl.encode(k[b, h].cpu()[torch.from_numpy(rows)], ks[h], c4[1], c4[0], S[h])
+            gb = np.concatenate([oqjl.unpack_bits(g[0][b, h], m),
+                                 oqjl.unpack_bits(g[2][b, h].reshape(-1, m // 8), m)])
+            gg = np.concatenate([g[1][b, h], g[3][b, h].reshape(-1)])
+            # the oracle's codes of the same keys, against the GPU tier build's
+            # rule: a key whose coordinates all sit away from the thresholds
+            # has the same codes on both sides
+            yd = np.abs(o["y"][:, :, None] - np.asarray(c4[1], np.float64)[None, None, :]).min(2)
+            same = np.all(yd > CODE_BAND, axis=1)
+            n_rows += len(rows)
+            n_near += int((~same).sum())
+            bad = gb[same] != o["bits"][same]
+            if bad.any():
+                assert np.all(np.abs(o["proj"][same][bad]) < PROJ_BAND), f"unit {(b, h)}"
+            np.testing.assert_allclose(gg[same], o["gamma"][same], rtol=1e-5, atol=1e-30,
+                                       err_msg=f"unit {(b, h)}")
+    print(f"  {n_near} of {n_rows} keys near a threshold, left out", flush=True)
+    assert n_near < 0.05 * n_rows
+
+
+def test_qjl_step_from_raw_keys():
+    # the whole TQ-QKV path on the GPU from raw keys: hsq_build_tiers,
+    # hsq_build_sketches, hsq_decode_step_qjl; every unit against the
+    # oracle's own build, fed the GPU's selection
+    w = W.QWEN3_8B_8K.smaller(T=1500, batch=2, n_marked=20, beta=24)
+    k, v = W.kv(w, 0, DEV)
+    q = W.query(w, 0, DEV)
+    ks, vs = W.signs(w.seed, 0, w.hkv, w.d)
+    S = W.sketch_matrices(w.seed, 0, w.hkv, w.d)
+    c4, c3 = ocb.codebook_f32(w.d, 4), ocb.codebook_f32(w.d, 3)
+    plans = [hsq.tier_plan(w.T, w.n_sink, w.n_recent, W.marked(w, b), w.group_n)
+             for b in range(w.batch)]
+    l1 = to_dev(np.stack([p[0] for p in plans]))
+    gp = to_dev(np.stack([p[1].reshape(-1) for p in plans]))
+    dks, dvs = signs_to_dev(ks), signs_to_dev(vs)
+    t = hsq.build_tiers(k, v, l1, gp, w.group_n, dks, dvs, to_dev(np.array(c4[1])),
+                        to_dev(np.array(c3[1])))
+    sk = hsq.build_sketches(k, l1, gp, w.group_n, dks, to_dev(np.array(c4[1])),
+                            to_dev(np.array(c4[0])), to_dev(S))
+    out, idx = hsq.decode_step_qjl(q, t, w.beta, dks, dvs, to_dev(np.array(c4[0])),
+                                   to_dev(np.array(c3[0])), *sk, to_dev(S))
+    torch.cuda.synchronize()
+    go, gi = out.double().cpu().numpy(), idx.cpu().numpy()
+    scale = 1.0 / math.sqrt(w.d)
+    worst = 0.0
+    for b in range(w.batch):
+        for h in range(w.hkv):
+            l1p, g = plans[b]
+            kb, vb = k[b, h].cpu(), v[b, h].cpu()
+            u = otiers.build_unit(kb, vb, l1p, g, ks[h], vs[h], c4, c3)
+            osk = dict(oqjl.unit_sketches(kb, l1p, g, ks[h], c4[1], c4[0], S[h]), S=S[h])
+            deq = odec.dequant_unit(u, w.d, w.group_n, ks[h], vs[h], c4, c3)
+            qh = q[b, h * w.G:(h + 1) * w.G].double().cpu().numpy()
+            want = odec.hsq_attention_unit(qh, deq, u["l3"], gi[b, h], w.group_n, w.d, ks[h],
+                                           vs[h], c4, scale, qjl=osk)
+            e = rel_l2(go[b, h * w.G:(h + 1) * w.G], want)
+            worst = max(worst, e)
+            assert e < ATTN_REL_L2, f"unit {(b, h)}: rel L2 {e:.3e}"
+    print(f"  worst rel L2 {worst:.2e}", flush=True)
