@@ -39,7 +39,7 @@ def inputs(n, d, dtype, seed, student=False):
 def encode_both(xt, signs, S, bits):
     d = xt.shape[1]
     c, t = ocb.codebook_f32(d, bits)
-    f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    f = lambda a: torch.from_numpy(np.array(a)).to(DEV)
     g = hsq.encode_qjl(xt.to(DEV), bits, signs_to_dev(signs), f(t), f(c), f(S))
     o = qjl.encode(xt, signs, t, c, S)
     return [a.cpu().numpy() for a in g], o, (c, t)
@@ -102,7 +102,7 @@ def test_qjl_logits_parity(d, bits, n_q):
     rng = np.random.default_rng(n_q)
     q = rng.standard_normal((n_q, d)).astype(np.float32)
     scale = 1 / np.sqrt(d)
-    f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    f = lambda a: torch.from_numpy(np.array(a)).to(DEV)
     got = hsq.qjl_logits(f(q), bits, f(codes), f(norms), f(sketch), f(gamma), signs_to_dev(signs),
                          f(c), f(S), float(scale)).cpu().numpy()
     want = qjl.logits_qjl(q, o["codes"], norms, o["bits"], gamma, signs, c, S, scale)
@@ -128,7 +128,7 @@ def test_codec_workload_head():
     rng = np.random.default_rng(11)
     S = rng.standard_normal((c.d, c.d)).astype(np.float32)
     cb, t = ocb.codebook_f32(c.d, 4)
-    f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    f = lambda a: torch.from_numpy(np.array(a)).to(DEV)
     g = [a.cpu().numpy() for a in hsq.encode_qjl(x, 4, signs_to_dev(ks[3]), f(t), f(cb), f(S))]
     rows = np.sort(rng.choice(c.tokens, size=2000, replace=False))
     o = qjl.encode(x[torch.from_numpy(rows).to(DEV)].cpu(), ks[3], t, cb, S)

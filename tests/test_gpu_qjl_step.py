@@ -33,7 +33,7 @@ NAMES = ("l1k", "l1k_n", "l1v", "l1v_n", "l2k", "l2k_n", "l2v", "l2v_n", "l3")
 
 
 def to_dev(a, dtype=None):
-    t = torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    t = torch.from_numpy(np.array(a)).to(DEV)
     return t if dtype is None else t.to(dtype)
 
 

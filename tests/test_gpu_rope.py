@@ -34,7 +34,7 @@ def archive(rng, n, d, bits, n_rot):
 
 
 def gpu(codes, norms, bits, d, signs, c32, pos, per_rot, n_rot, out, base=BASE):
-    f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    f = lambda a: torch.from_numpy(np.array(a)).to(DEV)
     return hsq.decode_rope(f(codec.pack(codes, bits)), f(norms), bits, d,
                            None if signs is None else signs_to_dev(signs), f(c32),
                            f(pos.astype(np.int32)), base, vecs_per_rot=per_rot, n_rot=n_rot,
@@ -91,7 +91,7 @@ def test_position_zero_is_the_plain_decode(d):
     rng = np.random.default_rng(5)
     signs, codes, norms = archive(rng, 777, d, 4, 1)
     c32, _ = ocb.codebook_f32(d, 4)
-    f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    f = lambda a: torch.from_numpy(np.array(a)).to(DEV)
     for out in (torch.float32, torch.bfloat16):
         a = hsq.decode(f(codec.pack(codes, 4)), f(norms), 4, d, signs_to_dev(signs), f(c32),
                        out_dtype=out)
