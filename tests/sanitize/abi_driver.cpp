@@ -282,6 +282,37 @@ void run_errors() {
   expect("qjl logits d=32", hsq_qjl_logits(f32, 4, 32, 4, u8, f32, u8, f32, 10, u32, f32, f32,
                                            0.1f, f32, nullptr),
          HSQ_ERR_UNSUPPORTED);
+
+  // pre-RoPE and TQ-QKV steps, sketch build
+  const size_t plain = hsq_workspace_bytes(2, 32, 8, 128, 10, 10, 4, 16);
+  const size_t pre = hsq_prerope_workspace_bytes(2, 32, 8, 128, 10, 10, 4, 16);
+  expect("prerope workspace size", pre >= plain + size_t(2) * 8 * 4 * 16 * 128 * 2 ? 0 : 1, 0);
+  void* wsa = reinterpret_cast<void*>(256);
+  auto prestep = [&](const int32_t* pos, double base, size_t wb) {
+    return hsq_decode_step_prerope(f32, 2, 32, 8, 128, u8, f32, u8, f32, 10, u8, f32, u8, f32, 10,
+                                   u8, 16, 4, 0, u32, u32, f32, f32, 0.1f, 0.f, pos, base, nullptr,
+                                   wsa, wb, f32, nullptr);
+  };
+  expect("prerope null positions", prestep(nullptr, 1e6, pre), HSQ_ERR_ARG, "group_pos");
+  expect("prerope base 0", prestep(i32, 0.0, pre), HSQ_ERR_ARG, "rope_base");
+  expect("prerope small workspace", prestep(i32, 1e6, plain), HSQ_ERR_WORKSPACE);
+  auto qstep = [&](const uint8_t* l1s, const float* l3g, const float* S) {
+    return hsq_decode_step_qjl(f32, 2, 32, 8, 128, u8, f32, u8, f32, 10, u8, f32, u8, f32, 10, u8,
+                               16, 4, 0, u32, u32, f32, f32, 0.1f, 0.f, l1s, f32, u8, l3g, S,
+                               nullptr, wsa, plain, f32, nullptr);
+  };
+  expect("qjl step null S", qstep(u8, f32, nullptr), HSQ_ERR_ARG, "S");
+  expect("qjl step null L1 sketch", qstep(nullptr, f32, f32), HSQ_ERR_ARG, "L1");
+  expect("qjl step null archive gamma", qstep(u8, nullptr, f32), HSQ_ERR_ARG, "archive");
+  expect("sketches n1+ng*N>T", hsq_build_sketches(p, 0, 1, 1, 40, 128, i32, 16, i32, 4, 8, u32,
+                                                   f32, f32, f32, u8, f32, u8, f32, nullptr),
+         HSQ_ERR_ARG);
+  expect("sketches d=96", hsq_build_sketches(p, 0, 1, 1, 64, 96, i32, 16, i32, 4, 8, u32, f32,
+                                              f32, f32, u8, f32, u8, f32, nullptr),
+         HSQ_ERR_UNSUPPORTED);
+  expect("sketches null S", hsq_build_sketches(p, 0, 1, 1, 64, 128, i32, 16, i32, 4, 8, u32, f32,
+                                                f32, nullptr, u8, f32, u8, f32, nullptr),
+         HSQ_ERR_ARG, "null");
   std::printf("errors %d\n", g_checked);
 }
 

@@ -109,6 +109,7 @@ CASES = {
     "q8_2k": (W.QWEN3_8B_8K.smaller(T=2048, batch=2, n_marked=41), None),
     "q14_1k_b4_n8": (W.QWEN3_14B_16K.smaller(T=1100, batch=4, n_marked=10, beta=9), None),
     "d64_g3_n8": (W.TINY.smaller(d=64, hq=6, hkv=2, group_n=8, T=700, beta=7), None),
+    "d64_n16": (W.TINY.smaller(d=64, hq=8, hkv=2, group_n=16, T=900, beta=5), None),
 }
 
 
