@@ -1796,14 +1796,15 @@ __device__ __forceinline__ TokBufs tok_bufs(const TokArgs& a, int unit) {
   const size_t kdu = (size_t)a.beta * N * D;  // fp16 values per unit
   B.kd = make_rsrc(a.kdense ? a.kdense + (size_t)unit * kdu : nullptr,
                    a.kdense ? (uint32_t)(kdu * 2) : 0u);
-  const bool q = a.l1_sk != nullptr;
+  // each sketch array on its own: a tier without entries may pass null
   const size_t n3 = (size_t)a.ng * N;  // archive keys per unit
-  B.l1sk = make_rsrc(q ? a.l1_sk + o1 * (D / 8) : nullptr, q ? (uint32_t)a.n1 * (D / 8) : 0u);
-  B.l1gm = make_rsrc(q ? a.l1_gam + o1 : nullptr, q ? (uint32_t)a.n1 * 4 : 0u);
-  B.l3sk = make_rsrc(q ? a.l3_sk + (size_t)unit * a.ngs * N * (D / 8) : nullptr,
-                     q ? (uint32_t)(n3 * (D / 8)) : 0u);
-  B.l3gm = make_rsrc(q ? a.l3_gam + (size_t)unit * a.ngs * N : nullptr,
-                     q ? (uint32_t)(n3 * 4) : 0u);
+  B.l1sk = make_rsrc(a.l1_sk ? a.l1_sk + o1 * (D / 8) : nullptr,
+                     a.l1_sk ? (uint32_t)a.n1 * (D / 8) : 0u);
+  B.l1gm = make_rsrc(a.l1_gam ? a.l1_gam + o1 : nullptr, a.l1_gam ? (uint32_t)a.n1 * 4 : 0u);
+  B.l3sk = make_rsrc(a.l3_sk ? a.l3_sk + (size_t)unit * a.ngs * N * (D / 8) : nullptr,
+                     a.l3_sk ? (uint32_t)(n3 * (D / 8)) : 0u);
+  B.l3gm = make_rsrc(a.l3_gam ? a.l3_gam + (size_t)unit * a.ngs * N : nullptr,
+                     a.l3_gam ? (uint32_t)(n3 * 4) : 0u);
   return B;
 }
 

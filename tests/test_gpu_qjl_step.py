@@ -140,6 +140,18 @@ def test_qjl_step_beta_edges(beta):
     run_case(W.TINY, beta)
 
 
+@pytest.mark.parametrize("case", ["no_l1", "no_groups"])
+def test_qjl_step_empty_tiers(case):
+    # a tier without entries passes null sketches: every position grouped
+    # (the archive's corrections alone), or everything in L1
+    base = W.QWEN3_8B_8K.smaller(T=1024, batch=2, n_marked=12)
+    if case == "no_l1":
+        w = base.smaller(n_sink=0, n_recent=0, n_marked=0, T=1024)
+    else:
+        w = base.smaller(T=60, n_marked=0)
+    run_case(w, w.beta)
+
+
 def test_qjl_step_mean_and_bias():
     w = W.QWEN3_14B_16K.smaller(T=1500, batch=2, n_marked=15, beta=11)
     run_case(w, w.beta, agg="mean", bias=0.75)
