@@ -495,6 +495,11 @@ extern "C" int hsq_decode_step_qjl(const float* q, int B, int Hq, int Hkv, int d
     return fail(HSQ_ERR_ARG, std::string(fn) + ": null L1 sketch or gamma");
   if (n_groups > 0 && (!l3_sketch || !l3_gamma))
     return fail(HSQ_ERR_ARG, std::string(fn) + ": null archive sketch or gamma");
+  if (reinterpret_cast<uintptr_t>(S) % 16 || reinterpret_cast<uintptr_t>(l1_sketch) % 4 ||
+      reinterpret_cast<uintptr_t>(l3_sketch) % 4 || reinterpret_cast<uintptr_t>(l1_gamma) % 4 ||
+      reinterpret_cast<uintptr_t>(l3_gamma) % 4)
+    return fail(HSQ_ERR_ARG, std::string(fn) +
+                                 ": S must be 16-byte aligned, sketches and gammas 4-byte aligned");
   const int b = beta < n_groups ? beta : n_groups;
   StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, b};
   Workspace w;
@@ -718,6 +723,8 @@ extern "C" int hsq_build_sketches(const void* k, int dtype, int B, int Hkv, int 
     return fail(HSQ_ERR_ARG, std::string(fn) + ": null L1 pointer");
   if (n_groups > 0 && (!group_pos || !l3_sketch || !l3_gamma))
     return fail(HSQ_ERR_ARG, std::string(fn) + ": null archive pointer");
+  if (reinterpret_cast<uintptr_t>(l1_sketch) % 2 || reinterpret_cast<uintptr_t>(l3_sketch) % 2)
+    return fail(HSQ_ERR_ARG, std::string(fn) + ": sketch arrays must be 2-byte aligned");
   const hipStream_t st = as_stream(stream);
   for (int h = 0; h < Hkv; ++h) {
     for (int tier = 0; tier < 2; ++tier) {

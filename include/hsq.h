@@ -346,12 +346,13 @@ int hsq_decode_step_prerope(const float* q, int B, int Hq, int Hkv, int d, const
  *               (the L1 keys in L1 order)
  *   l3_sketch   uint8 [B][Hkv][n_groups][group_n][d/8], l3_gamma fp32
  *               [B][Hkv][n_groups][group_n] (the grouped keys in group order)
- *   S           fp32 [Hkv][d][d], row j = sketch direction j of kv-head h
+ *   S           fp32 [Hkv][d][d], row j = sketch direction j of kv-head h,
+ *               16-byte aligned (sketch arrays and gammas 4-byte aligned)
  *   workspace   hsq_workspace_bytes(...) bytes, as hsq_decode_step
  *   other arguments as in hsq_decode_step
- * Errors: as hsq_decode_step, plus HSQ_ERR_ARG for a null S, or null
- * sketches or gammas of a tier that has entries, HSQ_ERR_UNSUPPORTED when
- * G * n_groups > 12288.
+ * Errors: as hsq_decode_step, plus HSQ_ERR_ARG for a null or misaligned S,
+ * null or misaligned sketches or gammas of a tier that has entries,
+ * HSQ_ERR_UNSUPPORTED when G * n_groups > 12288.
  */
 int hsq_decode_step_qjl(const float* q, int B, int Hq, int Hkv, int d, const uint8_t* l1k,
                         const float* l1k_n, const uint8_t* l1v, const float* l1v_n, int n_l1,
@@ -573,7 +574,9 @@ int hsq_encode_qjl(const void* x, int x_dtype, int64_t n_vec, int d, int bits,
  *               l3_sketch [B][Hkv][n_groups][group_n][d/8],
  *               l3_gamma [B][Hkv][n_groups][group_n]
  * Two launches per kv-head.  n1 == 0 or n_groups == 0 skip that tier.
- * Errors: HSQ_ERR_ARG (null pointers, bad sizes, n1 + n_groups*group_n > T),
+ * The sketch arrays are written 2 bytes at a time (2-byte aligned).
+ * Errors: HSQ_ERR_ARG (null pointers, bad sizes, n1 + n_groups*group_n > T,
+ * misaligned sketch arrays),
  * HSQ_ERR_UNSUPPORTED (d, dtype, B*Hkv*T >= 2^32), HSQ_ERR_HIP.
  */
 int hsq_build_sketches(const void* k, int dtype, int B, int Hkv, int T, int d,

@@ -134,6 +134,9 @@ def test_argument_errors_are_reported_without_launch():
     assert "S" in lib.hsq_last_error().decode()
     assert qjl_step(l1s=None) == -1
     assert qjl_step(l3g=None) == -1
+    assert qjl_step(S=ctypes.c_void_p(20)) == -1
+    assert "aligned" in lib.hsq_last_error().decode()
+    assert qjl_step(l1s=ctypes.c_void_p(18)) == -1
     assert lib.hsq_gather_l3_ordered(p, 1088, 1, 1, 4, p, 2, p, None, 0, None) == -1
     assert "turn" in lib.hsq_last_error().decode()
     assert lib.hsq_gather_l3_ordered(p, 1088, 1, 1, 4, p, 2, p, ctypes.c_void_p(18), 0, None) == -1
