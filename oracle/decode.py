@@ -19,10 +19,15 @@ Readings taken:
   in ascending group order; beta is clamped to [0, ng].
 * "Rotated back to their semantic positions" is the inverse TurboQuant
   rotation, i.e. dequantisation; the archive holds the same (post-RoPE) keys
-  the model caches, so no positional re-rotation happens.
+  the model caches, so no positional re-rotation happens.  The other reading
+  (an archive of keys before RoPE, each fetched key rotated to its token's
+  position) is the group_pos variant of hsq_attention_unit.
 * Each unfetched summary is one softmax entry with logit scale * q . k_hat_g
   (+ summary_bias, default 0); one joint softmax over all entries;
   scale defaults to 1 / sqrt(d).
+* TQ-QKV token keys (the qjl variant of hsq_attention_unit): the 4-bit token
+  keys carry QJL residual sketches and their logits the QJL estimate; the
+  summaries carry none.
 """
 import numpy as np
 
