@@ -270,3 +270,65 @@ def test_qjl_step_from_raw_keys():
             worst = max(worst, e)
             assert e < ATTN_REL_L2, f"unit {(b, h)}: rel L2 {e:.3e}"
     print(f"  worst rel L2 {worst:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("variant", ["qjl", "prerope"])
+def test_variant_steps_graph_replays_match_eager(variant):
+    # the TQ-QKV step (two launches) and the pre-RoPE step (three launches,
+    # the fetched-key rows handed over in the workspace) captured in a graph:
+    # three replays with eager work and a scrambled workspace between them
+    # equal the eager call bit for bit
+    w = W.QWEN3_14B_16K.smaller(T=2048, batch=4, n_marked=20)
+    print(f"graph replays: {variant}", flush=True)
+    k, v = W.kv(w, 0, DEV)
+    q = W.query(w, 0, DEV)
+    ks, vs = W.signs(w.seed, 0, w.hkv, w.d)
+    c4, c3 = ocb.codebook_f32(w.d, 4), ocb.codebook_f32(w.d, 3)
+    plans = [hsq.tier_plan(w.T, w.n_sink, w.n_recent, W.marked(w, b), w.group_n)
+             for b in range(w.batch)]
+    l1 = to_dev(np.stack([p[0] for p in plans]))
+    gp = to_dev(np.stack([p[1].reshape(-1) for p in plans]))
+    dks, dvs = signs_to_dev(ks), signs_to_dev(vs)
+    cb4, cb3 = to_dev(np.array(c4[0])), to_dev(np.array(c3[0]))
+    t = hsq.build_tiers(k, v, l1, gp, w.group_n, dks, dvs, to_dev(np.array(c4[1])),
+                        to_dev(np.array(c3[1])))
+    beta = min(w.beta, t.ng)
+    out = torch.empty((w.batch, w.hq, w.d), dtype=torch.float32, device=DEV)
+    idx = torch.empty((w.batch, w.hkv, beta), dtype=torch.int32, device=DEV)
+    if variant == "qjl":
+        S = to_dev(W.sketch_matrices(w.seed, 0, w.hkv, w.d))
+        sk = hsq.build_sketches(k, l1, gp, w.group_n, dks, to_dev(np.array(c4[1])), cb4, S)
+        ws = hsq.make_workspace(w.batch, w.hq, w.hkv, w.d, t.n1, t.ng, beta, w.group_n, DEV)
+
+        def step():
+            hsq.decode_step_qjl(q, t, w.beta, dks, dvs, cb4, cb3, *sk, S, ws=ws, out=out, idx=idx)
+    else:
+        ws = hsq.Workspace(hsq.prerope_workspace_bytes(w.batch, w.hq, w.hkv, w.d, t.n1, t.ng,
+                                                       beta, w.group_n), DEV)
+
+        def step():
+            hsq.decode_step_prerope(q, t, w.beta, dks, dvs, cb4, cb3, gp, 1e6, ws=ws, out=out,
+                                    idx=idx)
+
+    step()
+    torch.cuda.synchronize()
+    out0, idx0 = out.clone(), idx.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        step()
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            step()
+    for r in range(3):
+        out.fill_(float("nan"))
+        idx.fill_(-1)
+        ws.buf.fill_(0x5A)  # the workspace's contents must not matter
+        junk = torch.randn(1 << 20, device=DEV).sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, idx0), f"replay {r}: selection differs"
+        assert torch.equal(out, out0), f"replay {r}: output differs"
+        del junk
