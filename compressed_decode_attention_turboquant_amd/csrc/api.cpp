@@ -409,6 +409,58 @@ extern "C" size_t hsq_prerope_workspace_bytes(int B, int Hq, int Hkv, int d, int
   return prerope_rows_off(plan_workspace(s)) + prerope_rows_bytes(s);
 }
 
+extern "C" int hsq_step_attend_prerope(const float* q, int B, int Hq, int Hkv, int d,
+                                       const uint8_t* l1k, const float* l1k_n,
+                                       const uint8_t* l1v, const float* l1v_n, int n_l1,
+                                       int n_groups, const uint8_t* l3, int group_n,
+                                       int l3_staged, int beta, const uint32_t* k_signs,
+                                       const uint32_t* v_signs, const float* cb4, float scale,
+                                       const int32_t* group_pos, double rope_base,
+                                       void* workspace, size_t ws_bytes, float* out,
+                                       void* stream) {
+  const char* fn = "hsq_step_attend_prerope";
+  int rc = check_step_shape(fn, B, Hq, Hkv, d, n_l1, n_groups, group_n, beta);
+  if (rc) return rc;
+  if (!q || !out || !k_signs || !v_signs || !cb4)
+    return fail(HSQ_ERR_ARG, std::string(fn) + ": null pointer");
+  if (n_l1 > 0 && (!l1k || !l1k_n || !l1v || !l1v_n))
+    return fail(HSQ_ERR_ARG, std::string(fn) + ": null L1 pointer");
+  const int b = beta < n_groups ? beta : n_groups;
+  if (b > 0 && !l3) return fail(HSQ_ERR_ARG, std::string(fn) + ": null L3 pointer");
+  if (n_groups > 0 && !group_pos) return fail(HSQ_ERR_ARG, std::string(fn) + ": null group_pos");
+  if (!(rope_base > 0.0) || !std::isfinite(rope_base))
+    return fail(HSQ_ERR_ARG, std::string(fn) + ": rope_base must be finite and > 0");
+  StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, b};
+  Workspace w;
+  if ((rc = step_common(fn, s, workspace, ws_bytes, w))) return rc;
+  if (s.n_groups > 0 && !route_lds_ok(s))
+    return fail(HSQ_ERR_UNSUPPORTED,
+                std::string(fn) + ": G * n_groups exceeds 12288 (router logits beyond LDS)");
+  const size_t kd_off = prerope_rows_off(w);
+  if (ws_bytes < kd_off + prerope_rows_bytes(s))
+    return fail(HSQ_ERR_WORKSPACE,
+                std::string(fn) + ": workspace smaller than hsq_prerope_workspace_bytes()");
+  StepTensors t{};
+  t.q = q; t.l1k = l1k; t.l1k_n = l1k_n; t.l1v = l1v; t.l1v_n = l1v_n; t.l3 = l3;
+  t.l3_staged = l3_staged ? 1 : 0; t.k_signs = k_signs; t.v_signs = v_signs; t.cb4 = cb4;
+  t.scale = scale; t.out = out;
+  char* ws = static_cast<char*>(workspace);
+  const hipStream_t st = as_stream(stream);
+  const int32_t* idx = reinterpret_cast<const int32_t*>(ws + w.idx_off);
+  uint16_t* rows = reinterpret_cast<uint16_t*>(ws + kd_off);
+  if (b > 0) {
+    RopeKeysJob j{};
+    j.l3 = l3; j.unit_recs = n_groups; j.idx = idx; j.group_pos = group_pos;
+    j.pos_per_seq = (int64_t)n_groups * group_n; j.units = B * Hkv; j.Hkv = Hkv; j.d = d;
+    j.n_groups = n_groups; j.group_n = group_n; j.beta = b; j.k_signs = k_signs; j.cb4 = cb4;
+    j.rope_base = rope_base; j.out = rows; j.staged = t.l3_staged;
+    if ((rc = check_hip(launch_rope_keys(j, st), "hsq_step_attend_prerope fetched keys")))
+      return rc;
+  }
+  return check_hip(launch_attn_prerope(s, t, w, ws, idx, b > 0 ? rows : nullptr, st),
+                   "hsq_step_attend_prerope attention");
+}
+
 extern "C" int hsq_decode_step_prerope(const float* q, int B, int Hq, int Hkv, int d,
                                        const uint8_t* l1k, const float* l1k_n, const uint8_t* l1v,
                                        const float* l1v_n, int n_l1, const uint8_t* l2k,
@@ -436,40 +488,18 @@ extern "C" int hsq_decode_step_prerope(const float* q, int B, int Hq, int Hkv, i
   if (s.n_groups > 0 && !route_lds_ok(s))
     return fail(HSQ_ERR_UNSUPPORTED,
                 std::string(fn) + ": G * n_groups exceeds 12288 (router logits beyond LDS)");
-  const size_t kd_off = prerope_rows_off(w);
-  if (ws_bytes < kd_off + prerope_rows_bytes(s))
+  if (ws_bytes < prerope_rows_off(w) + prerope_rows_bytes(s))
     return fail(HSQ_ERR_WORKSPACE,
                 std::string(fn) + ": workspace smaller than hsq_prerope_workspace_bytes()");
-  StepTensors t{};
-  t.q = q; t.l1k = l1k; t.l1k_n = l1k_n; t.l1v = l1v; t.l1v_n = l1v_n;
-  t.l2k = l2k; t.l2k_n = l2k_n; t.l2v = l2v; t.l2v_n = l2v_n; t.l3 = l3; t.l3_staged = 0;
-  t.k_signs = k_signs; t.v_signs = v_signs; t.cb4 = cb4; t.cb3 = cb3; t.scale = scale;
-  t.summary_bias = summary_bias; t.agg = agg; t.out = out;
-  char* ws = static_cast<char*>(workspace);
-  const hipStream_t st = as_stream(stream);
-  int32_t* idx = reinterpret_cast<int32_t*>(ws + w.idx_off);
-  uint16_t* rows = reinterpret_cast<uint16_t*>(ws + kd_off);
-  if (s.n_groups > 0) {
-    if ((rc = check_hip(launch_route(s, t, w, ws, ROUTE_TOPK | ROUTE_PARTIALS, nullptr, nullptr,
-                                     idx, st),
-                        "hsq_decode_step_prerope route")))
-      return rc;
-    RopeKeysJob j{};
-    j.l3 = l3; j.unit_recs = n_groups; j.idx = idx; j.group_pos = group_pos;
-    j.pos_per_seq = (int64_t)n_groups * group_n; j.units = B * Hkv; j.Hkv = Hkv; j.d = d;
-    j.n_groups = n_groups; j.group_n = group_n; j.beta = b; j.k_signs = k_signs; j.cb4 = cb4;
-    j.rope_base = rope_base; j.out = rows;
-    if ((rc = check_hip(launch_rope_keys(j, st), "hsq_decode_step_prerope fetched keys")))
-      return rc;
-  }
-  if ((rc = check_hip(launch_attn_prerope(s, t, w, ws, idx, b > 0 ? rows : nullptr, st),
-                      "hsq_decode_step_prerope attention")))
+  // the route of the two-launch form (selection and summary partials into
+  // the workspace), then the pre-RoPE attend over the archive in place
+  if ((rc = hsq_step_route(q, B, Hq, Hkv, d, n_l1, l2k, l2k_n, l2v, l2v_n, n_groups, group_n, beta,
+                           agg, k_signs, cb3, scale, summary_bias, topk_idx, workspace, ws_bytes,
+                           stream)))
     return rc;
-  if (topk_idx && b > 0)
-    return check_hip(hipMemcpyAsync(topk_idx, idx, sizeof(int32_t) * (size_t)B * Hkv * b,
-                                    hipMemcpyDeviceToDevice, st),
-                     "hsq_decode_step_prerope topk copy");
-  return HSQ_OK;
+  return hsq_step_attend_prerope(q, B, Hq, Hkv, d, l1k, l1k_n, l1v, l1v_n, n_l1, n_groups, l3,
+                                 group_n, 0, beta, k_signs, v_signs, cb4, scale, group_pos,
+                                 rope_base, workspace, ws_bytes, out, stream);
 }
 
 extern "C" int hsq_decode_step_qjl(const float* q, int B, int Hq, int Hkv, int d,

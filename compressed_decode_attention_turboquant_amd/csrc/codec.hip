@@ -342,8 +342,9 @@ __global__ __launch_bounds__(kWG) void rope_keys_kernel(RopeKeysJob j) {
       const int g0 = j.idx[us];
       ok[k] = g0 >= 0 && g0 < j.n_groups;
       const uint32_t g = ok[k] ? (uint32_t)g0 : 0u;
-      codes[k] = *reinterpret_cast<const uint32_t*>(
-          j.l3 + ((uint64_t)u * j.unit_recs + g) * rec + t * CB + 4 * sub);
+      // the record: in place by group, or gathered by slot (staged)
+      const uint64_t r = j.staged ? (uint64_t)us : (uint64_t)u * j.unit_recs + g;
+      codes[k] = *reinterpret_cast<const uint32_t*>(j.l3 + r * rec + t * CB + 4 * sub);
       p[k] = j.group_pos[(uint64_t)b * j.pos_per_seq + g * N + t];
       sbyte[k] = sign_byte(j.k_signs + h * (D / 32), sub);
     }

@@ -79,6 +79,7 @@ struct RopeKeysJob {
   const float* cb4;         // 16 centroids
   double rope_base;
   uint16_t* out;            // fp16 bits [units][beta][group_n][d]
+  int staged;               // records gathered by slot: [units][beta] (unit_recs unused)
 };
 hipError_t launch_rope_keys(const RopeKeysJob& j, hipStream_t s);
 

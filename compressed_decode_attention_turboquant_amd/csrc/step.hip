@@ -3472,8 +3472,7 @@ hipError_t launch_attn(const StepShape& s, const StepTensors& t, const Workspace
 hipError_t launch_attn_prerope(const StepShape& s, const StepTensors& t, const Workspace& w,
                                char* ws, const int32_t* idx, const uint16_t* kdense,
                                hipStream_t st) {
-  if (!step_limits_ok(s) || (s.n_groups > 0 && !route_lds_ok(s)) || t.l3_staged ||
-      (s.beta > 0 && !kdense))
+  if (!step_limits_ok(s) || (s.n_groups > 0 && !route_lds_ok(s)) || (s.beta > 0 && !kdense))
     return hipErrorInvalidValue;
   return s.d == 128 ? token_d<128, TokTileK>(s, t, w, ws, idx, kdense, st)
                     : token_d<64, TokTileK>(s, t, w, ws, idx, kdense, st);

@@ -48,6 +48,9 @@ _SIGNATURES = {
                              _vp, _vp, _vp, _vp, _sz, _vp, _vp], _i),
     "hsq_build_sketches": ([_vp, _i, _i, _i, _i, _i, _vp, _i, _vp, _i, _i, _vp, _vp, _vp, _vp,
                             _vp, _vp, _vp, _vp, _vp], _i),
+    "hsq_step_attend_prerope": ([_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _vp, _i, _i,
+                                 _i, _vp, _vp, _vp, _f, _vp, _c.c_double, _vp, _sz, _vp, _vp],
+                                _i),
     "hsq_decode_step_static": ([_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp,
                                 _i, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _f, _f, _vp, _vp, _vp],
                                _i),
@@ -510,6 +513,25 @@ def step_attend(q, tiers, beta, k_signs, v_signs, cb4, ws, out, scale=None, l3=N
         int(l3_staged), beta, _dev(k_signs, torch.int32, "k_signs"),
         _dev(v_signs, torch.int32, "v_signs"), _dev(cb4, torch.float32, "cb4"), scale, ws.ptr,
         ws.nbytes, _dev(out, torch.float32, "out"), stream if stream is not None else _stream()))
+    return out
+
+
+def step_attend_prerope(q, tiers, beta, k_signs, v_signs, cb4, group_pos, rope_base, ws, out,
+                        scale=None, l3=None, l3_staged=False, stream=None):
+    """Second half of the pre-RoPE step (after step_route on ws, a workspace
+    of prerope_workspace_bytes): RoPE on the fetched keys, then attention."""
+    B, Hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    l3p = l3 if l3 is not None else tiers.l3.data_ptr()
+    _check(lib().hsq_step_attend_prerope(
+        _dev(q, torch.float32, "q"), B, Hq, tiers.Hkv, d, _dev(tiers.l1k), _dev(tiers.l1k_n),
+        _dev(tiers.l1v), _dev(tiers.l1v_n), tiers.n1, tiers.ng, l3p, tiers.group_n,
+        int(l3_staged), beta, _dev(k_signs, torch.int32, "k_signs"),
+        _dev(v_signs, torch.int32, "v_signs"), _dev(cb4, torch.float32, "cb4"), scale,
+        _dev(group_pos, torch.int32, "group_pos") if tiers.ng > 0 else None, float(rope_base),
+        ws.ptr, ws.nbytes, _dev(out, torch.float32, "out"),
+        stream if stream is not None else _stream()))
     return out
 
 

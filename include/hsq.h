@@ -301,7 +301,8 @@ int hsq_decode_step(const float* q, int B, int Hq, int Hkv, int d, const uint8_t
  * coordinate f < d/2 with f + d/2 as hsq_decode_rope does].  L1 and L2 hold
  * keys with RoPE applied, as for hsq_decode_step; the L3 records hold the
  * keys without it (values are never rotated).  The route, the selection, the
- * summaries and L1 are as in hsq_decode_step (two launches); between them a
+ * summaries and L1 are as in hsq_decode_step (hsq_step_route, then
+ * hsq_step_attend_prerope over the archive in place); between them a
  * third launch takes every fetched record's 4-bit key codes back to the
  * model's domain, rotates each token to its position, rotates the result
  * forward again into fp16 rows in the workspace, and the attention multiplies
@@ -322,6 +323,22 @@ int hsq_decode_step(const float* q, int B, int Hq, int Hkv, int d, const uint8_t
  */
 size_t hsq_prerope_workspace_bytes(int B, int Hq, int Hkv, int d, int n_l1, int n_groups,
                                    int beta, int group_n);
+/*
+ * hsq_step_attend_prerope -- the second half of the pre-RoPE step, after
+ * hsq_step_route on the same workspace (hsq_prerope_workspace_bytes bytes):
+ * the fetched keys rotated to their positions, then the attend.  With
+ * l3_staged != 0, l3 holds the fetched records gathered by hsq_gather_l3
+ * ([B][Hkv][beta] records, the CPU-RAM archive of the pages read over
+ * PCIe); else the whole archive in device memory.  The positions come from
+ * the selection hsq_step_route left in the workspace.  Arguments and errors
+ * as hsq_step_attend plus group_pos and rope_base as below.
+ */
+int hsq_step_attend_prerope(const float* q, int B, int Hq, int Hkv, int d, const uint8_t* l1k,
+                            const float* l1k_n, const uint8_t* l1v, const float* l1v_n, int n_l1,
+                            int n_groups, const uint8_t* l3, int group_n, int l3_staged, int beta,
+                            const uint32_t* k_signs, const uint32_t* v_signs, const float* cb4,
+                            float scale, const int32_t* group_pos, double rope_base,
+                            void* workspace, size_t ws_bytes, float* out, void* stream);
 int hsq_decode_step_prerope(const float* q, int B, int Hq, int Hkv, int d, const uint8_t* l1k,
                             const float* l1k_n, const uint8_t* l1v, const float* l1v_n, int n_l1,
                             const uint8_t* l2k, const float* l2k_n, const uint8_t* l2v,

@@ -326,3 +326,43 @@ def test_two_launches_beyond_on_chip_logits_match_the_split_step():
     torch.cuda.synchronize()
     assert torch.equal(idx, idx_one)
     assert torch.equal(out_two, out_one)
+
+
+def test_host_archive_prerope_step_matches_the_device_archive_prerope_step():
+    # the pages' CPU-RAM archive with keys before RoPE: route, gather over
+    # PCIe from pinned host memory, the fetched keys rotated to their
+    # positions from the staged records, attend; against the pre-RoPE step
+    # over the archive in device memory (the same kernels over the same
+    # bytes: identical outputs), and sampled units against the oracle's
+    # pre-RoPE reading
+    from oracle import decode as odec
+    w = W.QWEN3_8B_32K.smaller(layers=1, T=8192, batch=4, n_marked=80)
+    print(f"[host archive, pre-RoPE] T={w.T} B={w.batch} beta={w.beta}", flush=True)
+    sc = Scenario(w)
+    t = sc.tiers
+    rec, beta = t.rec_bytes, min(w.beta, t.ng)
+    gp = torch.from_numpy(np.stack([p[1].reshape(-1) for p in sc.plans])).to(DEV)
+    arch = hsq.HostArchive(t.l3.numel())
+    arch.host.copy_(t.l3.reshape(-1).cpu())
+    ws = hsq.Workspace(hsq.prerope_workspace_bytes(w.batch, w.hq, w.hkv, w.d, t.n1, t.ng, beta,
+                                                   w.group_n), DEV)
+    idx = torch.empty((w.batch, w.hkv, beta), dtype=torch.int32, device=DEV)
+    staging = torch.empty((w.batch, w.hkv, beta, rec), dtype=torch.uint8, device=DEV)
+    out_host = torch.empty((w.batch, w.hq, w.d), dtype=torch.float32, device=DEV)
+    hsq.step_route(sc.q, t, w.beta, sc.dks, sc.cb3, ws, idx=idx)
+    hsq.gather_l3(arch.dev_ptr, rec, w.batch, w.hkv, t.ng, idx, staging)
+    hsq.step_attend_prerope(sc.q, t, w.beta, sc.dks, sc.dvs, sc.cb4, gp, 1e6, ws, out_host,
+                            l3=staging.data_ptr(), l3_staged=True)
+    out_dev, idx_dev = hsq.decode_step_prerope(sc.q, t, w.beta, sc.dks, sc.dvs, sc.cb4, sc.cb3,
+                                               gp, 1e6)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_dev)
+    assert torch.equal(out_host, out_dev)
+    go = out_host.double().cpu().numpy()
+    for (b, h) in [(0, 0), (3, 6)]:
+        unit, deq = sc.oracle_unit(b, h)
+        want = odec.hsq_attention_unit(sc.q_unit(b, h), deq, unit["l3"], idx[b, h].cpu().numpy(),
+                                       w.group_n, w.d, sc.ks[h], sc.vs[h], sc.c4, sc.scale,
+                                       group_pos=sc.plans[b][1], rope_base=1e6)
+        e = float(np.linalg.norm(go[b, h * w.G:(h + 1) * w.G] - want) / np.linalg.norm(want))
+        assert e < 2e-3, f"unit {(b, h)}: rel L2 {e:.3e}"
