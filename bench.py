@@ -458,10 +458,12 @@ def host_archive(torch, hsq, W, reps=5, n_mb=2):
     lib = hsq.lib()
     per_seq = w.hkv * ng * rec  # archive bytes of one sequence in one layer
     # per half: a workspace per layer (it carries the selection and the summary
-    # partials from route to attend), one staging buffer
+    # partials from route to attend; sized for the pre-RoPE variant too), one
+    # staging buffer
     mb = []
     for b0, n in halves:
-        ws = [hsq.make_workspace(n, w.hq, w.hkv, w.d, n1, ng, beta, w.group_n, dev)
+        ws = [hsq.Workspace(hsq.prerope_workspace_bytes(n, w.hq, w.hkv, w.d, n1, ng, beta,
+                                                        w.group_n), dev)
               for _ in layers]
         stg = torch.empty((n, w.hkv, beta, rec), dtype=torch.uint8, device=dev)
         tv = [hsq.Tiers(n, w.hkv, w.d, n1, ng, w.group_n,
@@ -473,7 +475,7 @@ def host_archive(torch, hsq, W, reps=5, n_mb=2):
     main = streams[0]
     turn = torch.zeros(1, dtype=torch.int32, device=dev)
 
-    def one_step():
+    def one_step(prerope=False):
         # The gathers take the link in turn (micro-batch 0, 1, .. of layer 0,
         # then of layer 1, ..), each after the one before it, so that a
         # micro-batch's attend and next route run while another's records
@@ -495,8 +497,13 @@ def host_archive(torch, hsq, W, reps=5, n_mb=2):
                         beta, stg.data_ptr(), turn.data_ptr(), after & 0xFFFFFFFF,
                         st.cuda_stream))
                     after += n * w.hkv * beta
-                    hsq.step_attend(q, tv[i], w.beta, ly.dks, ly.dvs, cb["cb4"], ws[i],
-                                    ly.out[b0:b0 + n], l3=stg.data_ptr(), l3_staged=True)
+                    if prerope:  # the archive holds keys before RoPE
+                        hsq.step_attend_prerope(q, tv[i], w.beta, ly.dks, ly.dvs, cb["cb4"],
+                                                ly.gp[b0:b0 + n], 1e6, ws[i], ly.out[b0:b0 + n],
+                                                l3=stg.data_ptr(), l3_staged=True)
+                    else:
+                        hsq.step_attend(q, tv[i], w.beta, ly.dks, ly.dvs, cb["cb4"], ws[i],
+                                        ly.out[b0:b0 + n], l3=stg.data_ptr(), l3_staged=True)
         for st in streams[1:]:
             main.wait_stream(st)
 
@@ -506,6 +513,16 @@ def host_archive(torch, hsq, W, reps=5, n_mb=2):
     g = capture(torch, main, one_step)
     time_graph(torch, g, 1, main)
     ms = float(np.median(time_reps(torch, g, reps, main)))
+    del g
+    # the same step over a pre-RoPE archive: the fetched keys are rotated to
+    # their positions from the staged records before the attend
+    with torch.cuda.stream(main):
+        one_step(prerope=True)
+    torch.cuda.synchronize()
+    g = capture(torch, main, lambda: one_step(prerope=True))
+    time_graph(torch, g, 1, main)
+    ms_pre = float(np.median(time_reps(torch, g, reps, main)))
+    del g
     link_bytes = w.layers * w.batch * w.hkv * beta * rec
     # measured pinned host -> device copy rates, for context: 1 GiB copies, and
     # copies of one layer's gathered bytes (the transfer size of a gather)
@@ -548,6 +565,7 @@ def host_archive(torch, hsq, W, reps=5, n_mb=2):
         "workload": w.name, "layers": w.layers, "batch": w.batch, "T": w.T, "beta": beta,
         "micro_batches": len(halves),
         "ms_per_step": ms,
+        "prerope_ms_per_step": ms_pre,
         "value": w.batch * w.hkv * w.T * w.layers / (ms * 1e-3),
         "unit": "heads*tokens/s",
         "pcie_bytes_per_step": link_bytes,
@@ -558,7 +576,7 @@ def host_archive(torch, hsq, W, reps=5, n_mb=2):
         "gather_alone_gbs": gather_gbs,
         "archive_gib": per_layer * w.layers / 2 ** 30,
     }
-    del layers, arch, g, mb
+    del layers, arch, mb
     torch.cuda.empty_cache()
     return res
 
@@ -688,6 +706,7 @@ def _host_layer(w, layer, dev, hsq, W, cb, l3_dev_ptr):
     torch.cuda.synchronize()
     del k, v
     ly.tiers = t
+    ly.gp = gp  # the grouped tokens' positions (RoPE positions of a pre-RoPE archive)
     ly.q = W.query(w, layer, dev)
     ly.out = torch.empty((w.batch, w.hq, w.d), dtype=torch.float32, device=dev)
     return ly
