@@ -2148,8 +2148,9 @@ __device__ __forceinline__ void attend_unit(const TokArgs& a, const AttendLds& L
 
 // at most 128 VGPRs so that two work-groups (the LDS limit) fit on a CU.
 // TT = TokTileK: the fetched tiles multiply dense fp16 key rows (a.kdense)
-// instead of looking their codes up; the pipeline is one tile shallower to
-// make room for them.
+// instead of looking their codes up.  TT = TokTileQ: every tile also forms
+// the QJL correction of its keys (a.l1_sk ... a.S).  Both run the pipeline
+// one tile shallower to make room for their registers.
 template <int D, int N, typename TT = TokTile>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void token_kernel(TokArgs a) {
