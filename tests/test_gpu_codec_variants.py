@@ -143,7 +143,7 @@ def test_encode_4bit_any_symmetric_thresholds(close):
     rng = np.random.default_rng(8 + close)
     signs = rng.integers(0, 1 << 32, size=(1, d // 32), dtype=np.uint64).astype(np.uint32)
     x = _inputs(n, d, "f32", seed=77 + close)
-    codes, norms = hsq.encode(x.to(DEV), 4, signs_to_dev(signs), torch.from_numpy(t).to(DEV))
+    codes, norms = hsq.encode(x.to(DEV), 4, signs_to_dev(signs), torch.from_numpy(np.array(t)).to(DEV))
     torch.cuda.synchronize()
     oc, on, oy = codec.encode(x, signs[0], t)
     compare_codes(codes.cpu().numpy(), oc, oy, t, 4, d, f"close {close}")

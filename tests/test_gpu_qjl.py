@@ -73,7 +73,7 @@ def test_encode_qjl_parity(d, bits, dtype, n):
     check_encode(g, o, ct, bits, d, f"d={d} b={bits} {dtype} n={n}")
     # the codes and norms are the codec's, bit for bit
     c, t = ct
-    codes, norms = hsq.encode(xt.to(DEV), bits, signs_to_dev(signs), torch.from_numpy(t).to(DEV))
+    codes, norms = hsq.encode(xt.to(DEV), bits, signs_to_dev(signs), torch.from_numpy(np.array(t)).to(DEV))
     assert np.array_equal(codes.cpu().numpy(), g[0])
     assert np.array_equal(norms.cpu().numpy(), g[1])
 
