@@ -433,9 +433,6 @@ extern "C" int hsq_step_attend_prerope(const float* q, int B, int Hq, int Hkv, i
   StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, b};
   Workspace w;
   if ((rc = step_common(fn, s, workspace, ws_bytes, w))) return rc;
-  if (s.n_groups > 0 && !route_lds_ok(s))
-    return fail(HSQ_ERR_UNSUPPORTED,
-                std::string(fn) + ": G * n_groups exceeds 12288 (router logits beyond LDS)");
   const size_t kd_off = prerope_rows_off(w);
   if (ws_bytes < kd_off + prerope_rows_bytes(s))
     return fail(HSQ_ERR_WORKSPACE,
@@ -457,6 +454,9 @@ extern "C" int hsq_step_attend_prerope(const float* q, int B, int Hq, int Hkv, i
     if ((rc = check_hip(launch_rope_keys(j, st), "hsq_step_attend_prerope fetched keys")))
       return rc;
   }
+  if (s.n_groups > 0 && !route_lds_ok(s))  // the split step's second half, after its first
+    return check_hip(launch_split_half(s, t, w, ws, false, nullptr, st, b > 0 ? rows : nullptr),
+                     "hsq_step_attend_prerope (split)");
   return check_hip(launch_attn_prerope(s, t, w, ws, idx, b > 0 ? rows : nullptr, st),
                    "hsq_step_attend_prerope attention");
 }
@@ -485,9 +485,6 @@ extern "C" int hsq_decode_step_prerope(const float* q, int B, int Hq, int Hkv, i
   StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, b};
   Workspace w;
   if ((rc = step_common(fn, s, workspace, ws_bytes, w))) return rc;
-  if (s.n_groups > 0 && !route_lds_ok(s))
-    return fail(HSQ_ERR_UNSUPPORTED,
-                std::string(fn) + ": G * n_groups exceeds 12288 (router logits beyond LDS)");
   if (ws_bytes < prerope_rows_off(w) + prerope_rows_bytes(s))
     return fail(HSQ_ERR_WORKSPACE,
                 std::string(fn) + ": workspace smaller than hsq_prerope_workspace_bytes()");
@@ -534,9 +531,6 @@ extern "C" int hsq_decode_step_qjl(const float* q, int B, int Hq, int Hkv, int d
   StepShape s{B, Hq, Hkv, Hq / Hkv, d, n_l1, n_groups, group_n, b};
   Workspace w;
   if ((rc = step_common(fn, s, workspace, ws_bytes, w))) return rc;
-  if (s.n_groups > 0 && !route_lds_ok(s))
-    return fail(HSQ_ERR_UNSUPPORTED,
-                std::string(fn) + ": G * n_groups exceeds 12288 (router logits beyond LDS)");
   StepTensors t{};
   t.q = q; t.l1k = l1k; t.l1k_n = l1k_n; t.l1v = l1v; t.l1v_n = l1v_n;
   t.l2k = l2k; t.l2k_n = l2k_n; t.l2v = l2v; t.l2v_n = l2v_n; t.l3 = l3; t.l3_staged = 0;
@@ -544,14 +538,21 @@ extern "C" int hsq_decode_step_qjl(const float* q, int B, int Hq, int Hkv, int d
   t.summary_bias = summary_bias; t.agg = agg; t.out = out;
   char* ws = static_cast<char*>(workspace);
   const hipStream_t st = as_stream(stream);
+  const QjlKeys qk0{l1_sketch, l1_gamma, l3_sketch, l3_gamma, S};
+  if (s.n_groups > 0 && !route_lds_ok(s)) {  // router logits beyond LDS: the split step
+    if ((rc = check_hip(launch_split_half(s, t, w, ws, true, b > 0 ? topk_idx : nullptr, st),
+                        "hsq_decode_step_qjl route (split)")))
+      return rc;
+    return check_hip(launch_split_half(s, t, w, ws, false, nullptr, st, nullptr, &qk0),
+                     "hsq_decode_step_qjl attention (split)");
+  }
   int32_t* idx = reinterpret_cast<int32_t*>(ws + w.idx_off);
   if (s.n_groups > 0 &&
       (rc = check_hip(launch_route(s, t, w, ws, ROUTE_TOPK | ROUTE_PARTIALS, nullptr, nullptr,
                                    idx, st),
                       "hsq_decode_step_qjl route")))
     return rc;
-  const QjlKeys qk{l1_sketch, l1_gamma, l3_sketch, l3_gamma, S};
-  if ((rc = check_hip(launch_attn_qjl(s, t, w, ws, idx, qk, st), "hsq_decode_step_qjl attention")))
+  if ((rc = check_hip(launch_attn_qjl(s, t, w, ws, idx, qk0, st), "hsq_decode_step_qjl attention")))
     return rc;
   if (topk_idx && b > 0)
     return check_hip(hipMemcpyAsync(topk_idx, idx, sizeof(int32_t) * (size_t)B * Hkv * b,

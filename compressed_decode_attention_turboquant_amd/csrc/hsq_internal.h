@@ -131,8 +131,12 @@ hipError_t launch_split_step(const StepShape& s, const StepTensors& t, const Wor
 // (idx_out optional) and the summary-value chunks, from t's router inputs;
 // else the token chunks (L1 and the fetched records; staged ones by slot)
 // and the merge, from t's attend inputs.  Same shape and workspace in both.
+// The second half may run the pre-RoPE tiles (kdense: the fetched keys'
+// fp16 rows) or the TQ-QKV tiles (qk), as launch_attn_prerope / _qjl do.
+struct QjlKeys;
 hipError_t launch_split_half(const StepShape& s, const StepTensors& t, const Workspace& w,
-                             char* ws, bool first, int32_t* idx_out, hipStream_t st);
+                             char* ws, bool first, int32_t* idx_out, hipStream_t st,
+                             const uint16_t* kdense = nullptr, const QjlKeys* qk = nullptr);
 
 // mode bits for the summary kernel
 enum { ROUTE_TOPK = 1, ROUTE_PARTIALS = 2 };

@@ -3071,7 +3071,7 @@ __global__ __launch_bounds__(kThreads) void split_select_kernel(SplitArgs a) {
 // chunk k (tiles k * vt ..), else token chunk k - sv (tiles k - sv, with
 // stride st, of the unit's L1 and fetched tiles).  Each writes its partial
 // (m, l, O) per head to parts[unit][k].
-template <int D, int N>
+template <int D, int N, typename TT = TokTile>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void split_attend_kernel(SplitArgs a) {
   extern __shared__ __align__(16) char smem[];
@@ -3164,8 +3164,11 @@ void split_attend_kernel(SplitArgs a) {
   if (tid < 16) s_cb[tid] = cbv;
   rotate_query<D>(qin, ta.scale * rsqrtf((float)D), L.qf, tid);
   lds_barrier();
-  TokTile tt[kTokDepth];
-  attend_unit<D, N>(ta, L, tt, false, nullptr, nullptr, unit, k - p.sv, p.st, part);
+  // the variant tiles (pre-RoPE rows, TQ-QKV sketches) as in token_kernel
+  L.uf = reinterpret_cast<float*>(L.recoff + ((tok_slots<N>(ta.beta) + 3) & ~3));
+  constexpr int TD = std::is_same_v<TT, TokTile> ? kTokDepth : kTokDepth - 1;
+  TT tt[TD];
+  attend_unit<D, N, TT, TD>(ta, L, tt, false, nullptr, nullptr, unit, k - p.sv, p.st, part);
 }
 
 // Merge of one unit's partials and the inverse V rotation (8 * D / 8
@@ -3360,14 +3363,15 @@ hipError_t split_route_d(const SplitArgs& a, int units, bool exact, hipStream_t 
 }
 
 // Attend chunks [k0, k0 + n) of every unit; with merge, then the merge.
-template <int D, int N>
+template <int D, int N, typename TT = TokTile>
 hipError_t split_attend_dn(SplitArgs a, int units, int k0, int n, bool merge, hipStream_t st) {
   a.chunk0 = k0;
   a.nchunk = n;
   if (n > 0) {
-    const size_t smem = (size_t)kMaxG * kQS<D> * 4 + (size_t)tok_slots<N>(a.t.beta) * 4;
-    hipLaunchKernelGGL((split_attend_kernel<D, N>), dim3((unsigned)(units * n)), dim3(kThreads),
-                       smem, st, a);
+    const size_t smem = (size_t)kMaxG * kQS<D> * 4 + (size_t)((tok_slots<N>(a.t.beta) + 3) & ~3) * 4 +
+                        (std::is_same_v<TT, TokTileQ> ? (size_t)kMaxG * kQS<D> * 4 : 0);
+    hipLaunchKernelGGL((split_attend_kernel<D, N, TT>), dim3((unsigned)(units * n)),
+                       dim3(kThreads), smem, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -3394,6 +3398,8 @@ hipError_t split_halves_dn(const SplitArgs& a, int units, bool first, hipStream_
     if (e != hipSuccess) return e;
     return split_attend_dn<D, N>(a, units, 0, a.p.sv, false, st);
   }
+  if (a.t.kdense) return split_attend_dn<D, N, TokTileK>(a, units, a.p.sv, a.p.st, true, st);
+  if (a.t.S) return split_attend_dn<D, N, TokTileQ>(a, units, a.p.sv, a.p.st, true, st);
   return split_attend_dn<D, N>(a, units, a.p.sv, a.p.st, true, st);
 }
 
@@ -3410,10 +3416,22 @@ hipError_t launch_split_step(const StepShape& s, const StepTensors& t, const Wor
 }
 
 hipError_t launch_split_half(const StepShape& s, const StepTensors& t, const Workspace& w,
-                             char* ws, bool first, int32_t* idx_out, hipStream_t st) {
+                             char* ws, bool first, int32_t* idx_out, hipStream_t st,
+                             const uint16_t* kdense, const QjlKeys* qk) {
   if (!step_limits_ok(s) || !split_shape(s)) return hipErrorInvalidValue;
+  if (kdense && qk) return hipErrorInvalidValue;
   SplitArgs a = split_args(s, t, w, ws);
   a.idx_out = s.beta > 0 ? idx_out : nullptr;
+  if (!first) {
+    a.t.kdense = s.beta > 0 ? kdense : nullptr;
+    if (qk) {
+      if (!qk->S || (s.n_l1 > 0 && (!qk->l1_sk || !qk->l1_gam)) ||
+          (s.beta > 0 && (!qk->l3_sk || !qk->l3_gam)) || t.l3_staged)
+        return hipErrorInvalidValue;
+      a.t.l1_sk = qk->l1_sk; a.t.l1_gam = qk->l1_gam; a.t.l3_sk = qk->l3_sk;
+      a.t.l3_gam = qk->l3_gam; a.t.S = qk->S;
+    }
+  }
   const int units = s.B * s.Hkv;
   if (s.d == 128)
     return s.group_n == 16 ? split_halves_dn<128, 16>(a, units, first, st)

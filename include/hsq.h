@@ -315,9 +315,10 @@ int hsq_decode_step(const float* q, int B, int Hq, int Hkv, int d, const uint8_t
  *               hsq_workspace_bytes' plus B*Hkv*min(beta, n_groups)*group_n*d
  *               fp16 rows
  *   other arguments as in hsq_decode_step
+ * With G * n_groups > 12288 (router logits beyond the chip's LDS) the route
+ * and the attend are the split step's two halves, the RoPE pass between.
  * Errors: as hsq_decode_step, plus HSQ_ERR_ARG for a null group_pos (with
- * n_groups > 0) or a bad rope_base, HSQ_ERR_UNSUPPORTED when
- * G * n_groups > 12288 (router logits beyond the chip's LDS).
+ * n_groups > 0) or a bad rope_base.
  * hsq_prerope_workspace_bytes returns 0 for sizes hsq_workspace_bytes
  * rejects.
  */
@@ -367,9 +368,10 @@ int hsq_decode_step_prerope(const float* q, int B, int Hq, int Hkv, int d, const
  *               16-byte aligned (sketch arrays and gammas 4-byte aligned)
  *   workspace   hsq_workspace_bytes(...) bytes, as hsq_decode_step
  *   other arguments as in hsq_decode_step
+ * With G * n_groups > 12288 it runs as the split step's two halves, the
+ * token chunks with the sketch correction.
  * Errors: as hsq_decode_step, plus HSQ_ERR_ARG for a null or misaligned S,
- * null or misaligned sketches or gammas of a tier that has entries,
- * HSQ_ERR_UNSUPPORTED when G * n_groups > 12288.
+ * null or misaligned sketches or gammas of a tier that has entries.
  */
 int hsq_decode_step_qjl(const float* q, int B, int Hq, int Hkv, int d, const uint8_t* l1k,
                         const float* l1k_n, const uint8_t* l1v, const float* l1v_n, int n_l1,

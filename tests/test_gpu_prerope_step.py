@@ -182,3 +182,10 @@ def test_prerope_step_full_size_sampled_units():
     units = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.batch, 8),
                                               rng.integers(0, w.hkv, 8))]
     run_case(w, w.beta, units=sorted(set(units)))
+
+
+def test_prerope_step_beyond_on_chip_router_logits():
+    # G * n_groups = 5 * 3051 > 12288: the split route, the RoPE pass over
+    # its selection, and the split attend with the dense key rows
+    w = W.QWEN3_14B_16K.smaller(T=24576, batch=1, n_marked=100)
+    run_case(w, w.beta)

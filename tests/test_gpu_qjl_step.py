@@ -332,3 +332,10 @@ def test_variant_steps_graph_replays_match_eager(variant):
         assert torch.equal(idx, idx0), f"replay {r}: selection differs"
         assert torch.equal(out, out0), f"replay {r}: output differs"
         del junk
+
+
+def test_qjl_step_beyond_on_chip_router_logits():
+    # G * n_groups = 5 * 3051 > 12288: the split route and the split attend
+    # with the sketch correction
+    w = W.QWEN3_14B_16K.smaller(T=24576, batch=1, n_marked=100)
+    run_case(w, w.beta)
