@@ -362,15 +362,13 @@ __global__ __launch_bounds__(kWG) void rope_keys_kernel(RopeKeysJob j) {
 #pragma unroll
       for (int a = 0; a < 8; ++a) v[a] = flip(v[a] * isd, (sbyte[k] >> a) & 1u);
       rope8<LPV>(v, p[k], tlo, thi, sub);
-      // forward again: y = H D x / sqrt(d)
-#pragma unroll
-      for (int a = 0; a < 8; ++a) v[a] = flip(v[a], (sbyte[k] >> a) & 1u);
-      fwht8xlanes<LPV>(v, sub);
+      // the rows stay in the model's domain: the attend multiplies them
+      // against the unrotated query
       uint32_t w[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const _Float16 lo = ok[k] ? (_Float16)(v[2 * c] * isd) : (_Float16)0.f;
-        const _Float16 hi = ok[k] ? (_Float16)(v[2 * c + 1] * isd) : (_Float16)0.f;
+        const _Float16 lo = ok[k] ? (_Float16)v[2 * c] : (_Float16)0.f;
+        const _Float16 hi = ok[k] ? (_Float16)v[2 * c + 1] : (_Float16)0.f;
         w[c] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
                ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
       }

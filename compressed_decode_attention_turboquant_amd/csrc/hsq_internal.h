@@ -65,9 +65,10 @@ hipError_t launch_decode(const DecodeJob& j, hipStream_t s);
 
 // Fetched keys of a pre-RoPE archive (codec.hip): for every selection slot s
 // of every unit u and token t of the group, the 4-bit key of the record in
-// the rotated domain (unit norm), taken back to the model's domain, rotated
-// to the token's position, rotated forward again: fp16 out[u][s][t][d], the
-// rows the attend kernel multiplies in place of the table lookups.
+// the rotated domain (unit norm), taken back to the model's domain and
+// rotated to the token's position: fp16 out[u][s][t][d], the rows the attend
+// kernel multiplies against the unrotated query in place of the table
+// lookups.
 struct RopeKeysJob {
   const uint8_t* l3;        // archive records, N * (d + 8) bytes each
   int64_t unit_recs;        // records between consecutive units (n_groups or a capacity)
@@ -147,8 +148,9 @@ hipError_t launch_route(const StepShape& s, const StepTensors& t, const Workspac
 hipError_t launch_attn(const StepShape& s, const StepTensors& t, const Workspace& w, char* ws,
                        const int32_t* idx, hipStream_t st);
 // launch_attn over a pre-RoPE archive: the fetched tiles multiply the fp16
-// key rows kdense [units][beta][group_n][d] (launch_rope_keys) instead of
-// the records' key codes (kdense may be null when beta == 0)
+// model-domain key rows kdense [units][beta][group_n][d] (launch_rope_keys)
+// against the unrotated query instead of the records' key codes against the
+// rotated one (kdense may be null when beta == 0)
 hipError_t launch_attn_prerope(const StepShape& s, const StepTensors& t, const Workspace& w,
                                char* ws, const int32_t* idx, const uint16_t* kdense,
                                hipStream_t st);

@@ -1756,9 +1756,9 @@ struct TokTile {
   float vn;        // value norm of row 4gq + (lane & 3)
   uint32_t va[4];  // value bits of rows 4gq+j for lane rho = lane&15
 };
-// A tile that also carries the fetched keys' fp16 rows (pre-RoPE archive):
-// the lane's D/4 coordinates of token row lane&15, the MFMA operands as they
-// are (D=64 uses kd[0..1]).
+// A tile that also carries the fetched keys' fp16 rows (pre-RoPE archive, in
+// the model's domain): the lane's D/4 coordinates of token row lane&15, the
+// MFMA operands as they are (D=64 uses kd[0..1]).
 struct TokTileK : TokTile {
   u32x4 kd[4];
 };
@@ -1951,9 +1951,11 @@ __device__ __forceinline__ void consume_tok(const TT& T, bool masked, MaskF mask
   f32x4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   if constexpr (std::is_same_v<TT, TokTileK>) {
     if (dense) {  // wave-uniform: a fetched tile of a pre-RoPE archive
+      // model-domain rows against the unrotated query (uh: its fp16
+      // operands in LDS)
 #pragma unroll
       for (int m = 0; m < D / 32; ++m)
-        acc2[m & 1] = mfma16(__builtin_bit_cast(half8, T.kd[m]), qh[m], acc2[m & 1]);
+        acc2[m & 1] = mfma16(__builtin_bit_cast(half8, T.kd[m]), uh[m], acc2[m & 1]);
     }
   }
   if (!(std::is_same_v<TT, TokTileK> && dense)) {
@@ -2017,7 +2019,23 @@ struct AttendLds {
   float* cb;        // 16 centroids of the 4-bit codebook
   uint32_t* vsb;    // V sign byte per (head, lane of the inverse rotation)
   float* uf;        // TQ-QKV: scale sqrt(pi/2)/D S R q per head, kMaxG * kQS<D>
+  _Float16* qm;     // pre-RoPE: scale * q per head, unrotated, fp16 [kMaxG][D]
 };
+
+// Pre-RoPE: scale * q of the lane's coordinates into L.qm (fp16), from the
+// unrotated query values load_query brought (before rotate_query).
+template <int D>
+__device__ __forceinline__ void stage_query_model(const QueryIn& Q, float scale, _Float16* qm,
+                                                  int tid) {
+  constexpr int LPV = D / 8;
+  if (tid < kMaxG * LPV) {
+    const int h = tid / LPV, sub = tid % LPV;
+    half8 x;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = (_Float16)(Q.v[k] * scale);
+    *reinterpret_cast<half8*>(qm + h * D + 8 * sub) = x;
+  }
+}
 
 // L1 + fetched-token attention of one unit, merged with the summary partial,
 // inverse V rotation, output.  On entry every array of L except the table
@@ -2068,6 +2086,10 @@ __device__ __forceinline__ void attend_unit(const TokArgs& a, const AttendLds& L
   lds_barrier();
   half8 uh[QJL ? D / 32 : 1];
   if constexpr (QJL) qjl_operands<D>(L.uf, lane, uh);
+  // pre-RoPE: the B operands of the dense rows are read from LDS per tile
+  const half8* uq = uh;
+  if constexpr (std::is_same_v<TT, TokTileK>)
+    uq = reinterpret_cast<const half8*>(L.qm + col_head(lane & 15) * D + (lane >> 4) * (D / 4));
 
   Softmax<D> st;
   if (st_in)
@@ -2094,7 +2116,7 @@ __device__ __forceinline__ void attend_unit(const TokArgs& a, const AttendLds& L
           consume_tok<D>(
               T, masked,
               [&](float (&lg)[4]) { mask_rows<N>(lg, t, n1t, a.n1, a.beta, L.recoff, lane); },
-              qh, lut4, lane, lane4, st, t >= n1t, uh);
+              qh, lut4, lane, lane4, st, t >= n1t, uq);
         });
   }
   lds_barrier();  // the table is no longer needed: reuse as scratch
@@ -2161,7 +2183,7 @@ void token_kernel(TokArgs a) {
   __shared__ uint32_t s_vsb[kMaxG * (D / 8)];
   __shared__ int s_bad;  // some slot names no record
   // dynamic layout: [qf 8*(D+4) f32][summary partial 8*(D+2) f32]
-  //   [recoff tok_slots(beta)][TQ-QKV: uf 8*(D+4) f32]
+  //   [recoff tok_slots(beta)][TQ-QKV: uf 8*(D+4) f32 | pre-RoPE: qm 8*D f16]
   AttendLds L;
   L.lut4 = s_lut4;
   L.qf = reinterpret_cast<float*>(smem);
@@ -2170,6 +2192,7 @@ void token_kernel(TokArgs a) {
   L.cb = s_cb;
   L.vsb = s_vsb;
   L.uf = reinterpret_cast<float*>(L.recoff + ((tok_slots<N>(a.beta) + 3) & ~3));
+  L.qm = reinterpret_cast<_Float16*>(L.uf);
 
   const int tid = threadIdx.x, wave = wave_id();
   const int unit = blockIdx.x;
@@ -2213,6 +2236,7 @@ void token_kernel(TokArgs a) {
 #pragma unroll
   for (int r = 0; r < 3; ++r)
     if (tid + r * kThreads < np) L.part[tid + r * kThreads] = pv[r];
+  if constexpr (std::is_same_v<TT, TokTileK>) stage_query_model<D>(qin, a.scale, L.qm, tid);
   rotate_query<D>(qin, a.scale * rsqrtf((float)D), L.qf, tid);
   lds_barrier();
   if (bad) s_bad = 1;  // read after the next barrier
@@ -3162,10 +3186,12 @@ void split_attend_kernel(SplitArgs a) {
     L.recoff[s] = ok ? (int32_t)(r * (uint32_t)rec) : (int32_t)kFar;
   }
   if (tid < 16) s_cb[tid] = cbv;
-  rotate_query<D>(qin, ta.scale * rsqrtf((float)D), L.qf, tid);
-  lds_barrier();
   // the variant tiles (pre-RoPE rows, TQ-QKV sketches) as in token_kernel
   L.uf = reinterpret_cast<float*>(L.recoff + ((tok_slots<N>(ta.beta) + 3) & ~3));
+  L.qm = reinterpret_cast<_Float16*>(L.uf);
+  if constexpr (std::is_same_v<TT, TokTileK>) stage_query_model<D>(qin, ta.scale, L.qm, tid);
+  rotate_query<D>(qin, ta.scale * rsqrtf((float)D), L.qf, tid);
+  lds_barrier();
   constexpr int TD = std::is_same_v<TT, TokTile> ? kTokDepth : kTokDepth - 1;
   TT tt[TD];
   attend_unit<D, N, TT, TD>(ta, L, tt, false, nullptr, nullptr, unit, k - p.sv, p.st, part);
@@ -3212,10 +3238,12 @@ size_t summary_smem(int D, const StepShape& s) {
   return std::max(body, comb);
 }
 
-size_t token_smem(int D, const StepShape& s, bool qjl = false) {
+// variant: the region after the record offsets (TQ-QKV u rows, or the
+// pre-RoPE unrotated query)
+size_t token_smem(int D, const StepShape& s, bool variant = false) {
   const int slots = s.group_n == 16 ? tok_slots<16>(s.beta) : tok_slots<8>(s.beta);
   return (size_t)kMaxG * (D + 4) * 4 + (size_t)kMaxG * (D + 2) * 4 +
-         (size_t)((slots + 3) & ~3) * 4 + (qjl ? (size_t)kMaxG * (D + 4) * 4 : 0);
+         (size_t)((slots + 3) & ~3) * 4 + (variant ? (size_t)kMaxG * (D + 4) * 4 : 0);
 }
 
 // Waves per work-group of the one-launch step: 16 (one work-group per CU)
@@ -3369,7 +3397,7 @@ hipError_t split_attend_dn(SplitArgs a, int units, int k0, int n, bool merge, hi
   a.nchunk = n;
   if (n > 0) {
     const size_t smem = (size_t)kMaxG * kQS<D> * 4 + (size_t)((tok_slots<N>(a.t.beta) + 3) & ~3) * 4 +
-                        (std::is_same_v<TT, TokTileQ> ? (size_t)kMaxG * kQS<D> * 4 : 0);
+                        (std::is_same_v<TT, TokTile> ? 0 : (size_t)kMaxG * kQS<D> * 4);
     hipLaunchKernelGGL((split_attend_kernel<D, N, TT>), dim3((unsigned)(units * n)),
                        dim3(kThreads), smem, st, a);
     const hipError_t e = hipGetLastError();
@@ -3471,7 +3499,7 @@ hipError_t token_d(const StepShape& s, const StepTensors& t, const Workspace& w,
     a.l1_sk = qk->l1_sk; a.l1_gam = qk->l1_gam; a.l3_sk = qk->l3_sk; a.l3_gam = qk->l3_gam;
     a.S = qk->S;
   }
-  const size_t smem = token_smem(D, s, qk != nullptr);
+  const size_t smem = token_smem(D, s, !std::is_same_v<TT, TokTile>);
   if (s.group_n == 16)
     hipLaunchKernelGGL((token_kernel<D, 16, TT>), dim3((unsigned)(s.B * s.Hkv)), dim3(kThreads),
                        smem, st, a);
