@@ -304,10 +304,10 @@ int hsq_decode_step(const float* q, int B, int Hq, int Hkv, int d, const uint8_t
  * summaries and L1 are as in hsq_decode_step (hsq_step_route, then
  * hsq_step_attend_prerope over the archive in place); between them a
  * third launch takes every fetched record's 4-bit key codes back to the
- * model's domain, rotates each token to its position, rotates the result
- * forward again into fp16 rows in the workspace, and the attention multiplies
- * those rows where it would look the codes up (the norms, the values and
- * everything else unchanged).
+ * model's domain and rotates each token to its position, into fp16 rows in
+ * the workspace, and the attention multiplies those rows against the
+ * unrotated query where it would look the codes up (the norms, the values
+ * and everything else unchanged).
  *   group_pos   int32 [B][n_groups*group_n] (device): position of token t of
  *               group g of sequence b at [b][g*group_n + t], any value
  *   rope_base   the rotary base (1e6 for the Qwen3 models), finite, > 0
