@@ -301,12 +301,20 @@ hipError_t encode_dt(const EncodeJob& j, hipStream_t s) {
 // lanes, kDecVPT vectors per lane group with their loads issued together
 // (each vector's address waits on its selection entry), in blocks strided
 // over a grid of at most the resident work-groups (the turns table costs a
-// set-up per work-group).  A slot whose selection names no group gets a zero
-// row.  Indices past the end are clamped to the last vector (recomputed, not
-// stored), so every lane runs the cross-lane steps.
+// set-up per work-group).  Lane sub of a vector holds coordinates
+// 4 sub .. 4 sub + 3 (registers 0-3) and D/2 + 4 sub .. (registers 4-7), so
+// every rotary pair (f, f + D/2) sits in one lane and the rotation needs no
+// partner lane.  The transform back to the model's domain does not care
+// which coordinate bit a lane or register bit stands for (the Hadamard
+// matrix is the same under a permutation of the index bits applied to rows
+// and columns): register bits 0, 1, 2 are coordinate bits 0, 1 and
+// log2(D) - 1, lane bits are coordinate bits 2 .. log2(D) - 2.  A slot whose
+// selection names no group gets a zero row.  Indices past the end are
+// clamped to the last vector (recomputed, not stored), so every lane runs
+// the cross-lane steps.
 template <int D>
 __global__ __launch_bounds__(kWG) void rope_keys_kernel(RopeKeysJob j) {
-  constexpr int LPV = D / 8, VPB = kWG / LPV, CB = D / 2, U = kDecVPT;
+  constexpr int LPV = D / 8, VPB = kWG / LPV, CB = D / 2, U = kDecVPT, H = D / 2;
   __shared__ __align__(16) float tab[256 * 2];  // code byte -> its two centroids
   __shared__ uint32_t turns_lo[D / 2], turns_hi[D / 2];
   if (threadIdx.x < 256) {
@@ -316,8 +324,13 @@ __global__ __launch_bounds__(kWG) void rope_keys_kernel(RopeKeysJob j) {
   rope_turns<D>(j.rope_base, turns_lo, turns_hi);
   __syncthreads();
   const int sub = threadIdx.x % LPV;
+  // this lane's four pair angles: f = 4 sub + k
   uint32_t tlo[4], thi[4];
-  rope_lane_turns<LPV>(turns_lo, turns_hi, sub, tlo, thi);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    tlo[k] = turns_lo[4 * sub + k];
+    thi[k] = turns_hi[4 * sub + k];
+  }
   const uint32_t N = (uint32_t)j.group_n, beta = (uint32_t)j.beta, Hkv = (uint32_t)j.Hkv;
   const uint64_t rec = (uint64_t)N * (D + 8);
   const uint32_t n_vec = (uint32_t)j.units * beta * N;  // < 2^31 (launch_rope_keys)
@@ -326,7 +339,7 @@ __global__ __launch_bounds__(kWG) void rope_keys_kernel(RopeKeysJob j) {
   for (uint32_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
     uint32_t i[U];
     bool valid[U], ok[U];
-    uint32_t codes[U], sbyte[U];
+    uint32_t clo[U], chi[U], sbyte[U];
     int32_t p[U];
 #pragma unroll
     for (int k = 0; k < U; ++k) {
@@ -344,26 +357,43 @@ __global__ __launch_bounds__(kWG) void rope_keys_kernel(RopeKeysJob j) {
       const uint32_t g = ok[k] ? (uint32_t)g0 : 0u;
       // the record: in place by group, or gathered by slot (staged)
       const uint64_t r = j.staged ? (uint64_t)us : (uint64_t)u * j.unit_recs + g;
-      codes[k] = *reinterpret_cast<const uint32_t*>(j.l3 + r * rec + t * CB + 4 * sub);
+      const uint8_t* row = j.l3 + r * rec + t * CB;
+      // codes of coordinates 4 sub .. +3 and H + 4 sub .. +3 (two bytes each)
+      clo[k] = *reinterpret_cast<const uint16_t*>(row + 2 * sub);
+      chi[k] = *reinterpret_cast<const uint16_t*>(row + H / 2 + 2 * sub);
       p[k] = j.group_pos[(uint64_t)b * j.pos_per_seq + g * N + t];
-      sbyte[k] = sign_byte(j.k_signs + h * (D / 32), sub);
+      const uint32_t* m = j.k_signs + h * (D / 32);
+      const int c0 = 4 * sub, c1 = H + 4 * sub;
+      sbyte[k] = ((m[c0 >> 5] >> (c0 & 31)) & 0xfu) | (((m[c1 >> 5] >> (c1 & 31)) & 0xfu) << 4);
     }
 #pragma unroll
     for (int k = 0; k < U; ++k) {
       float v[8];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float2 e = reinterpret_cast<const float2*>(tab)[(codes[k] >> (8 * c)) & 0xffu];
-        v[2 * c] = e.x;
-        v[2 * c + 1] = e.y;
+      for (int c = 0; c < 2; ++c) {
+        const float2 e0 = reinterpret_cast<const float2*>(tab)[(clo[k] >> (8 * c)) & 0xffu];
+        const float2 e1 = reinterpret_cast<const float2*>(tab)[(chi[k] >> (8 * c)) & 0xffu];
+        v[2 * c] = e0.x;
+        v[2 * c + 1] = e0.y;
+        v[4 + 2 * c] = e1.x;
+        v[4 + 2 * c + 1] = e1.y;
       }
       // back to the model's domain: x = D H c / sqrt(d)
       fwht8xlanes<LPV>(v, sub);
 #pragma unroll
       for (int a = 0; a < 8; ++a) v[a] = flip(v[a] * isd, (sbyte[k] >> a) & 1u);
-      rope8<LPV>(v, p[k], tlo, thi, sub);
-      // the rows stay in the model's domain: the attend multiplies them
-      // against the unrotated query
+      // RoPE on the lane's four pairs (v[a], v[a + 4]), angle p * turns[4 sub + a]
+      const uint32_t pu = (uint32_t)p[k];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        // top word of p * turns mod 2^64 (a negative p is pu - 2^32)
+        const uint32_t top = __umulhi(pu, tlo[a]) + pu * thi[a] - (p[k] < 0 ? tlo[a] : 0u);
+        const float rev = (float)top * 0x1p-32f;
+        const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+        const float x0 = v[a], x1 = v[a + 4];
+        v[a] = x0 * cs - x1 * sn;
+        v[a + 4] = x1 * cs + x0 * sn;
+      }
       uint32_t w[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -372,9 +402,11 @@ __global__ __launch_bounds__(kWG) void rope_keys_kernel(RopeKeysJob j) {
         w[c] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
                ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
       }
-      if (valid[k])
-        *reinterpret_cast<uint4*>(j.out + (uint64_t)i[k] * D + 8 * sub) =
-            make_uint4(w[0], w[1], w[2], w[3]);
+      if (valid[k]) {
+        uint16_t* o = j.out + (uint64_t)i[k] * D;
+        *reinterpret_cast<uint2*>(o + 4 * sub) = make_uint2(w[0], w[1]);
+        *reinterpret_cast<uint2*>(o + H + 4 * sub) = make_uint2(w[2], w[3]);
+      }
     }
   }
 }
