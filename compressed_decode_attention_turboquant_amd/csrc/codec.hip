@@ -112,52 +112,7 @@ __device__ __forceinline__ void rope_turns(double base, uint32_t* lo, uint32_t* 
     hi[threadIdx.x] = (uint32_t)(fx >> 32);
   }
 }
-// Lane sub holds coordinates 8 sub .. 8 sub + 7; coordinate f < d/2 pairs
-// with f + d/2, in the same slot of lane sub ^ LPV/2.  Both lanes of a pair
-// need the same angles: the lower one takes slots 0..3, the upper one slots
-// 4..7, and they swap the results.  This lane's four turns:
-template <int LPV>
-__device__ __forceinline__ void rope_lane_turns(const uint32_t* lo, const uint32_t* hi, int sub,
-                                                uint32_t (&tlo)[4], uint32_t (&thi)[4]) {
-  constexpr int HALF = LPV / 2;
-  const bool upper = sub >= HALF;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int f = 8 * (sub % HALF) + (upper ? 4 : 0) + k;
-    tlo[k] = lo[f];
-    thi[k] = hi[f];
-  }
-}
-// Rotate the lane's 8 coordinates (with the partner lane's) to position p.
-template <int LPV>
-__device__ __forceinline__ void rope8(float (&v)[8], int32_t p, const uint32_t (&tlo)[4],
-                                      const uint32_t (&thi)[4], int sub) {
-  constexpr int HALF = LPV / 2;
-  const bool upper = sub >= HALF;
-  const uint32_t pu = (uint32_t)p;
-  float sn[8], cs[8];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    // top word of p * turns mod 2^64: the fraction of a turn in units of
-    // 2^-32 (a negative p is pu - 2^32, which takes tlo off that word)
-    const uint32_t top = __umulhi(pu, tlo[k]) + pu * thi[k] - (p < 0 ? tlo[k] : 0u);
-    const float rev = (float)top * 0x1p-32f;
-    // the hardware sine and cosine take their argument in turns
-    const float s1 = __builtin_amdgcn_sinf(rev), c1 = __builtin_amdgcn_cosf(rev);
-    const float s2 = xor_lane<HALF>(s1), c2 = xor_lane<HALF>(c1);
-    sn[k] = upper ? s2 : s1;
-    cs[k] = upper ? c2 : c1;
-    sn[k + 4] = upper ? s1 : s2;
-    cs[k + 4] = upper ? c1 : c2;
-  }
-#pragma unroll
-  for (int a = 0; a < 8; ++a) {
-    const float partner = xor_lane<HALF>(v[a]);
-    v[a] = v[a] * cs[a] + (upper ? partner : -partner) * sn[a];
-  }
-}
-
-template <int D, int BITS, int OUT, bool ROT, bool ROPE>
+template <int D, int BITS, int OUT, bool ROT>
 __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j, Div32 per_rot, Div32 n_rot) {
   constexpr int LPV = D / 8;
   constexpr int VPB = kWG / LPV;
@@ -166,34 +121,26 @@ __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j, Div32 per_rot,
   constexpr int CW = BITS == 3 ? 2 : 1;  // code dwords loaded per lane and vector
   constexpr int NE = DecTab<BITS>::kEntries, PER = DecTab<BITS>::kPer;
   __shared__ __align__(16) float tab[NE * PER];
-  // RoPE: turns per position of each coordinate pair (rope_turns)
-  __shared__ uint32_t turns_lo[ROPE ? D / 2 : 1], turns_hi[ROPE ? D / 2 : 1];
   if (threadIdx.x < NE) {
     constexpr uint32_t M = (1u << BITS) - 1;
 #pragma unroll
     for (int k = 0; k < PER; ++k)
       tab[threadIdx.x * PER + k] = j.centroids[(threadIdx.x >> (BITS * k)) & M];
   }
-  if constexpr (ROPE) rope_turns<D>(j.rope_base, turns_lo, turns_hi);
   __syncthreads();
   const int sub = threadIdx.x % LPV;
-  uint32_t tlo[4] = {}, thi[4] = {};
-  if constexpr (ROPE) rope_lane_turns<LPV>(turns_lo, turns_hi, sub, tlo, thi);
   // This lane's code bits of a row: BITS = 4 one dword; 2: half a dword;
   // 3: 24 bits from bit 24 sub (two dwords, the second inside the row).
   const int bit = BITS * 8 * sub;
   const int w0 = bit >> 5, sh = bit & 31;
   const int w1 = min(w0 + 1, CB / 4 - 1);
-  // Blocks of U * VPB vectors, one per work-group (the RoPE variant, whose
-  // table costs a set-up per work-group, strides over them with a grid of at
-  // most the resident work-groups); every load of a block (codes, norm, sign
-  // word, position) is issued before the first vector is decoded.
+  // Blocks of U * VPB vectors, one per work-group; every load of a block
+  // (codes, norm, sign word) is issued before the first vector is decoded.
   const uint64_t nblk = ((uint64_t)j.n_vec + U * VPB - 1) / (U * VPB);
   for (uint64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
     uint32_t cw[U][CW];
     float r[U];
     uint32_t sw[U];
-    int32_t ps[U];
     bool valid[U];
     uint32_t idx[U];
 #pragma unroll
@@ -208,8 +155,6 @@ __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j, Div32 per_rot,
       r[u] = j.norms[i];
       sw[u] = 0u;
       if constexpr (ROT) sw[u] = j.signs[rot_of(i, per_rot, n_rot) * (D / 32) + sub / 4];
-      ps[u] = 0;
-      if constexpr (ROPE) ps[u] = j.pos[i];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -253,7 +198,6 @@ __global__ __launch_bounds__(kWG) void decode_kernel(DecodeJob j, Div32 per_rot,
 #pragma unroll
       for (int a = 0; a < 8; ++a)
         v[a] = __uint_as_float(__float_as_uint(v[a] * s) ^ (((sbyte >> a) & 1u) << 31));
-      if constexpr (ROPE) rope8<LPV>(v, ps[u], tlo, thi, sub);
       if (valid[u]) {
         const uint32_t i = idx[u];
         if constexpr (OUT == HSQ_F32) {
@@ -411,21 +355,141 @@ __global__ __launch_bounds__(kWG) void rope_keys_kernel(RopeKeysJob j) {
   }
 }
 
+// RoPE fetch (hsq_decode_rope) with each rotary pair in one lane: lane sub
+// holds coordinates 4 sub .. 4 sub + 3 (registers 0-3) and D/2 + 4 sub ..
+// (registers 4-7), as in rope_keys_kernel, so the rotation needs no partner
+// lane; the in-register FWHT runs unchanged under that relabelling of the
+// coordinate bits.  kDecVPT vectors per lane group with all their loads
+// issued first; at most a chip of resident work-groups striding over the
+// blocks (the turns table costs a set-up per work-group).
+template <int D, int BITS, int OUT, bool ROT>
+__global__ __launch_bounds__(kWG) void rope_decode_kernel(DecodeJob j, Div32 per_rot,
+                                                          Div32 n_rot) {
+  constexpr int LPV = D / 8, VPB = kWG / LPV, U = kDecVPT, H = D / 2;
+  constexpr int CB = D * BITS / 8;
+  constexpr int NE = DecTab<BITS>::kEntries, PER = DecTab<BITS>::kPer;
+  constexpr int FB = BITS * PER;  // code bits per table entry
+  __shared__ __align__(16) float tab[NE * PER];
+  __shared__ uint32_t turns_lo[D / 2], turns_hi[D / 2];
+  if (threadIdx.x < NE) {
+    constexpr uint32_t M = (1u << BITS) - 1;
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+      tab[threadIdx.x * PER + k] = j.centroids[(threadIdx.x >> (BITS * k)) & M];
+  }
+  rope_turns<D>(j.rope_base, turns_lo, turns_hi);
+  __syncthreads();
+  const int sub = threadIdx.x % LPV;
+  uint32_t tlo[4], thi[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    tlo[k] = turns_lo[4 * sub + k];
+    thi[k] = turns_hi[4 * sub + k];
+  }
+  // the 4 * BITS code bits of coordinates c .. c + 3 of a row (byte loads:
+  // 3-bit fields start on half bytes)
+  auto codes4 = [&](const uint8_t* row, int c) -> uint32_t {
+    const int bit = BITS * c, b0 = bit >> 3;
+    uint32_t w = row[b0];
+    if constexpr (BITS > 2) w |= (uint32_t)row[b0 + 1] << 8;
+    return (w >> (bit & 7)) & ((1u << (4 * BITS)) - 1u);
+  };
+  const uint64_t nblk = ((uint64_t)j.n_vec + U * VPB - 1) / (U * VPB);
+  for (uint64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    uint32_t clo[U], chi[U], sbyte[U], idx[U];
+    float r[U];
+    int32_t ps[U];
+    bool valid[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t i64 = blk * (U * VPB) + (uint64_t)(u * VPB) + threadIdx.x / LPV;
+      valid[u] = i64 < (uint64_t)j.n_vec;
+      const uint32_t i = valid[u] ? (uint32_t)i64 : (uint32_t)(j.n_vec - 1);  // reread the last
+      idx[u] = i;
+      const uint8_t* row = j.codes + (int64_t)i * CB;
+      clo[u] = codes4(row, 4 * sub);
+      chi[u] = codes4(row, H + 4 * sub);
+      r[u] = j.norms[i];
+      sbyte[u] = 0u;
+      if constexpr (ROT) {
+        const uint32_t* m = j.signs + rot_of(i, per_rot, n_rot) * (D / 32);
+        const int c0 = 4 * sub, c1 = H + 4 * sub;
+        sbyte[u] = ((m[c0 >> 5] >> (c0 & 31)) & 0xfu) | (((m[c1 >> 5] >> (c1 & 31)) & 0xfu) << 4);
+      }
+      ps[u] = j.pos[i];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 4 / PER; ++e) {
+        const float* t0 = tab + ((clo[u] >> (FB * e)) & (NE - 1)) * PER;
+        const float* t1 = tab + ((chi[u] >> (FB * e)) & (NE - 1)) * PER;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+          v[PER * e + k] = t0[k];
+          v[4 + PER * e + k] = t1[k];
+        }
+      }
+      if constexpr (ROT) fwht8xlanes<LPV>(v, sub);
+      const float sc = ROT ? r[u] * (1.f / __builtin_sqrtf((float)D)) : r[u];
+#pragma unroll
+      for (int a = 0; a < 8; ++a) v[a] = flip(v[a] * sc, (sbyte[u] >> a) & 1u);
+      const uint32_t pu = (uint32_t)ps[u];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        // top word of p * turns mod 2^64 (a negative p is pu - 2^32)
+        const uint32_t top = __umulhi(pu, tlo[a]) + pu * thi[a] - (ps[u] < 0 ? tlo[a] : 0u);
+        const float rev = (float)top * 0x1p-32f;
+        const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+        const float x0 = v[a], x1 = v[a + 4];
+        v[a] = x0 * cs - x1 * sn;
+        v[a + 4] = x1 * cs + x0 * sn;
+      }
+      if (valid[u]) {
+        const int64_t o = (int64_t)idx[u] * D;
+        if constexpr (OUT == HSQ_F32) {
+          float* dst = static_cast<float*>(j.out) + o;
+          *reinterpret_cast<float4*>(dst + 4 * sub) = make_float4(v[0], v[1], v[2], v[3]);
+          *reinterpret_cast<float4*>(dst + H + 4 * sub) = make_float4(v[4], v[5], v[6], v[7]);
+        } else {
+          uint32_t w[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            w[k] = __builtin_bit_cast(uint32_t,
+                                      __builtin_convertvector(f32x2{v[2 * k], v[2 * k + 1]}, bf16x2));
+          uint16_t* dst = static_cast<uint16_t*>(j.out) + o;
+          *reinterpret_cast<uint2*>(dst + 4 * sub) = make_uint2(w[0], w[1]);
+          *reinterpret_cast<uint2*>(dst + H + 4 * sub) = make_uint2(w[2], w[3]);
+        }
+      }
+    }
+  }
+}
+
 template <int D, int BITS, bool ROT, bool ROPE>
 hipError_t decode_out(const DecodeJob& j, hipStream_t s) {
   constexpr int VPB = kWG / (D / 8);
   // the RoPE variant: at most a chip of resident work-groups (256 CUs, 4
-  // work-groups of 4 waves each: its register use allows 5 or 6), each
-  // striding over the blocks
+  // work-groups of 4 waves each), each striding over the blocks
   const int64_t blocks = (j.n_vec + kDecVPT * VPB - 1) / (kDecVPT * VPB);
   const int64_t grid = ROPE ? std::min<int64_t>(blocks, 256 * 4) : blocks;
   const Div32 per_rot = make_div32(j.vecs_per_rot), n_rot = make_div32(j.n_rot);
-  if (j.out_dtype == HSQ_F32)
-    hipLaunchKernelGGL((decode_kernel<D, BITS, HSQ_F32, ROT, ROPE>), dim3((unsigned)grid), dim3(kWG),
-                       0, s, j, per_rot, n_rot);
-  else
-    hipLaunchKernelGGL((decode_kernel<D, BITS, HSQ_BF16, ROT, ROPE>), dim3((unsigned)grid), dim3(kWG),
-                       0, s, j, per_rot, n_rot);
+  if constexpr (ROPE) {
+    if (j.out_dtype == HSQ_F32)
+      hipLaunchKernelGGL((rope_decode_kernel<D, BITS, HSQ_F32, ROT>), dim3((unsigned)grid),
+                         dim3(kWG), 0, s, j, per_rot, n_rot);
+    else
+      hipLaunchKernelGGL((rope_decode_kernel<D, BITS, HSQ_BF16, ROT>), dim3((unsigned)grid),
+                         dim3(kWG), 0, s, j, per_rot, n_rot);
+  } else {
+    if (j.out_dtype == HSQ_F32)
+      hipLaunchKernelGGL((decode_kernel<D, BITS, HSQ_F32, ROT>), dim3((unsigned)grid), dim3(kWG),
+                         0, s, j, per_rot, n_rot);
+    else
+      hipLaunchKernelGGL((decode_kernel<D, BITS, HSQ_BF16, ROT>), dim3((unsigned)grid), dim3(kWG),
+                         0, s, j, per_rot, n_rot);
+  }
   return hipGetLastError();
 }
 
